@@ -1,0 +1,121 @@
+"""Python front end of the fp64 KDA oracle (kda_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg; never by the product path.  It shares no code
+with the HIP library: it reads the exact input values the GPU receives
+(bf16 or fp32, upcast element by element to fp64) and runs the sequential
+recurrence of "Kimi K3: Open Frontier Intelligence and Implementation
+Framework", section "Hybrid Attention Mechanism" (the delta rule with a
+channel-wise forget gate; the exact form is written out in kda_oracle.c).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile kda_oracle.c with gcc (fp64, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off",
+                        "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load_library(path: str):
+    """Open a compiled oracle library and declare its entry point."""
+    lib = ctypes.CDLL(path)
+    p = ctypes.POINTER(ctypes.c_double)
+    lib.kda_oracle_recurrence.argtypes = [p, p, p, p, p, p, p, p,
+                                          ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    lib.kda_oracle_recurrence.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        _lib = load_library(_LIB)
+    return _lib
+
+
+def host_threads() -> int:
+    """Threads the oracle uses by default: the host cores this process may run on."""
+    return len(os.sched_getaffinity(0))
+
+
+def as_f64(x) -> np.ndarray:
+    """Exact upcast of a torch tensor (fp32 or bf16) or array to contiguous fp64."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().double().numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def recurrence(q, k, v, g, beta, cu_seqlens, s0=None, nthreads: int | None = None):
+    """Packed sequences.  q, k, g [tokens, H, K]; v [tokens, H, V]; beta [tokens, H];
+    cu_seqlens [N + 1]; s0 [N, H, K, V] or None.  Returns (o [tokens, H, V],
+    sT [N, H, K, V]) in fp64."""
+    q, k, v, g, beta, s0 = (as_f64(x) for x in (q, k, v, g, beta, s0))
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    tokens, H, K = q.shape
+    V = v.shape[-1]
+    N = len(cu) - 1
+    assert k.shape == (tokens, H, K) and g.shape == (tokens, H, K)
+    assert v.shape == (tokens, H, V) and beta.shape == (tokens, H)
+    assert cu[-1] == tokens
+    if s0 is not None:
+        assert s0.shape == (N, H, K, V)
+    o = np.zeros((tokens, H, V), dtype=np.float64)
+    sT = np.zeros((N, H, K, V), dtype=np.float64)
+    rc = _load().kda_oracle_recurrence(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(o), _ptr(sT),
+        cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), N, H, K, V,
+        int(nthreads or host_threads()))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_recurrence failed with code {rc}")
+    return o, sT
+
+
+def fixed(q, k, v, g, beta, s0=None, nthreads: int | None = None):
+    """Fixed-length batch [B, T, H, *]: the packed recurrence with cu = {0, T, .., B*T}.
+    Returns (o [B, T, H, V], sT [B, H, K, V])."""
+    q = as_f64(q)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    cu = np.arange(B + 1, dtype=np.int64) * T
+    o, sT = recurrence(q.reshape(B * T, H, K), as_f64(k).reshape(B * T, H, K),
+                       as_f64(v).reshape(B * T, H, V), as_f64(g).reshape(B * T, H, K),
+                       as_f64(beta).reshape(B * T, H), cu, s0, nthreads)
+    return o.reshape(B, T, H, V), sT
+
+
+def decode_step(q, k, v, g, beta, state, nthreads: int | None = None):
+    """One token per sequence: q, k, g [N, H, K]; v [N, H, V]; beta [N, H];
+    state [N, H, K, V] fp64.  Returns (o [N, H, V], new state)."""
+    q = as_f64(q)
+    N, H, K = q.shape
+    cu = np.arange(N + 1, dtype=np.int64)
+    return recurrence(q, k, v, g, beta, cu, state, nthreads)
