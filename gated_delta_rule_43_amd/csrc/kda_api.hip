@@ -1,0 +1,144 @@
+// kda_api.hip -- the C ABI of libkda.so (declared in include/kda.h).
+//
+// Host side only: argument validation (before any HIP call, so argument errors
+// never enqueue work), dispatch to the kernels by (K, V, chunk, dtype), and
+// mapping of HIP errors to kda_status_t.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "../../include/kda.h"
+
+namespace kda {
+hipError_t launch_decode(const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, float *state, void *o, int N, int H, int K, int V,
+                         bool in_bf16, bool out_bf16, hipStream_t stream);
+hipError_t launch_chunk_valu(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, const float *s0, void *o, float *sT,
+                             const int32_t *cu, int N, int fixedT, int totalT, int H, int K,
+                             int V, int C, bool in_bf16, bool out_bf16, hipStream_t stream);
+hipError_t launch_chunk_mfma(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, const float *s0, void *o, float *sT,
+                             const int32_t *cu, int N, int fixedT, int totalT, int H,
+                             bool out_bf16, hipStream_t stream);
+bool chunk_mfma_supported(int K, int V, int C);
+}  // namespace kda
+
+namespace {
+
+bool dtype_ok(kda_dtype_t d) { return d == KDA_F32 || d == KDA_BF16; }
+
+bool chunk_shape_supported(int K, int V, int C) {
+    return (K == 32 && V == 32 && C == 16) || (K == 128 && V == 128 && C == 64);
+}
+
+// Elements of a [rows, H, D] tensor must stay below 2^31 (kernels index
+// tiles with 32-bit arithmetic on top of 64-bit bases).
+bool fits(long long rows, long long H, long long D) {
+    return rows >= 0 && rows * H * D < (long long)INT_MAX;
+}
+
+kda_status_t from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+kda_status_t validate_fwd(const void *q, const void *k, const void *v, const void *g,
+                          const void *beta, const void *o, int N, int totalT, int H, int K,
+                          int V, int chunk, kda_dtype_t in_dtype, kda_dtype_t out_dtype) {
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
+    if (N < 0 || totalT < 0 || H <= 0 || K <= 0 || V <= 0 || chunk <= 0) return KDA_ERR_SHAPE;
+    if (!fits(totalT, H, K > V ? K : V) || !fits(N, H, (long long)K * V)) return KDA_ERR_SHAPE;
+    if (!chunk_shape_supported(K, V, chunk)) return KDA_ERR_UNSUPPORTED;
+    if (totalT > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+    return KDA_OK;
+}
+
+kda_status_t run_fwd(const void *q, const void *k, const void *v, const void *g,
+                     const void *beta, const float *s0, void *o, float *sT, const int32_t *cu,
+                     int N, int fixedT, int totalT, int H, int K, int V, int chunk,
+                     kda_dtype_t in_dtype, kda_dtype_t out_dtype, void *stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool in_bf16 = in_dtype == KDA_BF16, out_bf16 = out_dtype == KDA_BF16;
+    hipError_t e;
+    if (in_bf16 && kda::chunk_mfma_supported(K, V, chunk))
+        e = kda::launch_chunk_mfma(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H,
+                                   out_bf16, st);
+    else
+        e = kda::launch_chunk_valu(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H, K, V,
+                                   chunk, in_bf16, out_bf16, st);
+    return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return 100; }
+
+const char *kda_status_str(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: invalid or oversized dimensions";
+        case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: unknown dtype";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: (K, V, chunk) or dtype not supported";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace too small";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+size_t kda_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk) {
+    (void)N; (void)total_T; (void)H; (void)K; (void)V; (void)chunk;
+    return 0;
+}
+
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, const float *s0, void *o, float *sT, int B,
+                           int T, int H, int K, int V, int chunk, kda_dtype_t in_dtype,
+                           kda_dtype_t out_dtype, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    if (B < 0 || T < 0) return KDA_ERR_SHAPE;
+    const long long total = (long long)B * T;
+    if (total > INT_MAX) return KDA_ERR_SHAPE;
+    kda_status_t s = validate_fwd(q, k, v, g, beta, o, B, (int)total, H, K, V, chunk, in_dtype,
+                                  out_dtype);
+    if (s != KDA_OK) return s;
+    if (workspace_bytes < kda_workspace_bytes(B, (int)total, H, K, V, chunk)) return KDA_ERR_WORKSPACE;
+    (void)workspace;
+    if (B == 0) return KDA_OK;
+    if (T == 0 && !sT) return KDA_OK;
+    return run_fwd(q, k, v, g, beta, s0, o, sT, nullptr, B, T, (int)total, H, K, V, chunk,
+                   in_dtype, out_dtype, stream);
+}
+
+kda_status_t kda_varlen_fwd(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const float *s0, void *o, float *sT,
+                            const int32_t *cu_seqlens, int N, int total_T, int H, int K, int V,
+                            int chunk, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    kda_status_t s = validate_fwd(q, k, v, g, beta, o, N, total_T, H, K, V, chunk, in_dtype,
+                                  out_dtype);
+    if (s != KDA_OK) return s;
+    if (N > 0 && !cu_seqlens) return KDA_ERR_NULL;
+    if (workspace_bytes < kda_workspace_bytes(N, total_T, H, K, V, chunk)) return KDA_ERR_WORKSPACE;
+    (void)workspace;
+    if (N == 0) return KDA_OK;
+    return run_fwd(q, k, v, g, beta, s0, o, sT, cu_seqlens, N, 0, total_T, H, K, V, chunk,
+                   in_dtype, out_dtype, stream);
+}
+
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, float *state, void *o, int N, int H, int K,
+                             int V, kda_dtype_t in_dtype, kda_dtype_t out_dtype, void *stream) {
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
+    if (N < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_SHAPE;
+    if (!fits(N, H, (long long)K * V)) return KDA_ERR_SHAPE;
+    if (!((K == 128 && V == 128) || (K == 32 && V == 32))) return KDA_ERR_UNSUPPORTED;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
+    return from_hip(kda::launch_decode(q, k, v, g, beta, state, o, N, H, K, V,
+                                       in_dtype == KDA_BF16, out_dtype == KDA_BF16,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library, libkda.so.
+ *
+ * The operation.  "Kimi K3: Open Frontier Intelligence and Implementation
+ * Framework" (gemslabs.io), section "Hybrid Attention Mechanism", describes
+ * Kimi Delta Attention (KDA) as the delta-rule recurrence extended with a
+ * channel-wise forget gate, whose lower-bounded decay lets both the diagonal
+ * (intra-chunk) and off-diagonal (inter-chunk) tiles run as dense matrix
+ * products.  Per sequence and head, with S a K x V fp32 matrix whose rows are
+ * key channels:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t,            alpha_t = exp(g_t)
+ *
+ * The gate is passed as g = log(alpha), one value per (token, head, key
+ * channel); beta is one scalar per (token, head); no query scale is applied.
+ * Section "Inference Serving" of the same page keeps KDA recurrent states
+ * per sequence: the state S_T returned by a forward call is exactly the
+ * state to resume from (pass it back as s0), and the decode step updates a
+ * persistent state in place.
+ *
+ * Layouts (row-major, contiguous; "tokens" is B*T or total_T):
+ *   q, k, g : [tokens, H, K]        v, o : [tokens, H, V]     beta : [tokens, H]
+ *   s0, sT  : [N, H, K, V] fp32 (row index = key channel)
+ * q, k, v, g and beta all have in_dtype; o has out_dtype.
+ *
+ * Supported set: (K, V, chunk) = (32, 32, 16) or (128, 128, 64);
+ * in_dtype KDA_F32 or KDA_BF16; out_dtype KDA_F32 or KDA_BF16.  Anything
+ * else returns KDA_ERR_UNSUPPORTED before any GPU work.
+ *
+ * Numerical precondition (the lower-bounded decay): -g_lb <= g <= 0 with
+ * g_lb * chunk / 2 <= 8 (g_lb = 0.25 at chunk 64, 1.0 at chunk 16).  The
+ * bf16 chunked kernels factor the intra-chunk decay around the middle of the
+ * chunk and hold the factors in fp16; outside this bound results are
+ * unspecified (but every access stays in bounds).  The fp32-input kernels
+ * evaluate every decay factor exactly and accept any g <= 0.
+ *
+ * Ownership and ordering.  The caller allocates every buffer; the library
+ * allocates no device memory, keeps no state between calls and is
+ * thread-safe.  All pointers except the cu_seqlens host-side description
+ * below are device pointers.  Every call validates its arguments on the host,
+ * then enqueues its kernels on `stream` (a hipStream_t; NULL = the default
+ * stream) and returns without synchronising.  Results are ready when the
+ * stream is.
+ *
+ * Aliasing.  q, k, v, g, beta and o must not overlap each other or the
+ * states.  sT == s0 is allowed (in place); otherwise sT and s0 must not overlap.
+ *
+ * Errors.  Argument errors are detected before any launch: a nonzero status
+ * is returned and nothing is enqueued.  A failed launch returns KDA_ERR_HIP.
+ * Device-side precondition violations (non-monotone cu_seqlens, g outside
+ * the bound, non-finite inputs) give unspecified values but never
+ * out-of-bounds accesses: kernels clamp sequence bounds to [0, total_T].
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    KDA_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be,
+                                or the tensor would exceed 2^31 elements       */
+    KDA_ERR_DTYPE = 3,       /* unknown dtype enum                             */
+    KDA_ERR_UNSUPPORTED = 4, /* (K, V, chunk) or dtype combination not built   */
+    KDA_ERR_WORKSPACE = 5,   /* workspace smaller than kda_workspace_bytes()   */
+    KDA_ERR_HIP = 6          /* the HIP runtime reported an error              */
+} kda_status_t;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+
+/*
+ * Chunked forward pass over a fixed-length batch: B sequences of T tokens,
+ * tensors [B, T, H, *] (the same as the packed call with cu_seqlens =
+ * {0, T, 2T, .., B*T}).
+ *   s0 : [B, H, K, V] initial states, or NULL for zeros.
+ *   o  : [B, T, H, V] output, out_dtype.
+ *   sT : [B, H, K, V] final states, or NULL if not wanted.  May equal s0.
+ *   chunk : 16 or 64, as fixed by (K, V) above.
+ *   workspace : device scratch of at least kda_workspace_bytes(B, B*T, H, K, V,
+ *               chunk) bytes (NULL allowed when that is 0).
+ * T = 0 or B = 0 is allowed: sT receives s0 (or zeros) and o is untouched.
+ */
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, const float *s0, void *o, float *sT,
+                           int B, int T, int H, int K, int V, int chunk,
+                           kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Chunked forward pass over N packed sequences of different lengths.
+ *   cu_seqlens : DEVICE int32 [N + 1], cu[0] = 0, nondecreasing, cu[N] = total_T.
+ *                Sequence n holds tokens [cu[n], cu[n+1]); chunks restart at
+ *                every sequence start and the last chunk of each is partial.
+ *   s0, sT     : [N, H, K, V] as above; zero-length sequences get sT = s0.
+ */
+kda_status_t kda_varlen_fwd(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const float *s0, void *o, float *sT,
+                            const int32_t *cu_seqlens, int N, int total_T, int H, int K,
+                            int V, int chunk, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step: one new token for each of N sequences.
+ *   q, k, g : [N, H, K]; v : [N, H, V]; beta : [N, H]   (in_dtype)
+ *   state   : [N, H, K, V] fp32, read and updated in place (S_{t-1} -> S_t)
+ *   o       : [N, H, V] (out_dtype)
+ * Supported (K, V): (32, 32) and (128, 128).
+ */
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, float *state, void *o, int N, int H, int K,
+                             int V, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                             void *stream);
+
+/* Device scratch bytes the forward calls need for these sizes (0 if none). */
+size_t kda_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk);
+
+/* Static, human-readable name of a status code. */
+const char *kda_status_str(kda_status_t status);
+
+/* Library ABI version (major * 100 + minor). */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,100 @@
+"""The C-ABI library loads on the host, exports every declared symbol and
+rejects bad arguments before touching the GPU (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_43_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_43_amd import build
+        build.build()
+    return kda.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kda_chunk_fwd", "kda_varlen_fwd", "kda_decode_step", "kda_workspace_bytes",
+              "kda_status_str", "kda_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    for code in range(7):
+        s = lib.kda_status_str(code).decode()
+        assert s.startswith("KDA_")
+    assert lib.kda_status_str(99).decode() == "KDA_ERR_UNKNOWN"
+    assert lib.kda_version() == 100
+    assert lib.kda_workspace_bytes(4, 32768, 32, 128, 128, 64) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def chunk(lib, *, B=1, T=64, H=1, K=128, V=128, C=64, ind=1, outd=0, null=None, ws=0):
+    ptrs = [FAKE] * 8
+    if null is not None:
+        ptrs[null] = None
+    return lib.kda_chunk_fwd(*ptrs, B, T, H, K, V, C, ind, outd, None, ws, None)
+
+
+def test_chunk_argument_errors(lib):
+    assert chunk(lib, K=64, V=64) == 4                       # unsupported shape
+    assert chunk(lib, K=128, V=128, C=16) == 4
+    assert chunk(lib, K=32, V=32, C=64) == 4
+    assert chunk(lib, ind=7) == 3                            # unknown dtype
+    assert chunk(lib, outd=-1) == 3
+    assert chunk(lib, B=-1) == 2
+    assert chunk(lib, T=-5) == 2
+    assert chunk(lib, H=0) == 2
+    assert chunk(lib, T=1 << 22, H=64) == 2                   # > 2^31 elements
+    for i in (0, 1, 2, 3, 4, 6):                              # q, k, v, g, beta, o
+        assert chunk(lib, null=i) == 1
+
+
+def test_varlen_argument_errors(lib):
+    f = lib.kda_varlen_fwd
+    assert f(*[FAKE] * 8, None, 2, 10, 1, 128, 128, 64, 1, 0, None, 0, None) == 1  # no cu
+    assert f(*[FAKE] * 9, -1, 10, 1, 128, 128, 64, 1, 0, None, 0, None) == 2
+    assert f(*[FAKE] * 9, 2, -10, 1, 128, 128, 64, 1, 0, None, 0, None) == 2
+    assert f(*[FAKE] * 9, 2, 10, 1, 96, 128, 64, 1, 0, None, 0, None) == 4
+    assert f(*[FAKE] * 9, 2, 10, 1, 128, 128, 64, 5, 0, None, 0, None) == 3
+
+
+def test_decode_argument_errors(lib):
+    f = lib.kda_decode_step
+    assert f(*[FAKE] * 7, 4, 2, 64, 64, 1, 0, None) == 4
+    assert f(*[FAKE] * 7, -1, 2, 128, 128, 1, 0, None) == 2
+    assert f(*[FAKE] * 7, 4, 0, 128, 128, 1, 0, None) == 2
+    assert f(*[FAKE] * 7, 4, 2, 128, 128, 2, 0, None) == 3
+    for i in range(7):
+        ptrs = [FAKE] * 7
+        ptrs[i] = None
+        assert f(*ptrs, 4, 2, 128, 128, 1, 0, None) == 1
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 32)
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(x, x, x, x, torch.zeros(1, 4, 1))

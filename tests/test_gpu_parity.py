@@ -1,0 +1,167 @@
+"""GPU parity against the fp64 oracle at sizes the oracle finishes in seconds.
+
+Every case calls the HIP library through the C ABI (gated_delta_rule_43_amd.kda)
+and compares element by element with the sequential fp64 recurrence, to
+max|err| / RMS(ref) <= 1e-4 (fp32 inputs) or 2e-2 (bf16 inputs), on o and S_T.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_43_amd import inputs, kda
+from oracle import oracle
+from tests.parity import TOL, rel_err, report, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _fixed_case(name, seed, B, T, H, K, V, dtype, s0_std=None, g_lb=0.25, g_mode="default",
+                out_dtype=torch.float32, tol=None):
+    print(f"[case] {name} B={B} T={T} H={H} K={K} V={V} {dtype} g={g_mode}/{g_lb}", flush=True)
+    d = inputs.draw_fixed(seed, B, T, H, K, V, dtype, s0_std=s0_std, g_lb=g_lb, g_mode=g_mode)
+    o_ref, s_ref = oracle.fixed(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                oracle.as_f64(d["s0"]))
+    x = to_gpu(d)
+    o, sT = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], initial_state=x["s0"],
+                          out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+    report(name, o=eo, sT=es)
+    tol = tol or TOL[dtype]
+    assert eo <= tol and es <= tol
+    return eo, es
+
+
+def test_single_sequence_fp32_T64_d32():
+    # the fp32 workload at full size: B=1, H=1, T=64, d_k=d_v=32, chunk=16
+    w = inputs.WORKLOADS["single_f32_T64_d32"]
+    _fixed_case(w.name, w.seed, w.B, w.T, w.H, w.K, w.V, "f32")
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 100])
+def test_fp32_d32_ragged_lengths(T):
+    _fixed_case(f"f32_d32_T{T}", 100 + T, 2, T, 3, 32, 32, "f32", s0_std=0.1)
+
+
+def test_fp32_d32_no_decay_and_steep_decay():
+    _fixed_case("f32_d32_g0", 7, 1, 200, 2, 32, 32, "f32", s0_std=0.1, g_mode="zero")
+    _fixed_case("f32_d32_g2", 8, 1, 200, 2, 32, 32, "f32", s0_std=0.1, g_lb=2.0, g_mode="uniform")
+
+
+def test_fp32_d128():
+    _fixed_case("f32_d128", 9, 1, 150, 2, 128, 128, "f32", s0_std=0.1)
+
+
+def test_bf16_d32():
+    _fixed_case("bf16_d32", 10, 2, 77, 2, 32, 32, "bf16", s0_std=0.1)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 300])
+def test_bf16_d128_ragged_lengths(T):
+    _fixed_case(f"bf16_d128_T{T}", 200 + T, 2, T, 2, 128, 128, "bf16", s0_std=0.1)
+
+
+@pytest.mark.parametrize("g_mode,g_lb", [("zero", 0.25), ("bound", 0.25), ("uniform", 0.25)])
+def test_bf16_d128_decay_stress(g_mode, g_lb):
+    # no decay keeps every chunk's contribution alive, so an inter-chunk state
+    # bug cannot hide behind attenuation; "bound" sits every step on -g_lb
+    _fixed_case(f"bf16_d128_{g_mode}", 300, 1, 700, 3, 128, 128, "bf16", s0_std=0.1,
+                g_lb=g_lb, g_mode=g_mode)
+
+
+def test_bf16_output_dtype():
+    _fixed_case("bf16_out", 11, 1, 256, 2, 128, 128, "bf16", s0_std=0.1,
+                out_dtype=torch.bfloat16, tol=3e-2)
+
+
+def test_state_in_place_and_resume():
+    """sT may alias s0; two half-runs chained through the state equal one run."""
+    d = inputs.draw_fixed(12, 1, 256, 2, 128, 128, "bf16", s0_std=0.1)
+    x = to_gpu(d)
+    o_full, s_full = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"])
+    st = x["s0"].clone()
+    parts = []
+    for a, b in ((0, 100), (100, 256)):
+        sl = {k: x[k][:, a:b].contiguous() for k in ("q", "k", "v", "g", "beta")}
+        o, _ = kda.chunk_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], st, final_state=st)
+        parts.append(o)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.fixed(d["q"], d["k"], d["v"], d["g"], d["beta"], oracle.as_f64(d["s0"]))
+    assert rel_err(torch.cat(parts, 1), o_ref) <= TOL["bf16"]
+    assert rel_err(st, s_ref) <= TOL["bf16"]
+    assert rel_err(o_full, o_ref) <= TOL["bf16"]
+
+
+def test_zero_length_batch_returns_initial_state():
+    d = to_gpu(inputs.draw_fixed(13, 2, 0, 2, 128, 128, "bf16", s0_std=0.1))
+    o, sT = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(sT, d["s0"])
+
+
+@pytest.mark.parametrize("dtype,K", [("bf16", 128), ("f32", 32), ("bf16", 32)])
+def test_varlen_edge_lengths(dtype, K):
+    C = 16 if K == 32 else 64
+    lengths = [C + 1, 0, 1, C - 1, C, 3 * C + 5, 0, 2]
+    print(f"[case] varlen {dtype} K={K} lengths={lengths}", flush=True)
+    d = inputs.draw_varlen(14, H=3, K=K, V=K, dtype=dtype, lengths=lengths, s0_std=0.1)
+    o_ref, s_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                     d["cu_seqlens"].numpy(), oracle.as_f64(d["s0"]))
+    x = to_gpu(d)
+    o, sT = kda.varlen_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"], x["s0"])
+    torch.cuda.synchronize()
+    eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+    report(f"varlen_{dtype}_K{K}", o=eo, sT=es)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    # zero-length sequences return their initial state bit for bit
+    assert torch.equal(sT[1], x["s0"][1]) and torch.equal(sT[6], x["s0"][6])
+
+
+def test_output_fully_written_and_deterministic():
+    """Outputs poisoned with NaN beforehand must be fully overwritten, and two runs
+    must agree bit for bit (no atomics, no races)."""
+    d = to_gpu(inputs.draw_fixed(15, 2, 333, 4, 128, 128, "bf16", s0_std=0.1))
+    outs = []
+    for _ in range(2):
+        o = torch.full((2, 333, 4, 128), float("nan"), device="cuda")
+        s = torch.full((2, 4, 128, 128), float("nan"), device="cuda")
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], final_state=s, out=o)
+        torch.cuda.synchronize()
+        assert torch.isfinite(s).all() and torch.isfinite(o).all()
+        outs.append((o, s))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("K", [128, 32])
+def test_decode_steps_small(K):
+    N, H, steps = 5, 3, 12
+    state0 = inputs.draw_decode_state(40, N, H, K, K, 0.1)
+    st = state0.cuda()
+    ref = oracle.as_f64(state0)
+    worst = 0.0
+    for s in range(steps):
+        d = inputs.draw_decode_step(40, s, N, H, K, K, "bf16")
+        x = to_gpu(d)
+        o = kda.decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], st)
+        o_ref, ref = oracle.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], ref)
+        torch.cuda.synchronize()
+        worst = max(worst, rel_err(o, o_ref))
+    es = rel_err(st, ref)
+    report(f"decode_K{K}", o=worst, state=es)
+    assert worst <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_decode_fp32_inputs_tight():
+    N, H, K = 3, 2, 128
+    state0 = inputs.draw_decode_state(41, N, H, K, K, 0.1)
+    st = state0.cuda()
+    ref = oracle.as_f64(state0)
+    for s in range(5):
+        d = inputs.draw_decode_step(41, s, N, H, K, K, "f32")
+        x = to_gpu(d)
+        o = kda.decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], st)
+        o_ref, ref = oracle.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], ref)
+        torch.cuda.synchronize()
+        assert rel_err(o, o_ref) <= TOL["f32"]
+    assert rel_err(st, ref) <= TOL["f32"]
