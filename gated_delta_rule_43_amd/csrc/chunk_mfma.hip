@@ -1,14 +1,507 @@
-// chunk_mfma.hip -- bf16-input chunked KDA forward on the matrix cores (gfx950).
+// chunk_mfma.hip -- bf16-input chunked KDA forward on the gfx950 matrix cores.
+//
+// "Kimi K3: Open Frontier Intelligence and Implementation Framework", section
+// "Hybrid Attention Mechanism": KDA is the delta rule with a channel-wise
+// forget gate, and its lower-bounded decay lets both the diagonal
+// (intra-chunk) and off-diagonal (inter-chunk) tiles run as dense matrix
+// products.  This kernel is that chunked forward pass for K = V = 128 and
+// chunk C = 64, written for CDNA4:
+//
+//  * one workgroup (8 wavefronts) owns one (sequence, head, 64-column V tile);
+//    the 128 x 64 fp32 state tile lives in MFMA accumulator registers for the
+//    whole sequence (wave w holds key rows 16w..16w+15);
+//  * per chunk, q/k/g/v/beta are fetched with 16-byte loads one chunk ahead,
+//    the log-decay is summed along the chunk with a wave scan, and the
+//    decay-factored operands go to LDS as fp16;
+//  * the dense contractions use v_mfma_f32_16x16x32_f16 (fp16 operands, fp32
+//    accumulation); the unit-lower triangular solve runs in fp32 (VALU for the
+//    16 x 16 diagonal blocks, v_mfma_f32_16x16x4_f32 for the merges).
+//
+// Algebra for one chunk (rows r, s = tokens; G = running sum of g inside the
+// chunk; m = 31 the reference row; all exponentials per key channel):
+//   Kp = K * exp(G - G_m),  Km = K * exp(G_m - G),  Qp = Q * exp(G - G_m)
+//   A  = Diag(beta) strict_lower(Kp Km^T),   T = (I + A)^-1,   Tb = T Diag(beta)
+//   P  = lower(Qp Km^T)
+//   S' = Diag(exp(G_m)) S
+//   U  = Tb (V - Kp S'),   O = Qp S' + P U
+//   S  <- Diag(exp(G_C - G_m)) (S' + Km^T U)
+// Kp Km^T and Qp Km^T carry exp(G_r - G_s) <= 1 for s <= r.  With
+// -g_lb <= g <= 0 and g_lb * C / 2 <= 8 every factor stays inside fp16 range
+// (<= e^8); this is where the lower bound on the decay is used.
 #include "kda_common.hpp"
 
 namespace kda {
+namespace {
 
-bool chunk_mfma_supported(int K, int V, int C) { (void)K; (void)V; (void)C; return false; }
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-hipError_t launch_chunk_mfma(const void *, const void *, const void *, const void *,
-                             const void *, const float *, void *, float *, const int32_t *,
-                             int, int, int, int, bool, hipStream_t) {
-    return hipErrorInvalidValue;
+constexpr int C = 64;    // chunk length
+constexpr int KD = 128;  // key dimension
+constexpr int VD = 128;  // value dimension
+constexpr int VT = 64;   // value columns per workgroup
+constexpr int NT = 512;  // threads per workgroup
+constexpr int NW = NT / 64;
+constexpr int PK = 136;  // LDS pitch (halves) of [64][128] fp16 tiles
+constexpr int PC = 72;   // LDS pitch (halves) of [64][64] fp16 tiles
+constexpr int PA = 68;   // LDS pitch (floats) of [64][64] fp32 tiles
+
+struct Smem {
+    _Float16 kp[C * PK];   // Kp [s][c]
+    _Float16 km[C * PK];   // Km [s][c]
+    _Float16 qp[C * PK];   // Qp [s][c]
+    _Float16 st[VT * PK];  // S'^T [j][c]
+    float a[C * PA];       // A [r][s] (fp32); upper blocks used as scratch
+    float t[C * PA];       // T [r][s] (fp32, lower blocks)
+    _Float16 tb[C * PC];   // T Diag(beta) [r][s]
+    _Float16 p[C * PC];    // P [r][s]
+    _Float16 yt[VT * PC];  // (V - Kp S')^T [j][r]
+    _Float16 ut[VT * PC];  // U^T [j][r]
+    uint16_t v[C * PC];    // bf16 V tile [r][j]
+    float scan[NW * KD];   // per-wave channel sums of g, then exclusive prefixes
+    float gref[KD];        // G_m per channel (reference row m = 31)
+    float fm[KD];          // exp(G_m)
+    float fc[KD];          // exp(G_C - G_m)
+    float beta[C];
+};
+
+__device__ __forceinline__ floatx4 mma16(half8 a, half8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ floatx4 mma16_f32(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Operand fragment of rows row0..row0+15, k = k0..k0+31 from a row-major
+// [rows][k] fp16 tile: lane holds row (lane & 15), k = k0 + 8 (lane >> 4) .. +7.
+__device__ __forceinline__ half8 frag(const _Float16 *base, int pitch, int row0, int k0,
+                                      int lane) {
+    return *reinterpret_cast<const half8 *>(base + (row0 + (lane & 15)) * pitch + k0 +
+                                            8 * (lane >> 4));
+}
+// The same fragment taken from a tile stored transposed ([k][rows]).
+__device__ __forceinline__ half8 frag_t(const _Float16 *base, int pitch, int row0, int k0,
+                                        int lane) {
+    const _Float16 *q = base + (k0 + 8 * (lane >> 4)) * pitch + row0 + (lane & 15);
+    half8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = q[e * pitch];
+    return r;
+}
+
+// D = X Y (+ acc) for 16 x 16 fp32 blocks X, Y held in LDS with pitch PA.
+__device__ __forceinline__ floatx4 mm16_f32(const float *X, const float *Y, int lane,
+                                            floatx4 acc) {
+#pragma unroll
+    for (int k0 = 0; k0 < 16; k0 += 4)
+        acc = mma16_f32(X[(lane & 15) * PA + k0 + (lane >> 4)],
+                        Y[(k0 + (lane >> 4)) * PA + (lane & 15)], acc);
+    return acc;
+}
+// Store an accumulator block (times scale) to a 16 x 16 fp32 block with pitch PA.
+__device__ __forceinline__ void st16_f32(float *Z, floatx4 d, int lane, float scale) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Z[(4 * (lane >> 4) + i) * PA + (lane & 15)] = scale * d[i];
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ void unpack8(const uint4 &u, float *x) {
+    x[0] = bf16lo(u.x); x[1] = bf16hi(u.x); x[2] = bf16lo(u.y); x[3] = bf16hi(u.y);
+    x[4] = bf16lo(u.z); x[5] = bf16hi(u.z); x[6] = bf16lo(u.w); x[7] = bf16hi(u.w);
+}
+
+// Chunk inputs held in registers while the previous chunk computes.
+struct Raw {
+    uint4 q[2], k[2], g[2];  // tokens 2*tg and 2*tg+1, channels 8*cg..8*cg+7
+    uint4 v;                 // V tile row t>>3, columns 8*(t&7)..+7
+    uint32_t beta;           // threads 0..63: beta of token t
+};
+
+__device__ __forceinline__ void load_raw(Raw &R, const uint16_t *q, const uint16_t *k,
+                                         const uint16_t *g, const uint16_t *v,
+                                         const uint16_t *beta, int c0, int L, int H, int h,
+                                         int vt, int t) {
+    const int cg = t & 15, tg = t >> 4;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int r = 2 * tg + e;
+        R.q[e] = make_uint4(0u, 0u, 0u, 0u);
+        R.k[e] = R.q[e];
+        R.g[e] = R.q[e];
+        if (r < L) {
+            const size_t off = ((size_t)(c0 + r) * H + h) * KD + 8 * cg;
+            R.q[e] = *reinterpret_cast<const uint4 *>(q + off);
+            R.k[e] = *reinterpret_cast<const uint4 *>(k + off);
+            R.g[e] = *reinterpret_cast<const uint4 *>(g + off);
+        }
+    }
+    R.v = make_uint4(0u, 0u, 0u, 0u);
+    if ((t >> 3) < L)
+        R.v = *reinterpret_cast<const uint4 *>(v + ((size_t)(c0 + (t >> 3)) * H + h) * VD +
+                                               vt * VT + 8 * (t & 7));
+    R.beta = (t < C && t < L) ? beta[(size_t)(c0 + t) * H + h] : 0u;
+}
+
+template <typename TOut>
+__global__ __launch_bounds__(NT) void chunk_mfma_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, const uint16_t *__restrict__ g,
+    const uint16_t *__restrict__ beta, const float *s0, TOut *__restrict__ o, float *sT,
+    const int32_t *__restrict__ cu, int fixedT, int N, int H, int totalT) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+
+    // Both V tiles of a head land on the same XCD (workgroups are dealt to the
+    // 8 XCDs round-robin), so their shared q/k/g reads meet in one L2.
+    const int b = blockIdx.x;  // wave-uniform quantities below are kept in SGPRs
+    const int xcd = b & 7, slot = b >> 3;
+    const int vt = slot & 1;
+    const int unit = (slot >> 1) * 8 + xcd;
+    if (unit >= N * H) return;
+    const int n = unit / H, h = unit % H;
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    int bos, eos;
+    seq_bounds(cu, n, fixedT, totalT, bos, eos);
+
+    // State tile: wave w owns key rows c = 16w + 4*lg + i and columns
+    // j = 16*jb + l16 of this V tile.
+    const size_t sbase = (size_t)unit * (KD * VD) + (size_t)vt * VT;
+    floatx4 S[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 16 * w + 4 * lg + i, j = 16 * jb + l16;
+            S[jb][i] = s0 ? s0[sbase + (size_t)c * VD + j] : 0.f;
+        }
+
+    // Output blocks of this wave: rows 16*rb.., columns 16*(2*jp + e)..
+    const int rb = w >> 1, jp = w & 1;
+    const int cg = t & 15, tg = t >> 4;
+
+    Raw R;
+    if (bos < eos) load_raw(R, q, k, g, v, beta, bos, min(C, eos - bos), H, h, vt, t);
+
+    for (int c0 = bos; c0 < eos; c0 += C) {
+        const int L = min(C, eos - c0);
+
+        // ---- prologue: running log-decay and the decay-factored operands
+        // Thread (cg, tg) holds channels 8cg..8cg+7 of tokens 2tg, 2tg+1.
+        float g0[8], g1[8], ex[8];
+        unpack8(R.g[0], g0);
+        unpack8(R.g[1], g1);
+        *reinterpret_cast<uint4 *>(&sm.v[(t >> 3) * PC + 8 * (t & 7)]) = R.v;
+        if (t < C) sm.beta[t] = __uint_as_float(R.beta << 16);
+        // inclusive scan over the wave's four token pairs (lanes 16 apart
+        // share channels); ex = exclusive prefix inside the wave
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float loc = g0[c] + g1[c];
+            float s = loc;
+            float u = __shfl_up(s, 16);
+            if (lg >= 1) s += u;
+            u = __shfl_up(s, 32);
+            if (lg >= 2) s += u;
+            ex[c] = s - loc;
+            if (lg == 3) sm.scan[w * KD + 8 * cg + c] = s;
+        }
+        __syncthreads();  // B1: per-wave sums visible
+        if (t < KD) {
+            // exclusive prefixes over the 8 waves, G_m = G at token 31 (end of
+            // wave 3's tokens) and G_C = G at the last token
+            float run = 0.f, gm = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                const float x = sm.scan[ww * KD + t];
+                sm.scan[ww * KD + t] = run;
+                run += x;
+                if (ww == 3) gm = run;
+            }
+            sm.gref[t] = gm;
+            sm.fm[t] = fast_exp(gm);
+            sm.fc[t] = fast_exp(run - gm);
+        }
+        __syncthreads();  // B1b: prefixes and per-channel factors visible
+
+        // S' = Diag(exp(G_m)) S, written transposed as the fp16 B operand.
+        float fc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 16 * w + 4 * lg + i;
+            const float fm = sm.fm[c];
+            fc[i] = sm.fc[c];
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) S[jb][i] *= fm;
+        }
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            half4 hv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hv[i] = (_Float16)S[jb][i];
+            *reinterpret_cast<half4 *>(&sm.st[(16 * jb + l16) * PK + 16 * w + 4 * lg]) = hv;
+        }
+        // Running sums for this thread's two tokens and the factored operands.
+        {
+            half8 hkp0, hkm0, hqp0, hkp1, hkm1, hqp1;
+            float k0[8], k1[8], q0[8], q1[8];
+            unpack8(R.k[0], k0);
+            unpack8(R.k[1], k1);
+            unpack8(R.q[0], q0);
+            unpack8(R.q[1], q1);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int ch = 8 * cg + c;
+                const float pre = sm.scan[w * KD + ch] + ex[c] - sm.gref[ch];
+                const float G0 = pre + g0[c], G1 = G0 + g1[c];  // G - G_m
+                const float f0 = fast_exp(G0), f1 = fast_exp(G1);
+                const float i0 = __builtin_amdgcn_rcpf(f0), i1 = __builtin_amdgcn_rcpf(f1);
+                hkp0[c] = (_Float16)(k0[c] * f0);
+                hkm0[c] = (_Float16)(k0[c] * i0);
+                hqp0[c] = (_Float16)(q0[c] * f0);
+                hkp1[c] = (_Float16)(k1[c] * f1);
+                hkm1[c] = (_Float16)(k1[c] * i1);
+                hqp1[c] = (_Float16)(q1[c] * f1);
+            }
+            const int r = 2 * tg;
+            *reinterpret_cast<half8 *>(&sm.kp[r * PK + 8 * cg]) = hkp0;
+            *reinterpret_cast<half8 *>(&sm.km[r * PK + 8 * cg]) = hkm0;
+            *reinterpret_cast<half8 *>(&sm.qp[r * PK + 8 * cg]) = hqp0;
+            *reinterpret_cast<half8 *>(&sm.kp[(r + 1) * PK + 8 * cg]) = hkp1;
+            *reinterpret_cast<half8 *>(&sm.km[(r + 1) * PK + 8 * cg]) = hkm1;
+            *reinterpret_cast<half8 *>(&sm.qp[(r + 1) * PK + 8 * cg]) = hqp1;
+        }
+        __syncthreads();  // B2: operands, S'^T, V tile and beta in LDS
+        // Fetch the next chunk now; it lands while this chunk computes.
+        if (c0 + C < eos) load_raw(R, q, k, g, v, beta, c0 + C, min(C, eos - c0 - C), H, h, vt, t);
+
+        // ---- intra-chunk Gram and query-key blocks (10 lower 16x16 blocks each)
+        for (int task = w; task < 20; task += NW) {
+            const bool gram = task < 10;
+            int bi = task % 10, i = 0;
+            while (bi > i) { bi -= i + 1; ++i; }
+            const int j = bi;  // block (i, j), j <= i
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            const _Float16 *lhs = gram ? sm.kp : sm.qp;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                acc = mma16(frag(lhs, PK, 16 * i, 32 * ks, lane), frag(sm.km, PK, 16 * j, 32 * ks, lane), acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * i + 4 * lg + e, s = 16 * j + l16;
+                if (gram)
+                    sm.a[r * PA + s] = s < r ? sm.beta[r] * acc[e] : 0.f;
+                else
+                    sm.p[r * PC + s] = (_Float16)(s <= r ? acc[e] : 0.f);
+            }
+        }
+        // zero the two upper P blocks that the P U products read
+        if (w == NW - 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lg + e;
+                sm.p[r * PC + 16 + l16] = (_Float16)0.f;
+                sm.p[(32 + r) * PC + 48 + l16] = (_Float16)0.f;
+            }
+        }
+
+        // ---- X = Kp S' and Qp S' (the off-diagonal, state-dependent tiles)
+        floatx4 X[2], O[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            X[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+            O[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const half8 ak = frag(sm.kp, PK, 16 * rb, 32 * ks, lane);
+            const half8 aq = frag(sm.qp, PK, 16 * rb, 32 * ks, lane);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const half8 bs = frag(sm.st, PK, 16 * (2 * jp + e), 32 * ks, lane);
+                X[e] = mma16(ak, bs, X[e]);
+                O[e] = mma16(aq, bs, O[e]);
+            }
+        }
+        // Y = V - X, stored transposed as the B operand of Tb Y
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int j = 16 * (2 * jp + e) + l16;
+            half4 hv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * rb + 4 * lg + i;
+                const float vv = __uint_as_float((uint32_t)sm.v[r * PC + j] << 16);
+                hv[i] = (_Float16)(vv - X[e][i]);
+            }
+            *reinterpret_cast<half4 *>(&sm.yt[j * PC + 16 * rb + 4 * lg]) = hv;
+        }
+        __syncthreads();  // B3: A, P, Y^T ready
+
+        // ---- T = (I + A)^-1: 16 x 16 diagonal blocks by forward substitution
+        if (w == 0) {
+            const int blk = lg, j = l16;
+            const float *Ab = sm.a + (16 * blk) * PA + 16 * blk;
+            float tc[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == j) ? 1.f : 0.f;
+#pragma unroll
+                for (int s = 0; s < r; ++s) acc -= Ab[r * PA + s] * tc[s];
+                tc[r] = acc;
+            }
+            float *Tb = sm.t + (16 * blk) * PA + 16 * blk;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Tb[r * PA + j] = tc[r];
+        }
+        __syncthreads();
+        // level 1: T_{i,i-1} = -T_ii (A_{i,i-1} T_{i-1,i-1}), i = 1..3
+        if (w < 3) {
+            const int i = w + 1, j = w;
+            float *scr = sm.a + (16 * j) * PA + 16 * i;  // upper block (j, i) as scratch
+            floatx4 m = mm16_f32(sm.a + (16 * i) * PA + 16 * j, sm.t + (16 * j) * PA + 16 * j,
+                                 lane, floatx4{0.f, 0.f, 0.f, 0.f});
+            st16_f32(scr, m, lane, 1.f);
+        }
+        __syncthreads();
+        if (w < 3) {
+            const int i = w + 1, j = w;
+            const float *scr = sm.a + (16 * j) * PA + 16 * i;
+            floatx4 r = mm16_f32(sm.t + (16 * i) * PA + 16 * i, scr, lane, floatx4{0.f, 0.f, 0.f, 0.f});
+            st16_f32(sm.t + (16 * i) * PA + 16 * j, r, lane, -1.f);
+        }
+        __syncthreads();
+        // level 2: T_20 = -T_22 (A_20 T_00 + A_21 T_10), T_31 = -T_33 (A_31 T_11 + A_32 T_21)
+        if (w < 2) {
+            const int i = w + 2, j = w;
+            float *scr = sm.a + (16 * j) * PA + 16 * i;
+            floatx4 m = mm16_f32(sm.a + (16 * i) * PA + 16 * j, sm.t + (16 * j) * PA + 16 * j,
+                                 lane, floatx4{0.f, 0.f, 0.f, 0.f});
+            m = mm16_f32(sm.a + (16 * i) * PA + 16 * (j + 1), sm.t + (16 * (j + 1)) * PA + 16 * j,
+                         lane, m);
+            st16_f32(scr, m, lane, 1.f);
+        }
+        __syncthreads();
+        if (w < 2) {
+            const int i = w + 2, j = w;
+            const float *scr = sm.a + (16 * j) * PA + 16 * i;
+            floatx4 r = mm16_f32(sm.t + (16 * i) * PA + 16 * i, scr, lane, floatx4{0.f, 0.f, 0.f, 0.f});
+            st16_f32(sm.t + (16 * i) * PA + 16 * j, r, lane, -1.f);
+        }
+        __syncthreads();
+        // level 3: T_30 = -T_33 (A_30 T_00 + A_31 T_10 + A_32 T_20)
+        if (w == 0) {
+            float *scr = sm.a + 48;  // upper block (0, 3)
+            floatx4 m = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int l = 0; l < 3; ++l)
+                m = mm16_f32(sm.a + 48 * PA + 16 * l, sm.t + (16 * l) * PA, lane, m);
+            st16_f32(scr, m, lane, 1.f);
+        }
+        __syncthreads();
+        if (w == 0) {
+            floatx4 r = mm16_f32(sm.t + 48 * PA + 48, sm.a + 48, lane, floatx4{0.f, 0.f, 0.f, 0.f});
+            st16_f32(sm.t + 48 * PA, r, lane, -1.f);
+        }
+        __syncthreads();
+        // Tb = T Diag(beta) in fp16 (zero above the diagonal)
+        for (int idx = t; idx < C * C; idx += NT) {
+            const int r = idx >> 6, s = idx & 63;
+            sm.tb[r * PC + s] = (_Float16)(s <= r ? sm.t[r * PA + s] * sm.beta[s] : 0.f);
+        }
+        __syncthreads();  // B4: Tb ready
+
+        // ---- U = Tb Y (lower-triangular Tb: k range grows with the row block)
+        const int nks = rb < 2 ? 1 : 2;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int jb = 2 * jp + e;
+            floatx4 u = {0.f, 0.f, 0.f, 0.f};
+            for (int ks = 0; ks < nks; ++ks)
+                u = mma16(frag(sm.tb, PC, 16 * rb, 32 * ks, lane), frag(sm.yt, PC, 16 * jb, 32 * ks, lane), u);
+            half4 hv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hv[i] = (_Float16)u[i];
+            *reinterpret_cast<half4 *>(&sm.ut[(16 * jb + l16) * PC + 16 * rb + 4 * lg]) = hv;
+        }
+        __syncthreads();  // B5: U^T ready
+
+        // ---- O = Qp S' + P U, stored for the valid rows
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int jb = 2 * jp + e;
+            for (int ks = 0; ks < nks; ++ks)
+                O[e] = mma16(frag(sm.p, PC, 16 * rb, 32 * ks, lane), frag(sm.ut, PC, 16 * jb, 32 * ks, lane), O[e]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * rb + 4 * lg + i;
+                if (r < L)
+                    o[((size_t)(c0 + r) * H + h) * VD + vt * VT + 16 * jb + l16] = from_f32<TOut>(O[e][i]);
+            }
+        }
+        // ---- state advance: S = Diag(exp(G_C - G_m)) (S' + Km^T U)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const half8 a = frag_t(sm.km, PK, 16 * w, 32 * ks, lane);
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+                S[jb] = mma16(a, frag(sm.ut, PC, 16 * jb, 32 * ks, lane), S[jb]);
+        }
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[jb][i] *= fc[i];
+        // No barrier needed here: everything the next prologue writes before
+        // its first barrier (V tile, beta, per-wave sums) was last read before B4.
+    }
+
+    if (sT) {
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 16 * w + 4 * lg + i, j = 16 * jb + l16;
+                sT[sbase + (size_t)c * VD + j] = S[jb][i];
+            }
+    }
+}
+
+template <typename TOut>
+hipError_t launch_t(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                    const float *s0, void *o, float *sT, const int32_t *cu, int N, int fixedT,
+                    int totalT, int H, hipStream_t stream) {
+    auto kern = chunk_mfma_kernel<TOut>;
+    const size_t smem = sizeof(Smem);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    const int units = N * H;
+    const int grid = ((units + 7) / 8) * 16;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), smem, stream,
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                       static_cast<const uint16_t *>(v), static_cast<const uint16_t *>(g),
+                       static_cast<const uint16_t *>(beta), s0, static_cast<TOut *>(o), sT, cu,
+                       fixedT, N, H, totalT);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool chunk_mfma_supported(int K, int V, int Cc) { return K == KD && V == VD && Cc == C; }
+
+hipError_t launch_chunk_mfma(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, const float *s0, void *o, float *sT,
+                             const int32_t *cu, int N, int fixedT, int totalT, int H,
+                             bool out_bf16, hipStream_t stream) {
+    if (N == 0 || H == 0) return hipSuccess;
+    return out_bf16 ? launch_t<bf16_t>(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H, stream)
+                    : launch_t<float>(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H, stream);
+}
+
+size_t chunk_mfma_smem_bytes() { return sizeof(Smem); }
 
 }  // namespace kda
