@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""KDA forward throughput on one MI355X: chunked prefill and recurrent decode.
+
+One JSON line on stdout.  A step is one chunked forward pass (kda_chunk_fwd)
+over the prefill workload B=1, H=8, T=4096, d_k=d_v=128, chunk 64, bf16
+inputs with fp32 state, accumulation and output; `value` is its tokens/s.
+The decode leg (one token for each of 256 sequences x 32 heads, persistent
+fp32 state, kda_decode_step) is reported in the same line under "decode".
+
+Inputs are synthetic and already resident in HBM when the timed region starts.
+The roofline objects price each kernel's ALGORITHMIC bytes (and flops) per
+launch against MI355X peaks (HBM 8 TB/s; dense fp16/bf16 MFMA 2.5 PFLOP/s);
+kernel time comes from HIP events on the stream the kernels run on.
+The cpu_baseline leg times the fp64 oracle on the host cores.
+"""
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+PREFILL = "prefill_bf16_B1_H8_T4096"
+DECODE = "decode_bf16_N256_H32"
+
+
+def prefill_alg_bytes(B, T, H, K, V, in_bytes=2, out_bytes=4, s0=False, sT=True):
+    """q, k, g [B,T,H,K], v [B,T,H,V], beta [B,T,H] read; o [B,T,H,V] written;
+    S_0 read and S_T written at K*V*4 bytes per (sequence, head)."""
+    th = B * T * H
+    b = th * ((3 * K + V) * in_bytes + in_bytes + V * out_bytes)
+    b += B * H * K * V * 4 * (int(s0) + int(sT))
+    return b
+
+
+def prefill_alg_flops(B, T, H, K, V, C):
+    """Algorithmic flops of the chunked form per token-head: C(C-1)K (strictly
+    lower Gram), 2C(C+1)(K+V) over the chunk for the triangular intra-chunk
+    products, C^3/3 for the triangular solve, all divided by C; plus 6KV for
+    the three state contractions (K S, Q S, K^T U)."""
+    per_chunk = C * (C - 1) * K + 2 * C * (C + 1) * (K + V) + C ** 3 / 3.0
+    return B * T * H * (per_chunk / C + 6 * K * V)
+
+
+def decode_alg_bytes(N, H, K, V, in_bytes=2, out_bytes=4):
+    """State read + written (2 K V 4), q, k, g, v, beta read, o written."""
+    return N * H * (2 * K * V * 4 + (3 * K + V + 1) * in_bytes + V * out_bytes)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_43_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, launches_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/<kernel>_traffic.md), or None when that summary was taken on a
+    different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source hash:\s*`?([0-9a-f]+)`?", text)
+    b = re.search(r"HBM bytes per launch:\s*([0-9.eE+]+)", text)
+    if not m or not b or m.group(1) != kernel_source_hash():
+        return None
+    return float(b.group(1))
+
+
+def time_launches(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def cpu_baseline(d, w, wall_budget_s=2.5):
+    """fp64 oracle over the whole prefill workload (all heads), repeated until
+    about wall_budget_s of wall time (at most 20 passes); input conversion is
+    outside the timing."""
+    from oracle import oracle
+    q, k, v, g, beta = (oracle.as_f64(d[x]) for x in ("q", "k", "v", "g", "beta"))
+    threads = oracle.host_threads()
+    used = min(threads, w.B * w.H)
+    times = []
+    while len(times) < 20 and sum(times) < wall_budget_s:
+        t0 = time.perf_counter()
+        oracle.fixed(q, k, v, g, beta, nthreads=used)
+        times.append(time.perf_counter() - t0)
+    dt = sum(times) / len(times)
+    return {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"whole prefill workload B={w.B} H={w.H} T={w.T} ({len(times)} passes, "
+                      f"mean {dt:.3f} s wall each, ~{sum(times) * used:.0f} core-s in total), "
+                      f"parallel over the {w.B * w.H} (sequence, head) units; "
+                      f"{threads} host threads available"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the KDA path here runs on a single MI355X and "
+              f"--gpus {args.gpus} is not supported (each (sequence, head) unit is "
+              f"independent, so N GPUs would each run this same kernel on 1/N of the units).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_43_amd import inputs, kda
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_43_amd import build
+        build.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- prefill: the step
+    w = inputs.WORKLOADS[PREFILL]
+    d = inputs.draw_fixed(w.seed, w.B, w.T, w.H, w.K, w.V, w.dtype)
+    x = {key: (val.to(dev) if val is not None else None) for key, val in d.items()}
+    o = torch.empty(w.B, w.T, w.H, w.V, device=dev)
+    sT = torch.empty(w.B, w.H, w.K, w.V, device=dev)
+
+    def step():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], None, chunk=w.chunk,
+                      final_state=sT, out=o)
+
+    ms, wall = time_launches(step, args.steps, args.warmup, stream)
+    tokens = w.B * w.T
+    alg_b = prefill_alg_bytes(w.B, w.T, w.H, w.K, w.V, s0=False, sT=True)
+    alg_f = prefill_alg_flops(w.B, w.T, w.H, w.K, w.V, w.chunk)
+    achieved = alg_b / (ms * 1e-3) / 1e9
+    traffic = measured_traffic("chunk_mfma_kernel", alg_b)
+    result = {
+        "metric": "KDA fwd tokens/s (prefill, decode) + % of MFMA/HBM roofline, 1 MI355X",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, f16 MFMA operands, f32 accumulate/state/out",
+        "data": "synthetic",
+        "config": {"workload": PREFILL, "B": w.B, "T": w.T, "H": w.H, "d_k": w.K, "d_v": w.V,
+                   "chunk": w.chunk, "global_batch": w.B, "seq_len": w.T,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "chunk_mfma_kernel", "alg_bytes_per_launch": alg_b},
+        "roofline_mfma": {"achieved": alg_f / (ms * 1e-3) / 1e12, "peak": MFMA_F16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": alg_f / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                          "flops": "algorithmic", "alg_flops_per_launch": alg_f},
+        "wall_s_timed_region": wall,
+    }
+
+    # ---- decode leg
+    if not args.no_decode:
+        wd = inputs.WORKLOADS[DECODE]
+        state = inputs.draw_decode_state(wd.seed, wd.N, wd.H, wd.K, wd.V, wd.s0_std).to(dev)
+        nin = 8
+        steps_in = [{k2: v2.to(dev) for k2, v2 in
+                     inputs.draw_decode_step(wd.seed, s, wd.N, wd.H, wd.K, wd.V, wd.dtype).items()}
+                    for s in range(nin)]
+        od = torch.empty(wd.N, wd.H, wd.V, device=dev)
+        ctr = [0]
+
+        def dstep():
+            xi = steps_in[ctr[0] % nin]
+            ctr[0] += 1
+            kda.decode_step(xi["q"], xi["k"], xi["v"], xi["g"], xi["beta"], state, out=od)
+
+        dms, dwall = time_launches(dstep, args.decode_steps, 3, stream)
+        db = decode_alg_bytes(wd.N, wd.H, wd.K, wd.V)
+        dach = db / (dms * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": DECODE, "value": wd.N / (dms * 1e-3), "unit": "tokens/s",
+            "ms_per_step": dms, "steps": args.decode_steps,
+            "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dach / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("decode_step_kernel", db),
+                         "kernel": "decode_step_kernel", "alg_bytes_per_launch": db},
+        }
+        del state, steps_in
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(d, w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

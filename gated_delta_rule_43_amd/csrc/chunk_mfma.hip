@@ -5,29 +5,35 @@
 // forget gate, and its lower-bounded decay lets both the diagonal
 // (intra-chunk) and off-diagonal (inter-chunk) tiles run as dense matrix
 // products.  This kernel is that chunked forward pass for K = V = 128 and
-// chunk C = 64, written for CDNA4:
-//
-//  * one workgroup (8 wavefronts) owns one (sequence, head, 64-column V tile);
-//    the 128 x 64 fp32 state tile lives in MFMA accumulator registers for the
-//    whole sequence (wave w holds key rows 16w..16w+15);
-//  * per chunk, q/k/g/v/beta are fetched with 16-byte loads one chunk ahead,
-//    the log-decay is summed along the chunk with a wave scan, and the
-//    decay-factored operands go to LDS as fp16;
-//  * the dense contractions use v_mfma_f32_16x16x32_f16 (fp16 operands, fp32
-//    accumulation); the unit-lower triangular solve runs in fp32 (VALU for the
-//    16 x 16 diagonal blocks, v_mfma_f32_16x16x4_f32 for the merges).
+// chunk C = 64.
 //
 // Algebra for one chunk (rows r, s = tokens; G = running sum of g inside the
-// chunk; m = 31 the reference row; all exponentials per key channel):
+// chunk, per key channel; m = 31 the reference row; Q, K, V the chunk tiles):
 //   Kp = K * exp(G - G_m),  Km = K * exp(G_m - G),  Qp = Q * exp(G - G_m)
-//   A  = Diag(beta) strict_lower(Kp Km^T),   T = (I + A)^-1,   Tb = T Diag(beta)
-//   P  = lower(Qp Km^T)
+//   A  = Diag(beta) strict_lower(Kp Km^T)      P = lower(Qp Km^T)
 //   S' = Diag(exp(G_m)) S
-//   U  = Tb (V - Kp S'),   O = Qp S' + P U
+//   (I + A) U = Diag(beta) (V - Kp S')         O = Qp S' + P U
 //   S  <- Diag(exp(G_C - G_m)) (S' + Km^T U)
 // Kp Km^T and Qp Km^T carry exp(G_r - G_s) <= 1 for s <= r.  With
-// -g_lb <= g <= 0 and g_lb * C / 2 <= 8 every factor stays inside fp16 range
-// (<= e^8); this is where the lower bound on the decay is used.
+// -g_lb <= g <= 0 and g_lb * C / 2 <= 8 every factor stays within e^8, inside
+// fp16 range: this is where the lower bound on the decay is used.
+//
+// Mapping onto CDNA4.  One workgroup = 8 wavefronts owns one (sequence, head,
+// 64-column V tile) and runs two wave groups concurrently:
+//  * state waves 0-3: wave jb owns value columns 16 jb..16 jb+15 and keeps the
+//    128 x 16 fp32 state slice in MFMA accumulators for the whole sequence.
+//    Per chunk it forms S', the inter-chunk products Kp S' and Qp S'
+//    (v_mfma_f32_16x16x32_f16), solves (I + A) U = rhs by 16-row block
+//    substitution entirely in registers (the 16x16 accumulator layout is the
+//    B-operand layout of v_mfma_f32_16x16x16_f16), adds P U, stores O and
+//    advances the state.  Its LDS traffic is wave-private or read-only.
+//  * prep waves 4-7: wave p owns key channels 32p..32p+31.  While the state
+//    waves finish chunk c they build chunk c+1's operands (16-byte loads
+//    issued one chunk ahead, running decay sums by wave-local shuffles,
+//    exponentials, fp16 tiles in LDS); then, while the state waves start
+//    chunk c+1, they form its Gram and query-key blocks and the 16 x 16
+//    diagonal inverses (I + A_ii)^-1 in fp32.
+// Two workgroup barriers per chunk separate these phases.
 #include "kda_common.hpp"
 
 namespace kda {
@@ -41,68 +47,58 @@ constexpr int C = 64;    // chunk length
 constexpr int KD = 128;  // key dimension
 constexpr int VD = 128;  // value dimension
 constexpr int VT = 64;   // value columns per workgroup
-constexpr int NT = 512;  // threads per workgroup
-constexpr int NW = NT / 64;
+constexpr int NT = 768;  // threads per workgroup: 4 state waves + 8 prep waves
+constexpr int NP = 8;    // prep waves
 constexpr int PK = 136;  // LDS pitch (halves) of [64][128] fp16 tiles
-constexpr int PC = 72;   // LDS pitch (halves) of [64][64] fp16 tiles
-constexpr int PA = 68;   // LDS pitch (floats) of [64][64] fp32 tiles
+constexpr int PC = 72;   // LDS pitch (halves) of [*][64] fp16 tiles
+constexpr int PI = 24;   // LDS pitch (halves) of 16 x 16 fp16 blocks
+constexpr int PF = 17;   // LDS pitch (floats) of 16 x 16 fp32 blocks
 
 struct Smem {
-    _Float16 kp[C * PK];   // Kp [s][c]
-    _Float16 km[C * PK];   // Km [s][c]
-    _Float16 qp[C * PK];   // Qp [s][c]
-    _Float16 st[VT * PK];  // S'^T [j][c]
-    float a[C * PA];       // A [r][s] (fp32); upper blocks used as scratch
-    float t[C * PA];       // T [r][s] (fp32, lower blocks)
-    _Float16 tb[C * PC];   // T Diag(beta) [r][s]
-    _Float16 p[C * PC];    // P [r][s]
-    _Float16 yt[VT * PC];  // (V - Kp S')^T [j][r]
-    _Float16 ut[VT * PC];  // U^T [j][r]
-    uint16_t v[C * PC];    // bf16 V tile [r][j]
-    float scan[NW * KD];   // per-wave channel sums of g, then exclusive prefixes
-    float gref[KD];        // G_m per channel (reference row m = 31)
-    float fm[KD];          // exp(G_m)
-    float fc[KD];          // exp(G_C - G_m)
+    _Float16 kp[C * PK];        // Kp [s][c]
+    _Float16 qp[C * PK];        // Qp [s][c]
+    _Float16 km[C * PK];        // Km [s][c]   (Gram / query-key B operand)
+    _Float16 kmt[2][KD * PC];   // Km^T [c][s] (state-advance A operand), by chunk parity
+    _Float16 a16[C * PC];       // A [r][s], lower blocks
+    _Float16 p[C * PC];         // P [r][s], lower blocks
+    _Float16 tii[4][16 * PI];   // (I + A_ii)^-1, diagonal blocks
+    uint16_t v[C * PC];         // bf16 V tile [r][j]
     float beta[C];
+    float fm[2][KD];            // exp(G_m), by chunk parity
+    float fc[2][KD];            // exp(G_C - G_m), by chunk parity
+    _Float16 st[4][16 * PK];    // state waves: S'^T [j][c] (private)
+    _Float16 ut[4][16 * PC];    // state waves: U^T [j][s] (private)
+    float ad[4][16 * PF];       // prep waves: diagonal A blocks (private)
+    float gsum[NP][KD];         // prep waves: per-wave channel sums of g (next chunk)
 };
 
-__device__ __forceinline__ floatx4 mma16(half8 a, half8 b, floatx4 c) {
+__device__ __forceinline__ floatx4 mma32(half8 a, half8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ floatx4 mma16_f32(float a, float b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+__device__ __forceinline__ floatx4 mma16(half4 a, half4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-// Operand fragment of rows row0..row0+15, k = k0..k0+31 from a row-major
-// [rows][k] fp16 tile: lane holds row (lane & 15), k = k0 + 8 (lane >> 4) .. +7.
-__device__ __forceinline__ half8 frag(const _Float16 *base, int pitch, int row0, int k0,
-                                      int lane) {
+// 16x16x32 operand fragment of rows row0..row0+15, k = k0..k0+31 from a
+// row-major [rows][k] fp16 tile: lane holds row (lane & 15), k = k0 + 8 (lane >> 4) .. +7.
+__device__ __forceinline__ half8 frag8(const _Float16 *base, int pitch, int row0, int k0,
+                                       int lane) {
     return *reinterpret_cast<const half8 *>(base + (row0 + (lane & 15)) * pitch + k0 +
                                             8 * (lane >> 4));
 }
-// The same fragment taken from a tile stored transposed ([k][rows]).
-__device__ __forceinline__ half8 frag_t(const _Float16 *base, int pitch, int row0, int k0,
-                                        int lane) {
-    const _Float16 *q = base + (k0 + 8 * (lane >> 4)) * pitch + row0 + (lane & 15);
-    half8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = q[e * pitch];
-    return r;
+// 16x16x16 operand fragment: lane holds row (lane & 15), k = k0 + 4 (lane >> 4) .. +3.
+__device__ __forceinline__ half4 frag4(const _Float16 *base, int pitch, int row0, int k0,
+                                       int lane) {
+    return *reinterpret_cast<const half4 *>(base + (row0 + (lane & 15)) * pitch + k0 +
+                                            4 * (lane >> 4));
 }
-
-// D = X Y (+ acc) for 16 x 16 fp32 blocks X, Y held in LDS with pitch PA.
-__device__ __forceinline__ floatx4 mm16_f32(const float *X, const float *Y, int lane,
-                                            floatx4 acc) {
+// An accumulator block (rows 4 (lane >> 4) + i, column lane & 15) as fp16: this
+// is also the B fragment of a following 16x16x16 product with k = those rows.
+__device__ __forceinline__ half4 to_half4(floatx4 x) {
+    half4 h;
 #pragma unroll
-    for (int k0 = 0; k0 < 16; k0 += 4)
-        acc = mma16_f32(X[(lane & 15) * PA + k0 + (lane >> 4)],
-                        Y[(k0 + (lane >> 4)) * PA + (lane & 15)], acc);
-    return acc;
-}
-// Store an accumulator block (times scale) to a 16 x 16 fp32 block with pitch PA.
-__device__ __forceinline__ void st16_f32(float *Z, floatx4 d, int lane, float scale) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Z[(4 * (lane >> 4) + i) * PA + (lane & 15)] = scale * d[i];
+    for (int i = 0; i < 4; ++i) h[i] = (_Float16)x[i];
+    return h;
 }
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -112,36 +108,202 @@ __device__ __forceinline__ void unpack8(const uint4 &u, float *x) {
     x[4] = bf16lo(u.z); x[5] = bf16hi(u.z); x[6] = bf16lo(u.w); x[7] = bf16hi(u.w);
 }
 
-// Chunk inputs held in registers while the previous chunk computes.
+// One chunk's inputs, held in a prep wave's registers one chunk ahead.
+// Lane (cg = lane & 15, tb = lane >> 4) of prep wave p holds channels
+// 8 cg .. 8 cg + 7 of tokens 8p + 2 tb and 8p + 2 tb + 1, so each wave reads
+// whole 256-byte rows.
 struct Raw {
-    uint4 q[2], k[2], g[2];  // tokens 2*tg and 2*tg+1, channels 8*cg..8*cg+7
-    uint4 v;                 // V tile row t>>3, columns 8*(t&7)..+7
-    uint32_t beta;           // threads 0..63: beta of token t
+    uint4 q[2], k[2], g[2];
+    uint4 v;         // V tile piece: row idx >> 3, columns 8 (idx & 7) .., idx = 64p + lane
+    uint32_t beta;   // prep wave 0: beta of token lane
 };
 
 __device__ __forceinline__ void load_raw(Raw &R, const uint16_t *q, const uint16_t *k,
                                          const uint16_t *g, const uint16_t *v,
                                          const uint16_t *beta, int c0, int L, int H, int h,
-                                         int vt, int t) {
-    const int cg = t & 15, tg = t >> 4;
+                                         int vt, int p, int lane) {
+    const int cg = lane & 15, tb = lane >> 4;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int r = 2 * tg + e;
-        R.q[e] = make_uint4(0u, 0u, 0u, 0u);
-        R.k[e] = R.q[e];
-        R.g[e] = R.q[e];
+    for (int u = 0; u < 2; ++u) {
+        const int r = 8 * p + 2 * tb + u;
+        R.q[u] = make_uint4(0u, 0u, 0u, 0u);
+        R.k[u] = R.q[u];
+        R.g[u] = R.q[u];
         if (r < L) {
             const size_t off = ((size_t)(c0 + r) * H + h) * KD + 8 * cg;
-            R.q[e] = *reinterpret_cast<const uint4 *>(q + off);
-            R.k[e] = *reinterpret_cast<const uint4 *>(k + off);
-            R.g[e] = *reinterpret_cast<const uint4 *>(g + off);
+            R.q[u] = *reinterpret_cast<const uint4 *>(q + off);
+            R.k[u] = *reinterpret_cast<const uint4 *>(k + off);
+            R.g[u] = *reinterpret_cast<const uint4 *>(g + off);
         }
     }
+    const int idx = 64 * p + lane;
     R.v = make_uint4(0u, 0u, 0u, 0u);
-    if ((t >> 3) < L)
-        R.v = *reinterpret_cast<const uint4 *>(v + ((size_t)(c0 + (t >> 3)) * H + h) * VD +
-                                               vt * VT + 8 * (t & 7));
-    R.beta = (t < C && t < L) ? beta[(size_t)(c0 + t) * H + h] : 0u;
+    if ((idx >> 3) < L)
+        R.v = *reinterpret_cast<const uint4 *>(v + ((size_t)(c0 + (idx >> 3)) * H + h) * VD +
+                                               vt * VT + 8 * (idx & 7));
+    R.beta = (p == 0 && lane < L) ? beta[(size_t)(c0 + lane) * H + h] : 0u;
+}
+
+// Prep wave p, first half of the running log-decay sum: inclusive scan over
+// the wave's four token pairs (lanes 16 apart share channels).  The wave's
+// channel totals go to LDS; ex keeps the in-wave exclusive prefix.
+__device__ __forceinline__ void scan_partials(Smem &sm, const Raw &R, int p, int lane,
+                                              float *ex) {
+    const int cg = lane & 15, tb = lane >> 4;
+    float g0[8], g1[8];
+    unpack8(R.g[0], g0);
+    unpack8(R.g[1], g1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float loc = g0[e] + g1[e];
+        float s = loc;
+        float x = __shfl_up(s, 16);
+        if (tb >= 1) s += x;
+        x = __shfl_up(s, 32);
+        if (tb >= 2) s += x;
+        ex[e] = s - loc;
+        if (tb == 3) sm.gsum[p][8 * cg + e] = s;
+    }
+}
+
+// Prep wave p, second half: combine the wave totals into G - G_m for this
+// lane's tokens and write the fp16 operand tiles of the chunk.
+__device__ __forceinline__ void prologue(Smem &sm, const Raw &R, int par, int p, int lane,
+                                         const float *ex) {
+    const int cg = lane & 15, tb = lane >> 4;
+    const int ch0 = 8 * cg;
+    const int r0 = 8 * p + 2 * tb;
+    float g0[8], g1[8], kv0[8], kv1[8], qv0[8], qv1[8];
+    unpack8(R.g[0], g0);
+    unpack8(R.g[1], g1);
+    unpack8(R.k[0], kv0);
+    unpack8(R.k[1], kv1);
+    unpack8(R.q[0], qv0);
+    unpack8(R.q[1], qv1);
+    // offset of this wave's first token from the reference row m = 31 (the end
+    // of wave 3's tokens): + sum of waves 4..p-1, or - sum of waves p..3
+    float d[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = 0.f;
+    const int lo = p < 4 ? p : 4, hi = p < 4 ? 4 : p;
+    for (int ww = lo; ww < hi; ++ww) {
+        const floatx4 a = *reinterpret_cast<const floatx4 *>(&sm.gsum[ww][ch0]);
+        const floatx4 b = *reinterpret_cast<const floatx4 *>(&sm.gsum[ww][ch0 + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            d[e] += a[e];
+            d[e + 4] += b[e];
+        }
+    }
+    if (p == 0 && tb == 0) {  // per-channel factors exp(G_m) and exp(G_C - G_m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float gm = 0.f, gc = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NP; ++ww) {
+                const float x = sm.gsum[ww][ch0 + e];
+                if (ww < 4) gm += x;
+                gc += x;
+            }
+            sm.fm[par][ch0 + e] = fast_exp(gm);
+            sm.fc[par][ch0 + e] = fast_exp(gc - gm);
+        }
+    }
+    half8 hkp0, hkm0, hqp0, hkp1, hkm1, hqp1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float pre = ex[e] + (p < 4 ? -d[e] : d[e]);
+        const float G0 = pre + g0[e], G1 = G0 + g1[e];  // G - G_m
+        const float f0 = fast_exp(G0), f1 = fast_exp(G1);
+        const float i0 = __builtin_amdgcn_rcpf(f0), i1 = __builtin_amdgcn_rcpf(f1);
+        hkp0[e] = (_Float16)(kv0[e] * f0);
+        hkm0[e] = (_Float16)(kv0[e] * i0);
+        hqp0[e] = (_Float16)(qv0[e] * f0);
+        hkp1[e] = (_Float16)(kv1[e] * f1);
+        hkm1[e] = (_Float16)(kv1[e] * i1);
+        hqp1[e] = (_Float16)(qv1[e] * f1);
+    }
+    *reinterpret_cast<half8 *>(&sm.kp[r0 * PK + ch0]) = hkp0;
+    *reinterpret_cast<half8 *>(&sm.km[r0 * PK + ch0]) = hkm0;
+    *reinterpret_cast<half8 *>(&sm.qp[r0 * PK + ch0]) = hqp0;
+    *reinterpret_cast<half8 *>(&sm.kp[(r0 + 1) * PK + ch0]) = hkp1;
+    *reinterpret_cast<half8 *>(&sm.km[(r0 + 1) * PK + ch0]) = hkm1;
+    *reinterpret_cast<half8 *>(&sm.qp[(r0 + 1) * PK + ch0]) = hqp1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+        half2_t pr;
+        pr[0] = hkm0[e];
+        pr[1] = hkm1[e];
+        *reinterpret_cast<half2_t *>(&sm.kmt[par][(ch0 + e) * PC + r0]) = pr;
+    }
+    const int idx = 64 * p + lane;
+    *reinterpret_cast<uint4 *>(&sm.v[(idx >> 3) * PC + 8 * (idx & 7)]) = R.v;
+    if (p == 0) sm.beta[lane] = __uint_as_float(R.beta << 16);
+}
+
+__device__ __forceinline__ floatx4 block_product(const _Float16 *lhs, const _Float16 *rhs, int bi,
+                                                 int bj, int lane) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        acc = mma32(frag8(lhs, PK, 16 * bi, 32 * ks, lane), frag8(rhs, PK, 16 * bj, 32 * ks, lane), acc);
+    return acc;
+}
+
+// Prep wave p: the chunk's Gram / query-key blocks.  Waves 0-3 take the
+// diagonal blocks (p, p) and the inverse (I + A_pp)^-1; waves 4-7 take the
+// twelve off-diagonal blocks (six Gram, six query-key), three each.
+__device__ __forceinline__ void prep_blocks(Smem &sm, int p, int lane) {
+    const int l16 = lane & 15, lg = lane >> 4;
+    if (p < 4) {
+        const floatx4 a = block_product(sm.kp, sm.km, p, p, lane);
+        float *ad = sm.ad[p];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lg + i;
+            ad[r * PF + l16] = l16 < r ? sm.beta[16 * p + r] * a[i] : 0.f;
+        }
+        const floatx4 pq = block_product(sm.qp, sm.km, p, p, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lg + i;
+            sm.p[(16 * p + r) * PC + 16 * p + l16] = (_Float16)(l16 <= r ? pq[i] : 0.f);
+        }
+        // (I + A_pp)^-1 by forward substitution, one column per lane (lanes
+        // 16..63 repeat lanes 0..15 so the wave stays convergent; 0..15 store)
+        const int j = l16;
+        float tc[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int s = 0; s < r; ++s) acc -= ad[r * PF + s] * tc[s];
+            tc[r] = acc;
+        }
+        if (lane < 16) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.tii[p][r * PI + j] = (_Float16)tc[r];
+        }
+    } else {
+#pragma unroll
+        for (int tsk = 0; tsk < 3; ++tsk) {
+            const int o = 3 * (p - 4) + tsk;  // 0..11
+            const int oo = o % 6;
+            const bool gram = o < 6;
+            const int bi = oo < 1 ? 1 : (oo < 3 ? 2 : 3);
+            const int bj = oo < 1 ? 0 : (oo < 3 ? oo - 1 : oo - 3);
+            const floatx4 acc = block_product(gram ? sm.kp : sm.qp, sm.km, bi, bj, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * bi + 4 * lg + i, s = 16 * bj + l16;
+                if (gram)
+                    sm.a16[r * PC + s] = (_Float16)(sm.beta[r] * acc[i]);
+                else
+                    sm.p[r * PC + s] = (_Float16)acc[i];
+            }
+        }
+    }
 }
 
 template <typename TOut>
@@ -155,318 +317,152 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
 
     // Both V tiles of a head land on the same XCD (workgroups are dealt to the
     // 8 XCDs round-robin), so their shared q/k/g reads meet in one L2.
-    const int b = blockIdx.x;  // wave-uniform quantities below are kept in SGPRs
+    const int b = blockIdx.x;
     const int xcd = b & 7, slot = b >> 3;
     const int vt = slot & 1;
     const int unit = (slot >> 1) * 8 + xcd;
     if (unit >= N * H) return;
     const int n = unit / H, h = unit % H;
 
-    const int t = threadIdx.x, lane = t & 63;
-    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const bool state_wave = w < 4;
     const int l16 = lane & 15, lg = lane >> 4;
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
+    const int nchunks = (eos - bos + C - 1) / C;
 
-    // State tile: wave w owns key rows c = 16w + 4*lg + i and columns
-    // j = 16*jb + l16 of this V tile.
-    const size_t sbase = (size_t)unit * (KD * VD) + (size_t)vt * VT;
-    floatx4 S[4];
+    // The two wave groups run separate loops with the same barrier sequence
+    // (two before the loop, two per chunk), so their registers never overlap.
+    if (state_wave) {
+        // S[cb] holds rows c = 16 cb + 4 lg + i, column 16 w + l16 of the tile
+        const size_t sbase = (size_t)unit * (KD * VD) + (size_t)vt * VT + 16 * w + l16;
+        floatx4 S[8];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
+        for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = 16 * w + 4 * lg + i, j = 16 * jb + l16;
-            S[jb][i] = s0 ? s0[sbase + (size_t)c * VD + j] : 0.f;
-        }
-
-    // Output blocks of this wave: rows 16*rb.., columns 16*(2*jp + e)..
-    const int rb = w >> 1, jp = w & 1;
-    const int cg = t & 15, tg = t >> 4;
-
-    Raw R;
-    if (bos < eos) load_raw(R, q, k, g, v, beta, bos, min(C, eos - bos), H, h, vt, t);
-
-    for (int c0 = bos; c0 < eos; c0 += C) {
-        const int L = min(C, eos - c0);
-
-        // ---- prologue: running log-decay and the decay-factored operands
-        // Thread (cg, tg) holds channels 8cg..8cg+7 of tokens 2tg, 2tg+1.
-        float g0[8], g1[8], ex[8];
-        unpack8(R.g[0], g0);
-        unpack8(R.g[1], g1);
-        *reinterpret_cast<uint4 *>(&sm.v[(t >> 3) * PC + 8 * (t & 7)]) = R.v;
-        if (t < C) sm.beta[t] = __uint_as_float(R.beta << 16);
-        // inclusive scan over the wave's four token pairs (lanes 16 apart
-        // share channels); ex = exclusive prefix inside the wave
+            for (int i = 0; i < 4; ++i)
+                S[cb][i] = s0 ? s0[sbase + (size_t)(16 * cb + 4 * lg + i) * VD] : 0.f;
+        _Float16 *st = sm.st[w];
+        _Float16 *ut = sm.ut[w];
+        __syncthreads();
+        __syncthreads();
+        for (int ci = 0; ci < nchunks; ++ci) {
+            const int c0 = bos + ci * C;
+            const int L = min(C, eos - c0);
+            const int par = ci & 1;
+            floatx4 Y[4], O[4];
+            // ---- phase A: S' = Diag(exp(G_m)) S (kept in S, written transposed),
+            // the inter-chunk products Kp S' and Qp S', and beta (V - Kp S')
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const float loc = g0[c] + g1[c];
-            float s = loc;
-            float u = __shfl_up(s, 16);
-            if (lg >= 1) s += u;
-            u = __shfl_up(s, 32);
-            if (lg >= 2) s += u;
-            ex[c] = s - loc;
-            if (lg == 3) sm.scan[w * KD + 8 * cg + c] = s;
-        }
-        __syncthreads();  // B1: per-wave sums visible
-        if (t < KD) {
-            // exclusive prefixes over the 8 waves, G_m = G at token 31 (end of
-            // wave 3's tokens) and G_C = G at the last token
-            float run = 0.f, gm = 0.f;
+            for (int cb = 0; cb < 8; ++cb) {
+                const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.fm[par][16 * cb + 4 * lg]);
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                const float x = sm.scan[ww * KD + t];
-                sm.scan[ww * KD + t] = run;
-                run += x;
-                if (ww == 3) gm = run;
+                for (int i = 0; i < 4; ++i) S[cb][i] *= f[i];
+                *reinterpret_cast<half4 *>(&st[l16 * PK + 16 * cb + 4 * lg]) = to_half4(S[cb]);
             }
-            sm.gref[t] = gm;
-            sm.fm[t] = fast_exp(gm);
-            sm.fc[t] = fast_exp(run - gm);
-        }
-        __syncthreads();  // B1b: prefixes and per-channel factors visible
-
-        // S' = Diag(exp(G_m)) S, written transposed as the fp16 B operand.
-        float fc[4];
+            half8 bs[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = 16 * w + 4 * lg + i;
-            const float fm = sm.fm[c];
-            fc[i] = sm.fc[c];
+            for (int ks = 0; ks < 4; ++ks) bs[ks] = frag8(st, PK, 0, 32 * ks, lane);
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) S[jb][i] *= fm;
-        }
+            for (int rb = 0; rb < 4; ++rb) {
+                floatx4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            half4 hv;
+                for (int ks = 0; ks < 4; ++ks) {
+                    x = mma32(frag8(sm.kp, PK, 16 * rb, 32 * ks, lane), bs[ks], x);
+                    y = mma32(frag8(sm.qp, PK, 16 * rb, 32 * ks, lane), bs[ks], y);
+                }
+                O[rb] = y;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) hv[i] = (_Float16)S[jb][i];
-            *reinterpret_cast<half4 *>(&sm.st[(16 * jb + l16) * PK + 16 * w + 4 * lg]) = hv;
-        }
-        // Running sums for this thread's two tokens and the factored operands.
-        {
-            half8 hkp0, hkm0, hqp0, hkp1, hkm1, hqp1;
-            float k0[8], k1[8], q0[8], q1[8];
-            unpack8(R.k[0], k0);
-            unpack8(R.k[1], k1);
-            unpack8(R.q[0], q0);
-            unpack8(R.q[1], q1);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int ch = 8 * cg + c;
-                const float pre = sm.scan[w * KD + ch] + ex[c] - sm.gref[ch];
-                const float G0 = pre + g0[c], G1 = G0 + g1[c];  // G - G_m
-                const float f0 = fast_exp(G0), f1 = fast_exp(G1);
-                const float i0 = __builtin_amdgcn_rcpf(f0), i1 = __builtin_amdgcn_rcpf(f1);
-                hkp0[c] = (_Float16)(k0[c] * f0);
-                hkm0[c] = (_Float16)(k0[c] * i0);
-                hqp0[c] = (_Float16)(q0[c] * f0);
-                hkp1[c] = (_Float16)(k1[c] * f1);
-                hkm1[c] = (_Float16)(k1[c] * i1);
-                hqp1[c] = (_Float16)(q1[c] * f1);
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * rb + 4 * lg + i;
+                    const float vv = __uint_as_float((uint32_t)sm.v[r * PC + 16 * w + l16] << 16);
+                    Y[rb][i] = sm.beta[r] * (vv - x[i]);
+                }
             }
-            const int r = 2 * tg;
-            *reinterpret_cast<half8 *>(&sm.kp[r * PK + 8 * cg]) = hkp0;
-            *reinterpret_cast<half8 *>(&sm.km[r * PK + 8 * cg]) = hkm0;
-            *reinterpret_cast<half8 *>(&sm.qp[r * PK + 8 * cg]) = hqp0;
-            *reinterpret_cast<half8 *>(&sm.kp[(r + 1) * PK + 8 * cg]) = hkp1;
-            *reinterpret_cast<half8 *>(&sm.km[(r + 1) * PK + 8 * cg]) = hkm1;
-            *reinterpret_cast<half8 *>(&sm.qp[(r + 1) * PK + 8 * cg]) = hqp1;
-        }
-        __syncthreads();  // B2: operands, S'^T, V tile and beta in LDS
-        // Fetch the next chunk now; it lands while this chunk computes.
-        if (c0 + C < eos) load_raw(R, q, k, g, v, beta, c0 + C, min(C, eos - c0 - C), H, h, vt, t);
-
-        // ---- intra-chunk Gram and query-key blocks (10 lower 16x16 blocks each)
-        for (int task = w; task < 20; task += NW) {
-            const bool gram = task < 10;
-            int bi = task % 10, i = 0;
-            while (bi > i) { bi -= i + 1; ++i; }
-            const int j = bi;  // block (i, j), j <= i
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            const _Float16 *lhs = gram ? sm.kp : sm.qp;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                acc = mma16(frag(lhs, PK, 16 * i, 32 * ks, lane), frag(sm.km, PK, 16 * j, 32 * ks, lane), acc);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * i + 4 * lg + e, s = 16 * j + l16;
-                if (gram)
-                    sm.a[r * PA + s] = s < r ? sm.beta[r] * acc[e] : 0.f;
-                else
-                    sm.p[r * PC + s] = (_Float16)(s <= r ? acc[e] : 0.f);
-            }
-        }
-        // zero the two upper P blocks that the P U products read
-        if (w == NW - 1) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * lg + e;
-                sm.p[r * PC + 16 + l16] = (_Float16)0.f;
-                sm.p[(32 + r) * PC + 48 + l16] = (_Float16)0.f;
-            }
-        }
-
-        // ---- X = Kp S' and Qp S' (the off-diagonal, state-dependent tiles)
-        floatx4 X[2], O[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            X[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-            O[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const half8 ak = frag(sm.kp, PK, 16 * rb, 32 * ks, lane);
-            const half8 aq = frag(sm.qp, PK, 16 * rb, 32 * ks, lane);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const half8 bs = frag(sm.st, PK, 16 * (2 * jp + e), 32 * ks, lane);
-                X[e] = mma16(ak, bs, X[e]);
-                O[e] = mma16(aq, bs, O[e]);
-            }
-        }
-        // Y = V - X, stored transposed as the B operand of Tb Y
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int j = 16 * (2 * jp + e) + l16;
-            half4 hv;
+            __syncthreads();
+            // ---- phase B: (I + A) U = Y by 16-row blocks,
+            // U_i = T_ii (Y_i - sum_{j<i} A_ij U_j), all in registers
+            half4 U[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * rb + 4 * lg + i;
-                const float vv = __uint_as_float((uint32_t)sm.v[r * PC + j] << 16);
-                hv[i] = (_Float16)(vv - X[e][i]);
+                floatx4 z = Y[i];
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < i; ++j) acc = mma16(frag4(sm.a16, PC, 16 * i, 16 * j, lane), U[j], acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) z[e] -= acc[e];
+                const floatx4 u = mma16(frag4(sm.tii[i], PI, 0, 0, lane), to_half4(z),
+                                        floatx4{0.f, 0.f, 0.f, 0.f});
+                U[i] = to_half4(u);
+                *reinterpret_cast<half4 *>(&ut[l16 * PC + 16 * i + 4 * lg]) = U[i];
             }
-            *reinterpret_cast<half4 *>(&sm.yt[j * PC + 16 * rb + 4 * lg]) = hv;
-        }
-        __syncthreads();  // B3: A, P, Y^T ready
-
-        // ---- T = (I + A)^-1: 16 x 16 diagonal blocks by forward substitution
-        if (w == 0) {
-            const int blk = lg, j = l16;
-            const float *Ab = sm.a + (16 * blk) * PA + 16 * blk;
-            float tc[16];
+            // O = Qp S' + P U, stored for the valid rows
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == j) ? 1.f : 0.f;
+            for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
-                for (int s = 0; s < r; ++s) acc -= Ab[r * PA + s] * tc[s];
-                tc[r] = acc;
+                for (int i = 0; i <= rb; ++i) O[rb] = mma16(frag4(sm.p, PC, 16 * rb, 16 * i, lane), U[i], O[rb]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * lg + e;
+                    if (r < L)
+                        o[((size_t)(c0 + r) * H + h) * VD + vt * VT + 16 * w + l16] = from_f32<TOut>(O[rb][e]);
+                }
             }
-            float *Tb = sm.t + (16 * blk) * PA + 16 * blk;
+            // S = Diag(exp(G_C - G_m)) (S' + Km^T U)
+            half8 bu[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Tb[r * PA + j] = tc[r];
-        }
-        __syncthreads();
-        // level 1: T_{i,i-1} = -T_ii (A_{i,i-1} T_{i-1,i-1}), i = 1..3
-        if (w < 3) {
-            const int i = w + 1, j = w;
-            float *scr = sm.a + (16 * j) * PA + 16 * i;  // upper block (j, i) as scratch
-            floatx4 m = mm16_f32(sm.a + (16 * i) * PA + 16 * j, sm.t + (16 * j) * PA + 16 * j,
-                                 lane, floatx4{0.f, 0.f, 0.f, 0.f});
-            st16_f32(scr, m, lane, 1.f);
-        }
-        __syncthreads();
-        if (w < 3) {
-            const int i = w + 1, j = w;
-            const float *scr = sm.a + (16 * j) * PA + 16 * i;
-            floatx4 r = mm16_f32(sm.t + (16 * i) * PA + 16 * i, scr, lane, floatx4{0.f, 0.f, 0.f, 0.f});
-            st16_f32(sm.t + (16 * i) * PA + 16 * j, r, lane, -1.f);
-        }
-        __syncthreads();
-        // level 2: T_20 = -T_22 (A_20 T_00 + A_21 T_10), T_31 = -T_33 (A_31 T_11 + A_32 T_21)
-        if (w < 2) {
-            const int i = w + 2, j = w;
-            float *scr = sm.a + (16 * j) * PA + 16 * i;
-            floatx4 m = mm16_f32(sm.a + (16 * i) * PA + 16 * j, sm.t + (16 * j) * PA + 16 * j,
-                                 lane, floatx4{0.f, 0.f, 0.f, 0.f});
-            m = mm16_f32(sm.a + (16 * i) * PA + 16 * (j + 1), sm.t + (16 * (j + 1)) * PA + 16 * j,
-                         lane, m);
-            st16_f32(scr, m, lane, 1.f);
-        }
-        __syncthreads();
-        if (w < 2) {
-            const int i = w + 2, j = w;
-            const float *scr = sm.a + (16 * j) * PA + 16 * i;
-            floatx4 r = mm16_f32(sm.t + (16 * i) * PA + 16 * i, scr, lane, floatx4{0.f, 0.f, 0.f, 0.f});
-            st16_f32(sm.t + (16 * i) * PA + 16 * j, r, lane, -1.f);
-        }
-        __syncthreads();
-        // level 3: T_30 = -T_33 (A_30 T_00 + A_31 T_10 + A_32 T_20)
-        if (w == 0) {
-            float *scr = sm.a + 48;  // upper block (0, 3)
-            floatx4 m = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int ks = 0; ks < 2; ++ks) bu[ks] = frag8(ut, PC, 0, 32 * ks, lane);
 #pragma unroll
-            for (int l = 0; l < 3; ++l)
-                m = mm16_f32(sm.a + 48 * PA + 16 * l, sm.t + (16 * l) * PA, lane, m);
-            st16_f32(scr, m, lane, 1.f);
-        }
-        __syncthreads();
-        if (w == 0) {
-            floatx4 r = mm16_f32(sm.t + 48 * PA + 48, sm.a + 48, lane, floatx4{0.f, 0.f, 0.f, 0.f});
-            st16_f32(sm.t + 48 * PA, r, lane, -1.f);
-        }
-        __syncthreads();
-        // Tb = T Diag(beta) in fp16 (zero above the diagonal)
-        for (int idx = t; idx < C * C; idx += NT) {
-            const int r = idx >> 6, s = idx & 63;
-            sm.tb[r * PC + s] = (_Float16)(s <= r ? sm.t[r * PA + s] * sm.beta[s] : 0.f);
-        }
-        __syncthreads();  // B4: Tb ready
-
-        // ---- U = Tb Y (lower-triangular Tb: k range grows with the row block)
-        const int nks = rb < 2 ? 1 : 2;
+            for (int cb = 0; cb < 8; ++cb) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int jb = 2 * jp + e;
-            floatx4 u = {0.f, 0.f, 0.f, 0.f};
-            for (int ks = 0; ks < nks; ++ks)
-                u = mma16(frag(sm.tb, PC, 16 * rb, 32 * ks, lane), frag(sm.yt, PC, 16 * jb, 32 * ks, lane), u);
-            half4 hv;
+                for (int ks = 0; ks < 2; ++ks)
+                    S[cb] = mma32(frag8(sm.kmt[par], PC, 16 * cb, 32 * ks, lane), bu[ks], S[cb]);
+                const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.fc[par][16 * cb + 4 * lg]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) hv[i] = (_Float16)u[i];
-            *reinterpret_cast<half4 *>(&sm.ut[(16 * jb + l16) * PC + 16 * rb + 4 * lg]) = hv;
-        }
-        __syncthreads();  // B5: U^T ready
-
-        // ---- O = Qp S' + P U, stored for the valid rows
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int jb = 2 * jp + e;
-            for (int ks = 0; ks < nks; ++ks)
-                O[e] = mma16(frag(sm.p, PC, 16 * rb, 32 * ks, lane), frag(sm.ut, PC, 16 * jb, 32 * ks, lane), O[e]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * rb + 4 * lg + i;
-                if (r < L)
-                    o[((size_t)(c0 + r) * H + h) * VD + vt * VT + 16 * jb + l16] = from_f32<TOut>(O[e][i]);
+                for (int i = 0; i < 4; ++i) S[cb][i] *= f[i];
             }
+            __syncthreads();
         }
-        // ---- state advance: S = Diag(exp(G_C - G_m)) (S' + Km^T U)
+        if (sT) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const half8 a = frag_t(sm.km, PK, 16 * w, 32 * ks, lane);
+            for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb)
-                S[jb] = mma16(a, frag(sm.ut, PC, 16 * jb, 32 * ks, lane), S[jb]);
+                for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * cb + 4 * lg + i) * VD] = S[cb][i];
         }
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[jb][i] *= fc[i];
-        // No barrier needed here: everything the next prologue writes before
-        // its first barrier (V tile, beta, per-wave sums) was last read before B4.
-    }
-
-    if (sT) {
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = 16 * w + 4 * lg + i, j = 16 * jb + l16;
-                sT[sbase + (size_t)c * VD + j] = S[jb][i];
+    } else {
+        const int p = w - 4;
+        Raw R;
+        float ex[8];
+        if (nchunks > 0) {
+            load_raw(R, q, k, g, v, beta, bos, min(C, eos - bos), H, h, vt, p, lane);
+            scan_partials(sm, R, p, lane, ex);
+        }
+        __syncthreads();
+        if (nchunks > 0) {
+            prologue(sm, R, 0, p, lane, ex);
+            if (nchunks > 1)
+                load_raw(R, q, k, g, v, beta, bos + C, min(C, eos - bos - C), H, h, vt, p, lane);
+        }
+        __syncthreads();
+        for (int ci = 0; ci < nchunks; ++ci) {
+            const int c0 = bos + ci * C;
+            const bool next = ci + 1 < nchunks;
+            // ---- phase A: this chunk's Gram / query-key blocks and diagonal
+            // inverses; the next chunk's per-wave decay sums
+            if (next) scan_partials(sm, R, p, lane, ex);
+            prep_blocks(sm, p, lane);
+            __syncthreads();
+            // ---- phase B: operands of the next chunk; then fetch the one after it
+            if (next) {
+                prologue(sm, R, (ci & 1) ^ 1, p, lane, ex);
+                if (ci + 2 < nchunks) {
+                    const int cn = c0 + 2 * C;
+                    load_raw(R, q, k, g, v, beta, cn, min(C, eos - cn), H, h, vt, p, lane);
+                }
             }
+            __syncthreads();
+        }
     }
 }
 
