@@ -115,6 +115,43 @@ def cpu_baseline(d, w, wall_budget_s=2.5):
                       f"{threads} host threads available"}
 
 
+def decode_leg(args, dev, stream):
+    """Decode workload: persistent fp32 state [256, 32, 128, 128], a fresh token per
+    sequence each step (8 pre-drawn steps cycled), one kda_decode_step per step."""
+    import torch
+    from gated_delta_rule_43_amd import inputs, kda
+    wd = inputs.WORKLOADS[DECODE]
+    state = inputs.draw_decode_state(wd.seed, wd.N, wd.H, wd.K, wd.V, wd.s0_std).to(dev)
+    nin = 8
+    steps_in = [{k2: v2.to(dev) for k2, v2 in
+                 inputs.draw_decode_step(wd.seed, s, wd.N, wd.H, wd.K, wd.V, wd.dtype).items()}
+                for s in range(nin)]
+    od = torch.empty(wd.N, wd.H, wd.V, device=dev)
+    ctr = [0]
+
+    def dstep():
+        xi = steps_in[ctr[0] % nin]
+        ctr[0] += 1
+        kda.decode_step(xi["q"], xi["k"], xi["v"], xi["g"], xi["beta"], state, out=od)
+
+    if args.only == "decode":
+        for _ in range(args.steps):
+            dstep()
+        torch.cuda.synchronize()
+        return {"only": "decode", "workload": DECODE, "launches": args.steps}
+    dms, dwall = time_launches(dstep, args.decode_steps, 3, stream)
+    db = decode_alg_bytes(wd.N, wd.H, wd.K, wd.V)
+    dach = db / (dms * 1e-3) / 1e9
+    return {
+        "workload": DECODE, "value": wd.N / (dms * 1e-3), "unit": "tokens/s",
+        "ms_per_step": dms, "steps": args.decode_steps,
+        "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dach / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("decode_step_kernel", db),
+                     "kernel": "decode_step_kernel", "alg_bytes_per_launch": db},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +160,11 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--prefill-workload", default=PREFILL,
+                    choices=["prefill_bf16_B1_H8_T4096", "batched_bf16_B4_H32_T8192"])
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="profiling mode: launch only this kernel --steps times and print "
+                         "nothing else (copy = a 512 MiB device copy for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the KDA path here runs on a single MI355X and "
@@ -140,20 +182,42 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
+    if args.only == "copy":
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_per_copy": src.numel()}), flush=True)
+        return
+
+    if args.only == "decode":
+        print(json.dumps(decode_leg(args, dev, stream)), flush=True)
+        return
+
     # ---- prefill: the step
-    w = inputs.WORKLOADS[PREFILL]
-    d = inputs.draw_fixed(w.seed, w.B, w.T, w.H, w.K, w.V, w.dtype)
+    w = inputs.WORKLOADS[args.prefill_workload]
+    d = inputs.draw_fixed(w.seed, w.B, w.T, w.H, w.K, w.V, w.dtype, s0_std=w.s0_std)
     x = {key: (val.to(dev) if val is not None else None) for key, val in d.items()}
     o = torch.empty(w.B, w.T, w.H, w.V, device=dev)
     sT = torch.empty(w.B, w.H, w.K, w.V, device=dev)
 
     def step():
-        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], None, chunk=w.chunk,
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], chunk=w.chunk,
                       final_state=sT, out=o)
+
+    if args.only == "prefill":
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "prefill", "workload": w.name, "launches": args.steps}),
+              flush=True)
+        return
 
     ms, wall = time_launches(step, args.steps, args.warmup, stream)
     tokens = w.B * w.T
-    alg_b = prefill_alg_bytes(w.B, w.T, w.H, w.K, w.V, s0=False, sT=True)
+    alg_b = prefill_alg_bytes(w.B, w.T, w.H, w.K, w.V, s0=w.s0_std is not None, sT=True)
     alg_f = prefill_alg_flops(w.B, w.T, w.H, w.K, w.V, w.chunk)
     achieved = alg_b / (ms * 1e-3) / 1e9
     traffic = measured_traffic("chunk_mfma_kernel", alg_b)
@@ -170,7 +234,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16 in, f16 MFMA operands, f32 accumulate/state/out",
         "data": "synthetic",
-        "config": {"workload": PREFILL, "B": w.B, "T": w.T, "H": w.H, "d_k": w.K, "d_v": w.V,
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d_k": w.K, "d_v": w.V,
                    "chunk": w.chunk, "global_batch": w.B, "seq_len": w.T,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -184,33 +248,7 @@ def main():
 
     # ---- decode leg
     if not args.no_decode:
-        wd = inputs.WORKLOADS[DECODE]
-        state = inputs.draw_decode_state(wd.seed, wd.N, wd.H, wd.K, wd.V, wd.s0_std).to(dev)
-        nin = 8
-        steps_in = [{k2: v2.to(dev) for k2, v2 in
-                     inputs.draw_decode_step(wd.seed, s, wd.N, wd.H, wd.K, wd.V, wd.dtype).items()}
-                    for s in range(nin)]
-        od = torch.empty(wd.N, wd.H, wd.V, device=dev)
-        ctr = [0]
-
-        def dstep():
-            xi = steps_in[ctr[0] % nin]
-            ctr[0] += 1
-            kda.decode_step(xi["q"], xi["k"], xi["v"], xi["g"], xi["beta"], state, out=od)
-
-        dms, dwall = time_launches(dstep, args.decode_steps, 3, stream)
-        db = decode_alg_bytes(wd.N, wd.H, wd.K, wd.V)
-        dach = db / (dms * 1e-3) / 1e9
-        result["decode"] = {
-            "workload": DECODE, "value": wd.N / (dms * 1e-3), "unit": "tokens/s",
-            "ms_per_step": dms, "steps": args.decode_steps,
-            "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dach / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("decode_step_kernel", db),
-                         "kernel": "decode_step_kernel", "alg_bytes_per_launch": db},
-        }
-        del state, steps_in
-
+        result["decode"] = decode_leg(args, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, w)
     print(json.dumps(result), flush=True)

@@ -34,14 +34,10 @@
 //    chunk c+1, they form its Gram and query-key blocks and the 16 x 16
 //    diagonal inverses (I + A_ii)^-1 in fp32.
 // Two workgroup barriers per chunk separate these phases.
-#include "kda_common.hpp"
+#include "kda_mfma.hpp"
 
 namespace kda {
 namespace {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;    // chunk length
 constexpr int KD = 128;  // key dimension
@@ -50,17 +46,19 @@ constexpr int VT = 64;   // value columns per workgroup
 constexpr int NT = 768;  // threads per workgroup: 4 state waves + 8 prep waves
 constexpr int NP = 8;    // prep waves
 constexpr int PK = 136;  // LDS pitch (halves) of [64][128] fp16 tiles
-constexpr int PC = 72;   // LDS pitch (halves) of [*][64] fp16 tiles
-constexpr int PI = 24;   // LDS pitch (halves) of 16 x 16 fp16 blocks
+constexpr int PC = 72;   // LDS pitch (halves) of [*][64] fp16 tiles read as 16-byte fragments
+constexpr int P4 = 76;   // LDS pitch (halves) of [64][64] fp16 tiles read as 8-byte fragments
+constexpr int PI = 20;   // LDS pitch (halves) of 16 x 16 fp16 blocks
 constexpr int PF = 17;   // LDS pitch (floats) of 16 x 16 fp32 blocks
 
 struct Smem {
     _Float16 kp[C * PK];        // Kp [s][c]
     _Float16 qp[C * PK];        // Qp [s][c]
     _Float16 km[C * PK];        // Km [s][c]   (Gram / query-key B operand)
-    _Float16 kmt[2][KD * PC];   // Km^T [c][s] (state-advance A operand), by chunk parity
-    _Float16 a16[C * PC];       // A [r][s], lower blocks
-    _Float16 p[C * PC];         // P [r][s], lower blocks
+    _Float16 kmt[2][KD * PC];   // Km^T [c][s] (state-advance A operand), by chunk parity;
+                                // 8-token column blocks XOR-swizzled by (c >> 3) & 7
+    _Float16 a16[C * P4];       // A [r][s], lower blocks
+    _Float16 p[C * P4];         // P [r][s], lower blocks
     _Float16 tii[4][16 * PI];   // (I + A_ii)^-1, diagonal blocks
     uint16_t v[C * PC];         // bf16 V tile [r][j]
     float beta[C];
@@ -72,68 +70,48 @@ struct Smem {
     float gsum[NP][KD];         // prep waves: per-wave channel sums of g (next chunk)
 };
 
-__device__ __forceinline__ floatx4 mma32(half8 a, half8 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+// frag8 from the swizzled Km^T tile: row c, logical 8-token block kb = 4 ks + (lane >> 4)
+// stored at block kb ^ ((c >> 3) & 7).
+__device__ __forceinline__ half8 frag8_kmt(const _Float16 *base, int row0, int ks, int lane) {
+    const int c = row0 + (lane & 15);
+    const int kb = (4 * ks + (lane >> 4)) ^ ((c >> 3) & 7);
+    return *reinterpret_cast<const half8 *>(base + c * PC + 8 * kb);
 }
-__device__ __forceinline__ floatx4 mma16(half4 a, half4 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-
-// 16x16x32 operand fragment of rows row0..row0+15, k = k0..k0+31 from a
-// row-major [rows][k] fp16 tile: lane holds row (lane & 15), k = k0 + 8 (lane >> 4) .. +7.
-__device__ __forceinline__ half8 frag8(const _Float16 *base, int pitch, int row0, int k0,
-                                       int lane) {
-    return *reinterpret_cast<const half8 *>(base + (row0 + (lane & 15)) * pitch + k0 +
-                                            8 * (lane >> 4));
-}
-// 16x16x16 operand fragment: lane holds row (lane & 15), k = k0 + 4 (lane >> 4) .. +3.
-__device__ __forceinline__ half4 frag4(const _Float16 *base, int pitch, int row0, int k0,
-                                       int lane) {
-    return *reinterpret_cast<const half4 *>(base + (row0 + (lane & 15)) * pitch + k0 +
-                                            4 * (lane >> 4));
-}
-// An accumulator block (rows 4 (lane >> 4) + i, column lane & 15) as fp16: this
-// is also the B fragment of a following 16x16x16 product with k = those rows.
-__device__ __forceinline__ half4 to_half4(floatx4 x) {
-    half4 h;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = (_Float16)x[i];
-    return h;
-}
-
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ void unpack8(const uint4 &u, float *x) {
-    x[0] = bf16lo(u.x); x[1] = bf16hi(u.x); x[2] = bf16lo(u.y); x[3] = bf16hi(u.y);
-    x[4] = bf16lo(u.z); x[5] = bf16hi(u.z); x[6] = bf16lo(u.w); x[7] = bf16hi(u.w);
-}
-
-// One chunk's inputs, held in a prep wave's registers one chunk ahead.
+// One chunk's inputs, held in a prep wave's registers ahead of use.
 // Lane (cg = lane & 15, tb = lane >> 4) of prep wave p holds channels
 // 8 cg .. 8 cg + 7 of tokens 8p + 2 tb and 8p + 2 tb + 1, so each wave reads
-// whole 256-byte rows.
+// whole 256-byte rows.  g is fetched one phase earlier than the rest because
+// its running sum is needed first.
 struct Raw {
-    uint4 q[2], k[2], g[2];
+    uint4 q[2], k[2];
     uint4 v;         // V tile piece: row idx >> 3, columns 8 (idx & 7) .., idx = 64p + lane
     uint32_t beta;   // prep wave 0: beta of token lane
 };
 
+__device__ __forceinline__ void load_g(uint4 *rg, const uint16_t *g, int c0, int L, int H, int h,
+                                       int p, int lane) {
+    const int cg = lane & 15, tb = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int r = 8 * p + 2 * tb + u;
+        rg[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (r < L) rg[u] = *reinterpret_cast<const uint4 *>(g + ((size_t)(c0 + r) * H + h) * KD + 8 * cg);
+    }
+}
+
 __device__ __forceinline__ void load_raw(Raw &R, const uint16_t *q, const uint16_t *k,
-                                         const uint16_t *g, const uint16_t *v,
-                                         const uint16_t *beta, int c0, int L, int H, int h,
-                                         int vt, int p, int lane) {
+                                         const uint16_t *v, const uint16_t *beta, int c0, int L,
+                                         int H, int h, int vt, int p, int lane) {
     const int cg = lane & 15, tb = lane >> 4;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int r = 8 * p + 2 * tb + u;
         R.q[u] = make_uint4(0u, 0u, 0u, 0u);
         R.k[u] = R.q[u];
-        R.g[u] = R.q[u];
         if (r < L) {
             const size_t off = ((size_t)(c0 + r) * H + h) * KD + 8 * cg;
             R.q[u] = *reinterpret_cast<const uint4 *>(q + off);
             R.k[u] = *reinterpret_cast<const uint4 *>(k + off);
-            R.g[u] = *reinterpret_cast<const uint4 *>(g + off);
         }
     }
     const int idx = 64 * p + lane;
@@ -144,18 +122,19 @@ __device__ __forceinline__ void load_raw(Raw &R, const uint16_t *q, const uint16
     R.beta = (p == 0 && lane < L) ? beta[(size_t)(c0 + lane) * H + h] : 0u;
 }
 
-// Prep wave p, first half of the running log-decay sum: inclusive scan over
-// the wave's four token pairs (lanes 16 apart share channels).  The wave's
-// channel totals go to LDS; ex keeps the in-wave exclusive prefix.
-__device__ __forceinline__ void scan_partials(Smem &sm, const Raw &R, int p, int lane,
-                                              float *ex) {
+// Prep wave p, first half of the running log-decay sum: lc = running sum over
+// this lane's two tokens, then an inclusive scan over the wave's four token
+// pairs (lanes 16 apart share channels).  The wave's channel totals go to LDS;
+// ex keeps the in-wave exclusive prefix.
+__device__ __forceinline__ void scan_partials(Smem &sm, const uint4 *rg, int p, int lane,
+                                              float (*lc)[8], float *ex) {
     const int cg = lane & 15, tb = lane >> 4;
-    float g0[8], g1[8];
-    unpack8(R.g[0], g0);
-    unpack8(R.g[1], g1);
+    unpack8(rg[0], lc[0]);
+    unpack8(rg[1], lc[1]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float loc = g0[e] + g1[e];
+        lc[1][e] += lc[0][e];
+        const float loc = lc[1][e];
         float s = loc;
         float x = __shfl_up(s, 16);
         if (tb >= 1) s += x;
@@ -169,13 +148,11 @@ __device__ __forceinline__ void scan_partials(Smem &sm, const Raw &R, int p, int
 // Prep wave p, second half: combine the wave totals into G - G_m for this
 // lane's tokens and write the fp16 operand tiles of the chunk.
 __device__ __forceinline__ void prologue(Smem &sm, const Raw &R, int par, int p, int lane,
-                                         const float *ex) {
+                                         const float (*lc)[8], const float *ex) {
     const int cg = lane & 15, tb = lane >> 4;
     const int ch0 = 8 * cg;
     const int r0 = 8 * p + 2 * tb;
-    float g0[8], g1[8], kv0[8], kv1[8], qv0[8], qv1[8];
-    unpack8(R.g[0], g0);
-    unpack8(R.g[1], g1);
+    float kv0[8], kv1[8], qv0[8], qv1[8];
     unpack8(R.k[0], kv0);
     unpack8(R.k[1], kv1);
     unpack8(R.q[0], qv0);
@@ -213,7 +190,7 @@ __device__ __forceinline__ void prologue(Smem &sm, const Raw &R, int par, int p,
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float pre = ex[e] + (p < 4 ? -d[e] : d[e]);
-        const float G0 = pre + g0[e], G1 = G0 + g1[e];  // G - G_m
+        const float G0 = pre + lc[0][e], G1 = pre + lc[1][e];  // G - G_m
         const float f0 = fast_exp(G0), f1 = fast_exp(G1);
         const float i0 = __builtin_amdgcn_rcpf(f0), i1 = __builtin_amdgcn_rcpf(f1);
         hkp0[e] = (_Float16)(kv0[e] * f0);
@@ -231,11 +208,11 @@ __device__ __forceinline__ void prologue(Smem &sm, const Raw &R, int par, int p,
     *reinterpret_cast<half8 *>(&sm.qp[(r0 + 1) * PK + ch0]) = hqp1;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-        half2_t pr;
+        half2v pr;
         pr[0] = hkm0[e];
         pr[1] = hkm1[e];
-        *reinterpret_cast<half2_t *>(&sm.kmt[par][(ch0 + e) * PC + r0]) = pr;
+        // column block p of row ch0 + e, swizzled by the row's channel group cg
+        *reinterpret_cast<half2v *>(&sm.kmt[par][(ch0 + e) * PC + 8 * (p ^ (cg & 7)) + 2 * tb]) = pr;
     }
     const int idx = 64 * p + lane;
     *reinterpret_cast<uint4 *>(&sm.v[(idx >> 3) * PC + 8 * (idx & 7)]) = R.v;
@@ -268,23 +245,36 @@ __device__ __forceinline__ void prep_blocks(Smem &sm, int p, int lane) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * lg + i;
-            sm.p[(16 * p + r) * PC + 16 * p + l16] = (_Float16)(l16 <= r ? pq[i] : 0.f);
+            sm.p[(16 * p + r) * P4 + 16 * p + l16] = (_Float16)(l16 <= r ? pq[i] : 0.f);
         }
-        // (I + A_pp)^-1 by forward substitution, one column per lane (lanes
-        // 16..63 repeat lanes 0..15 so the wave stays convergent; 0..15 store)
-        const int j = l16;
-        float tc[16];
+        // (I + A_pp)^-1 by forward substitution: the quad of lanes 4j..4j+3
+        // owns column j; lane q of the quad sums the terms s = q (mod 4), a
+        // quad butterfly completes each row, and lane r & 3 keeps t_r.
+        const int j = lane >> 2, q = lane & 3;
+        float coef[4][16];               // A[r][s] for this lane's s = 4m + q (0 when s >= r)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                coef[m][r] = (4 * m < r) ? ad[r * PF + 4 * m + q] : 0.f;  // s = 4m + q
+        float t_own[4];                  // t_s for s = 4m + q
+#pragma unroll
+        for (int m = 0; m < 4; ++m) t_own[m] = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float acc = (r == j) ? 1.f : 0.f;
+            float part = 0.f;
 #pragma unroll
-            for (int s = 0; s < r; ++s) acc -= ad[r * PF + s] * tc[s];
-            tc[r] = acc;
+            for (int m = 0; m < 4; ++m)
+                if (4 * m < r) part += coef[m][r] * t_own[m];
+            part += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                                  __builtin_bit_cast(int, part), 0xB1, 0xF, 0xF, true));
+            part += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                                  __builtin_bit_cast(int, part), 0x4E, 0xF, 0xF, true));
+            const float tr = (r == j ? 1.f : 0.f) - part;
+            if ((r & 3) == q) t_own[r >> 2] = tr;
         }
-        if (lane < 16) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.tii[p][r * PI + j] = (_Float16)tc[r];
-        }
+        for (int m = 0; m < 4; ++m) sm.tii[p][(4 * m + q) * PI + j] = (_Float16)t_own[m];
     } else {
 #pragma unroll
         for (int tsk = 0; tsk < 3; ++tsk) {
@@ -298,9 +288,9 @@ __device__ __forceinline__ void prep_blocks(Smem &sm, int p, int lane) {
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * bi + 4 * lg + i, s = 16 * bj + l16;
                 if (gram)
-                    sm.a16[r * PC + s] = (_Float16)(sm.beta[r] * acc[i]);
+                    sm.a16[r * P4 + s] = (_Float16)(sm.beta[r] * acc[i]);
                 else
-                    sm.p[r * PC + s] = (_Float16)acc[i];
+                    sm.p[r * P4 + s] = (_Float16)acc[i];
             }
         }
     }
@@ -389,7 +379,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
                 floatx4 z = Y[i];
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < i; ++j) acc = mma16(frag4(sm.a16, PC, 16 * i, 16 * j, lane), U[j], acc);
+                for (int j = 0; j < i; ++j) acc = mma16(frag4(sm.a16, P4, 16 * i, 16 * j, lane), U[j], acc);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) z[e] -= acc[e];
                 const floatx4 u = mma16(frag4(sm.tii[i], PI, 0, 0, lane), to_half4(z),
@@ -401,7 +391,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
-                for (int i = 0; i <= rb; ++i) O[rb] = mma16(frag4(sm.p, PC, 16 * rb, 16 * i, lane), U[i], O[rb]);
+                for (int i = 0; i <= rb; ++i) O[rb] = mma16(frag4(sm.p, P4, 16 * rb, 16 * i, lane), U[i], O[rb]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * rb + 4 * lg + e;
@@ -417,7 +407,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             for (int cb = 0; cb < 8; ++cb) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    S[cb] = mma32(frag8(sm.kmt[par], PC, 16 * cb, 32 * ks, lane), bu[ks], S[cb]);
+                    S[cb] = mma32(frag8_kmt(sm.kmt[par], 16 * cb, ks, lane), bu[ks], S[cb]);
                 const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.fc[par][16 * cb + 4 * lg]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[cb][i] *= f[i];
@@ -433,33 +423,38 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
     } else {
         const int p = w - 4;
         Raw R;
-        float ex[8];
+        uint4 rg[2];
+        float lc[2][8], ex[8];
         if (nchunks > 0) {
-            load_raw(R, q, k, g, v, beta, bos, min(C, eos - bos), H, h, vt, p, lane);
-            scan_partials(sm, R, p, lane, ex);
+            load_g(rg, g, bos, min(C, eos - bos), H, h, p, lane);
+            load_raw(R, q, k, v, beta, bos, min(C, eos - bos), H, h, vt, p, lane);
+            scan_partials(sm, rg, p, lane, lc, ex);
+            if (nchunks > 1) load_g(rg, g, bos + C, min(C, eos - bos - C), H, h, p, lane);
         }
         __syncthreads();
         if (nchunks > 0) {
-            prologue(sm, R, 0, p, lane, ex);
+            prologue(sm, R, 0, p, lane, lc, ex);
             if (nchunks > 1)
-                load_raw(R, q, k, g, v, beta, bos + C, min(C, eos - bos - C), H, h, vt, p, lane);
+                load_raw(R, q, k, v, beta, bos + C, min(C, eos - bos - C), H, h, vt, p, lane);
         }
         __syncthreads();
         for (int ci = 0; ci < nchunks; ++ci) {
-            const int c0 = bos + ci * C;
-            const bool next = ci + 1 < nchunks;
-            // ---- phase A: this chunk's Gram / query-key blocks and diagonal
-            // inverses; the next chunk's per-wave decay sums
-            if (next) scan_partials(sm, R, p, lane, ex);
+            const bool next = ci + 1 < nchunks, next2 = ci + 2 < nchunks;
+            const int c2 = bos + (ci + 2) * C;
+            // ---- phase A: the next chunk's per-wave decay sums (then fetch g
+            // two chunks ahead), and this chunk's Gram / query-key blocks and
+            // diagonal inverses
+            if (next) {
+                scan_partials(sm, rg, p, lane, lc, ex);
+                if (next2) load_g(rg, g, c2, min(C, eos - c2), H, h, p, lane);
+            }
             prep_blocks(sm, p, lane);
             __syncthreads();
-            // ---- phase B: operands of the next chunk; then fetch the one after it
+            // ---- phase B: operands of the next chunk; then fetch the rest of
+            // the chunk after it
             if (next) {
-                prologue(sm, R, (ci & 1) ^ 1, p, lane, ex);
-                if (ci + 2 < nchunks) {
-                    const int cn = c0 + 2 * C;
-                    load_raw(R, q, k, g, v, beta, cn, min(C, eos - cn), H, h, vt, p, lane);
-                }
+                prologue(sm, R, (ci & 1) ^ 1, p, lane, lc, ex);
+                if (next2) load_raw(R, q, k, v, beta, c2, min(C, eos - c2), H, h, vt, p, lane);
             }
             __syncthreads();
         }
