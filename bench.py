@@ -3,14 +3,18 @@
 
 One JSON line on stdout.  A step is one chunked forward pass (kda_chunk_fwd)
 over the prefill workload B=1, H=8, T=4096, d_k=d_v=128, chunk 64, bf16
-inputs with fp32 state, accumulation and output; `value` is its tokens/s.
-The decode leg (one token for each of 256 sequences x 32 heads, persistent
-fp32 state, kda_decode_step) is reported in the same line under "decode".
+inputs with fp32 state, accumulation and output, on the implementation the
+library recommends for it (kda_workspace_bytes > 0: the two-pass path, three
+launches: chunk offsets, the intra-chunk pass over all chunks, the sequential
+state pass); `value` is its tokens/s.  The single-pass fused kernel's time on
+the same workload is reported alongside.  The decode leg (one token for each
+of 256 sequences x 32 heads, persistent fp32 state, kda_decode_step) is
+reported in the same line under "decode".
 
 Inputs are synthetic and already resident in HBM when the timed region starts.
-The roofline objects price each kernel's ALGORITHMIC bytes (and flops) per
-launch against MI355X peaks (HBM 8 TB/s; dense fp16/bf16 MFMA 2.5 PFLOP/s);
-kernel time comes from HIP events on the stream the kernels run on.
+The roofline objects price the ALGORITHMIC bytes (and flops) of one forward
+call against MI355X peaks (HBM 8 TB/s; dense fp16/bf16 MFMA 2.5 PFLOP/s);
+call time comes from HIP events on the stream the kernels run on.
 The cpu_baseline leg times the fp64 oracle on the host cores.
 """
 
@@ -30,6 +34,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 PREFILL = "prefill_bf16_B1_H8_T4096"
 DECODE = "decode_bf16_N256_H32"
+DECODE_TAG = "decode_N256_H32"
 
 
 def prefill_alg_bytes(B, T, H, K, V, in_bytes=2, out_bytes=4, s0=False, sT=True):
@@ -62,11 +67,12 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, launches_bytes):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    (profiles/<kernel>_traffic.md), or None when that summary was taken on a
-    different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.md")
+def measured_traffic(stem):
+    """HBM bytes per call from the committed rocprofv3 counter summary
+    (profiles/<stem>_traffic.md: FETCH_SIZE + WRITE_SIZE summed over the
+    call's kernels, scaled by the plain-copy calibration), or None when that
+    summary was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{stem}_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -147,7 +153,7 @@ def decode_leg(args, dev, stream):
         "ms_per_step": dms, "steps": args.decode_steps,
         "roofline": {"bound": "hbm", "achieved": dach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": dach / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("decode_step_kernel", db),
+                     "traffic": measured_traffic(f"decode_step_kernel_{DECODE_TAG}"),
                      "kernel": "decode_step_kernel", "alg_bytes_per_launch": db},
     }
 
@@ -202,10 +208,19 @@ def main():
     x = {key: (val.to(dev) if val is not None else None) for key, val in d.items()}
     o = torch.empty(w.B, w.T, w.H, w.V, device=dev)
     sT = torch.empty(w.B, w.H, w.K, w.V, device=dev)
+    nws = kda.workspace_bytes(w.B, w.B * w.T, w.H, w.K, w.V, w.chunk)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    path = "two-pass" if nws else "fused single-pass"
+    kernels = ("chunk_offsets_kernel + chunk_prep_kernel + chunk_state_kernel" if nws
+               else "chunk_mfma_kernel")
 
     def step():
         kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], chunk=w.chunk,
-                      final_state=sT, out=o)
+                      final_state=sT, out=o, workspace=ws)
+
+    def step_fused():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], chunk=w.chunk,
+                      final_state=sT, out=o, two_pass=False)
 
     if args.only == "prefill":
         for _ in range(args.steps):
@@ -216,11 +231,13 @@ def main():
         return
 
     ms, wall = time_launches(step, args.steps, args.warmup, stream)
+    ms_fused, _ = time_launches(step_fused, max(5, args.steps // 5), 2, stream) if nws else (ms, 0)
     tokens = w.B * w.T
     alg_b = prefill_alg_bytes(w.B, w.T, w.H, w.K, w.V, s0=w.s0_std is not None, sT=True)
     alg_f = prefill_alg_flops(w.B, w.T, w.H, w.K, w.V, w.chunk)
     achieved = alg_b / (ms * 1e-3) / 1e9
-    traffic = measured_traffic("chunk_mfma_kernel", alg_b)
+    tag = w.name.replace("prefill_bf16_", "prefill_").replace("batched_bf16_", "batched_")
+    traffic = measured_traffic(("kda_chunk_fwd_two_pass_" if nws else "chunk_mfma_kernel_") + tag)
     result = {
         "metric": "KDA fwd tokens/s (prefill, decode) + % of MFMA/HBM roofline, 1 MI355X",
         "value": tokens / (ms * 1e-3),
@@ -239,11 +256,14 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "chunk_mfma_kernel", "alg_bytes_per_launch": alg_b},
+                     "kernel": f"kda_chunk_fwd {path}: {kernels}",
+                     "alg_bytes_per_launch": alg_b},
         "roofline_mfma": {"achieved": alg_f / (ms * 1e-3) / 1e12, "peak": MFMA_F16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": alg_f / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
                           "flops": "algorithmic", "alg_flops_per_launch": alg_f},
         "wall_s_timed_region": wall,
+        "path": path,
+        "fused_single_pass_ms_per_step": ms_fused,
     }
 
     # ---- decode leg

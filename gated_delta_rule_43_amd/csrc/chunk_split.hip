@@ -1,0 +1,699 @@
+// chunk_split.hip -- two-pass bf16 KDA forward for few (sequence, head) units.
+//
+// Same recurrence and chunk algebra as chunk_mfma.hip ("Kimi K3: Open
+// Frontier Intelligence and Implementation Framework", section "Hybrid
+// Attention Mechanism": delta rule with a channel-wise forget gate whose
+// lower-bounded decay lets intra- and inter-chunk tiles run as dense
+// products), reorganised for workloads whose sequential chains are too few to
+// fill the GPU.  Everything that does not depend on the state is computed
+// first, for all chunks at once; the sequential pass is then a short chain.
+//
+// With Kp, Km, Qp, A, P, G_m and G_C as in chunk_mfma.hip and
+// T = (I + A)^-1 Diag(beta) (never formed):
+//   W  = T Kp,   U~ = T V,   Q^ = Qp - P W,   O^ = P U~          (pass 1)
+//   S' = Diag(exp(G_m)) S
+//   U  = U~ - W S',   O = Q^ S' + O^,   S <- Diag(exp(G_C - G_m)) (S' + Km^T U)   (pass 2)
+// (substituting U into O = Qp S' + P U gives the pass-2 form).
+//
+// Pass 1 (chunk_prep_kernel): one workgroup of 4 waves per (chunk, head),
+// all chunks in parallel.  Pass 2 (chunk_state_kernel): one workgroup per
+// (sequence, head, 16-column value tile); one state wave runs the chain with
+// the state in registers while seven loader waves stream the next chunk's
+// W, Q^, Km^T tiles into double-buffered LDS with direct loads.
+// Intermediates live in the caller's workspace.
+#include "kda_mfma.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int C = 64, KD = 128, VD = 128;
+constexpr int STATE_WAVES = 1;   // state waves per workgroup in pass 2
+constexpr int LOADER_WAVES = 7;  // tile-streaming waves per workgroup in pass 2
+constexpr int PK = 136;  // LDS pitch (halves), [64][128] fp16 tiles
+constexpr int PC = 72;   // LDS pitch (halves), [128][64] tiles read as 16-byte fragments
+constexpr int P4 = 76;   // LDS pitch (halves), [64][64] tiles read as 8-byte fragments
+constexpr int PI = 20;   // LDS pitch (halves), 16 x 16 fp16 blocks
+constexpr int PF = 17;   // LDS pitch (floats), 16 x 16 fp32 blocks
+
+// Per-(chunk, head) record in the workspace (bytes).  The contraction index
+// of W, Q^ (c) and Km^T (s) is stored permuted within each 32-wide block,
+// see kperm_pos below.
+constexpr size_t R_W = 0;             // fp16 [64][128]  W     [r][c]
+constexpr size_t R_QH = 16384;        // fp16 [64][128]  Q^    [r][c]
+constexpr size_t R_KMT = 32768;       // fp16 [128][64]  Km^T  [c][s]
+constexpr size_t R_UT = 49152;        // fp16 [128][64]  U~    [j][r]
+constexpr size_t R_OH = 65536;        // fp32 [128][64]  O^    [j][r]
+constexpr size_t R_FM = 98304;        // fp32 [128]      exp(G_m)
+constexpr size_t R_FC = 98816;        // fp32 [128]      exp(G_C - G_m)
+constexpr size_t REC = 99328;
+constexpr size_t OFFS_BYTES = 512;    // int32 chunk offsets, up to 127 sequences
+
+// The pass-2 products contract over an index (c for W S' and Q^ S', s for
+// Km^T U) whose right operand comes straight out of MFMA accumulators: lane l
+// holds rows 4 (l >> 4) .. +3 of each 16-row block.  A 16x16x32 B fragment
+// wants 8 k values per lane; taking the lane's rows of blocks 2 ks and
+// 2 ks + 1 as those 8 values leaves the state in registers, provided the left
+// operand's k values are laid out in the same order.  Within each 32-wide
+// block, stored position 8 g + t holds logical index 4 g + t (t < 4) or
+// 16 + 4 g + t - 4 (t >= 4); kperm_pos gives the stored position of the
+// logical 4-group [4 q, 4 q + 4).
+__device__ __forceinline__ int kperm_pos(int q) {
+    return 32 * (q >> 3) + 8 * (q & 3) + 4 * ((q >> 2) & 1);
+}
+
+// ---------------------------------------------------------------- offsets
+// offs[n] = first chunk of sequence n in the packed chunk list, clamped so that
+// the list never exceeds `cap` chunks (malformed offsets cannot overrun the
+// workspace).
+__global__ void chunk_offsets_kernel(const int32_t *cu, int fixedT, int N, int totalT, int cap,
+                                     int32_t *offs) {
+    if (threadIdx.x != 0) return;
+    int acc = 0;
+    offs[0] = 0;
+    for (int n = 0; n < N; ++n) {
+        int bos, eos;
+        seq_bounds(cu, n, fixedT, totalT, bos, eos);
+        acc += (eos - bos + C - 1) / C;
+        if (acc > cap) acc = cap;
+        offs[n + 1] = acc;
+    }
+}
+
+// ---------------------------------------------------------------- pass 1
+struct PrepSmem {
+    _Float16 kp[C * PK];    // Kp [s][c]
+    _Float16 qp[C * PK];    // Qp [s][c], then Q^ in place
+    _Float16 km[C * PK];    // Km [s][c], then W
+    uint16_t v[C * PK];     // bf16 V tile [r][j]
+    _Float16 a16[C * P4];   // A [r][s], off-diagonal lower blocks
+    _Float16 p[C * P4];     // P [r][s], lower blocks
+    _Float16 tii[4][16 * PI];
+    float ad[4][16 * PF];   // diagonal A blocks, fp32
+    float beta[C];
+    float gsum[4][KD];      // per-wave channel sums of g
+};
+
+__device__ __forceinline__ floatx4 block32(const _Float16 *lhs, const _Float16 *rhs, int bi, int bj,
+                                           int lane) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        acc = mma32(frag8(lhs, PK, 16 * bi, 32 * ks, lane), frag8(rhs, PK, 16 * bj, 32 * ks, lane), acc);
+    return acc;
+}
+
+__global__ __launch_bounds__(256) void chunk_prep_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, const uint16_t *__restrict__ g,
+    const uint16_t *__restrict__ beta, const int32_t *__restrict__ cu, int fixedT, int N, int H,
+    int totalT, unsigned char *__restrict__ ws) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    PrepSmem &sm = *reinterpret_cast<PrepSmem *>(smem_raw);
+    const int32_t *offs = reinterpret_cast<const int32_t *>(ws);
+    const int gc = blockIdx.x, h = blockIdx.y;
+    if (gc >= offs[N]) return;
+    int n = 0;
+    while (n + 1 < N && offs[n + 1] <= gc) ++n;
+    int bos, eos;
+    seq_bounds(cu, n, fixedT, totalT, bos, eos);
+    const int c0 = bos + (gc - offs[n]) * C;
+    const int L = min(C, eos - c0);
+    // records of one head are contiguous, in chunk order
+    unsigned char *rec = ws + OFFS_BYTES + ((size_t)h * gridDim.x + gc) * REC;
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int cg = t & 15, rg = t >> 4;  // channels 8 cg .., rows 4 rg .. 4 rg + 3
+
+    // ---- loads and the running log-decay sum
+    uint4 rq[4], rk[4], rgv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = 4 * rg + u;
+        rq[u] = make_uint4(0u, 0u, 0u, 0u);
+        rk[u] = rq[u];
+        rgv[u] = rq[u];
+        if (r < L) {
+            const size_t off = ((size_t)(c0 + r) * H + h) * KD + 8 * cg;
+            rq[u] = *reinterpret_cast<const uint4 *>(q + off);
+            rk[u] = *reinterpret_cast<const uint4 *>(k + off);
+            rgv[u] = *reinterpret_cast<const uint4 *>(g + off);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = 256 * e + t, r = idx >> 4;
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (r < L) x = *reinterpret_cast<const uint4 *>(v + ((size_t)(c0 + r) * H + h) * VD + 8 * (idx & 15));
+        *reinterpret_cast<uint4 *>(&sm.v[r * PK + 8 * (idx & 15)]) = x;
+    }
+    if (t < C) sm.beta[t] = t < L ? __uint_as_float((uint32_t)beta[(size_t)(c0 + t) * H + h] << 16) : 0.f;
+
+    float G[4][8], ex[8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) unpack8(rgv[u], G[u]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        G[1][e] += G[0][e];
+        G[2][e] += G[1][e];
+        G[3][e] += G[2][e];
+        const float tot = G[3][e];
+        float s = tot;
+        float x = __shfl_up(s, 16);
+        if (lg >= 1) s += x;
+        x = __shfl_up(s, 32);
+        if (lg >= 2) s += x;
+        ex[e] = s - tot;
+        if (lg == 3) sm.gsum[w][8 * cg + e] = s;
+    }
+    __syncthreads();
+    {
+        float kv[4][8], qv[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            unpack8(rk[u], kv[u]);
+            unpack8(rq[u], qv[u]);
+        }
+        half4 kmT[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int ch = 8 * cg + e;
+            const float s0w = sm.gsum[0][ch], s1w = sm.gsum[1][ch], s2w = sm.gsum[2][ch],
+                        s3w = sm.gsum[3][ch];
+            const float gm = s0w + s1w;                 // G at token 31 (end of wave 1's rows)
+            const float gcl = gm + s2w + s3w;           // G at token 63
+            float pre = ex[e] - gm;
+            if (w >= 1) pre += s0w;
+            if (w >= 2) pre += s1w;
+            if (w >= 3) pre += s2w;
+            if (rg == 0) {
+                reinterpret_cast<float *>(rec + R_FM)[ch] = fast_exp(gm);
+                reinterpret_cast<float *>(rec + R_FC)[ch] = fast_exp(gcl - gm);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float f = fast_exp(pre + G[u][e]);  // exp(G - G_m)
+                const float fi = __builtin_amdgcn_rcpf(f);
+                const int r = 4 * rg + u;
+                sm.kp[r * PK + ch] = (_Float16)(kv[u][e] * f);
+                sm.qp[r * PK + ch] = (_Float16)(qv[u][e] * f);
+                const _Float16 m = (_Float16)(kv[u][e] * fi);
+                sm.km[r * PK + ch] = m;
+                kmT[e][u] = m;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            *reinterpret_cast<half4 *>(rec + R_KMT + 2 * ((size_t)(8 * cg + e) * C + kperm_pos(rg))) = kmT[e];
+    }
+    __syncthreads();
+
+    // ---- Gram / query-key blocks: wave w takes the diagonal blocks (w, w) and
+    // three of the twelve off-diagonal blocks, then inverts I + A_ww.
+    {
+        const floatx4 a = block32(sm.kp, sm.km, w, w, lane);
+        float *ad = sm.ad[w];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lg + i;
+            ad[r * PF + l16] = l16 < r ? sm.beta[16 * w + r] * a[i] : 0.f;
+        }
+        const floatx4 pq = block32(sm.qp, sm.km, w, w, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lg + i;
+            sm.p[(16 * w + r) * P4 + 16 * w + l16] = (_Float16)(l16 <= r ? pq[i] : 0.f);
+        }
+#pragma unroll
+        for (int tsk = 0; tsk < 3; ++tsk) {
+            const int o = 3 * w + tsk, oo = o % 6;
+            const bool gram = o < 6;
+            const int bi = oo < 1 ? 1 : (oo < 3 ? 2 : 3);
+            const int bj = oo < 1 ? 0 : (oo < 3 ? oo - 1 : oo - 3);
+            const floatx4 acc = block32(gram ? sm.kp : sm.qp, sm.km, bi, bj, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * bi + 4 * lg + i, s = 16 * bj + l16;
+                if (gram)
+                    sm.a16[r * P4 + s] = (_Float16)(sm.beta[r] * acc[i]);
+                else
+                    sm.p[r * P4 + s] = (_Float16)acc[i];
+            }
+        }
+        // (I + A_ww)^-1: quad 4j..4j+3 owns column j, lane q sums s = q (mod 4)
+        const int j = lane >> 2, qd = lane & 3;
+        float coef[4][16];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) coef[m][r] = (4 * m < r) ? ad[r * PF + 4 * m + qd] : 0.f;
+        float t_own[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float part = 0.f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                if (4 * m < r) part += coef[m][r] * t_own[m];
+            part += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, part), 0xB1, 0xF, 0xF, true));
+            part += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, part), 0x4E, 0xF, 0xF, true));
+            const float tr = (r == j ? 1.f : 0.f) - part;
+            if ((r & 3) == qd) t_own[r >> 2] = tr;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) sm.tii[w][(4 * m + qd) * PI + j] = (_Float16)t_own[m];
+    }
+    __syncthreads();
+
+    // ---- (I + A) [W | U~] = Diag(beta) [Kp | V] by 16-row block substitution.
+    // Waves 0, 1 solve for the Kp columns (W), waves 2, 3 for the V columns (U~);
+    // each wave owns four 16-column blocks.
+    const bool wside = w < 2;
+    floatx4 X[4][4];  // [column block][row block], fp32
+    half4 Xh[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int col = 64 * (w & 1) + 16 * b + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            floatx4 z;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * i + 4 * lg + e;
+                const float xv = wside ? (float)sm.kp[r * PK + col]
+                                       : __uint_as_float((uint32_t)sm.v[r * PK + col] << 16);
+                z[e] = sm.beta[r] * xv;
+            }
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < i; ++jj) acc = mma16(frag4(sm.a16, P4, 16 * i, 16 * jj, lane), Xh[b][jj], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] -= acc[e];
+            X[b][i] = mma16(frag4(sm.tii[i], PI, 0, 0, lane), to_half4(z), floatx4{0.f, 0.f, 0.f, 0.f});
+            Xh[b][i] = to_half4(X[b][i]);
+        }
+    }
+    // ---- Q^ = Qp - P W (waves 0, 1, in place over Qp; W into the Km tile) and
+    // O^ = P U~ (waves 2, 3, straight to the workspace with U~)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int col = 64 * (w & 1) + 16 * b + l16;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i <= rb; ++i) acc = mma16(frag4(sm.p, P4, 16 * rb, 16 * i, lane), Xh[b][i], acc);
+            if (wside) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * lg + e;
+                    sm.qp[r * PK + col] = (_Float16)((float)sm.qp[r * PK + col] - acc[e]);
+                    sm.km[r * PK + col] = Xh[b][rb][e];
+                }
+            } else {
+                *reinterpret_cast<half4 *>(rec + R_UT + 2 * ((size_t)col * C + 16 * rb + 4 * lg)) = Xh[b][rb];
+                *reinterpret_cast<floatx4 *>(rec + R_OH + 4 * ((size_t)col * C + 16 * rb + 4 * lg)) = acc;
+            }
+        }
+    }
+    __syncthreads();
+    // ---- W and Q^ rows to the workspace, k-permuted (16-byte stores: stored
+    // block b of a row takes logical 4-groups 8 (b >> 2) + (b & 3) and that + 4)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = 256 * e + t, r = idx >> 4, b = idx & 15;
+        const int l0 = 32 * (b >> 2) + 4 * (b & 3), l1 = l0 + 16;
+        half8 wv, qv;
+        const half4 w0 = *reinterpret_cast<const half4 *>(&sm.km[r * PK + l0]);
+        const half4 w1 = *reinterpret_cast<const half4 *>(&sm.km[r * PK + l1]);
+        const half4 q0 = *reinterpret_cast<const half4 *>(&sm.qp[r * PK + l0]);
+        const half4 q1 = *reinterpret_cast<const half4 *>(&sm.qp[r * PK + l1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            wv[i] = w0[i];
+            wv[4 + i] = w1[i];
+            qv[i] = q0[i];
+            qv[4 + i] = q1[i];
+        }
+        *reinterpret_cast<half8 *>(rec + R_W + 2 * ((size_t)r * KD + 8 * b)) = wv;
+        *reinterpret_cast<half8 *>(rec + R_QH + 2 * ((size_t)r * KD + 8 * b)) = qv;
+    }
+}
+
+// ---------------------------------------------------------------- pass 2
+// One chunk's state-pass operands in LDS: W, Q^ ([64][128] fp16) and Km^T
+// ([128][64] fp16) without padding, each row's 16-byte blocks XOR-permuted by
+// (row & 7) so that the 16 rows of an MFMA fragment read hit distinct banks;
+// then exp(G_m), exp(G_C - G_m).  Loader waves fill it with direct
+// global-to-LDS loads: 49 wave-wide 1 KB segments, each lane fetching the
+// global 16-byte block that belongs in its LDS slot.
+struct ChunkTiles {
+    _Float16 w[C * KD];
+    _Float16 qh[C * KD];
+    _Float16 kmt[KD * C];
+    float fmc[2 * KD];
+};
+constexpr int SEGMENTS = (int)sizeof(ChunkTiles) / 1024;  // 49
+static_assert(sizeof(ChunkTiles) == 49 * 1024, "segment count");
+
+// NSW state waves own 16 value columns each (a VT = 16 NSW column tile);
+// NLW loader waves stream the tiles (one CU sustains its highest direct-load
+// rate only with several waves' loads in flight).
+template <int NLW>
+struct StateSmem {
+    ChunkTiles buf[2];           // by chunk parity
+    uint32_t sink[NLW][64];      // landing slots of the L2 prefetches (never read)
+};
+
+// Chunks of look-ahead for the L2 prefetch of the tiles.
+constexpr int PREFETCH_AHEAD = 3;
+
+// Workgroup barrier for the loader waves, which touch LDS only through their
+// direct loads and wait for those explicitly: no fence, so the compiler does
+// not add a wait for every outstanding load (the L2 prefetches included).
+__device__ __forceinline__ void loader_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Global source of LDS slot p (16-byte units) of a ChunkTiles image.
+__device__ __forceinline__ const unsigned char *tile_source(const unsigned char *rec, int p) {
+    if (p < 2048) {  // W, Q^: 16 blocks per 256-byte row
+        const int t = p >> 10, r = (p >> 4) & 63, b = (p & 15) ^ (r & 7);
+        return rec + 16384 * t + 256 * r + 16 * b;
+    }
+    if (p < 3072) {  // Km^T: 8 blocks per 128-byte row
+        const int c = (p - 2048) >> 3, b = (p & 7) ^ (c & 7);
+        return rec + R_KMT + 128 * c + 16 * b;
+    }
+    return rec + R_FM + 16 * (p - 3072);
+}
+
+template <int NLW>
+__device__ __forceinline__ void load_tiles(ChunkTiles &dst, const unsigned char *rec, int lw,
+                                           int lane) {
+    for (int s = lw; s < SEGMENTS; s += NLW) {
+        __builtin_amdgcn_global_load_lds(
+            tile_source(rec, 64 * s + lane),
+            (__attribute__((address_space(3))) void *)(reinterpret_cast<unsigned char *>(&dst) + 1024 * s),
+            16, 0, 0);
+    }
+}
+
+// Pull one chunk's tile bytes (the first 48 KB of the record and the 1 KB of
+// scale factors: 392 lines of 128 bytes) towards L2, one 4-byte load per line,
+// spread over the `parts` loader waves of the unit's workgroups; the loaded
+// words land in a scratch LDS slot nobody reads.
+__device__ __forceinline__ void prefetch_tiles(uint32_t *sink, const unsigned char *rec, int part,
+                                               int lane) {
+    const int li = min(64 * part + lane, 391);
+    const unsigned char *src = li < 384 ? rec + 128 * li : rec + R_FM + 128 * (li - 384);
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)sink, 4, 0, 0);
+}
+
+// 16x16x32 fragment from a swizzled tile with `rowlen` halves per row.
+__device__ __forceinline__ half8 frag8_sw(const _Float16 *base, int rowlen, int row0, int ks,
+                                          int lane) {
+    const int r = row0 + (lane & 15);
+    const int kb = (4 * ks + (lane >> 4)) ^ (r & 7);
+    return *reinterpret_cast<const half8 *>(base + r * rowlen + 8 * kb);
+}
+
+// Output rows of one chunk through a buffer resource that spans exactly the
+// chunk's L valid rows: the hardware range check drops the rows past L, and
+// the per-lane offset is loop-invariant.
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+}
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, bf16_t x) {
+    __builtin_amdgcn_raw_buffer_store_b16(x.bits, r, off, 0, 0);
+}
+
+template <typename TOut>
+__device__ __forceinline__ void store_o(TOut *o, const floatx4 (&Y)[4], int c0, int L, int H,
+                                        int lane_off) {
+    const int row_bytes = H * VD * (int)sizeof(TOut);
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        o + (size_t)c0 * H * VD, 0, L * row_bytes, 0x00020000);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            store_elem(r, lane_off + (16 * rb + e) * row_bytes, from_f32<TOut>(Y[rb][e]));
+}
+
+// B fragment of a k-permuted product from accumulator blocks 2 ks, 2 ks + 1.
+__device__ __forceinline__ half8 bfrag(const floatx4 &lo, const floatx4 &hi) {
+    half8 b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        b[i] = (_Float16)lo[i];
+        b[4 + i] = (_Float16)hi[i];
+    }
+    return b;
+}
+
+// One chunk of the state chain for one state wave (16 value columns), all in
+// registers: the left operands come from the LDS tiles, the right operands
+// are the wave's own accumulators.  The output products are issued after U
+// is formed, off the chain.
+template <typename TOut>
+__device__ __forceinline__ void state_chunk(floatx4 (&S)[8], const ChunkTiles &tl,
+                                            const half4 (&ucur)[4], const floatx4 (&ocur)[4],
+                                            TOut *o, int c0, int L, int H, int o_lane_off,
+                                            int lane) {
+    const int lg = lane >> 4;
+    // S' = Diag(exp(G_m)) S
+    floatx4 f[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) f[cb] = *reinterpret_cast<const floatx4 *>(&tl.fmc[16 * cb + 4 * lg]);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[cb][i] *= f[cb][i];
+    half8 bs[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) bs[ks] = bfrag(S[2 * ks], S[2 * ks + 1]);
+    // U = U~ - W S'
+    floatx4 X[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        X[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) X[rb] = mma32(frag8_sw(tl.w, KD, 16 * rb, ks, lane), bs[ks], X[rb]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[rb][e] = (float)ucur[rb][e] - X[rb][e];
+    half8 bu[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) bu[ks] = bfrag(X[2 * ks], X[2 * ks + 1]);
+    // O = Q^ S' + O^
+    floatx4 Y[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        Y[rb] = ocur[rb];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) Y[rb] = mma32(frag8_sw(tl.qh, KD, 16 * rb, ks, lane), bs[ks], Y[rb]);
+    }
+    // S = Diag(exp(G_C - G_m)) (S' + Km^T U)
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) f[cb] = *reinterpret_cast<const floatx4 *>(&tl.fmc[KD + 16 * cb + 4 * lg]);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) S[cb] = mma32(frag8_sw(tl.kmt, C, 16 * cb, ks, lane), bu[ks], S[cb]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[cb][i] *= f[cb][i];
+    }
+    store_o(o, Y, c0, L, H, o_lane_off);
+}
+
+// Grid: one workgroup per (unit, value tile), XCD-aware: workgroup b runs on
+// XCD b mod 8, and all value tiles of a unit share that XCD (and its L2),
+// which serves their common W, Q^, Km^T tiles.
+template <int NSW, int NLW, typename TOut>
+__global__ __launch_bounds__(64 * (NSW + NLW)) void chunk_state_kernel(
+    const float *s0, TOut *__restrict__ o, float *sT, const int32_t *__restrict__ cu, int fixedT,
+    int N, int H, int totalT, int cap, const unsigned char *__restrict__ ws) {
+    constexpr int VTILE = 16 * NSW, NVT = VD / VTILE;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    StateSmem<NLW> &sm = *reinterpret_cast<StateSmem<NLW> *>(smem_raw);
+    const int32_t *offs = reinterpret_cast<const int32_t *>(ws);
+    const int b = blockIdx.x, slot = b >> 3;
+    const int vt = slot % NVT;
+    const int unit = (slot / NVT) * 8 + (b & 7);
+    if (unit >= N * H) return;
+    const int n = unit / H, h = unit - n * H;
+    int bos, eos;
+    seq_bounds(cu, n, fixedT, totalT, bos, eos);
+    const int ch0 = offs[n];
+    const int nchunks = offs[n + 1] - ch0;
+    const unsigned char *recs = ws + OFFS_BYTES;
+    auto rec = [&](int ci) { return recs + ((size_t)h * cap + ch0 + ci) * REC; };
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lg = lane >> 4;
+
+    if (w < NSW) {
+        const int jcol = vt * VTILE + 16 * w + (lane & 15);  // this lane's value column
+        const size_t sbase = (size_t)unit * (KD * VD) + jcol;
+        const int o_lane_off = ((4 * lg * H + h) * VD + jcol) * (int)sizeof(TOut);
+        floatx4 S[8];
+        if (s0) {
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[cb][i] = s0[sbase + (size_t)(16 * cb + 4 * lg + i) * VD];
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) S[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+        // this wave's slices of U~ and O^, fetched one chunk ahead into two
+        // register sets used alternately
+        half4 ua[4], ub[4];
+        floatx4 oa[4], ob[4];
+        auto fetch = [&](int ci, half4 (&un)[4], floatx4 (&on)[4]) {
+            const unsigned char *r = rec(ci);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                un[rb] = *reinterpret_cast<const half4 *>(r + R_UT + 2 * ((size_t)jcol * C + 16 * rb + 4 * lg));
+                on[rb] = *reinterpret_cast<const floatx4 *>(r + R_OH + 4 * ((size_t)jcol * C + 16 * rb + 4 * lg));
+            }
+        };
+        // The initial state is complete before the loop, and the prefetches are
+        // unconditional (the index clamped to the last chunk), so that the
+        // memory waits inside the loop are those for the register set about
+        // to be used.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        const int last = nchunks - 1;
+        if (nchunks > 0) fetch(0, ua, oa);
+        __syncthreads();
+        for (int ci = 0; ci < nchunks; ci += 2) {
+            fetch(min(ci + 1, last), ub, ob);
+            int c0 = bos + ci * C;
+            state_chunk(S, sm.buf[0], ua, oa, o, c0, min(C, eos - c0), H, o_lane_off, lane);
+            __syncthreads();
+            if (ci + 1 >= nchunks) break;
+            fetch(min(ci + 2, last), ua, oa);
+            c0 += C;
+            state_chunk(S, sm.buf[1], ub, ob, o, c0, min(C, eos - c0), H, o_lane_off, lane);
+            __syncthreads();
+        }
+        if (sT) {
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * cb + 4 * lg + i) * VD] = S[cb][i];
+        }
+    } else {
+        // loader waves: chunk ci + 1 streams into the other buffer while the
+        // state waves work on chunk ci; each wave waits for its own loads
+        // before the barrier that hands the buffer over
+        // Loader waves 0..6 of the unit (across its workgroups) also prefetch
+        // 1/7 of chunk ci + 1 + PREFETCH_AHEAD's tiles into L2 after their
+        // tile loads, and wait for all but that last load (loads complete in
+        // issue order); the others wait for all their loads.
+        const int lw = w - NSW;
+        const int part = __builtin_amdgcn_readfirstlane(vt * NLW + lw);
+        uint32_t *sink = sm.sink[lw];
+        const int last = nchunks - 1;
+        if (nchunks > 0) {
+            if (part < 7) {
+#pragma unroll 1
+                for (int a = 1; a <= PREFETCH_AHEAD; ++a) prefetch_tiles(sink, rec(min(a, last)), part, lane);
+            }
+            load_tiles<NLW>(sm.buf[0], rec(0), lw, lane);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        }
+        __syncthreads();
+        for (int ci = 0; ci < nchunks; ++ci) {
+            if (ci + 1 < nchunks) {
+                load_tiles<NLW>(sm.buf[(ci + 1) & 1], rec(ci + 1), lw, lane);
+                if (part < 7) {
+                    prefetch_tiles(sink, rec(min(ci + 1 + PREFETCH_AHEAD, last)), part, lane);
+                    __builtin_amdgcn_s_waitcnt(0x0F71);  // vmcnt(1)
+                } else {
+                    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+                }
+            }
+            loader_barrier();
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing left in flight
+    }
+}
+
+template <int NSW, int NLW, typename TOut>
+hipError_t launch_state(const float *s0, void *o, float *sT, const int32_t *cu, int N, int fixedT,
+                        int totalT, int H, int cap, const unsigned char *ws, hipStream_t stream) {
+    auto kern = chunk_state_kernel<NSW, NLW, TOut>;
+    constexpr int smem = (int)sizeof(StateSmem<NLW>);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+    const int groups = (N * H + 7) / 8;
+    hipLaunchKernelGGL(kern, dim3(groups * 8 * (VD / (16 * NSW))), dim3(64 * (NSW + NLW)), smem, stream,
+                       s0, static_cast<TOut *>(o), sT, cu, fixedT, N, H, totalT, cap, ws);
+    return hipGetLastError();
+}
+
+int max_chunks(int N, int totalT, int fixedT, bool varlen) {
+    if (!varlen) return N * ((fixedT + C - 1) / C);
+    return (int)(((long long)totalT + (long long)(C - 1) * N + C - 1) / C);
+}
+
+}  // namespace
+
+// The two-pass path serves bf16 inputs with (K, V, C) = (128, 128, 64) and
+// fewer than 127 sequences.  It beats the single-pass kernel while its pass-2
+// workgroups (8 per unit) leave the GPU underfilled and sequences are long
+// enough to amortise the extra launches: up to 32 units, at least 8 chunks
+// per sequence on average.
+bool chunk_split_supported(int N, int H, int K, int V, int Cc) {
+    return K == KD && V == VD && Cc == C && N > 0 && N < 127 && H > 0;
+}
+
+bool chunk_split_recommended(int N, int totalT, int H, int K, int V, int Cc) {
+    return chunk_split_supported(N, H, K, V, Cc) && (long long)N * H <= 32 &&
+           (long long)totalT >= 8LL * C * N;
+}
+
+size_t chunk_split_workspace_bytes(int N, int totalT, int H) {
+    return OFFS_BYTES + (size_t)max_chunks(N, totalT, 0, true) * H * REC;
+}
+
+hipError_t launch_chunk_split(const void *q, const void *k, const void *v, const void *g,
+                              const void *beta, const float *s0, void *o, float *sT,
+                              const int32_t *cu, int N, int fixedT, int totalT, int H,
+                              bool out_bf16, void *workspace, hipStream_t stream) {
+    if (N == 0 || H == 0) return hipSuccess;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    const int cap = max_chunks(N, totalT, fixedT, cu != nullptr);
+    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, stream, cu, fixedT, N, totalT,
+                       cap, reinterpret_cast<int32_t *>(ws));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (cap > 0) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(chunk_prep_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PrepSmem));
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(chunk_prep_kernel, dim3(cap, H), dim3(256), sizeof(PrepSmem), stream,
+                           static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                           static_cast<const uint16_t *>(v), static_cast<const uint16_t *>(g),
+                           static_cast<const uint16_t *>(beta), cu, fixedT, N, H, totalT, ws);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return out_bf16
+               ? launch_state<STATE_WAVES, LOADER_WAVES, bf16_t>(s0, o, sT, cu, N, fixedT, totalT, H,
+                                                                 cap, ws, stream)
+               : launch_state<STATE_WAVES, LOADER_WAVES, float>(s0, o, sT, cu, N, fixedT, totalT, H,
+                                                                cap, ws, stream);
+}
+
+}  // namespace kda

@@ -23,6 +23,13 @@ hipError_t launch_chunk_mfma(const void *q, const void *k, const void *v, const 
                              const int32_t *cu, int N, int fixedT, int totalT, int H,
                              bool out_bf16, hipStream_t stream);
 bool chunk_mfma_supported(int K, int V, int C);
+bool chunk_split_supported(int N, int H, int K, int V, int C);
+bool chunk_split_recommended(int N, int totalT, int H, int K, int V, int C);
+size_t chunk_split_workspace_bytes(int N, int totalT, int H);
+hipError_t launch_chunk_split(const void *q, const void *k, const void *v, const void *g,
+                              const void *beta, const float *s0, void *o, float *sT,
+                              const int32_t *cu, int N, int fixedT, int totalT, int H,
+                              bool out_bf16, void *workspace, hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -52,14 +59,32 @@ kda_status_t validate_fwd(const void *q, const void *k, const void *v, const voi
     return KDA_OK;
 }
 
+// The workspace is optional: a workspace of at least
+// kda_two_pass_workspace_bytes() selects the two-pass bf16 path (when that
+// size is nonzero), none selects the single-pass kernels; a nonzero workspace
+// that is too small is an error.
+kda_status_t check_workspace(const void *workspace, size_t workspace_bytes, size_t need,
+                             bool &two_pass) {
+    two_pass = false;
+    if (workspace_bytes == 0) return KDA_OK;
+    if (!workspace) return KDA_ERR_NULL;
+    if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    two_pass = need > 0;
+    return KDA_OK;
+}
+
 kda_status_t run_fwd(const void *q, const void *k, const void *v, const void *g,
                      const void *beta, const float *s0, void *o, float *sT, const int32_t *cu,
                      int N, int fixedT, int totalT, int H, int K, int V, int chunk,
-                     kda_dtype_t in_dtype, kda_dtype_t out_dtype, void *stream) {
+                     kda_dtype_t in_dtype, kda_dtype_t out_dtype, void *workspace,
+                     bool two_pass, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool in_bf16 = in_dtype == KDA_BF16, out_bf16 = out_dtype == KDA_BF16;
     hipError_t e;
-    if (in_bf16 && kda::chunk_mfma_supported(K, V, chunk))
+    if (in_bf16 && two_pass && kda::chunk_split_supported(N, H, K, V, chunk))
+        e = kda::launch_chunk_split(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H,
+                                    out_bf16, workspace, st);
+    else if (in_bf16 && kda::chunk_mfma_supported(K, V, chunk))
         e = kda::launch_chunk_mfma(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H,
                                    out_bf16, st);
     else
@@ -87,9 +112,15 @@ const char *kda_status_str(kda_status_t s) {
     return "KDA_ERR_UNKNOWN";
 }
 
+size_t kda_two_pass_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk) {
+    if (N <= 0 || total_T < 0 || H <= 0 || !kda::chunk_split_supported(N, H, K, V, chunk)) return 0;
+    return kda::chunk_split_workspace_bytes(N, total_T, H);
+}
+
 size_t kda_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk) {
-    (void)N; (void)total_T; (void)H; (void)K; (void)V; (void)chunk;
-    return 0;
+    if (N <= 0 || total_T < 0 || H <= 0 || !kda::chunk_split_recommended(N, total_T, H, K, V, chunk))
+        return 0;
+    return kda::chunk_split_workspace_bytes(N, total_T, H);
 }
 
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
@@ -103,12 +134,14 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
     kda_status_t s = validate_fwd(q, k, v, g, beta, o, B, (int)total, H, K, V, chunk, in_dtype,
                                   out_dtype);
     if (s != KDA_OK) return s;
-    if (workspace_bytes < kda_workspace_bytes(B, (int)total, H, K, V, chunk)) return KDA_ERR_WORKSPACE;
-    (void)workspace;
+    bool two_pass;
+    s = check_workspace(workspace, workspace_bytes,
+                        kda_two_pass_workspace_bytes(B, (int)total, H, K, V, chunk), two_pass);
+    if (s != KDA_OK) return s;
     if (B == 0) return KDA_OK;
     if (T == 0 && !sT) return KDA_OK;
     return run_fwd(q, k, v, g, beta, s0, o, sT, nullptr, B, T, (int)total, H, K, V, chunk,
-                   in_dtype, out_dtype, stream);
+                   in_dtype, out_dtype, workspace, two_pass, stream);
 }
 
 kda_status_t kda_varlen_fwd(const void *q, const void *k, const void *v, const void *g,
@@ -120,11 +153,13 @@ kda_status_t kda_varlen_fwd(const void *q, const void *k, const void *v, const v
                                   out_dtype);
     if (s != KDA_OK) return s;
     if (N > 0 && !cu_seqlens) return KDA_ERR_NULL;
-    if (workspace_bytes < kda_workspace_bytes(N, total_T, H, K, V, chunk)) return KDA_ERR_WORKSPACE;
-    (void)workspace;
+    bool two_pass;
+    s = check_workspace(workspace, workspace_bytes,
+                        kda_two_pass_workspace_bytes(N, total_T, H, K, V, chunk), two_pass);
+    if (s != KDA_OK) return s;
     if (N == 0) return KDA_OK;
     return run_fwd(q, k, v, g, beta, s0, o, sT, cu_seqlens, N, 0, total_T, H, K, V, chunk,
-                   in_dtype, out_dtype, stream);
+                   in_dtype, out_dtype, workspace, two_pass, stream);
 }
 
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g,

@@ -13,7 +13,8 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "varlen_fwd", "decode_step", "workspace_bytes", "library",
+__all__ = ["chunk_fwd", "varlen_fwd", "decode_step", "workspace_bytes",
+           "two_pass_workspace_bytes", "library",
            "KdaError", "LIB_PATH", "F32", "BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -48,6 +49,8 @@ def library():
     lib.kda_decode_step.restype = i32
     lib.kda_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.kda_workspace_bytes.restype = sz
+    lib.kda_two_pass_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.kda_two_pass_workspace_bytes.restype = sz
     lib.kda_status_str.argtypes = [i32]
     lib.kda_status_str.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -95,18 +98,43 @@ def _stream(dev):
 
 
 def workspace_bytes(N: int, total_T: int, H: int, K: int, V: int, chunk: int) -> int:
+    """Workspace bytes of the recommended implementation (0: single pass)."""
     return int(library().kda_workspace_bytes(N, total_T, H, K, V, chunk))
 
 
-def _workspace(dev, N, total, H, K, V, chunk):
-    nbytes = workspace_bytes(N, total, H, K, V, chunk)
+def two_pass_workspace_bytes(N: int, total_T: int, H: int, K: int, V: int, chunk: int) -> int:
+    """Workspace bytes that select the two-pass path (0: not supported)."""
+    return int(library().kda_two_pass_workspace_bytes(N, total_T, H, K, V, chunk))
+
+
+def _workspace(dev, N, total, H, K, V, chunk, two_pass, workspace):
+    """Workspace for one call: none when two_pass is False (single-pass kernels);
+    the two-pass size when two_pass is True (ValueError if unsupported) or when
+    two_pass is None and the library recommends it; the caller's uint8 tensor
+    if given, else a fresh one."""
+    if two_pass is False:
+        return None, 0
+    if two_pass:
+        nbytes = two_pass_workspace_bytes(N, total, H, K, V, chunk)
+        if nbytes == 0:
+            raise ValueError(f"the two-pass path does not support N={N}, (K, V, chunk)="
+                             f"({K}, {V}, {chunk})")
+    else:
+        nbytes = workspace_bytes(N, total, H, K, V, chunk)
     if nbytes == 0:
         return None, 0
+    if workspace is not None:
+        if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+        if workspace.numel() < nbytes:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, {nbytes} needed")
+        return workspace, workspace.numel()
     return torch.empty(nbytes, dtype=torch.uint8, device=dev), nbytes
 
 
 def chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, chunk=None,
-              out_dtype=torch.float32, final_state=None, out=None):
+              out_dtype=torch.float32, final_state=None, out=None, two_pass=None,
+              workspace=None):
     """Chunked KDA forward over a fixed-length batch.
 
     q, k, g: [B, T, H, K]; v: [B, T, H, V]; beta: [B, T, H]; all float32 or all bfloat16.
@@ -114,6 +142,10 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, chu
     Returns (o [B, T, H, V] of out_dtype, final state [B, H, K, V] float32 or None).
     final_state may be passed to receive S_T in place (it may be initial_state itself);
     out may be passed to receive o.
+    two_pass: None takes the library's recommendation (the two-pass bf16 kernels
+    when kda_workspace_bytes is nonzero: few (sequence, head) units, long
+    sequences); True forces the two-pass path, False the single-pass kernels.
+    workspace: optional preallocated uint8 tensor.
     """
     _need_gpu(q, k, v, g, beta, initial_state, final_state, out)
     B, T, H, K = q.shape
@@ -134,7 +166,7 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, chu
     sT = final_state
     if sT is None and output_final_state:
         sT = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
-    ws, nws = _workspace(dev, B, B * T, H, K, V, chunk)
+    ws, nws = _workspace(dev, B, B * T, H, K, V, chunk, two_pass, workspace)
     st = library().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                  _ptr(initial_state), _ptr(o), _ptr(sT),
                                  B, T, H, K, V, chunk, _dtype_code(dt), _dtype_code(o.dtype),
@@ -144,12 +176,14 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, chu
 
 
 def varlen_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, output_final_state=True,
-               chunk=None, out_dtype=torch.float32, final_state=None, out=None):
+               chunk=None, out_dtype=torch.float32, final_state=None, out=None, two_pass=None,
+               workspace=None):
     """Chunked KDA forward over packed sequences.
 
     q, k, g: [total_T, H, K]; v: [total_T, H, V]; beta: [total_T, H];
     cu_seqlens: int32 [N + 1] on the GPU.  initial_state: [N, H, K, V] float32 or None.
     Returns (o [total_T, H, V], final states [N, H, K, V] or None).
+    two_pass, workspace: as for chunk_fwd.
     """
     _need_gpu(q, k, v, g, beta, cu_seqlens, initial_state, final_state, out)
     total, H, K = q.shape
@@ -173,7 +207,7 @@ def varlen_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, output_final_st
     sT = final_state
     if sT is None and output_final_state:
         sT = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
-    ws, nws = _workspace(dev, N, total, H, K, V, chunk)
+    ws, nws = _workspace(dev, N, total, H, K, V, chunk, two_pass, workspace)
     st = library().kda_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   _ptr(initial_state), _ptr(o), _ptr(sT), _ptr(cu_seqlens),
                                   N, total, H, K, V, chunk, _dtype_code(dt),

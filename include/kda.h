@@ -83,8 +83,19 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  *   o  : [B, T, H, V] output, out_dtype.
  *   sT : [B, H, K, V] final states, or NULL if not wanted.  May equal s0.
  *   chunk : 16 or 64, as fixed by (K, V) above.
- *   workspace : device scratch of at least kda_workspace_bytes(B, B*T, H, K, V,
- *               chunk) bytes (NULL allowed when that is 0).
+ *   workspace : optional device scratch that selects the implementation:
+ *               workspace_bytes == 0 (workspace ignored, may be NULL) runs the
+ *               single-pass kernels; workspace_bytes >=
+ *               kda_two_pass_workspace_bytes(B, B*T, H, K, V, chunk) > 0 runs
+ *               the two-pass bf16 path (intra-chunk pass over all chunks,
+ *               then the sequential state pass), which is faster when few
+ *               (sequence, head) units leave the GPU underfilled;
+ *               kda_workspace_bytes() gives the size to pass for the
+ *               recommended choice.  A nonzero workspace_bytes smaller than
+ *               kda_two_pass_workspace_bytes() fails with KDA_ERR_WORKSPACE,
+ *               and a NULL workspace with nonzero workspace_bytes with
+ *               KDA_ERR_NULL.  The caller owns it; concurrent calls need
+ *               separate workspaces; its contents are scratch.
  * T = 0 or B = 0 is allowed: sT receives s0 (or zeros) and o is untouched.
  */
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
@@ -118,8 +129,17 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
                              int V, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
                              void *stream);
 
-/* Device scratch bytes the forward calls need for these sizes (0 if none). */
+/* Workspace bytes for the recommended implementation of a forward call over
+ * N sequences, total_T tokens: nonzero (the two-pass size) when the two-pass
+ * path is supported and expected to be faster (bf16 inputs assumed; at most
+ * 32 units, sequences of at least 8 chunks on average), else 0. */
 size_t kda_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk);
+
+/* Workspace bytes that select the two-pass path whenever it is supported:
+ * (K, V, chunk) = (128, 128, 64), 1 <= N <= 126; 0 when it is not.  The
+ * two-pass path runs for bf16 inputs only; fp32 inputs ignore the workspace.
+ * Size: 512 + ceil((total_T + 63 N) / 64) * H * 99328 bytes. */
+size_t kda_two_pass_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk);
 
 /* Static, human-readable name of a status code. */
 const char *kda_status_str(kda_status_t status);

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kda_chunk_fwd", "kda_varlen_fwd", "kda_decode_step", "kda_workspace_bytes",
-              "kda_status_str", "kda_version"):
+              "kda_two_pass_workspace_bytes", "kda_status_str", "kda_version"):
         assert n in names
 
 
@@ -45,17 +45,39 @@ def test_status_strings_and_version(lib):
         assert s.startswith("KDA_")
     assert lib.kda_status_str(99).decode() == "KDA_ERR_UNKNOWN"
     assert lib.kda_version() == 100
-    assert lib.kda_workspace_bytes(4, 32768, 32, 128, 128, 64) == 0
+
+
+def two_pass_size(N, total, H):
+    # offsets block, then one 99328-byte record per (chunk, head) for the
+    # packed-sequence chunk bound
+    return 512 + -(-(total + 63 * N) // 64) * H * 99328
+
+
+def test_workspace_sizes(lib):
+    rec, two = lib.kda_workspace_bytes, lib.kda_two_pass_workspace_bytes
+    # recommended: two-pass for few units and long sequences only
+    assert rec(1, 4096, 8, 128, 128, 64) == two_pass_size(1, 4096, 8)
+    assert rec(1, 4096, 32, 128, 128, 64) == two_pass_size(1, 4096, 32)
+    assert rec(1, 4096, 33, 128, 128, 64) == 0
+    assert rec(4, 32768, 32, 128, 128, 64) == 0
+    assert rec(1, 511, 8, 128, 128, 64) == 0
+    # supported whenever (K, V, chunk) = (128, 128, 64) and N < 127
+    assert two(4, 32768, 32, 128, 128, 64) == two_pass_size(4, 32768, 32)
+    assert two(2, 0, 3, 128, 128, 64) == two_pass_size(2, 0, 3)
+    assert two(126, 1000, 1, 128, 128, 64) > 0
+    assert two(127, 1000, 1, 128, 128, 64) == 0
+    assert two(1, 64, 1, 32, 32, 16) == 0
+    assert two(0, 0, 1, 128, 128, 64) == 0
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
 
 
-def chunk(lib, *, B=1, T=64, H=1, K=128, V=128, C=64, ind=1, outd=0, null=None, ws=0):
+def chunk(lib, *, B=1, T=64, H=1, K=128, V=128, C=64, ind=1, outd=0, null=None, wsp=None, ws=0):
     ptrs = [FAKE] * 8
     if null is not None:
         ptrs[null] = None
-    return lib.kda_chunk_fwd(*ptrs, B, T, H, K, V, C, ind, outd, None, ws, None)
+    return lib.kda_chunk_fwd(*ptrs, B, T, H, K, V, C, ind, outd, wsp, ws, None)
 
 
 def test_chunk_argument_errors(lib):
@@ -70,6 +92,10 @@ def test_chunk_argument_errors(lib):
     assert chunk(lib, T=1 << 22, H=64) == 2                   # > 2^31 elements
     for i in (0, 1, 2, 3, 4, 6):                              # q, k, v, g, beta, o
         assert chunk(lib, null=i) == 1
+    need = two_pass_size(1, 64, 1)
+    assert chunk(lib, wsp=None, ws=need) == 1                 # workspace size but no pointer
+    assert chunk(lib, wsp=FAKE, ws=need - 1) == 5             # workspace too small
+    assert chunk(lib, wsp=FAKE, ws=1, K=32, V=32, C=16, B=-1) == 2  # shape checked first
 
 
 def test_varlen_argument_errors(lib):

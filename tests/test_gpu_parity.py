@@ -16,15 +16,22 @@ from tests.parity import TOL, rel_err, report, to_gpu
 pytestmark = pytest.mark.gpu
 
 
+# The bf16 (K, V) = (128, 128) path has two implementations: the two-pass
+# kernels and the single-pass fused kernel; the cases below force each.
+PATHS = {"two_pass": True, "fused": False}
+
+
 def _fixed_case(name, seed, B, T, H, K, V, dtype, s0_std=None, g_lb=0.25, g_mode="default",
-                out_dtype=torch.float32, tol=None):
-    print(f"[case] {name} B={B} T={T} H={H} K={K} V={V} {dtype} g={g_mode}/{g_lb}", flush=True)
+                out_dtype=torch.float32, tol=None, path="two_pass"):
+    print(f"[case] {name} B={B} T={T} H={H} K={K} V={V} {dtype} g={g_mode}/{g_lb} path={path}",
+          flush=True)
     d = inputs.draw_fixed(seed, B, T, H, K, V, dtype, s0_std=s0_std, g_lb=g_lb, g_mode=g_mode)
     o_ref, s_ref = oracle.fixed(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                 oracle.as_f64(d["s0"]))
     x = to_gpu(d)
+    tp = PATHS[path] if dtype == "bf16" and K == 128 else None
     o, sT = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], initial_state=x["s0"],
-                          out_dtype=out_dtype)
+                          out_dtype=out_dtype, two_pass=tp)
     torch.cuda.synchronize()
     eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
     report(name, o=eo, sT=es)
@@ -57,34 +64,58 @@ def test_bf16_d32():
     _fixed_case("bf16_d32", 10, 2, 77, 2, 32, 32, "bf16", s0_std=0.1)
 
 
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 300])
-def test_bf16_d128_ragged_lengths(T):
-    _fixed_case(f"bf16_d128_T{T}", 200 + T, 2, T, 2, 128, 128, "bf16", s0_std=0.1)
+def test_bf16_d128_ragged_lengths(T, path):
+    _fixed_case(f"bf16_d128_T{T}", 200 + T, 2, T, 2, 128, 128, "bf16", s0_std=0.1, path=path)
 
 
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("g_mode,g_lb", [("zero", 0.25), ("bound", 0.25), ("uniform", 0.25)])
-def test_bf16_d128_decay_stress(g_mode, g_lb):
+def test_bf16_d128_decay_stress(g_mode, g_lb, path):
     # no decay keeps every chunk's contribution alive, so an inter-chunk state
     # bug cannot hide behind attenuation; "bound" sits every step on -g_lb
     _fixed_case(f"bf16_d128_{g_mode}", 300, 1, 700, 3, 128, 128, "bf16", s0_std=0.1,
-                g_lb=g_lb, g_mode=g_mode)
+                g_lb=g_lb, g_mode=g_mode, path=path)
 
 
-def test_bf16_output_dtype():
+@pytest.mark.parametrize("path", list(PATHS))
+def test_bf16_output_dtype(path):
     _fixed_case("bf16_out", 11, 1, 256, 2, 128, 128, "bf16", s0_std=0.1,
-                out_dtype=torch.bfloat16, tol=3e-2)
+                out_dtype=torch.bfloat16, tol=3e-2, path=path)
 
 
-def test_state_in_place_and_resume():
+@pytest.mark.parametrize("H,expect_two_pass", [(32, True), (33, False)])
+def test_bf16_d128_default_choice_at_the_unit_switch(H, expect_two_pass):
+    # with the default arguments the library recommends the two-pass path up to
+    # 32 (sequence, head) units of long enough sequences, the fused kernel above
+    B, T = 1, 600
+    assert (kda.workspace_bytes(B, B * T, H, 128, 128, 64) > 0) == expect_two_pass
+    print(f"[case] default choice B={B} T={T} H={H} two_pass={expect_two_pass}", flush=True)
+    d = inputs.draw_fixed(16, B, T, H, 128, 128, "bf16", s0_std=0.1)
+    o_ref, s_ref = oracle.fixed(d["q"], d["k"], d["v"], d["g"], d["beta"], oracle.as_f64(d["s0"]))
+    x = to_gpu(d)
+    o, sT = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], initial_state=x["s0"])
+    torch.cuda.synchronize()
+    eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+    report(f"default_choice_H{H}", o=eo, sT=es)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_state_in_place_and_resume(path):
     """sT may alias s0; two half-runs chained through the state equal one run."""
     d = inputs.draw_fixed(12, 1, 256, 2, 128, 128, "bf16", s0_std=0.1)
     x = to_gpu(d)
-    o_full, s_full = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"])
+    tp = PATHS[path]
+    o_full, s_full = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"],
+                                   two_pass=tp)
     st = x["s0"].clone()
     parts = []
     for a, b in ((0, 100), (100, 256)):
         sl = {k: x[k][:, a:b].contiguous() for k in ("q", "k", "v", "g", "beta")}
-        o, _ = kda.chunk_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], st, final_state=st)
+        o, _ = kda.chunk_fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], st, final_state=st,
+                             two_pass=tp)
         parts.append(o)
     torch.cuda.synchronize()
     o_ref, s_ref = oracle.fixed(d["q"], d["k"], d["v"], d["g"], d["beta"], oracle.as_f64(d["s0"]))
@@ -93,40 +124,49 @@ def test_state_in_place_and_resume():
     assert rel_err(o_full, o_ref) <= TOL["bf16"]
 
 
-def test_zero_length_batch_returns_initial_state():
+@pytest.mark.parametrize("path", list(PATHS))
+def test_zero_length_batch_returns_initial_state(path):
     d = to_gpu(inputs.draw_fixed(13, 2, 0, 2, 128, 128, "bf16", s0_std=0.1))
-    o, sT = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+    o, sT = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"],
+                          two_pass=PATHS[path])
     torch.cuda.synchronize()
     assert o.numel() == 0 and torch.equal(sT, d["s0"])
 
 
-@pytest.mark.parametrize("dtype,K", [("bf16", 128), ("f32", 32), ("bf16", 32)])
-def test_varlen_edge_lengths(dtype, K):
+@pytest.mark.parametrize("dtype,K,path", [("bf16", 128, "two_pass"), ("bf16", 128, "fused"),
+                                          ("f32", 32, "fused"), ("bf16", 32, "fused")])
+def test_varlen_edge_lengths(dtype, K, path):
     C = 16 if K == 32 else 64
     lengths = [C + 1, 0, 1, C - 1, C, 3 * C + 5, 0, 2]
-    print(f"[case] varlen {dtype} K={K} lengths={lengths}", flush=True)
+    print(f"[case] varlen {dtype} K={K} lengths={lengths} path={path}", flush=True)
     d = inputs.draw_varlen(14, H=3, K=K, V=K, dtype=dtype, lengths=lengths, s0_std=0.1)
     o_ref, s_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                      d["cu_seqlens"].numpy(), oracle.as_f64(d["s0"]))
     x = to_gpu(d)
-    o, sT = kda.varlen_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"], x["s0"])
+    o, sT = kda.varlen_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"], x["s0"],
+                           two_pass=PATHS[path] if K == 128 else None)
     torch.cuda.synchronize()
     eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
-    report(f"varlen_{dtype}_K{K}", o=eo, sT=es)
+    report(f"varlen_{dtype}_K{K}_{path}", o=eo, sT=es)
     assert eo <= TOL[dtype] and es <= TOL[dtype]
     # zero-length sequences return their initial state bit for bit
     assert torch.equal(sT[1], x["s0"][1]) and torch.equal(sT[6], x["s0"][6])
 
 
-def test_output_fully_written_and_deterministic():
+@pytest.mark.parametrize("path", list(PATHS))
+def test_output_fully_written_and_deterministic(path):
     """Outputs poisoned with NaN beforehand must be fully overwritten, and two runs
-    must agree bit for bit (no atomics, no races)."""
+    must agree bit for bit (no atomics, no races).  The two-pass runs also
+    poison the workspace."""
     d = to_gpu(inputs.draw_fixed(15, 2, 333, 4, 128, 128, "bf16", s0_std=0.1))
+    nws = kda.two_pass_workspace_bytes(2, 666, 4, 128, 128, 64)
     outs = []
     for _ in range(2):
         o = torch.full((2, 333, 4, 128), float("nan"), device="cuda")
         s = torch.full((2, 4, 128, 128), float("nan"), device="cuda")
-        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], final_state=s, out=o)
+        ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device="cuda") if path == "two_pass" else None
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], final_state=s, out=o,
+                      two_pass=PATHS[path], workspace=ws)
         torch.cuda.synchronize()
         assert torch.isfinite(s).all() and torch.isfinite(o).all()
         outs.append((o, s))
