@@ -37,15 +37,16 @@ constexpr int PF = 17;   // LDS pitch (floats), 16 x 16 fp32 blocks
 
 // Per-(chunk, head) record in the workspace (bytes).  The contraction index
 // of W, Q^ (c) and Km^T (s) is stored permuted within each 32-wide block,
-// see kperm_pos below.
+// see kperm_pos below.  The first 33 KB are what the state pass streams.
 constexpr size_t R_W = 0;             // fp16 [64][128]  W     [r][c]
-constexpr size_t R_QH = 16384;        // fp16 [64][128]  Q^    [r][c]
-constexpr size_t R_KMT = 32768;       // fp16 [128][64]  Km^T  [c][s]
-constexpr size_t R_UT = 49152;        // fp16 [128][64]  U~    [j][r]
-constexpr size_t R_OH = 65536;        // fp32 [128][64]  O^    [j][r]
-constexpr size_t R_FM = 98304;        // fp32 [128]      exp(G_m)
-constexpr size_t R_FC = 98816;        // fp32 [128]      exp(G_C - G_m)
-constexpr size_t REC = 99328;
+constexpr size_t R_KMT = 16384;       // fp16 [128][64]  Km^T  [c][s]
+constexpr size_t R_FM = 32768;        // fp32 [128]      exp(G_m)
+constexpr size_t R_FC = 33280;        // fp32 [128]      exp(G_C - G_m + G_m of the next chunk)
+constexpr size_t R_UT = 33792;        // fp16 [128][64]  U~    [j][r]
+constexpr size_t R_QH = 50176;        // fp16 [64][128]  Q^    [r][c]
+constexpr size_t R_P = 66560;         // fp16 [64][64]   P     [r][s], zero above the diagonal
+constexpr size_t R_SP = 74752;        // fp16 S' as MFMA B fragments [8 tiles][4 ks][64 lanes][8]
+constexpr size_t REC = 107520;
 constexpr size_t OFFS_BYTES = 512;    // int32 chunk offsets, up to 127 sequences
 
 // The pass-2 products contract over an index (c for W S' and Q^ S', s for
@@ -60,6 +61,13 @@ constexpr size_t OFFS_BYTES = 512;    // int32 chunk offsets, up to 127 sequence
 __device__ __forceinline__ int kperm_pos(int q) {
     return 32 * (q >> 3) + 8 * (q & 3) + 4 * ((q >> 2) & 1);
 }
+
+// W and Km^T rows and U~ columns are stored with their 16-byte blocks
+// XOR-permuted by (row or column index & 7): the state pass copies them into
+// LDS unchanged (linear, fully coalesced direct loads), where the permutation
+// makes the 16 rows of an MFMA fragment read land in distinct banks.
+// swz(x, r): stored half offset of logical half offset x within row r.
+__device__ __forceinline__ int swz(int x, int r) { return (((x >> 3) ^ (r & 7)) << 3) | (x & 7); }
 
 // ---------------------------------------------------------------- offsets
 // offs[n] = first chunk of sequence n in the packed chunk list, clamped so that
@@ -79,18 +87,41 @@ __global__ void chunk_offsets_kernel(const int32_t *cu, int fixedT, int N, int t
     }
 }
 
+// Locating chunks: for N fixed-length sequences the chunk list is regular
+// (sequence n owns chunks [n cps, (n + 1) cps)) and no offset table is built;
+// packed sequences read the table chunk_offsets_kernel wrote.
+struct ChunkMap {
+    const int32_t *offs;  // nullptr for fixed-length sequences
+    int cps;              // chunks per sequence (fixed length)
+    __device__ __forceinline__ int first(int n) const { return offs ? offs[n] : n * cps; }
+    // sequence holding packed chunk gc (gc < first(N))
+    __device__ __forceinline__ int seq_of(int gc, int N) const {
+        if (!offs) return gc / cps;
+        int n = 0;
+        while (n + 1 < N && offs[n + 1] <= gc) ++n;
+        return n;
+    }
+};
+
+__device__ __forceinline__ ChunkMap chunk_map(const int32_t *cu, int fixedT, const unsigned char *ws) {
+    ChunkMap m;
+    m.offs = cu ? reinterpret_cast<const int32_t *>(ws) : nullptr;
+    m.cps = (fixedT + C - 1) / C;
+    return m;
+}
+
 // ---------------------------------------------------------------- pass 1
 struct PrepSmem {
     _Float16 kp[C * PK];    // Kp [s][c]
     _Float16 qp[C * PK];    // Qp [s][c], then Q^ in place
     _Float16 km[C * PK];    // Km [s][c], then W
-    uint16_t v[C * PK];     // bf16 V tile [r][j]
     _Float16 a16[C * P4];   // A [r][s], off-diagonal lower blocks
     _Float16 p[C * P4];     // P [r][s], lower blocks
     _Float16 tii[4][16 * PI];
     float ad[4][16 * PF];   // diagonal A blocks, fp32
     float beta[C];
     float gsum[4][KD];      // per-wave channel sums of g
+    float gnext[2][KD];     // per-wave sums of the next chunk's first 32 rows of g
 };
 
 __device__ __forceinline__ floatx4 block32(const _Float16 *lhs, const _Float16 *rhs, int bi, int bj,
@@ -109,14 +140,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     int totalT, unsigned char *__restrict__ ws) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     PrepSmem &sm = *reinterpret_cast<PrepSmem *>(smem_raw);
-    const int32_t *offs = reinterpret_cast<const int32_t *>(ws);
+    const ChunkMap cm = chunk_map(cu, fixedT, ws);
     const int gc = blockIdx.x, h = blockIdx.y;
-    if (gc >= offs[N]) return;
-    int n = 0;
-    while (n + 1 < N && offs[n + 1] <= gc) ++n;
+    if (gc >= cm.first(N)) return;
+    const int n = cm.seq_of(gc, N);
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
-    const int c0 = bos + (gc - offs[n]) * C;
+    const int c0 = bos + (gc - cm.first(n)) * C;
     const int L = min(C, eos - c0);
     // records of one head are contiguous, in chunk order
     unsigned char *rec = ws + OFFS_BYTES + ((size_t)h * gridDim.x + gc) * REC;
@@ -141,14 +171,32 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             rgv[u] = *reinterpret_cast<const uint4 *>(g + off);
         }
     }
+    // V goes straight to the two waves that solve for U~, already in the MFMA
+    // accumulator layout they use (rows 16 i + 4 lg + e, column 64 (w & 1) +
+    // 16 b + l16), so it needs no LDS tile.
+    uint16_t vz[4][4][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int idx = 256 * e + t, r = idx >> 4;
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (r < L) x = *reinterpret_cast<const uint4 *>(v + ((size_t)(c0 + r) * H + h) * VD + 8 * (idx & 15));
-        *reinterpret_cast<uint4 *>(&sm.v[r * PK + 8 * (idx & 15)]) = x;
-    }
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * i + 4 * lg + e;
+                vz[b][i][e] = 0;
+                if (w >= 2 && r < L)
+                    vz[b][i][e] = v[((size_t)(c0 + r) * H + h) * VD + 64 * (w & 1) + 16 * b + l16];
+            }
     if (t < C) sm.beta[t] = t < L ? __uint_as_float((uint32_t)beta[(size_t)(c0 + t) * H + h] << 16) : 0.f;
+    // The first half of the next chunk of this sequence (if any): its G_m is
+    // folded into this chunk's end-of-chunk scale factor.
+    uint4 rgn[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = C + 4 * rg + u;
+        rgn[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (w < 2 && c0 + r < eos)
+            rgn[u] = *reinterpret_cast<const uint4 *>(g + ((size_t)(c0 + r) * H + h) * KD + 8 * cg);
+    }
 
     float G[4][8], ex[8];
 #pragma unroll
@@ -167,6 +215,18 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         ex[e] = s - tot;
         if (lg == 3) sm.gsum[w][8 * cg + e] = s;
     }
+    if (w < 2) {
+        float gn[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) unpack8(rgn[u], gn[u]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = gn[0][e] + gn[1][e] + gn[2][e] + gn[3][e];
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            if (lg == 0) sm.gnext[w][8 * cg + e] = x;
+        }
+    }
     __syncthreads();
     {
         float kv[4][8], qv[4][8];
@@ -176,6 +236,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             unpack8(rq[u], qv[u]);
         }
         half4 kmT[8];
+        half8 kpr[4], qpr[4], kmr[4];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int ch = 8 * cg + e;
@@ -189,23 +250,31 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             if (w >= 3) pre += s2w;
             if (rg == 0) {
                 reinterpret_cast<float *>(rec + R_FM)[ch] = fast_exp(gm);
-                reinterpret_cast<float *>(rec + R_FC)[ch] = fast_exp(gcl - gm);
+                reinterpret_cast<float *>(rec + R_FC)[ch] =
+                    fast_exp(gcl - gm + sm.gnext[0][ch] + sm.gnext[1][ch]);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const float f = fast_exp(pre + G[u][e]);  // exp(G - G_m)
                 const float fi = __builtin_amdgcn_rcpf(f);
-                const int r = 4 * rg + u;
-                sm.kp[r * PK + ch] = (_Float16)(kv[u][e] * f);
-                sm.qp[r * PK + ch] = (_Float16)(qv[u][e] * f);
+                kpr[u][e] = (_Float16)(kv[u][e] * f);
+                qpr[u][e] = (_Float16)(qv[u][e] * f);
                 const _Float16 m = (_Float16)(kv[u][e] * fi);
-                sm.km[r * PK + ch] = m;
+                kmr[u][e] = m;
                 kmT[e][u] = m;
             }
         }
 #pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = 4 * rg + u;
+            *reinterpret_cast<half8 *>(&sm.kp[r * PK + 8 * cg]) = kpr[u];
+            *reinterpret_cast<half8 *>(&sm.qp[r * PK + 8 * cg]) = qpr[u];
+            *reinterpret_cast<half8 *>(&sm.km[r * PK + 8 * cg]) = kmr[u];
+        }
+#pragma unroll
         for (int e = 0; e < 8; ++e)
-            *reinterpret_cast<half4 *>(rec + R_KMT + 2 * ((size_t)(8 * cg + e) * C + kperm_pos(rg))) = kmT[e];
+            *reinterpret_cast<half4 *>(rec + R_KMT + 2 * ((size_t)(8 * cg + e) * C +
+                                                          swz(kperm_pos(rg), 8 * cg + e))) = kmT[e];
     }
     __syncthreads();
 
@@ -281,7 +350,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * i + 4 * lg + e;
                 const float xv = wside ? (float)sm.kp[r * PK + col]
-                                       : __uint_as_float((uint32_t)sm.v[r * PK + col] << 16);
+                                       : __uint_as_float((uint32_t)vz[b][i][e] << 16);
                 z[e] = sm.beta[r] * xv;
             }
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -293,27 +362,33 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             Xh[b][i] = to_half4(X[b][i]);
         }
     }
-    // ---- Q^ = Qp - P W (waves 0, 1, in place over Qp; W into the Km tile) and
-    // O^ = P U~ (waves 2, 3, straight to the workspace with U~)
+    // ---- Q^ = Qp - P W (waves 0, 1, in place over Qp; W into the Km tile);
+    // U~ straight to the workspace (waves 2, 3)
+    if (wside) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int col = 64 * (w & 1) + 16 * b + l16;
+        for (int b = 0; b < 4; ++b) {
+            const int col = 64 * (w & 1) + 16 * b + l16;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int rb = 0; rb < 4; ++rb) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i <= rb; ++i) acc = mma16(frag4(sm.p, P4, 16 * rb, 16 * i, lane), Xh[b][i], acc);
-            if (wside) {
+                for (int i = 0; i <= rb; ++i) acc = mma16(frag4(sm.p, P4, 16 * rb, 16 * i, lane), Xh[b][i], acc);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * rb + 4 * lg + e;
                     sm.qp[r * PK + col] = (_Float16)((float)sm.qp[r * PK + col] - acc[e]);
                     sm.km[r * PK + col] = Xh[b][rb][e];
                 }
-            } else {
-                *reinterpret_cast<half4 *>(rec + R_UT + 2 * ((size_t)col * C + 16 * rb + 4 * lg)) = Xh[b][rb];
-                *reinterpret_cast<floatx4 *>(rec + R_OH + 4 * ((size_t)col * C + 16 * rb + 4 * lg)) = acc;
             }
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int col = 64 * (w & 1) + 16 * b + l16;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+                *reinterpret_cast<half4 *>(rec + R_UT + 2 * ((size_t)col * C + swz(16 * rb + 4 * lg, col))) =
+                    Xh[b][rb];
         }
     }
     __syncthreads();
@@ -335,42 +410,57 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             qv[i] = q0[i];
             qv[4 + i] = q1[i];
         }
-        *reinterpret_cast<half8 *>(rec + R_W + 2 * ((size_t)r * KD + 8 * b)) = wv;
+        *reinterpret_cast<half8 *>(rec + R_W + 2 * ((size_t)r * KD + swz(8 * b, r))) = wv;
         *reinterpret_cast<half8 *>(rec + R_QH + 2 * ((size_t)r * KD + 8 * b)) = qv;
+    }
+    // ---- P rows, with the blocks above the diagonal zeroed (16-byte stores)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int idx = 256 * e + t, r = idx >> 3, b = idx & 7;
+        half8 pv;
+        if ((b >> 1) > (r >> 4)) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pv[i] = (_Float16)0.f;
+        } else {
+            const half4 p0 = *reinterpret_cast<const half4 *>(&sm.p[r * P4 + 8 * b]);
+            const half4 p1 = *reinterpret_cast<const half4 *>(&sm.p[r * P4 + 8 * b + 4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pv[i] = p0[i];
+                pv[4 + i] = p1[i];
+            }
+        }
+        *reinterpret_cast<half8 *>(rec + R_P + 2 * ((size_t)r * C + 8 * b)) = pv;
     }
 }
 
 // ---------------------------------------------------------------- pass 2
-// One chunk's state-pass operands in LDS: W, Q^ ([64][128] fp16) and Km^T
-// ([128][64] fp16) without padding, each row's 16-byte blocks XOR-permuted by
-// (row & 7) so that the 16 rows of an MFMA fragment read hit distinct banks;
-// then exp(G_m), exp(G_C - G_m).  Loader waves fill it with direct
-// global-to-LDS loads: 49 wave-wide 1 KB segments, each lane fetching the
-// global 16-byte block that belongs in its LDS slot.
+// One chunk's state-pass operands in LDS, for a workgroup owning VT = 16 NSW
+// value columns: W ([64][128] fp16) and Km^T ([128][64] fp16) without padding,
+// each row's 16-byte blocks XOR-permuted by (row & 7) as stored (swz); the
+// scale factors; then the workgroup's columns of U~ (blocks permuted by the
+// column index).  Loader waves copy it with direct global-to-LDS loads in
+// wave-wide 1 KB segments.
+template <int NSW>
 struct ChunkTiles {
     _Float16 w[C * KD];
-    _Float16 qh[C * KD];
     _Float16 kmt[KD * C];
     float fmc[2 * KD];
+    _Float16 ut[16 * NSW * C];  // [j][r]
 };
-constexpr int SEGMENTS = (int)sizeof(ChunkTiles) / 1024;  // 49
-static_assert(sizeof(ChunkTiles) == 49 * 1024, "segment count");
+static_assert(sizeof(ChunkTiles<1>) == 35 * 1024, "segment count");
 
-// NSW state waves own 16 value columns each (a VT = 16 NSW column tile);
-// NLW loader waves stream the tiles (one CU sustains its highest direct-load
-// rate only with several waves' loads in flight).
-template <int NLW>
+// NSW state waves own 16 value columns each; NLW loader waves stream the
+// tiles (one CU sustains its highest direct-load rate only with several
+// waves' loads in flight).
+template <int NSW, int NLW>
 struct StateSmem {
-    ChunkTiles buf[2];           // by chunk parity
-    uint32_t sink[NLW][64];      // landing slots of the L2 prefetches (never read)
+    ChunkTiles<NSW> buf[2];  // by chunk parity
 };
-
-// Chunks of look-ahead for the L2 prefetch of the tiles.
-constexpr int PREFETCH_AHEAD = 3;
 
 // Workgroup barrier for the loader waves, which touch LDS only through their
-// direct loads and wait for those explicitly: no fence, so the compiler does
-// not add a wait for every outstanding load (the L2 prefetches included).
+// direct loads and wait for those explicitly: no fence, so the compiler adds
+// no waits of its own.
 __device__ __forceinline__ void loader_barrier() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
@@ -379,39 +469,30 @@ __device__ __forceinline__ void loader_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Global source of LDS slot p (16-byte units) of a ChunkTiles image.
-__device__ __forceinline__ const unsigned char *tile_source(const unsigned char *rec, int p) {
-    if (p < 2048) {  // W, Q^: 16 blocks per 256-byte row
-        const int t = p >> 10, r = (p >> 4) & 63, b = (p & 15) ^ (r & 7);
-        return rec + 16384 * t + 256 * r + 16 * b;
-    }
-    if (p < 3072) {  // Km^T: 8 blocks per 128-byte row
-        const int c = (p - 2048) >> 3, b = (p & 7) ^ (c & 7);
-        return rec + R_KMT + 128 * c + 16 * b;
-    }
-    return rec + R_FM + 16 * (p - 3072);
+// Global source of LDS slot p (16-byte units) of a ChunkTiles<NSW> image for
+// value columns [col0, col0 + 16 NSW): the record's first 33 KB (W, Km^T,
+// scale factors) and the tile's U~ columns, both copied linearly.
+template <int NSW>
+__device__ __forceinline__ const unsigned char *tile_source(const unsigned char *rec, int p,
+                                                            int col0) {
+    constexpr int HEAD = (int)(R_UT / 16);  // 2112
+    return p < HEAD ? rec + 16 * p : rec + R_UT + 128 * col0 + 16 * (p - HEAD);
 }
 
-template <int NLW>
-__device__ __forceinline__ void load_tiles(ChunkTiles &dst, const unsigned char *rec, int lw,
-                                           int lane) {
+// One direct global-to-LDS load: 16 bytes per lane from `src`, landing at
+// lds + 16 lane (lds is wave-uniform).
+__device__ __forceinline__ void lds_dma16(const unsigned char *src, unsigned char *lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+template <int NSW, int NLW>
+__device__ __forceinline__ void load_tiles(unsigned char *dst, const unsigned char *rec, int col0,
+                                           int lw, int lane) {
+    constexpr int SEGMENTS = (int)(sizeof(ChunkTiles<NSW>) / 1024);
     for (int s = lw; s < SEGMENTS; s += NLW) {
-        __builtin_amdgcn_global_load_lds(
-            tile_source(rec, 64 * s + lane),
-            (__attribute__((address_space(3))) void *)(reinterpret_cast<unsigned char *>(&dst) + 1024 * s),
-            16, 0, 0);
+        const unsigned char *src = tile_source<NSW>(rec, 64 * s + lane, col0);
+        lds_dma16(src, dst + 1024 * s);
     }
-}
-
-// Pull one chunk's tile bytes (the first 48 KB of the record and the 1 KB of
-// scale factors: 392 lines of 128 bytes) towards L2, one 4-byte load per line,
-// spread over the `parts` loader waves of the unit's workgroups; the loaded
-// words land in a scratch LDS slot nobody reads.
-__device__ __forceinline__ void prefetch_tiles(uint32_t *sink, const unsigned char *rec, int part,
-                                               int lane) {
-    const int li = min(64 * part + lane, 391);
-    const unsigned char *src = li < 384 ? rec + 128 * li : rec + R_FM + 128 * (li - 384);
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)sink, 4, 0, 0);
 }
 
 // 16x16x32 fragment from a swizzled tile with `rowlen` halves per row.
@@ -420,29 +501,6 @@ __device__ __forceinline__ half8 frag8_sw(const _Float16 *base, int rowlen, int 
     const int r = row0 + (lane & 15);
     const int kb = (4 * ks + (lane >> 4)) ^ (r & 7);
     return *reinterpret_cast<const half8 *>(base + r * rowlen + 8 * kb);
-}
-
-// Output rows of one chunk through a buffer resource that spans exactly the
-// chunk's L valid rows: the hardware range check drops the rows past L, and
-// the per-lane offset is loop-invariant.
-__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, float x) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
-}
-__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, bf16_t x) {
-    __builtin_amdgcn_raw_buffer_store_b16(x.bits, r, off, 0, 0);
-}
-
-template <typename TOut>
-__device__ __forceinline__ void store_o(TOut *o, const floatx4 (&Y)[4], int c0, int L, int H,
-                                        int lane_off) {
-    const int row_bytes = H * VD * (int)sizeof(TOut);
-    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        o + (size_t)c0 * H * VD, 0, L * row_bytes, 0x00020000);
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            store_elem(r, lane_off + (16 * rb + e) * row_bytes, from_f32<TOut>(Y[rb][e]));
 }
 
 // B fragment of a k-permuted product from accumulator blocks 2 ks, 2 ks + 1.
@@ -456,94 +514,103 @@ __device__ __forceinline__ half8 bfrag(const floatx4 &lo, const floatx4 &hi) {
     return b;
 }
 
-// One chunk of the state chain for one state wave (16 value columns), all in
-// registers: the left operands come from the LDS tiles, the right operands
-// are the wave's own accumulators.  The output products are issued after U
-// is formed, off the chain.
-template <typename TOut>
-__device__ __forceinline__ void state_chunk(floatx4 (&S)[8], const ChunkTiles &tl,
-                                            const half4 (&ucur)[4], const floatx4 (&ocur)[4],
-                                            TOut *o, int c0, int L, int H, int o_lane_off,
-                                            int lane) {
-    const int lg = lane >> 4;
-    // S' = Diag(exp(G_m)) S
+// One chunk of the state chain for state wave `sw` (16 value columns), all in
+// registers: the left operands and U~ come from the LDS tiles, the right
+// operands are the wave's own accumulators, which hold S' = Diag(exp(G_m)) S
+// on entry.  S' is published (as the fp16 B
+// fragments the output product needs) to the chunk's record.  Each phase's
+// LDS reads are issued as a group ahead of the arithmetic that consumes them.
+template <int NSW>
+__device__ __forceinline__ void state_chunk(floatx4 (&S)[8], const ChunkTiles<NSW> &tl,
+                                            unsigned char *sp_out, int sw, int lane) {
+    const int lg = lane >> 4, j = 16 * sw + (lane & 15);
     floatx4 f[8];
+    half8 a[4][4];
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) f[cb] = *reinterpret_cast<const floatx4 *>(&tl.fmc[16 * cb + 4 * lg]);
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) a[ks][rb] = frag8_sw(tl.w, KD, 16 * rb, ks, lane);
+    half4 ut[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        const int blk = (2 * rb + (lg >> 1)) ^ (j & 7);
+        ut[rb] = *reinterpret_cast<const half4 *>(&tl.ut[j * C + 8 * blk + 4 * (lg & 1)]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    half8 bs[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) bs[ks] = bfrag(S[2 * ks], S[2 * ks + 1]);
+    // X = W S'
+    floatx4 X[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) X[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) X[rb] = mma32(a[ks][rb], bs[ks], X[rb]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        *reinterpret_cast<half8 *>(sp_out + 1024 * ks + 16 * lane) = bs[ks];
+    half8 k2[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) k2[ks][cb] = frag8_sw(tl.kmt, C, 16 * cb, ks, lane);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) f[cb] = *reinterpret_cast<const floatx4 *>(&tl.fmc[KD + 16 * cb + 4 * lg]);
+    __builtin_amdgcn_sched_barrier(0);
+    // U = U~ - X
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[rb][e] = (float)ut[rb][e] - X[rb][e];
+    half8 bu[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) bu[ks] = bfrag(X[2 * ks], X[2 * ks + 1]);
+    // S'' = Diag(exp(G_C - G_m + G_m')) (S' + Km^T U): the next chunk's S'
+    // (G_m' its mid-chunk reference; for a sequence's last chunk the factor is
+    // exp(G_C - G_m), which leaves S itself)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) S[cb] = mma32(k2[ks][cb], bu[ks], S[cb]);
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[cb][i] *= f[cb][i];
-    half8 bs[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) bs[ks] = bfrag(S[2 * ks], S[2 * ks + 1]);
-    // U = U~ - W S'
-    floatx4 X[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-        X[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) X[rb] = mma32(frag8_sw(tl.w, KD, 16 * rb, ks, lane), bs[ks], X[rb]);
-    }
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) X[rb][e] = (float)ucur[rb][e] - X[rb][e];
-    half8 bu[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) bu[ks] = bfrag(X[2 * ks], X[2 * ks + 1]);
-    // O = Q^ S' + O^
-    floatx4 Y[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-        Y[rb] = ocur[rb];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) Y[rb] = mma32(frag8_sw(tl.qh, KD, 16 * rb, ks, lane), bs[ks], Y[rb]);
-    }
-    // S = Diag(exp(G_C - G_m)) (S' + Km^T U)
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) f[cb] = *reinterpret_cast<const floatx4 *>(&tl.fmc[KD + 16 * cb + 4 * lg]);
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) S[cb] = mma32(frag8_sw(tl.kmt, C, 16 * cb, ks, lane), bu[ks], S[cb]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[cb][i] *= f[cb][i];
-    }
-    store_o(o, Y, c0, L, H, o_lane_off);
 }
 
 // Grid: one workgroup per (unit, value tile), XCD-aware: workgroup b runs on
 // XCD b mod 8, and all value tiles of a unit share that XCD (and its L2),
-// which serves their common W, Q^, Km^T tiles.
-template <int NSW, int NLW, typename TOut>
+// which serves their common W, Km^T tiles.  Waves: NSW state waves, NLW
+// loader waves; one barrier per chunk.
+template <int NSW, int NLW>
 __global__ __launch_bounds__(64 * (NSW + NLW)) void chunk_state_kernel(
-    const float *s0, TOut *__restrict__ o, float *sT, const int32_t *__restrict__ cu, int fixedT,
-    int N, int H, int totalT, int cap, const unsigned char *__restrict__ ws) {
+    const float *s0, float *sT, const int32_t *__restrict__ cu, int fixedT, int N, int H,
+    int totalT, int cap, unsigned char *__restrict__ ws) {
     constexpr int VTILE = 16 * NSW, NVT = VD / VTILE;
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    StateSmem<NLW> &sm = *reinterpret_cast<StateSmem<NLW> *>(smem_raw);
-    const int32_t *offs = reinterpret_cast<const int32_t *>(ws);
+    StateSmem<NSW, NLW> &sm = *reinterpret_cast<StateSmem<NSW, NLW> *>(smem_raw);
+    const ChunkMap cm = chunk_map(cu, fixedT, ws);
     const int b = blockIdx.x, slot = b >> 3;
     const int vt = slot % NVT;
     const int unit = (slot / NVT) * 8 + (b & 7);
     if (unit >= N * H) return;
     const int n = unit / H, h = unit - n * H;
-    int bos, eos;
-    seq_bounds(cu, n, fixedT, totalT, bos, eos);
-    const int ch0 = offs[n];
-    const int nchunks = offs[n + 1] - ch0;
-    const unsigned char *recs = ws + OFFS_BYTES;
+    const int ch0 = cm.first(n);
+    const int nchunks = cm.first(n + 1) - ch0;
+    unsigned char *recs = ws + OFFS_BYTES;
     auto rec = [&](int ci) { return recs + ((size_t)h * cap + ch0 + ci) * REC; };
+    const int col0 = vt * VTILE;
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lg = lane >> 4;
 
     if (w < NSW) {
-        const int jcol = vt * VTILE + 16 * w + (lane & 15);  // this lane's value column
+        const int jcol = col0 + 16 * w + (lane & 15);  // this lane's value column
         const size_t sbase = (size_t)unit * (KD * VD) + jcol;
-        const int o_lane_off = ((4 * lg * H + h) * VD + jcol) * (int)sizeof(TOut);
+        const int tile = (col0 >> 4) + w;                // 16-column tile of the S' record
         floatx4 S[8];
         if (s0) {
 #pragma unroll
@@ -554,35 +621,19 @@ __global__ __launch_bounds__(64 * (NSW + NLW)) void chunk_state_kernel(
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) S[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
-        // this wave's slices of U~ and O^, fetched one chunk ahead into two
-        // register sets used alternately
-        half4 ua[4], ub[4];
-        floatx4 oa[4], ob[4];
-        auto fetch = [&](int ci, half4 (&un)[4], floatx4 (&on)[4]) {
-            const unsigned char *r = rec(ci);
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                un[rb] = *reinterpret_cast<const half4 *>(r + R_UT + 2 * ((size_t)jcol * C + 16 * rb + 4 * lg));
-                on[rb] = *reinterpret_cast<const floatx4 *>(r + R_OH + 4 * ((size_t)jcol * C + 16 * rb + 4 * lg));
-            }
-        };
-        // The initial state is complete before the loop, and the prefetches are
-        // unconditional (the index clamped to the last chunk), so that the
-        // memory waits inside the loop are those for the register set about
-        // to be used.
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        const int last = nchunks - 1;
-        if (nchunks > 0) fetch(0, ua, oa);
         __syncthreads();
-        for (int ci = 0; ci < nchunks; ci += 2) {
-            fetch(min(ci + 1, last), ub, ob);
-            int c0 = bos + ci * C;
-            state_chunk(S, sm.buf[0], ua, oa, o, c0, min(C, eos - c0), H, o_lane_off, lane);
-            __syncthreads();
-            if (ci + 1 >= nchunks) break;
-            fetch(min(ci + 2, last), ua, oa);
-            c0 += C;
-            state_chunk(S, sm.buf[1], ub, ob, o, c0, min(C, eos - c0), H, o_lane_off, lane);
+        if (nchunks > 0) {
+            // S' of the first chunk; later chunks receive theirs from the
+            // previous chunk's end-of-chunk factor
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) {
+                const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.buf[0].fmc[16 * cb + 4 * lg]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[cb][i] *= f[i];
+            }
+        }
+        for (int ci = 0; ci < nchunks; ++ci) {
+            state_chunk<NSW>(S, sm.buf[ci & 1], rec(ci) + R_SP + 4096 * tile, w, lane);
             __syncthreads();
         }
         if (sT) {
@@ -592,54 +643,113 @@ __global__ __launch_bounds__(64 * (NSW + NLW)) void chunk_state_kernel(
                 for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * cb + 4 * lg + i) * VD] = S[cb][i];
         }
     } else {
-        // loader waves: chunk ci + 1 streams into the other buffer while the
+        // Loader waves: chunk ci + 1 streams into the other buffer while the
         // state waves work on chunk ci; each wave waits for its own loads
-        // before the barrier that hands the buffer over
-        // Loader waves 0..6 of the unit (across its workgroups) also prefetch
-        // 1/7 of chunk ci + 1 + PREFETCH_AHEAD's tiles into L2 after their
-        // tile loads, and wait for all but that last load (loads complete in
-        // issue order); the others wait for all their loads.
+        // before the barrier that hands the buffer over.
         const int lw = w - NSW;
-        const int part = __builtin_amdgcn_readfirstlane(vt * NLW + lw);
-        uint32_t *sink = sm.sink[lw];
-        const int last = nchunks - 1;
         if (nchunks > 0) {
-            if (part < 7) {
-#pragma unroll 1
-                for (int a = 1; a <= PREFETCH_AHEAD; ++a) prefetch_tiles(sink, rec(min(a, last)), part, lane);
-            }
-            load_tiles<NLW>(sm.buf[0], rec(0), lw, lane);
+            load_tiles<NSW, NLW>(reinterpret_cast<unsigned char *>(&sm.buf[0]), rec(0), col0, lw, lane);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         }
         __syncthreads();
         for (int ci = 0; ci < nchunks; ++ci) {
             if (ci + 1 < nchunks) {
-                load_tiles<NLW>(sm.buf[(ci + 1) & 1], rec(ci + 1), lw, lane);
-                if (part < 7) {
-                    prefetch_tiles(sink, rec(min(ci + 1 + PREFETCH_AHEAD, last)), part, lane);
-                    __builtin_amdgcn_s_waitcnt(0x0F71);  // vmcnt(1)
-                } else {
-                    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-                }
+                load_tiles<NSW, NLW>(reinterpret_cast<unsigned char *>(&sm.buf[(ci + 1) & 1]), rec(ci + 1),
+                                     col0, lw, lane);
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             }
             loader_barrier();
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing left in flight
     }
 }
 
-template <int NSW, int NLW, typename TOut>
-hipError_t launch_state(const float *s0, void *o, float *sT, const int32_t *cu, int N, int fixedT,
-                        int totalT, int H, int cap, const unsigned char *ws, hipStream_t stream) {
-    auto kern = chunk_state_kernel<NSW, NLW, TOut>;
-    constexpr int smem = (int)sizeof(StateSmem<NLW>);
+template <int NSW, int NLW>
+hipError_t launch_state(const float *s0, float *sT, const int32_t *cu, int N, int fixedT,
+                        int totalT, int H, int cap, unsigned char *ws, hipStream_t stream) {
+    auto kern = chunk_state_kernel<NSW, NLW>;
+    constexpr int smem = (int)sizeof(StateSmem<NSW, NLW>);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     const int groups = (N * H + 7) / 8;
-    hipLaunchKernelGGL(kern, dim3(groups * 8 * (VD / (16 * NSW))), dim3(64 * (NSW + NLW)), smem, stream,
-                       s0, static_cast<TOut *>(o), sT, cu, fixedT, N, H, totalT, cap, ws);
+    hipLaunchKernelGGL(kern, dim3(groups * 8 * (VD / (16 * NSW))), dim3(64 * (NSW + NLW)), smem,
+                       stream, s0, sT, cu, fixedT, N, H, totalT, cap, ws);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- pass 3
+// O = Q^ S' + P U~ for every (chunk, head) at once: one workgroup of 4 waves
+// per record, wave w producing value tiles 2 w and 2 w + 1 (16 columns each).
+// Operands are read as MFMA fragments straight from the record (Q^ with its
+// permuted contraction index matching the S' fragments; P and U~ in natural
+// order); outputs leave through a buffer resource spanning the chunk's valid
+// rows.
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+}
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, bf16_t x) {
+    __builtin_amdgcn_raw_buffer_store_b16(x.bits, r, off, 0, 0);
+}
+
+template <typename TOut>
+__global__ __launch_bounds__(256) void chunk_output_kernel(TOut *__restrict__ o,
+                                                           const int32_t *__restrict__ cu,
+                                                           int fixedT, int N, int H, int totalT,
+                                                           const unsigned char *__restrict__ ws) {
+    const ChunkMap cm = chunk_map(cu, fixedT, ws);
+    const int gc = blockIdx.x, h = blockIdx.y;
+    if (gc >= cm.first(N)) return;
+    const int n = cm.seq_of(gc, N);
+    int bos, eos;
+    seq_bounds(cu, n, fixedT, totalT, bos, eos);
+    const int c0 = bos + (gc - cm.first(n)) * C;
+    const int L = min(C, eos - c0);
+    const unsigned char *rec = ws + OFFS_BYTES + ((size_t)h * gridDim.x + gc) * REC;
+
+    const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    half8 aq[4][4], ap[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            aq[ks][rb] = *reinterpret_cast<const half8 *>(rec + R_QH + 2 * ((16 * rb + l16) * KD + 8 * (4 * ks + lg)));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            ap[ks][rb] = *reinterpret_cast<const half8 *>(rec + R_P + 2 * ((16 * rb + l16) * C + 32 * ks + 8 * lg));
+    const int row_bytes = H * VD * (int)sizeof(TOut);
+    __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        o + (size_t)c0 * H * VD, 0, L * row_bytes, 0x00020000);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int tile = 2 * w + tt, j = 16 * tile + l16;
+        half8 bs[4], bu[2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            bs[ks] = *reinterpret_cast<const half8 *>(rec + R_SP + 4096 * tile + 1024 * ks + 16 * lane);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            bu[ks] = *reinterpret_cast<const half8 *>(rec + R_UT + 2 * (j * C + swz(32 * ks + 8 * lg, j)));
+        floatx4 Y[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) Y[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) Y[rb] = mma32(ap[ks][rb], bu[ks], Y[rb]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) Y[rb] = mma32(aq[ks][rb], bs[ks], Y[rb]);
+        const int lane_off = ((4 * lg * H + h) * VD + j) * (int)sizeof(TOut);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                store_elem(orsrc, lane_off + (16 * rb + e) * row_bytes, from_f32<TOut>(Y[rb][e]));
+    }
 }
 
 int max_chunks(int N, int totalT, int fixedT, bool varlen) {
@@ -674,10 +784,13 @@ hipError_t launch_chunk_split(const void *q, const void *k, const void *v, const
     if (N == 0 || H == 0) return hipSuccess;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     const int cap = max_chunks(N, totalT, fixedT, cu != nullptr);
-    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, stream, cu, fixedT, N, totalT,
-                       cap, reinterpret_cast<int32_t *>(ws));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (cu) {
+        hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, stream, cu, fixedT, N,
+                           totalT, cap, reinterpret_cast<int32_t *>(ws));
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (cap > 0) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(chunk_prep_kernel),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PrepSmem));
@@ -689,11 +802,15 @@ hipError_t launch_chunk_split(const void *q, const void *k, const void *v, const
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    return out_bf16
-               ? launch_state<STATE_WAVES, LOADER_WAVES, bf16_t>(s0, o, sT, cu, N, fixedT, totalT, H,
-                                                                 cap, ws, stream)
-               : launch_state<STATE_WAVES, LOADER_WAVES, float>(s0, o, sT, cu, N, fixedT, totalT, H,
-                                                                cap, ws, stream);
+    e = launch_state<STATE_WAVES, LOADER_WAVES>(s0, sT, cu, N, fixedT, totalT, H, cap, ws, stream);
+    if (e != hipSuccess || cap == 0) return e;
+    if (out_bf16)
+        hipLaunchKernelGGL(chunk_output_kernel<bf16_t>, dim3(cap, H), dim3(256), 0, stream,
+                           static_cast<bf16_t *>(o), cu, fixedT, N, H, totalT, ws);
+    else
+        hipLaunchKernelGGL(chunk_output_kernel<float>, dim3(cap, H), dim3(256), 0, stream,
+                           static_cast<float *>(o), cu, fixedT, N, H, totalT, ws);
+    return hipGetLastError();
 }
 
 }  // namespace kda
