@@ -34,12 +34,13 @@ constexpr int PC = 72;   // LDS pitch (halves), [128][64] tiles read as 16-byte 
 constexpr int P4 = 76;   // LDS pitch (halves), [64][64] tiles read as 8-byte fragments
 constexpr int PI = 20;   // LDS pitch (halves), 16 x 16 fp16 blocks
 constexpr int PF = 17;   // LDS pitch (floats), 16 x 16 fp32 blocks
+constexpr int VTP = 68;  // LDS pitch (bf16), V^T staging tile [128][64]
 
 // Per-(chunk, head) record in the workspace (bytes).  The contraction index
 // of W, Q^ (c) and Km^T (s) is stored permuted within each 32-wide block,
 // see kperm_pos below.  The first 33 KB are what the state pass streams.
 constexpr size_t R_W = 0;             // fp16 [64][128]  W     [r][c]
-constexpr size_t R_KMT = 16384;       // fp16 [128][64]  Km^T  [c][s]
+constexpr size_t R_KMT = 16384;       // fp16 [128][64]  Diag(f) Km^T [c][s], f = the R_FC factor
 constexpr size_t R_FM = 32768;        // fp32 [128]      exp(G_m)
 constexpr size_t R_FC = 33280;        // fp32 [128]      exp(G_C - G_m + G_m of the next chunk)
 constexpr size_t R_UT = 33792;        // fp16 [128][64]  U~    [j][r]
@@ -171,21 +172,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             rgv[u] = *reinterpret_cast<const uint4 *>(g + off);
         }
     }
-    // V goes straight to the two waves that solve for U~, already in the MFMA
-    // accumulator layout they use (rows 16 i + 4 lg + e, column 64 (w & 1) +
-    // 16 b + l16), so it needs no LDS tile.
-    uint16_t vz[4][4][4];
+    uint4 rv[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * i + 4 * lg + e;
-                vz[b][i][e] = 0;
-                if (w >= 2 && r < L)
-                    vz[b][i][e] = v[((size_t)(c0 + r) * H + h) * VD + 64 * (w & 1) + 16 * b + l16];
-            }
+    for (int u = 0; u < 4; ++u) {
+        const int r = 4 * rg + u;
+        rv[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (r < L) rv[u] = *reinterpret_cast<const uint4 *>(v + ((size_t)(c0 + r) * H + h) * VD + 8 * cg);
+    }
     if (t < C) sm.beta[t] = t < L ? __uint_as_float((uint32_t)beta[(size_t)(c0 + t) * H + h] << 16) : 0.f;
     // The first half of the next chunk of this sequence (if any): its G_m is
     // folded into this chunk's end-of-chunk scale factor.
@@ -215,6 +208,25 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         ex[e] = s - tot;
         if (lg == 3) sm.gsum[w][8 * cg + e] = s;
     }
+    // V^T staging copy (bf16 [column][row], pitch VTP) in the A/P tiles, which
+    // are not used before the Gram phase: the two waves that solve for U~
+    // read it back in their MFMA accumulator layout
+    {
+        uint16_t *vst = reinterpret_cast<uint16_t *>(sm.a16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint16_t c4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t wv = (&rv[u].x)[e >> 1];
+                c4[u] = (uint16_t)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
+            }
+            uint2 pk;
+            pk.x = (uint32_t)c4[0] | ((uint32_t)c4[1] << 16);
+            pk.y = (uint32_t)c4[2] | ((uint32_t)c4[3] << 16);
+            *reinterpret_cast<uint2 *>(&vst[(8 * cg + e) * VTP + 4 * rg]) = pk;
+        }
+    }
     if (w < 2) {
         float gn[4][8];
 #pragma unroll
@@ -228,6 +240,17 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         }
     }
     __syncthreads();
+    // V in the accumulator layout of waves 2, 3 (rows 16 i + 4 lg + e, column
+    // 64 (w & 1) + 16 b + l16)
+    uint2 vz[4][4];
+    if (w >= 2) {
+        const uint16_t *vst = reinterpret_cast<const uint16_t *>(sm.a16);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vz[b][i] = *reinterpret_cast<const uint2 *>(&vst[(64 * (w & 1) + 16 * b + l16) * VTP + 16 * i + 4 * lg]);
+    }
     {
         float kv[4][8], qv[4][8];
 #pragma unroll
@@ -248,10 +271,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             if (w >= 1) pre += s0w;
             if (w >= 2) pre += s1w;
             if (w >= 3) pre += s2w;
+            // end-of-chunk factor: exp(G_C - G_m + G_m of the next chunk)
+            const float fe = fast_exp(gcl - gm + sm.gnext[0][ch] + sm.gnext[1][ch]);
             if (rg == 0) {
                 reinterpret_cast<float *>(rec + R_FM)[ch] = fast_exp(gm);
-                reinterpret_cast<float *>(rec + R_FC)[ch] =
-                    fast_exp(gcl - gm + sm.gnext[0][ch] + sm.gnext[1][ch]);
+                reinterpret_cast<float *>(rec + R_FC)[ch] = fe;
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -259,9 +283,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
                 const float fi = __builtin_amdgcn_rcpf(f);
                 kpr[u][e] = (_Float16)(kv[u][e] * f);
                 qpr[u][e] = (_Float16)(qv[u][e] * f);
-                const _Float16 m = (_Float16)(kv[u][e] * fi);
-                kmr[u][e] = m;
-                kmT[e][u] = m;
+                kmr[u][e] = (_Float16)(kv[u][e] * fi);
+                kmT[e][u] = (_Float16)(kv[u][e] * fi * fe);
             }
         }
 #pragma unroll
@@ -272,9 +295,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             *reinterpret_cast<half8 *>(&sm.km[r * PK + 8 * cg]) = kmr[u];
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            *reinterpret_cast<half4 *>(rec + R_KMT + 2 * ((size_t)(8 * cg + e) * C +
-                                                          swz(kperm_pos(rg), 8 * cg + e))) = kmT[e];
+        for (int e = 0; e < 8; ++e) {
+            const int c = 8 * cg + e;
+            *reinterpret_cast<half4 *>(rec + R_KMT + 2 * ((size_t)c * C + swz(kperm_pos(rg), c))) = kmT[e];
+        }
     }
     __syncthreads();
 
@@ -338,38 +362,40 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     // Waves 0, 1 solve for the Kp columns (W), waves 2, 3 for the V columns (U~);
     // each wave owns four 16-column blocks.
     const bool wside = w < 2;
-    floatx4 X[4][4];  // [column block][row block], fp32
-    half4 Xh[4][4];
+    // Row block i outer, the four independent column blocks inner.
+    half4 Xh[4][4];  // [column block][row block]
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int col = 64 * (w & 1) + 16 * b + l16;
+    for (int i = 0; i < 4; ++i) {
+        const floatx4 bt = *reinterpret_cast<const floatx4 *>(&sm.beta[16 * i + 4 * lg]);
+        const half4 ti = frag4(sm.tii[i], PI, 0, 0, lane);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int b = 0; b < 4; ++b) {
+            const int col = 64 * (w & 1) + 16 * b + l16;
             floatx4 z;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * i + 4 * lg + e;
+                const uint32_t vw = (e < 2) ? vz[b][i].x : vz[b][i].y;
                 const float xv = wside ? (float)sm.kp[r * PK + col]
-                                       : __uint_as_float((uint32_t)vz[b][i][e] << 16);
-                z[e] = sm.beta[r] * xv;
+                                       : __uint_as_float((e & 1) ? (vw & 0xffff0000u) : (vw << 16));
+                z[e] = bt[e] * xv;
             }
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int jj = 0; jj < i; ++jj) acc = mma16(frag4(sm.a16, P4, 16 * i, 16 * jj, lane), Xh[b][jj], acc);
 #pragma unroll
             for (int e = 0; e < 4; ++e) z[e] -= acc[e];
-            X[b][i] = mma16(frag4(sm.tii[i], PI, 0, 0, lane), to_half4(z), floatx4{0.f, 0.f, 0.f, 0.f});
-            Xh[b][i] = to_half4(X[b][i]);
+            Xh[b][i] = to_half4(mma16(ti, to_half4(z), floatx4{0.f, 0.f, 0.f, 0.f}));
         }
     }
     // ---- Q^ = Qp - P W (waves 0, 1, in place over Qp; W into the Km tile);
     // U~ straight to the workspace (waves 2, 3)
     if (wside) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int col = 64 * (w & 1) + 16 * b + l16;
+        for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
+            for (int b = 0; b < 4; ++b) {
+                const int col = 64 * (w & 1) + 16 * b + l16;
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int i = 0; i <= rb; ++i) acc = mma16(frag4(sm.p, P4, 16 * rb, 16 * i, lane), Xh[b][i], acc);
@@ -381,37 +407,55 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
                 }
             }
         }
-    } else {
+    }
+    __syncthreads();
+    // U~ (waves 2, 3) into a staging copy laid out as in the record, over the
+    // Kp tile (no longer read), for linear global stores below
+    if (!wside) {
+        _Float16 *stage = sm.kp;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int col = 64 * (w & 1) + 16 * b + l16;
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb)
-                *reinterpret_cast<half4 *>(rec + R_UT + 2 * ((size_t)col * C + swz(16 * rb + 4 * lg, col))) =
-                    Xh[b][rb];
+                *reinterpret_cast<half4 *>(&stage[col * C + swz(16 * rb + 4 * lg, col)]) = Xh[b][rb];
         }
     }
-    __syncthreads();
     // ---- W and Q^ rows to the workspace, k-permuted (16-byte stores: stored
     // block b of a row takes logical 4-groups 8 (b >> 2) + (b & 3) and that + 4)
+    // (stored 16-byte block bp of a W row holds logical block bp ^ (r & 7))
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int idx = 256 * e + t, r = idx >> 4, b = idx & 15;
-        const int l0 = 32 * (b >> 2) + 4 * (b & 3), l1 = l0 + 16;
+        const int idx = 256 * e + t, r = idx >> 4, bp = idx & 15;
         half8 wv, qv;
-        const half4 w0 = *reinterpret_cast<const half4 *>(&sm.km[r * PK + l0]);
-        const half4 w1 = *reinterpret_cast<const half4 *>(&sm.km[r * PK + l1]);
-        const half4 q0 = *reinterpret_cast<const half4 *>(&sm.qp[r * PK + l0]);
-        const half4 q1 = *reinterpret_cast<const half4 *>(&sm.qp[r * PK + l1]);
+        {
+            const int b = bp ^ (r & 7), l0 = 32 * (b >> 2) + 4 * (b & 3), l1 = l0 + 16;
+            const half4 w0 = *reinterpret_cast<const half4 *>(&sm.km[r * PK + l0]);
+            const half4 w1 = *reinterpret_cast<const half4 *>(&sm.km[r * PK + l1]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wv[i] = w0[i];
-            wv[4 + i] = w1[i];
-            qv[i] = q0[i];
-            qv[4 + i] = q1[i];
+            for (int i = 0; i < 4; ++i) {
+                wv[i] = w0[i];
+                wv[4 + i] = w1[i];
+            }
         }
-        *reinterpret_cast<half8 *>(rec + R_W + 2 * ((size_t)r * KD + swz(8 * b, r))) = wv;
-        *reinterpret_cast<half8 *>(rec + R_QH + 2 * ((size_t)r * KD + 8 * b)) = qv;
+        {
+            const int l0 = 32 * (bp >> 2) + 4 * (bp & 3), l1 = l0 + 16;
+            const half4 q0 = *reinterpret_cast<const half4 *>(&sm.qp[r * PK + l0]);
+            const half4 q1 = *reinterpret_cast<const half4 *>(&sm.qp[r * PK + l1]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qv[i] = q0[i];
+                qv[4 + i] = q1[i];
+            }
+        }
+        *reinterpret_cast<half8 *>(rec + R_W + 2 * ((size_t)r * KD + 8 * bp)) = wv;
+        *reinterpret_cast<half8 *>(rec + R_QH + 2 * ((size_t)r * KD + 8 * bp)) = qv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = 256 * e + t;
+        *reinterpret_cast<uint4 *>(rec + R_UT + 16 * idx) = *reinterpret_cast<const uint4 *>(&sm.kp[8 * idx]);
     }
     // ---- P rows, with the blocks above the diagonal zeroed (16-byte stores)
 #pragma unroll
@@ -527,6 +571,8 @@ __device__ __forceinline__ void state_chunk(floatx4 (&S)[8], const ChunkTiles<NS
     floatx4 f[8];
     half8 a[4][4];
 #pragma unroll
+    for (int cb = 0; cb < 8; ++cb) f[cb] = *reinterpret_cast<const floatx4 *>(&tl.fmc[KD + 16 * cb + 4 * lg]);
+#pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) a[ks][rb] = frag8_sw(tl.w, KD, 16 * rb, ks, lane);
@@ -548,6 +594,12 @@ __device__ __forceinline__ void state_chunk(floatx4 (&S)[8], const ChunkTiles<NS
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) X[rb] = mma32(a[ks][rb], bs[ks], X[rb]);
+    // Diag(f) S', the accumulator the state update adds onto (off the chain,
+    // while the products above run)
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[cb][i] *= f[cb][i];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
         *reinterpret_cast<half8 *>(sp_out + 1024 * ks + 16 * lane) = bs[ks];
@@ -556,8 +608,6 @@ __device__ __forceinline__ void state_chunk(floatx4 (&S)[8], const ChunkTiles<NS
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) k2[ks][cb] = frag8_sw(tl.kmt, C, 16 * cb, ks, lane);
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) f[cb] = *reinterpret_cast<const floatx4 *>(&tl.fmc[KD + 16 * cb + 4 * lg]);
     __builtin_amdgcn_sched_barrier(0);
     // U = U~ - X
 #pragma unroll
@@ -567,17 +617,14 @@ __device__ __forceinline__ void state_chunk(floatx4 (&S)[8], const ChunkTiles<NS
     half8 bu[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) bu[ks] = bfrag(X[2 * ks], X[2 * ks + 1]);
-    // S'' = Diag(exp(G_C - G_m + G_m')) (S' + Km^T U): the next chunk's S'
-    // (G_m' its mid-chunk reference; for a sequence's last chunk the factor is
-    // exp(G_C - G_m), which leaves S itself)
+    // S'' = Diag(f) (S' + Km^T U) = Diag(f) S' + (Diag(f) Km^T) U with
+    // f = exp(G_C - G_m + G_m'): the next chunk's S' (G_m' its mid-chunk
+    // reference; for a sequence's last chunk f = exp(G_C - G_m), which leaves S
+    // itself).  The record holds Km^T already scaled by f.
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) S[cb] = mma32(k2[ks][cb], bu[ks], S[cb]);
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[cb][i] *= f[cb][i];
 }
 
 // Grid: one workgroup per (unit, value tile), XCD-aware: workgroup b runs on
