@@ -362,7 +362,21 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     // Waves 0, 1 solve for the Kp columns (W), waves 2, 3 for the V columns (U~);
     // each wave owns four 16-column blocks.
     const bool wside = w < 2;
-    // Row block i outer, the four independent column blocks inner.
+    // Right-hand sides for all (i, b) first (their LDS reads all in flight
+    // together), then row block i outer, the four independent column blocks
+    // inner.
+    float zx[4][4][4];  // [i][b][e]
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * i + 4 * lg + e, col = 64 * (w & 1) + 16 * b + l16;
+                const uint32_t vw = (e < 2) ? vz[b][i].x : vz[b][i].y;
+                zx[i][b][e] = wside ? (float)sm.kp[r * PK + col]
+                                    : __uint_as_float((e & 1) ? (vw & 0xffff0000u) : (vw << 16));
+            }
     half4 Xh[4][4];  // [column block][row block]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -370,16 +384,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         const half4 ti = frag4(sm.tii[i], PI, 0, 0, lane);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const int col = 64 * (w & 1) + 16 * b + l16;
             floatx4 z;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * i + 4 * lg + e;
-                const uint32_t vw = (e < 2) ? vz[b][i].x : vz[b][i].y;
-                const float xv = wside ? (float)sm.kp[r * PK + col]
-                                       : __uint_as_float((e & 1) ? (vw & 0xffff0000u) : (vw << 16));
-                z[e] = bt[e] * xv;
-            }
+            for (int e = 0; e < 4; ++e) z[e] = bt[e] * zx[i][b][e];
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int jj = 0; jj < i; ++jj) acc = mma16(frag4(sm.a16, P4, 16 * i, 16 * jj, lane), Xh[b][jj], acc);
@@ -388,23 +395,27 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             Xh[b][i] = to_half4(mma16(ti, to_half4(z), floatx4{0.f, 0.f, 0.f, 0.f}));
         }
     }
-    // ---- Q^ = Qp - P W (waves 0, 1, in place over Qp; W into the Km tile);
-    // U~ straight to the workspace (waves 2, 3)
+    // ---- Q^ = Qp - P W (waves 0, 1, in place over Qp; W into the Km tile).
+    // The product is formed transposed, (P W)^T = W^T P^T: a lane's W
+    // accumulator block read as a 16x16x16 A operand is a block of W^T, and
+    // P's row fragment serves as the B operand, so each lane ends up with four
+    // consecutive columns of one row: one 8-byte read-modify-write of Qp.
     if (wside) {
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const int col = 64 * (w & 1) + 16 * b + l16;
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i <= rb; ++i) acc = mma16(frag4(sm.p, P4, 16 * rb, 16 * i, lane), Xh[b][i], acc);
+                for (int i = 0; i <= rb; ++i) acc = mma16(Xh[b][i], frag4(sm.p, P4, 16 * rb, 16 * i, lane), acc);
+                _Float16 *qrow = &sm.qp[(16 * rb + l16) * PK + 64 * (w & 1) + 16 * b + 4 * lg];
+                half4 qv = *reinterpret_cast<const half4 *>(qrow);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * rb + 4 * lg + e;
-                    sm.qp[r * PK + col] = (_Float16)((float)sm.qp[r * PK + col] - acc[e]);
-                    sm.km[r * PK + col] = Xh[b][rb][e];
-                }
+                for (int e = 0; e < 4; ++e) qv[e] = (_Float16)((float)qv[e] - acc[e]);
+                *reinterpret_cast<half4 *>(qrow) = qv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sm.km[(16 * rb + 4 * lg + e) * PK + 64 * (w & 1) + 16 * b + l16] = Xh[b][rb][e];
             }
         }
     }
