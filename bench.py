@@ -5,8 +5,8 @@ One JSON line on stdout.  A step is one chunked forward pass (kda_chunk_fwd)
 over the prefill workload B=1, H=8, T=4096, d_k=d_v=128, chunk 64, bf16
 inputs with fp32 state, accumulation and output, on the implementation the
 library recommends for it (kda_workspace_bytes > 0: the two-pass path, three
-launches: chunk offsets, the intra-chunk pass over all chunks, the sequential
-state pass); `value` is its tokens/s.  The single-pass fused kernel's time on
+launches: the intra-chunk pass over all chunks, the sequential state pass, the
+output pass over all chunks); `value` is its tokens/s.  The single-pass fused kernel's time on
 the same workload is reported alongside.  The decode leg (one token for each
 of 256 sequences x 32 heads, persistent fp32 state, kda_decode_step) is
 reported in the same line under "decode".
@@ -211,7 +211,7 @@ def main():
     nws = kda.workspace_bytes(w.B, w.B * w.T, w.H, w.K, w.V, w.chunk)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
     path = "two-pass" if nws else "fused single-pass"
-    kernels = ("chunk_offsets_kernel + chunk_prep_kernel + chunk_state_kernel" if nws
+    kernels = ("chunk_prep_kernel + chunk_state_kernel + chunk_output_kernel" if nws
                else "chunk_mfma_kernel")
 
     def step():
