@@ -510,7 +510,7 @@ static_assert(sizeof(ChunkTiles<1>) == 35 * 1024, "segment count");
 // waves' loads in flight).
 template <int NSW, int NLW>
 struct StateSmem {
-    ChunkTiles<NSW> buf[2];  // by chunk parity
+    ChunkTiles<NSW> buf[3];  // chunk ci in buf[ci % 3]
 };
 
 // Workgroup barrier for the loader waves, which touch LDS only through their
@@ -540,10 +540,15 @@ __device__ __forceinline__ void lds_dma16(const unsigned char *src, unsigned cha
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
 }
 
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (expcnt and lgkmcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
+
 template <int NSW, int NLW>
 __device__ __forceinline__ void load_tiles(unsigned char *dst, const unsigned char *rec, int col0,
                                            int lw, int lane) {
     constexpr int SEGMENTS = (int)(sizeof(ChunkTiles<NSW>) / 1024);
+#pragma unroll
     for (int s = lw; s < SEGMENTS; s += NLW) {
         const unsigned char *src = tile_source<NSW>(rec, 64 * s + lane, col0);
         lds_dma16(src, dst + 1024 * s);
@@ -569,31 +574,38 @@ __device__ __forceinline__ half8 bfrag(const floatx4 &lo, const floatx4 &hi) {
     return b;
 }
 
-// One chunk of the state chain for state wave `sw` (16 value columns), all in
-// registers: the left operands and U~ come from the LDS tiles, the right
-// operands are the wave's own accumulators, which hold S' = Diag(exp(G_m)) S
-// on entry.  S' is published (as the fp16 B
-// fragments the output product needs) to the chunk's record.  Each phase's
-// LDS reads are issued as a group ahead of the arithmetic that consumes them.
+// W fragments of one chunk for the state wave: 16x16x32 A operands for the
+// four row blocks and four k-steps.
 template <int NSW>
-__device__ __forceinline__ void state_chunk(floatx4 (&S)[8], const ChunkTiles<NSW> &tl,
-                                            unsigned char *sp_out, int sw, int lane) {
-    const int lg = lane >> 4, j = 16 * sw + (lane & 15);
-    floatx4 f[8];
-    half8 a[4][4];
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) f[cb] = *reinterpret_cast<const floatx4 *>(&tl.fmc[KD + 16 * cb + 4 * lg]);
+__device__ __forceinline__ void load_w(half8 (&a)[4][4], const ChunkTiles<NSW> &tl, int lane) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) a[ks][rb] = frag8_sw(tl.w, KD, 16 * rb, ks, lane);
+}
+
+// One chunk of the state chain for state wave `sw` (16 value columns), all in
+// registers: the left operands and U~ come from the LDS tiles, the right
+// operands are the wave's own accumulators, which hold S' = Diag(exp(G_m)) S
+// on entry.  S' is published (as the
+// fp16 B fragments the output product needs) to the chunk's record.  Each
+// phase's LDS reads are issued as a group ahead of the arithmetic that
+// consumes them.
+template <int NSW>
+__device__ __forceinline__ void state_chunk(floatx4 (&S)[8], const ChunkTiles<NSW> &tl,
+                                            unsigned char *sp_out, int sw, int lane) {
+    const int lg = lane >> 4, j = 16 * sw + (lane & 15);
+    half8 a[4][4];
+    load_w<NSW>(a, tl, lane);
+    floatx4 f[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) f[cb] = *reinterpret_cast<const floatx4 *>(&tl.fmc[KD + 16 * cb + 4 * lg]);
     half4 ut[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
         const int blk = (2 * rb + (lg >> 1)) ^ (j & 7);
         ut[rb] = *reinterpret_cast<const half4 *>(&tl.ut[j * C + 8 * blk + 4 * (lg & 1)]);
     }
-    __builtin_amdgcn_sched_barrier(0);
     half8 bs[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) bs[ks] = bfrag(S[2 * ks], S[2 * ks + 1]);
@@ -605,6 +617,11 @@ __device__ __forceinline__ void state_chunk(floatx4 (&S)[8], const ChunkTiles<NS
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) X[rb] = mma32(a[ks][rb], bs[ks], X[rb]);
+    half8 k2[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) k2[ks][cb] = frag8_sw(tl.kmt, C, 16 * cb, ks, lane);
     // Diag(f) S', the accumulator the state update adds onto (off the chain,
     // while the products above run)
 #pragma unroll
@@ -614,11 +631,6 @@ __device__ __forceinline__ void state_chunk(floatx4 (&S)[8], const ChunkTiles<NS
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
         *reinterpret_cast<half8 *>(sp_out + 1024 * ks + 16 * lane) = bs[ks];
-    half8 k2[2][8];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) k2[ks][cb] = frag8_sw(tl.kmt, C, 16 * cb, ks, lane);
     __builtin_amdgcn_sched_barrier(0);
     // U = U~ - X
 #pragma unroll
@@ -647,6 +659,7 @@ __global__ __launch_bounds__(64 * (NSW + NLW)) void chunk_state_kernel(
     const float *s0, float *sT, const int32_t *__restrict__ cu, int fixedT, int N, int H,
     int totalT, int cap, unsigned char *__restrict__ ws) {
     constexpr int VTILE = 16 * NSW, NVT = VD / VTILE;
+    constexpr int SEGS = (int)(sizeof(ChunkTiles<NSW>) / 1024);
     extern __shared__ __align__(16) unsigned char smem_raw[];
     StateSmem<NSW, NLW> &sm = *reinterpret_cast<StateSmem<NSW, NLW> *>(smem_raw);
     const ChunkMap cm = chunk_map(cu, fixedT, ws);
@@ -691,7 +704,7 @@ __global__ __launch_bounds__(64 * (NSW + NLW)) void chunk_state_kernel(
             }
         }
         for (int ci = 0; ci < nchunks; ++ci) {
-            state_chunk<NSW>(S, sm.buf[ci & 1], rec(ci) + R_SP + 4096 * tile, w, lane);
+            state_chunk<NSW>(S, sm.buf[ci % 3], rec(ci) + R_SP + 4096 * tile, w, lane);
             __syncthreads();
         }
         if (sT) {
@@ -701,20 +714,30 @@ __global__ __launch_bounds__(64 * (NSW + NLW)) void chunk_state_kernel(
                 for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * cb + 4 * lg + i) * VD] = S[cb][i];
         }
     } else {
-        // Loader waves: chunk ci + 1 streams into the other buffer while the
-        // state waves work on chunk ci; each wave waits for its own loads
-        // before the barrier that hands the buffer over.
+        // Loader waves, three buffers: while the state waves work on chunk ci,
+        // chunk ci + 2 is issued into the buffer chunk ci - 1 used, and the
+        // loads of chunk ci + 1 (issued one chunk earlier) must land before the
+        // barrier that ends chunk ci; loads complete in issue order, so a wave
+        // waits until no more than its ci + 2 loads are outstanding.  Each load
+        // thus has two chunk times to arrive.
+        static_assert(SEGS % NLW == 0, "equal load counts per loader wave");
+        constexpr int PER_WAVE = SEGS / NLW;
         const int lw = w - NSW;
-        if (nchunks > 0) {
-            load_tiles<NSW, NLW>(reinterpret_cast<unsigned char *>(&sm.buf[0]), rec(0), col0, lw, lane);
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        }
+        auto issue = [&](int ci) {
+            load_tiles<NSW, NLW>(reinterpret_cast<unsigned char *>(&sm.buf[ci % 3]), rec(ci), col0, lw, lane);
+        };
+        for (int c = 0; c < 2 && c < nchunks; ++c) issue(c);
+        if (nchunks > 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_WAVE));  // chunk 0 landed
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
         for (int ci = 0; ci < nchunks; ++ci) {
-            if (ci + 1 < nchunks) {
-                load_tiles<NSW, NLW>(reinterpret_cast<unsigned char *>(&sm.buf[(ci + 1) & 1]), rec(ci + 1),
-                                     col0, lw, lane);
-                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            if (ci + 2 < nchunks) {
+                issue(ci + 2);
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_WAVE));
+            } else {
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
             loader_barrier();
         }
