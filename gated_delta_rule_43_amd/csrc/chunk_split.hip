@@ -606,6 +606,7 @@ __device__ __forceinline__ void state_chunk(floatx4 (&S)[8], const ChunkTiles<NS
         const int blk = (2 * rb + (lg >> 1)) ^ (j & 7);
         ut[rb] = *reinterpret_cast<const half4 *>(&tl.ut[j * C + 8 * blk + 4 * (lg & 1)]);
     }
+    __builtin_amdgcn_sched_barrier(0);  // all of the reads above in flight before the products
     half8 bs[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) bs[ks] = bfrag(S[2 * ks], S[2 * ks + 1]);
