@@ -8,18 +8,24 @@
 // fill the GPU.  Everything that does not depend on the state is computed
 // first, for all chunks at once; the sequential pass is then a short chain.
 //
-// With Kp, Km, Qp, A, P, G_m and G_C as in chunk_mfma.hip and
-// T = (I + A)^-1 Diag(beta) (never formed):
-//   W  = T Kp,   U~ = T V,   Q^ = Qp - P W,   O^ = P U~          (pass 1)
-//   S' = Diag(exp(G_m)) S
-//   U  = U~ - W S',   O = Q^ S' + O^,   S <- Diag(exp(G_C - G_m)) (S' + Km^T U)   (pass 2)
-// (substituting U into O = Qp S' + P U gives the pass-2 form).
+// With Kp, Km, Qp, A, P, G_m and G_C as in chunk_mfma.hip,
+// T = (I + A)^-1 Diag(beta) (never formed) and the end-of-chunk factor
+// f = exp(G_C - G_m + G_m of the next chunk of the sequence) (for a
+// sequence's last chunk, exp(G_C - G_m)):
+//   W  = T Kp,   U~ = T V,   Q^ = Qp - P W,
+//   M' = -Diag(f) Km^T W,   N = Diag(f) Km^T U~                       (pass 1)
+//   S' <- Diag(f) S' + M' S' + N,   S' = Diag(exp(G_m)) S             (pass 2)
+//   O  = Q^ S' + P U~                                                  (pass 3)
+// (the chunk update S <- Diag(exp(G_C - G_m)) (S' + Km^T (U~ - W S')) and
+// O = Qp S' + P (U~ - W S') regrouped, with the next chunk's G_m folded in so
+// that the state stays in S' form between chunks).
 //
-// Pass 1 (chunk_prep_kernel): one workgroup of 4 waves per (chunk, head),
-// all chunks in parallel.  Pass 2 (chunk_state_kernel): one workgroup per
+// Pass 1 (chunk_prep_kernel): one workgroup of 4 waves per (chunk, head), all
+// chunks in parallel.  Pass 2 (chunk_state_kernel): one workgroup per
 // (sequence, head, 16-column value tile); one state wave runs the chain with
-// the state in registers while seven loader waves stream the next chunk's
-// W, Q^, Km^T tiles into double-buffered LDS with direct loads.
+// the state in registers (one 128 x 128 x 16 product per chunk) while seven
+// loader waves stream the next chunks' M', N and f into LDS with direct loads.
+// Pass 3 (chunk_output_kernel): one workgroup per (chunk, head).
 // Intermediates live in the caller's workspace.
 #include "kda_mfma.hpp"
 
@@ -27,48 +33,46 @@ namespace kda {
 namespace {
 
 constexpr int C = 64, KD = 128, VD = 128;
-constexpr int STATE_WAVES = 1;   // state waves per workgroup in pass 2
-constexpr int LOADER_WAVES = 7;  // tile-streaming waves per workgroup in pass 2
+constexpr int STATE_WAVES = 4;   // pass-2 waves running the chain (128 / STATE_WAVES state rows each)
+constexpr int LOADER_WAVES = 4;  // pass-2 waves streaming the tiles
+constexpr int RBW = 8 / STATE_WAVES;  // 16-row blocks of the state per state wave
+constexpr int KSW = 4 / STATE_WAVES;  // k-steps whose B fragments a state wave owns
+constexpr int NBUF = 4;          // pass-2 LDS buffers (chunk ci in buffer ci % 4)
 constexpr int PK = 136;  // LDS pitch (halves), [64][128] fp16 tiles
-constexpr int PC = 72;   // LDS pitch (halves), [128][64] tiles read as 16-byte fragments
 constexpr int P4 = 76;   // LDS pitch (halves), [64][64] tiles read as 8-byte fragments
 constexpr int PI = 20;   // LDS pitch (halves), 16 x 16 fp16 blocks
 constexpr int PF = 17;   // LDS pitch (floats), 16 x 16 fp32 blocks
 constexpr int VTP = 68;  // LDS pitch (bf16), V^T staging tile [128][64]
 
-// Per-(chunk, head) record in the workspace (bytes).  The contraction index
-// of W, Q^ (c) and Km^T (s) is stored permuted within each 32-wide block,
-// see kperm_pos below.  The first 33 KB are what the state pass streams.
-constexpr size_t R_W = 0;             // fp16 [64][128]  W     [r][c]
-constexpr size_t R_KMT = 16384;       // fp16 [128][64]  Diag(f) Km^T [c][s], f = the R_FC factor
-constexpr size_t R_FM = 32768;        // fp32 [128]      exp(G_m)
-constexpr size_t R_FC = 33280;        // fp32 [128]      exp(G_C - G_m + G_m of the next chunk)
-constexpr size_t R_UT = 33792;        // fp16 [128][64]  U~    [j][r]
-constexpr size_t R_QH = 50176;        // fp16 [64][128]  Q^    [r][c]
-constexpr size_t R_P = 66560;         // fp16 [64][64]   P     [r][s], zero above the diagonal
-constexpr size_t R_SP = 74752;        // fp16 S' as MFMA B fragments [8 tiles][4 ks][64 lanes][8]
-constexpr size_t REC = 107520;
-constexpr size_t OFFS_BYTES = 512;    // int32 chunk offsets, up to 127 sequences
+// Per-(chunk, head) record in the workspace (bytes).  "A order" / "B order":
+// MFMA 16x16x32 operand fragments stored lane by lane, [block][k-step][64
+// lanes][8 halves], so that a wave reads a fragment as one contiguous 1 KB.
+// Contraction indices are stored permuted within each 32-wide block (see
+// kperm_pos).  The first 37 KB of a record (with the tile's 4 KB of N) are
+// what the state pass streams.
+constexpr size_t R_M = 0;         // fp16 M' in A order [8 row blocks][4 k-steps]
+constexpr size_t R_N = 32768;     // fp16 N as accumulators [8 value tiles][8 row blocks][64 lanes][4]
+constexpr size_t R_FC = 65536;    // fp32 [128]  f
+constexpr size_t R_FM = 66048;    // fp32 [128]  exp(G_m)
+constexpr size_t R_UT = 66560;    // fp16 U~ in B order [8 value tiles][2 k-steps]
+constexpr size_t R_QH = 82944;    // fp16 [64][128]  Q^ [r][c]
+constexpr size_t R_P = 99328;     // fp16 [64][64]   P [r][s], zero above the diagonal
+constexpr size_t R_SP = 107520;   // fp16 S' in B order [8 value tiles][4 k-steps]
+constexpr size_t REC = 140288;
+constexpr size_t OFFS_BYTES = 512;  // int32 chunk offsets, up to 127 sequences
 
-// The pass-2 products contract over an index (c for W S' and Q^ S', s for
-// Km^T U) whose right operand comes straight out of MFMA accumulators: lane l
-// holds rows 4 (l >> 4) .. +3 of each 16-row block.  A 16x16x32 B fragment
-// wants 8 k values per lane; taking the lane's rows of blocks 2 ks and
-// 2 ks + 1 as those 8 values leaves the state in registers, provided the left
-// operand's k values are laid out in the same order.  Within each 32-wide
-// block, stored position 8 g + t holds logical index 4 g + t (t < 4) or
-// 16 + 4 g + t - 4 (t >= 4); kperm_pos gives the stored position of the
-// logical 4-group [4 q, 4 q + 4).
+// Several products take an operand straight out of MFMA accumulators, where
+// lane l holds rows 4 (l >> 4) .. +3 of each 16-row block: the state S' (in
+// M' S' and Q^ S'), and W and U~ (in M' and N).  A 16x16x32 fragment wants 8
+// k values per lane; taking the lane's rows of blocks 2 ks and 2 ks + 1 as
+// those 8 values keeps the operand in registers, provided the other operand's
+// k values are laid out in the same order.  Within each 32-wide block, stored
+// position 8 g + t holds logical index 4 g + t (t < 4) or 16 + 4 g + t - 4
+// (t >= 4); kperm_pos gives the stored position of the logical 4-group
+// [4 q, 4 q + 4).
 __device__ __forceinline__ int kperm_pos(int q) {
     return 32 * (q >> 3) + 8 * (q & 3) + 4 * ((q >> 2) & 1);
 }
-
-// W and Km^T rows and U~ columns are stored with their 16-byte blocks
-// XOR-permuted by (row or column index & 7): the state pass copies them into
-// LDS unchanged (linear, fully coalesced direct loads), where the permutation
-// makes the 16 rows of an MFMA fragment read land in distinct banks.
-// swz(x, r): stored half offset of logical half offset x within row r.
-__device__ __forceinline__ int swz(int x, int r) { return (((x >> 3) ^ (r & 7)) << 3) | (x & 7); }
 
 // ---------------------------------------------------------------- offsets
 // offs[n] = first chunk of sequence n in the packed chunk list, clamped so that
@@ -112,10 +116,35 @@ __device__ __forceinline__ ChunkMap chunk_map(const int32_t *cu, int fixedT, con
 }
 
 // ---------------------------------------------------------------- pass 1
+// Diag(f) Km^T tile of pass 1 ([128][64] fp16, no padding): half offset of the
+// logical 4-group q of row c (the contraction index s permuted as kperm_pos
+// says, then the row's 16-byte blocks XOR-permuted by (c & 7) so that the 16
+// rows of a fragment read fall in distinct banks), and of the 16x16x32
+// fragment (rows 16 cb .. +15, k-step ks) a lane reads.
+__device__ __forceinline__ int kt_off(int c, int q) {
+    const int pos = kperm_pos(q);
+    return c * C + ((((pos >> 3) ^ (c & 7))) << 3) + (pos & 7);
+}
+__device__ __forceinline__ int kt_frag_off(int cb, int ks, int lane) {
+    const int c = 16 * cb + (lane & 15);
+    return c * C + (((4 * ks + (lane >> 4)) ^ (c & 7)) << 3);
+}
+// Two accumulator blocks (16 rows each) of one lane as the 8 k values of a
+// 16x16x32 fragment in permuted order (block 2 ks first, then 2 ks + 1).
+__device__ __forceinline__ half8 pair8(half4 lo, half4 hi) {
+    half8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = lo[i];
+        r[4 + i] = hi[i];
+    }
+    return r;
+}
+
 struct PrepSmem {
-    _Float16 kp[C * PK];    // Kp [s][c]
+    _Float16 kp[C * PK];    // Kp [s][c], then Diag(f) Km^T (see kt_off)
     _Float16 qp[C * PK];    // Qp [s][c], then Q^ in place
-    _Float16 km[C * PK];    // Km [s][c], then W
+    _Float16 km[C * PK];    // Km [s][c]
     _Float16 a16[C * P4];   // A [r][s], off-diagonal lower blocks
     _Float16 p[C * P4];     // P [r][s], lower blocks
     _Float16 tii[4][16 * PI];
@@ -157,39 +186,44 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const int l16 = lane & 15, lg = lane >> 4;
     const int cg = t & 15, rg = t >> 4;  // channels 8 cg .., rows 4 rg .. 4 rg + 3
 
-    // ---- loads and the running log-decay sum
-    uint4 rq[4], rk[4], rgv[4];
+    // ---- loads and the running log-decay sum.  Every load is issued
+    // unconditionally (rows past the chunk's end re-read its last row and are
+    // zeroed afterwards), so that all of them are in flight together.
+    uint4 rq[4], rk[4], rgv[4], rv[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int r = 4 * rg + u;
-        rq[u] = make_uint4(0u, 0u, 0u, 0u);
-        rk[u] = rq[u];
-        rgv[u] = rq[u];
-        if (r < L) {
-            const size_t off = ((size_t)(c0 + r) * H + h) * KD + 8 * cg;
-            rq[u] = *reinterpret_cast<const uint4 *>(q + off);
-            rk[u] = *reinterpret_cast<const uint4 *>(k + off);
-            rgv[u] = *reinterpret_cast<const uint4 *>(g + off);
-        }
+        const int r = min(4 * rg + u, L - 1);
+        const size_t off = ((size_t)(c0 + r) * H + h) * KD + 8 * cg;
+        rq[u] = *reinterpret_cast<const uint4 *>(q + off);
+        rk[u] = *reinterpret_cast<const uint4 *>(k + off);
+        rgv[u] = *reinterpret_cast<const uint4 *>(g + off);
+        rv[u] = *reinterpret_cast<const uint4 *>(v + off);
     }
-    uint4 rv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int r = 4 * rg + u;
-        rv[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (r < L) rv[u] = *reinterpret_cast<const uint4 *>(v + ((size_t)(c0 + r) * H + h) * VD + 8 * cg);
-    }
-    if (t < C) sm.beta[t] = t < L ? __uint_as_float((uint32_t)beta[(size_t)(c0 + t) * H + h] << 16) : 0.f;
+    float bt_in = 0.f;
+    if (w == 0) bt_in = __uint_as_float((uint32_t)beta[(size_t)(c0 + min(t, L - 1)) * H + h] << 16);
     // The first half of the next chunk of this sequence (if any): its G_m is
     // folded into this chunk's end-of-chunk scale factor.
-    uint4 rgn[4];
+    uint4 rgn[4] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u),
+                     make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+    if (w < 2) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = min(c0 + C + 4 * rg + u, eos - 1);
+            rgn[u] = *reinterpret_cast<const uint4 *>(g + ((size_t)r * H + h) * KD + 8 * cg);
+        }
+    }
+    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int r = C + 4 * rg + u;
-        rgn[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (w < 2 && c0 + r < eos)
-            rgn[u] = *reinterpret_cast<const uint4 *>(g + ((size_t)(c0 + r) * H + h) * KD + 8 * cg);
+        if (4 * rg + u >= L) {
+            rq[u] = zero4;
+            rk[u] = zero4;
+            rgv[u] = zero4;
+            rv[u] = zero4;
+        }
+        if (c0 + C + 4 * rg + u >= eos) rgn[u] = zero4;
     }
+    if (w == 0) sm.beta[t] = t < L ? bt_in : 0.f;
 
     float G[4][8], ex[8];
 #pragma unroll
@@ -251,6 +285,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             for (int i = 0; i < 4; ++i)
                 vz[b][i] = *reinterpret_cast<const uint2 *>(&vst[(64 * (w & 1) + 16 * b + l16) * VTP + 16 * i + 4 * lg]);
     }
+    // Diag(f) Km^T: this thread's channels 8 cg + e, rows 4 rg .. 4 rg + 3,
+    // kept in registers until the tile it goes to is free
+    half4 kmT[8];
     {
         float kv[4][8], qv[4][8];
 #pragma unroll
@@ -258,7 +295,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             unpack8(rk[u], kv[u]);
             unpack8(rq[u], qv[u]);
         }
-        half4 kmT[8];
         half8 kpr[4], qpr[4], kmr[4];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -293,11 +329,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             *reinterpret_cast<half8 *>(&sm.kp[r * PK + 8 * cg]) = kpr[u];
             *reinterpret_cast<half8 *>(&sm.qp[r * PK + 8 * cg]) = qpr[u];
             *reinterpret_cast<half8 *>(&sm.km[r * PK + 8 * cg]) = kmr[u];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = 8 * cg + e;
-            *reinterpret_cast<half4 *>(rec + R_KMT + 2 * ((size_t)c * C + swz(kperm_pos(rg), c))) = kmT[e];
         }
     }
     __syncthreads();
@@ -395,7 +426,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             Xh[b][i] = to_half4(mma16(ti, to_half4(z), floatx4{0.f, 0.f, 0.f, 0.f}));
         }
     }
-    // ---- Q^ = Qp - P W (waves 0, 1, in place over Qp; W into the Km tile).
+    // ---- Q^ = Qp - P W (waves 0, 1, in place over Qp).
     // The product is formed transposed, (P W)^T = W^T P^T: a lane's W
     // accumulator block read as a 16x16x16 A operand is a block of W^T, and
     // P's row fragment serves as the B operand, so each lane ends up with four
@@ -413,109 +444,119 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) qv[e] = (_Float16)((float)qv[e] - acc[e]);
                 *reinterpret_cast<half4 *>(qrow) = qv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sm.km[(16 * rb + 4 * lg + e) * PK + 64 * (w & 1) + 16 * b + l16] = Xh[b][rb][e];
             }
         }
     }
     __syncthreads();
-    // U~ (waves 2, 3) into a staging copy laid out as in the record, over the
-    // Kp tile (no longer read), for linear global stores below
-    if (!wside) {
-        _Float16 *stage = sm.kp;
+    // ---- Diag(f) Km^T into the Kp tile (no longer read): [c][s], s permuted
+    // as the contraction index, 16-byte blocks of a row XOR-permuted by (c & 7)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int col = 64 * (w & 1) + 16 * b + l16;
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-                *reinterpret_cast<half4 *>(&stage[col * C + swz(16 * rb + 4 * lg, col)]) = Xh[b][rb];
-        }
-    }
-    // ---- W and Q^ rows to the workspace, k-permuted (16-byte stores: stored
-    // block b of a row takes logical 4-groups 8 (b >> 2) + (b & 3) and that + 4)
-    // (stored 16-byte block bp of a W row holds logical block bp ^ (r & 7))
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<half4 *>(&sm.kp[kt_off(8 * cg + e, rg)]) = kmT[e];
+    // ---- Q^ rows to the workspace, k-permuted (16-byte stores: stored block b
+    // of a row takes logical 4-groups 8 (b >> 2) + (b & 3) and that + 4)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int idx = 256 * e + t, r = idx >> 4, bp = idx & 15;
-        half8 wv, qv;
-        {
-            const int b = bp ^ (r & 7), l0 = 32 * (b >> 2) + 4 * (b & 3), l1 = l0 + 16;
-            const half4 w0 = *reinterpret_cast<const half4 *>(&sm.km[r * PK + l0]);
-            const half4 w1 = *reinterpret_cast<const half4 *>(&sm.km[r * PK + l1]);
+        const int l0 = 32 * (bp >> 2) + 4 * (bp & 3), l1 = l0 + 16;
+        const half4 q0 = *reinterpret_cast<const half4 *>(&sm.qp[r * PK + l0]);
+        const half4 q1 = *reinterpret_cast<const half4 *>(&sm.qp[r * PK + l1]);
+        half8 qv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                wv[i] = w0[i];
-                wv[4 + i] = w1[i];
-            }
+        for (int i = 0; i < 4; ++i) {
+            qv[i] = q0[i];
+            qv[4 + i] = q1[i];
         }
-        {
-            const int l0 = 32 * (bp >> 2) + 4 * (bp & 3), l1 = l0 + 16;
-            const half4 q0 = *reinterpret_cast<const half4 *>(&sm.qp[r * PK + l0]);
-            const half4 q1 = *reinterpret_cast<const half4 *>(&sm.qp[r * PK + l1]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                qv[i] = q0[i];
-                qv[4 + i] = q1[i];
-            }
-        }
-        *reinterpret_cast<half8 *>(rec + R_W + 2 * ((size_t)r * KD + 8 * bp)) = wv;
         *reinterpret_cast<half8 *>(rec + R_QH + 2 * ((size_t)r * KD + 8 * bp)) = qv;
     }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int idx = 256 * e + t;
-        *reinterpret_cast<uint4 *>(rec + R_UT + 16 * idx) = *reinterpret_cast<const uint4 *>(&sm.kp[8 * idx]);
-    }
-    // ---- P rows, with the blocks above the diagonal zeroed (16-byte stores)
+    // ---- P rows, s permuted likewise, zero above the diagonal (16-byte stores)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int idx = 256 * e + t, r = idx >> 3, b = idx & 7;
+        const int l0 = 32 * (b >> 2) + 4 * (b & 3), l1 = l0 + 16;
+        half4 p0 = *reinterpret_cast<const half4 *>(&sm.p[r * P4 + l0]);
+        half4 p1 = *reinterpret_cast<const half4 *>(&sm.p[r * P4 + l1]);
         half8 pv;
-        if ((b >> 1) > (r >> 4)) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pv[i] = (_Float16)0.f;
-        } else {
-            const half4 p0 = *reinterpret_cast<const half4 *>(&sm.p[r * P4 + 8 * b]);
-            const half4 p1 = *reinterpret_cast<const half4 *>(&sm.p[r * P4 + 8 * b + 4]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pv[i] = p0[i];
-                pv[4 + i] = p1[i];
-            }
+        for (int i = 0; i < 4; ++i) {
+            pv[i] = (l0 >> 4) > (r >> 4) ? (_Float16)0.f : p0[i];
+            pv[4 + i] = (l1 >> 4) > (r >> 4) ? (_Float16)0.f : p1[i];
         }
         *reinterpret_cast<half8 *>(rec + R_P + 2 * ((size_t)r * C + 8 * b)) = pv;
+    }
+    __syncthreads();
+    // ---- M' = -Diag(f) Km^T W (waves 0, 1) and N = Diag(f) Km^T U~ (waves 2,
+    // 3), contracting over s with the W / U~ accumulator blocks as operands.
+    // M' is formed transposed (M'^T = -W^T (Diag(f) Km^T)^T): each lane then
+    // holds four consecutive contraction indices of one row of M', which is
+    // what its A-order fragment takes.
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+        half8 kt[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) kt[ks] = *reinterpret_cast<const half8 *>(&sm.kp[kt_frag_off(cb, ks, lane)]);
+        if (wside) {
+#pragma unroll
+            for (int jp = 0; jp < 2; ++jp) {
+                floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    a0 = mma32(pair8(Xh[2 * jp][2 * ks], Xh[2 * jp][2 * ks + 1]), kt[ks], a0);
+                    a1 = mma32(pair8(Xh[2 * jp + 1][2 * ks], Xh[2 * jp + 1][2 * ks + 1]), kt[ks], a1);
+                }
+                half8 mv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    mv[i] = (_Float16)(-a0[i]);
+                    mv[4 + i] = (_Float16)(-a1[i]);
+                }
+                *reinterpret_cast<half8 *>(rec + R_M + 16 * ((cb * 4 + 2 * (w & 1) + jp) * 64 + lane)) = mv;
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    acc = mma32(kt[ks], pair8(Xh[b][2 * ks], Xh[b][2 * ks + 1]), acc);
+                const int jt = 4 * (w & 1) + b;
+                *reinterpret_cast<half4 *>(rec + R_N + 8 * ((jt * 8 + cb) * 64 + lane)) = to_half4(acc);
+            }
+        }
+    }
+    // ---- U~ (waves 2, 3) in B order, straight from the accumulator blocks
+    if (!wside) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                *reinterpret_cast<half8 *>(rec + R_UT + 16 * (((4 * (w & 1) + b) * 2 + ks) * 64 + lane)) =
+                    pair8(Xh[b][2 * ks], Xh[b][2 * ks + 1]);
     }
 }
 
 // ---------------------------------------------------------------- pass 2
-// One chunk's state-pass operands in LDS, for a workgroup owning VT = 16 NSW
-// value columns: W ([64][128] fp16) and Km^T ([128][64] fp16) without padding,
-// each row's 16-byte blocks XOR-permuted by (row & 7) as stored (swz); the
-// scale factors; then the workgroup's columns of U~ (blocks permuted by the
-// column index).  Loader waves copy it with direct global-to-LDS loads in
+// One chunk's state-pass operands in LDS for a workgroup owning one 16-column
+// value tile, as copied from the record: M' in A order, the tile's N, f and
+// exp(G_m).  Loader waves copy it with direct global-to-LDS loads in
 // wave-wide 1 KB segments.
-template <int NSW>
 struct ChunkTiles {
-    _Float16 w[C * KD];
-    _Float16 kmt[KD * C];
-    float fmc[2 * KD];
-    _Float16 ut[16 * NSW * C];  // [j][r]
+    _Float16 m[8 * 4 * 64 * 8];  // M' fragments [row block][k-step][lane][8]
+    _Float16 n[8 * 64 * 4];      // N [row block][lane][4], accumulator layout
+    float fc[KD];                // f
+    float fm[KD];                // exp(G_m)
 };
-static_assert(sizeof(ChunkTiles<1>) == 35 * 1024, "segment count");
+constexpr int SEGS = (int)(sizeof(ChunkTiles) / 1024);  // 37
+static_assert(sizeof(ChunkTiles) == 37 * 1024, "segment count");
+static_assert(R_FM == R_FC + 512, "f and exp(G_m) form the last segment");
 
-// NSW state waves own 16 value columns each; NLW loader waves stream the
-// tiles (one CU sustains its highest direct-load rate only with several
-// waves' loads in flight).
-template <int NSW, int NLW>
 struct StateSmem {
-    ChunkTiles<NSW> buf[3];  // chunk ci in buf[ci % 3]
+    ChunkTiles buf[NBUF];
+    _Float16 xb[2][4][64 * 8];  // S' B fragments exchanged between the state waves [parity][k-step]
 };
 
-// Workgroup barrier for the loader waves, which touch LDS only through their
-// direct loads and wait for those explicitly: no fence, so the compiler adds
-// no waits of its own.
+// Workgroup barrier without a memory fence: waves that must see each other's
+// LDS writes wait for them explicitly, so the compiler adds no waits of its
+// own (direct loads in flight and fragment reads stay in flight across it).
 __device__ __forceinline__ void loader_barrier() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
@@ -524,14 +565,12 @@ __device__ __forceinline__ void loader_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Global source of LDS slot p (16-byte units) of a ChunkTiles<NSW> image for
-// value columns [col0, col0 + 16 NSW): the record's first 33 KB (W, Km^T,
-// scale factors) and the tile's U~ columns, both copied linearly.
-template <int NSW>
-__device__ __forceinline__ const unsigned char *tile_source(const unsigned char *rec, int p,
-                                                            int col0) {
-    constexpr int HEAD = (int)(R_UT / 16);  // 2112
-    return p < HEAD ? rec + 16 * p : rec + R_UT + 128 * col0 + 16 * (p - HEAD);
+// Global source of LDS slot p (16-byte units) of a ChunkTiles image for value
+// tile jt: M' (2048 slots), the tile's N (256), then f and exp(G_m) (64).
+__device__ __forceinline__ const unsigned char *tile_source(const unsigned char *rec, int p, int jt) {
+    return p < 2048 ? rec + R_M + 16 * p
+         : p < 2304 ? rec + R_N + 4096 * jt + 16 * (p - 2048)
+                    : rec + R_FC + 16 * (p - 2304);
 }
 
 // One direct global-to-LDS load: 16 bytes per lane from `src`, landing at
@@ -544,23 +583,47 @@ __device__ __forceinline__ void lds_dma16(const unsigned char *src, unsigned cha
 // (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
-template <int NSW, int NLW>
-__device__ __forceinline__ void load_tiles(unsigned char *dst, const unsigned char *rec, int col0,
+// Loader wave lw copies segments lw, lw + LOADER_WAVES, ... (PW of them).
+template <int PW>
+__device__ __forceinline__ void load_tiles(unsigned char *dst, const unsigned char *rec, int jt,
                                            int lw, int lane) {
-    constexpr int SEGMENTS = (int)(sizeof(ChunkTiles<NSW>) / 1024);
 #pragma unroll
-    for (int s = lw; s < SEGMENTS; s += NLW) {
-        const unsigned char *src = tile_source<NSW>(rec, 64 * s + lane, col0);
-        lds_dma16(src, dst + 1024 * s);
+    for (int i = 0; i < PW; ++i) {
+        const int sg = lw + LOADER_WAVES * i;
+        lds_dma16(tile_source(rec, 64 * sg + lane, jt), dst + 1024 * sg);
     }
 }
 
-// 16x16x32 fragment from a swizzled tile with `rowlen` halves per row.
-__device__ __forceinline__ half8 frag8_sw(const _Float16 *base, int rowlen, int row0, int ks,
-                                          int lane) {
-    const int r = row0 + (lane & 15);
-    const int kb = (4 * ks + (lane >> 4)) ^ (r & 7);
-    return *reinterpret_cast<const half8 *>(base + r * rowlen + 8 * kb);
+// The loader waves' side of the pipeline.  Chunk ci is copied into buffer
+// ci % 4.  Barrier ci (early in the state waves' chunk ci) certifies that
+// chunk ci + 1 has landed (if there is one); after it chunk ci + 3 is issued into the
+// buffer chunk ci - 1 used, which the state wave finished reading before
+// barrier ci - 1.  Loads complete in issue order, so "chunk ci + 1 landed" is
+// "at most the loads of chunk ci + 2 outstanding": each chunk has two chunk
+// times to arrive.
+template <int PW>
+__device__ __forceinline__ void loader_loop(StateSmem &sm, const unsigned char *recs, int cap,
+                                            int h, int ch0, int nchunks, int jt, int lw, int lane) {
+    auto issue = [&](int ci) {
+        load_tiles<PW>(reinterpret_cast<unsigned char *>(&sm.buf[ci % NBUF]),
+                       recs + ((size_t)h * cap + ch0 + ci) * REC, jt, lw, lane);
+    };
+    for (int c = 0; c < 3 && c < nchunks; ++c) issue(c);
+    if (nchunks > 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PW));  // chunk 0 landed
+    else if (nchunks > 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PW));
+    else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    for (int ci = 0; ci < nchunks; ++ci) {
+        if (ci + 2 < nchunks)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(PW));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        loader_barrier();
+        if (ci + 3 < nchunks) issue(ci + 3);
+    }
 }
 
 // B fragment of a k-permuted product from accumulator blocks 2 ks, 2 ks + 1.
@@ -574,187 +637,158 @@ __device__ __forceinline__ half8 bfrag(const floatx4 &lo, const floatx4 &hi) {
     return b;
 }
 
-// W fragments of one chunk for the state wave: 16x16x32 A operands for the
-// four row blocks and four k-steps.
-template <int NSW>
-__device__ __forceinline__ void load_w(half8 (&a)[4][4], const ChunkTiles<NSW> &tl, int lane) {
+// M' fragments of k-step ks for the row blocks [RBW sw, RBW sw + RBW).
+__device__ __forceinline__ void read_m(half8 (&a)[RBW], const ChunkTiles &tl, int sw, int ks, int lane) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) a[ks][rb] = frag8_sw(tl.w, KD, 16 * rb, ks, lane);
+    for (int r = 0; r < RBW; ++r)
+        a[r] = *reinterpret_cast<const half8 *>(&tl.m[8 * (((RBW * sw + r) * 4 + ks) * 64 + lane)]);
 }
-
-// One chunk of the state chain for state wave `sw` (16 value columns), all in
-// registers: the left operands and U~ come from the LDS tiles, the right
-// operands are the wave's own accumulators, which hold S' = Diag(exp(G_m)) S
-// on entry.  S' is published (as the
-// fp16 B fragments the output product needs) to the chunk's record.  Each
-// phase's LDS reads are issued as a group ahead of the arithmetic that
-// consumes them.
-template <int NSW>
-__device__ __forceinline__ void state_chunk(floatx4 (&S)[8], const ChunkTiles<NSW> &tl,
-                                            unsigned char *sp_out, int sw, int lane) {
-    const int lg = lane >> 4, j = 16 * sw + (lane & 15);
-    half8 a[4][4];
-    load_w<NSW>(a, tl, lane);
-    floatx4 f[8];
+// The tile's N and f of a chunk for those row blocks, in the accumulator layout.
+__device__ __forceinline__ void read_nf(half4 (&nv)[RBW], floatx4 (&fv)[RBW], const ChunkTiles &tl,
+                                        int sw, int lane) {
+    const int lg = lane >> 4;
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) f[cb] = *reinterpret_cast<const floatx4 *>(&tl.fmc[KD + 16 * cb + 4 * lg]);
-    half4 ut[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-        const int blk = (2 * rb + (lg >> 1)) ^ (j & 7);
-        ut[rb] = *reinterpret_cast<const half4 *>(&tl.ut[j * C + 8 * blk + 4 * (lg & 1)]);
+    for (int r = 0; r < RBW; ++r) {
+        const int cb = RBW * sw + r;
+        nv[r] = *reinterpret_cast<const half4 *>(&tl.n[4 * (cb * 64 + lane)]);
+        fv[r] = *reinterpret_cast<const floatx4 *>(&tl.fc[16 * cb + 4 * lg]);
     }
-    __builtin_amdgcn_sched_barrier(0);  // all of the reads above in flight before the products
-    half8 bs[4];
+}
+// MFMAs of one k-step on this wave's rows: S += M'[own rows, ks block] * b.
+__device__ __forceinline__ void mfma_step(floatx4 (&S)[RBW], const half8 (&a)[RBW], const half8 &b) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) bs[ks] = bfrag(S[2 * ks], S[2 * ks + 1]);
-    // X = W S'
-    floatx4 X[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) X[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) X[rb] = mma32(a[ks][rb], bs[ks], X[rb]);
-    half8 k2[2][8];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) k2[ks][cb] = frag8_sw(tl.kmt, C, 16 * cb, ks, lane);
-    // Diag(f) S', the accumulator the state update adds onto (off the chain,
-    // while the products above run)
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[cb][i] *= f[cb][i];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        *reinterpret_cast<half8 *>(sp_out + 1024 * ks + 16 * lane) = bs[ks];
-    __builtin_amdgcn_sched_barrier(0);
-    // U = U~ - X
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) X[rb][e] = (float)ut[rb][e] - X[rb][e];
-    half8 bu[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) bu[ks] = bfrag(X[2 * ks], X[2 * ks + 1]);
-    // S'' = Diag(f) (S' + Km^T U) = Diag(f) S' + (Diag(f) Km^T) U with
-    // f = exp(G_C - G_m + G_m'): the next chunk's S' (G_m' its mid-chunk
-    // reference; for a sequence's last chunk f = exp(G_C - G_m), which leaves S
-    // itself).  The record holds Km^T already scaled by f.
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) S[cb] = mma32(k2[ks][cb], bu[ks], S[cb]);
+    for (int r = 0; r < RBW; ++r) S[r] = mma32(a[r], b, S[r]);
 }
 
 // Grid: one workgroup per (unit, value tile), XCD-aware: workgroup b runs on
 // XCD b mod 8, and all value tiles of a unit share that XCD (and its L2),
-// which serves their common W, Km^T tiles.  Waves: NSW state waves, NLW
-// loader waves; one barrier per chunk.
-template <int NSW, int NLW>
-__global__ __launch_bounds__(64 * (NSW + NLW)) void chunk_state_kernel(
+// which serves their common M' tiles.  Waves [0, STATE_WAVES) are the state
+// waves, the rest the loaders.
+//
+// State wave sw keeps RBW row blocks of the tile's 128 x 16 slice of S' in
+// accumulators: the rows of its k-steps KSW sw .. KSW sw + KSW - 1.  Per chunk
+// it converts them to those k-steps' fp16 B fragments, publishes them (for
+// the output pass) and hands them to the other state waves through LDS;
+// barrier ci makes all of them visible.  It then forms Diag(f) S' + N on its
+// rows and adds the products of its own k-steps first and the others' after
+// (cyclic order from its own), reading M' fragments one k-step ahead and the
+// next chunk's first ones after this chunk's last; the exchanged fragments
+// have the own k-steps' products to arrive.
+__global__ __launch_bounds__(64 * (STATE_WAVES + LOADER_WAVES)) void chunk_state_kernel(
     const float *s0, float *sT, const int32_t *__restrict__ cu, int fixedT, int N, int H,
     int totalT, int cap, unsigned char *__restrict__ ws) {
-    constexpr int VTILE = 16 * NSW, NVT = VD / VTILE;
-    constexpr int SEGS = (int)(sizeof(ChunkTiles<NSW>) / 1024);
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    StateSmem<NSW, NLW> &sm = *reinterpret_cast<StateSmem<NSW, NLW> *>(smem_raw);
+    StateSmem &sm = *reinterpret_cast<StateSmem *>(smem_raw);
     const ChunkMap cm = chunk_map(cu, fixedT, ws);
     const int b = blockIdx.x, slot = b >> 3;
-    const int vt = slot % NVT;
-    const int unit = (slot / NVT) * 8 + (b & 7);
+    const int jt = slot % 8;                   // 16-column value tile
+    const int unit = (slot / 8) * 8 + (b & 7);
     if (unit >= N * H) return;
     const int n = unit / H, h = unit - n * H;
     const int ch0 = cm.first(n);
     const int nchunks = cm.first(n + 1) - ch0;
     unsigned char *recs = ws + OFFS_BYTES;
     auto rec = [&](int ci) { return recs + ((size_t)h * cap + ch0 + ci) * REC; };
-    const int col0 = vt * VTILE;
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lg = lane >> 4;
 
-    if (w < NSW) {
-        const int jcol = col0 + 16 * w + (lane & 15);  // this lane's value column
+    if (w < STATE_WAVES) {
+        const int sw = w;
+        auto korder = [&](int t) { return (KSW * sw + t) & 3; };  // k-step order, own first
+        const int jcol = 16 * jt + (lane & 15);                    // this lane's value column
         const size_t sbase = (size_t)unit * (KD * VD) + jcol;
-        const int tile = (col0 >> 4) + w;                // 16-column tile of the S' record
-        floatx4 S[8];
+        floatx4 S[RBW];  // rows 16 (RBW sw + r) + 4 lg + i
         if (s0) {
 #pragma unroll
-            for (int cb = 0; cb < 8; ++cb)
+            for (int r = 0; r < RBW; ++r)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[cb][i] = s0[sbase + (size_t)(16 * cb + 4 * lg + i) * VD];
+                for (int i = 0; i < 4; ++i) S[r][i] = s0[sbase + (size_t)(16 * (RBW * sw + r) + 4 * lg + i) * VD];
         } else {
 #pragma unroll
-            for (int cb = 0; cb < 8; ++cb) S[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < RBW; ++r) S[r] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
         __syncthreads();
+        half8 a[RBW], bq[RBW];
+        half4 nv[RBW];
+        floatx4 fv[RBW];
         if (nchunks > 0) {
             // S' of the first chunk; later chunks receive theirs from the
             // previous chunk's end-of-chunk factor
 #pragma unroll
-            for (int cb = 0; cb < 8; ++cb) {
-                const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.buf[0].fmc[16 * cb + 4 * lg]);
+            for (int r = 0; r < RBW; ++r) {
+                const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.buf[0].fm[16 * (RBW * sw + r) + 4 * lg]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[cb][i] *= f[i];
+                for (int i = 0; i < 4; ++i) S[r][i] *= f[i];
             }
+            read_m(a, sm.buf[0], sw, korder(0), lane);
+            read_nf(nv, fv, sm.buf[0], sw, lane);
         }
         for (int ci = 0; ci < nchunks; ++ci) {
-            state_chunk<NSW>(S, sm.buf[ci % 3], rec(ci) + R_SP + 4096 * tile, w, lane);
-            __syncthreads();
+            const ChunkTiles &tl = sm.buf[ci % NBUF];
+            unsigned char *sp = rec(ci) + R_SP + 4096 * jt;
+            half8 bk[4];  // B fragments in this wave's k-step order
+#pragma unroll
+            for (int t = 0; t < KSW; ++t) {
+                bk[t] = bfrag(S[2 * t], S[2 * t + 1]);
+                *reinterpret_cast<half8 *>(&sm.xb[ci & 1][korder(t)][8 * lane]) = bk[t];
+                *reinterpret_cast<half8 *>(sp + 1024 * korder(t) + 16 * lane) = bk[t];
+            }
+            // Barrier ci: all of S' exchanged, chunk ci + 1 landed, and every
+            // read of this wave from earlier chunks' buffers done.
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            loader_barrier();
+#pragma unroll
+            for (int t = KSW; t < 4; ++t)
+                bk[t] = *reinterpret_cast<const half8 *>(&sm.xb[ci & 1][korder(t)][8 * lane]);
+            read_m(bq, tl, sw, korder(1), lane);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < RBW; ++r) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[r][i] = __builtin_fmaf(fv[r][i], S[r][i], (float)nv[r][i]);
+                S[r] = mma32(a[r], bk[0], S[r]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            read_m(a, tl, sw, korder(2), lane);
+            mfma_step(S, bq, bk[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            read_m(bq, tl, sw, korder(3), lane);
+            mfma_step(S, a, bk[2]);
+            __builtin_amdgcn_sched_barrier(0);
+            // the next chunk's first fragments, N and f (unused after the last chunk)
+            const ChunkTiles &nx = sm.buf[(ci + 1) % NBUF];
+            read_m(a, nx, sw, korder(0), lane);
+            read_nf(nv, fv, nx, sw, lane);
+            mfma_step(S, bq, bk[3]);
         }
         if (sT) {
 #pragma unroll
-            for (int cb = 0; cb < 8; ++cb)
+            for (int r = 0; r < RBW; ++r)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * cb + 4 * lg + i) * VD] = S[cb][i];
+                for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * (RBW * sw + r) + 4 * lg + i) * VD] = S[r][i];
         }
     } else {
-        // Loader waves, three buffers: while the state waves work on chunk ci,
-        // chunk ci + 2 is issued into the buffer chunk ci - 1 used, and the
-        // loads of chunk ci + 1 (issued one chunk earlier) must land before the
-        // barrier that ends chunk ci; loads complete in issue order, so a wave
-        // waits until no more than its ci + 2 loads are outstanding.  Each load
-        // thus has two chunk times to arrive.
-        static_assert(SEGS % NLW == 0, "equal load counts per loader wave");
-        constexpr int PER_WAVE = SEGS / NLW;
-        const int lw = w - NSW;
-        auto issue = [&](int ci) {
-            load_tiles<NSW, NLW>(reinterpret_cast<unsigned char *>(&sm.buf[ci % 3]), rec(ci), col0, lw, lane);
-        };
-        for (int c = 0; c < 2 && c < nchunks; ++c) issue(c);
-        if (nchunks > 1)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_WAVE));  // chunk 0 landed
+        // Segments per loader wave: the first SEGS % LOADER_WAVES waves take one more.
+        constexpr int PW = SEGS / LOADER_WAVES;
+        static_assert(SEGS % LOADER_WAVES == 1, "segment split");
+        const int lw = w - STATE_WAVES;
+        if (lw == 0)
+            loader_loop<PW + 1>(sm, recs, cap, h, ch0, nchunks, jt, lw, lane);
         else
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __syncthreads();
-        for (int ci = 0; ci < nchunks; ++ci) {
-            if (ci + 2 < nchunks) {
-                issue(ci + 2);
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_WAVE));
-            } else {
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-            }
-            loader_barrier();
-        }
+            loader_loop<PW>(sm, recs, cap, h, ch0, nchunks, jt, lw, lane);
     }
 }
 
-template <int NSW, int NLW>
 hipError_t launch_state(const float *s0, float *sT, const int32_t *cu, int N, int fixedT,
                         int totalT, int H, int cap, unsigned char *ws, hipStream_t stream) {
-    auto kern = chunk_state_kernel<NSW, NLW>;
-    constexpr int smem = (int)sizeof(StateSmem<NSW, NLW>);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+    constexpr int smem = (int)sizeof(StateSmem);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(chunk_state_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     const int groups = (N * H + 7) / 8;
-    hipLaunchKernelGGL(kern, dim3(groups * 8 * (VD / (16 * NSW))), dim3(64 * (NSW + NLW)), smem,
+    hipLaunchKernelGGL(chunk_state_kernel, dim3(groups * 8 * 8), dim3(64 * (STATE_WAVES + LOADER_WAVES)), smem,
                        stream, s0, sT, cu, fixedT, N, H, totalT, cap, ws);
     return hipGetLastError();
 }
@@ -762,10 +796,9 @@ hipError_t launch_state(const float *s0, float *sT, const int32_t *cu, int N, in
 // ---------------------------------------------------------------- pass 3
 // O = Q^ S' + P U~ for every (chunk, head) at once: one workgroup of 4 waves
 // per record, wave w producing value tiles 2 w and 2 w + 1 (16 columns each).
-// Operands are read as MFMA fragments straight from the record (Q^ with its
-// permuted contraction index matching the S' fragments; P and U~ in natural
-// order); outputs leave through a buffer resource spanning the chunk's valid
-// rows.
+// Operands are read as MFMA fragments straight from the record (Q^ and P
+// with their contraction indices permuted to match the S' and U~ fragments);
+// outputs leave through a buffer resource spanning the chunk's valid rows.
 __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, float x) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
 }
@@ -813,7 +846,7 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(TOut *__restrict__ o,
             bs[ks] = *reinterpret_cast<const half8 *>(rec + R_SP + 4096 * tile + 1024 * ks + 16 * lane);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            bu[ks] = *reinterpret_cast<const half8 *>(rec + R_UT + 2 * (j * C + swz(32 * ks + 8 * lg, j)));
+            bu[ks] = *reinterpret_cast<const half8 *>(rec + R_UT + 16 * ((tile * 2 + ks) * 64 + lane));
         floatx4 Y[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) Y[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -884,7 +917,7 @@ hipError_t launch_chunk_split(const void *q, const void *k, const void *v, const
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    e = launch_state<STATE_WAVES, LOADER_WAVES>(s0, sT, cu, N, fixedT, totalT, H, cap, ws, stream);
+    e = launch_state(s0, sT, cu, N, fixedT, totalT, H, cap, ws, stream);
     if (e != hipSuccess || cap == 0) return e;
     if (out_bf16)
         hipLaunchKernelGGL(chunk_output_kernel<bf16_t>, dim3(cap, H), dim3(256), 0, stream,
