@@ -25,6 +25,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the accumulator-register form costs one
+    # v_accvgpr_read per result element wherever a result feeds vector code
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"),
 ]
 
