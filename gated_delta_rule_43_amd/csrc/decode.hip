@@ -16,7 +16,10 @@
 // workgroup owns one (sequence, head) state: each thread keeps its rows of
 // four consecutive columns in registers between the read and the write-back,
 // so the state crosses HBM exactly twice.  Loads are 16-byte and a wavefront
-// covers whole rows, so every access is fully coalesced.
+// covers whole rows, so every access is fully coalesced.  The write-back uses
+// non-temporal stores: the new state is not read again within the step, and
+// streaming it past the caches lifts the read+write stream from about 5.0 to
+// 6.7 TB/s on MI355X (non-temporal loads, by contrast, slow it down).
 #include "kda_common.hpp"
 
 namespace kda {
@@ -100,13 +103,13 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(
     u.z = b * (to_f32(vp[2]) - RK.z);
     u.w = b * (to_f32(vp[3]) - RK.w);
 
+    typedef float f4v __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rg + i * RG;
         const float kr = sk[r];
-        float4 x = s[i];
-        x.x += kr * u.x; x.y += kr * u.y; x.z += kr * u.z; x.w += kr * u.w;
-        S[r * CG + cg] = x;
+        const f4v x = {s[i].x + kr * u.x, s[i].y + kr * u.y, s[i].z + kr * u.z, s[i].w + kr * u.w};
+        __builtin_nontemporal_store(x, reinterpret_cast<f4v *>(&S[r * CG + cg]));
     }
     if (rg == 0) {
         const float kq = skq;
