@@ -733,7 +733,7 @@ __global__ __launch_bounds__(64 * (STATE_WAVES + LOADER_WAVES)) void chunk_state
             for (int t = 0; t < KSW; ++t) {
                 bk[t] = bfrag(S[2 * t], S[2 * t + 1]);
                 *reinterpret_cast<half8 *>(&sm.xb[ci & 1][korder(t)][8 * lane]) = bk[t];
-                *reinterpret_cast<half8 *>(sp + 1024 * korder(t) + 16 * lane) = bk[t];
+                __builtin_nontemporal_store(bk[t], reinterpret_cast<half8 *>(sp + 1024 * korder(t) + 16 * lane));
             }
             // Barrier ci: all of S' exchanged, chunk ci + 1 landed, and every
             // read of this wave from earlier chunks' buffers done.
@@ -798,12 +798,14 @@ hipError_t launch_state(const float *s0, float *sT, const int32_t *cu, int N, in
 // per record, wave w producing value tiles 2 w and 2 w + 1 (16 columns each).
 // Operands are read as MFMA fragments straight from the record (Q^ and P
 // with their contraction indices permuted to match the S' and U~ fragments);
-// outputs leave through a buffer resource spanning the chunk's valid rows.
+// outputs leave through a buffer resource spanning the chunk's valid rows,
+// as non-temporal stores (nothing in the call reads them back).
+constexpr int CPOL_NT = 2;
 __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, float x) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, CPOL_NT);
 }
 __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, bf16_t x) {
-    __builtin_amdgcn_raw_buffer_store_b16(x.bits, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(x.bits, r, off, 0, CPOL_NT);
 }
 
 template <typename TOut>
