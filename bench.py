@@ -145,7 +145,7 @@ def decode_leg(args, dev, stream):
             dstep()
         torch.cuda.synchronize()
         return {"only": "decode", "workload": DECODE, "launches": args.steps}
-    dms, dwall = time_launches(dstep, args.decode_steps, 3, stream)
+    dms, dwall = time_launches(dstep, args.decode_steps, 20, stream)
     db = decode_alg_bytes(wd.N, wd.H, wd.K, wd.V)
     dach = db / (dms * 1e-3) / 1e9
     return {
@@ -162,7 +162,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU reaches its steady clock after ~100 prefill calls (~7 ms)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
