@@ -274,16 +274,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         }
     }
     __syncthreads();
-    // V in the accumulator layout of waves 2, 3 (rows 16 i + 4 lg + e, column
-    // 64 (w & 1) + 16 b + l16)
-    uint2 vz[4][4];
-    if (w >= 2) {
+    // V in the accumulator layout of this wave's U~ blocks (rows 16 i + 4 lg + e,
+    // column 32 w + 16 b + l16)
+    uint2 vz[2][4];
+    {
         const uint16_t *vst = reinterpret_cast<const uint16_t *>(sm.a16);
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                vz[b][i] = *reinterpret_cast<const uint2 *>(&vst[(64 * (w & 1) + 16 * b + l16) * VTP + 16 * i + 4 * lg]);
+                vz[b][i] = *reinterpret_cast<const uint2 *>(&vst[(32 * w + 16 * b + l16) * VTP + 16 * i + 4 * lg]);
     }
     // Diag(f) Km^T: this thread's channels 8 cg + e, rows 4 rg .. 4 rg + 3,
     // kept in registers until the tile it goes to is free
@@ -390,9 +390,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     __syncthreads();
 
     // ---- (I + A) [W | U~] = Diag(beta) [Kp | V] by 16-row block substitution.
-    // Waves 0, 1 solve for the Kp columns (W), waves 2, 3 for the V columns (U~);
-    // each wave owns four 16-column blocks.
-    const bool wside = w < 2;
+    // Wave w owns column blocks 2 w, 2 w + 1 of both: Xh[0..1] are W's
+    // (Kp columns 32 w .. 32 w + 31), Xh[2..3] U~'s (V columns likewise), so
+    // that the products which follow (Q^ from W, M' from W, N from U~) split
+    // evenly over the four waves.
     // Right-hand sides for all (i, b) first (their LDS reads all in flight
     // together), then row block i outer, the four independent column blocks
     // inner.
@@ -403,10 +404,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 16 * i + 4 * lg + e, col = 64 * (w & 1) + 16 * b + l16;
-                const uint32_t vw = (e < 2) ? vz[b][i].x : vz[b][i].y;
-                zx[i][b][e] = wside ? (float)sm.kp[r * PK + col]
-                                    : __uint_as_float((e & 1) ? (vw & 0xffff0000u) : (vw << 16));
+                const int r = 16 * i + 4 * lg + e, col = 32 * w + 16 * (b & 1) + l16;
+                if (b < 2) {
+                    zx[i][b][e] = (float)sm.kp[r * PK + col];
+                } else {
+                    const uint32_t vw = (e < 2) ? vz[b - 2][i].x : vz[b - 2][i].y;
+                    zx[i][b][e] = __uint_as_float((e & 1) ? (vw & 0xffff0000u) : (vw << 16));
+                }
             }
     half4 Xh[4][4];  // [column block][row block]
 #pragma unroll
@@ -426,25 +430,23 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             Xh[b][i] = to_half4(mma16(ti, to_half4(z), floatx4{0.f, 0.f, 0.f, 0.f}));
         }
     }
-    // ---- Q^ = Qp - P W (waves 0, 1, in place over Qp).
+    // ---- Q^ = Qp - P W (each wave its two W blocks, in place over Qp).
     // The product is formed transposed, (P W)^T = W^T P^T: a lane's W
     // accumulator block read as a 16x16x16 A operand is a block of W^T, and
     // P's row fragment serves as the B operand, so each lane ends up with four
     // consecutive columns of one row: one 8-byte read-modify-write of Qp.
-    if (wside) {
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < 2; ++b) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i <= rb; ++i) acc = mma16(Xh[b][i], frag4(sm.p, P4, 16 * rb, 16 * i, lane), acc);
-                _Float16 *qrow = &sm.qp[(16 * rb + l16) * PK + 64 * (w & 1) + 16 * b + 4 * lg];
-                half4 qv = *reinterpret_cast<const half4 *>(qrow);
+            for (int i = 0; i <= rb; ++i) acc = mma16(Xh[b][i], frag4(sm.p, P4, 16 * rb, 16 * i, lane), acc);
+            _Float16 *qrow = &sm.qp[(16 * rb + l16) * PK + 32 * w + 16 * b + 4 * lg];
+            half4 qv = *reinterpret_cast<const half4 *>(qrow);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) qv[e] = (_Float16)((float)qv[e] - acc[e]);
-                *reinterpret_cast<half4 *>(qrow) = qv;
-            }
+            for (int e = 0; e < 4; ++e) qv[e] = (_Float16)((float)qv[e] - acc[e]);
+            *reinterpret_cast<half4 *>(qrow) = qv;
         }
     }
     __syncthreads();
@@ -484,54 +486,47 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         *reinterpret_cast<half8 *>(rec + R_P + 2 * ((size_t)r * C + 8 * b)) = pv;
     }
     __syncthreads();
-    // ---- M' = -Diag(f) Km^T W (waves 0, 1) and N = Diag(f) Km^T U~ (waves 2,
-    // 3), contracting over s with the W / U~ accumulator blocks as operands.
+    // ---- M' = -Diag(f) Km^T W (from Xh[0..1]) and N = Diag(f) Km^T U~ (from
+    // Xh[2..3]), contracting over s with the accumulator blocks as operands.
     // M' is formed transposed (M'^T = -W^T (Diag(f) Km^T)^T): each lane then
     // holds four consecutive contraction indices of one row of M', which is
-    // what its A-order fragment takes.
+    // what its A-order fragment takes; this wave's two W blocks are the two
+    // halves of k-step w.
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
         half8 kt[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) kt[ks] = *reinterpret_cast<const half8 *>(&sm.kp[kt_frag_off(cb, ks, lane)]);
-        if (wside) {
+        floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
-            for (int jp = 0; jp < 2; ++jp) {
-                floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    a0 = mma32(pair8(Xh[2 * jp][2 * ks], Xh[2 * jp][2 * ks + 1]), kt[ks], a0);
-                    a1 = mma32(pair8(Xh[2 * jp + 1][2 * ks], Xh[2 * jp + 1][2 * ks + 1]), kt[ks], a1);
-                }
-                half8 mv;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    mv[i] = (_Float16)(-a0[i]);
-                    mv[4 + i] = (_Float16)(-a1[i]);
-                }
-                *reinterpret_cast<half8 *>(rec + R_M + 16 * ((cb * 4 + 2 * (w & 1) + jp) * 64 + lane)) = mv;
-            }
-        } else {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    acc = mma32(kt[ks], pair8(Xh[b][2 * ks], Xh[b][2 * ks + 1]), acc);
-                const int jt = 4 * (w & 1) + b;
-                *reinterpret_cast<half4 *>(rec + R_N + 8 * ((jt * 8 + cb) * 64 + lane)) = to_half4(acc);
-            }
+        for (int ks = 0; ks < 2; ++ks) {
+            a0 = mma32(pair8(Xh[0][2 * ks], Xh[0][2 * ks + 1]), kt[ks], a0);
+            a1 = mma32(pair8(Xh[1][2 * ks], Xh[1][2 * ks + 1]), kt[ks], a1);
         }
-    }
-    // ---- U~ (waves 2, 3) in B order, straight from the accumulator blocks
-    if (!wside) {
+        half8 mv;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int i = 0; i < 4; ++i) {
+            mv[i] = (_Float16)(-a0[i]);
+            mv[4 + i] = (_Float16)(-a1[i]);
+        }
+        *reinterpret_cast<half8 *>(rec + R_M + 16 * ((cb * 4 + w) * 64 + lane)) = mv;
+#pragma unroll
+        for (int b = 2; b < 4; ++b) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                *reinterpret_cast<half8 *>(rec + R_UT + 16 * (((4 * (w & 1) + b) * 2 + ks) * 64 + lane)) =
-                    pair8(Xh[b][2 * ks], Xh[b][2 * ks + 1]);
+                acc = mma32(kt[ks], pair8(Xh[b][2 * ks], Xh[b][2 * ks + 1]), acc);
+            const int jt = 2 * w + b - 2;
+            *reinterpret_cast<half4 *>(rec + R_N + 8 * ((jt * 8 + cb) * 64 + lane)) = to_half4(acc);
+        }
     }
+    // ---- U~ in B order, straight from the accumulator blocks
+#pragma unroll
+    for (int b = 2; b < 4; ++b)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            *reinterpret_cast<half8 *>(rec + R_UT + 16 * (((2 * w + b - 2) * 2 + ks) * 64 + lane)) =
+                pair8(Xh[b][2 * ks], Xh[b][2 * ks + 1]);
 }
 
 // ---------------------------------------------------------------- pass 2
