@@ -12,10 +12,10 @@
 // T = (I + A)^-1 Diag(beta) (never formed) and the end-of-chunk factor
 // f = exp(G_C - G_m + G_m of the next chunk of the sequence) (for a
 // sequence's last chunk, exp(G_C - G_m)):
-//   W  = T Kp,   U~ = T V,   Q^ = Qp - P W,
+//   W  = T Kp,   U~ = T V,   Q^ = Qp - P W,   O^ = P U~,
 //   M' = -Diag(f) Km^T W,   N = Diag(f) Km^T U~                       (pass 1)
 //   S' <- Diag(f) S' + M' S' + N,   S' = Diag(exp(G_m)) S             (pass 2)
-//   O  = Q^ S' + P U~                                                  (pass 3)
+//   O  = Q^ S' + O^                                                    (pass 3)
 // (the chunk update S <- Diag(exp(G_C - G_m)) (S' + Km^T (U~ - W S')) and
 // O = Qp S' + P (U~ - W S') regrouped, with the next chunk's G_m folded in so
 // that the state stays in S' form between chunks).
@@ -47,18 +47,17 @@ constexpr int VTP = 68;  // LDS pitch (bf16), V^T staging tile [128][64]
 // Per-(chunk, head) record in the workspace (bytes).  "A order" / "B order":
 // MFMA 16x16x32 operand fragments stored lane by lane, [block][k-step][64
 // lanes][8 halves], so that a wave reads a fragment as one contiguous 1 KB.
-// Contraction indices are stored permuted within each 32-wide block (see
+// Q^'s contraction index is stored permuted within each 32-wide block (see
 // kperm_pos).  The first 37 KB of a record (with the tile's 4 KB of N) are
 // what the state pass streams.
 constexpr size_t R_M = 0;         // fp16 M' in A order [8 row blocks][4 k-steps]
 constexpr size_t R_N = 32768;     // fp16 N as accumulators [8 value tiles][8 row blocks][64 lanes][4]
 constexpr size_t R_FC = 65536;    // fp32 [128]  f
 constexpr size_t R_FM = 66048;    // fp32 [128]  exp(G_m)
-constexpr size_t R_UT = 66560;    // fp16 U~ in B order [8 value tiles][2 k-steps]
+constexpr size_t R_OH = 66560;    // fp16 O^ as accumulators [8 value tiles][4 row blocks][64 lanes][4]
 constexpr size_t R_QH = 82944;    // fp16 [64][128]  Q^ [r][c]
-constexpr size_t R_P = 99328;     // fp16 [64][64]   P [r][s], zero above the diagonal
-constexpr size_t R_SP = 107520;   // fp16 S' in B order [8 value tiles][4 k-steps]
-constexpr size_t REC = 140288;
+constexpr size_t R_SP = 99328;    // fp16 S' in B order [8 value tiles][4 k-steps]
+constexpr size_t REC = 132096;
 constexpr size_t OFFS_BYTES = 512;  // int32 chunk offsets, up to 127 sequences
 
 // Several products take an operand straight out of MFMA accumulators, where
@@ -470,21 +469,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         }
         *reinterpret_cast<half8 *>(rec + R_QH + 2 * ((size_t)r * KD + 8 * bp)) = qv;
     }
-    // ---- P rows, s permuted likewise, zero above the diagonal (16-byte stores)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int idx = 256 * e + t, r = idx >> 3, b = idx & 7;
-        const int l0 = 32 * (b >> 2) + 4 * (b & 3), l1 = l0 + 16;
-        half4 p0 = *reinterpret_cast<const half4 *>(&sm.p[r * P4 + l0]);
-        half4 p1 = *reinterpret_cast<const half4 *>(&sm.p[r * P4 + l1]);
-        half8 pv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pv[i] = (l0 >> 4) > (r >> 4) ? (_Float16)0.f : p0[i];
-            pv[4 + i] = (l1 >> 4) > (r >> 4) ? (_Float16)0.f : p1[i];
-        }
-        *reinterpret_cast<half8 *>(rec + R_P + 2 * ((size_t)r * C + 8 * b)) = pv;
-    }
     __syncthreads();
     // ---- M' = -Diag(f) Km^T W (from Xh[0..1]) and N = Diag(f) Km^T U~ (from
     // Xh[2..3]), contracting over s with the accumulator blocks as operands.
@@ -520,13 +504,33 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             *reinterpret_cast<half4 *>(rec + R_N + 8 * ((jt * 8 + cb) * 64 + lane)) = to_half4(acc);
         }
     }
-    // ---- U~ in B order, straight from the accumulator blocks
+    // ---- O^ = P U~ for this wave's U~ blocks (value tiles 2 w, 2 w + 1), stored
+    // as the output pass's accumulators.  P's A fragments take the permuted
+    // contraction order of the U~ pairs: logical s = 32 ks + 4 lg .. +3 and
+    // that + 16, from the [r][s] tile; blocks above P's diagonal block are
+    // zero (their LDS is never written).
+    half8 pf[4][2];
 #pragma unroll
-    for (int b = 2; b < 4; ++b)
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            *reinterpret_cast<half8 *>(rec + R_UT + 16 * (((2 * w + b - 2) * 2 + ks) * 64 + lane)) =
-                pair8(Xh[b][2 * ks], Xh[b][2 * ks + 1]);
+        for (int ks = 0; ks < 2; ++ks) {
+            const _Float16 *prow = &sm.p[(16 * rb + l16) * P4 + 32 * ks + 4 * lg];
+            const half4 lo = 2 * ks > rb ? half4{0, 0, 0, 0} : *reinterpret_cast<const half4 *>(prow);
+            const half4 hi = 2 * ks + 1 > rb ? half4{0, 0, 0, 0} : *reinterpret_cast<const half4 *>(prow + 16);
+            pf[rb][ks] = pair8(lo, hi);
+        }
+#pragma unroll
+    for (int b = 2; b < 4; ++b) {
+        const int jt = 2 * w + b - 2;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                if (2 * ks <= rb) acc = mma32(pf[rb][ks], pair8(Xh[b][2 * ks], Xh[b][2 * ks + 1]), acc);
+            *reinterpret_cast<half4 *>(rec + R_OH + 8 * ((jt * 4 + rb) * 64 + lane)) = to_half4(acc);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- pass 2
@@ -789,10 +793,10 @@ hipError_t launch_state(const float *s0, float *sT, const int32_t *cu, int N, in
 }
 
 // ---------------------------------------------------------------- pass 3
-// O = Q^ S' + P U~ for every (chunk, head) at once: one workgroup of 4 waves
+// O = Q^ S' + O^ for every (chunk, head) at once: one workgroup of 4 waves
 // per record, wave w producing value tiles 2 w and 2 w + 1 (16 columns each).
-// Operands are read as MFMA fragments straight from the record (Q^ and P
-// with their contraction indices permuted to match the S' and U~ fragments);
+// The accumulators start from O^; Q^ (contraction index permuted to match the
+// S' fragments) and S' are read as MFMA fragments straight from the record;
 // outputs leave through a buffer resource spanning the chunk's valid rows,
 // as non-temporal stores (nothing in the call reads them back).
 constexpr int CPOL_NT = 2;
@@ -820,37 +824,29 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(TOut *__restrict__ o,
 
     const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    half8 aq[4][4], ap[2][4];
+    half8 aq[4][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
             aq[ks][rb] = *reinterpret_cast<const half8 *>(rec + R_QH + 2 * ((16 * rb + l16) * KD + 8 * (4 * ks + lg)));
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-            ap[ks][rb] = *reinterpret_cast<const half8 *>(rec + R_P + 2 * ((16 * rb + l16) * C + 32 * ks + 8 * lg));
     const int row_bytes = H * VD * (int)sizeof(TOut);
     __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
         o + (size_t)c0 * H * VD, 0, L * row_bytes, 0x00020000);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
         const int tile = 2 * w + tt, j = 16 * tile + l16;
-        half8 bs[4], bu[2];
+        half8 bs[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
             bs[ks] = *reinterpret_cast<const half8 *>(rec + R_SP + 4096 * tile + 1024 * ks + 16 * lane);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            bu[ks] = *reinterpret_cast<const half8 *>(rec + R_UT + 16 * ((tile * 2 + ks) * 64 + lane));
         floatx4 Y[4];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) Y[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int rb = 0; rb < 4; ++rb) {
+            const half4 oh = *reinterpret_cast<const half4 *>(rec + R_OH + 8 * ((tile * 4 + rb) * 64 + lane));
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) Y[rb] = mma32(ap[ks][rb], bu[ks], Y[rb]);
+            for (int e = 0; e < 4; ++e) Y[rb][e] = (float)oh[e];
+        }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
