@@ -732,7 +732,9 @@ __global__ __launch_bounds__(64 * (STATE_WAVES + LOADER_WAVES)) void chunk_state
             for (int t = 0; t < KSW; ++t) {
                 bk[t] = bfrag(S[2 * t], S[2 * t + 1]);
                 *reinterpret_cast<half8 *>(&sm.xb[ci & 1][korder(t)][8 * lane]) = bk[t];
-                __builtin_nontemporal_store(bk[t], reinterpret_cast<half8 *>(sp + 1024 * korder(t) + 16 * lane));
+                // an ordinary (L2-resident) store: the output pass reads the
+                // snapshot back shortly; a non-temporal one costs ~6% of the call
+                *reinterpret_cast<half8 *>(sp + 1024 * korder(t) + 16 * lane) = bk[t];
             }
             // Barrier ci: all of S' exchanged, chunk ci + 1 landed, and every
             // read of this wave from earlier chunks' buffers done.
