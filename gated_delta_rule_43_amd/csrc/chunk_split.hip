@@ -8,22 +8,26 @@
 // fill the GPU.  Everything that does not depend on the state is computed
 // first, for all chunks at once; the sequential pass is then a short chain.
 //
-// With Kp, Km, Qp, A, P, G_m and G_C as in chunk_mfma.hip,
-// T = (I + A)^-1 Diag(beta) (never formed) and the end-of-chunk factor
-// f = exp(G_C - G_m + G_m of the next chunk of the sequence) (for a
-// sequence's last chunk, exp(G_C - G_m)):
-//   W  = T Kp,   U~ = T V,   Q^ = Qp - P W,   O^ = P U~,
-//   M' = -Diag(f) Km^T W,   N = Diag(f) Km^T U~                       (pass 1)
-//   S' <- Diag(f) S' + M' S' + N,   S' = Diag(exp(G_m)) S             (pass 2)
-//   O  = Q^ S' + O^                                                    (pass 3)
-// (the chunk update S <- Diag(exp(G_C - G_m)) (S' + Km^T (U~ - W S')) and
-// O = Qp S' + P (U~ - W S') regrouped, with the next chunk's G_m folded in so
-// that the state stays in S' form between chunks).
+// With Kp, Km, Qp, A, P, G_m and G_C as in chunk_mfma.hip, S the state at
+// the chunk's start, E = Diag(exp(G_m)) and T = (I + A)^-1 Diag(beta) (never
+// formed):
+//   W  = T Kp,   U~ = T V,   Q^ = (Qp - P W) E,   O^ = P U~,
+//   M' = -Diag(exp(G_C - G_m)) Km^T W E,
+//   N  =  Diag(exp(G_C - G_m)) Km^T U~,   f = exp(G_C)                 (pass 1)
+//   S <- Diag(f) S + M' S + N                                          (pass 2)
+//   O  = Q^ S + O^                                                     (pass 3)
+// which is the chunk update S <- Diag(exp(G_C)) S + Diag(exp(G_C - G_m))
+// Km^T (U~ - W E S) and output O = (Qp - P W) E S + P U~ regrouped.  The
+// mid-chunk reference G_m keeps Kp, Km and Qp (fp16 MFMA operands) within
+// e^+-8; the column factor E is applied in fp32 before the one rounding of
+// Q^ and M' to fp16, whose entries then have magnitude of at most those of
+// q and of an undecayed update.  Each chunk's records depend on that chunk
+// alone.
 //
 // Pass 1 (chunk_prep_kernel): one workgroup of 4 waves per (chunk, head), all
 // chunks in parallel.  Pass 2 (chunk_state_kernel): one workgroup per
-// (sequence, head, 16-column value tile); one state wave runs the chain with
-// the state in registers (one 128 x 128 x 16 product per chunk) while seven
+// (sequence, head, 16-column value tile); four state waves run the chain with
+// the state in registers (one 128 x 128 x 16 product per chunk) while four
 // loader waves stream the next chunks' M', N and f into LDS with direct loads.
 // Pass 3 (chunk_output_kernel): one workgroup per (chunk, head).
 // Intermediates live in the caller's workspace.
@@ -48,21 +52,20 @@ constexpr int VTP = 68;  // LDS pitch (bf16), V^T staging tile [128][64]
 // MFMA 16x16x32 operand fragments stored lane by lane, [block][k-step][64
 // lanes][8 halves], so that a wave reads a fragment as one contiguous 1 KB.
 // Q^'s contraction index is stored permuted within each 32-wide block (see
-// kperm_pos).  The first 37 KB of a record (with the tile's 4 KB of N) are
-// what the state pass streams.
+// kperm_pos).  M', f and one value tile's 4 KB of N (36.5 KB) are what the
+// state pass streams per chunk.
 constexpr size_t R_M = 0;         // fp16 M' in A order [8 row blocks][4 k-steps]
 constexpr size_t R_N = 32768;     // fp16 N as accumulators [8 value tiles][8 row blocks][64 lanes][4]
 constexpr size_t R_FC = 65536;    // fp32 [128]  f
-constexpr size_t R_FM = 66048;    // fp32 [128]  exp(G_m)
-constexpr size_t R_OH = 66560;    // fp16 O^ as accumulators [8 value tiles][4 row blocks][64 lanes][4]
-constexpr size_t R_QH = 82944;    // fp16 [64][128]  Q^ [r][c]
-constexpr size_t R_SP = 99328;    // fp16 S' in B order [8 value tiles][4 k-steps]
-constexpr size_t REC = 132096;
+constexpr size_t R_OH = 66048;    // fp16 O^ as accumulators [8 value tiles][4 row blocks][64 lanes][4]
+constexpr size_t R_QH = 82432;    // fp16 [64][128]  Q^ [r][c]
+constexpr size_t R_SP = 98816;    // fp16 S (chunk-start state) in B order [8 value tiles][4 k-steps]
+constexpr size_t REC = 131584;
 constexpr size_t OFFS_BYTES = 512;  // int32 chunk offsets, up to 127 sequences
 
 // Several products take an operand straight out of MFMA accumulators, where
-// lane l holds rows 4 (l >> 4) .. +3 of each 16-row block: the state S' (in
-// M' S' and Q^ S'), and W and U~ (in M' and N).  A 16x16x32 fragment wants 8
+// lane l holds rows 4 (l >> 4) .. +3 of each 16-row block: the state S (in
+// M' S and Q^ S), and W and U~ (in M' and N).  A 16x16x32 fragment wants 8
 // k values per lane; taking the lane's rows of blocks 2 ks and 2 ks + 1 as
 // those 8 values keeps the operand in registers, provided the other operand's
 // k values are laid out in the same order.  Within each 32-wide block, stored
@@ -150,7 +153,7 @@ struct PrepSmem {
     float ad[4][16 * PF];   // diagonal A blocks, fp32
     float beta[C];
     float gsum[4][KD];      // per-wave channel sums of g
-    float gnext[2][KD];     // per-wave sums of the next chunk's first 32 rows of g
+    float egm[KD];          // exp(G_m)
 };
 
 __device__ __forceinline__ floatx4 block32(const _Float16 *lhs, const _Float16 *rhs, int bi, int bj,
@@ -200,17 +203,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     }
     float bt_in = 0.f;
     if (w == 0) bt_in = __uint_as_float((uint32_t)beta[(size_t)(c0 + min(t, L - 1)) * H + h] << 16);
-    // The first half of the next chunk of this sequence (if any): its G_m is
-    // folded into this chunk's end-of-chunk scale factor.
-    uint4 rgn[4] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u),
-                     make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
-    if (w < 2) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int r = min(c0 + C + 4 * rg + u, eos - 1);
-            rgn[u] = *reinterpret_cast<const uint4 *>(g + ((size_t)r * H + h) * KD + 8 * cg);
-        }
-    }
     const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -220,7 +212,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             rgv[u] = zero4;
             rv[u] = zero4;
         }
-        if (c0 + C + 4 * rg + u >= eos) rgn[u] = zero4;
     }
     if (w == 0) sm.beta[t] = t < L ? bt_in : 0.f;
 
@@ -260,18 +251,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             *reinterpret_cast<uint2 *>(&vst[(8 * cg + e) * VTP + 4 * rg]) = pk;
         }
     }
-    if (w < 2) {
-        float gn[4][8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) unpack8(rgn[u], gn[u]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = gn[0][e] + gn[1][e] + gn[2][e] + gn[3][e];
-            x += __shfl_xor(x, 16);
-            x += __shfl_xor(x, 32);
-            if (lg == 0) sm.gnext[w][8 * cg + e] = x;
-        }
-    }
     __syncthreads();
     // V in the accumulator layout of this wave's U~ blocks (rows 16 i + 4 lg + e,
     // column 32 w + 16 b + l16)
@@ -306,11 +285,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             if (w >= 1) pre += s0w;
             if (w >= 2) pre += s1w;
             if (w >= 3) pre += s2w;
-            // end-of-chunk factor: exp(G_C - G_m + G_m of the next chunk)
-            const float fe = fast_exp(gcl - gm + sm.gnext[0][ch] + sm.gnext[1][ch]);
+            // row factor of M' and N: exp(G_C - G_m)
+            const float fe = fast_exp(gcl - gm);
             if (rg == 0) {
-                reinterpret_cast<float *>(rec + R_FM)[ch] = fast_exp(gm);
-                reinterpret_cast<float *>(rec + R_FC)[ch] = fe;
+                sm.egm[ch] = fast_exp(gm);
+                reinterpret_cast<float *>(rec + R_FC)[ch] = fast_exp(gcl);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -429,11 +408,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             Xh[b][i] = to_half4(mma16(ti, to_half4(z), floatx4{0.f, 0.f, 0.f, 0.f}));
         }
     }
-    // ---- Q^ = Qp - P W (each wave its two W blocks, in place over Qp).
+    // ---- Q^ = (Qp - P W) E (each wave its two W blocks, in place over Qp).
     // The product is formed transposed, (P W)^T = W^T P^T: a lane's W
     // accumulator block read as a 16x16x16 A operand is a block of W^T, and
     // P's row fragment serves as the B operand, so each lane ends up with four
     // consecutive columns of one row: one 8-byte read-modify-write of Qp.
+    // The lane's key channels here (32 w + 16 b + 4 lg + e) are also those of
+    // its M' elements below: their exp(G_m) factors, read once.
+    floatx4 ecol[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) ecol[b] = *reinterpret_cast<const floatx4 *>(&sm.egm[32 * w + 16 * b + 4 * lg]);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
@@ -444,7 +428,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             _Float16 *qrow = &sm.qp[(16 * rb + l16) * PK + 32 * w + 16 * b + 4 * lg];
             half4 qv = *reinterpret_cast<const half4 *>(qrow);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) qv[e] = (_Float16)((float)qv[e] - acc[e]);
+            for (int e = 0; e < 4; ++e) qv[e] = (_Float16)(((float)qv[e] - acc[e]) * ecol[b][e]);
             *reinterpret_cast<half4 *>(qrow) = qv;
         }
     }
@@ -470,12 +454,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         *reinterpret_cast<half8 *>(rec + R_QH + 2 * ((size_t)r * KD + 8 * bp)) = qv;
     }
     __syncthreads();
-    // ---- M' = -Diag(f) Km^T W (from Xh[0..1]) and N = Diag(f) Km^T U~ (from
-    // Xh[2..3]), contracting over s with the accumulator blocks as operands.
-    // M' is formed transposed (M'^T = -W^T (Diag(f) Km^T)^T): each lane then
-    // holds four consecutive contraction indices of one row of M', which is
-    // what its A-order fragment takes; this wave's two W blocks are the two
-    // halves of k-step w.
+    // ---- M' = -Diag(f) Km^T W E (from Xh[0..1]) and N = Diag(f) Km^T U~
+    // (from Xh[2..3]), f = exp(G_C - G_m) here, contracting over s with the
+    // accumulator blocks as operands.  M' is formed transposed
+    // (M'^T = -E W^T (Diag(f) Km^T)^T): each lane then holds four consecutive
+    // contraction indices of one row of M' (key channels 32 w + 4 lg + i and
+    // that + 16, whose E factors are ecol), which is what its A-order fragment
+    // takes; this wave's two W blocks are the two halves of k-step w.
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
         half8 kt[2];
@@ -490,8 +475,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         half8 mv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            mv[i] = (_Float16)(-a0[i]);
-            mv[4 + i] = (_Float16)(-a1[i]);
+            mv[i] = (_Float16)(-a0[i] * ecol[0][i]);
+            mv[4 + i] = (_Float16)(-a1[i] * ecol[1][i]);
         }
         *reinterpret_cast<half8 *>(rec + R_M + 16 * ((cb * 4 + w) * 64 + lane)) = mv;
 #pragma unroll
@@ -542,15 +527,16 @@ struct ChunkTiles {
     _Float16 m[8 * 4 * 64 * 8];  // M' fragments [row block][k-step][lane][8]
     _Float16 n[8 * 64 * 4];      // N [row block][lane][4], accumulator layout
     float fc[KD];                // f
-    float fm[KD];                // exp(G_m)
 };
-constexpr int SEGS = (int)(sizeof(ChunkTiles) / 1024);  // 37
-static_assert(sizeof(ChunkTiles) == 37 * 1024, "segment count");
-static_assert(R_FM == R_FC + 512, "f and exp(G_m) form the last segment");
+// The tiles are copied in 1 KB segments (16 bytes per lane); the last one, f,
+// is half a segment.
+constexpr int SLOTS = (int)(sizeof(ChunkTiles) / 16);  // 2336
+constexpr int SEGS = (SLOTS + 63) / 64;                 // 37
+static_assert(SLOTS == 36 * 64 + 32, "segment count");
 
 struct StateSmem {
     ChunkTiles buf[NBUF];
-    _Float16 xb[2][4][64 * 8];  // S' B fragments exchanged between the state waves [parity][k-step]
+    _Float16 xb[2][4][64 * 8];  // S B fragments exchanged between the state waves [parity][k-step]
 };
 
 // Workgroup barrier without a memory fence: waves that must see each other's
@@ -565,7 +551,7 @@ __device__ __forceinline__ void loader_barrier() {
 }
 
 // Global source of LDS slot p (16-byte units) of a ChunkTiles image for value
-// tile jt: M' (2048 slots), the tile's N (256), then f and exp(G_m) (64).
+// tile jt: M' (2048 slots), the tile's N (256), then f (32).
 __device__ __forceinline__ const unsigned char *tile_source(const unsigned char *rec, int p, int jt) {
     return p < 2048 ? rec + R_M + 16 * p
          : p < 2304 ? rec + R_N + 4096 * jt + 16 * (p - 2048)
@@ -582,14 +568,16 @@ __device__ __forceinline__ void lds_dma16(const unsigned char *src, unsigned cha
 // (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
-// Loader wave lw copies segments lw, lw + LOADER_WAVES, ... (PW of them).
-template <int PW>
+// Loader wave lw copies segments lw, lw + LOADER_WAVES, ... (PW of them);
+// HALF_LAST: its last one is the half segment (lanes 0-31 only).
+template <int PW, bool HALF_LAST>
 __device__ __forceinline__ void load_tiles(unsigned char *dst, const unsigned char *rec, int jt,
                                            int lw, int lane) {
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
         const int sg = lw + LOADER_WAVES * i;
-        lds_dma16(tile_source(rec, 64 * sg + lane, jt), dst + 1024 * sg);
+        if (!(HALF_LAST && i == PW - 1) || lane < 32)
+            lds_dma16(tile_source(rec, 64 * sg + lane, jt), dst + 1024 * sg);
     }
 }
 
@@ -600,11 +588,11 @@ __device__ __forceinline__ void load_tiles(unsigned char *dst, const unsigned ch
 // barrier ci - 1.  Loads complete in issue order, so "chunk ci + 1 landed" is
 // "at most the loads of chunk ci + 2 outstanding": each chunk has two chunk
 // times to arrive.
-template <int PW>
+template <int PW, bool HALF_LAST>
 __device__ __forceinline__ void loader_loop(StateSmem &sm, const unsigned char *recs, int cap,
                                             int h, int ch0, int nchunks, int jt, int lw, int lane) {
     auto issue = [&](int ci) {
-        load_tiles<PW>(reinterpret_cast<unsigned char *>(&sm.buf[ci % NBUF]),
+        load_tiles<PW, HALF_LAST>(reinterpret_cast<unsigned char *>(&sm.buf[ci % NBUF]),
                        recs + ((size_t)h * cap + ch0 + ci) * REC, jt, lw, lane);
     };
     for (int c = 0; c < 3 && c < nchunks; ++c) issue(c);
@@ -664,11 +652,11 @@ __device__ __forceinline__ void mfma_step(floatx4 (&S)[RBW], const half8 (&a)[RB
 // which serves their common M' tiles.  Waves [0, STATE_WAVES) are the state
 // waves, the rest the loaders.
 //
-// State wave sw keeps RBW row blocks of the tile's 128 x 16 slice of S' in
+// State wave sw keeps RBW row blocks of the tile's 128 x 16 slice of S in
 // accumulators: the rows of its k-steps KSW sw .. KSW sw + KSW - 1.  Per chunk
 // it converts them to those k-steps' fp16 B fragments, publishes them (for
 // the output pass) and hands them to the other state waves through LDS;
-// barrier ci makes all of them visible.  It then forms Diag(f) S' + N on its
+// barrier ci makes all of them visible.  It then forms Diag(f) S + N on its
 // rows and adds the products of its own k-steps first and the others' after
 // (cyclic order from its own), reading M' fragments one k-step ahead and the
 // next chunk's first ones after this chunk's last; the exchanged fragments
@@ -713,14 +701,6 @@ __global__ __launch_bounds__(64 * (STATE_WAVES + LOADER_WAVES)) void chunk_state
         half4 nv[RBW];
         floatx4 fv[RBW];
         if (nchunks > 0) {
-            // S' of the first chunk; later chunks receive theirs from the
-            // previous chunk's end-of-chunk factor
-#pragma unroll
-            for (int r = 0; r < RBW; ++r) {
-                const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.buf[0].fm[16 * (RBW * sw + r) + 4 * lg]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[r][i] *= f[i];
-            }
             read_m(a, sm.buf[0], sw, korder(0), lane);
             read_nf(nv, fv, sm.buf[0], sw, lane);
         }
@@ -736,7 +716,7 @@ __global__ __launch_bounds__(64 * (STATE_WAVES + LOADER_WAVES)) void chunk_state
                 // snapshot back shortly; a non-temporal one costs ~6% of the call
                 *reinterpret_cast<half8 *>(sp + 1024 * korder(t) + 16 * lane) = bk[t];
             }
-            // Barrier ci: all of S' exchanged, chunk ci + 1 landed, and every
+            // Barrier ci: all of S exchanged, chunk ci + 1 landed, and every
             // read of this wave from earlier chunks' buffers done.
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
             loader_barrier();
@@ -776,9 +756,9 @@ __global__ __launch_bounds__(64 * (STATE_WAVES + LOADER_WAVES)) void chunk_state
         static_assert(SEGS % LOADER_WAVES == 1, "segment split");
         const int lw = w - STATE_WAVES;
         if (lw == 0)
-            loader_loop<PW + 1>(sm, recs, cap, h, ch0, nchunks, jt, lw, lane);
+            loader_loop<PW + 1, true>(sm, recs, cap, h, ch0, nchunks, jt, lw, lane);
         else
-            loader_loop<PW>(sm, recs, cap, h, ch0, nchunks, jt, lw, lane);
+            loader_loop<PW, false>(sm, recs, cap, h, ch0, nchunks, jt, lw, lane);
     }
 }
 
@@ -795,10 +775,11 @@ hipError_t launch_state(const float *s0, float *sT, const int32_t *cu, int N, in
 }
 
 // ---------------------------------------------------------------- pass 3
-// O = Q^ S' + O^ for every (chunk, head) at once: one workgroup of 4 waves
+// O = Q^ S + O^ for every (chunk, head) at once: one workgroup of 4 waves
 // per record, wave w producing value tiles 2 w and 2 w + 1 (16 columns each).
 // The accumulators start from O^; Q^ (contraction index permuted to match the
-// S' fragments) and S' are read as MFMA fragments straight from the record;
+// S fragments) and the chunk-start state S are read as MFMA fragments
+// straight from the record;
 // outputs leave through a buffer resource spanning the chunk's valid rows,
 // as non-temporal stores (nothing in the call reads them back).
 constexpr int CPOL_NT = 2;

@@ -138,7 +138,7 @@ size_t kda_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk);
 /* Workspace bytes that select the two-pass path whenever it is supported:
  * (K, V, chunk) = (128, 128, 64), 1 <= N <= 126; 0 when it is not.  The
  * two-pass path runs for bf16 inputs only; fp32 inputs ignore the workspace.
- * Size: 512 + ceil((total_T + 63 N) / 64) * H * 132096 bytes. */
+ * Size: 512 + ceil((total_T + 63 N) / 64) * H * 131584 bytes. */
 size_t kda_two_pass_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk);
 
 /* Static, human-readable name of a status code. */

@@ -48,9 +48,9 @@ def test_status_strings_and_version(lib):
 
 
 def two_pass_size(N, total, H):
-    # offsets block, then one 132096-byte record per (chunk, head) for the
+    # offsets block, then one 131584-byte record per (chunk, head) for the
     # packed-sequence chunk bound
-    return 512 + -(-(total + 63 * N) // 64) * H * 132096
+    return 512 + -(-(total + 63 * N) // 64) * H * 131584
 
 
 def test_workspace_sizes(lib):
