@@ -120,16 +120,19 @@ __device__ __forceinline__ ChunkMap chunk_map(const int32_t *cu, int fixedT, con
 // ---------------------------------------------------------------- pass 1
 // Diag(f) Km^T tile of pass 1 ([128][64] fp16, no padding): half offset of the
 // logical 4-group q of row c (the contraction index s permuted as kperm_pos
-// says, then the row's 16-byte blocks XOR-permuted by (c & 7) so that the 16
-// rows of a fragment read fall in distinct banks), and of the 16x16x32
-// fragment (rows 16 cb .. +15, k-step ks) a lane reads.
+// says, then the row's 16-byte blocks XOR-permuted by kt_swz(c)), and of the
+// 16x16x32 fragment (rows 16 cb .. +15, k-step ks) a lane reads.  The rows of
+// a fragment read (16 consecutive c) and of one write instruction (c = 8 cg +
+// e for 16 values of cg) both get 8 distinct swizzles, so neither piles onto
+// one bank group.
+__device__ __forceinline__ int kt_swz(int c) { return (c ^ (c >> 3)) & 7; }
 __device__ __forceinline__ int kt_off(int c, int q) {
     const int pos = kperm_pos(q);
-    return c * C + ((((pos >> 3) ^ (c & 7))) << 3) + (pos & 7);
+    return c * C + (((pos >> 3) ^ kt_swz(c)) << 3) + (pos & 7);
 }
 __device__ __forceinline__ int kt_frag_off(int cb, int ks, int lane) {
     const int c = 16 * cb + (lane & 15);
-    return c * C + (((4 * ks + (lane >> 4)) ^ (c & 7)) << 3);
+    return c * C + (((4 * ks + (lane >> 4)) ^ kt_swz(c)) << 3);
 }
 // Two accumulator blocks (16 rows each) of one lane as the 8 k values of a
 // 16x16x32 fragment in permuted order (block 2 ks first, then 2 ks + 1).
@@ -274,11 +277,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             unpack8(rq[u], qv[u]);
         }
         half8 kpr[4], qpr[4], kmr[4];
+        floatx4 gs[4][2];  // the four waves' channel sums for channels 8 cg ..
+#pragma unroll
+        for (int wi = 0; wi < 4; ++wi)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) gs[wi][hh] = *reinterpret_cast<const floatx4 *>(&sm.gsum[wi][8 * cg + 4 * hh]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int ch = 8 * cg + e;
-            const float s0w = sm.gsum[0][ch], s1w = sm.gsum[1][ch], s2w = sm.gsum[2][ch],
-                        s3w = sm.gsum[3][ch];
+            const float s0w = gs[0][e >> 2][e & 3], s1w = gs[1][e >> 2][e & 3], s2w = gs[2][e >> 2][e & 3],
+                        s3w = gs[3][e >> 2][e & 3];
             const float gm = s0w + s1w;                 // G at token 31 (end of wave 1's rows)
             const float gcl = gm + s2w + s3w;           // G at token 63
             float pre = ex[e] - gm;
