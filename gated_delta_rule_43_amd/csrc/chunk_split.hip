@@ -191,21 +191,26 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const int l16 = lane & 15, lg = lane >> 4;
     const int cg = t & 15, rg = t >> 4;  // channels 8 cg .., rows 4 rg .. 4 rg + 3
 
-    // ---- loads and the running log-decay sum.  Every load is issued
-    // unconditionally (rows past the chunk's end re-read its last row and are
-    // zeroed afterwards), so that all of them are in flight together.
+    // ---- loads, issued unconditionally (rows past the chunk's end re-read
+    // its last row and are zeroed afterwards) and in the order they are
+    // needed: g (the gate scan and every decay factor), then k and q (the
+    // scaled operands), then v (staged last), so that the scan and the
+    // exponentials run while the later rows are still arriving.
     uint4 rq[4], rk[4], rgv[4], rv[4];
+    size_t off[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int r = min(4 * rg + u, L - 1);
-        const size_t off = ((size_t)(c0 + r) * H + h) * KD + 8 * cg;
-        rq[u] = *reinterpret_cast<const uint4 *>(q + off);
-        rk[u] = *reinterpret_cast<const uint4 *>(k + off);
-        rgv[u] = *reinterpret_cast<const uint4 *>(g + off);
-        rv[u] = *reinterpret_cast<const uint4 *>(v + off);
-    }
-    float bt_in = 0.f;
-    if (w == 0) bt_in = __uint_as_float((uint32_t)beta[(size_t)(c0 + min(t, L - 1)) * H + h] << 16);
+    for (int u = 0; u < 4; ++u) off[u] = ((size_t)(c0 + min(4 * rg + u, L - 1)) * H + h) * KD + 8 * cg;
+    // beta of row t & 63 (every wave loads it, so that no wave waits on a
+    // load of its own before issuing the rest; wave 0 stores it)
+    const uint16_t bt_raw = beta[(size_t)(c0 + min(t & 63, L - 1)) * H + h];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rgv[u] = *reinterpret_cast<const uint4 *>(g + off[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rk[u] = *reinterpret_cast<const uint4 *>(k + off[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rq[u] = *reinterpret_cast<const uint4 *>(q + off[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rv[u] = *reinterpret_cast<const uint4 *>(v + off[u]);
     const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -216,28 +221,104 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             rv[u] = zero4;
         }
     }
-    if (w == 0) sm.beta[t] = t < L ? bt_in : 0.f;
 
+    // ---- running log-decay sum: within the thread's 4 rows, then across the
+    // wave's 4 row groups (two shuffles, all 8 channels together), then across
+    // waves through LDS
     float G[4][8], ex[8];
 #pragma unroll
     for (int u = 0; u < 4; ++u) unpack8(rgv[u], G[u]);
+    float sc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         G[1][e] += G[0][e];
         G[2][e] += G[1][e];
         G[3][e] += G[2][e];
-        const float tot = G[3][e];
-        float s = tot;
-        float x = __shfl_up(s, 16);
-        if (lg >= 1) s += x;
-        x = __shfl_up(s, 32);
-        if (lg >= 2) s += x;
-        ex[e] = s - tot;
-        if (lg == 3) sm.gsum[w][8 * cg + e] = s;
+        sc[e] = G[3][e];
     }
-    // V^T staging copy (bf16 [column][row], pitch VTP) in the A/P tiles, which
-    // are not used before the Gram phase: the two waves that solve for U~
-    // read it back in their MFMA accumulator layout
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = __shfl_up(sc[e], 16);
+        if (lg >= 1) sc[e] += x;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = __shfl_up(sc[e], 32);
+        if (lg >= 2) sc[e] += x;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ex[e] = sc[e] - G[3][e];
+    if (lg == 3) {
+        *reinterpret_cast<floatx4 *>(&sm.gsum[w][8 * cg]) = floatx4{sc[0], sc[1], sc[2], sc[3]};
+        *reinterpret_cast<floatx4 *>(&sm.gsum[w][8 * cg + 4]) = floatx4{sc[4], sc[5], sc[6], sc[7]};
+    }
+    if (w == 0) sm.beta[t] = t < L ? __uint_as_float((uint32_t)bt_raw << 16) : 0.f;
+    __syncthreads();
+
+    // ---- decay factors of this thread's rows and channels (g only):
+    // f = exp(G - G_m) and its reciprocal; per channel exp(G_C - G_m) (the row
+    // factor of M' and N), exp(G_m) and f of the state pass, exp(G_C)
+    float fx[4][8], fr[4][8], fe[8];
+    {
+        floatx4 gs[4][2];  // the four waves' channel sums for channels 8 cg ..
+#pragma unroll
+        for (int wi = 0; wi < 4; ++wi)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) gs[wi][hh] = *reinterpret_cast<const floatx4 *>(&sm.gsum[wi][8 * cg + 4 * hh]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int ch = 8 * cg + e;
+            const float s0w = gs[0][e >> 2][e & 3], s1w = gs[1][e >> 2][e & 3], s2w = gs[2][e >> 2][e & 3],
+                        s3w = gs[3][e >> 2][e & 3];
+            const float gm = s0w + s1w;                 // G at token 31 (end of wave 1's rows)
+            const float gcl = gm + s2w + s3w;           // G at token 63
+            float pre = ex[e] - gm;
+            if (w >= 1) pre += s0w;
+            if (w >= 2) pre += s1w;
+            if (w >= 3) pre += s2w;
+            fe[e] = fast_exp(gcl - gm);
+            if (rg == 0) {
+                sm.egm[ch] = fast_exp(gm);
+                reinterpret_cast<float *>(rec + R_FC)[ch] = fast_exp(gcl);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                fx[u][e] = fast_exp(pre + G[u][e]);  // exp(G - G_m)
+                fr[u][e] = __builtin_amdgcn_rcpf(fx[u][e]);
+            }
+        }
+    }
+    // ---- Kp, Qp, Km (and Diag(f) Km^T, kept in registers for this thread's
+    // channels 8 cg + e and rows 4 rg .. 4 rg + 3 until the tile it goes to
+    // is free)
+    half4 kmT[8];
+    {
+        half8 kpr[4], qpr[4], kmr[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float kv[8], qv[8];
+            unpack8(rk[u], kv);
+            unpack8(rq[u], qv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kpr[u][e] = (_Float16)(kv[e] * fx[u][e]);
+                qpr[u][e] = (_Float16)(qv[e] * fx[u][e]);
+                const float km = kv[e] * fr[u][e];
+                kmr[u][e] = (_Float16)km;
+                kmT[e][u] = (_Float16)(km * fe[e]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = 4 * rg + u;
+            *reinterpret_cast<half8 *>(&sm.kp[r * PK + 8 * cg]) = kpr[u];
+            *reinterpret_cast<half8 *>(&sm.qp[r * PK + 8 * cg]) = qpr[u];
+            *reinterpret_cast<half8 *>(&sm.km[r * PK + 8 * cg]) = kmr[u];
+        }
+    }
+    // ---- V^T staging copy (bf16 [column][row], pitch VTP) in the A/P tiles,
+    // which are not used before the Gram phase: each wave reads back its U~
+    // blocks' columns in the MFMA accumulator layout
     {
         uint16_t *vst = reinterpret_cast<uint16_t *>(sm.a16);
 #pragma unroll
@@ -256,7 +337,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     }
     __syncthreads();
     // V in the accumulator layout of this wave's U~ blocks (rows 16 i + 4 lg + e,
-    // column 32 w + 16 b + l16)
+    // column 32 w + 16 b + l16); the Gram phase overwrites the staging tile
+    // after the barrier that follows
     uint2 vz[2][4];
     {
         const uint16_t *vst = reinterpret_cast<const uint16_t *>(sm.a16);
@@ -266,57 +348,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             for (int i = 0; i < 4; ++i)
                 vz[b][i] = *reinterpret_cast<const uint2 *>(&vst[(32 * w + 16 * b + l16) * VTP + 16 * i + 4 * lg]);
     }
-    // Diag(f) Km^T: this thread's channels 8 cg + e, rows 4 rg .. 4 rg + 3,
-    // kept in registers until the tile it goes to is free
-    half4 kmT[8];
-    {
-        float kv[4][8], qv[4][8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            unpack8(rk[u], kv[u]);
-            unpack8(rq[u], qv[u]);
-        }
-        half8 kpr[4], qpr[4], kmr[4];
-        floatx4 gs[4][2];  // the four waves' channel sums for channels 8 cg ..
-#pragma unroll
-        for (int wi = 0; wi < 4; ++wi)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) gs[wi][hh] = *reinterpret_cast<const floatx4 *>(&sm.gsum[wi][8 * cg + 4 * hh]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int ch = 8 * cg + e;
-            const float s0w = gs[0][e >> 2][e & 3], s1w = gs[1][e >> 2][e & 3], s2w = gs[2][e >> 2][e & 3],
-                        s3w = gs[3][e >> 2][e & 3];
-            const float gm = s0w + s1w;                 // G at token 31 (end of wave 1's rows)
-            const float gcl = gm + s2w + s3w;           // G at token 63
-            float pre = ex[e] - gm;
-            if (w >= 1) pre += s0w;
-            if (w >= 2) pre += s1w;
-            if (w >= 3) pre += s2w;
-            // row factor of M' and N: exp(G_C - G_m)
-            const float fe = fast_exp(gcl - gm);
-            if (rg == 0) {
-                sm.egm[ch] = fast_exp(gm);
-                reinterpret_cast<float *>(rec + R_FC)[ch] = fast_exp(gcl);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float f = fast_exp(pre + G[u][e]);  // exp(G - G_m)
-                const float fi = __builtin_amdgcn_rcpf(f);
-                kpr[u][e] = (_Float16)(kv[u][e] * f);
-                qpr[u][e] = (_Float16)(qv[u][e] * f);
-                kmr[u][e] = (_Float16)(kv[u][e] * fi);
-                kmT[e][u] = (_Float16)(kv[u][e] * fi * fe);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int r = 4 * rg + u;
-            *reinterpret_cast<half8 *>(&sm.kp[r * PK + 8 * cg]) = kpr[u];
-            *reinterpret_cast<half8 *>(&sm.qp[r * PK + 8 * cg]) = qpr[u];
-            *reinterpret_cast<half8 *>(&sm.km[r * PK + 8 * cg]) = kmr[u];
-        }
-    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the staging reads are done
     __syncthreads();
 
     // ---- Gram / query-key blocks: wave w takes the diagonal blocks (w, w) and
