@@ -148,6 +148,16 @@ def decode_leg(args, dev, stream):
     dms, dwall = time_launches(dstep, args.decode_steps, 20, stream)
     db = decode_alg_bytes(wd.N, wd.H, wd.K, wd.V)
     dach = db / (dms * 1e-3) / 1e9
+    # the same step on states kept in pool slots (slot n in place)
+    slots = torch.arange(wd.N, dtype=torch.int32, device=dev)
+
+    def dstep_paged():
+        xi = steps_in[ctr[0] % nin]
+        ctr[0] += 1
+        kda.decode_step_paged(xi["q"], xi["k"], xi["v"], xi["g"], xi["beta"], state, slots, slots,
+                              out=od)
+
+    pms, _ = time_launches(dstep_paged, args.decode_steps, 20, stream)
     return {
         "workload": DECODE, "value": wd.N / (dms * 1e-3), "unit": "tokens/s",
         "ms_per_step": dms, "steps": args.decode_steps,
@@ -155,6 +165,7 @@ def decode_leg(args, dev, stream):
                      "frac": dach / HBM_PEAK_GBS,
                      "traffic": measured_traffic(f"decode_step_kernel_{DECODE_TAG}"),
                      "kernel": "decode_step_kernel", "alg_bytes_per_launch": db},
+        "paged_ms_per_step": pms,
     }
 
 
@@ -233,6 +244,28 @@ def main():
 
     ms, wall = time_launches(step, args.steps, args.warmup, stream)
     ms_fused, _ = time_launches(step_fused, max(5, args.steps // 5), 2, stream) if nws else (ms, 0)
+
+    # the same step through the paged entry point, leaving a state snapshot
+    # every 512 tokens (prefix caching: one 6144-token page per sequence)
+    snap, page = 512, 6144
+    per_page = page // snap
+    pages = -(-w.T // page)
+    pool = torch.zeros(w.B * pages * per_page + w.B, w.H, w.K, w.V, device=dev)
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)
+    table = i32([[b * pages + j for j in range(pages)] for b in range(w.B)])
+    sT_slot = i32([w.B * pages * per_page + b for b in range(w.B)])
+    cu = i32([b * w.T for b in range(w.B + 1)])
+    flat = {key: x[key].reshape(w.B * w.T, *x[key].shape[2:]) for key in ("q", "k", "v", "g", "beta")}
+    o_flat = o.view(w.B * w.T, w.H, w.V)
+    nws_p = kda.workspace_bytes(w.B, w.B * w.T, w.H, w.K, w.V, w.chunk)
+
+    def step_snap():
+        kda.varlen_fwd_paged(flat["q"], flat["k"], flat["v"], flat["g"], flat["beta"], cu, pool,
+                             sT_slot=sT_slot, block_table=table, snap_tokens=snap,
+                             page_tokens=page, chunk=w.chunk, out=o_flat,
+                             workspace=ws if nws_p else None, two_pass=bool(nws_p))
+
+    ms_snap, _ = time_launches(step_snap, args.steps, 20, stream)
     tokens = w.B * w.T
     alg_b = prefill_alg_bytes(w.B, w.T, w.H, w.K, w.V, s0=w.s0_std is not None, sT=True)
     alg_f = prefill_alg_flops(w.B, w.T, w.H, w.K, w.V, w.chunk)
@@ -265,6 +298,8 @@ def main():
         "wall_s_timed_region": wall,
         "path": path,
         "fused_single_pass_ms_per_step": ms_fused,
+        "prefix_cache": {"ms_per_step_with_snapshots": ms_snap, "snap_tokens": snap,
+                         "page_tokens": page, "snapshots_per_call": w.B * w.H * (w.T // snap)},
     }
 
     # ---- decode leg

@@ -35,6 +35,7 @@
 //    diagonal inverses (I + A_ii)^-1 in fp32.
 // Two workgroup barriers per chunk separate these phases.
 #include "kda_mfma.hpp"
+#include "state_io.hpp"
 
 namespace kda {
 namespace {
@@ -300,7 +301,7 @@ template <typename TOut>
 __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ g,
-    const uint16_t *__restrict__ beta, const float *s0, TOut *__restrict__ o, float *sT,
+    const uint16_t *__restrict__ beta, StateIO io, TOut *__restrict__ o,
     const int32_t *__restrict__ cu, int fixedT, int N, int H, int totalT) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
@@ -325,14 +326,18 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
     // The two wave groups run separate loops with the same barrier sequence
     // (two before the loop, two per chunk), so their registers never overlap.
     if (state_wave) {
-        // S[cb] holds rows c = 16 cb + 4 lg + i, column 16 w + l16 of the tile
-        const size_t sbase = (size_t)unit * (KD * VD) + (size_t)vt * VT + 16 * w + l16;
+        // S[cb] holds rows c = 16 cb + 4 lg + i, column 16 w + l16 of the tile;
+        // element (c, column) of a state is at [c * VD + column]
+        const int col = vt * VT + 16 * w + l16;
+        const float *s0p = state_in(io, n, h, H, KD * VD);
+        SnapCursor snap;
+        snap.init(io, n);
         floatx4 S[8];
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                S[cb][i] = s0 ? s0[sbase + (size_t)(16 * cb + 4 * lg + i) * VD] : 0.f;
+                S[cb][i] = s0p ? s0p[(16 * cb + 4 * lg + i) * VD + col] : 0.f;
         _Float16 *st = sm.st[w];
         _Float16 *ut = sm.ut[w];
         __syncthreads();
@@ -412,13 +417,29 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[cb][i] *= f[i];
             }
+            // prefix snapshot when the state now covers a boundary
+            if (snap.due(c0 - bos + L)) {
+                float *sp = snap.dest(io, h, H, KD * VD);
+                snap.advance(io);
+                if (sp) {
+                    // one 16-byte store per row block: after the quad
+                    // transpose a lane holds row 4 lg + (lane & 3), columns
+                    // col - (lane & 3) .. +3
+#pragma unroll
+                    for (int cb = 0; cb < 8; ++cb) {
+                        const floatx4 t = quad_transpose(S[cb], lane);
+                        *reinterpret_cast<floatx4 *>(&sp[(16 * cb + 4 * lg + (lane & 3)) * VD + col - (lane & 3)]) = t;
+                    }
+                }
+            }
             __syncthreads();
         }
-        if (sT) {
+        float *sTp = state_out(io, n, h, H, KD * VD);
+        if (sTp) {
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * cb + 4 * lg + i) * VD] = S[cb][i];
+                for (int i = 0; i < 4; ++i) sTp[(16 * cb + 4 * lg + i) * VD + col] = S[cb][i];
         }
     } else {
         const int p = w - 4;
@@ -463,19 +484,19 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
 
 template <typename TOut>
 hipError_t launch_t(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                    const float *s0, void *o, float *sT, const int32_t *cu, int N, int fixedT,
-                    int totalT, int H, hipStream_t stream) {
+                    const StateIO &io, void *o, const int32_t *cu, int N, int fixedT, int totalT,
+                    int H, hipStream_t stream) {
     auto kern = chunk_mfma_kernel<TOut>;
     const size_t smem = sizeof(Smem);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(kern), (int)smem, lds_set);
     if (e != hipSuccess) return e;
     const int units = N * H;
     const int grid = ((units + 7) / 8) * 16;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), smem, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), static_cast<const uint16_t *>(g),
-                       static_cast<const uint16_t *>(beta), s0, static_cast<TOut *>(o), sT, cu,
+                       static_cast<const uint16_t *>(beta), io, static_cast<TOut *>(o), cu,
                        fixedT, N, H, totalT);
     return hipGetLastError();
 }
@@ -485,12 +506,12 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *g, 
 bool chunk_mfma_supported(int K, int V, int Cc) { return K == KD && V == VD && Cc == C; }
 
 hipError_t launch_chunk_mfma(const void *q, const void *k, const void *v, const void *g,
-                             const void *beta, const float *s0, void *o, float *sT,
-                             const int32_t *cu, int N, int fixedT, int totalT, int H,
-                             bool out_bf16, hipStream_t stream) {
+                             const void *beta, const StateIO &io, void *o, const int32_t *cu,
+                             int N, int fixedT, int totalT, int H, bool out_bf16,
+                             hipStream_t stream) {
     if (N == 0 || H == 0) return hipSuccess;
-    return out_bf16 ? launch_t<bf16_t>(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H, stream)
-                    : launch_t<float>(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H, stream);
+    return out_bf16 ? launch_t<bf16_t>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, stream)
+                    : launch_t<float>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, stream);
 }
 
 size_t chunk_mfma_smem_bytes() { return sizeof(Smem); }

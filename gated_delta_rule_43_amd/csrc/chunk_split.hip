@@ -32,6 +32,7 @@
 // Pass 3 (chunk_output_kernel): one workgroup per (chunk, head).
 // Intermediates live in the caller's workspace.
 #include "kda_mfma.hpp"
+#include "state_io.hpp"
 
 namespace kda {
 namespace {
@@ -61,7 +62,6 @@ constexpr size_t R_OH = 66048;    // fp16 O^ as accumulators [8 value tiles][4 r
 constexpr size_t R_QH = 82432;    // fp16 [64][128]  Q^ [r][c]
 constexpr size_t R_SP = 98816;    // fp16 S (chunk-start state) in B order [8 value tiles][4 k-steps]
 constexpr size_t REC = 131584;
-constexpr size_t OFFS_BYTES = 512;  // int32 chunk offsets, up to 127 sequences
 
 // Several products take an operand straight out of MFMA accumulators, where
 // lane l holds rows 4 (l >> 4) .. +3 of each 16-row block: the state S (in
@@ -76,44 +76,69 @@ __device__ __forceinline__ int kperm_pos(int q) {
     return 32 * (q >> 3) + 8 * (q & 3) + 4 * ((q >> 2) & 1);
 }
 
-// ---------------------------------------------------------------- offsets
-// offs[n] = first chunk of sequence n in the packed chunk list, clamped so that
-// the list never exceeds `cap` chunks (malformed offsets cannot overrun the
-// workspace).
-__global__ void chunk_offsets_kernel(const int32_t *cu, int fixedT, int N, int totalT, int cap,
-                                     int32_t *offs) {
-    if (threadIdx.x != 0) return;
-    int acc = 0;
-    offs[0] = 0;
-    for (int n = 0; n < N; ++n) {
-        int bos, eos;
-        seq_bounds(cu, n, fixedT, totalT, bos, eos);
-        acc += (eos - bos + C - 1) / C;
-        if (acc > cap) acc = cap;
-        offs[n + 1] = acc;
+// ---------------------------------------------------------------- chunk map
+// Fixed-length sequences own regular ranges of the chunk list (sequence n:
+// [n cps, (n + 1) cps)).  For packed sequences every wave derives the map from
+// cu itself: lane l counts the chunks of sequences l and l + 64, a wave-wide
+// inclusive scan turns the counts into each sequence's end chunk, and lookups
+// read one lane (the index is wave-uniform) or count lanes with a ballot.  End
+// chunks are clamped to cap, the list's capacity, so malformed offsets cannot
+// overrun the workspace.
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
     }
+    return x;
 }
 
-// Locating chunks: for N fixed-length sequences the chunk list is regular
-// (sequence n owns chunks [n cps, (n + 1) cps)) and no offset table is built;
-// packed sequences read the table chunk_offsets_kernel wrote.
 struct ChunkMap {
-    const int32_t *offs;  // nullptr for fixed-length sequences
-    int cps;              // chunks per sequence (fixed length)
-    __device__ __forceinline__ int first(int n) const { return offs ? offs[n] : n * cps; }
-    // sequence holding packed chunk gc (gc < first(N))
-    __device__ __forceinline__ int seq_of(int gc, int N) const {
-        if (!offs) return gc / cps;
-        int n = 0;
-        while (n + 1 < N && offs[n + 1] <= gc) ++n;
-        return n;
+    bool packed;
+    int cps;             // chunks per sequence (fixed length)
+    int N;
+    int end_lo, end_hi;  // end chunk of sequences lane and lane + 64 (packed)
+    __device__ __forceinline__ int first(int n) const {
+        if (!packed) return n * cps;
+        if (n <= 0) return 0;
+        const int m = n - 1;  // first(n) = end of sequence n - 1
+        return m < 64 ? __builtin_amdgcn_readlane(end_lo, m) : __builtin_amdgcn_readlane(end_hi, m - 64);
+    }
+    // sequence holding chunk gc (gc < first(N)): the number of sequences
+    // ending at or before it
+    __device__ __forceinline__ int seq_of(int gc) const {
+        if (!packed) return gc / cps;
+        const int lane = __lane_id();
+        return __popcll(__ballot(lane < N && end_lo <= gc)) +
+               __popcll(__ballot(lane + 64 < N && end_hi <= gc));
     }
 };
 
-__device__ __forceinline__ ChunkMap chunk_map(const int32_t *cu, int fixedT, const unsigned char *ws) {
+__device__ __forceinline__ ChunkMap chunk_map(const int32_t *cu, int fixedT, int N, int totalT,
+                                              int cap) {
     ChunkMap m;
-    m.offs = cu ? reinterpret_cast<const int32_t *>(ws) : nullptr;
+    m.packed = cu != nullptr;
     m.cps = (fixedT + C - 1) / C;
+    m.N = N;
+    m.end_lo = m.end_hi = 0;
+    if (m.packed) {
+        const int lane = __lane_id();
+        int c_lo = 0, c_hi = 0, bos, eos;
+        if (lane < N) {
+            seq_bounds(cu, lane, 0, totalT, bos, eos);
+            c_lo = (eos - bos + C - 1) / C;
+        }
+        if (lane + 64 < N) {
+            seq_bounds(cu, lane + 64, 0, totalT, bos, eos);
+            c_hi = (eos - bos + C - 1) / C;
+        }
+        const int s_lo = wave_incl_scan(c_lo, lane);
+        m.end_lo = min(s_lo, cap);
+        if (N > 64) {
+            const int s_hi = wave_incl_scan(c_hi, lane) + __builtin_amdgcn_readlane(s_lo, 63);
+            m.end_hi = min(s_hi, cap);
+        }
+    }
     return m;
 }
 
@@ -175,16 +200,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     int totalT, unsigned char *__restrict__ ws) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     PrepSmem &sm = *reinterpret_cast<PrepSmem *>(smem_raw);
-    const ChunkMap cm = chunk_map(cu, fixedT, ws);
+    const ChunkMap cm = chunk_map(cu, fixedT, N, totalT, gridDim.x);
     const int gc = blockIdx.x, h = blockIdx.y;
     if (gc >= cm.first(N)) return;
-    const int n = cm.seq_of(gc, N);
+    const int n = cm.seq_of(gc);
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
     const int c0 = bos + (gc - cm.first(n)) * C;
     const int L = min(C, eos - c0);
     // records of one head are contiguous, in chunk order
-    unsigned char *rec = ws + OFFS_BYTES + ((size_t)h * gridDim.x + gc) * REC;
+    unsigned char *rec = ws + ((size_t)h * gridDim.x + gc) * REC;
 
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -701,12 +726,15 @@ __device__ __forceinline__ void mfma_step(floatx4 (&S)[RBW], const half8 (&a)[RB
 // (cyclic order from its own), reading M' fragments one k-step ahead and the
 // next chunk's first ones after this chunk's last; the exchanged fragments
 // have the own k-steps' products to arrive.
+// SNAP: the call writes prefix snapshots (a separate instantiation, so that
+// calls without them keep the check off the chain).
+template <bool SNAP>
 __global__ __launch_bounds__(64 * (STATE_WAVES + LOADER_WAVES)) void chunk_state_kernel(
-    const float *s0, float *sT, const int32_t *__restrict__ cu, int fixedT, int N, int H,
-    int totalT, int cap, unsigned char *__restrict__ ws) {
+    StateIO io, const int32_t *__restrict__ cu, int fixedT, int N, int H, int totalT, int cap,
+    unsigned char *__restrict__ ws) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     StateSmem &sm = *reinterpret_cast<StateSmem *>(smem_raw);
-    const ChunkMap cm = chunk_map(cu, fixedT, ws);
+    const ChunkMap cm = chunk_map(cu, fixedT, N, totalT, cap);
     const int b = blockIdx.x, slot = b >> 3;
     const int jt = slot % 8;                   // 16-column value tile
     const int unit = (slot / 8) * 8 + (b & 7);
@@ -714,7 +742,7 @@ __global__ __launch_bounds__(64 * (STATE_WAVES + LOADER_WAVES)) void chunk_state
     const int n = unit / H, h = unit - n * H;
     const int ch0 = cm.first(n);
     const int nchunks = cm.first(n + 1) - ch0;
-    unsigned char *recs = ws + OFFS_BYTES;
+    unsigned char *recs = ws;
     auto rec = [&](int ci) { return recs + ((size_t)h * cap + ch0 + ci) * REC; };
 
     const int lane = threadIdx.x & 63;
@@ -725,13 +753,21 @@ __global__ __launch_bounds__(64 * (STATE_WAVES + LOADER_WAVES)) void chunk_state
         const int sw = w;
         auto korder = [&](int t) { return (KSW * sw + t) & 3; };  // k-step order, own first
         const int jcol = 16 * jt + (lane & 15);                    // this lane's value column
-        const size_t sbase = (size_t)unit * (KD * VD) + jcol;
+        // element (row, jcol) of a state is at [row * VD + jcol]; this lane's
+        // rows are 16 (RBW sw + r) + 4 lg + i
+        auto elem = [&](int r, int i) { return (16 * (RBW * sw + r) + 4 * lg + i) * VD + jcol; };
+        const float *s0p = state_in(io, n, h, H, KD * VD);
+        int bos, eos;
+        seq_bounds(cu, n, fixedT, totalT, bos, eos);
+        const int len = eos - bos;
+        SnapCursor snap;
+        if (SNAP) snap.init(io, n);
         floatx4 S[RBW];  // rows 16 (RBW sw + r) + 4 lg + i
-        if (s0) {
+        if (s0p) {
 #pragma unroll
             for (int r = 0; r < RBW; ++r)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[r][i] = s0[sbase + (size_t)(16 * (RBW * sw + r) + 4 * lg + i) * VD];
+                for (int i = 0; i < 4; ++i) S[r][i] = s0p[elem(r, i)];
         } else {
 #pragma unroll
             for (int r = 0; r < RBW; ++r) S[r] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -783,12 +819,29 @@ __global__ __launch_bounds__(64 * (STATE_WAVES + LOADER_WAVES)) void chunk_state
             read_m(a, nx, sw, korder(0), lane);
             read_nf(nv, fv, nx, sw, lane);
             mfma_step(S, bq, bk[3]);
+            // prefix snapshot when the state now covers a boundary
+            if (SNAP && snap.due(min(C * (ci + 1), len))) {
+                float *sp = snap.dest(io, h, H, KD * VD);
+                snap.advance(io);
+                if (sp) {
+                    // one 16-byte store per row block: after the quad
+                    // transpose a lane holds row 4 lg + (lane & 3), columns
+                    // 4 ((lane & 15) >> 2) .. +3 of the tile
+#pragma unroll
+                    for (int r = 0; r < RBW; ++r) {
+                        const floatx4 t = quad_transpose(S[r], lane);
+                        *reinterpret_cast<floatx4 *>(&sp[(16 * (RBW * sw + r) + 4 * lg + (lane & 3)) * VD +
+                                                          16 * jt + 4 * ((lane & 15) >> 2)]) = t;
+                    }
+                }
+            }
         }
-        if (sT) {
+        float *sTp = state_out(io, n, h, H, KD * VD);
+        if (sTp) {
 #pragma unroll
             for (int r = 0; r < RBW; ++r)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sT[sbase + (size_t)(16 * (RBW * sw + r) + 4 * lg + i) * VD] = S[r][i];
+                for (int i = 0; i < 4; ++i) sTp[elem(r, i)] = S[r][i];
         }
     } else {
         // Segments per loader wave: the first SEGS % LOADER_WAVES waves take one more.
@@ -802,15 +855,17 @@ __global__ __launch_bounds__(64 * (STATE_WAVES + LOADER_WAVES)) void chunk_state
     }
 }
 
-hipError_t launch_state(const float *s0, float *sT, const int32_t *cu, int N, int fixedT,
-                        int totalT, int H, int cap, unsigned char *ws, hipStream_t stream) {
+hipError_t launch_state(const StateIO &io, const int32_t *cu, int N, int fixedT, int totalT,
+                        int H, int cap, unsigned char *ws, hipStream_t stream) {
     constexpr int smem = (int)sizeof(StateSmem);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(chunk_state_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    auto kern = io.snap ? chunk_state_kernel<true> : chunk_state_kernel<false>;
+    static std::atomic<uint64_t> lds_set[2];
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(kern), smem,
+                                      lds_set[io.snap ? 1 : 0]);
     if (e != hipSuccess) return e;
     const int groups = (N * H + 7) / 8;
-    hipLaunchKernelGGL(chunk_state_kernel, dim3(groups * 8 * 8), dim3(64 * (STATE_WAVES + LOADER_WAVES)), smem,
-                       stream, s0, sT, cu, fixedT, N, H, totalT, cap, ws);
+    hipLaunchKernelGGL(kern, dim3(groups * 8 * 8), dim3(64 * (STATE_WAVES + LOADER_WAVES)), smem,
+                       stream, io, cu, fixedT, N, H, totalT, cap, ws);
     return hipGetLastError();
 }
 
@@ -835,15 +890,15 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(TOut *__restrict__ o,
                                                            const int32_t *__restrict__ cu,
                                                            int fixedT, int N, int H, int totalT,
                                                            const unsigned char *__restrict__ ws) {
-    const ChunkMap cm = chunk_map(cu, fixedT, ws);
+    const ChunkMap cm = chunk_map(cu, fixedT, N, totalT, gridDim.x);
     const int gc = blockIdx.x, h = blockIdx.y;
     if (gc >= cm.first(N)) return;
-    const int n = cm.seq_of(gc, N);
+    const int n = cm.seq_of(gc);
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
     const int c0 = bos + (gc - cm.first(n)) * C;
     const int L = min(C, eos - c0);
-    const unsigned char *rec = ws + OFFS_BYTES + ((size_t)h * gridDim.x + gc) * REC;
+    const unsigned char *rec = ws + ((size_t)h * gridDim.x + gc) * REC;
 
     const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -905,26 +960,21 @@ bool chunk_split_recommended(int N, int totalT, int H, int K, int V, int Cc) {
 }
 
 size_t chunk_split_workspace_bytes(int N, int totalT, int H) {
-    return OFFS_BYTES + (size_t)max_chunks(N, totalT, 0, true) * H * REC;
+    return (size_t)max_chunks(N, totalT, 0, true) * H * REC;
 }
 
 hipError_t launch_chunk_split(const void *q, const void *k, const void *v, const void *g,
-                              const void *beta, const float *s0, void *o, float *sT,
-                              const int32_t *cu, int N, int fixedT, int totalT, int H,
-                              bool out_bf16, void *workspace, hipStream_t stream) {
+                              const void *beta, const StateIO &io, void *o, const int32_t *cu,
+                              int N, int fixedT, int totalT, int H, bool out_bf16,
+                              void *workspace, hipStream_t stream) {
     if (N == 0 || H == 0) return hipSuccess;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     const int cap = max_chunks(N, totalT, fixedT, cu != nullptr);
     hipError_t e;
-    if (cu) {
-        hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, stream, cu, fixedT, N,
-                           totalT, cap, reinterpret_cast<int32_t *>(ws));
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     if (cap > 0) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(chunk_prep_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PrepSmem));
+        static std::atomic<uint64_t> lds_set{0};
+        e = ensure_dynamic_lds(reinterpret_cast<const void *>(chunk_prep_kernel),
+                               (int)sizeof(PrepSmem), lds_set);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(chunk_prep_kernel, dim3(cap, H), dim3(256), sizeof(PrepSmem), stream,
                            static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
@@ -933,7 +983,7 @@ hipError_t launch_chunk_split(const void *q, const void *k, const void *v, const
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    e = launch_state(s0, sT, cu, N, fixedT, totalT, H, cap, ws, stream);
+    e = launch_state(io, cu, N, fixedT, totalT, H, cap, ws, stream);
     if (e != hipSuccess || cap == 0) return e;
     if (out_bf16)
         hipLaunchKernelGGL(chunk_output_kernel<bf16_t>, dim3(cap, H), dim3(256), 0, stream,

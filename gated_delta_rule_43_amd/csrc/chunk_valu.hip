@@ -22,6 +22,7 @@
 // stays in LDS for the whole sequence.  Columns of the state evolve
 // independently, so V-tiles need no communication.
 #include "kda_common.hpp"
+#include "state_io.hpp"
 
 namespace kda {
 
@@ -34,9 +35,8 @@ struct ValuSmem {
 template <int K, int V, int C, int VT, int NT, typename TIn, typename TOut>
 __global__ __launch_bounds__(NT) void chunk_valu_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
-    const TIn *__restrict__ g, const TIn *__restrict__ beta, const float *__restrict__ s0,
-    TOut *__restrict__ o, float *__restrict__ sT, const int32_t *__restrict__ cu, int fixedT,
-    int H, int totalT) {
+    const TIn *__restrict__ g, const TIn *__restrict__ beta, StateIO io,
+    TOut *__restrict__ o, const int32_t *__restrict__ cu, int fixedT, int H, int totalT) {
     extern __shared__ float smem[];
     float *sQ = smem;            // [C][K]
     float *sK = sQ + C * K;      // [C][K]
@@ -52,11 +52,14 @@ __global__ __launch_bounds__(NT) void chunk_valu_kernel(
     const int vt = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
-    const size_t sbase = ((size_t)n * H + h) * (size_t)(K * V) + (size_t)vt * VT;
+    // element (r, c) of this tile of a state is at [r * V + vt * VT + c]
+    const float *s0p = state_in(io, n, h, H, K * V);
+    SnapCursor snap;
+    snap.init(io, n);
 
     for (int i = t; i < K * VT; i += NT) {
         const int r = i / VT, c = i % VT;
-        sS[i] = s0 ? s0[sbase + (size_t)r * V + c] : 0.f;
+        sS[i] = s0p ? s0p[r * V + vt * VT + c] : 0.f;
     }
 
     for (int c0 = bos; c0 < eos; c0 += C) {
@@ -140,60 +143,69 @@ __global__ __launch_bounds__(NT) void chunk_valu_kernel(
             for (int s = 0; s < L; ++s) acc += sK[s * K + c] * fast_exp(gl - sG[s * K + c]) * sU[s * VT + j];
             sS[i] = acc;
         }
+        // prefix snapshot when the state now covers a boundary (each thread
+        // copies the elements it has just advanced)
+        if (snap.due(c0 - bos + L)) {
+            float *sp = snap.dest(io, h, H, K * V);
+            snap.advance(io);
+            if (sp) {
+                for (int i = t; i < K * VT; i += NT) sp[(i / VT) * V + vt * VT + i % VT] = sS[i];
+            }
+        }
     }
     __syncthreads();
-    if (sT) {
+    float *sTp = state_out(io, n, h, H, K * V);
+    if (sTp) {
         for (int i = t; i < K * VT; i += NT) {
             const int r = i / VT, c = i % VT;
-            sT[sbase + (size_t)r * V + c] = sS[i];
+            sTp[r * V + vt * VT + c] = sS[i];
         }
     }
 }
 
 template <int K, int V, int C, int VT, typename TIn, typename TOut>
 static hipError_t launch_valu_t(const void *q, const void *k, const void *v, const void *g,
-                                const void *beta, const float *s0, void *o, float *sT,
-                                const int32_t *cu, int N, int fixedT, int totalT, int H,
-                                hipStream_t stream) {
+                                const void *beta, const StateIO &io, void *o, const int32_t *cu,
+                                int N, int fixedT, int totalT, int H, hipStream_t stream) {
     constexpr int NT = 256;
     using SM = ValuSmem<K, V, C, VT, NT>;
     auto kern = chunk_valu_kernel<K, V, C, VT, NT, TIn, TOut>;
     if (SM::bytes > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(SM::bytes));
+        static std::atomic<uint64_t> lds_set{0};
+        hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(kern),
+                                          static_cast<int>(SM::bytes), lds_set);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(V / VT, H, N), dim3(NT), SM::bytes, stream,
                        static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                        static_cast<const TIn *>(v), static_cast<const TIn *>(g),
-                       static_cast<const TIn *>(beta), s0, static_cast<TOut *>(o), sT, cu,
-                       fixedT, H, totalT);
+                       static_cast<const TIn *>(beta), io, static_cast<TOut *>(o), cu, fixedT,
+                       H, totalT);
     return hipGetLastError();
 }
 
 template <int K, int V, int C, int VT>
 static hipError_t launch_valu_kvc(const void *q, const void *k, const void *v, const void *g,
-                                  const void *beta, const float *s0, void *o, float *sT,
-                                  const int32_t *cu, int N, int fixedT, int totalT, int H,
-                                  bool in_bf16, bool out_bf16, hipStream_t stream) {
+                                  const void *beta, const StateIO &io, void *o, const int32_t *cu,
+                                  int N, int fixedT, int totalT, int H, bool in_bf16,
+                                  bool out_bf16, hipStream_t stream) {
     if (in_bf16)
-        return out_bf16 ? launch_valu_t<K, V, C, VT, bf16_t, bf16_t>(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H, stream)
-                        : launch_valu_t<K, V, C, VT, bf16_t, float>(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H, stream);
-    return out_bf16 ? launch_valu_t<K, V, C, VT, float, bf16_t>(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H, stream)
-                    : launch_valu_t<K, V, C, VT, float, float>(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H, stream);
+        return out_bf16 ? launch_valu_t<K, V, C, VT, bf16_t, bf16_t>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, stream)
+                        : launch_valu_t<K, V, C, VT, bf16_t, float>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, stream);
+    return out_bf16 ? launch_valu_t<K, V, C, VT, float, bf16_t>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, stream)
+                    : launch_valu_t<K, V, C, VT, float, float>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, stream);
 }
 
 // Internal launcher.  cu == nullptr means fixed-length sequences of fixedT tokens.
 hipError_t launch_chunk_valu(const void *q, const void *k, const void *v, const void *g,
-                             const void *beta, const float *s0, void *o, float *sT,
-                             const int32_t *cu, int N, int fixedT, int totalT, int H, int K,
-                             int V, int C, bool in_bf16, bool out_bf16, hipStream_t stream) {
+                             const void *beta, const StateIO &io, void *o, const int32_t *cu,
+                             int N, int fixedT, int totalT, int H, int K, int V, int C,
+                             bool in_bf16, bool out_bf16, hipStream_t stream) {
     if (N == 0 || H == 0) return hipSuccess;
     if (K == 32 && V == 32 && C == 16)
-        return launch_valu_kvc<32, 32, 16, 32>(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H, in_bf16, out_bf16, stream);
+        return launch_valu_kvc<32, 32, 16, 32>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, in_bf16, out_bf16, stream);
     if (K == 128 && V == 128 && C == 64)
-        return launch_valu_kvc<128, 128, 64, 16>(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H, in_bf16, out_bf16, stream);
+        return launch_valu_kvc<128, 128, 64, 16>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, in_bf16, out_bf16, stream);
     return hipErrorInvalidValue;
 }
 

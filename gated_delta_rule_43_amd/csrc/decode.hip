@@ -24,11 +24,14 @@
 
 namespace kda {
 
-template <int K, int V, int NT, typename TIn, typename TOut>
+// PAGED: the states live in pool slots (slot_in / slot_out); otherwise the
+// unit's own entry of a dense [N, H, K, V] array is updated in place.
+template <int K, int V, int NT, typename TIn, typename TOut, bool PAGED>
 __global__ __launch_bounds__(NT) void decode_step_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const TIn *__restrict__ g, const TIn *__restrict__ beta, float *__restrict__ state,
-    TOut *__restrict__ o) {
+    const int32_t *__restrict__ slot_in, const int32_t *__restrict__ slot_out, int pool_slots,
+    int H, TOut *__restrict__ o) {
     constexpr int CG = V / 4;    // column groups of four floats
     constexpr int RG = NT / CG;  // row groups
     constexpr int RPT = K / RG;  // rows per thread
@@ -45,12 +48,32 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(
     const int cg = t % CG, rg = t / CG;
     const int lane = t & 63, w = t >> 6;
 
-    float4 *S = reinterpret_cast<float4 *>(state + unit * (size_t)(K * V));
+    // The state is read from Sin and written to Sout: the unit's own entry of
+    // a dense [N, H, K, V] array, or slots slot_in[n] / slot_out[n] of a pool
+    // (equal slots update in place; an input slot outside the pool reads as
+    // zeros, an output slot outside it is not written).
+    const float4 *Sin = reinterpret_cast<const float4 *>(state + unit * (size_t)(K * V));
+    float4 *Sout = reinterpret_cast<float4 *>(state + unit * (size_t)(K * V));
+    if constexpr (PAGED) {
+        const int n = (int)(unit / H), h = (int)(unit % H);
+        const int si = slot_in[n], so = slot_out[n];
+        Sin = si >= 0 && si < pool_slots
+                  ? reinterpret_cast<const float4 *>(state + ((size_t)si * H + h) * (K * V))
+                  : nullptr;
+        Sout = so >= 0 && so < pool_slots
+                   ? reinterpret_cast<float4 *>(state + ((size_t)so * H + h) * (K * V))
+                   : nullptr;
+    }
 
     // Issue the state loads first; the small per-head vectors follow.
     float4 s[RPT];
+    if (!PAGED || Sin) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) s[i] = S[(rg + i * RG) * CG + cg];
+        for (int i = 0; i < RPT; ++i) s[i] = Sin[(rg + i * RG) * CG + cg];
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 
     for (int c = t; c < K; c += NT) {
         sq[c] = to_f32(q[unit * K + c]);
@@ -104,12 +127,14 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(
     u.w = b * (to_f32(vp[3]) - RK.w);
 
     typedef float f4v __attribute__((ext_vector_type(4)));
+    if (!PAGED || Sout) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg + i * RG;
-        const float kr = sk[r];
-        const f4v x = {s[i].x + kr * u.x, s[i].y + kr * u.y, s[i].z + kr * u.z, s[i].w + kr * u.w};
-        __builtin_nontemporal_store(x, reinterpret_cast<f4v *>(&S[r * CG + cg]));
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + i * RG;
+            const float kr = sk[r];
+            const f4v x = {s[i].x + kr * u.x, s[i].y + kr * u.y, s[i].z + kr * u.z, s[i].w + kr * u.w};
+            __builtin_nontemporal_store(x, reinterpret_cast<f4v *>(&Sout[r * CG + cg]));
+        }
     }
     if (rg == 0) {
         const float kq = skq;
@@ -121,39 +146,58 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(
     }
 }
 
+// Slot arrays null: dense states [N, H, K, V] updated in place.
+struct DecodeStates {
+    float *state;
+    const int32_t *slot_in, *slot_out;
+    int pool_slots;
+};
+
 template <int K, int V, int NT, typename TIn, typename TOut>
 static hipError_t launch_decode_t(const void *q, const void *k, const void *v, const void *g,
-                                  const void *beta, float *state, void *o, int units,
-                                  hipStream_t stream) {
-    hipLaunchKernelGGL((decode_step_kernel<K, V, NT, TIn, TOut>), dim3(units), dim3(NT), 0,
-                       stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                       static_cast<const TIn *>(v), static_cast<const TIn *>(g),
-                       static_cast<const TIn *>(beta), state, static_cast<TOut *>(o));
+                                  const void *beta, const DecodeStates &st, void *o, int units,
+                                  int H, hipStream_t stream) {
+    if (st.slot_in)
+        hipLaunchKernelGGL((decode_step_kernel<K, V, NT, TIn, TOut, true>), dim3(units), dim3(NT),
+                           0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                           static_cast<const TIn *>(v), static_cast<const TIn *>(g),
+                           static_cast<const TIn *>(beta), st.state, st.slot_in, st.slot_out,
+                           st.pool_slots, H, static_cast<TOut *>(o));
+    else
+        hipLaunchKernelGGL((decode_step_kernel<K, V, NT, TIn, TOut, false>), dim3(units), dim3(NT),
+                           0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                           static_cast<const TIn *>(v), static_cast<const TIn *>(g),
+                           static_cast<const TIn *>(beta), st.state, nullptr, nullptr, 0, H,
+                           static_cast<TOut *>(o));
     return hipGetLastError();
 }
 
 template <int K, int V, int NT>
 static hipError_t launch_decode_kv(const void *q, const void *k, const void *v, const void *g,
-                                   const void *beta, float *state, void *o, int units,
-                                   bool in_bf16, bool out_bf16, hipStream_t stream) {
+                                   const void *beta, const DecodeStates &st, void *o, int units,
+                                   int H, bool in_bf16, bool out_bf16, hipStream_t stream) {
     if (in_bf16) {
-        return out_bf16 ? launch_decode_t<K, V, NT, bf16_t, bf16_t>(q, k, v, g, beta, state, o, units, stream)
-                        : launch_decode_t<K, V, NT, bf16_t, float>(q, k, v, g, beta, state, o, units, stream);
+        return out_bf16 ? launch_decode_t<K, V, NT, bf16_t, bf16_t>(q, k, v, g, beta, st, o, units, H, stream)
+                        : launch_decode_t<K, V, NT, bf16_t, float>(q, k, v, g, beta, st, o, units, H, stream);
     }
-    return out_bf16 ? launch_decode_t<K, V, NT, float, bf16_t>(q, k, v, g, beta, state, o, units, stream)
-                    : launch_decode_t<K, V, NT, float, float>(q, k, v, g, beta, state, o, units, stream);
+    return out_bf16 ? launch_decode_t<K, V, NT, float, bf16_t>(q, k, v, g, beta, st, o, units, H, stream)
+                    : launch_decode_t<K, V, NT, float, float>(q, k, v, g, beta, st, o, units, H, stream);
 }
 
-// Internal launcher: shapes were validated by the caller.
+// Internal launcher: shapes were validated by the caller.  slot_in / slot_out
+// null: state is a dense [N, H, K, V] array updated in place; else state is a
+// pool of pool_slots slots.
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *g,
-                         const void *beta, float *state, void *o, int N, int H, int K, int V,
-                         bool in_bf16, bool out_bf16, hipStream_t stream) {
+                         const void *beta, float *state, const int32_t *slot_in,
+                         const int32_t *slot_out, int pool_slots, void *o, int N, int H, int K,
+                         int V, bool in_bf16, bool out_bf16, hipStream_t stream) {
     const int units = N * H;
     if (units == 0) return hipSuccess;
+    const DecodeStates st{state, slot_in, slot_out, pool_slots};
     if (K == 128 && V == 128)
-        return launch_decode_kv<128, 128, 256>(q, k, v, g, beta, state, o, units, in_bf16, out_bf16, stream);
+        return launch_decode_kv<128, 128, 256>(q, k, v, g, beta, st, o, units, H, in_bf16, out_bf16, stream);
     if (K == 32 && V == 32)
-        return launch_decode_kv<32, 32, 64>(q, k, v, g, beta, state, o, units, in_bf16, out_bf16, stream);
+        return launch_decode_kv<32, 32, 64>(q, k, v, g, beta, st, o, units, H, in_bf16, out_bf16, stream);
     return hipErrorInvalidValue;
 }
 

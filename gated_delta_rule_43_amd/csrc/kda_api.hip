@@ -9,27 +9,29 @@
 #include <cstdint>
 
 #include "../../include/kda.h"
+#include "state_io.hpp"
 
 namespace kda {
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *g,
-                         const void *beta, float *state, void *o, int N, int H, int K, int V,
-                         bool in_bf16, bool out_bf16, hipStream_t stream);
+                         const void *beta, float *state, const int32_t *slot_in,
+                         const int32_t *slot_out, int pool_slots, void *o, int N, int H, int K,
+                         int V, bool in_bf16, bool out_bf16, hipStream_t stream);
 hipError_t launch_chunk_valu(const void *q, const void *k, const void *v, const void *g,
-                             const void *beta, const float *s0, void *o, float *sT,
-                             const int32_t *cu, int N, int fixedT, int totalT, int H, int K,
-                             int V, int C, bool in_bf16, bool out_bf16, hipStream_t stream);
+                             const void *beta, const StateIO &io, void *o, const int32_t *cu,
+                             int N, int fixedT, int totalT, int H, int K, int V, int C,
+                             bool in_bf16, bool out_bf16, hipStream_t stream);
 hipError_t launch_chunk_mfma(const void *q, const void *k, const void *v, const void *g,
-                             const void *beta, const float *s0, void *o, float *sT,
-                             const int32_t *cu, int N, int fixedT, int totalT, int H,
-                             bool out_bf16, hipStream_t stream);
+                             const void *beta, const StateIO &io, void *o, const int32_t *cu,
+                             int N, int fixedT, int totalT, int H, bool out_bf16,
+                             hipStream_t stream);
 bool chunk_mfma_supported(int K, int V, int C);
 bool chunk_split_supported(int N, int H, int K, int V, int C);
 bool chunk_split_recommended(int N, int totalT, int H, int K, int V, int C);
 size_t chunk_split_workspace_bytes(int N, int totalT, int H);
 hipError_t launch_chunk_split(const void *q, const void *k, const void *v, const void *g,
-                              const void *beta, const float *s0, void *o, float *sT,
-                              const int32_t *cu, int N, int fixedT, int totalT, int H,
-                              bool out_bf16, void *workspace, hipStream_t stream);
+                              const void *beta, const StateIO &io, void *o, const int32_t *cu,
+                              int N, int fixedT, int totalT, int H, bool out_bf16,
+                              void *workspace, hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -74,7 +76,7 @@ kda_status_t check_workspace(const void *workspace, size_t workspace_bytes, size
 }
 
 kda_status_t run_fwd(const void *q, const void *k, const void *v, const void *g,
-                     const void *beta, const float *s0, void *o, float *sT, const int32_t *cu,
+                     const void *beta, const kda::StateIO &io, void *o, const int32_t *cu,
                      int N, int fixedT, int totalT, int H, int K, int V, int chunk,
                      kda_dtype_t in_dtype, kda_dtype_t out_dtype, void *workspace,
                      bool two_pass, void *stream) {
@@ -82,22 +84,34 @@ kda_status_t run_fwd(const void *q, const void *k, const void *v, const void *g,
     const bool in_bf16 = in_dtype == KDA_BF16, out_bf16 = out_dtype == KDA_BF16;
     hipError_t e;
     if (in_bf16 && two_pass && kda::chunk_split_supported(N, H, K, V, chunk))
-        e = kda::launch_chunk_split(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H,
-                                    out_bf16, workspace, st);
+        e = kda::launch_chunk_split(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, out_bf16,
+                                    workspace, st);
     else if (in_bf16 && kda::chunk_mfma_supported(K, V, chunk))
-        e = kda::launch_chunk_mfma(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H,
-                                   out_bf16, st);
+        e = kda::launch_chunk_mfma(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, out_bf16,
+                                   st);
     else
-        e = kda::launch_chunk_valu(q, k, v, g, beta, s0, o, sT, cu, N, fixedT, totalT, H, K, V,
+        e = kda::launch_chunk_valu(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, K, V,
                                    chunk, in_bf16, out_bf16, st);
     return from_hip(e);
+}
+
+kda::StateIO dense_states(const float *s0, float *sT) {
+    kda::StateIO io;
+    io.s0 = s0;
+    io.sT = sT;
+    return io;
+}
+
+// A pool of pool_slots slots of H K x V fp32 states must be addressable.
+bool pool_ok(int pool_slots, int H, int K, int V) {
+    return pool_slots >= 1 && (long long)pool_slots * H <= LLONG_MAX / 4 / ((long long)K * V);
 }
 
 }  // namespace
 
 extern "C" {
 
-int kda_version(void) { return 100; }
+int kda_version(void) { return 101; }
 
 const char *kda_status_str(kda_status_t s) {
     switch (s) {
@@ -140,8 +154,8 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
     if (s != KDA_OK) return s;
     if (B == 0) return KDA_OK;
     if (T == 0 && !sT) return KDA_OK;
-    return run_fwd(q, k, v, g, beta, s0, o, sT, nullptr, B, T, (int)total, H, K, V, chunk,
-                   in_dtype, out_dtype, workspace, two_pass, stream);
+    return run_fwd(q, k, v, g, beta, dense_states(s0, sT), o, nullptr, B, T, (int)total, H, K, V,
+                   chunk, in_dtype, out_dtype, workspace, two_pass, stream);
 }
 
 kda_status_t kda_varlen_fwd(const void *q, const void *k, const void *v, const void *g,
@@ -158,8 +172,50 @@ kda_status_t kda_varlen_fwd(const void *q, const void *k, const void *v, const v
                         kda_two_pass_workspace_bytes(N, total_T, H, K, V, chunk), two_pass);
     if (s != KDA_OK) return s;
     if (N == 0) return KDA_OK;
-    return run_fwd(q, k, v, g, beta, s0, o, sT, cu_seqlens, N, 0, total_T, H, K, V, chunk,
-                   in_dtype, out_dtype, workspace, two_pass, stream);
+    return run_fwd(q, k, v, g, beta, dense_states(s0, sT), o, cu_seqlens, N, 0, total_T, H, K, V,
+                   chunk, in_dtype, out_dtype, workspace, two_pass, stream);
+}
+
+kda_status_t kda_varlen_fwd_paged(const void *q, const void *k, const void *v, const void *g,
+                                  const void *beta, float *pool, int pool_slots,
+                                  const int32_t *s0_slot, const int32_t *sT_slot,
+                                  const int32_t *start_pos, const int32_t *block_table,
+                                  int table_stride, int snap_tokens, int page_tokens, void *o,
+                                  const int32_t *cu_seqlens, int N, int total_T, int H, int K,
+                                  int V, int chunk, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    kda_status_t s = validate_fwd(q, k, v, g, beta, o, N, total_T, H, K, V, chunk, in_dtype,
+                                  out_dtype);
+    if (s != KDA_OK) return s;
+    if (!pool) return KDA_ERR_NULL;
+    if (!pool_ok(pool_slots, H, K, V)) return KDA_ERR_SHAPE;
+    if (block_table &&
+        (table_stride < 1 || snap_tokens < 1 || snap_tokens % chunk != 0 || page_tokens < 1 ||
+         page_tokens % snap_tokens != 0))
+        return KDA_ERR_SHAPE;
+    if (N > 0 && !cu_seqlens) return KDA_ERR_NULL;
+    bool two_pass;
+    s = check_workspace(workspace, workspace_bytes,
+                        kda_two_pass_workspace_bytes(N, total_T, H, K, V, chunk), two_pass);
+    if (s != KDA_OK) return s;
+    if (N == 0) return KDA_OK;
+    kda::StateIO io;
+    io.s0 = s0_slot ? pool : nullptr;
+    io.s0_slot = s0_slot;
+    io.sT = sT_slot ? pool : nullptr;
+    io.sT_slot = sT_slot;
+    if (block_table) {
+        io.snap = pool;
+        io.block_table = block_table;
+        io.table_stride = table_stride;
+        io.snap_tokens = snap_tokens;
+        io.page_tokens = page_tokens;
+        io.snaps_per_page = page_tokens / snap_tokens;
+    }
+    io.start_pos = start_pos;
+    io.pool_slots = pool_slots;
+    return run_fwd(q, k, v, g, beta, io, o, cu_seqlens, N, 0, total_T, H, K, V, chunk, in_dtype,
+                   out_dtype, workspace, two_pass, stream);
 }
 
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g,
@@ -171,8 +227,25 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
     if (!((K == 128 && V == 128) || (K == 32 && V == 32))) return KDA_ERR_UNSUPPORTED;
     if (N == 0) return KDA_OK;
     if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
-    return from_hip(kda::launch_decode(q, k, v, g, beta, state, o, N, H, K, V,
-                                       in_dtype == KDA_BF16, out_dtype == KDA_BF16,
+    return from_hip(kda::launch_decode(q, k, v, g, beta, state, nullptr, nullptr, 0, o, N, H, K,
+                                       V, in_dtype == KDA_BF16, out_dtype == KDA_BF16,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_decode_step_paged(const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, float *pool, int pool_slots,
+                                   const int32_t *slot_in, const int32_t *slot_out, void *o,
+                                   int N, int H, int K, int V, kda_dtype_t in_dtype,
+                                   kda_dtype_t out_dtype, void *stream) {
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
+    if (N < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_SHAPE;
+    if (!fits(N, H, (long long)K * V)) return KDA_ERR_SHAPE;
+    if (!((K == 128 && V == 128) || (K == 32 && V == 32))) return KDA_ERR_UNSUPPORTED;
+    if (!pool_ok(pool_slots, H, K, V)) return KDA_ERR_SHAPE;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !pool || !slot_in || !slot_out || !o) return KDA_ERR_NULL;
+    return from_hip(kda::launch_decode(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o,
+                                       N, H, K, V, in_dtype == KDA_BF16, out_dtype == KDA_BF16,
                                        static_cast<hipStream_t>(stream)));
 }
 

@@ -13,7 +13,8 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "varlen_fwd", "decode_step", "workspace_bytes",
+__all__ = ["chunk_fwd", "varlen_fwd", "decode_step", "varlen_fwd_paged", "decode_step_paged",
+           "workspace_bytes",
            "two_pass_workspace_bytes", "library",
            "KdaError", "LIB_PATH", "F32", "BF16"]
 
@@ -47,6 +48,13 @@ def library():
     lib.kda_varlen_fwd.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_step.restype = i32
+    lib.kda_varlen_fwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                                         i32, i32, i32, vp, vp,
+                                         i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    lib.kda_varlen_fwd_paged.restype = i32
+    lib.kda_decode_step_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                          i32, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_step_paged.restype = i32
     lib.kda_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.kda_workspace_bytes.restype = sz
     lib.kda_two_pass_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -234,4 +242,87 @@ def decode_step(q, k, v, g, beta, state, out_dtype=torch.float32, out=None):
                                    _ptr(o), N, H, K, V, _dtype_code(dt), _dtype_code(o.dtype),
                                    _stream(q.device))
     _check("kda_decode_step", st)
+    return o
+
+
+def _slots(t, N, name):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.shape != (N,):
+        raise ValueError(f"{name} must be int32 [N]")
+    return t
+
+
+def _pool_check(pool, H, K, V):
+    if pool.dtype != torch.float32 or pool.dim() != 4 or tuple(pool.shape[1:]) != (H, K, V):
+        raise ValueError("pool must be float32 [slots, H, K, V]")
+    return pool.shape[0]
+
+
+def varlen_fwd_paged(q, k, v, g, beta, cu_seqlens, pool, s0_slot=None, sT_slot=None,
+                     start_pos=None, block_table=None, snap_tokens=512, page_tokens=6144,
+                     chunk=None, out_dtype=torch.float32, out=None, two_pass=None,
+                     workspace=None):
+    """kda_varlen_fwd_paged: packed sequences whose states live in a pool.
+
+    pool: float32 [slots, H, K, V]; s0_slot, sT_slot, start_pos: int32 [N] or None;
+    block_table: int32 [N, blocks] (physical page of each page_tokens block) or None
+    for no snapshots.  Returns o [total_T, H, V]; states and snapshots land in pool.
+    """
+    _need_gpu(q, k, v, g, beta, cu_seqlens, pool, s0_slot, sT_slot, start_pos, block_table, out)
+    total, H, K = q.shape
+    V = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    dt = q.dtype
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if any(x.dtype != dt for x in (k, v, g, beta)):
+        raise ValueError("q, k, v, g and beta must share one dtype")
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (total, H, V) or beta.shape != (total, H):
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    slots = _pool_check(pool, H, K, V)
+    for t, name in ((s0_slot, "s0_slot"), (sT_slot, "sT_slot"), (start_pos, "start_pos")):
+        _slots(t, N, name)
+    stride = 0
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != N:
+            raise ValueError("block_table must be int32 [N, blocks]")
+        stride = block_table.shape[1]
+    chunk = chunk or _default_chunk(K)
+    dev = q.device
+    o = out if out is not None else torch.empty((total, H, V), dtype=out_dtype, device=dev)
+    if o.shape != (total, H, V):
+        raise ValueError("out must be [total_T, H, V]")
+    ws, nws = _workspace(dev, N, total, H, K, V, chunk, two_pass, workspace)
+    st = library().kda_varlen_fwd_paged(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(pool), slots, _ptr(s0_slot),
+        _ptr(sT_slot), _ptr(start_pos), _ptr(block_table), stride, snap_tokens, page_tokens,
+        _ptr(o), _ptr(cu_seqlens), N, total, H, K, V, chunk, _dtype_code(dt),
+        _dtype_code(o.dtype), _ptr(ws), nws, _stream(dev))
+    _check("kda_varlen_fwd_paged", st)
+    return o
+
+
+def decode_step_paged(q, k, v, g, beta, pool, slot_in, slot_out, out_dtype=torch.float32,
+                      out=None):
+    """kda_decode_step_paged: one step for N sequences whose states live in a pool
+    (float32 [slots, H, K, V]); sequence n reads slot_in[n] and writes slot_out[n]
+    (int32 [N] each).  Returns o [N, H, V]."""
+    _need_gpu(q, k, v, g, beta, pool, slot_in, slot_out, out)
+    N, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    if any(x.dtype != dt for x in (k, v, g, beta)):
+        raise ValueError("q, k, v, g and beta must share one dtype")
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (N, H, V) or beta.shape != (N, H):
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    slots = _pool_check(pool, H, K, V)
+    _slots(slot_in, N, "slot_in")
+    _slots(slot_out, N, "slot_out")
+    o = out if out is not None else torch.empty((N, H, V), dtype=out_dtype, device=q.device)
+    st = library().kda_decode_step_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                         _ptr(pool), slots, _ptr(slot_in), _ptr(slot_out),
+                                         _ptr(o), N, H, K, V, _dtype_code(dt),
+                                         _dtype_code(o.dtype), _stream(q.device))
+    _check("kda_decode_step_paged", st)
     return o

@@ -129,6 +129,66 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
                              int V, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
                              void *stream);
 
+/*
+ * Paged states for prefix caching.  Section "Inference Serving" of the page
+ * above keeps KDA recurrent states in one paged pool shared with the
+ * attention KV cache, and lets a request hit a cached prefix at 512-token
+ * boundaries even inside 6144-token physical blocks.  Here a pool is a
+ * caller-owned fp32 array of pool_slots slots; slot s holds the H states
+ * [H, K, V] of one sequence at one point in time, at pool + s*H*K*V.
+ *
+ * kda_varlen_fwd_paged: kda_varlen_fwd with the states in a pool, and prefix
+ * snapshots.
+ *   s0_slot     : DEVICE int32 [N], slot of each sequence's initial state
+ *                 (< 0 or >= pool_slots: zeros), or NULL for all zeros.
+ *   sT_slot     : DEVICE int32 [N], slot receiving each final state (< 0 or
+ *                 >= pool_slots: not written), or NULL for none.
+ *                 sT_slot[n] == s0_slot[n] updates in place.
+ *   start_pos   : DEVICE int32 [N], absolute position of each sequence's first
+ *                 token in this call (its cached prefix length), or NULL for
+ *                 all 0.  Must be a multiple of chunk for snapshots to be
+ *                 written (boundaries off the chunk grid are skipped).
+ *   block_table : DEVICE int32 [N, table_stride], or NULL for no snapshots.
+ *                 Entry b is the physical page holding the sequence's
+ *                 absolute tokens [b*page_tokens, (b+1)*page_tokens), or < 0.
+ *   snap_tokens, page_tokens : boundary interval (a multiple of chunk; 512)
+ *                 and page size (a multiple of snap_tokens; 6144), so a page
+ *                 holds page_tokens/snap_tokens slots.
+ * For every boundary p = j*snap_tokens with start_pos[n] < p <=
+ * start_pos[n] + len_n, the state after the sequence's first p tokens is
+ * written to slot page*(page_tokens/snap_tokens) + ((p-1) % page_tokens) /
+ * snap_tokens, page = block_table[n*table_stride + (p-1)/page_tokens]; the
+ * boundary at a page's end belongs to that page.  Blocks at or past
+ * table_stride, negative pages and slots at or past pool_slots are skipped.
+ * Slots written by one call (final states and snapshots) must be distinct
+ * from each other and from every slot the call reads, except a sequence's
+ * own in-place sT_slot.  Everything else is as for kda_varlen_fwd (o,
+ * workspace and implementation choice, supported set, errors).
+ */
+kda_status_t kda_varlen_fwd_paged(const void *q, const void *k, const void *v, const void *g,
+                                  const void *beta, float *pool, int pool_slots,
+                                  const int32_t *s0_slot, const int32_t *sT_slot,
+                                  const int32_t *start_pos, const int32_t *block_table,
+                                  int table_stride, int snap_tokens, int page_tokens, void *o,
+                                  const int32_t *cu_seqlens, int N, int total_T, int H, int K,
+                                  int V, int chunk, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_decode_step_paged: kda_decode_step with the states in a pool.
+ * Sequence n reads its state from slot slot_in[n] (< 0 or >= pool_slots:
+ * zeros) and writes the new state to slot slot_out[n] (< 0 or >= pool_slots:
+ * not written); slot_in and slot_out are DEVICE int32 [N].  Equal slots
+ * update in place; different slots leave the old state in place, e.g. as the
+ * snapshot at a boundary, or to branch a sequence.  Output slots must be
+ * distinct from each other and from the input slots of other sequences.
+ */
+kda_status_t kda_decode_step_paged(const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, float *pool, int pool_slots,
+                                   const int32_t *slot_in, const int32_t *slot_out, void *o,
+                                   int N, int H, int K, int V, kda_dtype_t in_dtype,
+                                   kda_dtype_t out_dtype, void *stream);
+
 /* Workspace bytes for the recommended implementation of a forward call over
  * N sequences, total_T tokens: nonzero (the two-pass size) when the two-pass
  * path is supported and expected to be faster (bf16 inputs assumed; at most
@@ -138,7 +198,7 @@ size_t kda_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk);
 /* Workspace bytes that select the two-pass path whenever it is supported:
  * (K, V, chunk) = (128, 128, 64), 1 <= N <= 126; 0 when it is not.  The
  * two-pass path runs for bf16 inputs only; fp32 inputs ignore the workspace.
- * Size: 512 + ceil((total_T + 63 N) / 64) * H * 131584 bytes. */
+ * Size: ceil((total_T + 63 N) / 64) * H * 131584 bytes. */
 size_t kda_two_pass_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk);
 
 /* Static, human-readable name of a status code. */

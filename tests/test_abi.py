@@ -29,8 +29,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("kda_chunk_fwd", "kda_varlen_fwd", "kda_decode_step", "kda_workspace_bytes",
-              "kda_two_pass_workspace_bytes", "kda_status_str", "kda_version"):
+    for n in ("kda_chunk_fwd", "kda_varlen_fwd", "kda_decode_step", "kda_varlen_fwd_paged",
+              "kda_decode_step_paged", "kda_workspace_bytes", "kda_two_pass_workspace_bytes",
+              "kda_status_str", "kda_version"):
         assert n in names
 
 
@@ -44,13 +45,12 @@ def test_status_strings_and_version(lib):
         s = lib.kda_status_str(code).decode()
         assert s.startswith("KDA_")
     assert lib.kda_status_str(99).decode() == "KDA_ERR_UNKNOWN"
-    assert lib.kda_version() == 100
+    assert lib.kda_version() == 101
 
 
 def two_pass_size(N, total, H):
-    # offsets block, then one 131584-byte record per (chunk, head) for the
-    # packed-sequence chunk bound
-    return 512 + -(-(total + 63 * N) // 64) * H * 131584
+    # one 131584-byte record per (chunk, head) for the packed-sequence chunk bound
+    return -(-(total + 63 * N) // 64) * H * 131584
 
 
 def test_workspace_sizes(lib):
@@ -124,3 +124,43 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 4, 1, 32)
     with pytest.raises(ValueError):
         kda.chunk_fwd(x, x, x, x, torch.zeros(1, 4, 1))
+
+
+def paged_fwd(lib, *, pool=FAKE, slots=4, table=None, stride=0, snap=512, page=6144, N=2, T=10,
+              H=1, K=128, V=128, C=64, cu=FAKE, null=None):
+    ptrs = [FAKE] * 5
+    if null is not None:
+        ptrs[null] = None
+    return lib.kda_varlen_fwd_paged(*ptrs, pool, slots, None, None, None, table, stride, snap,
+                                    page, FAKE, cu, N, T, H, K, V, C, 1, 0, None, 0, None)
+
+
+def test_paged_fwd_argument_errors(lib):
+    assert paged_fwd(lib, pool=None) == 1                     # no pool
+    assert paged_fwd(lib, slots=0) == 2                       # empty pool
+    assert paged_fwd(lib, cu=None) == 1
+    assert paged_fwd(lib, K=96) == 4
+    for i in range(5):
+        assert paged_fwd(lib, null=i) == 1
+    # snapshot schedule: only checked when a block table is given
+    assert paged_fwd(lib, table=FAKE, stride=0) == 2
+    assert paged_fwd(lib, table=FAKE, stride=4, snap=100) == 2     # not a multiple of chunk
+    assert paged_fwd(lib, table=FAKE, stride=4, snap=0) == 2
+    assert paged_fwd(lib, table=FAKE, stride=4, page=1000) == 2    # not a multiple of snap
+    assert paged_fwd(lib, table=FAKE, stride=4, page=0) == 2
+
+
+def test_paged_decode_argument_errors(lib):
+    f = lib.kda_decode_step_paged
+
+    def call(null=None, slots=8, N=4, K=128):
+        ptrs = [FAKE] * 10   # q, k, v, g, beta, pool, (slots), slot_in, slot_out, o
+        if null is not None:
+            ptrs[null] = None
+        return f(*ptrs[:6], slots, *ptrs[6:9], N, 2, K, K, 1, 0, None)
+
+    assert call(K=64) == 4
+    assert call(slots=0) == 2
+    assert call(N=-1) == 2
+    for i in range(9):
+        assert call(null=i) == 1

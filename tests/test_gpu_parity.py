@@ -205,3 +205,24 @@ def test_decode_fp32_inputs_tight():
         torch.cuda.synchronize()
         assert rel_err(o, o_ref) <= TOL["f32"]
     assert rel_err(st, ref) <= TOL["f32"]
+
+
+def test_varlen_many_sequences_two_pass():
+    """More than 64 packed sequences (the two-pass chunk map covers sequences
+    l and l + 64 in lane l), empty ones at the lane edges, on the two-pass path."""
+    rng = np.random.default_rng(31)
+    lengths = rng.integers(1, 200, size=100)
+    lengths[[0, 63, 64, 65, 99]] = 0
+    print(f"[case] varlen two-pass N={len(lengths)} total={int(lengths.sum())}", flush=True)
+    d = inputs.draw_varlen(31, H=2, K=128, V=128, dtype="bf16", lengths=lengths, s0_std=0.1)
+    o_ref, s_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                     d["cu_seqlens"].numpy(), oracle.as_f64(d["s0"]))
+    x = to_gpu(d)
+    o, sT = kda.varlen_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"], x["s0"],
+                           two_pass=True)
+    torch.cuda.synchronize()
+    eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+    report("varlen_many_two_pass", o=eo, sT=es)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    for n in (0, 63, 64, 65, 99):
+        assert torch.equal(sT[n], x["s0"][n])
