@@ -158,6 +158,27 @@ def decode_leg(args, dev, stream):
                               out=od)
 
     pms, _ = time_launches(dstep_paged, args.decode_steps, 20, stream)
+
+    # draft verification: 4 tokens per sequence in one pass over each state
+    # (kda_decode_multi_paged), keeping the state after every draft token in
+    # its own slot, or only the last one, in place
+    td = 4
+    dd = inputs.draw_varlen(wd.seed + 1, H=wd.H, K=wd.K, V=wd.V, dtype=wd.dtype, lengths=[td] * wd.N)
+    sh = lambda t: t.to(dev).reshape(wd.N, td, *t.shape[1:])
+    dq, dk, dv, dg, dbt = (sh(dd[key]) for key in ("q", "k", "v", "g", "beta"))
+    mpool = torch.empty(wd.N * (1 + td), wd.H, wd.K, wd.V, device=dev)
+    mpool[:wd.N].copy_(state)
+    m_in = torch.arange(wd.N, dtype=torch.int32, device=dev)
+    keep_all = (wd.N + torch.arange(wd.N * td, dtype=torch.int32, device=dev)).reshape(wd.N, td)
+    keep_last = torch.full((wd.N, td), -1, dtype=torch.int32, device=dev)
+    keep_last[:, -1] = m_in
+    mo = torch.empty(wd.N, td, wd.H, wd.V, device=dev)
+
+    def verify(slots_out):
+        return lambda: kda.decode_multi_paged(dq, dk, dv, dg, dbt, mpool, m_in, slots_out, out=mo)
+
+    vms_all, _ = time_launches(verify(keep_all), args.decode_steps, 10, stream)
+    vms_last, _ = time_launches(verify(keep_last), args.decode_steps, 10, stream)
     return {
         "workload": DECODE, "value": wd.N / (dms * 1e-3), "unit": "tokens/s",
         "ms_per_step": dms, "steps": args.decode_steps,
@@ -166,6 +187,10 @@ def decode_leg(args, dev, stream):
                      "traffic": measured_traffic(f"decode_step_kernel_{DECODE_TAG}"),
                      "kernel": "decode_step_kernel", "alg_bytes_per_launch": db},
         "paged_ms_per_step": pms,
+        "draft_verify": {"draft_tokens": td, "ms_keep_every_state": vms_all,
+                         "ms_keep_last_state": vms_last,
+                         "tokens_per_s_keep_last": wd.N * td / (vms_last * 1e-3),
+                         "ms_same_tokens_as_single_steps": td * dms},
     }
 
 

@@ -24,29 +24,132 @@
 
 namespace kda {
 
-// PAGED: the states live in pool slots (slot_in / slot_out); otherwise the
-// unit's own entry of a dense [N, H, K, V] array is updated in place.
+// One workgroup of NT threads per (sequence, head): thread (cg, rg) keeps
+// rows rg, rg + RG, .. (RPT of them) of columns 4 cg .. 4 cg + 3 of the state.
+template <int K, int V, int NT>
+struct DecodeShape {
+    static constexpr int CG = V / 4;    // column groups of four floats
+    static constexpr int RG = NT / CG;  // row groups
+    static constexpr int RPT = K / RG;  // rows per thread
+    static constexpr int NW = NT / 64;  // wavefronts per workgroup
+    static_assert(V % 4 == 0 && CG <= 64 && 64 % CG == 0, "column groups must tile a wave");
+    static_assert(NT % CG == 0 && K % RG == 0, "rows must tile the workgroup");
+};
+
+template <int K, int V, int NT>
+struct DecodeLds {
+    float sq[K], sk[K], sa[K];
+    float4 red[DecodeShape<K, V, NT>::NW][DecodeShape<K, V, NT>::CG][2];
+    float skq;
+};
+
+// One token through the recurrence for the workgroup's (sequence, head):
+// scales this thread's rows s[0 .. RPT) by alpha in place, writes o (row group 0) and
+// returns u for its four columns; the new state is s + k_r u on row r.
+// q, k, g point at the token's [K] vectors, v at its [V] vector.  Leaves
+// lds.sk valid for the caller; callers that run another token first pass a
+// barrier (every thread is done reading lds).
+template <int K, int V, int NT, typename TIn, typename TOut>
+__device__ __forceinline__ float4 decode_token(float4 *s, const TIn *q, const TIn *k, const TIn *g,
+                                               const TIn *beta, const TIn *v, TOut *o,
+                                               DecodeLds<K, V, NT> &lds) {
+    using D = DecodeShape<K, V, NT>;
+    const int t = threadIdx.x;
+    const int cg = t % D::CG, rg = t / D::CG;
+    const int lane = t & 63, w = t >> 6;
+    for (int c = t; c < K; c += NT) {
+        lds.sq[c] = to_f32(q[c]);
+        lds.sk[c] = to_f32(k[c]);
+        lds.sa[c] = fast_exp(to_f32(g[c]));
+    }
+    __syncthreads();
+    if (w == 0) {
+        float p = 0.f;
+        for (int c = lane; c < K; c += 64) p += lds.sk[c] * lds.sq[c];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+        if (lane == 0) lds.skq = p;
+    }
+
+    float4 rk = make_float4(0.f, 0.f, 0.f, 0.f), rq = rk;
+#pragma unroll
+    for (int i = 0; i < D::RPT; ++i) {
+        const int r = rg + i * D::RG;
+        const float a = lds.sa[r], kr = lds.sk[r], qr = lds.sq[r];
+        s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
+        rk.x += kr * s[i].x; rk.y += kr * s[i].y; rk.z += kr * s[i].z; rk.w += kr * s[i].w;
+        rq.x += qr * s[i].x; rq.y += qr * s[i].y; rq.z += qr * s[i].z; rq.w += qr * s[i].w;
+    }
+    // Lanes of one wave holding the same columns differ by multiples of CG.
+#pragma unroll
+    for (int off = D::CG; off < 64; off <<= 1) {
+        rk.x += __shfl_xor(rk.x, off); rk.y += __shfl_xor(rk.y, off);
+        rk.z += __shfl_xor(rk.z, off); rk.w += __shfl_xor(rk.w, off);
+        rq.x += __shfl_xor(rq.x, off); rq.y += __shfl_xor(rq.y, off);
+        rq.z += __shfl_xor(rq.z, off); rq.w += __shfl_xor(rq.w, off);
+    }
+    if (lane < D::CG) {
+        lds.red[w][lane][0] = rk;
+        lds.red[w][lane][1] = rq;
+    }
+    __syncthreads();
+    float4 RK = lds.red[0][cg][0], RQ = lds.red[0][cg][1];
+#pragma unroll
+    for (int ww = 1; ww < D::NW; ++ww) {
+        const float4 a = lds.red[ww][cg][0], b = lds.red[ww][cg][1];
+        RK.x += a.x; RK.y += a.y; RK.z += a.z; RK.w += a.w;
+        RQ.x += b.x; RQ.y += b.y; RQ.z += b.z; RQ.w += b.w;
+    }
+    const float b = to_f32(beta[0]);
+    const TIn *vp = v + 4 * cg;
+    float4 u;
+    u.x = b * (to_f32(vp[0]) - RK.x);
+    u.y = b * (to_f32(vp[1]) - RK.y);
+    u.z = b * (to_f32(vp[2]) - RK.z);
+    u.w = b * (to_f32(vp[3]) - RK.w);
+    if (rg == 0) {
+        const float kq = lds.skq;
+        TOut *op = o + 4 * cg;
+        op[0] = from_f32<TOut>(RQ.x + kq * u.x);
+        op[1] = from_f32<TOut>(RQ.y + kq * u.y);
+        op[2] = from_f32<TOut>(RQ.z + kq * u.z);
+        op[3] = from_f32<TOut>(RQ.w + kq * u.w);
+    }
+    return u;
+}
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// Writes this thread's rows of the new state s + k_r u to S (non-temporal).
+template <int K, int V, int NT>
+__device__ __forceinline__ void store_state(float4 *S, const float4 *s, const float4 &u,
+                                            const float *sk) {
+    using D = DecodeShape<K, V, NT>;
+    const int cg = threadIdx.x % D::CG, rg = threadIdx.x / D::CG;
+#pragma unroll
+    for (int i = 0; i < D::RPT; ++i) {
+        const int r = rg + i * D::RG;
+        const float kr = sk[r];
+        const f4v x = {s[i].x + kr * u.x, s[i].y + kr * u.y, s[i].z + kr * u.z, s[i].w + kr * u.w};
+        __builtin_nontemporal_store(x, reinterpret_cast<f4v *>(&S[r * D::CG + cg]));
+    }
+}
+
+// One decode step.  PAGED: the states live in pool slots (slot_in /
+// slot_out); otherwise the unit's own entry of a dense [N, H, K, V] array is
+// updated in place.
 template <int K, int V, int NT, typename TIn, typename TOut, bool PAGED>
 __global__ __launch_bounds__(NT) void decode_step_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const TIn *__restrict__ g, const TIn *__restrict__ beta, float *__restrict__ state,
     const int32_t *__restrict__ slot_in, const int32_t *__restrict__ slot_out, int pool_slots,
     int H, TOut *__restrict__ o) {
-    constexpr int CG = V / 4;    // column groups of four floats
-    constexpr int RG = NT / CG;  // row groups
-    constexpr int RPT = K / RG;  // rows per thread
-    constexpr int NW = NT / 64;  // wavefronts per workgroup
-    static_assert(V % 4 == 0 && CG <= 64 && 64 % CG == 0, "column groups must tile a wave");
-    static_assert(NT % CG == 0 && K % RG == 0, "rows must tile the workgroup");
-
-    __shared__ float sq[K], sk[K], sa[K];
-    __shared__ float4 red[NW][CG][2];
-    __shared__ float skq;
+    using D = DecodeShape<K, V, NT>;
+    __shared__ DecodeLds<K, V, NT> lds;
 
     const size_t unit = blockIdx.x;  // n * H + h
     const int t = threadIdx.x;
-    const int cg = t % CG, rg = t / CG;
-    const int lane = t & 63, w = t >> 6;
+    const int cg = t % D::CG, rg = t / D::CG;
 
     // The state is read from Sin and written to Sout: the unit's own entry of
     // a dense [N, H, K, V] array, or slots slot_in[n] / slot_out[n] of a pool
@@ -66,83 +169,64 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(
     }
 
     // Issue the state loads first; the small per-head vectors follow.
-    float4 s[RPT];
+    float4 s[D::RPT];
     if (!PAGED || Sin) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) s[i] = Sin[(rg + i * RG) * CG + cg];
+        for (int i = 0; i < D::RPT; ++i) s[i] = Sin[(rg + i * D::RG) * D::CG + cg];
     } else {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = 0; i < D::RPT; ++i) s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    const float4 u = decode_token<K, V, NT, TIn, TOut>(s, q + unit * K, k + unit * K, g + unit * K,
+                                                       beta + unit, v + unit * V, o + unit * V, lds);
+    if (!PAGED || Sout) store_state<K, V, NT>(Sout, s, u, lds.sk);
+}
 
-    for (int c = t; c < K; c += NT) {
-        sq[c] = to_f32(q[unit * K + c]);
-        sk[c] = to_f32(k[unit * K + c]);
-        sa[c] = fast_exp(to_f32(g[unit * K + c]));
-    }
-    __syncthreads();
-    if (w == 0) {
-        float p = 0.f;
-        for (int c = lane; c < K; c += 64) p += sk[c] * sq[c];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
-        if (lane == 0) skq = p;
-    }
+// T consecutive tokens per sequence in one pass over each state (the
+// verification step of speculative decoding): tokens are [N, T, H, *]; the
+// state is read once from slot_in[n], kept in registers, advanced token by
+// token, and after token j written to slot slot_out[n * T + j] when that slot
+// lies in the pool (so the caller keeps exactly the prefixes it may accept).
+template <int K, int V, int NT, typename TIn, typename TOut>
+__global__ __launch_bounds__(NT) void decode_multi_kernel(
+    const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
+    const TIn *__restrict__ g, const TIn *__restrict__ beta, float *__restrict__ pool,
+    const int32_t *__restrict__ slot_in, const int32_t *__restrict__ slot_out, int pool_slots,
+    int T, int H, TOut *__restrict__ o) {
+    using D = DecodeShape<K, V, NT>;
+    __shared__ DecodeLds<K, V, NT> lds;
 
-    float4 rk = make_float4(0.f, 0.f, 0.f, 0.f), rq = rk;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg + i * RG;
-        const float a = sa[r], kr = sk[r], qr = sq[r];
-        s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
-        rk.x += kr * s[i].x; rk.y += kr * s[i].y; rk.z += kr * s[i].z; rk.w += kr * s[i].w;
-        rq.x += qr * s[i].x; rq.y += qr * s[i].y; rq.z += qr * s[i].z; rq.w += qr * s[i].w;
-    }
-    // Lanes of one wave holding the same columns differ by multiples of CG.
-#pragma unroll
-    for (int off = CG; off < 64; off <<= 1) {
-        rk.x += __shfl_xor(rk.x, off); rk.y += __shfl_xor(rk.y, off);
-        rk.z += __shfl_xor(rk.z, off); rk.w += __shfl_xor(rk.w, off);
-        rq.x += __shfl_xor(rq.x, off); rq.y += __shfl_xor(rq.y, off);
-        rq.z += __shfl_xor(rq.z, off); rq.w += __shfl_xor(rq.w, off);
-    }
-    if (lane < CG) {
-        red[w][lane][0] = rk;
-        red[w][lane][1] = rq;
-    }
-    __syncthreads();
-    float4 RK = red[0][cg][0], RQ = red[0][cg][1];
-#pragma unroll
-    for (int ww = 1; ww < NW; ++ww) {
-        const float4 a = red[ww][cg][0], b = red[ww][cg][1];
-        RK.x += a.x; RK.y += a.y; RK.z += a.z; RK.w += a.w;
-        RQ.x += b.x; RQ.y += b.y; RQ.z += b.z; RQ.w += b.w;
-    }
-    const float b = to_f32(beta[unit]);
-    const TIn *vp = v + unit * V + 4 * cg;
-    float4 u;
-    u.x = b * (to_f32(vp[0]) - RK.x);
-    u.y = b * (to_f32(vp[1]) - RK.y);
-    u.z = b * (to_f32(vp[2]) - RK.z);
-    u.w = b * (to_f32(vp[3]) - RK.w);
+    const int unit = blockIdx.x;  // n * H + h
+    const int n = unit / H, h = unit % H;
+    const int t = threadIdx.x;
+    const int cg = t % D::CG, rg = t / D::CG;
+    auto slot_ptr = [&](int sl) {
+        return sl >= 0 && sl < pool_slots ? reinterpret_cast<float4 *>(pool + ((size_t)sl * H + h) * (K * V))
+                                          : nullptr;
+    };
 
-    typedef float f4v __attribute__((ext_vector_type(4)));
-    if (!PAGED || Sout) {
+    const float4 *Sin = slot_ptr(slot_in[n]);
+    float4 s[D::RPT];
+    if (Sin) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = rg + i * RG;
-            const float kr = sk[r];
-            const f4v x = {s[i].x + kr * u.x, s[i].y + kr * u.y, s[i].z + kr * u.z, s[i].w + kr * u.w};
-            __builtin_nontemporal_store(x, reinterpret_cast<f4v *>(&Sout[r * CG + cg]));
+        for (int i = 0; i < D::RPT; ++i) s[i] = Sin[(rg + i * D::RG) * D::CG + cg];
+    } else {
+#pragma unroll
+        for (int i = 0; i < D::RPT; ++i) s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int j = 0; j < T; ++j) {
+        if (j > 0) __syncthreads();  // every thread is done with the previous token's lds
+        const size_t tok = ((size_t)n * T + j) * H + h;
+        const float4 u = decode_token<K, V, NT, TIn, TOut>(s, q + tok * K, k + tok * K, g + tok * K,
+                                                           beta + tok, v + tok * V, o + tok * V, lds);
+        float4 *Sout = slot_ptr(slot_out[(size_t)n * T + j]);
+        if (Sout) store_state<K, V, NT>(Sout, s, u, lds.sk);
+        // the new state stays in registers for the next token
+#pragma unroll
+        for (int i = 0; i < D::RPT; ++i) {
+            const float kr = lds.sk[rg + i * D::RG];
+            s[i].x += kr * u.x; s[i].y += kr * u.y; s[i].z += kr * u.z; s[i].w += kr * u.w;
         }
-    }
-    if (rg == 0) {
-        const float kq = skq;
-        TOut *op = o + unit * V + 4 * cg;
-        op[0] = from_f32<TOut>(RQ.x + kq * u.x);
-        op[1] = from_f32<TOut>(RQ.y + kq * u.y);
-        op[2] = from_f32<TOut>(RQ.z + kq * u.z);
-        op[3] = from_f32<TOut>(RQ.w + kq * u.w);
     }
 }
 
@@ -198,6 +282,45 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const void
         return launch_decode_kv<128, 128, 256>(q, k, v, g, beta, st, o, units, H, in_bf16, out_bf16, stream);
     if (K == 32 && V == 32)
         return launch_decode_kv<32, 32, 64>(q, k, v, g, beta, st, o, units, H, in_bf16, out_bf16, stream);
+    return hipErrorInvalidValue;
+}
+
+template <int K, int V, int NT, typename TIn, typename TOut>
+static hipError_t launch_multi_t(const void *q, const void *k, const void *v, const void *g,
+                                 const void *beta, float *pool, const int32_t *slot_in,
+                                 const int32_t *slot_out, int pool_slots, void *o, int N, int T,
+                                 int H, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_multi_kernel<K, V, NT, TIn, TOut>), dim3(N * H), dim3(NT), 0, stream,
+                       static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                       static_cast<const TIn *>(v), static_cast<const TIn *>(g),
+                       static_cast<const TIn *>(beta), pool, slot_in, slot_out, pool_slots, T, H,
+                       static_cast<TOut *>(o));
+    return hipGetLastError();
+}
+
+template <int K, int V, int NT>
+static hipError_t launch_multi_kv(const void *q, const void *k, const void *v, const void *g,
+                                  const void *beta, float *pool, const int32_t *slot_in,
+                                  const int32_t *slot_out, int pool_slots, void *o, int N, int T,
+                                  int H, bool in_bf16, bool out_bf16, hipStream_t stream) {
+    if (in_bf16)
+        return out_bf16 ? launch_multi_t<K, V, NT, bf16_t, bf16_t>(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o, N, T, H, stream)
+                        : launch_multi_t<K, V, NT, bf16_t, float>(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o, N, T, H, stream);
+    return out_bf16 ? launch_multi_t<K, V, NT, float, bf16_t>(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o, N, T, H, stream)
+                    : launch_multi_t<K, V, NT, float, float>(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o, N, T, H, stream);
+}
+
+// Internal launcher of the multi-token step: shapes were validated by the caller.
+hipError_t launch_decode_multi(const void *q, const void *k, const void *v, const void *g,
+                               const void *beta, float *pool, const int32_t *slot_in,
+                               const int32_t *slot_out, int pool_slots, void *o, int N, int T,
+                               int H, int K, int V, bool in_bf16, bool out_bf16,
+                               hipStream_t stream) {
+    if (N == 0 || T == 0) return hipSuccess;
+    if (K == 128 && V == 128)
+        return launch_multi_kv<128, 128, 256>(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o, N, T, H, in_bf16, out_bf16, stream);
+    if (K == 32 && V == 32)
+        return launch_multi_kv<32, 32, 64>(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o, N, T, H, in_bf16, out_bf16, stream);
     return hipErrorInvalidValue;
 }
 

@@ -16,6 +16,11 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const void
                          const void *beta, float *state, const int32_t *slot_in,
                          const int32_t *slot_out, int pool_slots, void *o, int N, int H, int K,
                          int V, bool in_bf16, bool out_bf16, hipStream_t stream);
+hipError_t launch_decode_multi(const void *q, const void *k, const void *v, const void *g,
+                               const void *beta, float *pool, const int32_t *slot_in,
+                               const int32_t *slot_out, int pool_slots, void *o, int N, int T,
+                               int H, int K, int V, bool in_bf16, bool out_bf16,
+                               hipStream_t stream);
 hipError_t launch_chunk_valu(const void *q, const void *k, const void *v, const void *g,
                              const void *beta, const StateIO &io, void *o, const int32_t *cu,
                              int N, int fixedT, int totalT, int H, int K, int V, int C,
@@ -111,7 +116,7 @@ bool pool_ok(int pool_slots, int H, int K, int V) {
 
 extern "C" {
 
-int kda_version(void) { return 101; }
+int kda_version(void) { return 102; }
 
 const char *kda_status_str(kda_status_t s) {
     switch (s) {
@@ -247,6 +252,23 @@ kda_status_t kda_decode_step_paged(const void *q, const void *k, const void *v, 
     return from_hip(kda::launch_decode(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o,
                                        N, H, K, V, in_dtype == KDA_BF16, out_dtype == KDA_BF16,
                                        static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_decode_multi_paged(const void *q, const void *k, const void *v, const void *g,
+                                    const void *beta, float *pool, int pool_slots,
+                                    const int32_t *slot_in, const int32_t *slot_out, void *o,
+                                    int N, int T, int H, int K, int V, kda_dtype_t in_dtype,
+                                    kda_dtype_t out_dtype, void *stream) {
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
+    if (N < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_SHAPE;
+    if (!fits((long long)N * T, H, K > V ? K : V)) return KDA_ERR_SHAPE;
+    if (!((K == 128 && V == 128) || (K == 32 && V == 32))) return KDA_ERR_UNSUPPORTED;
+    if (!pool_ok(pool_slots, H, K, V)) return KDA_ERR_SHAPE;
+    if (N == 0 || T == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !pool || !slot_in || !slot_out || !o) return KDA_ERR_NULL;
+    return from_hip(kda::launch_decode_multi(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots,
+                                             o, N, T, H, K, V, in_dtype == KDA_BF16,
+                                             out_dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

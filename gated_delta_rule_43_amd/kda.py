@@ -14,6 +14,7 @@ import os
 import torch
 
 __all__ = ["chunk_fwd", "varlen_fwd", "decode_step", "varlen_fwd_paged", "decode_step_paged",
+           "decode_multi_paged",
            "workspace_bytes",
            "two_pass_workspace_bytes", "library",
            "KdaError", "LIB_PATH", "F32", "BF16"]
@@ -55,6 +56,9 @@ def library():
     lib.kda_decode_step_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                           i32, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_step_paged.restype = i32
+    lib.kda_decode_multi_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                           i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_multi_paged.restype = i32
     lib.kda_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.kda_workspace_bytes.restype = sz
     lib.kda_two_pass_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -325,4 +329,31 @@ def decode_step_paged(q, k, v, g, beta, pool, slot_in, slot_out, out_dtype=torch
                                          _ptr(o), N, H, K, V, _dtype_code(dt),
                                          _dtype_code(o.dtype), _stream(q.device))
     _check("kda_decode_step_paged", st)
+    return o
+
+
+def decode_multi_paged(q, k, v, g, beta, pool, slot_in, slot_out, out_dtype=torch.float32,
+                       out=None):
+    """kda_decode_multi_paged: T tokens per sequence in one pass (draft verification).
+    q, k, g [N, T, H, K]; v [N, T, H, V]; beta [N, T, H]; pool float32 [slots, H, K, V];
+    slot_in int32 [N]; slot_out int32 [N, T] (state after token j, -1: not kept).
+    Returns o [N, T, H, V]."""
+    _need_gpu(q, k, v, g, beta, pool, slot_in, slot_out, out)
+    N, T, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    if any(x.dtype != dt for x in (k, v, g, beta)):
+        raise ValueError("q, k, v, g and beta must share one dtype")
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (N, T, H, V) or beta.shape != (N, T, H):
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    slots = _pool_check(pool, H, K, V)
+    _slots(slot_in, N, "slot_in")
+    if slot_out.dtype != torch.int32 or slot_out.shape != (N, T):
+        raise ValueError("slot_out must be int32 [N, T]")
+    o = out if out is not None else torch.empty((N, T, H, V), dtype=out_dtype, device=q.device)
+    st = library().kda_decode_multi_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                          _ptr(pool), slots, _ptr(slot_in), _ptr(slot_out),
+                                          _ptr(o), N, T, H, K, V, _dtype_code(dt),
+                                          _dtype_code(o.dtype), _stream(q.device))
+    _check("kda_decode_multi_paged", st)
     return o

@@ -189,6 +189,31 @@ kda_status_t kda_decode_step_paged(const void *q, const void *k, const void *v, 
                                    int N, int H, int K, int V, kda_dtype_t in_dtype,
                                    kda_dtype_t out_dtype, void *stream);
 
+/*
+ * kda_decode_multi_paged: T consecutive tokens per sequence in one pass over
+ * each state, the verification step of speculative decoding (section
+ * "Inference Serving" of the page above pairs KDA serving with speculative
+ * drafts).  The outputs are those of T decode steps in a row; the state is
+ * read once and, after token j of sequence n, written to a slot the caller
+ * picks, so that whichever draft prefix is accepted, its state is ready with
+ * no second pass.
+ *   q, k, g : [N, T, H, K]; v : [N, T, H, V]; beta : [N, T, H]   (in_dtype)
+ *   o       : [N, T, H, V] (out_dtype)
+ *   slot_in : DEVICE int32 [N], slot of each sequence's state before the
+ *             drafts (< 0 or >= pool_slots: zeros)
+ *   slot_out: DEVICE int32 [N, T], slot receiving the state after token j
+ *             (< 0 or >= pool_slots: not written)
+ * The slots written must be distinct from each other and from the input
+ * slots of other sequences; a sequence's own input slot may be among its
+ * output slots (it is read before anything is written).  T = 1 matches
+ * kda_decode_step_paged bit for bit.  Supported (K, V): (32, 32), (128, 128).
+ */
+kda_status_t kda_decode_multi_paged(const void *q, const void *k, const void *v, const void *g,
+                                    const void *beta, float *pool, int pool_slots,
+                                    const int32_t *slot_in, const int32_t *slot_out, void *o,
+                                    int N, int T, int H, int K, int V, kda_dtype_t in_dtype,
+                                    kda_dtype_t out_dtype, void *stream);
+
 /* Workspace bytes for the recommended implementation of a forward call over
  * N sequences, total_T tokens: nonzero (the two-pass size) when the two-pass
  * path is supported and expected to be faster (bf16 inputs assumed; at most

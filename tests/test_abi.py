@@ -30,8 +30,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kda_chunk_fwd", "kda_varlen_fwd", "kda_decode_step", "kda_varlen_fwd_paged",
-              "kda_decode_step_paged", "kda_workspace_bytes", "kda_two_pass_workspace_bytes",
-              "kda_status_str", "kda_version"):
+              "kda_decode_step_paged", "kda_decode_multi_paged", "kda_workspace_bytes",
+              "kda_two_pass_workspace_bytes", "kda_status_str", "kda_version"):
         assert n in names
 
 
@@ -45,7 +45,7 @@ def test_status_strings_and_version(lib):
         s = lib.kda_status_str(code).decode()
         assert s.startswith("KDA_")
     assert lib.kda_status_str(99).decode() == "KDA_ERR_UNKNOWN"
-    assert lib.kda_version() == 101
+    assert lib.kda_version() == 102
 
 
 def two_pass_size(N, total, H):
@@ -162,5 +162,23 @@ def test_paged_decode_argument_errors(lib):
     assert call(K=64) == 4
     assert call(slots=0) == 2
     assert call(N=-1) == 2
+    for i in range(9):
+        assert call(null=i) == 1
+
+
+def test_multi_decode_argument_errors(lib):
+    f = lib.kda_decode_multi_paged
+
+    def call(null=None, slots=8, N=4, T=3, K=128):
+        ptrs = [FAKE] * 9   # q, k, v, g, beta, pool, slot_in, slot_out, o
+        if null is not None:
+            ptrs[null] = None
+        return f(*ptrs[:6], slots, *ptrs[6:9], N, T, 2, K, K, 1, 0, None)
+
+    assert call(K=64) == 4
+    assert call(slots=0) == 2
+    assert call(T=-1) == 2
+    assert call(N=-1) == 2
+    assert call(T=0, null=0) == 0       # nothing to do: no pointer is needed
     for i in range(9):
         assert call(null=i) == 1

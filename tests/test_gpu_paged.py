@@ -185,3 +185,66 @@ def test_paged_decode_matches_dense_decode():
                                 ids, ids)
     torch.cuda.synchronize()
     assert torch.equal(o_d, o_p) and torch.equal(dense, pool)
+
+
+@pytest.mark.parametrize("dtype,K", [("bf16", 128), ("f32", 128), ("bf16", 32)])
+def test_multi_token_decode(dtype, K):
+    """T draft tokens per sequence in one pass: outputs equal T decode steps, and
+    the state after token j lands in slot_out[n][j] (the oracle's state after
+    that prefix); a sequence may end in its own input slot."""
+    N, T, H = 3, 5, 2
+    slots = 16
+    slot_in = [0, -1, 2]
+    slot_out = [[3, -1, 4, -1, 0],
+                [5, 6, 7, 8, 9],
+                [-1, -1, -1, -1, 10]]
+    print(f"[case] multi-token decode {dtype} K={K} N={N} T={T}", flush=True)
+    pool0 = _pool(28, slots, H, K, K)
+    d = inputs.draw_varlen(29, H=H, K=K, V=K, dtype=dtype, lengths=[T] * N)
+    cu = np.arange(N + 1) * T
+    s0 = np.zeros((N, H, K, K))
+    for n in range(N):
+        if slot_in[n] >= 0:
+            s0[n] = pool0[slot_in[n]].double().numpy()
+    o_ref, _ = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, s0)
+    ref_states = {}
+    for n in range(N):
+        for j in range(T):
+            if slot_out[n][j] >= 0:
+                sl = {x: d[x][n * T:n * T + j + 1] for x in ("q", "k", "v", "g", "beta")}
+                _, st = oracle.recurrence(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"],
+                                          np.array([0, j + 1]), s0[n:n + 1])
+                ref_states[slot_out[n][j]] = st[0]
+    x = to_gpu(d)
+    shp = lambda t, D: t.reshape(N, T, H, D) if D else t.reshape(N, T, H)
+    pool = pool0.cuda()
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    o = kda.decode_multi_paged(shp(x["q"], K), shp(x["k"], K), shp(x["v"], K), shp(x["g"], K),
+                               shp(x["beta"], 0), pool, i32(slot_in), i32(slot_out))
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    errs = {"o": rel_err(o.reshape(N * T, H, K), o_ref)}
+    for slot, ref in ref_states.items():
+        errs[f"s{slot}"] = rel_err(pool[slot], ref)
+    report(f"multi_decode_{dtype}_K{K}", **errs)
+    assert all(e <= tol for e in errs.values()), errs
+    for s in set(range(slots)) - set(ref_states):
+        assert torch.equal(pool[s].cpu(), pool0[s]), f"slot {s} was modified"
+
+
+def test_multi_token_decode_one_token_equals_single_step():
+    N, H, K = 4, 2, 128
+    print("[case] multi-token decode T=1 vs single paged step", flush=True)
+    pool0 = _pool(30, 2 * N, H, K, K)
+    step = to_gpu(inputs.draw_decode_step(31, 0, N, H, K, K, "bf16"))
+    ids = torch.arange(N, dtype=torch.int32, device="cuda")
+    outs = ids + N
+    pa = pool0.cuda()
+    o_a = kda.decode_step_paged(step["q"], step["k"], step["v"], step["g"], step["beta"], pa, ids,
+                                outs)
+    pb = pool0.cuda()
+    u = lambda t: t.unsqueeze(1).contiguous()
+    o_b = kda.decode_multi_paged(u(step["q"]), u(step["k"]), u(step["v"]), u(step["g"]),
+                                 u(step["beta"]), pb, ids, outs.reshape(N, 1).contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b[:, 0]) and torch.equal(pa, pb)
