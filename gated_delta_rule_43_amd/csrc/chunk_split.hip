@@ -59,7 +59,7 @@ constexpr size_t R_M = 0;         // fp16 M' in A order [8 row blocks][4 k-steps
 constexpr size_t R_N = 32768;     // fp16 N as accumulators [8 value tiles][8 row blocks][64 lanes][4]
 constexpr size_t R_FC = 65536;    // fp32 [128]  f
 constexpr size_t R_OH = 66048;    // fp16 O^ as accumulators [8 value tiles][4 row blocks][64 lanes][4]
-constexpr size_t R_QH = 82432;    // fp16 [64][128]  Q^ [r][c]
+constexpr size_t R_QH = 82432;    // fp16 Q^ in A order [4 row blocks][4 k-steps]
 constexpr size_t R_SP = 98816;    // fp16 S (chunk-start state) in B order [8 value tiles][4 k-steps]
 constexpr size_t REC = 131584;
 
@@ -502,21 +502,15 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     // as the contraction index, 16-byte blocks of a row XOR-permuted by (c & 7)
 #pragma unroll
     for (int e = 0; e < 8; ++e) *reinterpret_cast<half4 *>(&sm.kp[kt_off(8 * cg + e, rg)]) = kmT[e];
-    // ---- Q^ rows to the workspace, k-permuted (16-byte stores: stored block b
-    // of a row takes logical 4-groups 8 (b >> 2) + (b & 3) and that + 4)
+    // ---- Q^ to the workspace as A fragments, k-permuted: wave w writes row
+    // block w, one whole 1 KB fragment per k-step (a lane's 8 values are
+    // logical k 32 ks + 4 lg .. +3 and that + 16 of row 16 w + l16)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int idx = 256 * e + t, r = idx >> 4, bp = idx & 15;
-        const int l0 = 32 * (bp >> 2) + 4 * (bp & 3), l1 = l0 + 16;
+    for (int ks = 0; ks < 4; ++ks) {
+        const int r = 16 * w + l16, l0 = 32 * ks + 4 * lg;
         const half4 q0 = *reinterpret_cast<const half4 *>(&sm.qp[r * PK + l0]);
-        const half4 q1 = *reinterpret_cast<const half4 *>(&sm.qp[r * PK + l1]);
-        half8 qv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qv[i] = q0[i];
-            qv[4 + i] = q1[i];
-        }
-        *reinterpret_cast<half8 *>(rec + R_QH + 2 * ((size_t)r * KD + 8 * bp)) = qv;
+        const half4 q1 = *reinterpret_cast<const half4 *>(&sm.qp[r * PK + l0 + 16]);
+        *reinterpret_cast<half8 *>(rec + R_QH + 16 * ((w * 4 + ks) * 64 + lane)) = pair8(q0, q1);
     }
     __syncthreads();
     // ---- M' = -Diag(f) Km^T W E (from Xh[0..1]) and N = Diag(f) Km^T U~
@@ -902,12 +896,19 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(TOut *__restrict__ o,
 
     const int lane = threadIdx.x & 63, l16 = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Q^ (A fragments, 16 KB) is shared by the four waves: each copies four of
+    // its fragments into LDS with direct loads
+    __shared__ __align__(16) unsigned char qs[16 * 1024];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(rec + R_QH + 1024 * (4 * w + i) + 16 * lane, qs + 1024 * (4 * w + i));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
     half8 aq[4][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
-            aq[ks][rb] = *reinterpret_cast<const half8 *>(rec + R_QH + 2 * ((16 * rb + l16) * KD + 8 * (4 * ks + lg)));
+            aq[ks][rb] = *reinterpret_cast<const half8 *>(qs + 1024 * (rb * 4 + ks) + 16 * lane);
     const int row_bytes = H * VD * (int)sizeof(TOut);
     __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
         o + (size_t)c0 * H * VD, 0, L * row_bytes, 0x00020000);
