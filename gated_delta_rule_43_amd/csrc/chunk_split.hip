@@ -872,11 +872,18 @@ hipError_t launch_state(const StateIO &io, const int32_t *cu, int N, int fixedT,
 // outputs leave through a buffer resource spanning the chunk's valid rows,
 // as non-temporal stores (nothing in the call reads them back).
 constexpr int CPOL_NT = 2;
-__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, float x) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, CPOL_NT);
+// Four consecutive columns of one output row: 16 bytes (fp32) or 8 (bf16).
+__device__ __forceinline__ void store_row4(__amdgpu_buffer_rsrc_t r, int off, const floatx4 &y, float) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4 b = {(int)__float_as_uint(y[0]), (int)__float_as_uint(y[1]), (int)__float_as_uint(y[2]),
+                     (int)__float_as_uint(y[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(b, r, off, 0, CPOL_NT);
 }
-__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int off, bf16_t x) {
-    __builtin_amdgcn_raw_buffer_store_b16(x.bits, r, off, 0, CPOL_NT);
+__device__ __forceinline__ void store_row4(__amdgpu_buffer_rsrc_t r, int off, const floatx4 &y, bf16_t) {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    const i32x2 b = {(int)(from_f32<bf16_t>(y[0]).bits | ((uint32_t)from_f32<bf16_t>(y[1]).bits << 16)),
+                     (int)(from_f32<bf16_t>(y[2]).bits | ((uint32_t)from_f32<bf16_t>(y[3]).bits << 16))};
+    __builtin_amdgcn_raw_buffer_store_b64(b, r, off, 0, CPOL_NT);
 }
 
 template <typename TOut>
@@ -930,12 +937,12 @@ __global__ __launch_bounds__(256) void chunk_output_kernel(TOut *__restrict__ o,
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) Y[rb] = mma32(aq[ks][rb], bs[ks], Y[rb]);
-        const int lane_off = ((4 * lg * H + h) * VD + j) * (int)sizeof(TOut);
+        // after a 4 x 4 transpose inside each quad of lanes, a lane holds row
+        // 4 lg + (lane & 3) of each row block, columns j - (lane & 3) .. +3
+        const int lane_off = (((4 * lg + (lane & 3)) * H + h) * VD + j - (lane & 3)) * (int)sizeof(TOut);
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                store_elem(orsrc, lane_off + (16 * rb + e) * row_bytes, from_f32<TOut>(Y[rb][e]));
+            store_row4(orsrc, lane_off + 16 * rb * row_bytes, quad_transpose(Y[rb], lane), TOut{});
     }
 }
 
