@@ -963,8 +963,8 @@ bool chunk_split_supported(int N, int H, int K, int V, int Cc) {
 }
 
 bool chunk_split_recommended(int N, int totalT, int H, int K, int V, int Cc) {
-    return chunk_split_supported(N, H, K, V, Cc) && (long long)N * H <= 32 &&
-           (long long)totalT >= 8LL * C * N;
+    return chunk_split_supported(N, H, K, V, Cc) && (long long)N * H <= 48 &&
+           (long long)totalT >= 4LL * C * N;
 }
 
 size_t chunk_split_workspace_bytes(int N, int totalT, int H) {

@@ -217,7 +217,7 @@ kda_status_t kda_decode_multi_paged(const void *q, const void *k, const void *v,
 /* Workspace bytes for the recommended implementation of a forward call over
  * N sequences, total_T tokens: nonzero (the two-pass size) when the two-pass
  * path is supported and expected to be faster (bf16 inputs assumed; at most
- * 32 units, sequences of at least 8 chunks on average), else 0. */
+ * 48 units, sequences of at least 4 chunks on average), else 0. */
 size_t kda_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk);
 
 /* Workspace bytes that select the two-pass path whenever it is supported:

@@ -57,10 +57,11 @@ def test_workspace_sizes(lib):
     rec, two = lib.kda_workspace_bytes, lib.kda_two_pass_workspace_bytes
     # recommended: two-pass for few units and long sequences only
     assert rec(1, 4096, 8, 128, 128, 64) == two_pass_size(1, 4096, 8)
-    assert rec(1, 4096, 32, 128, 128, 64) == two_pass_size(1, 4096, 32)
-    assert rec(1, 4096, 33, 128, 128, 64) == 0
+    assert rec(1, 4096, 48, 128, 128, 64) == two_pass_size(1, 4096, 48)
+    assert rec(1, 4096, 49, 128, 128, 64) == 0
     assert rec(4, 32768, 32, 128, 128, 64) == 0
-    assert rec(1, 511, 8, 128, 128, 64) == 0
+    assert rec(1, 256, 8, 128, 128, 64) == two_pass_size(1, 256, 8)
+    assert rec(1, 255, 8, 128, 128, 64) == 0
     # supported whenever (K, V, chunk) = (128, 128, 64) and N < 127
     assert two(4, 32768, 32, 128, 128, 64) == two_pass_size(4, 32768, 32)
     assert two(2, 0, 3, 128, 128, 64) == two_pass_size(2, 0, 3)

@@ -85,10 +85,10 @@ def test_bf16_output_dtype(path):
                 out_dtype=torch.bfloat16, tol=3e-2, path=path)
 
 
-@pytest.mark.parametrize("H,expect_two_pass", [(32, True), (33, False)])
+@pytest.mark.parametrize("H,expect_two_pass", [(48, True), (49, False)])
 def test_bf16_d128_default_choice_at_the_unit_switch(H, expect_two_pass):
     # with the default arguments the library recommends the two-pass path up to
-    # 32 (sequence, head) units of long enough sequences, the fused kernel above
+    # 48 (sequence, head) units of long enough sequences, the fused kernel above
     B, T = 1, 600
     assert (kda.workspace_bytes(B, B * T, H, 128, 128, 64) > 0) == expect_two_pass
     print(f"[case] default choice B={B} T={T} H={H} two_pass={expect_two_pass}", flush=True)
