@@ -46,9 +46,9 @@ constexpr int VD = 128;  // value dimension
 constexpr int VT = 64;   // value columns per workgroup
 constexpr int NT = 768;  // threads per workgroup: 4 state waves + 8 prep waves
 constexpr int NP = 8;    // prep waves
-constexpr int PK = 136;  // LDS pitch (halves) of [64][128] fp16 tiles
+constexpr int PK = 144;  // LDS pitch (halves) of [64][128] fp16 tiles
 constexpr int PC = 72;   // LDS pitch (halves) of [*][64] fp16 tiles read as 16-byte fragments
-constexpr int P4 = 76;   // LDS pitch (halves) of [64][64] fp16 tiles read as 8-byte fragments
+constexpr int P4 = 68;   // LDS pitch (halves) of [64][64] fp16 tiles read as 8-byte fragments
 constexpr int PI = 20;   // LDS pitch (halves) of 16 x 16 fp16 blocks
 constexpr int PF = 17;   // LDS pitch (floats) of 16 x 16 fp32 blocks
 
