@@ -161,6 +161,54 @@ def draw_varlen(seed: int, H: int, K: int, V: int, dtype: str, N: int = 0,
                 cu_seqlens=torch.from_numpy(cu.astype(np.int32)), lengths=lengths)
 
 
+def _draw_raw_token_tensors(rng: np.random.Generator, tokens: int, H: int, K: int, V: int,
+                            dtype: str):
+    """Raw projections for the input prologue: q, k ~ N(0, 1) per element times a
+    per-(token, head) scale exp(U(-2, 2)) (so row norms vary over e^+-2 sqrt(K));
+    v ~ N(0, 1); gate logits ~ N(0, 1) per (token, head, channel); beta logits
+    ~ N(0, 1) per (token, head)."""
+    def rows(n):
+        x = rng.standard_normal((tokens, H, n), dtype=np.float32)
+        return x * np.exp(rng.uniform(-2.0, 2.0, size=(tokens, H, 1))).astype(np.float32)
+    q = to_dtype(rows(K), dtype)
+    k = to_dtype(rows(K), dtype)
+    v = to_dtype(rng.standard_normal((tokens, H, V), dtype=np.float32), dtype)
+    x = to_dtype(rng.standard_normal((tokens, H, K), dtype=np.float32), dtype)
+    b = to_dtype(rng.standard_normal((tokens, H), dtype=np.float32), dtype)
+    return q, k, v, x, b
+
+
+def draw_raw_fixed(seed: int, B: int, T: int, H: int, K: int, V: int, dtype: str,
+                   s0_std: Optional[float] = None) -> dict:
+    """Raw prologue inputs, fixed-length batch: q, k [B, T, H, K] (unnormalised),
+    g [B, T, H, K] gate logits, v [B, T, H, V], beta [B, T, H] logits; s0 or None."""
+    rng = np.random.default_rng(seed)
+    q, k, v, x, b = _draw_raw_token_tensors(rng, B * T, H, K, V, dtype)
+    s0 = None
+    if s0_std is not None:
+        s0 = torch.from_numpy(
+            (rng.standard_normal((B, H, K, V), dtype=np.float32) * np.float32(s0_std)))
+    return dict(q=q.view(B, T, H, K), k=k.view(B, T, H, K), v=v.view(B, T, H, V),
+                g=x.view(B, T, H, K), beta=b.view(B, T, H), s0=s0)
+
+
+def draw_raw_varlen(seed: int, H: int, K: int, V: int, dtype: str, lengths,
+                    s0_std: Optional[float] = None) -> dict:
+    """Raw prologue inputs for packed sequences of the given lengths."""
+    rng = np.random.default_rng(seed)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    N = len(lengths)
+    cu = np.zeros(N + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    q, k, v, x, b = _draw_raw_token_tensors(rng, int(cu[-1]), H, K, V, dtype)
+    s0 = None
+    if s0_std is not None:
+        s0 = torch.from_numpy(
+            (rng.standard_normal((N, H, K, V), dtype=np.float32) * np.float32(s0_std)))
+    return dict(q=q, k=k, v=v, g=x, beta=b, s0=s0,
+                cu_seqlens=torch.from_numpy(cu.astype(np.int32)), lengths=lengths)
+
+
 def draw_decode_state(seed: int, N: int, H: int, K: int, V: int, s0_std: float) -> torch.Tensor:
     """Initial persistent decode state [N, H, K, V] fp32 ~ N(0, s0_std^2)."""
     rng = np.random.default_rng(seed)

@@ -112,6 +112,32 @@ def fixed(q, k, v, g, beta, s0=None, nthreads: int | None = None):
     return o.reshape(B, T, H, V), sT
 
 
+def prologue(q, k, g, beta, normalize_qk: bool = False, gate_lower_bound=None,
+             beta_logits: bool = False, norm_eps: float = 0.0):
+    """The input prologue, in fp64: maps raw projections to what the recurrence
+    reads.  "Kimi K3: Open Frontier Intelligence and Implementation Framework",
+    section "Hybrid Attention Mechanism", calls KDA's gate channel-wise and its
+    decay lower-bounded; the parameterisation taken here is
+        g    = -g_lb * sigmoid(x)             (gate logits x, g_lb = gate_lower_bound)
+        beta = sigmoid(b)                     (beta logits b)
+        q, k = x / sqrt(sum_c x_c^2 + eps)    (per token and head; 0 if the sum is 0)
+    with sigmoid(x) = 1 / (1 + exp(-x)).  Each map applies only when selected;
+    the others pass their input through.  Returns fp64 (q, k, g, beta)."""
+    q, k, g, beta = (as_f64(x) for x in (q, k, g, beta))
+    if normalize_qk:
+        def unit(x):
+            s = np.sum(x * x, axis=-1, keepdims=True) + norm_eps
+            safe = np.where(s > 0.0, s, 1.0)
+            return np.where(s > 0.0, x / np.sqrt(safe), 0.0)
+        q, k = unit(q), unit(k)
+    with np.errstate(over="ignore"):
+        if gate_lower_bound is not None:
+            g = -float(gate_lower_bound) / (1.0 + np.exp(-g))
+        if beta_logits:
+            beta = 1.0 / (1.0 + np.exp(-beta))
+    return q, k, g, beta
+
+
 def decode_step(q, k, v, g, beta, state, nthreads: int | None = None):
     """One token per sequence: q, k, g [N, H, K]; v [N, H, V]; beta [N, H];
     state [N, H, K, V] fp64.  Returns (o [N, H, V], new state)."""
