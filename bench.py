@@ -159,6 +159,20 @@ def decode_leg(args, dev, stream):
 
     pms, _ = time_launches(dstep_paged, args.decode_steps, 20, stream)
 
+    # the same step from raw projections: q/k L2 normalisation and the gate and
+    # beta logit maps inside the kernel (kda_decode_step_prologue)
+    raw = [{k2: v2.to(dev) for k2, v2 in
+            inputs.draw_raw_varlen(wd.seed + 100 + s, wd.H, wd.K, wd.V, wd.dtype, [1] * wd.N).items()
+            if isinstance(v2, torch.Tensor) and v2.dim() >= 2} for s in range(2)]
+    pro = kda.Prologue(normalize_qk=True, gate_lower_bound=0.25, beta_logits=True, norm_eps=1e-6)
+
+    def dstep_pro():
+        xi = raw[ctr[0] % 2]
+        ctr[0] += 1
+        kda.decode_step(xi["q"], xi["k"], xi["v"], xi["g"], xi["beta"], state, out=od, prologue=pro)
+
+    proms, _ = time_launches(dstep_pro, args.decode_steps, 20, stream)
+
     # draft verification: 4 tokens per sequence in one pass over each state
     # (kda_decode_multi_paged), keeping the state after every draft token in
     # its own slot, or only the last one, in place
@@ -187,6 +201,7 @@ def decode_leg(args, dev, stream):
                      "traffic": measured_traffic(f"decode_step_kernel_{DECODE_TAG}"),
                      "kernel": "decode_step_kernel", "alg_bytes_per_launch": db},
         "paged_ms_per_step": pms,
+        "prologue_ms_per_step": proms,
         "draft_verify": {"draft_tokens": td, "ms_keep_every_state": vms_all,
                          "ms_keep_last_state": vms_last,
                          "tokens_per_s_keep_last": wd.N * td / (vms_last * 1e-3),
@@ -291,6 +306,31 @@ def main():
                              workspace=ws if nws_p else None, two_pass=bool(nws_p))
 
     ms_snap, _ = time_launches(step_snap, args.steps, 20, stream)
+
+    # the same step from raw projections (unnormalised q and k, gate logits,
+    # beta logits): the maps run inside the kernels' loads
+    # (kda_chunk_fwd_prologue), against a model-side version that first runs
+    # them as separate elementwise passes in torch and then makes the plain call
+    r = inputs.draw_raw_fixed(w.seed + 100, w.B, w.T, w.H, w.K, w.V, w.dtype, s0_std=w.s0_std)
+    xr = {key: (val.to(dev) if val is not None else None) for key, val in r.items()}
+    pro = kda.Prologue(normalize_qk=True, gate_lower_bound=0.25, beta_logits=True, norm_eps=1e-6)
+
+    def step_pro():
+        kda.chunk_fwd(xr["q"], xr["k"], xr["v"], xr["g"], xr["beta"], xr["s0"], chunk=w.chunk,
+                      final_state=sT, out=o, workspace=ws, prologue=pro)
+
+    def step_torch_prologue():
+        def unit(t):
+            t32 = t.float()
+            return (t32 * torch.rsqrt((t32 * t32).sum(-1, keepdim=True) + 1e-6)).to(t.dtype)
+        gq, gk = unit(xr["q"]), unit(xr["k"])
+        gg = (-0.25 * torch.sigmoid(xr["g"].float())).to(xr["g"].dtype)
+        gb = torch.sigmoid(xr["beta"].float()).to(xr["beta"].dtype)
+        kda.chunk_fwd(gq, gk, xr["v"], gg, gb, xr["s0"], chunk=w.chunk, final_state=sT, out=o,
+                      workspace=ws)
+
+    ms_pro, _ = time_launches(step_pro, args.steps, 20, stream)
+    ms_torch_pro, _ = time_launches(step_torch_prologue, args.steps, 20, stream)
     tokens = w.B * w.T
     alg_b = prefill_alg_bytes(w.B, w.T, w.H, w.K, w.V, s0=w.s0_std is not None, sT=True)
     alg_f = prefill_alg_flops(w.B, w.T, w.H, w.K, w.V, w.chunk)
@@ -325,6 +365,10 @@ def main():
         "fused_single_pass_ms_per_step": ms_fused,
         "prefix_cache": {"ms_per_step_with_snapshots": ms_snap, "snap_tokens": snap,
                          "page_tokens": page, "snapshots_per_call": w.B * w.H * (w.T // snap)},
+        "prologue": {"ms_per_step_fused_maps": ms_pro,
+                     "ms_per_step_torch_maps_then_plain_call": ms_torch_pro,
+                     "maps": "q, k L2-normalised (eps 1e-6); g = -0.25 sigmoid(gate logits); "
+                             "beta = sigmoid(beta logits)"},
     }
 
     # ---- decode leg

@@ -35,6 +35,7 @@
 //    diagonal inverses (I + A_ii)^-1 in fp32.
 // Two workgroup barriers per chunk separate these phases.
 #include "kda_mfma.hpp"
+#include "prologue.hpp"
 #include "state_io.hpp"
 
 namespace kda {
@@ -89,20 +90,22 @@ struct Raw {
     uint32_t beta;   // prep wave 0: beta of token lane
 };
 
+// Rows past the chunk's end read as `pad` (zeros, or gate logits mapping to 0).
 __device__ __forceinline__ void load_g(uint4 *rg, const uint16_t *g, int c0, int L, int H, int h,
-                                       int p, int lane) {
+                                       int p, int lane, uint32_t pad) {
     const int cg = lane & 15, tb = lane >> 4;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int r = 8 * p + 2 * tb + u;
-        rg[u] = make_uint4(0u, 0u, 0u, 0u);
+        rg[u] = make_uint4(pad, pad, pad, pad);
         if (r < L) rg[u] = *reinterpret_cast<const uint4 *>(g + ((size_t)(c0 + r) * H + h) * KD + 8 * cg);
     }
 }
 
+// Beta of tokens past the chunk's end reads as `bpad` (zero, or a logit mapping to 0).
 __device__ __forceinline__ void load_raw(Raw &R, const uint16_t *q, const uint16_t *k,
                                          const uint16_t *v, const uint16_t *beta, int c0, int L,
-                                         int H, int h, int vt, int p, int lane) {
+                                         int H, int h, int vt, int p, int lane, uint32_t bpad) {
     const int cg = lane & 15, tb = lane >> 4;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -120,18 +123,27 @@ __device__ __forceinline__ void load_raw(Raw &R, const uint16_t *q, const uint16
     if ((idx >> 3) < L)
         R.v = *reinterpret_cast<const uint4 *>(v + ((size_t)(c0 + (idx >> 3)) * H + h) * VD +
                                                vt * VT + 8 * (idx & 7));
-    R.beta = (p == 0 && lane < L) ? beta[(size_t)(c0 + lane) * H + h] : 0u;
+    R.beta = (p == 0 && lane < L) ? beta[(size_t)(c0 + lane) * H + h] : bpad;
 }
 
 // Prep wave p, first half of the running log-decay sum: lc = running sum over
 // this lane's two tokens, then an inclusive scan over the wave's four token
 // pairs (lanes 16 apart share channels).  The wave's channel totals go to LDS;
-// ex keeps the in-wave exclusive prefix.
+// ex keeps the in-wave exclusive prefix.  PM (a ProMode): rg holds gate
+// logits when the prologue's gate map applies.
+template <int PM>
 __device__ __forceinline__ void scan_partials(Smem &sm, const uint4 *rg, int p, int lane,
-                                              float (*lc)[8], float *ex) {
+                                              float (*lc)[8], float *ex, const Prologue &pro) {
     const int cg = lane & 15, tb = lane >> 4;
     unpack8(rg[0], lc[0]);
     unpack8(rg[1], lc[1]);
+    if (pro_on<PM>(pro, PRO_GATE_LOGIT)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            lc[0][e] = gate_from_logit(lc[0][e], pro.glb);
+            lc[1][e] = gate_from_logit(lc[1][e], pro.glb);
+        }
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         lc[1][e] += lc[0][e];
@@ -147,17 +159,16 @@ __device__ __forceinline__ void scan_partials(Smem &sm, const uint4 *rg, int p, 
 }
 
 // Prep wave p, second half: combine the wave totals into G - G_m for this
-// lane's tokens and write the fp16 operand tiles of the chunk.
-__device__ __forceinline__ void prologue(Smem &sm, const Raw &R, int par, int p, int lane,
-                                         const float (*lc)[8], const float *ex) {
+// lane's tokens and write the fp16 operand tiles of the chunk (after the
+// prologue's normalisation of q and k, whose 128 channels of a token lie in
+// one 16-lane DPP row).
+template <int PM>
+__device__ __forceinline__ void build_operands(Smem &sm, const Raw &R, int par, int p, int lane,
+                                               const float (*lc)[8], const float *ex,
+                                               const Prologue &pro) {
     const int cg = lane & 15, tb = lane >> 4;
     const int ch0 = 8 * cg;
     const int r0 = 8 * p + 2 * tb;
-    float kv0[8], kv1[8], qv0[8], qv1[8];
-    unpack8(R.k[0], kv0);
-    unpack8(R.k[1], kv1);
-    unpack8(R.q[0], qv0);
-    unpack8(R.q[1], qv1);
     // offset of this wave's first token from the reference row m = 31 (the end
     // of wave 3's tokens): + sum of waves 4..p-1, or - sum of waves p..3
     float d[8];
@@ -187,26 +198,41 @@ __device__ __forceinline__ void prologue(Smem &sm, const Raw &R, int par, int p,
             sm.fc[par][ch0 + e] = fast_exp(gc - gm);
         }
     }
-    half8 hkp0, hkm0, hqp0, hkp1, hkm1, hqp1;
+    float pre[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float pre = ex[e] + (p < 4 ? -d[e] : d[e]);
-        const float G0 = pre + lc[0][e], G1 = pre + lc[1][e];  // G - G_m
-        const float f0 = fast_exp(G0), f1 = fast_exp(G1);
-        const float i0 = __builtin_amdgcn_rcpf(f0), i1 = __builtin_amdgcn_rcpf(f1);
-        hkp0[e] = (_Float16)(kv0[e] * f0);
-        hkm0[e] = (_Float16)(kv0[e] * i0);
-        hqp0[e] = (_Float16)(qv0[e] * f0);
-        hkp1[e] = (_Float16)(kv1[e] * f1);
-        hkm1[e] = (_Float16)(kv1[e] * i1);
-        hqp1[e] = (_Float16)(qv1[e] * f1);
+    for (int e = 0; e < 8; ++e) pre[e] = ex[e] + (p < 4 ? -d[e] : d[e]);
+    // one token row at a time (fewer live registers); Km of both rows is kept
+    // for the transposed tile
+    half8 hkm0, hkm1;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        float kv[8], qv[8];
+        unpack8(R.k[u], kv);
+        unpack8(R.q[u], qv);
+        if (pro_on<PM>(pro, PRO_NORM_QK)) {
+            const float ik = inv_norm(row16_sum(sumsq8(kv)), pro.eps);
+            const float iq = inv_norm(row16_sum(sumsq8(qv)), pro.eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kv[e] *= ik;
+                qv[e] *= iq;
+            }
+        }
+        half8 hkp, hkm, hqp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float f = fast_exp(pre[e] + lc[u][e]);  // exp(G - G_m)
+            const float i = __builtin_amdgcn_rcpf(f);
+            hkp[e] = (_Float16)(kv[e] * f);
+            hkm[e] = (_Float16)(kv[e] * i);
+            hqp[e] = (_Float16)(qv[e] * f);
+        }
+        *reinterpret_cast<half8 *>(&sm.kp[(r0 + u) * PK + ch0]) = hkp;
+        *reinterpret_cast<half8 *>(&sm.km[(r0 + u) * PK + ch0]) = hkm;
+        *reinterpret_cast<half8 *>(&sm.qp[(r0 + u) * PK + ch0]) = hqp;
+        if (u == 0) hkm0 = hkm;
+        else hkm1 = hkm;
     }
-    *reinterpret_cast<half8 *>(&sm.kp[r0 * PK + ch0]) = hkp0;
-    *reinterpret_cast<half8 *>(&sm.km[r0 * PK + ch0]) = hkm0;
-    *reinterpret_cast<half8 *>(&sm.qp[r0 * PK + ch0]) = hqp0;
-    *reinterpret_cast<half8 *>(&sm.kp[(r0 + 1) * PK + ch0]) = hkp1;
-    *reinterpret_cast<half8 *>(&sm.km[(r0 + 1) * PK + ch0]) = hkm1;
-    *reinterpret_cast<half8 *>(&sm.qp[(r0 + 1) * PK + ch0]) = hqp1;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         half2v pr;
@@ -217,7 +243,10 @@ __device__ __forceinline__ void prologue(Smem &sm, const Raw &R, int par, int p,
     }
     const int idx = 64 * p + lane;
     *reinterpret_cast<uint4 *>(&sm.v[(idx >> 3) * PC + 8 * (idx & 7)]) = R.v;
-    if (p == 0) sm.beta[lane] = __uint_as_float(R.beta << 16);
+    if (p == 0) {
+        const float b = __uint_as_float(R.beta << 16);
+        sm.beta[lane] = pro_on<PM>(pro, PRO_BETA_LOGIT) ? sigmoid_f(b) : b;
+    }
 }
 
 __device__ __forceinline__ floatx4 block_product(const _Float16 *lhs, const _Float16 *rhs, int bi,
@@ -297,11 +326,11 @@ __device__ __forceinline__ void prep_blocks(Smem &sm, int p, int lane) {
     }
 }
 
-template <typename TOut>
+template <typename TOut, int PM>
 __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ g,
-    const uint16_t *__restrict__ beta, StateIO io, TOut *__restrict__ o,
+    const uint16_t *__restrict__ beta, StateIO io, Prologue pro, TOut *__restrict__ o,
     const int32_t *__restrict__ cu, int fixedT, int N, int H, int totalT) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
@@ -443,20 +472,22 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
         }
     } else {
         const int p = w - 4;
+        const uint32_t gpad = pro_on<PM>(pro, PRO_GATE_LOGIT) ? BF16_NEG_INF_PAIR : 0u;
+        const uint32_t bpad = pro_on<PM>(pro, PRO_BETA_LOGIT) ? (BF16_NEG_INF_PAIR & 0xFFFFu) : 0u;
         Raw R;
         uint4 rg[2];
         float lc[2][8], ex[8];
         if (nchunks > 0) {
-            load_g(rg, g, bos, min(C, eos - bos), H, h, p, lane);
-            load_raw(R, q, k, v, beta, bos, min(C, eos - bos), H, h, vt, p, lane);
-            scan_partials(sm, rg, p, lane, lc, ex);
-            if (nchunks > 1) load_g(rg, g, bos + C, min(C, eos - bos - C), H, h, p, lane);
+            load_g(rg, g, bos, min(C, eos - bos), H, h, p, lane, gpad);
+            load_raw(R, q, k, v, beta, bos, min(C, eos - bos), H, h, vt, p, lane, bpad);
+            scan_partials<PM>(sm, rg, p, lane, lc, ex, pro);
+            if (nchunks > 1) load_g(rg, g, bos + C, min(C, eos - bos - C), H, h, p, lane, gpad);
         }
         __syncthreads();
         if (nchunks > 0) {
-            prologue(sm, R, 0, p, lane, lc, ex);
+            build_operands<PM>(sm, R, 0, p, lane, lc, ex, pro);
             if (nchunks > 1)
-                load_raw(R, q, k, v, beta, bos + C, min(C, eos - bos - C), H, h, vt, p, lane);
+                load_raw(R, q, k, v, beta, bos + C, min(C, eos - bos - C), H, h, vt, p, lane, bpad);
         }
         __syncthreads();
         for (int ci = 0; ci < nchunks; ++ci) {
@@ -466,27 +497,27 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             // two chunks ahead), and this chunk's Gram / query-key blocks and
             // diagonal inverses
             if (next) {
-                scan_partials(sm, rg, p, lane, lc, ex);
-                if (next2) load_g(rg, g, c2, min(C, eos - c2), H, h, p, lane);
+                scan_partials<PM>(sm, rg, p, lane, lc, ex, pro);
+                if (next2) load_g(rg, g, c2, min(C, eos - c2), H, h, p, lane, gpad);
             }
             prep_blocks(sm, p, lane);
             __syncthreads();
             // ---- phase B: operands of the next chunk; then fetch the rest of
             // the chunk after it
             if (next) {
-                prologue(sm, R, (ci & 1) ^ 1, p, lane, lc, ex);
-                if (next2) load_raw(R, q, k, v, beta, c2, min(C, eos - c2), H, h, vt, p, lane);
+                build_operands<PM>(sm, R, (ci & 1) ^ 1, p, lane, lc, ex, pro);
+                if (next2) load_raw(R, q, k, v, beta, c2, min(C, eos - c2), H, h, vt, p, lane, bpad);
             }
             __syncthreads();
         }
     }
 }
 
-template <typename TOut>
+template <typename TOut, int PM>
 hipError_t launch_t(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                    const StateIO &io, void *o, const int32_t *cu, int N, int fixedT, int totalT,
-                    int H, hipStream_t stream) {
-    auto kern = chunk_mfma_kernel<TOut>;
+                    const StateIO &io, const Prologue &pro, void *o, const int32_t *cu, int N,
+                    int fixedT, int totalT, int H, hipStream_t stream) {
+    auto kern = chunk_mfma_kernel<TOut, PM>;
     const size_t smem = sizeof(Smem);
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(kern), (int)smem, lds_set);
@@ -496,7 +527,7 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *g, 
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), smem, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), static_cast<const uint16_t *>(g),
-                       static_cast<const uint16_t *>(beta), io, static_cast<TOut *>(o), cu,
+                       static_cast<const uint16_t *>(beta), io, pro, static_cast<TOut *>(o), cu,
                        fixedT, N, H, totalT);
     return hipGetLastError();
 }
@@ -506,12 +537,21 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *g, 
 bool chunk_mfma_supported(int K, int V, int Cc) { return K == KD && V == VD && Cc == C; }
 
 hipError_t launch_chunk_mfma(const void *q, const void *k, const void *v, const void *g,
-                             const void *beta, const StateIO &io, void *o, const int32_t *cu,
-                             int N, int fixedT, int totalT, int H, bool out_bf16,
-                             hipStream_t stream) {
+                             const void *beta, const StateIO &io, const Prologue &pro, void *o,
+                             const int32_t *cu, int N, int fixedT, int totalT, int H,
+                             bool out_bf16, hipStream_t stream) {
     if (N == 0 || H == 0) return hipSuccess;
-    return out_bf16 ? launch_t<bf16_t>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, stream)
-                    : launch_t<float>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, stream);
+    switch (pro_mode(pro)) {
+        case PRO_FULL:
+            return out_bf16 ? launch_t<bf16_t, PRO_FULL>(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, stream)
+                            : launch_t<float, PRO_FULL>(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, stream);
+        case PRO_RUNTIME:
+            return out_bf16 ? launch_t<bf16_t, PRO_RUNTIME>(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, stream)
+                            : launch_t<float, PRO_RUNTIME>(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, stream);
+        default:
+            return out_bf16 ? launch_t<bf16_t, PRO_OFF>(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, stream)
+                            : launch_t<float, PRO_OFF>(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, stream);
+    }
 }
 
 size_t chunk_mfma_smem_bytes() { return sizeof(Smem); }

@@ -32,6 +32,7 @@
 // Pass 3 (chunk_output_kernel): one workgroup per (chunk, head).
 // Intermediates live in the caller's workspace.
 #include "kda_mfma.hpp"
+#include "prologue.hpp"
 #include "state_io.hpp"
 
 namespace kda {
@@ -193,11 +194,12 @@ __device__ __forceinline__ floatx4 block32(const _Float16 *lhs, const _Float16 *
     return acc;
 }
 
+template <int PM>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ g,
     const uint16_t *__restrict__ beta, const int32_t *__restrict__ cu, int fixedT, int N, int H,
-    int totalT, unsigned char *__restrict__ ws) {
+    int totalT, Prologue pro, unsigned char *__restrict__ ws) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     PrepSmem &sm = *reinterpret_cast<PrepSmem *>(smem_raw);
     const ChunkMap cm = chunk_map(cu, fixedT, N, totalT, gridDim.x);
@@ -237,12 +239,14 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) rv[u] = *reinterpret_cast<const uint4 *>(v + off[u]);
     const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+    // padding rows: zeros, and gate logits that map to g = 0
+    const uint32_t gpad = pro_on<PM>(pro, PRO_GATE_LOGIT) ? BF16_NEG_INF_PAIR : 0u;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         if (4 * rg + u >= L) {
             rq[u] = zero4;
             rk[u] = zero4;
-            rgv[u] = zero4;
+            rgv[u] = make_uint4(gpad, gpad, gpad, gpad);
             rv[u] = zero4;
         }
     }
@@ -253,6 +257,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
     float G[4][8], ex[8];
 #pragma unroll
     for (int u = 0; u < 4; ++u) unpack8(rgv[u], G[u]);
+    if (pro_on<PM>(pro, PRO_GATE_LOGIT)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) G[u][e] = gate_from_logit(G[u][e], pro.glb);
+    }
     float sc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -277,7 +287,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
         *reinterpret_cast<floatx4 *>(&sm.gsum[w][8 * cg]) = floatx4{sc[0], sc[1], sc[2], sc[3]};
         *reinterpret_cast<floatx4 *>(&sm.gsum[w][8 * cg + 4]) = floatx4{sc[4], sc[5], sc[6], sc[7]};
     }
-    if (w == 0) sm.beta[t] = t < L ? __uint_as_float((uint32_t)bt_raw << 16) : 0.f;
+    if (w == 0) {
+        float b = __uint_as_float((uint32_t)bt_raw << 16);
+        if (pro_on<PM>(pro, PRO_BETA_LOGIT)) b = sigmoid_f(b);
+        sm.beta[t] = t < L ? b : 0.f;
+    }
     __syncthreads();
 
     // ---- decay factors of this thread's rows and channels (g only):
@@ -324,6 +338,15 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(
             float kv[8], qv[8];
             unpack8(rk[u], kv);
             unpack8(rq[u], qv);
+            if (pro_on<PM>(pro, PRO_NORM_QK)) {  // a row's 128 channels lie in one DPP row
+                const float ik = inv_norm(row16_sum(sumsq8(kv)), pro.eps);
+                const float iq = inv_norm(row16_sum(sumsq8(qv)), pro.eps);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    kv[e] *= ik;
+                    qv[e] *= iq;
+                }
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 kpr[u][e] = (_Float16)(kv[e] * fx[u][e]);
@@ -972,22 +995,26 @@ size_t chunk_split_workspace_bytes(int N, int totalT, int H) {
 }
 
 hipError_t launch_chunk_split(const void *q, const void *k, const void *v, const void *g,
-                              const void *beta, const StateIO &io, void *o, const int32_t *cu,
-                              int N, int fixedT, int totalT, int H, bool out_bf16,
-                              void *workspace, hipStream_t stream) {
+                              const void *beta, const StateIO &io, const Prologue &pro, void *o,
+                              const int32_t *cu, int N, int fixedT, int totalT, int H,
+                              bool out_bf16, void *workspace, hipStream_t stream) {
     if (N == 0 || H == 0) return hipSuccess;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     const int cap = max_chunks(N, totalT, fixedT, cu != nullptr);
     hipError_t e;
     if (cap > 0) {
-        static std::atomic<uint64_t> lds_set{0};
-        e = ensure_dynamic_lds(reinterpret_cast<const void *>(chunk_prep_kernel),
-                               (int)sizeof(PrepSmem), lds_set);
+        static std::atomic<uint64_t> lds_set[3];
+        const int pm = pro_mode(pro);
+        auto kern = pm == PRO_FULL      ? chunk_prep_kernel<PRO_FULL>
+                    : pm == PRO_RUNTIME ? chunk_prep_kernel<PRO_RUNTIME>
+                                        : chunk_prep_kernel<PRO_OFF>;
+        e = ensure_dynamic_lds(reinterpret_cast<const void *>(kern), (int)sizeof(PrepSmem),
+                               lds_set[pm]);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(chunk_prep_kernel, dim3(cap, H), dim3(256), sizeof(PrepSmem), stream,
+        hipLaunchKernelGGL(kern, dim3(cap, H), dim3(256), sizeof(PrepSmem), stream,
                            static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                            static_cast<const uint16_t *>(v), static_cast<const uint16_t *>(g),
-                           static_cast<const uint16_t *>(beta), cu, fixedT, N, H, totalT, ws);
+                           static_cast<const uint16_t *>(beta), cu, fixedT, N, H, totalT, pro, ws);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

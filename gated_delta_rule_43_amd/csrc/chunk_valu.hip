@@ -22,6 +22,7 @@
 // stays in LDS for the whole sequence.  Columns of the state evolve
 // independently, so V-tiles need no communication.
 #include "kda_common.hpp"
+#include "prologue.hpp"
 #include "state_io.hpp"
 
 namespace kda {
@@ -32,11 +33,15 @@ struct ValuSmem {
     static constexpr size_t bytes = sizeof(float) * floats;
 };
 
-template <int K, int V, int C, int VT, int NT, typename TIn, typename TOut>
+// PRO: the input prologue (prologue.hpp) applies, as pro.flags selects.
+template <int K, int V, int C, int VT, int NT, typename TIn, typename TOut, bool PRO>
 __global__ __launch_bounds__(NT) void chunk_valu_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
-    const TIn *__restrict__ g, const TIn *__restrict__ beta, StateIO io,
+    const TIn *__restrict__ g, const TIn *__restrict__ beta, StateIO io, Prologue pro,
     TOut *__restrict__ o, const int32_t *__restrict__ cu, int fixedT, int H, int totalT) {
+    const bool gate_logit = PRO && (pro.flags & PRO_GATE_LOGIT);
+    const bool beta_logit = PRO && (pro.flags & PRO_BETA_LOGIT);
+    const bool norm_qk = PRO && (pro.flags & PRO_NORM_QK);
     extern __shared__ float smem[];
     float *sQ = smem;            // [C][K]
     float *sK = sQ + C * K;      // [C][K]
@@ -71,14 +76,36 @@ __global__ __launch_bounds__(NT) void chunk_valu_kernel(
             const size_t off = ((size_t)(c0 + r) * H + h) * K + c;
             sQ[i] = in ? to_f32(q[off]) : 0.f;
             sK[i] = in ? to_f32(k[off]) : 0.f;
-            sG[i] = in ? to_f32(g[off]) : 0.f;
+            float gv = in ? to_f32(g[off]) : 0.f;
+            if (gate_logit && in) gv = gate_from_logit(gv, pro.glb);
+            sG[i] = gv;
         }
         for (int i = t; i < C * VT; i += NT) {
             const int r = i / VT, c = i % VT;
             sV[i] = r < L ? to_f32(v[((size_t)(c0 + r) * H + h) * V + (size_t)vt * VT + c]) : 0.f;
         }
-        for (int r = t; r < C; r += NT) sB[r] = r < L ? to_f32(beta[(size_t)(c0 + r) * H + h]) : 0.f;
+        for (int r = t; r < C; r += NT) {
+            float b = r < L ? to_f32(beta[(size_t)(c0 + r) * H + h]) : 0.f;
+            if (beta_logit && r < L) b = sigmoid_f(b);
+            sB[r] = b;
+        }
         __syncthreads();
+
+        // Prologue: unit-norm rows of Q and K (padding rows stay zero).
+        if (norm_qk) {
+            for (int r = t; r < C; r += NT) {
+                float sq = 0.f, sk = 0.f;
+                for (int c = 0; c < K; ++c) {
+                    sq += sQ[r * K + c] * sQ[r * K + c];
+                    sk += sK[r * K + c] * sK[r * K + c];
+                }
+                const float iq = inv_norm(sq, pro.eps), ik = inv_norm(sk, pro.eps);
+                for (int c = 0; c < K; ++c) {
+                    sQ[r * K + c] *= iq;
+                    sK[r * K + c] *= ik;
+                }
+            }
+        }
 
         // Running sum of the log-decay per key channel (padding rows add 0).
         for (int c = t; c < K; c += NT) {
@@ -163,13 +190,14 @@ __global__ __launch_bounds__(NT) void chunk_valu_kernel(
     }
 }
 
-template <int K, int V, int C, int VT, typename TIn, typename TOut>
+template <int K, int V, int C, int VT, typename TIn, typename TOut, bool PRO>
 static hipError_t launch_valu_t(const void *q, const void *k, const void *v, const void *g,
-                                const void *beta, const StateIO &io, void *o, const int32_t *cu,
-                                int N, int fixedT, int totalT, int H, hipStream_t stream) {
+                                const void *beta, const StateIO &io, const Prologue &pro, void *o,
+                                const int32_t *cu, int N, int fixedT, int totalT, int H,
+                                hipStream_t stream) {
     constexpr int NT = 256;
     using SM = ValuSmem<K, V, C, VT, NT>;
-    auto kern = chunk_valu_kernel<K, V, C, VT, NT, TIn, TOut>;
+    auto kern = chunk_valu_kernel<K, V, C, VT, NT, TIn, TOut, PRO>;
     if (SM::bytes > 64 * 1024) {
         static std::atomic<uint64_t> lds_set{0};
         hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(kern),
@@ -179,33 +207,45 @@ static hipError_t launch_valu_t(const void *q, const void *k, const void *v, con
     hipLaunchKernelGGL(kern, dim3(V / VT, H, N), dim3(NT), SM::bytes, stream,
                        static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                        static_cast<const TIn *>(v), static_cast<const TIn *>(g),
-                       static_cast<const TIn *>(beta), io, static_cast<TOut *>(o), cu, fixedT,
+                       static_cast<const TIn *>(beta), io, pro, static_cast<TOut *>(o), cu, fixedT,
                        H, totalT);
     return hipGetLastError();
 }
 
+template <int K, int V, int C, int VT, bool PRO>
+static hipError_t launch_valu_pro(const void *q, const void *k, const void *v, const void *g,
+                                  const void *beta, const StateIO &io, const Prologue &pro,
+                                  void *o, const int32_t *cu, int N, int fixedT, int totalT, int H,
+                                  bool in_bf16, bool out_bf16, hipStream_t stream) {
+    if (in_bf16)
+        return out_bf16 ? launch_valu_t<K, V, C, VT, bf16_t, bf16_t, PRO>(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, stream)
+                        : launch_valu_t<K, V, C, VT, bf16_t, float, PRO>(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, stream);
+    return out_bf16 ? launch_valu_t<K, V, C, VT, float, bf16_t, PRO>(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, stream)
+                    : launch_valu_t<K, V, C, VT, float, float, PRO>(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, stream);
+}
+
 template <int K, int V, int C, int VT>
 static hipError_t launch_valu_kvc(const void *q, const void *k, const void *v, const void *g,
-                                  const void *beta, const StateIO &io, void *o, const int32_t *cu,
-                                  int N, int fixedT, int totalT, int H, bool in_bf16,
-                                  bool out_bf16, hipStream_t stream) {
-    if (in_bf16)
-        return out_bf16 ? launch_valu_t<K, V, C, VT, bf16_t, bf16_t>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, stream)
-                        : launch_valu_t<K, V, C, VT, bf16_t, float>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, stream);
-    return out_bf16 ? launch_valu_t<K, V, C, VT, float, bf16_t>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, stream)
-                    : launch_valu_t<K, V, C, VT, float, float>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, stream);
+                                  const void *beta, const StateIO &io, const Prologue &pro,
+                                  void *o, const int32_t *cu, int N, int fixedT, int totalT, int H,
+                                  bool in_bf16, bool out_bf16, hipStream_t stream) {
+    if (pro.flags)
+        return launch_valu_pro<K, V, C, VT, true>(q, k, v, g, beta, io, pro, o, cu, N, fixedT,
+                                                  totalT, H, in_bf16, out_bf16, stream);
+    return launch_valu_pro<K, V, C, VT, false>(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT,
+                                               H, in_bf16, out_bf16, stream);
 }
 
 // Internal launcher.  cu == nullptr means fixed-length sequences of fixedT tokens.
 hipError_t launch_chunk_valu(const void *q, const void *k, const void *v, const void *g,
-                             const void *beta, const StateIO &io, void *o, const int32_t *cu,
-                             int N, int fixedT, int totalT, int H, int K, int V, int C,
-                             bool in_bf16, bool out_bf16, hipStream_t stream) {
+                             const void *beta, const StateIO &io, const Prologue &pro, void *o,
+                             const int32_t *cu, int N, int fixedT, int totalT, int H, int K, int V,
+                             int C, bool in_bf16, bool out_bf16, hipStream_t stream) {
     if (N == 0 || H == 0) return hipSuccess;
     if (K == 32 && V == 32 && C == 16)
-        return launch_valu_kvc<32, 32, 16, 32>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, in_bf16, out_bf16, stream);
+        return launch_valu_kvc<32, 32, 16, 32>(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, in_bf16, out_bf16, stream);
     if (K == 128 && V == 128 && C == 64)
-        return launch_valu_kvc<128, 128, 64, 16>(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, in_bf16, out_bf16, stream);
+        return launch_valu_kvc<128, 128, 64, 16>(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, in_bf16, out_bf16, stream);
     return hipErrorInvalidValue;
 }
 

@@ -21,6 +21,7 @@
 // streaming it past the caches lifts the read+write stream from about 5.0 to
 // 6.7 TB/s on MI355X (non-temporal loads, by contrast, slow it down).
 #include "kda_common.hpp"
+#include "prologue.hpp"
 
 namespace kda {
 
@@ -48,19 +49,56 @@ struct DecodeLds {
 // returns u for its four columns; the new state is s + k_r u on row r.
 // q, k, g point at the token's [K] vectors, v at its [V] vector.  Leaves
 // lds.sk valid for the caller; callers that run another token first pass a
-// barrier (every thread is done reading lds).
-template <int K, int V, int NT, typename TIn, typename TOut>
+// barrier (every thread is done reading lds).  PRO: the input prologue
+// (prologue.hpp) applies as pro.flags selects; wave 0 then normalises q and k
+// (a wave-wide sum of squares) while the other waves fill in the decay.
+template <int K, int V, int NT, typename TIn, typename TOut, bool PRO>
 __device__ __forceinline__ float4 decode_token(float4 *s, const TIn *q, const TIn *k, const TIn *g,
                                                const TIn *beta, const TIn *v, TOut *o,
-                                               DecodeLds<K, V, NT> &lds) {
+                                               DecodeLds<K, V, NT> &lds, const Prologue &pro) {
     using D = DecodeShape<K, V, NT>;
     const int t = threadIdx.x;
     const int cg = t % D::CG, rg = t / D::CG;
     const int lane = t & 63, w = t >> 6;
-    for (int c = t; c < K; c += NT) {
-        lds.sq[c] = to_f32(q[c]);
-        lds.sk[c] = to_f32(k[c]);
-        lds.sa[c] = fast_exp(to_f32(g[c]));
+    const bool gate_logit = PRO && (pro.flags & PRO_GATE_LOGIT);
+    if (PRO && (pro.flags & PRO_NORM_QK)) {
+        if (w == 0) {
+            constexpr int CPL = (K + 63) / 64;  // channels per lane
+            float qv[CPL], kv[CPL], sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = lane + 64 * i;
+                qv[i] = c < K ? to_f32(q[c]) : 0.f;
+                kv[i] = c < K ? to_f32(k[c]) : 0.f;
+                sq += qv[i] * qv[i];
+                sk += kv[i] * kv[i];
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                sq += __shfl_xor(sq, off);
+                sk += __shfl_xor(sk, off);
+            }
+            const float iq = inv_norm(sq, pro.eps), ik = inv_norm(sk, pro.eps);
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = lane + 64 * i;
+                if (c < K) {
+                    lds.sq[c] = qv[i] * iq;
+                    lds.sk[c] = kv[i] * ik;
+                }
+            }
+        }
+        for (int c = t; c < K; c += NT) {
+            const float x = to_f32(g[c]);
+            lds.sa[c] = fast_exp(gate_logit ? gate_from_logit(x, pro.glb) : x);
+        }
+    } else {
+        for (int c = t; c < K; c += NT) {
+            lds.sq[c] = to_f32(q[c]);
+            lds.sk[c] = to_f32(k[c]);
+            const float x = to_f32(g[c]);
+            lds.sa[c] = fast_exp(gate_logit ? gate_from_logit(x, pro.glb) : x);
+        }
     }
     __syncthreads();
     if (w == 0) {
@@ -100,7 +138,8 @@ __device__ __forceinline__ float4 decode_token(float4 *s, const TIn *q, const TI
         RK.x += a.x; RK.y += a.y; RK.z += a.z; RK.w += a.w;
         RQ.x += b.x; RQ.y += b.y; RQ.z += b.z; RQ.w += b.w;
     }
-    const float b = to_f32(beta[0]);
+    float b = to_f32(beta[0]);
+    if (PRO && (pro.flags & PRO_BETA_LOGIT)) b = sigmoid_f(b);
     const TIn *vp = v + 4 * cg;
     float4 u;
     u.x = b * (to_f32(vp[0]) - RK.x);
@@ -137,13 +176,13 @@ __device__ __forceinline__ void store_state(float4 *S, const float4 *s, const fl
 
 // One decode step.  PAGED: the states live in pool slots (slot_in /
 // slot_out); otherwise the unit's own entry of a dense [N, H, K, V] array is
-// updated in place.
-template <int K, int V, int NT, typename TIn, typename TOut, bool PAGED>
+// updated in place.  PRO: with the input prologue.
+template <int K, int V, int NT, typename TIn, typename TOut, bool PAGED, bool PRO>
 __global__ __launch_bounds__(NT) void decode_step_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const TIn *__restrict__ g, const TIn *__restrict__ beta, float *__restrict__ state,
     const int32_t *__restrict__ slot_in, const int32_t *__restrict__ slot_out, int pool_slots,
-    int H, TOut *__restrict__ o) {
+    int H, Prologue pro, TOut *__restrict__ o) {
     using D = DecodeShape<K, V, NT>;
     __shared__ DecodeLds<K, V, NT> lds;
 
@@ -177,8 +216,9 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(
 #pragma unroll
         for (int i = 0; i < D::RPT; ++i) s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    const float4 u = decode_token<K, V, NT, TIn, TOut>(s, q + unit * K, k + unit * K, g + unit * K,
-                                                       beta + unit, v + unit * V, o + unit * V, lds);
+    const float4 u = decode_token<K, V, NT, TIn, TOut, PRO>(s, q + unit * K, k + unit * K,
+                                                            g + unit * K, beta + unit, v + unit * V,
+                                                            o + unit * V, lds, pro);
     if (!PAGED || Sout) store_state<K, V, NT>(Sout, s, u, lds.sk);
 }
 
@@ -187,12 +227,12 @@ __global__ __launch_bounds__(NT) void decode_step_kernel(
 // state is read once from slot_in[n], kept in registers, advanced token by
 // token, and after token j written to slot slot_out[n * T + j] when that slot
 // lies in the pool (so the caller keeps exactly the prefixes it may accept).
-template <int K, int V, int NT, typename TIn, typename TOut>
+template <int K, int V, int NT, typename TIn, typename TOut, bool PRO>
 __global__ __launch_bounds__(NT) void decode_multi_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const TIn *__restrict__ g, const TIn *__restrict__ beta, float *__restrict__ pool,
     const int32_t *__restrict__ slot_in, const int32_t *__restrict__ slot_out, int pool_slots,
-    int T, int H, TOut *__restrict__ o) {
+    int T, int H, Prologue pro, TOut *__restrict__ o) {
     using D = DecodeShape<K, V, NT>;
     __shared__ DecodeLds<K, V, NT> lds;
 
@@ -217,8 +257,9 @@ __global__ __launch_bounds__(NT) void decode_multi_kernel(
     for (int j = 0; j < T; ++j) {
         if (j > 0) __syncthreads();  // every thread is done with the previous token's lds
         const size_t tok = ((size_t)n * T + j) * H + h;
-        const float4 u = decode_token<K, V, NT, TIn, TOut>(s, q + tok * K, k + tok * K, g + tok * K,
-                                                           beta + tok, v + tok * V, o + tok * V, lds);
+        const float4 u = decode_token<K, V, NT, TIn, TOut, PRO>(s, q + tok * K, k + tok * K,
+                                                                g + tok * K, beta + tok, v + tok * V,
+                                                                o + tok * V, lds, pro);
         float4 *Sout = slot_ptr(slot_out[(size_t)n * T + j]);
         if (Sout) store_state<K, V, NT>(Sout, s, u, lds.sk);
         // the new state stays in registers for the next token
@@ -237,35 +278,43 @@ struct DecodeStates {
     int pool_slots;
 };
 
+template <int K, int V, int NT, typename TIn, typename TOut, bool PAGED, bool PRO>
+static void launch_step(const void *q, const void *k, const void *v, const void *g,
+                        const void *beta, const DecodeStates &st, const Prologue &pro, void *o,
+                        int units, int H, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_step_kernel<K, V, NT, TIn, TOut, PAGED, PRO>), dim3(units), dim3(NT),
+                       0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                       static_cast<const TIn *>(v), static_cast<const TIn *>(g),
+                       static_cast<const TIn *>(beta), st.state, PAGED ? st.slot_in : nullptr,
+                       PAGED ? st.slot_out : nullptr, PAGED ? st.pool_slots : 0, H, pro,
+                       static_cast<TOut *>(o));
+}
+
 template <int K, int V, int NT, typename TIn, typename TOut>
 static hipError_t launch_decode_t(const void *q, const void *k, const void *v, const void *g,
-                                  const void *beta, const DecodeStates &st, void *o, int units,
-                                  int H, hipStream_t stream) {
-    if (st.slot_in)
-        hipLaunchKernelGGL((decode_step_kernel<K, V, NT, TIn, TOut, true>), dim3(units), dim3(NT),
-                           0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                           static_cast<const TIn *>(v), static_cast<const TIn *>(g),
-                           static_cast<const TIn *>(beta), st.state, st.slot_in, st.slot_out,
-                           st.pool_slots, H, static_cast<TOut *>(o));
-    else
-        hipLaunchKernelGGL((decode_step_kernel<K, V, NT, TIn, TOut, false>), dim3(units), dim3(NT),
-                           0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                           static_cast<const TIn *>(v), static_cast<const TIn *>(g),
-                           static_cast<const TIn *>(beta), st.state, nullptr, nullptr, 0, H,
-                           static_cast<TOut *>(o));
+                                  const void *beta, const DecodeStates &st, const Prologue &pro,
+                                  void *o, int units, int H, hipStream_t stream) {
+    if (st.slot_in) {
+        if (pro.flags) launch_step<K, V, NT, TIn, TOut, true, true>(q, k, v, g, beta, st, pro, o, units, H, stream);
+        else launch_step<K, V, NT, TIn, TOut, true, false>(q, k, v, g, beta, st, pro, o, units, H, stream);
+    } else {
+        if (pro.flags) launch_step<K, V, NT, TIn, TOut, false, true>(q, k, v, g, beta, st, pro, o, units, H, stream);
+        else launch_step<K, V, NT, TIn, TOut, false, false>(q, k, v, g, beta, st, pro, o, units, H, stream);
+    }
     return hipGetLastError();
 }
 
 template <int K, int V, int NT>
 static hipError_t launch_decode_kv(const void *q, const void *k, const void *v, const void *g,
-                                   const void *beta, const DecodeStates &st, void *o, int units,
-                                   int H, bool in_bf16, bool out_bf16, hipStream_t stream) {
+                                   const void *beta, const DecodeStates &st, const Prologue &pro,
+                                   void *o, int units, int H, bool in_bf16, bool out_bf16,
+                                   hipStream_t stream) {
     if (in_bf16) {
-        return out_bf16 ? launch_decode_t<K, V, NT, bf16_t, bf16_t>(q, k, v, g, beta, st, o, units, H, stream)
-                        : launch_decode_t<K, V, NT, bf16_t, float>(q, k, v, g, beta, st, o, units, H, stream);
+        return out_bf16 ? launch_decode_t<K, V, NT, bf16_t, bf16_t>(q, k, v, g, beta, st, pro, o, units, H, stream)
+                        : launch_decode_t<K, V, NT, bf16_t, float>(q, k, v, g, beta, st, pro, o, units, H, stream);
     }
-    return out_bf16 ? launch_decode_t<K, V, NT, float, bf16_t>(q, k, v, g, beta, st, o, units, H, stream)
-                    : launch_decode_t<K, V, NT, float, float>(q, k, v, g, beta, st, o, units, H, stream);
+    return out_bf16 ? launch_decode_t<K, V, NT, float, bf16_t>(q, k, v, g, beta, st, pro, o, units, H, stream)
+                    : launch_decode_t<K, V, NT, float, float>(q, k, v, g, beta, st, pro, o, units, H, stream);
 }
 
 // Internal launcher: shapes were validated by the caller.  slot_in / slot_out
@@ -273,54 +322,67 @@ static hipError_t launch_decode_kv(const void *q, const void *k, const void *v, 
 // pool of pool_slots slots.
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *g,
                          const void *beta, float *state, const int32_t *slot_in,
-                         const int32_t *slot_out, int pool_slots, void *o, int N, int H, int K,
-                         int V, bool in_bf16, bool out_bf16, hipStream_t stream) {
+                         const int32_t *slot_out, int pool_slots, const Prologue &pro, void *o,
+                         int N, int H, int K, int V, bool in_bf16, bool out_bf16,
+                         hipStream_t stream) {
     const int units = N * H;
     if (units == 0) return hipSuccess;
     const DecodeStates st{state, slot_in, slot_out, pool_slots};
     if (K == 128 && V == 128)
-        return launch_decode_kv<128, 128, 256>(q, k, v, g, beta, st, o, units, H, in_bf16, out_bf16, stream);
+        return launch_decode_kv<128, 128, 256>(q, k, v, g, beta, st, pro, o, units, H, in_bf16, out_bf16, stream);
     if (K == 32 && V == 32)
-        return launch_decode_kv<32, 32, 64>(q, k, v, g, beta, st, o, units, H, in_bf16, out_bf16, stream);
+        return launch_decode_kv<32, 32, 64>(q, k, v, g, beta, st, pro, o, units, H, in_bf16, out_bf16, stream);
     return hipErrorInvalidValue;
 }
 
+struct MultiArgs {
+    float *pool;
+    const int32_t *slot_in, *slot_out;
+    int pool_slots, N, T, H;
+};
+
 template <int K, int V, int NT, typename TIn, typename TOut>
 static hipError_t launch_multi_t(const void *q, const void *k, const void *v, const void *g,
-                                 const void *beta, float *pool, const int32_t *slot_in,
-                                 const int32_t *slot_out, int pool_slots, void *o, int N, int T,
-                                 int H, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_multi_kernel<K, V, NT, TIn, TOut>), dim3(N * H), dim3(NT), 0, stream,
-                       static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                       static_cast<const TIn *>(v), static_cast<const TIn *>(g),
-                       static_cast<const TIn *>(beta), pool, slot_in, slot_out, pool_slots, T, H,
-                       static_cast<TOut *>(o));
+                                 const void *beta, const MultiArgs &a, const Prologue &pro,
+                                 void *o, hipStream_t stream) {
+    if (pro.flags)
+        hipLaunchKernelGGL((decode_multi_kernel<K, V, NT, TIn, TOut, true>), dim3(a.N * a.H), dim3(NT),
+                           0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                           static_cast<const TIn *>(v), static_cast<const TIn *>(g),
+                           static_cast<const TIn *>(beta), a.pool, a.slot_in, a.slot_out,
+                           a.pool_slots, a.T, a.H, pro, static_cast<TOut *>(o));
+    else
+        hipLaunchKernelGGL((decode_multi_kernel<K, V, NT, TIn, TOut, false>), dim3(a.N * a.H), dim3(NT),
+                           0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                           static_cast<const TIn *>(v), static_cast<const TIn *>(g),
+                           static_cast<const TIn *>(beta), a.pool, a.slot_in, a.slot_out,
+                           a.pool_slots, a.T, a.H, pro, static_cast<TOut *>(o));
     return hipGetLastError();
 }
 
 template <int K, int V, int NT>
 static hipError_t launch_multi_kv(const void *q, const void *k, const void *v, const void *g,
-                                  const void *beta, float *pool, const int32_t *slot_in,
-                                  const int32_t *slot_out, int pool_slots, void *o, int N, int T,
-                                  int H, bool in_bf16, bool out_bf16, hipStream_t stream) {
+                                  const void *beta, const MultiArgs &a, const Prologue &pro,
+                                  void *o, bool in_bf16, bool out_bf16, hipStream_t stream) {
     if (in_bf16)
-        return out_bf16 ? launch_multi_t<K, V, NT, bf16_t, bf16_t>(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o, N, T, H, stream)
-                        : launch_multi_t<K, V, NT, bf16_t, float>(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o, N, T, H, stream);
-    return out_bf16 ? launch_multi_t<K, V, NT, float, bf16_t>(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o, N, T, H, stream)
-                    : launch_multi_t<K, V, NT, float, float>(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o, N, T, H, stream);
+        return out_bf16 ? launch_multi_t<K, V, NT, bf16_t, bf16_t>(q, k, v, g, beta, a, pro, o, stream)
+                        : launch_multi_t<K, V, NT, bf16_t, float>(q, k, v, g, beta, a, pro, o, stream);
+    return out_bf16 ? launch_multi_t<K, V, NT, float, bf16_t>(q, k, v, g, beta, a, pro, o, stream)
+                    : launch_multi_t<K, V, NT, float, float>(q, k, v, g, beta, a, pro, o, stream);
 }
 
 // Internal launcher of the multi-token step: shapes were validated by the caller.
 hipError_t launch_decode_multi(const void *q, const void *k, const void *v, const void *g,
                                const void *beta, float *pool, const int32_t *slot_in,
-                               const int32_t *slot_out, int pool_slots, void *o, int N, int T,
-                               int H, int K, int V, bool in_bf16, bool out_bf16,
-                               hipStream_t stream) {
+                               const int32_t *slot_out, int pool_slots, const Prologue &pro,
+                               void *o, int N, int T, int H, int K, int V, bool in_bf16,
+                               bool out_bf16, hipStream_t stream) {
     if (N == 0 || T == 0) return hipSuccess;
+    const MultiArgs a{pool, slot_in, slot_out, pool_slots, N, T, H};
     if (K == 128 && V == 128)
-        return launch_multi_kv<128, 128, 256>(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o, N, T, H, in_bf16, out_bf16, stream);
+        return launch_multi_kv<128, 128, 256>(q, k, v, g, beta, a, pro, o, in_bf16, out_bf16, stream);
     if (K == 32 && V == 32)
-        return launch_multi_kv<32, 32, 64>(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o, N, T, H, in_bf16, out_bf16, stream);
+        return launch_multi_kv<32, 32, 64>(q, k, v, g, beta, a, pro, o, in_bf16, out_bf16, stream);
     return hipErrorInvalidValue;
 }
 

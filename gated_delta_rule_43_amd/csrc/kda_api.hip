@@ -6,37 +6,40 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cmath>
 #include <cstdint>
 
 #include "../../include/kda.h"
+#include "prologue.hpp"
 #include "state_io.hpp"
 
 namespace kda {
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *g,
                          const void *beta, float *state, const int32_t *slot_in,
-                         const int32_t *slot_out, int pool_slots, void *o, int N, int H, int K,
-                         int V, bool in_bf16, bool out_bf16, hipStream_t stream);
+                         const int32_t *slot_out, int pool_slots, const Prologue &pro, void *o,
+                         int N, int H, int K, int V, bool in_bf16, bool out_bf16,
+                         hipStream_t stream);
 hipError_t launch_decode_multi(const void *q, const void *k, const void *v, const void *g,
                                const void *beta, float *pool, const int32_t *slot_in,
-                               const int32_t *slot_out, int pool_slots, void *o, int N, int T,
-                               int H, int K, int V, bool in_bf16, bool out_bf16,
-                               hipStream_t stream);
+                               const int32_t *slot_out, int pool_slots, const Prologue &pro,
+                               void *o, int N, int T, int H, int K, int V, bool in_bf16,
+                               bool out_bf16, hipStream_t stream);
 hipError_t launch_chunk_valu(const void *q, const void *k, const void *v, const void *g,
-                             const void *beta, const StateIO &io, void *o, const int32_t *cu,
-                             int N, int fixedT, int totalT, int H, int K, int V, int C,
-                             bool in_bf16, bool out_bf16, hipStream_t stream);
+                             const void *beta, const StateIO &io, const Prologue &pro, void *o,
+                             const int32_t *cu, int N, int fixedT, int totalT, int H, int K, int V,
+                             int C, bool in_bf16, bool out_bf16, hipStream_t stream);
 hipError_t launch_chunk_mfma(const void *q, const void *k, const void *v, const void *g,
-                             const void *beta, const StateIO &io, void *o, const int32_t *cu,
-                             int N, int fixedT, int totalT, int H, bool out_bf16,
-                             hipStream_t stream);
+                             const void *beta, const StateIO &io, const Prologue &pro, void *o,
+                             const int32_t *cu, int N, int fixedT, int totalT, int H,
+                             bool out_bf16, hipStream_t stream);
 bool chunk_mfma_supported(int K, int V, int C);
 bool chunk_split_supported(int N, int H, int K, int V, int C);
 bool chunk_split_recommended(int N, int totalT, int H, int K, int V, int C);
 size_t chunk_split_workspace_bytes(int N, int totalT, int H);
 hipError_t launch_chunk_split(const void *q, const void *k, const void *v, const void *g,
-                              const void *beta, const StateIO &io, void *o, const int32_t *cu,
-                              int N, int fixedT, int totalT, int H, bool out_bf16,
-                              void *workspace, hipStream_t stream);
+                              const void *beta, const StateIO &io, const Prologue &pro, void *o,
+                              const int32_t *cu, int N, int fixedT, int totalT, int H,
+                              bool out_bf16, void *workspace, hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -54,6 +57,23 @@ bool fits(long long rows, long long H, long long D) {
 }
 
 kda_status_t from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+// Range checks of the prologue's scalars.  chunk > 0 with bf16 inputs: the
+// gate's lower bound must keep the chunked kernels' fp16 decay factors in
+// range (g_lb * chunk / 2 <= 8).
+kda_status_t make_prologue(unsigned flags, float glb, float eps, kda_dtype_t in_dtype, int chunk,
+                           kda::Prologue &pro) {
+    if (flags & ~kda::PRO_ALL) return KDA_ERR_VALUE;
+    if (!std::isfinite(eps) || eps < 0.f) return KDA_ERR_VALUE;
+    if (flags & kda::PRO_GATE_LOGIT) {
+        if (!std::isfinite(glb) || glb < 0.f) return KDA_ERR_VALUE;
+        if (chunk > 0 && in_dtype == KDA_BF16 && (double)glb * chunk > 16.0) return KDA_ERR_VALUE;
+    }
+    pro.flags = flags;
+    pro.glb = glb;
+    pro.eps = eps;
+    return KDA_OK;
+}
 
 kda_status_t validate_fwd(const void *q, const void *k, const void *v, const void *g,
                           const void *beta, const void *o, int N, int totalT, int H, int K,
@@ -81,21 +101,21 @@ kda_status_t check_workspace(const void *workspace, size_t workspace_bytes, size
 }
 
 kda_status_t run_fwd(const void *q, const void *k, const void *v, const void *g,
-                     const void *beta, const kda::StateIO &io, void *o, const int32_t *cu,
-                     int N, int fixedT, int totalT, int H, int K, int V, int chunk,
-                     kda_dtype_t in_dtype, kda_dtype_t out_dtype, void *workspace,
+                     const void *beta, const kda::StateIO &io, const kda::Prologue &pro, void *o,
+                     const int32_t *cu, int N, int fixedT, int totalT, int H, int K, int V,
+                     int chunk, kda_dtype_t in_dtype, kda_dtype_t out_dtype, void *workspace,
                      bool two_pass, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool in_bf16 = in_dtype == KDA_BF16, out_bf16 = out_dtype == KDA_BF16;
     hipError_t e;
     if (in_bf16 && two_pass && kda::chunk_split_supported(N, H, K, V, chunk))
-        e = kda::launch_chunk_split(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, out_bf16,
-                                    workspace, st);
+        e = kda::launch_chunk_split(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H,
+                                    out_bf16, workspace, st);
     else if (in_bf16 && kda::chunk_mfma_supported(K, V, chunk))
-        e = kda::launch_chunk_mfma(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, out_bf16,
-                                   st);
+        e = kda::launch_chunk_mfma(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H,
+                                   out_bf16, st);
     else
-        e = kda::launch_chunk_valu(q, k, v, g, beta, io, o, cu, N, fixedT, totalT, H, K, V,
+        e = kda::launch_chunk_valu(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, K, V,
                                    chunk, in_bf16, out_bf16, st);
     return from_hip(e);
 }
@@ -116,7 +136,7 @@ bool pool_ok(int pool_slots, int H, int K, int V) {
 
 extern "C" {
 
-int kda_version(void) { return 102; }
+int kda_version(void) { return 103; }
 
 const char *kda_status_str(kda_status_t s) {
     switch (s) {
@@ -127,6 +147,7 @@ const char *kda_status_str(kda_status_t s) {
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: (K, V, chunk) or dtype not supported";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace too small";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error";
+        case KDA_ERR_VALUE: return "KDA_ERR_VALUE: scalar argument out of range";
     }
     return "KDA_ERR_UNKNOWN";
 }
@@ -142,16 +163,20 @@ size_t kda_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk) {
     return kda::chunk_split_workspace_bytes(N, total_T, H);
 }
 
-kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
-                           const void *beta, const float *s0, void *o, float *sT, int B,
-                           int T, int H, int K, int V, int chunk, kda_dtype_t in_dtype,
-                           kda_dtype_t out_dtype, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+kda_status_t kda_chunk_fwd_prologue(const void *q, const void *k, const void *v, const void *g,
+                                    const void *beta, const float *s0, void *o, float *sT, int B,
+                                    int T, int H, int K, int V, int chunk, kda_dtype_t in_dtype,
+                                    kda_dtype_t out_dtype, void *workspace,
+                                    size_t workspace_bytes, unsigned prologue,
+                                    float gate_lower_bound, float norm_eps, void *stream) {
     if (B < 0 || T < 0) return KDA_ERR_SHAPE;
     const long long total = (long long)B * T;
     if (total > INT_MAX) return KDA_ERR_SHAPE;
     kda_status_t s = validate_fwd(q, k, v, g, beta, o, B, (int)total, H, K, V, chunk, in_dtype,
                                   out_dtype);
+    if (s != KDA_OK) return s;
+    kda::Prologue pro;
+    s = make_prologue(prologue, gate_lower_bound, norm_eps, in_dtype, chunk, pro);
     if (s != KDA_OK) return s;
     bool two_pass;
     s = check_workspace(workspace, workspace_bytes,
@@ -159,17 +184,31 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
     if (s != KDA_OK) return s;
     if (B == 0) return KDA_OK;
     if (T == 0 && !sT) return KDA_OK;
-    return run_fwd(q, k, v, g, beta, dense_states(s0, sT), o, nullptr, B, T, (int)total, H, K, V,
-                   chunk, in_dtype, out_dtype, workspace, two_pass, stream);
+    return run_fwd(q, k, v, g, beta, dense_states(s0, sT), pro, o, nullptr, B, T, (int)total, H,
+                   K, V, chunk, in_dtype, out_dtype, workspace, two_pass, stream);
 }
 
-kda_status_t kda_varlen_fwd(const void *q, const void *k, const void *v, const void *g,
-                            const void *beta, const float *s0, void *o, float *sT,
-                            const int32_t *cu_seqlens, int N, int total_T, int H, int K, int V,
-                            int chunk, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
-                            void *workspace, size_t workspace_bytes, void *stream) {
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, const float *s0, void *o, float *sT, int B,
+                           int T, int H, int K, int V, int chunk, kda_dtype_t in_dtype,
+                           kda_dtype_t out_dtype, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    return kda_chunk_fwd_prologue(q, k, v, g, beta, s0, o, sT, B, T, H, K, V, chunk, in_dtype,
+                                  out_dtype, workspace, workspace_bytes, 0u, 0.f, 0.f, stream);
+}
+
+kda_status_t kda_varlen_fwd_prologue(const void *q, const void *k, const void *v, const void *g,
+                                     const void *beta, const float *s0, void *o, float *sT,
+                                     const int32_t *cu_seqlens, int N, int total_T, int H, int K,
+                                     int V, int chunk, kda_dtype_t in_dtype,
+                                     kda_dtype_t out_dtype, void *workspace,
+                                     size_t workspace_bytes, unsigned prologue,
+                                     float gate_lower_bound, float norm_eps, void *stream) {
     kda_status_t s = validate_fwd(q, k, v, g, beta, o, N, total_T, H, K, V, chunk, in_dtype,
                                   out_dtype);
+    if (s != KDA_OK) return s;
+    kda::Prologue pro;
+    s = make_prologue(prologue, gate_lower_bound, norm_eps, in_dtype, chunk, pro);
     if (s != KDA_OK) return s;
     if (N > 0 && !cu_seqlens) return KDA_ERR_NULL;
     bool two_pass;
@@ -177,20 +216,32 @@ kda_status_t kda_varlen_fwd(const void *q, const void *k, const void *v, const v
                         kda_two_pass_workspace_bytes(N, total_T, H, K, V, chunk), two_pass);
     if (s != KDA_OK) return s;
     if (N == 0) return KDA_OK;
-    return run_fwd(q, k, v, g, beta, dense_states(s0, sT), o, cu_seqlens, N, 0, total_T, H, K, V,
-                   chunk, in_dtype, out_dtype, workspace, two_pass, stream);
+    return run_fwd(q, k, v, g, beta, dense_states(s0, sT), pro, o, cu_seqlens, N, 0, total_T, H,
+                   K, V, chunk, in_dtype, out_dtype, workspace, two_pass, stream);
 }
 
-kda_status_t kda_varlen_fwd_paged(const void *q, const void *k, const void *v, const void *g,
-                                  const void *beta, float *pool, int pool_slots,
-                                  const int32_t *s0_slot, const int32_t *sT_slot,
-                                  const int32_t *start_pos, const int32_t *block_table,
-                                  int table_stride, int snap_tokens, int page_tokens, void *o,
-                                  const int32_t *cu_seqlens, int N, int total_T, int H, int K,
-                                  int V, int chunk, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
-                                  void *workspace, size_t workspace_bytes, void *stream) {
+kda_status_t kda_varlen_fwd(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const float *s0, void *o, float *sT,
+                            const int32_t *cu_seqlens, int N, int total_T, int H, int K, int V,
+                            int chunk, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    return kda_varlen_fwd_prologue(q, k, v, g, beta, s0, o, sT, cu_seqlens, N, total_T, H, K, V,
+                                   chunk, in_dtype, out_dtype, workspace, workspace_bytes, 0u,
+                                   0.f, 0.f, stream);
+}
+
+kda_status_t kda_varlen_fwd_paged_prologue(
+    const void *q, const void *k, const void *v, const void *g, const void *beta, float *pool,
+    int pool_slots, const int32_t *s0_slot, const int32_t *sT_slot, const int32_t *start_pos,
+    const int32_t *block_table, int table_stride, int snap_tokens, int page_tokens, void *o,
+    const int32_t *cu_seqlens, int N, int total_T, int H, int K, int V, int chunk,
+    kda_dtype_t in_dtype, kda_dtype_t out_dtype, void *workspace, size_t workspace_bytes,
+    unsigned prologue, float gate_lower_bound, float norm_eps, void *stream) {
     kda_status_t s = validate_fwd(q, k, v, g, beta, o, N, total_T, H, K, V, chunk, in_dtype,
                                   out_dtype);
+    if (s != KDA_OK) return s;
+    kda::Prologue pro;
+    s = make_prologue(prologue, gate_lower_bound, norm_eps, in_dtype, chunk, pro);
     if (s != KDA_OK) return s;
     if (!pool) return KDA_ERR_NULL;
     if (!pool_ok(pool_slots, H, K, V)) return KDA_ERR_SHAPE;
@@ -219,21 +270,71 @@ kda_status_t kda_varlen_fwd_paged(const void *q, const void *k, const void *v, c
     }
     io.start_pos = start_pos;
     io.pool_slots = pool_slots;
-    return run_fwd(q, k, v, g, beta, io, o, cu_seqlens, N, 0, total_T, H, K, V, chunk, in_dtype,
-                   out_dtype, workspace, two_pass, stream);
+    return run_fwd(q, k, v, g, beta, io, pro, o, cu_seqlens, N, 0, total_T, H, K, V, chunk,
+                   in_dtype, out_dtype, workspace, two_pass, stream);
+}
+
+kda_status_t kda_varlen_fwd_paged(const void *q, const void *k, const void *v, const void *g,
+                                  const void *beta, float *pool, int pool_slots,
+                                  const int32_t *s0_slot, const int32_t *sT_slot,
+                                  const int32_t *start_pos, const int32_t *block_table,
+                                  int table_stride, int snap_tokens, int page_tokens, void *o,
+                                  const int32_t *cu_seqlens, int N, int total_T, int H, int K,
+                                  int V, int chunk, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    return kda_varlen_fwd_paged_prologue(q, k, v, g, beta, pool, pool_slots, s0_slot, sT_slot,
+                                         start_pos, block_table, table_stride, snap_tokens,
+                                         page_tokens, o, cu_seqlens, N, total_T, H, K, V, chunk,
+                                         in_dtype, out_dtype, workspace, workspace_bytes, 0u, 0.f,
+                                         0.f, stream);
+}
+
+kda_status_t kda_decode_step_prologue(const void *q, const void *k, const void *v, const void *g,
+                                      const void *beta, float *state, void *o, int N, int H,
+                                      int K, int V, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                                      unsigned prologue, float gate_lower_bound, float norm_eps,
+                                      void *stream) {
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
+    if (N < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_SHAPE;
+    if (!fits(N, H, (long long)K * V)) return KDA_ERR_SHAPE;
+    if (!((K == 128 && V == 128) || (K == 32 && V == 32))) return KDA_ERR_UNSUPPORTED;
+    kda::Prologue pro;
+    kda_status_t s = make_prologue(prologue, gate_lower_bound, norm_eps, in_dtype, 0, pro);
+    if (s != KDA_OK) return s;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
+    return from_hip(kda::launch_decode(q, k, v, g, beta, state, nullptr, nullptr, 0, pro, o, N,
+                                       H, K, V, in_dtype == KDA_BF16, out_dtype == KDA_BF16,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g,
                              const void *beta, float *state, void *o, int N, int H, int K,
                              int V, kda_dtype_t in_dtype, kda_dtype_t out_dtype, void *stream) {
+    return kda_decode_step_prologue(q, k, v, g, beta, state, o, N, H, K, V, in_dtype, out_dtype,
+                                    0u, 0.f, 0.f, stream);
+}
+
+kda_status_t kda_decode_step_paged_prologue(const void *q, const void *k, const void *v,
+                                            const void *g, const void *beta, float *pool,
+                                            int pool_slots, const int32_t *slot_in,
+                                            const int32_t *slot_out, void *o, int N, int H,
+                                            int K, int V, kda_dtype_t in_dtype,
+                                            kda_dtype_t out_dtype, unsigned prologue,
+                                            float gate_lower_bound, float norm_eps,
+                                            void *stream) {
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
     if (N < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_SHAPE;
     if (!fits(N, H, (long long)K * V)) return KDA_ERR_SHAPE;
     if (!((K == 128 && V == 128) || (K == 32 && V == 32))) return KDA_ERR_UNSUPPORTED;
+    if (!pool_ok(pool_slots, H, K, V)) return KDA_ERR_SHAPE;
+    kda::Prologue pro;
+    kda_status_t s = make_prologue(prologue, gate_lower_bound, norm_eps, in_dtype, 0, pro);
+    if (s != KDA_OK) return s;
     if (N == 0) return KDA_OK;
-    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
-    return from_hip(kda::launch_decode(q, k, v, g, beta, state, nullptr, nullptr, 0, o, N, H, K,
-                                       V, in_dtype == KDA_BF16, out_dtype == KDA_BF16,
+    if (!q || !k || !v || !g || !beta || !pool || !slot_in || !slot_out || !o) return KDA_ERR_NULL;
+    return from_hip(kda::launch_decode(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, pro,
+                                       o, N, H, K, V, in_dtype == KDA_BF16, out_dtype == KDA_BF16,
                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -242,16 +343,32 @@ kda_status_t kda_decode_step_paged(const void *q, const void *k, const void *v, 
                                    const int32_t *slot_in, const int32_t *slot_out, void *o,
                                    int N, int H, int K, int V, kda_dtype_t in_dtype,
                                    kda_dtype_t out_dtype, void *stream) {
+    return kda_decode_step_paged_prologue(q, k, v, g, beta, pool, pool_slots, slot_in, slot_out,
+                                          o, N, H, K, V, in_dtype, out_dtype, 0u, 0.f, 0.f,
+                                          stream);
+}
+
+kda_status_t kda_decode_multi_paged_prologue(const void *q, const void *k, const void *v,
+                                             const void *g, const void *beta, float *pool,
+                                             int pool_slots, const int32_t *slot_in,
+                                             const int32_t *slot_out, void *o, int N, int T,
+                                             int H, int K, int V, kda_dtype_t in_dtype,
+                                             kda_dtype_t out_dtype, unsigned prologue,
+                                             float gate_lower_bound, float norm_eps,
+                                             void *stream) {
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
-    if (N < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_SHAPE;
-    if (!fits(N, H, (long long)K * V)) return KDA_ERR_SHAPE;
+    if (N < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_SHAPE;
+    if (!fits((long long)N * T, H, K > V ? K : V)) return KDA_ERR_SHAPE;
     if (!((K == 128 && V == 128) || (K == 32 && V == 32))) return KDA_ERR_UNSUPPORTED;
     if (!pool_ok(pool_slots, H, K, V)) return KDA_ERR_SHAPE;
-    if (N == 0) return KDA_OK;
+    kda::Prologue pro;
+    kda_status_t s = make_prologue(prologue, gate_lower_bound, norm_eps, in_dtype, 0, pro);
+    if (s != KDA_OK) return s;
+    if (N == 0 || T == 0) return KDA_OK;
     if (!q || !k || !v || !g || !beta || !pool || !slot_in || !slot_out || !o) return KDA_ERR_NULL;
-    return from_hip(kda::launch_decode(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots, o,
-                                       N, H, K, V, in_dtype == KDA_BF16, out_dtype == KDA_BF16,
-                                       static_cast<hipStream_t>(stream)));
+    return from_hip(kda::launch_decode_multi(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots,
+                                             pro, o, N, T, H, K, V, in_dtype == KDA_BF16,
+                                             out_dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
 }
 
 kda_status_t kda_decode_multi_paged(const void *q, const void *k, const void *v, const void *g,
@@ -259,16 +376,9 @@ kda_status_t kda_decode_multi_paged(const void *q, const void *k, const void *v,
                                     const int32_t *slot_in, const int32_t *slot_out, void *o,
                                     int N, int T, int H, int K, int V, kda_dtype_t in_dtype,
                                     kda_dtype_t out_dtype, void *stream) {
-    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
-    if (N < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return KDA_ERR_SHAPE;
-    if (!fits((long long)N * T, H, K > V ? K : V)) return KDA_ERR_SHAPE;
-    if (!((K == 128 && V == 128) || (K == 32 && V == 32))) return KDA_ERR_UNSUPPORTED;
-    if (!pool_ok(pool_slots, H, K, V)) return KDA_ERR_SHAPE;
-    if (N == 0 || T == 0) return KDA_OK;
-    if (!q || !k || !v || !g || !beta || !pool || !slot_in || !slot_out || !o) return KDA_ERR_NULL;
-    return from_hip(kda::launch_decode_multi(q, k, v, g, beta, pool, slot_in, slot_out, pool_slots,
-                                             o, N, T, H, K, V, in_dtype == KDA_BF16,
-                                             out_dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
+    return kda_decode_multi_paged_prologue(q, k, v, g, beta, pool, pool_slots, slot_in, slot_out,
+                                           o, N, T, H, K, V, in_dtype, out_dtype, 0u, 0.f, 0.f,
+                                           stream);
 }
 
 }  // extern "C"

@@ -10,18 +10,44 @@ from __future__ import annotations
 
 import ctypes
 import os
+from dataclasses import dataclass
+from typing import Optional
 
 import torch
 
 __all__ = ["chunk_fwd", "varlen_fwd", "decode_step", "varlen_fwd_paged", "decode_step_paged",
-           "decode_multi_paged",
+           "decode_multi_paged", "Prologue",
            "workspace_bytes",
            "two_pass_workspace_bytes", "library",
            "KdaError", "LIB_PATH", "F32", "BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 F32, BF16 = 0, 1
+PROLOGUE_NORM_QK, PROLOGUE_GATE_LOGIT, PROLOGUE_BETA_LOGIT = 1, 2, 4
 _lib = None
+
+
+@dataclass(frozen=True)
+class Prologue:
+    """Input prologue of the *_prologue entry points (kda.h): the kernels take raw
+    projections and apply, while loading,
+      normalize_qk:     q, k <- x (sum x^2 + norm_eps)^-1/2 per (token, head);
+      gate_lower_bound: g holds logits x and g = -gate_lower_bound * sigmoid(x)
+                        (None: g is the decay itself);
+      beta_logits:      beta holds logits b and beta = sigmoid(b)."""
+    normalize_qk: bool = False
+    gate_lower_bound: Optional[float] = None
+    beta_logits: bool = False
+    norm_eps: float = 0.0
+
+    def flags(self) -> int:
+        return ((PROLOGUE_NORM_QK if self.normalize_qk else 0)
+                | (PROLOGUE_GATE_LOGIT if self.gate_lower_bound is not None else 0)
+                | (PROLOGUE_BETA_LOGIT if self.beta_logits else 0))
+
+    def args(self):
+        glb = 0.0 if self.gate_lower_bound is None else float(self.gate_lower_bound)
+        return (ctypes.c_uint(self.flags()), ctypes.c_float(glb), ctypes.c_float(self.norm_eps))
 
 
 class KdaError(RuntimeError):
@@ -59,6 +85,14 @@ def library():
     lib.kda_decode_multi_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                            i32, i32, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_multi_paged.restype = i32
+    # the *_prologue variants: the same arguments, then (flags, gate_lower_bound,
+    # norm_eps) before the stream
+    u32, f32 = ctypes.c_uint, ctypes.c_float
+    for name in ("kda_chunk_fwd", "kda_varlen_fwd", "kda_varlen_fwd_paged", "kda_decode_step",
+                 "kda_decode_step_paged", "kda_decode_multi_paged"):
+        fn = getattr(lib, name + "_prologue")
+        fn.argtypes = getattr(lib, name).argtypes[:-1] + [u32, f32, f32, vp]
+        fn.restype = i32
     lib.kda_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.kda_workspace_bytes.restype = sz
     lib.kda_two_pass_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -74,7 +108,7 @@ def library():
 def _check(fn: str, status: int):
     if status != 0:
         msg = library().kda_status_str(status).decode()
-        if status in (1, 2, 3, 4, 5):
+        if status in (1, 2, 3, 4, 5, 7):
             raise ValueError(f"{fn}: {msg}")
         raise KdaError(fn, status, msg)
 
@@ -107,6 +141,18 @@ def _default_chunk(K: int) -> int:
 
 def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _call(name, prologue, *args):
+    """Call entry point `name`, or its _prologue variant when a prologue is given;
+    args end with the stream."""
+    lib = library()
+    if prologue is None:
+        st = getattr(lib, name)(*args)
+    else:
+        name = name + "_prologue"
+        st = getattr(lib, name)(*args[:-1], *prologue.args(), args[-1])
+    _check(name, st)
 
 
 def workspace_bytes(N: int, total_T: int, H: int, K: int, V: int, chunk: int) -> int:
@@ -146,7 +192,7 @@ def _workspace(dev, N, total, H, K, V, chunk, two_pass, workspace):
 
 def chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, chunk=None,
               out_dtype=torch.float32, final_state=None, out=None, two_pass=None,
-              workspace=None):
+              workspace=None, prologue=None):
     """Chunked KDA forward over a fixed-length batch.
 
     q, k, g: [B, T, H, K]; v: [B, T, H, V]; beta: [B, T, H]; all float32 or all bfloat16.
@@ -158,6 +204,7 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, chu
     when kda_workspace_bytes is nonzero: few (sequence, head) units, long
     sequences); True forces the two-pass path, False the single-pass kernels.
     workspace: optional preallocated uint8 tensor.
+    prologue: a Prologue (raw q/k, gate and beta logits), or None.
     """
     _need_gpu(q, k, v, g, beta, initial_state, final_state, out)
     B, T, H, K = q.shape
@@ -179,23 +226,21 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, chu
     if sT is None and output_final_state:
         sT = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
     ws, nws = _workspace(dev, B, B * T, H, K, V, chunk, two_pass, workspace)
-    st = library().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                 _ptr(initial_state), _ptr(o), _ptr(sT),
-                                 B, T, H, K, V, chunk, _dtype_code(dt), _dtype_code(o.dtype),
-                                 _ptr(ws), nws, _stream(dev))
-    _check("kda_chunk_fwd", st)
+    _call("kda_chunk_fwd", prologue, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+          _ptr(initial_state), _ptr(o), _ptr(sT), B, T, H, K, V, chunk, _dtype_code(dt),
+          _dtype_code(o.dtype), _ptr(ws), nws, _stream(dev))
     return o, sT
 
 
 def varlen_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, output_final_state=True,
                chunk=None, out_dtype=torch.float32, final_state=None, out=None, two_pass=None,
-               workspace=None):
+               workspace=None, prologue=None):
     """Chunked KDA forward over packed sequences.
 
     q, k, g: [total_T, H, K]; v: [total_T, H, V]; beta: [total_T, H];
     cu_seqlens: int32 [N + 1] on the GPU.  initial_state: [N, H, K, V] float32 or None.
     Returns (o [total_T, H, V], final states [N, H, K, V] or None).
-    two_pass, workspace: as for chunk_fwd.
+    two_pass, workspace, prologue: as for chunk_fwd.
     """
     _need_gpu(q, k, v, g, beta, cu_seqlens, initial_state, final_state, out)
     total, H, K = q.shape
@@ -220,17 +265,16 @@ def varlen_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, output_final_st
     if sT is None and output_final_state:
         sT = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
     ws, nws = _workspace(dev, N, total, H, K, V, chunk, two_pass, workspace)
-    st = library().kda_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                  _ptr(initial_state), _ptr(o), _ptr(sT), _ptr(cu_seqlens),
-                                  N, total, H, K, V, chunk, _dtype_code(dt),
-                                  _dtype_code(o.dtype), _ptr(ws), nws, _stream(dev))
-    _check("kda_varlen_fwd", st)
+    _call("kda_varlen_fwd", prologue, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+          _ptr(initial_state), _ptr(o), _ptr(sT), _ptr(cu_seqlens), N, total, H, K, V, chunk,
+          _dtype_code(dt), _dtype_code(o.dtype), _ptr(ws), nws, _stream(dev))
     return o, sT
 
 
-def decode_step(q, k, v, g, beta, state, out_dtype=torch.float32, out=None):
+def decode_step(q, k, v, g, beta, state, out_dtype=torch.float32, out=None, prologue=None):
     """One recurrent step: q, k, g [N, H, K]; v [N, H, V]; beta [N, H];
-    state [N, H, K, V] float32, updated in place.  Returns o [N, H, V]."""
+    state [N, H, K, V] float32, updated in place.  Returns o [N, H, V].
+    prologue: as for chunk_fwd."""
     _need_gpu(q, k, v, g, beta, state, out)
     N, H, K = q.shape
     V = v.shape[-1]
@@ -242,10 +286,9 @@ def decode_step(q, k, v, g, beta, state, out_dtype=torch.float32, out=None):
     if state.dtype != torch.float32 or state.shape != (N, H, K, V):
         raise ValueError("state must be float32 [N, H, K, V]")
     o = out if out is not None else torch.empty((N, H, V), dtype=out_dtype, device=q.device)
-    st = library().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                                   _ptr(o), N, H, K, V, _dtype_code(dt), _dtype_code(o.dtype),
-                                   _stream(q.device))
-    _check("kda_decode_step", st)
+    _call("kda_decode_step", prologue, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+          _ptr(state), _ptr(o), N, H, K, V, _dtype_code(dt), _dtype_code(o.dtype),
+          _stream(q.device))
     return o
 
 
@@ -266,12 +309,13 @@ def _pool_check(pool, H, K, V):
 def varlen_fwd_paged(q, k, v, g, beta, cu_seqlens, pool, s0_slot=None, sT_slot=None,
                      start_pos=None, block_table=None, snap_tokens=512, page_tokens=6144,
                      chunk=None, out_dtype=torch.float32, out=None, two_pass=None,
-                     workspace=None):
+                     workspace=None, prologue=None):
     """kda_varlen_fwd_paged: packed sequences whose states live in a pool.
 
     pool: float32 [slots, H, K, V]; s0_slot, sT_slot, start_pos: int32 [N] or None;
     block_table: int32 [N, blocks] (physical page of each page_tokens block) or None
     for no snapshots.  Returns o [total_T, H, V]; states and snapshots land in pool.
+    prologue: as for chunk_fwd.
     """
     _need_gpu(q, k, v, g, beta, cu_seqlens, pool, s0_slot, sT_slot, start_pos, block_table, out)
     total, H, K = q.shape
@@ -298,20 +342,19 @@ def varlen_fwd_paged(q, k, v, g, beta, cu_seqlens, pool, s0_slot=None, sT_slot=N
     if o.shape != (total, H, V):
         raise ValueError("out must be [total_T, H, V]")
     ws, nws = _workspace(dev, N, total, H, K, V, chunk, two_pass, workspace)
-    st = library().kda_varlen_fwd_paged(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(pool), slots, _ptr(s0_slot),
-        _ptr(sT_slot), _ptr(start_pos), _ptr(block_table), stride, snap_tokens, page_tokens,
-        _ptr(o), _ptr(cu_seqlens), N, total, H, K, V, chunk, _dtype_code(dt),
-        _dtype_code(o.dtype), _ptr(ws), nws, _stream(dev))
-    _check("kda_varlen_fwd_paged", st)
+    _call("kda_varlen_fwd_paged", prologue,
+          _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(pool), slots, _ptr(s0_slot),
+          _ptr(sT_slot), _ptr(start_pos), _ptr(block_table), stride, snap_tokens, page_tokens,
+          _ptr(o), _ptr(cu_seqlens), N, total, H, K, V, chunk, _dtype_code(dt),
+          _dtype_code(o.dtype), _ptr(ws), nws, _stream(dev))
     return o
 
 
 def decode_step_paged(q, k, v, g, beta, pool, slot_in, slot_out, out_dtype=torch.float32,
-                      out=None):
+                      out=None, prologue=None):
     """kda_decode_step_paged: one step for N sequences whose states live in a pool
     (float32 [slots, H, K, V]); sequence n reads slot_in[n] and writes slot_out[n]
-    (int32 [N] each).  Returns o [N, H, V]."""
+    (int32 [N] each).  Returns o [N, H, V].  prologue: as for chunk_fwd."""
     _need_gpu(q, k, v, g, beta, pool, slot_in, slot_out, out)
     N, H, K = q.shape
     V = v.shape[-1]
@@ -324,20 +367,18 @@ def decode_step_paged(q, k, v, g, beta, pool, slot_in, slot_out, out_dtype=torch
     _slots(slot_in, N, "slot_in")
     _slots(slot_out, N, "slot_out")
     o = out if out is not None else torch.empty((N, H, V), dtype=out_dtype, device=q.device)
-    st = library().kda_decode_step_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                         _ptr(pool), slots, _ptr(slot_in), _ptr(slot_out),
-                                         _ptr(o), N, H, K, V, _dtype_code(dt),
-                                         _dtype_code(o.dtype), _stream(q.device))
-    _check("kda_decode_step_paged", st)
+    _call("kda_decode_step_paged", prologue, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+          _ptr(pool), slots, _ptr(slot_in), _ptr(slot_out), _ptr(o), N, H, K, V,
+          _dtype_code(dt), _dtype_code(o.dtype), _stream(q.device))
     return o
 
 
 def decode_multi_paged(q, k, v, g, beta, pool, slot_in, slot_out, out_dtype=torch.float32,
-                       out=None):
+                       out=None, prologue=None):
     """kda_decode_multi_paged: T tokens per sequence in one pass (draft verification).
     q, k, g [N, T, H, K]; v [N, T, H, V]; beta [N, T, H]; pool float32 [slots, H, K, V];
     slot_in int32 [N]; slot_out int32 [N, T] (state after token j, -1: not kept).
-    Returns o [N, T, H, V]."""
+    Returns o [N, T, H, V].  prologue: as for chunk_fwd."""
     _need_gpu(q, k, v, g, beta, pool, slot_in, slot_out, out)
     N, T, H, K = q.shape
     V = v.shape[-1]
@@ -351,9 +392,7 @@ def decode_multi_paged(q, k, v, g, beta, pool, slot_in, slot_out, out_dtype=torc
     if slot_out.dtype != torch.int32 or slot_out.shape != (N, T):
         raise ValueError("slot_out must be int32 [N, T]")
     o = out if out is not None else torch.empty((N, T, H, V), dtype=out_dtype, device=q.device)
-    st = library().kda_decode_multi_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                          _ptr(pool), slots, _ptr(slot_in), _ptr(slot_out),
-                                          _ptr(o), N, T, H, K, V, _dtype_code(dt),
-                                          _dtype_code(o.dtype), _stream(q.device))
-    _check("kda_decode_multi_paged", st)
+    _call("kda_decode_multi_paged", prologue, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+          _ptr(beta), _ptr(pool), slots, _ptr(slot_in), _ptr(slot_out), _ptr(o), N, T, H, K, V,
+          _dtype_code(dt), _dtype_code(o.dtype), _stream(q.device))
     return o

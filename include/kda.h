@@ -70,7 +70,9 @@ typedef enum {
     KDA_ERR_DTYPE = 3,       /* unknown dtype enum                             */
     KDA_ERR_UNSUPPORTED = 4, /* (K, V, chunk) or dtype combination not built   */
     KDA_ERR_WORKSPACE = 5,   /* workspace smaller than kda_workspace_bytes()   */
-    KDA_ERR_HIP = 6          /* the HIP runtime reported an error              */
+    KDA_ERR_HIP = 6,         /* the HIP runtime reported an error              */
+    KDA_ERR_VALUE = 7        /* a scalar argument out of its range (prologue
+                                flags, gate lower bound, normalisation eps)    */
 } kda_status_t;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
@@ -213,6 +215,82 @@ kda_status_t kda_decode_multi_paged(const void *q, const void *k, const void *v,
                                     const int32_t *slot_in, const int32_t *slot_out, void *o,
                                     int N, int T, int H, int K, int V, kda_dtype_t in_dtype,
                                     kda_dtype_t out_dtype, void *stream);
+
+/*
+ * Input prologue.  The same section describes KDA's decay as lower-bounded
+ * and its gate as channel-wise; the parameterisation taken here computes the
+ * decay from gate logits x as g = -g_lb * sigmoid(x), which keeps g in
+ * [-g_lb, 0], beta as sigmoid(b) of beta logits, and feeds the recurrence
+ * L2-normalised queries and keys.  The *_prologue entry points take those
+ * raw projections and apply the selected maps inside the kernels' input
+ * loads, in fp32, so that a model layer needs no separate elementwise passes
+ * (the bytes moved are the same).  prologue is a bitwise OR of:
+ *   KDA_PROLOGUE_NORM_QK    q and k are raw: every [K] vector of q and of k
+ *                           is scaled by (sum of its squares + norm_eps)^-1/2
+ *                           (a vector whose sum is 0 stays 0);
+ *   KDA_PROLOGUE_GATE_LOGIT g holds logits x; the decay used is
+ *                           g = -gate_lower_bound * sigmoid(x);
+ *   KDA_PROLOGUE_BETA_LOGIT beta holds logits b; the value used is sigmoid(b).
+ * prologue = 0 is the plain entry point.  Range checks (KDA_ERR_VALUE):
+ * unknown bits; norm_eps negative or not finite; with GATE_LOGIT,
+ * gate_lower_bound negative or not finite, or, for bf16 inputs of a chunked
+ * call, gate_lower_bound * chunk > 16 (the numerical precondition above).
+ * Everything else (shapes, layouts, states, workspace, errors) is as for the
+ * entry point of the same name without the suffix.
+ */
+typedef enum {
+    KDA_PROLOGUE_NORM_QK = 1,
+    KDA_PROLOGUE_GATE_LOGIT = 2,
+    KDA_PROLOGUE_BETA_LOGIT = 4
+} kda_prologue_flags_t;
+
+kda_status_t kda_chunk_fwd_prologue(const void *q, const void *k, const void *v, const void *g,
+                                    const void *beta, const float *s0, void *o, float *sT,
+                                    int B, int T, int H, int K, int V, int chunk,
+                                    kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                                    void *workspace, size_t workspace_bytes,
+                                    unsigned prologue, float gate_lower_bound, float norm_eps,
+                                    void *stream);
+
+kda_status_t kda_varlen_fwd_prologue(const void *q, const void *k, const void *v, const void *g,
+                                     const void *beta, const float *s0, void *o, float *sT,
+                                     const int32_t *cu_seqlens, int N, int total_T, int H, int K,
+                                     int V, int chunk, kda_dtype_t in_dtype,
+                                     kda_dtype_t out_dtype, void *workspace,
+                                     size_t workspace_bytes, unsigned prologue,
+                                     float gate_lower_bound, float norm_eps, void *stream);
+
+kda_status_t kda_varlen_fwd_paged_prologue(
+    const void *q, const void *k, const void *v, const void *g, const void *beta, float *pool,
+    int pool_slots, const int32_t *s0_slot, const int32_t *sT_slot, const int32_t *start_pos,
+    const int32_t *block_table, int table_stride, int snap_tokens, int page_tokens, void *o,
+    const int32_t *cu_seqlens, int N, int total_T, int H, int K, int V, int chunk,
+    kda_dtype_t in_dtype, kda_dtype_t out_dtype, void *workspace, size_t workspace_bytes,
+    unsigned prologue, float gate_lower_bound, float norm_eps, void *stream);
+
+kda_status_t kda_decode_step_prologue(const void *q, const void *k, const void *v, const void *g,
+                                      const void *beta, float *state, void *o, int N, int H,
+                                      int K, int V, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                                      unsigned prologue, float gate_lower_bound, float norm_eps,
+                                      void *stream);
+
+kda_status_t kda_decode_step_paged_prologue(const void *q, const void *k, const void *v,
+                                            const void *g, const void *beta, float *pool,
+                                            int pool_slots, const int32_t *slot_in,
+                                            const int32_t *slot_out, void *o, int N, int H,
+                                            int K, int V, kda_dtype_t in_dtype,
+                                            kda_dtype_t out_dtype, unsigned prologue,
+                                            float gate_lower_bound, float norm_eps,
+                                            void *stream);
+
+kda_status_t kda_decode_multi_paged_prologue(const void *q, const void *k, const void *v,
+                                             const void *g, const void *beta, float *pool,
+                                             int pool_slots, const int32_t *slot_in,
+                                             const int32_t *slot_out, void *o, int N, int T,
+                                             int H, int K, int V, kda_dtype_t in_dtype,
+                                             kda_dtype_t out_dtype, unsigned prologue,
+                                             float gate_lower_bound, float norm_eps,
+                                             void *stream);
 
 /* Workspace bytes for the recommended implementation of a forward call over
  * N sequences, total_T tokens: nonzero (the two-pass size) when the two-pass

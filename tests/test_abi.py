@@ -31,7 +31,10 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kda_chunk_fwd", "kda_varlen_fwd", "kda_decode_step", "kda_varlen_fwd_paged",
               "kda_decode_step_paged", "kda_decode_multi_paged", "kda_workspace_bytes",
-              "kda_two_pass_workspace_bytes", "kda_status_str", "kda_version"):
+              "kda_two_pass_workspace_bytes", "kda_status_str", "kda_version",
+              "kda_chunk_fwd_prologue", "kda_varlen_fwd_prologue",
+              "kda_varlen_fwd_paged_prologue", "kda_decode_step_prologue",
+              "kda_decode_step_paged_prologue", "kda_decode_multi_paged_prologue"):
         assert n in names
 
 
@@ -41,11 +44,12 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(7):
+    for code in range(8):
         s = lib.kda_status_str(code).decode()
         assert s.startswith("KDA_")
+    assert lib.kda_status_str(7).decode().startswith("KDA_ERR_VALUE")
     assert lib.kda_status_str(99).decode() == "KDA_ERR_UNKNOWN"
-    assert lib.kda_version() == 102
+    assert lib.kda_version() == 103
 
 
 def two_pass_size(N, total, H):
@@ -183,3 +187,55 @@ def test_multi_decode_argument_errors(lib):
     assert call(T=0, null=0) == 0       # nothing to do: no pointer is needed
     for i in range(9):
         assert call(null=i) == 1
+
+
+def pro_args(flags, glb=0.25, eps=0.0):
+    return ctypes.c_uint(flags), ctypes.c_float(glb), ctypes.c_float(eps)
+
+
+def chunk_pro(lib, flags, glb=0.25, eps=0.0, *, C=64, K=128, ind=1, B=1, ws=0):
+    # ws = 1: an undersized workspace, the check that follows the prologue's
+    # (so a call whose prologue is accepted still fails, with KDA_ERR_WORKSPACE)
+    return lib.kda_chunk_fwd_prologue(*[FAKE] * 8, B, 64, 1, K, K, C, ind, 0,
+                                      FAKE if ws else None, ws, *pro_args(flags, glb, eps), None)
+
+
+def test_prologue_argument_errors(lib):
+    nan, inf = float("nan"), float("inf")
+    assert chunk_pro(lib, 8) == 7                             # unknown flag bit
+    assert chunk_pro(lib, 1 << 31) == 7
+    assert chunk_pro(lib, 1, eps=-1e-6) == 7                  # negative eps
+    assert chunk_pro(lib, 1, eps=nan) == 7
+    assert chunk_pro(lib, 0, eps=inf) == 7
+    assert chunk_pro(lib, 2, glb=-0.1) == 7                   # negative gate bound
+    assert chunk_pro(lib, 2, glb=nan) == 7
+    assert chunk_pro(lib, 2, glb=0.26) == 7                   # bf16, chunk 64: g_lb * 64 <= 16
+    assert chunk_pro(lib, 2, glb=1.01, C=16, K=32) == 7       # bf16, chunk 16: g_lb <= 1
+    assert chunk_pro(lib, 2, glb=2.0, ind=0, ws=1) == 5       # fp32 inputs: any finite bound
+    assert chunk_pro(lib, 5, glb=100.0, ws=1) == 5            # bound unused without the gate map
+    assert chunk_pro(lib, 7, glb=0.25, eps=1e-6, ws=1) == 5   # the largest bf16 bound at chunk 64
+    assert chunk_pro(lib, 7, B=-1) == 2                       # shapes are checked first
+    v = lib.kda_varlen_fwd_prologue
+    assert v(*[FAKE] * 9, 2, 10, 1, 128, 128, 64, 1, 0, None, 0, *pro_args(16), None) == 7
+    vp = lib.kda_varlen_fwd_paged_prologue
+    assert vp(*[FAKE] * 6, 4, None, None, None, None, 0, 512, 6144, FAKE, FAKE, 2, 10, 1,
+              128, 128, 64, 1, 0, None, 0, *pro_args(2, glb=0.5), None) == 7
+    d = lib.kda_decode_step_prologue
+    assert d(*[FAKE] * 7, 4, 2, 128, 128, 1, 0, *pro_args(2, glb=-1.0), None) == 7
+    assert d(*[FAKE] * 7, 4, 2, 128, 128, 1, 0, *pro_args(64), None) == 7
+    dp = lib.kda_decode_step_paged_prologue
+    assert dp(*[FAKE] * 6, 8, FAKE, FAKE, FAKE, 4, 2, 128, 128, 1, 0,
+              *pro_args(1, eps=-1.0), None) == 7
+    dm = lib.kda_decode_multi_paged_prologue
+    assert dm(*[FAKE] * 6, 8, FAKE, FAKE, FAKE, 4, 3, 2, 128, 128, 1, 0,
+              *pro_args(9), None) == 7
+    # decode has no chunk: a large gate bound is accepted (N = 0: nothing to launch)
+    assert d(*[FAKE] * 7, 0, 2, 128, 128, 1, 0, *pro_args(2, glb=5.0), None) == 0
+
+
+def test_binding_prologue_flags():
+    assert kda.Prologue().flags() == 0
+    assert kda.Prologue(normalize_qk=True).flags() == 1
+    assert kda.Prologue(gate_lower_bound=0.25).flags() == 2
+    assert kda.Prologue(beta_logits=True).flags() == 4
+    assert kda.Prologue(True, 0.25, True, 1e-6).flags() == 7

@@ -1,0 +1,240 @@
+"""GPU parity of the input prologue (the *_prologue entry points of kda.h):
+raw q and k, gate logits and beta logits go in, and the kernels' results must
+match the oracle's prologue followed by its recurrence, to the same bounds as
+the plain entry points (1e-4 for fp32 inputs, 2e-2 for bf16)."""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_43_amd import inputs, kda
+from oracle import oracle
+from tests.parity import TOL, rel_err, report, to_gpu
+from tests.test_gpu_paged import _expected_paged_fwd, _pool
+
+pytestmark = pytest.mark.gpu
+
+G_LB = 0.25  # the largest gate bound the bf16 chunked kernels accept at chunk 64
+ALL = 7
+
+
+def _prologue(flags, eps=0.0, glb=G_LB):
+    return kda.Prologue(normalize_qk=bool(flags & 1), gate_lower_bound=glb if flags & 2 else None,
+                        beta_logits=bool(flags & 4), norm_eps=eps)
+
+
+def _mix(raw, plain, flags):
+    """Inputs for a prologue with the given flags: raw tensors where a map is
+    selected, ready-made ones (unit q/k, decay g, beta in (0, 1)) elsewhere."""
+    d = dict(raw)
+    if not flags & 1:
+        d["q"], d["k"] = plain["q"], plain["k"]
+    if not flags & 2:
+        d["g"] = plain["g"]
+    if not flags & 4:
+        d["beta"] = plain["beta"]
+    return d
+
+
+def _oracle_inputs(d, p):
+    q, k, g, b = oracle.prologue(d["q"], d["k"], d["g"], d["beta"], normalize_qk=p.normalize_qk,
+                                 gate_lower_bound=p.gate_lower_bound, beta_logits=p.beta_logits,
+                                 norm_eps=p.norm_eps)
+    return dict(q=q, k=k, v=oracle.as_f64(d["v"]), g=g, beta=b)
+
+
+# (dtype, K, two_pass, flags): both bf16 d=128 kernels with every map, each
+# map alone on the single-pass kernel, and the fp32-arithmetic kernel
+CASES = [("bf16", 128, True, ALL), ("bf16", 128, False, ALL), ("bf16", 128, False, 1),
+         ("bf16", 128, False, 2), ("bf16", 128, False, 4), ("bf16", 128, True, 1),
+         ("bf16", 32, None, ALL), ("f32", 32, None, ALL), ("f32", 128, None, ALL)]
+
+
+@pytest.mark.parametrize("dtype,K,two_pass,flags", CASES)
+def test_prologue_chunk_fwd(dtype, K, two_pass, flags):
+    B, H = 2, 3
+    T = 150 if (dtype == "f32" and K == 128) else 300
+    print(f"[case] prologue chunk_fwd {dtype} K={K} two_pass={two_pass} flags={flags} "
+          f"B={B} T={T} H={H}", flush=True)
+    raw = inputs.draw_raw_fixed(60, B, T, H, K, K, dtype, s0_std=0.1)
+    plain = inputs.draw_fixed(61, B, T, H, K, K, dtype, g_lb=G_LB)
+    d = _mix(raw, plain, flags)
+    p = _prologue(flags, eps=1e-6 if flags & 1 else 0.0)
+    r = _oracle_inputs(d, p)
+    o_ref, s_ref = oracle.fixed(r["q"], r["k"], r["v"], r["g"], r["beta"], oracle.as_f64(d["s0"]))
+    x = to_gpu(d)
+    o, sT = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], initial_state=x["s0"],
+                          two_pass=two_pass, prologue=p)
+    torch.cuda.synchronize()
+    eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+    report(f"prologue_chunk_{dtype}_K{K}_{two_pass}_f{flags}", o=eo, sT=es)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("two_pass", [True, False])
+def test_prologue_varlen_edge_lengths(two_pass):
+    """Empty, single-token, chunk-edge and ragged sequences: the padding rows of
+    a partial chunk must add nothing even though a zero gate logit or beta logit
+    would map to a nonzero value."""
+    lengths = [0, 1, 63, 64, 65, 200, 0, 130]
+    H, K = 2, 128
+    print(f"[case] prologue varlen two_pass={two_pass} lengths={lengths}", flush=True)
+    d = inputs.draw_raw_varlen(62, H, K, K, "bf16", lengths, s0_std=0.1)
+    p = _prologue(ALL)
+    r = _oracle_inputs(d, p)
+    cu = d["cu_seqlens"].numpy().astype(np.int64)
+    o_ref, s_ref = oracle.recurrence(r["q"], r["k"], r["v"], r["g"], r["beta"], cu,
+                                     oracle.as_f64(d["s0"]))
+    x = to_gpu(d)
+    o, sT = kda.varlen_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"],
+                           initial_state=x["s0"], two_pass=two_pass, prologue=p)
+    torch.cuda.synchronize()
+    eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+    report(f"prologue_varlen_{two_pass}", o=eo, sT=es)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_prologue_zero_rows_and_eps():
+    """Zero q and k rows stay zero (eps = 0: the map sends them to 0, not NaN)."""
+    B, T, H, K = 1, 130, 2, 128
+    print("[case] prologue zero rows, eps=0", flush=True)
+    d = inputs.draw_raw_fixed(63, B, T, H, K, K, "bf16")
+    d["q"][0, 5] = 0
+    d["k"][0, 70:75] = 0
+    p = _prologue(ALL, eps=0.0)
+    r = _oracle_inputs(d, p)
+    o_ref, s_ref = oracle.fixed(r["q"], r["k"], r["v"], r["g"], r["beta"])
+    x = to_gpu(d)
+    for tp in (True, False):
+        o, sT = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], two_pass=tp, prologue=p)
+        torch.cuda.synchronize()
+        eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+        report(f"prologue_zero_rows_{tp}", o=eo, sT=es)
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,K,two_pass", [("bf16", 128, True), ("bf16", 128, False),
+                                              ("f32", 32, None)])
+def test_prologue_paged_prefill(dtype, K, two_pass):
+    C = 16 if K == 32 else 64
+    f = C / 64
+    snap, page = int(256 * f), int(1024 * f)
+    lengths = [int(700 * f), int(337 * f), 0]
+    start = [0, int(1536 * f), int(512 * f)]
+    H = 2
+    table = [[2, -1], [-1, 0], [-1, -1]]
+    s0_slot, sT_slot, slots = [-1, 12, 13], [14, 12, 15], 16
+    print(f"[case] prologue paged prefill {dtype} K={K} two_pass={two_pass}", flush=True)
+    d = inputs.draw_raw_varlen(64, H, K, K, dtype, lengths)
+    p = _prologue(ALL)
+    r = _oracle_inputs(d, p)
+    cu = d["cu_seqlens"].numpy().astype(np.int64)
+    pool0 = _pool(65, slots, H, K, K)
+    o_ref, s_ref, snaps = _expected_paged_fwd(r, cu, pool0, s0_slot, start, table, snap, page)
+    assert len(snaps) == 3
+    x = to_gpu(d)
+    pool = pool0.cuda()
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    o = kda.varlen_fwd_paged(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"], pool,
+                             s0_slot=i32(s0_slot), sT_slot=i32(sT_slot), start_pos=i32(start),
+                             block_table=i32(table), snap_tokens=snap, page_tokens=page,
+                             two_pass=two_pass, prologue=p)
+    torch.cuda.synchronize()
+    errs = {"o": rel_err(o, o_ref)}
+    for n in range(3):
+        errs[f"sT{n}"] = rel_err(pool[sT_slot[n]], s_ref[n])
+    for slot, ref in snaps.items():
+        errs[f"snap{slot}"] = rel_err(pool[slot], ref)
+    report(f"prologue_paged_{dtype}_K{K}_{two_pass}", **errs)
+    assert all(e <= TOL[dtype] for e in errs.values()), errs
+
+
+@pytest.mark.parametrize("dtype,K", [("bf16", 128), ("f32", 128), ("bf16", 32)])
+def test_prologue_decode_steps(dtype, K):
+    """Dense decode steps with every map, against the oracle step by step."""
+    N, H, steps = 5, 3, 6
+    print(f"[case] prologue decode {dtype} K={K} N={N} H={H} steps={steps}", flush=True)
+    state0 = inputs.draw_decode_state(66, N, H, K, K, 0.1)
+    st = state0.cuda()
+    ref = oracle.as_f64(state0)
+    p = _prologue(ALL, eps=1e-6)
+    worst = 0.0
+    for s in range(steps):
+        d = inputs.draw_raw_varlen(67 + s, H, K, K, dtype, [1] * N)
+        r = _oracle_inputs(d, p)
+        o_ref, ref = oracle.decode_step(r["q"], r["k"], r["v"], r["g"], r["beta"], ref)
+        x = to_gpu(d)
+        o = kda.decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], st, prologue=p)
+        torch.cuda.synchronize()
+        worst = max(worst, rel_err(o, o_ref))
+    es = rel_err(st, ref)
+    report(f"prologue_decode_{dtype}_K{K}", o=worst, state=es)
+    assert worst <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("K", [128, 32])
+def test_prologue_paged_and_multi_decode(K):
+    """Paged single step and the multi-token step with every map: T = 3 draft
+    tokens per sequence, each intermediate state kept."""
+    N, T, H = 3, 3, 2
+    slots = 12
+    print(f"[case] prologue paged/multi decode K={K} N={N} T={T}", flush=True)
+    pool0 = _pool(70, slots, H, K, K)
+    p = _prologue(ALL)
+    d = inputs.draw_raw_varlen(71, H, K, K, "bf16", [T] * N)
+    r = _oracle_inputs(d, p)
+    slot_in = [0, -1, 1]
+    slot_out = [[2, 3, 4], [5, 6, 7], [8, 9, 1]]
+    cu = np.arange(N + 1) * T
+    s0 = np.zeros((N, H, K, K))
+    for n in range(N):
+        if slot_in[n] >= 0:
+            s0[n] = pool0[slot_in[n]].double().numpy()
+    o_ref, _ = oracle.recurrence(r["q"], r["k"], r["v"], r["g"], r["beta"], cu, s0)
+    ref_states = {}
+    for n in range(N):
+        for j in range(T):
+            sl = {kk: r[kk][n * T:n * T + j + 1] for kk in ("q", "k", "v", "g", "beta")}
+            _, sj = oracle.recurrence(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"],
+                                      np.array([0, j + 1]), s0[n:n + 1])
+            ref_states[slot_out[n][j]] = sj[0]
+    x = to_gpu(d)
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    shp = lambda t, D: t.reshape(N, T, H, D) if D else t.reshape(N, T, H)
+    pool = pool0.cuda()
+    o = kda.decode_multi_paged(shp(x["q"], K), shp(x["k"], K), shp(x["v"], K), shp(x["g"], K),
+                               shp(x["beta"], 0), pool, i32(slot_in), i32(slot_out), prologue=p)
+    torch.cuda.synchronize()
+    errs = {"o": rel_err(o.reshape(N * T, H, K), o_ref)}
+    for slot, ref in ref_states.items():
+        errs[f"s{slot}"] = rel_err(pool[slot], ref)
+    # the paged single step on the first draft token reproduces the multi step's first state
+    pool2 = pool0.cuda()
+    o1 = kda.decode_step_paged(shp(x["q"], K)[:, 0].contiguous(), shp(x["k"], K)[:, 0].contiguous(),
+                               shp(x["v"], K)[:, 0].contiguous(), shp(x["g"], K)[:, 0].contiguous(),
+                               shp(x["beta"], 0)[:, 0].contiguous(), pool2, i32(slot_in),
+                               i32([s[0] for s in slot_out]), prologue=p)
+    torch.cuda.synchronize()
+    report(f"prologue_multi_decode_K{K}", **errs)
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
+    assert torch.equal(o1, o[:, 0])
+    for n in range(N):
+        assert torch.equal(pool2[slot_out[n][0]], pool[slot_out[n][0]])
+
+
+def test_prologue_prefill_full_size():
+    """The prefill workload (B=1, H=8, T=4096, d=128, bf16) with every map on the
+    two-pass path, whole tensors against the oracle."""
+    B, T, H, K = 1, 4096, 8, 128
+    print(f"[case] prologue full-size prefill B={B} T={T} H={H}", flush=True)
+    d = inputs.draw_raw_fixed(72, B, T, H, K, K, "bf16")
+    p = _prologue(ALL, eps=1e-6)
+    r = _oracle_inputs(d, p)
+    o_ref, s_ref = oracle.fixed(r["q"], r["k"], r["v"], r["g"], r["beta"])
+    x = to_gpu(d)
+    for tp in (True, False):
+        o, sT = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], two_pass=tp, prologue=p)
+        torch.cuda.synchronize()
+        eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+        report(f"prologue_full_size_{tp}", o=eo, sT=es)
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
