@@ -138,6 +138,51 @@ def prologue(q, k, g, beta, normalize_qk: bool = False, gate_lower_bound=None,
     return q, k, g, beta
 
 
+def backward(q, k, v, g, beta, cu_seqlens, s0, do, dsT):
+    """Gradients of the recurrence, in fp64: for the scalar loss
+        L = sum(do * o) + sum(dsT * sT)
+    returns (dq, dk, dv, dg, dbeta, ds0) with the shapes of q, k, v, g, beta and
+    of the states [N, H, K, V].  The recurrence is the one of
+    kda_oracle.c (section "Hybrid Attention Mechanism" of "Kimi K3: Open
+    Frontier Intelligence and Implementation Framework": the delta rule with a
+    channel-wise forget gate), written here as a plain token loop in torch fp64
+    on the CPU, one sequence at a time with its heads as a batch, and
+    differentiated by torch.autograd (no chunking, no hand-derived gradient).
+    s0 and dsT may be None (zeros).  Memory grows with tokens * H * K * V:
+    meant for test-sized inputs."""
+    import torch
+    q, k, v, g, beta, do = (as_f64(x) for x in (q, k, v, g, beta, do))
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    tokens, H, K = q.shape
+    V = v.shape[-1]
+    N = len(cu) - 1
+    s0 = np.zeros((N, H, K, V)) if s0 is None else as_f64(s0)
+    dsT = np.zeros((N, H, K, V)) if dsT is None else as_f64(dsT)
+    outs = [np.zeros_like(x) for x in (q, k, v, g, beta)] + [np.zeros((N, H, K, V))]
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        ts = [torch.tensor(x[a:b], dtype=torch.float64, requires_grad=True)
+              for x in (q, k, v, g, beta)]
+        S0 = torch.tensor(s0[n], dtype=torch.float64, requires_grad=True)
+        tq, tk, tv, tg, tb = ts
+        S = S0
+        loss = torch.zeros((), dtype=torch.float64)
+        dO = torch.tensor(do[a:b], dtype=torch.float64)
+        for t in range(b - a):
+            S = torch.exp(tg[t])[:, :, None] * S                        # Diag(alpha_t) S
+            e = tv[t] - torch.einsum("hkv,hk->hv", S, tk[t])            # v_t - S^T k_t
+            S = S + tb[t][:, None, None] * tk[t][:, :, None] * e[:, None, :]
+            o = torch.einsum("hkv,hk->hv", S, tq[t])                    # S_t^T q_t
+            loss = loss + (o * dO[t]).sum()
+        loss = loss + (S * torch.tensor(dsT[n], dtype=torch.float64)).sum()
+        loss.backward()
+        for i, x in enumerate(ts):
+            if x.grad is not None:          # None for an empty sequence
+                outs[i][a:b] = x.grad.numpy()
+        outs[5][n] = S0.grad.numpy()
+    return tuple(outs)
+
+
 def decode_step(q, k, v, g, beta, state, nthreads: int | None = None):
     """One token per sequence: q, k, g [N, H, K]; v [N, H, V]; beta [N, H];
     state [N, H, K, V] fp64.  Returns (o [N, H, V], new state)."""
