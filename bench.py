@@ -55,6 +55,15 @@ def prefill_alg_flops(B, T, H, K, V, C):
     return B * T * H * (per_chunk / C + 6 * K * V)
 
 
+def bwd_alg_bytes(B, T, H, K, V, in_bytes=2):
+    """Algorithmic HBM bytes of one backward call: q, k, v, g, beta read once,
+    do (fp32) read once, dq, dk, dv, dg, dbeta (fp32) written once, dsT read and
+    ds0 written (fp32 states)."""
+    th = B * T * H
+    return (th * ((3 * K + V) * in_bytes + in_bytes + V * 4 + (3 * K + V) * 4 + 4)
+            + 2 * B * H * K * V * 4)
+
+
 def decode_alg_bytes(N, H, K, V, in_bytes=2, out_bytes=4):
     """State read + written (2 K V 4), q, k, g, v, beta read, o written."""
     return N * H * (2 * K * V * 4 + (3 * K + V + 1) * in_bytes + V * out_bytes)
@@ -220,7 +229,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--prefill-workload", default=PREFILL,
                     choices=["prefill_bf16_B1_H8_T4096", "batched_bf16_B4_H32_T8192"])
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward"], default=None,
                     help="profiling mode: launch only this kernel --steps times and print "
                          "nothing else (copy = a 512 MiB device copy for counter calibration)")
     args = ap.parse_args()
@@ -274,6 +283,15 @@ def main():
         kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], chunk=w.chunk,
                       final_state=sT, out=o, two_pass=False)
 
+    if args.only == "backward":
+        do = torch.randn(w.B, w.T, w.H, w.V, device=dev)
+        for _ in range(args.steps):
+            kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, initial_state=x["s0"],
+                          chunk=w.chunk)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "backward", "workload": w.name, "launches": args.steps}),
+              flush=True)
+        return
     if args.only == "prefill":
         for _ in range(args.steps):
             step()
@@ -331,6 +349,20 @@ def main():
 
     ms_pro, _ = time_launches(step_pro, args.steps, 20, stream)
     ms_torch_pro, _ = time_launches(step_torch_prologue, args.steps, 20, stream)
+
+    # backward of the same step (kda_chunk_bwd): gradients of every input for
+    # a given do and dsT, workspace preallocated
+    do = torch.randn(w.B, w.T, w.H, w.V, device=dev, generator=torch.Generator(dev).manual_seed(7))
+    dsT = torch.randn(w.B, w.H, w.K, w.V, device=dev, generator=torch.Generator(dev).manual_seed(8))
+    bws = torch.empty(kda.bwd_workspace_bytes(w.B, w.B * w.T, w.H, w.K, w.V, w.chunk),
+                      dtype=torch.uint8, device=dev)
+
+    def step_bwd():
+        kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, initial_state=x["s0"],
+                      dsT=dsT, chunk=w.chunk, workspace=bws)
+
+    ms_bwd, _ = time_launches(step_bwd, max(5, args.steps // 5), 3, stream)
+    bwd_b = bwd_alg_bytes(w.B, w.T, w.H, w.K, w.V)
     tokens = w.B * w.T
     alg_b = prefill_alg_bytes(w.B, w.T, w.H, w.K, w.V, s0=w.s0_std is not None, sT=True)
     alg_f = prefill_alg_flops(w.B, w.T, w.H, w.K, w.V, w.chunk)
@@ -365,6 +397,12 @@ def main():
         "fused_single_pass_ms_per_step": ms_fused,
         "prefix_cache": {"ms_per_step_with_snapshots": ms_snap, "snap_tokens": snap,
                          "page_tokens": page, "snapshots_per_call": w.B * w.H * (w.T // snap)},
+        "backward": {"ms_per_step": ms_bwd, "tokens_per_s": tokens / (ms_bwd * 1e-3),
+                     "kernels": "bwd_prep_kernel + bwd_states_kernel + bwd_dstate_kernel + "
+                                "bwd_grads_kernel (fp32 vector ALU)",
+                     "alg_bytes_per_call": bwd_b,
+                     "achieved_GBps": bwd_b / (ms_bwd * 1e-3) / 1e9,
+                     "hbm_frac": bwd_b / (ms_bwd * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "prologue": {"ms_per_step_fused_maps": ms_pro,
                      "ms_per_step_torch_maps_then_plain_call": ms_torch_pro,
                      "maps": "q, k L2-normalised (eps 1e-6); g = -0.25 sigmoid(gate logits); "

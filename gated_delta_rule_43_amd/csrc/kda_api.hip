@@ -33,6 +33,15 @@ hipError_t launch_chunk_mfma(const void *q, const void *k, const void *v, const 
                              const int32_t *cu, int N, int fixedT, int totalT, int H,
                              bool out_bf16, hipStream_t stream);
 bool chunk_mfma_supported(int K, int V, int C);
+bool chunk_bwd_supported(int K, int V, int C);
+size_t chunk_bwd_workspace_bytes(int N, int totalT, int fixedT, bool packed, int H, int K, int V,
+                                 int C);
+hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const float *s0, const float *dout,
+                            const float *dsT, float *dq, float *dk, float *dv, float *dg,
+                            float *dbeta, float *ds0, const int32_t *cu, int N, int fixedT,
+                            int totalT, int H, int K, int V, int C, bool in_bf16,
+                            void *workspace, hipStream_t stream);
 bool chunk_split_supported(int N, int H, int K, int V, int C);
 bool chunk_split_recommended(int N, int totalT, int H, int K, int V, int C);
 size_t chunk_split_workspace_bytes(int N, int totalT, int H);
@@ -136,7 +145,7 @@ bool pool_ok(int pool_slots, int H, int K, int V) {
 
 extern "C" {
 
-int kda_version(void) { return 103; }
+int kda_version(void) { return 104; }
 
 const char *kda_status_str(kda_status_t s) {
     switch (s) {
@@ -379,6 +388,64 @@ kda_status_t kda_decode_multi_paged(const void *q, const void *k, const void *v,
     return kda_decode_multi_paged_prologue(q, k, v, g, beta, pool, pool_slots, slot_in, slot_out,
                                            o, N, T, H, K, V, in_dtype, out_dtype, 0u, 0.f, 0.f,
                                            stream);
+}
+
+size_t kda_bwd_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk) {
+    if (N < 0 || total_T < 0 || H <= 0 || !kda::chunk_bwd_supported(K, V, chunk)) return 0;
+    return kda::chunk_bwd_workspace_bytes(N, total_T, 0, true, H, K, V, chunk);
+}
+
+}  // extern "C"
+
+namespace {
+
+kda_status_t run_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                     const float *s0, const float *dout, const float *dsT, float *dq, float *dk,
+                     float *dv, float *dg, float *dbeta, float *ds0, const int32_t *cu, int N,
+                     int fixedT, int totalT, int H, int K, int V, int chunk, kda_dtype_t in_dtype,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    if (!dtype_ok(in_dtype)) return KDA_ERR_DTYPE;
+    if (N < 0 || totalT < 0 || H <= 0 || K <= 0 || V <= 0 || chunk <= 0) return KDA_ERR_SHAPE;
+    if (!fits(totalT, H, K > V ? K : V) || !fits(N, H, (long long)K * V)) return KDA_ERR_SHAPE;
+    if (!kda::chunk_bwd_supported(K, V, chunk)) return KDA_ERR_UNSUPPORTED;
+    if (totalT > 0 && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
+        return KDA_ERR_NULL;
+    if (cu == nullptr && N > 0 && fixedT < 0) return KDA_ERR_SHAPE;
+    const size_t need = kda::chunk_bwd_workspace_bytes(N, totalT, 0, true, H, K, V, chunk);
+    if (need > 0 && !workspace) return KDA_ERR_NULL;
+    if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    if (N == 0) return KDA_OK;
+    return from_hip(kda::launch_chunk_bwd(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta,
+                                          ds0, cu, N, fixedT, totalT, H, K, V, chunk,
+                                          in_dtype == KDA_BF16, workspace,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, const float *s0, const float *do_, const float *dsT,
+                           float *dq, float *dk, float *dv, float *dg, float *dbeta, float *ds0,
+                           int B, int T, int H, int K, int V, int chunk, kda_dtype_t in_dtype,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    if (B < 0 || T < 0) return KDA_ERR_SHAPE;
+    const long long total = (long long)B * T;
+    if (total > INT_MAX) return KDA_ERR_SHAPE;
+    return run_bwd(q, k, v, g, beta, s0, do_, dsT, dq, dk, dv, dg, dbeta, ds0, nullptr, B, T,
+                   (int)total, H, K, V, chunk, in_dtype, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_varlen_bwd(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const float *s0, const float *do_,
+                            const float *dsT, float *dq, float *dk, float *dv, float *dg,
+                            float *dbeta, float *ds0, const int32_t *cu_seqlens, int N,
+                            int total_T, int H, int K, int V, int chunk, kda_dtype_t in_dtype,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    if (N > 0 && !cu_seqlens) return KDA_ERR_NULL;
+    return run_bwd(q, k, v, g, beta, s0, do_, dsT, dq, dk, dv, dg, dbeta, ds0, cu_seqlens, N, 0,
+                   total_T, H, K, V, chunk, in_dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 __all__ = ["chunk_fwd", "varlen_fwd", "decode_step", "varlen_fwd_paged", "decode_step_paged",
-           "decode_multi_paged", "Prologue",
+           "decode_multi_paged", "Prologue", "chunk_bwd", "varlen_bwd", "bwd_workspace_bytes",
            "workspace_bytes",
            "two_pass_workspace_bytes", "library",
            "KdaError", "LIB_PATH", "F32", "BF16"]
@@ -93,6 +93,12 @@ def library():
         fn = getattr(lib, name + "_prologue")
         fn.argtypes = getattr(lib, name).argtypes[:-1] + [u32, f32, f32, vp]
         fn.restype = i32
+    lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i32] * 7 + [vp, sz, vp]
+    lib.kda_chunk_bwd.restype = i32
+    lib.kda_varlen_bwd.argtypes = [vp] * 15 + [i32] * 7 + [vp, sz, vp]
+    lib.kda_varlen_bwd.restype = i32
+    lib.kda_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.kda_bwd_workspace_bytes.restype = sz
     lib.kda_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.kda_workspace_bytes.restype = sz
     lib.kda_two_pass_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -396,3 +402,67 @@ def decode_multi_paged(q, k, v, g, beta, pool, slot_in, slot_out, out_dtype=torc
           _ptr(beta), _ptr(pool), slots, _ptr(slot_in), _ptr(slot_out), _ptr(o), N, T, H, K, V,
           _dtype_code(dt), _dtype_code(o.dtype), _stream(q.device))
     return o
+
+
+def bwd_workspace_bytes(N: int, total_T: int, H: int, K: int, V: int, chunk: int) -> int:
+    """Workspace bytes of a backward call (kda_bwd_workspace_bytes)."""
+    return int(library().kda_bwd_workspace_bytes(N, total_T, H, K, V, chunk))
+
+
+def _bwd_common(q, k, v, g, beta, do, N, total, initial_state, dsT, need_ds0, chunk, workspace):
+    _need_gpu(q, k, v, g, beta, do, initial_state, dsT, workspace)
+    H, K = q.shape[-2], q.shape[-1]
+    V = v.shape[-1]
+    dt = q.dtype
+    if any(x.dtype != dt for x in (k, v, g, beta)):
+        raise ValueError("q, k, v, g and beta must share one dtype")
+    if do.dtype != torch.float32 or do.shape != v.shape:
+        raise ValueError("do must be float32 with the shape of v")
+    for s in (initial_state, dsT):
+        if s is not None and (s.dtype != torch.float32 or s.shape != (N, H, K, V)):
+            raise ValueError("states and their gradients must be float32 [N, H, K, V]")
+    chunk = chunk or _default_chunk(K)
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    grads = (torch.empty(q.shape, **f32), torch.empty(k.shape, **f32), torch.empty(v.shape, **f32),
+             torch.empty(g.shape, **f32), torch.empty(beta.shape, **f32))
+    ds0 = torch.empty((N, H, K, V), **f32) if need_ds0 else None
+    nbytes = bwd_workspace_bytes(N, total, H, K, V, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.dtype != torch.uint8 or workspace.numel() < nbytes:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {nbytes} bytes")
+    return H, K, V, chunk, dt, grads, ds0, workspace
+
+
+def chunk_bwd(q, k, v, g, beta, do, initial_state=None, dsT=None, chunk=None, need_ds0=True,
+              workspace=None):
+    """Gradients of sum(do * o) + sum(dsT * S_T) for the chunk_fwd call with the same
+    inputs: returns (dq, dk, dv, dg, dbeta, ds0 or None), all float32.
+    q, k, g: [B, T, H, K]; v, do: [B, T, H, V]; beta: [B, T, H]; states [B, H, K, V]."""
+    B, T = q.shape[0], q.shape[1]
+    H, K, V, chunk, dt, grads, ds0, ws = _bwd_common(q, k, v, g, beta, do, B, B * T,
+                                                     initial_state, dsT, need_ds0, chunk,
+                                                     workspace)
+    _call("kda_chunk_bwd", None, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+          _ptr(initial_state), _ptr(do), _ptr(dsT), *(_ptr(x) for x in grads), _ptr(ds0),
+          B, T, H, K, V, chunk, _dtype_code(dt), _ptr(ws), ws.numel(), _stream(q.device))
+    return (*grads, ds0)
+
+
+def varlen_bwd(q, k, v, g, beta, do, cu_seqlens, initial_state=None, dsT=None, chunk=None,
+               need_ds0=True, workspace=None):
+    """Gradients for the varlen_fwd call with the same inputs (packed sequences):
+    returns (dq, dk, dv, dg, dbeta, ds0 or None), all float32."""
+    _need_gpu(cu_seqlens)
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    N, total = cu_seqlens.numel() - 1, q.shape[0]
+    H, K, V, chunk, dt, grads, ds0, ws = _bwd_common(q, k, v, g, beta, do, N, total,
+                                                     initial_state, dsT, need_ds0, chunk,
+                                                     workspace)
+    _call("kda_varlen_bwd", None, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+          _ptr(initial_state), _ptr(do), _ptr(dsT), *(_ptr(x) for x in grads), _ptr(ds0),
+          _ptr(cu_seqlens), N, total, H, K, V, chunk, _dtype_code(dt), _ptr(ws), ws.numel(),
+          _stream(q.device))
+    return (*grads, ds0)

@@ -292,6 +292,44 @@ kda_status_t kda_decode_multi_paged_prologue(const void *q, const void *k, const
                                              float gate_lower_bound, float norm_eps,
                                              void *stream);
 
+/*
+ * Backward pass: the gradients of the loss L = sum(do * o) + sum(dsT * S_T)
+ * with respect to every input of the forward call with the same arguments
+ * (the recurrence above, differentiated through the same chunked algebra in
+ * reverse: the per-chunk products, then the state gradient carried from each
+ * chunk's end to its start, chunk after chunk from the last).
+ *   do_   : [tokens, H, V] fp32, the gradient of o.
+ *   dsT   : [N, H, K, V] fp32, the gradient of S_T, or NULL for zeros.
+ *   s0    : the forward's initial states, or NULL for zeros.
+ *   dq, dk, dg : [tokens, H, K] fp32;  dv : [tokens, H, V] fp32;
+ *   dbeta : [tokens, H] fp32;  ds0 : [N, H, K, V] fp32, or NULL if not wanted.
+ * Every gradient is written in full (rows of every token).  All arithmetic is
+ * fp32 (bf16 inputs are widened exactly).  The workspace is required: at
+ * least kda_bwd_workspace_bytes(N, total_T, ...) bytes (a per-(chunk, head)
+ * record of the chunk's products plus each chunk's start state and end-state
+ * gradient); NULL with a nonzero requirement is KDA_ERR_NULL, too small is
+ * KDA_ERR_WORKSPACE.  Numerical precondition: that of the bf16 forward
+ * (-g_lb <= g <= 0 with g_lb * chunk / 2 <= 8), for both input dtypes, since
+ * the decay factors are factored around the middle of each chunk.
+ * Supported (K, V, chunk): (32, 32, 16) and (128, 128, 64).
+ */
+kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, const float *s0, const float *do_, const float *dsT,
+                           float *dq, float *dk, float *dv, float *dg, float *dbeta, float *ds0,
+                           int B, int T, int H, int K, int V, int chunk, kda_dtype_t in_dtype,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+kda_status_t kda_varlen_bwd(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const float *s0, const float *do_,
+                            const float *dsT, float *dq, float *dk, float *dv, float *dg,
+                            float *dbeta, float *ds0, const int32_t *cu_seqlens, int N,
+                            int total_T, int H, int K, int V, int chunk, kda_dtype_t in_dtype,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of a backward call over N sequences and total_T tokens
+ * (an upper bound for any lengths; 0 for an unsupported shape). */
+size_t kda_bwd_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk);
+
 /* Workspace bytes for the recommended implementation of a forward call over
  * N sequences, total_T tokens: nonzero (the two-pass size) when the two-pass
  * path is supported and expected to be faster (bf16 inputs assumed; at most

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
               "kda_two_pass_workspace_bytes", "kda_status_str", "kda_version",
               "kda_chunk_fwd_prologue", "kda_varlen_fwd_prologue",
               "kda_varlen_fwd_paged_prologue", "kda_decode_step_prologue",
-              "kda_decode_step_paged_prologue", "kda_decode_multi_paged_prologue"):
+              "kda_decode_step_paged_prologue", "kda_decode_multi_paged_prologue",
+              "kda_chunk_bwd", "kda_varlen_bwd", "kda_bwd_workspace_bytes"):
         assert n in names
 
 
@@ -49,7 +50,7 @@ def test_status_strings_and_version(lib):
         assert s.startswith("KDA_")
     assert lib.kda_status_str(7).decode().startswith("KDA_ERR_VALUE")
     assert lib.kda_status_str(99).decode() == "KDA_ERR_UNKNOWN"
-    assert lib.kda_version() == 103
+    assert lib.kda_version() == 104
 
 
 def two_pass_size(N, total, H):
@@ -239,3 +240,30 @@ def test_binding_prologue_flags():
     assert kda.Prologue(gate_lower_bound=0.25).flags() == 2
     assert kda.Prologue(beta_logits=True).flags() == 4
     assert kda.Prologue(True, 0.25, True, 1e-6).flags() == 7
+
+
+def test_backward_argument_errors(lib):
+    need = lib.kda_bwd_workspace_bytes(1, 64, 1, 128, 128, 64)
+    assert need == 1 * 1 * (4 * (4 * 64 * 128 + 3 * 64 * 64 + 64 + 2 * 128) + 2 * 4 * 128 * 128)
+    assert lib.kda_bwd_workspace_bytes(1, 64, 1, 64, 64, 64) == 0        # unsupported
+    assert lib.kda_bwd_workspace_bytes(3, 100, 2, 32, 32, 16) == \
+        ((100 + 15 * 3) // 16) * 2 * (4 * (4 * 16 * 32 + 3 * 16 * 16 + 16 + 2 * 32) + 2 * 4 * 32 * 32)
+    f = lib.kda_chunk_bwd
+
+    def call(B=1, T=64, H=1, K=128, C=64, ind=1, null=None, ws=FAKE, nws=None):
+        ptrs = [FAKE] * 14
+        if null is not None:
+            ptrs[null] = None
+        return f(*ptrs, B, T, H, K, K, C, ind, ws, need if nws is None else nws, None)
+
+    assert call(K=64, C=64) == 4
+    assert call(ind=3) == 3
+    assert call(B=-1) == 2
+    assert call(H=0) == 2
+    for i in (0, 1, 2, 3, 4, 6, 8, 9, 10, 11, 12):       # inputs, do, the five gradients
+        assert call(null=i) == 1
+    assert call(ws=None) == 1                              # workspace required
+    assert call(nws=need - 1) == 5
+    v = lib.kda_varlen_bwd
+    assert v(*[FAKE] * 14, None, 2, 10, 1, 128, 128, 64, 1, FAKE, 1 << 30, None) == 1  # no cu
+    assert v(*[FAKE] * 15, 2, 10, 1, 128, 128, 64, 1, FAKE, 10, None) == 5
