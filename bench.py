@@ -69,9 +69,26 @@ def decode_alg_bytes(N, H, K, V, in_bytes=2, out_bytes=4):
     return N * H * (2 * K * V * 4 + (3 * K + V + 1) * in_bytes + V * out_bytes)
 
 
-def kernel_source_hash():
+# The sources each profiled kernel is built from (a change elsewhere in the
+# library leaves its counter summary valid).
+_COMMON = ["kda_common.hpp", "kda_mfma.hpp", "prologue.hpp", "state_io.hpp"]
+PROFILE_SOURCES = {
+    "kda_chunk_fwd_two_pass": ["chunk_split.hip"] + _COMMON,
+    "chunk_mfma_kernel": ["chunk_mfma.hip"] + _COMMON,
+    "decode_step_kernel": ["decode.hip"] + _COMMON,
+    "kda_chunk_bwd": ["chunk_bwd.hip", "kda_common.hpp"],
+}
+
+
+def kernel_source_hash(stem=None):
+    """sha256 prefix of the kernel sources behind profile `stem` (all of
+    csrc/ when stem is None or unknown)."""
+    csrc = os.path.join(ROOT, "gated_delta_rule_43_amd", "csrc")
+    names = next((v for k, v in PROFILE_SOURCES.items() if stem and stem.startswith(k)), None)
+    files = ([os.path.join(csrc, n) for n in names] if names
+             else sorted(glob.glob(os.path.join(csrc, "*"))))
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_43_amd", "csrc", "*"))):
+    for f in files:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
@@ -87,7 +104,7 @@ def measured_traffic(stem):
     text = open(path).read()
     m = re.search(r"source hash:\s*`?([0-9a-f]+)`?", text)
     b = re.search(r"HBM bytes per launch:\s*([0-9.eE+]+)", text)
-    if not m or not b or m.group(1) != kernel_source_hash():
+    if not m or not b or m.group(1) != kernel_source_hash(stem):
         return None
     return float(b.group(1))
 

@@ -23,13 +23,17 @@
 // G_m cancels from the forward result, so its own gradient is zero and it is
 // treated as a constant.
 //
-// Four launches:
+// Five launches:
 //   bwd_prep_kernel    (chunk, head), all chunks at once: Kp, Km, Qp, E, Gk,
 //                      P, T, beta, F, exp(G_m) into the chunk's record;
+//   bwd_trans_kernel   (chunk, head): the chunk's state transition
+//                      S_end = MM S_start + NN and the adjoint's constant NB;
 //   bwd_states_kernel  (sequence, head, value tile): the forward state chain,
-//                      leaving every chunk's start state in the workspace;
-//   bwd_dstate_kernel  (sequence, head, value tile): the reverse chain of
-//                      dS_end, chunk after chunk from the last, and ds0;
+//                      one [K][K] product per chunk, leaving every chunk's
+//                      start state in the workspace;
+//   bwd_dstate_kernel  (sequence, head, value tile): the reverse chain
+//                      dS_start = MM^T dS_end + NB, chunk after chunk from
+//                      the last, and ds0;
 //   bwd_grads_kernel   (chunk, head): every input gradient of the chunk.
 // The state chains are column-separable (value tiles need no communication);
 // the gradients of q, k, g and beta sum over all value columns, so the last
@@ -41,13 +45,15 @@ namespace {
 
 constexpr int BNT = 256;  // threads per workgroup of the prep and state-chain kernels
 
-// Record of one (chunk, head), in floats.
-template <int K, int C>
+// Record of one (chunk, head), in floats.  MM, NN, NB: the chunk's state
+// transition S_end = MM S_start + NN and its adjoint dS_start = MM^T dS_end + NB.
+template <int K, int V, int C>
 struct BwdRec {
     static constexpr size_t KP = 0, KM = KP + C * K, QP = KM + C * K, EE = QP + C * K;
     static constexpr size_t GK = EE + C * K, PP = GK + C * C, TT = PP + C * C;
     static constexpr size_t BETA = TT + C * C, FF = BETA + C, EGM = FF + K;
-    static constexpr size_t floats = EGM + K;
+    static constexpr size_t MM = EGM + K, NN = MM + K * K, NB = NN + K * V;
+    static constexpr size_t floats = NB + K * V;
 };
 
 __device__ __forceinline__ int chunks_of(const int32_t *cu, int n, int fixedT, int totalT, int C) {
@@ -125,18 +131,76 @@ __device__ void locate_chunk(const int32_t *cu, int N, int fixedT, int totalT, i
     __syncthreads();
 }
 
+// A [K][K] fp32 matrix as float4 pieces, MQ per thread, held in registers so
+// that the next chunk's copy is in flight while this chunk's is used.
+template <int K, int NT>
+struct MatPrefetch {
+    static constexpr int MQ = K * K / 4 / NT;
+    static_assert(K * K % (4 * NT) == 0, "matrix must split evenly");
+    float4 m[MQ];
+    __device__ __forceinline__ void load(const float *src) {
+#pragma unroll
+        for (int i = 0; i < MQ; ++i)
+            m[i] = reinterpret_cast<const float4 *>(src)[threadIdx.x + NT * i];
+    }
+    // to LDS with row pitch P (one 16-byte store when P keeps rows aligned)
+    template <int P>
+    __device__ __forceinline__ void store(float *dst) const {
+#pragma unroll
+        for (int i = 0; i < MQ; ++i) {
+            const int e = 4 * (threadIdx.x + NT * i), r = e / K, c = e % K;
+            float *d = dst + r * P + c;
+            if constexpr (P % 4 == 0) {
+                *reinterpret_cast<float4 *>(d) = m[i];
+            } else {
+                d[0] = m[i].x;
+                d[1] = m[i].y;
+                d[2] = m[i].z;
+                d[3] = m[i].w;
+            }
+        }
+    }
+};
+
+// Copies a contiguous [R][D] fp32 block to LDS with row pitch P, float4 loads
+// (all of a thread's loads issued before its stores).
+template <int R, int D, int P, int NT>
+__device__ __forceinline__ void rows_to_lds(float *dst, const float *src) {
+    constexpr int Q = R * D / 4, PER = (Q + NT - 1) / NT;
+    static_assert(D % 4 == 0, "rows must split into float4");
+    float4 x[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int qi = threadIdx.x + NT * i;
+        if (qi < Q) x[i] = reinterpret_cast<const float4 *>(src)[qi];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int qi = threadIdx.x + NT * i;
+        if (qi < Q) {
+            const int e = 4 * qi, r = e / D, c = e % D;
+            float *d = dst + r * P + c;
+            d[0] = x[i].x;
+            d[1] = x[i].y;
+            d[2] = x[i].z;
+            d[3] = x[i].w;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ pass 0
 template <int K, int V, int C, typename TIn>
 __global__ __launch_bounds__(BNT) void bwd_prep_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ g,
     const TIn *__restrict__ beta, const int32_t *__restrict__ cu, int N, int fixedT, int totalT,
     int H, float *__restrict__ ws) {
-    using Rc = BwdRec<K, C>;
+    using Rc = BwdRec<K, V, C>;
     extern __shared__ float smem[];
-    float *sKp = smem;             // [C][K]
-    float *sKm = sKp + C * K;      // [C][K]
-    float *sQp = sKm + C * K;      // [C][K]
-    float *sX = sQp + C * K;       // [C][K]: G, later Gk [C][C] and T [C][C]
+    constexpr int PK = K + 1;     // row pitch: a wave reading one column hits distinct banks
+    float *sKp = smem;             // [C][PK]
+    float *sKm = sKp + C * PK;     // [C][PK]
+    float *sQp = sKm + C * PK;     // [C][PK]
+    float *sX = sQp + C * PK;      // [C][K]: G, later Gk [C][C] and T [C][C]
     float *sB = sX + C * K;        // [C]
     float *sGm = sB + C;           // [K]
     int *red = reinterpret_cast<int *>(sGm + K);  // [BNT]
@@ -180,9 +244,9 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(
         const float ep = fast_exp(d), em = fast_exp(-d);
         const size_t off = ((size_t)(c0 + r) * H + h) * K + c;
         const float kv = r < L ? to_f32(k[off]) : 0.f, qv = r < L ? to_f32(q[off]) : 0.f;
-        sKp[e] = kv * ep;
-        sKm[e] = kv * em;
-        sQp[e] = qv * ep;
+        sKp[r * PK + c] = kv * ep;
+        sKm[r * PK + c] = kv * em;
+        sQp[r * PK + c] = qv * ep;
         rec[Rc::KP + e] = kv * ep;
         rec[Rc::KM + e] = kv * em;
         rec[Rc::QP + e] = qv * ep;
@@ -196,9 +260,9 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(
         float a = 0.f, p = 0.f;
         if (s <= r) {
             for (int c = 0; c < K; ++c) {
-                const float km = sKm[s * K + c];
-                a += sKp[r * K + c] * km;
-                p += sQp[r * K + c] * km;
+                const float km = sKm[s * PK + c];
+                a += sKp[r * PK + c] * km;
+                p += sQp[r * PK + c] * km;
             }
         }
         const float gk = s < r ? a : 0.f;
@@ -221,161 +285,222 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(
     for (int e = t; e < C * C; e += BNT) rec[Rc::TT + e] = sT[e];
 }
 
-// ------------------------------------------------------------------ pass 1
-// Forward state chain of one value tile: writes the start state of every
-// chunk of the sequence to Sst[chunk][h] (fp32 [K][V]).
-template <int K, int V, int C, int VT, typename TIn>
-__global__ __launch_bounds__(BNT) void bwd_states_kernel(
-    const TIn *__restrict__ v, const float *__restrict__ s0, const int32_t *__restrict__ cu,
-    int fixedT, int totalT, int H, const float *__restrict__ recs, float *__restrict__ Sst) {
-    using Rc = BwdRec<K, C>;
+// -------------------------------------------------------------- pass 0b
+// The chunk's transition: with W = T Diag(beta) Kp, U~ = T Diag(beta) V and
+// Q^ = Qp - P W (so that U = U~ - W S' and O = Q^ S' + P U~),
+//   MM = F (I - Km^T W) Diag(exp(G_m)),   NN = F Km^T U~,
+//   NB = Diag(exp(G_m)) Q^T dO            (dS_start = MM^T dS_end + NB).
+// Three [C][D+1] buffers are reused in turn (pitch D+1: rows fall on
+// different banks when a wave reads one column).
+template <int K, int V, int C, typename TIn>
+__global__ __launch_bounds__(BNT) void bwd_trans_kernel(
+    const TIn *__restrict__ v, const float *__restrict__ dout, const int32_t *__restrict__ cu,
+    int N, int fixedT, int totalT, int H, float *__restrict__ recs) {
+    using Rc = BwdRec<K, V, C>;
+    static_assert(K == V, "one buffer pitch for key and value tiles");
+    constexpr int PD = K + 1, PC = C + 1, RB = 4;  // RB output rows per thread
     extern __shared__ float smem[];
-    float *sKp = smem;           // [C][K]
-    float *sKm = sKp + C * K;    // [C][K]
-    float *sT = sKm + C * K;     // [C][C]
-    float *sS = sT + C * C;      // [K][VT]
-    float *sY = sS + K * VT;     // [C][VT]
-    float *sU = sY + C * VT;     // [C][VT]
-    float *sB = sU + C * VT;     // [C]
-    float *sF = sB + C;          // [K]
-    float *sE = sF + K;          // [K]
+    float *b0 = smem, *b1 = b0 + C * PD, *b2 = b1 + C * PD;
+    float *sT = b2 + C * PD, *sP = sT + C * PC;
+    float *sB = sP + C * PC, *sF = sB + C, *sE = sF + K;
     int *red = reinterpret_cast<int *>(sE + K);
+
+    const int gc = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    int n, ci;
+    locate_chunk<BNT>(cu, N, fixedT, totalT, C, gc, n, ci, red);
+    if (n < 0) return;
+    int bos, eos;
+    seq_bounds(cu, n, fixedT, totalT, bos, eos);
+    const int c0 = bos + ci * C, L = min(C, eos - c0);
+    float *rec = recs + ((size_t)gc * H + h) * Rc::floats;
+
+    auto load_rows = [&](float *dst, size_t src_off) {
+        rows_to_lds<C, K, PD, BNT>(dst, rec + src_off);
+    };
+    // out[r][j] = sum_{s<=r} T[r][s] beta_s in[s][j]   (r < C, j < K)
+    auto tri_apply = [&](float *out, const float *in) {
+        for (int e = t; e < C * K; e += BNT) {
+            const int r = e / K, j = e % K;
+            float acc = 0.f;
+            for (int s2 = 0; s2 <= r; ++s2) acc += sT[r * PC + s2] * sB[s2] * in[s2 * PD + j];
+            out[r * PD + j] = acc;
+        }
+    };
+    // out[c][j] = sum_r a[r][c] b[r][j] for RB consecutive c per thread
+    auto at_b = [&](const float *a, const float *b, auto &&store) {
+        for (int e = t; e < (K / RB) * K; e += BNT) {
+            const int cb = (e / K) * RB, j = e % K;
+            float acc[RB] = {};
+            for (int r = 0; r < C; ++r) {
+                const float bv = b[r * PD + j];
+#pragma unroll
+                for (int i = 0; i < RB; ++i) acc[i] += a[r * PD + cb + i] * bv;
+            }
+#pragma unroll
+            for (int i = 0; i < RB; ++i) store(cb + i, j, acc[i]);
+        }
+    };
+
+    for (int e = t; e < C * C; e += BNT) {
+        sT[(e / C) * PC + e % C] = rec[Rc::TT + e];
+        sP[(e / C) * PC + e % C] = rec[Rc::PP + e];
+    }
+    for (int r = t; r < C; r += BNT) sB[r] = rec[Rc::BETA + r];
+    for (int c = t; c < K; c += BNT) {
+        sF[c] = rec[Rc::FF + c];
+        sE[c] = rec[Rc::EGM + c];
+    }
+    load_rows(b0, Rc::KP);
+    __syncthreads();
+    tri_apply(b1, b0);  // W
+    __syncthreads();
+    load_rows(b0, Rc::QP);
+    __syncthreads();
+    for (int e = t; e < C * K; e += BNT) {  // Q^ = Qp - P W
+        const int r = e / K, j = e % K;
+        float acc = b0[r * PD + j];
+        for (int s2 = 0; s2 <= r; ++s2) acc -= sP[r * PC + s2] * b1[s2 * PD + j];
+        b2[r * PD + j] = acc;
+    }
+    __syncthreads();
+    for (int e = t; e < C * V; e += BNT) {
+        const int r = e / V, j = e % V;
+        b0[r * PD + j] = r < L ? dout[((size_t)(c0 + r) * H + h) * V + j] : 0.f;
+    }
+    __syncthreads();
+    at_b(b2, b0, [&](int c, int j, float x) { rec[Rc::NB + (size_t)c * V + j] = sE[c] * x; });
+    __syncthreads();
+    load_rows(b0, Rc::KM);
+    __syncthreads();
+    at_b(b0, b1, [&](int c, int j, float x) {
+        rec[Rc::MM + (size_t)c * K + j] = sF[c] * ((c == j ? 1.f : 0.f) - x) * sE[j];
+    });
+    __syncthreads();
+    for (int e = t; e < C * V; e += BNT) {
+        const int r = e / V, j = e % V;
+        b1[r * PD + j] = r < L ? to_f32(v[((size_t)(c0 + r) * H + h) * V + j]) : 0.f;
+    }
+    __syncthreads();
+    tri_apply(b2, b1);  // U~
+    __syncthreads();
+    at_b(b0, b2, [&](int c, int j, float x) { rec[Rc::NN + (size_t)c * V + j] = sF[c] * x; });
+}
+
+// ------------------------------------------------------------------ pass 1
+// Forward state chain of one value tile, S <- MM S + NN chunk after chunk:
+// writes the start state of every chunk of the sequence to Sst[chunk][h].
+// RB rows of one column per thread; MM staged with row pitch K + 1 (the four
+// row blocks a wave reads fall on different banks; unpadded rows with
+// 16-byte reads measured 2.3x slower).
+template <int K, int V, int C, int VT>
+__global__ __launch_bounds__(BNT) void bwd_states_kernel(
+    const float *__restrict__ s0, const int32_t *__restrict__ cu, int fixedT, int totalT, int H,
+    const float *__restrict__ recs, float *__restrict__ Sst) {
+    using Rc = BwdRec<K, V, C>;
+    constexpr int PK = K + 1, RB = K * VT / BNT;
+    static_assert(K * VT % BNT == 0 && BNT % VT == 0, "tile must cover the workgroup");
+    extern __shared__ float smem[];
+    float *sM = smem;            // [K][K + 1]
+    float *sS = sM + K * PK;     // [K][VT]
+    int *red = reinterpret_cast<int *>(sS + K * VT);
 
     const int vt = blockIdx.x, h = blockIdx.y, n = blockIdx.z, t = threadIdx.x;
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
     const int nch = (eos - bos + C - 1) / C;
     const int first = first_chunk<BNT>(cu, n, fixedT, totalT, C, red);
-    for (int e = t; e < K * VT; e += BNT) {
-        const int c = e / VT, j = e % VT;
-        sS[e] = s0 ? s0[((size_t)n * H + h) * K * V + (size_t)c * V + vt * VT + j] : 0.f;
-    }
+    const int j = t % VT, cb = (t / VT) * RB;  // this thread's column and first row
+    float S[RB], nn[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+        S[i] = s0 ? s0[((size_t)n * H + h) * K * V + (size_t)(cb + i) * V + vt * VT + j] : 0.f;
+    MatPrefetch<K, BNT> pm;
+    auto fetch = [&](int ci) {  // chunk ci's MM and this thread's NN entries
+        const float *rec = recs + ((size_t)(first + ci) * H + h) * Rc::floats;
+        pm.load(rec + Rc::MM);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) nn[i] = rec[Rc::NN + (size_t)(cb + i) * V + vt * VT + j];
+    };
+    if (nch > 0) fetch(0);
     for (int ci = 0; ci < nch; ++ci) {
-        const int gc = first + ci, c0 = bos + ci * C, L = min(C, eos - c0);
-        const float *rec = recs + ((size_t)gc * H + h) * Rc::floats;
-        float *dst = Sst + ((size_t)gc * H + h) * K * V;
+        const int gc = first + ci;
+        float *dst = Sst + ((size_t)gc * H + h) * K * V + vt * VT + j;
+#pragma unroll
+        for (int i = 0; i < RB; ++i) dst[(size_t)(cb + i) * V] = S[i];
         __syncthreads();
-        for (int e = t; e < K * VT; e += BNT) dst[(size_t)(e / VT) * V + vt * VT + e % VT] = sS[e];
-        for (int e = t; e < C * K; e += BNT) {
-            sKp[e] = rec[Rc::KP + e];
-            sKm[e] = rec[Rc::KM + e];
-        }
-        for (int e = t; e < C * C; e += BNT) sT[e] = rec[Rc::TT + e];
-        for (int r = t; r < C; r += BNT) sB[r] = rec[Rc::BETA + r];
-        for (int c = t; c < K; c += BNT) {
-            sF[c] = rec[Rc::FF + c];
-            sE[c] = rec[Rc::EGM + c];
+        pm.template store<PK>(sM);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            sS[(cb + i) * VT + j] = S[i];
+            S[i] = nn[i];
         }
         __syncthreads();
-        for (int e = t; e < K * VT; e += BNT) sS[e] *= sE[e / VT];  // S' = Diag(exp(G_m)) S
-        __syncthreads();
-        for (int e = t; e < C * VT; e += BNT) {  // Y = Diag(beta) (V - Kp S')
-            const int r = e / VT, j = e % VT;
-            float acc = r < L ? to_f32(v[((size_t)(c0 + r) * H + h) * V + vt * VT + j]) : 0.f;
-            for (int c = 0; c < K; ++c) acc -= sKp[r * K + c] * sS[c * VT + j];
-            sY[e] = sB[r] * acc;
-        }
-        __syncthreads();
-        for (int e = t; e < C * VT; e += BNT) {  // U = T Y
-            const int r = e / VT, j = e % VT;
-            float acc = 0.f;
-            for (int s = 0; s <= r; ++s) acc += sT[r * C + s] * sY[s * VT + j];
-            sU[e] = acc;
-        }
-        __syncthreads();
-        for (int e = t; e < K * VT; e += BNT) {  // S = F (S' + Km^T U)
-            const int c = e / VT, j = e % VT;
-            float acc = sS[e];
-            for (int r = 0; r < C; ++r) acc += sKm[r * K + c] * sU[r * VT + j];
-            sS[e] = sF[c] * acc;
+        if (ci + 1 < nch) fetch(ci + 1);
+        for (int c2 = 0; c2 < K; ++c2) {
+            const float sv = sS[c2 * VT + j];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) S[i] += sM[(cb + i) * PK + c2] * sv;
         }
     }
 }
 
 // ------------------------------------------------------------------ pass 2
-// Reverse chain of the state gradient for one value tile: writes the gradient
-// at the end of every chunk to dSe[chunk][h] and the gradient of S_0 to ds0.
+// Reverse chain of the state gradient for one value tile, dS <- MM^T dS + NB
+// chunk after chunk from the last: writes the gradient at the end of every
+// chunk to dSe[chunk][h] and the gradient of S_0 to ds0.
 template <int K, int V, int C, int VT>
 __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(
-    const float *__restrict__ dout, const float *__restrict__ dsT, float *__restrict__ ds0,
-    const int32_t *__restrict__ cu, int fixedT, int totalT, int H, const float *__restrict__ recs,
-    float *__restrict__ dSe) {
-    using Rc = BwdRec<K, C>;
+    const float *__restrict__ dsT, float *__restrict__ ds0, const int32_t *__restrict__ cu,
+    int fixedT, int totalT, int H, const float *__restrict__ recs, float *__restrict__ dSe) {
+    using Rc = BwdRec<K, V, C>;
+    constexpr int PK = K + 1, RB = K * VT / BNT;
+    static_assert(K * VT % BNT == 0 && BNT % VT == 0, "tile must cover the workgroup");
     extern __shared__ float smem[];
-    float *sKp = smem;           // [C][K]
-    float *sKm = sKp + C * K;    // [C][K]
-    float *sQp = sKm + C * K;    // [C][K]
-    float *sT = sQp + C * K;     // [C][C]
-    float *sP = sT + C * C;      // [C][C]
-    float *sX = sP + C * C;      // [K][VT]  dS, then X = F dS, then dS'
-    float *sO = sX + K * VT;     // [C][VT]  dO
-    float *sU = sO + C * VT;     // [C][VT]  dU
-    float *sY = sU + C * VT;     // [C][VT]  dY
-    float *sB = sY + C * VT;     // [C]
-    float *sF = sB + C;          // [K]
-    float *sE = sF + K;          // [K]
-    int *red = reinterpret_cast<int *>(sE + K);
+    float *sM = smem;            // [K][K + 1]
+    float *sS = sM + K * PK;     // [K][VT]
+    int *red = reinterpret_cast<int *>(sS + K * VT);
 
     const int vt = blockIdx.x, h = blockIdx.y, n = blockIdx.z, t = threadIdx.x;
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
     const int nch = (eos - bos + C - 1) / C;
     const int first = first_chunk<BNT>(cu, n, fixedT, totalT, C, red);
-    const size_t sbase = ((size_t)n * H + h) * K * V + vt * VT;
-    for (int e = t; e < K * VT; e += BNT)
-        sX[e] = dsT ? dsT[sbase + (size_t)(e / VT) * V + e % VT] : 0.f;
+    const int j = t % VT, cb = (t / VT) * RB;
+    const size_t sbase = ((size_t)n * H + h) * K * V + vt * VT + j;
+    float D[RB], nb[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) D[i] = dsT ? dsT[sbase + (size_t)(cb + i) * V] : 0.f;
+    MatPrefetch<K, BNT> pm;
+    auto fetch = [&](int ci) {  // chunk ci's MM and this thread's NB entries
+        const float *rec = recs + ((size_t)(first + ci) * H + h) * Rc::floats;
+        pm.load(rec + Rc::MM);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) nb[i] = rec[Rc::NB + (size_t)(cb + i) * V + vt * VT + j];
+    };
+    if (nch > 0) fetch(nch - 1);
     for (int ci = nch - 1; ci >= 0; --ci) {
-        const int gc = first + ci, c0 = bos + ci * C, L = min(C, eos - c0);
-        const float *rec = recs + ((size_t)gc * H + h) * Rc::floats;
-        float *dst = dSe + ((size_t)gc * H + h) * K * V;
+        const int gc = first + ci;
+        float *dst = dSe + ((size_t)gc * H + h) * K * V + vt * VT + j;
+#pragma unroll
+        for (int i = 0; i < RB; ++i) dst[(size_t)(cb + i) * V] = D[i];
         __syncthreads();
-        for (int e = t; e < K * VT; e += BNT) dst[(size_t)(e / VT) * V + vt * VT + e % VT] = sX[e];
-        for (int e = t; e < C * K; e += BNT) {
-            sKp[e] = rec[Rc::KP + e];
-            sKm[e] = rec[Rc::KM + e];
-            sQp[e] = rec[Rc::QP + e];
-        }
-        for (int e = t; e < C * C; e += BNT) {
-            sT[e] = rec[Rc::TT + e];
-            sP[e] = rec[Rc::PP + e];
-        }
-        for (int r = t; r < C; r += BNT) sB[r] = rec[Rc::BETA + r];
-        for (int c = t; c < K; c += BNT) {
-            sF[c] = rec[Rc::FF + c];
-            sE[c] = rec[Rc::EGM + c];
-        }
-        for (int e = t; e < C * VT; e += BNT) {
-            const int r = e / VT, j = e % VT;
-            sO[e] = r < L ? dout[((size_t)(c0 + r) * H + h) * V + vt * VT + j] : 0.f;
+        pm.template store<PK>(sM);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            sS[(cb + i) * VT + j] = D[i];
+            D[i] = nb[i];
         }
         __syncthreads();
-        for (int e = t; e < K * VT; e += BNT) sX[e] *= sF[e / VT];  // X = F dS_end
-        __syncthreads();
-        for (int e = t; e < C * VT; e += BNT) {  // dU = Km X + P^T dO
-            const int r = e / VT, j = e % VT;
-            float acc = 0.f;
-            for (int c = 0; c < K; ++c) acc += sKm[r * K + c] * sX[c * VT + j];
-            for (int s = r; s < C; ++s) acc += sP[s * C + r] * sO[s * VT + j];
-            sU[e] = acc;
-        }
-        __syncthreads();
-        for (int e = t; e < C * VT; e += BNT) {  // dY = T^T dU, scaled by beta
-            const int r = e / VT, j = e % VT;
-            float acc = 0.f;
-            for (int s = r; s < C; ++s) acc += sT[s * C + r] * sU[s * VT + j];
-            sY[e] = sB[r] * acc;
-        }
-        __syncthreads();
-        for (int e = t; e < K * VT; e += BNT) {  // dS = exp(G_m) (X + Qp^T dO - Kp^T beta dY)
-            const int c = e / VT, j = e % VT;
-            float acc = sX[e];
-            for (int r = 0; r < C; ++r) acc += sQp[r * K + c] * sO[r * VT + j] - sKp[r * K + c] * sY[r * VT + j];
-            sX[e] = sE[c] * acc;
+        if (ci > 0) fetch(ci - 1);
+        for (int c2 = 0; c2 < K; ++c2) {
+            const float dv = sS[c2 * VT + j];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) D[i] += sM[c2 * PK + cb + i] * dv;
         }
     }
-    __syncthreads();
     if (ds0)
-        for (int e = t; e < K * VT; e += BNT) ds0[sbase + (size_t)(e / VT) * V + e % VT] = sX[e];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) ds0[sbase + (size_t)(cb + i) * V] = D[i];
 }
 
 // ------------------------------------------------------------------ pass 3
@@ -388,21 +513,24 @@ __global__ __launch_bounds__(GNT) void bwd_grads_kernel(
     const float *__restrict__ Sst, const float *__restrict__ dSe, float *__restrict__ dq,
     float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dg,
     float *__restrict__ dbeta) {
-    using Rc = BwdRec<K, C>;
+    using Rc = BwdRec<K, V, C>;
     // thread t owns elements t + GNT i of the [C][K] and [C][C] accumulators:
     // channel (or column) t % K (t % C) of rows t / K + RK i (t / C + RC i)
     constexpr int MCK = C * K / GNT, MCC = C * C / GNT, RK = GNT / K, RC = GNT / C;
     static_assert(C * K % GNT == 0 && C * C % GNT == 0 && GNT % K == 0 && GNT % C == 0,
                   "ownership must tile the workgroup");
     extern __shared__ float smem[];
-    float *sKp = smem;           // [C][K]  (finally D)
-    float *sKm = sKp + C * K;    // [C][K]
-    float *sQp = sKm + C * K;    // [C][K]
-    float *sT = sQp + C * K;     // [C][C]  (finally Gk)
-    float *sP = sT + C * C;      // [C][C]  (finally dA)
-    float *sS = sP + C * C;      // [K][VS] S'
-    float *sX = sS + K * VS;     // [K][VS] X = F dS_end
-    float *sR = sX + K * VS;     // [C][VS] R = V - Kp S'
+    // row pitches PK = K + 1, PC = C + 1, PS = VS + 1: a wave reading one
+    // column of a tile touches distinct banks
+    constexpr int PK = K + 1, PC = C + 1, PS = VS + 1;
+    float *sKp = smem;           // [C][PK]  (finally D)
+    float *sKm = sKp + C * PK;   // [C][PK]
+    float *sQp = sKm + C * PK;   // [C][PK]
+    float *sT = sQp + C * PK;    // [C][PC]  (finally Gk)
+    float *sP = sT + C * PC;     // [C][PC]  (finally dA)
+    float *sS = sP + C * PC;     // [K][PS] S'
+    float *sX = sS + K * PS;     // [K][PS] X = F dS_end
+    float *sR = sX + K * PS;     // [C][VS] R = V - Kp S'
     float *sO = sR + C * VS;     // [C][VS] dO
     float *sU = sO + C * VS;     // [C][VS] U
     float *sDU = sU + C * VS;    // [C][VS] dU
@@ -413,8 +541,8 @@ __global__ __launch_bounds__(GNT) void bwd_grads_kernel(
     float *sH = sE + K;          // [K]   rowsum(S_end * dS_end)
     float *sDb = sH + K;         // [C]   dbeta
     int *red = reinterpret_cast<int *>(sDb + C);
-    float *sDp = sS;             // [C][C] dP, over the column buffers after the loop
-    static_assert(C * C <= 2 * K * VS + 5 * C * VS, "dP must fit the column buffers");
+    float *sDp = sS;             // [C][PC] dP, over the column buffers after the loop
+    static_assert(C * PC <= 2 * K * PS + 5 * C * VS, "dP must fit the column buffers");
 
     const int gc = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
     int n, ci;
@@ -427,15 +555,11 @@ __global__ __launch_bounds__(GNT) void bwd_grads_kernel(
     const float *S0c = Sst + ((size_t)gc * H + h) * K * V;
     const float *dSc = dSe + ((size_t)gc * H + h) * K * V;
 
-    for (int e = t; e < C * K; e += GNT) {
-        sKp[e] = rec[Rc::KP + e];
-        sKm[e] = rec[Rc::KM + e];
-        sQp[e] = rec[Rc::QP + e];
-    }
-    for (int e = t; e < C * C; e += GNT) {
-        sT[e] = rec[Rc::TT + e];
-        sP[e] = rec[Rc::PP + e];
-    }
+    rows_to_lds<C, K, PK, GNT>(sKp, rec + Rc::KP);
+    rows_to_lds<C, K, PK, GNT>(sKm, rec + Rc::KM);
+    rows_to_lds<C, K, PK, GNT>(sQp, rec + Rc::QP);
+    rows_to_lds<C, C, PC, GNT>(sT, rec + Rc::TT);
+    rows_to_lds<C, C, PC, GNT>(sP, rec + Rc::PP);
     for (int r = t; r < C; r += GNT) {
         sB[r] = rec[Rc::BETA + r];
         sDb[r] = 0.f;
@@ -457,8 +581,8 @@ __global__ __launch_bounds__(GNT) void bwd_grads_kernel(
         __syncthreads();
         for (int e = t; e < K * VS; e += GNT) {
             const int c = e / VS, j = e % VS;
-            sS[e] = sE[c] * S0c[(size_t)c * V + j0 + j];
-            sX[e] = sF[c] * dSc[(size_t)c * V + j0 + j];
+            sS[c * PS + j] = sE[c] * S0c[(size_t)c * V + j0 + j];
+            sX[c * PS + j] = sF[c] * dSc[(size_t)c * V + j0 + j];
         }
         for (int e = t; e < C * VS; e += GNT) {
             const int r = e / VS, j = e % VS;
@@ -471,15 +595,15 @@ __global__ __launch_bounds__(GNT) void bwd_grads_kernel(
             const int r = e / VS, j = e % VS;
             float acc = sR[e];
             #pragma unroll 4
-            for (int c = 0; c < K; ++c) acc -= sKp[r * K + c] * sS[c * VS + j];
+            for (int c = 0; c < K; ++c) acc -= sKp[r * PK + c] * sS[c * PS + j];
             sR[e] = acc;
         }
         __syncthreads();
         for (int e = t; e < C * VS; e += GNT) {  // U = T Diag(beta) R;  dU = P^T dO
             const int r = e / VS, j = e % VS;
             float u = 0.f, du = 0.f;
-            for (int s = 0; s <= r; ++s) u += sT[r * C + s] * sB[s] * sR[s * VS + j];
-            for (int s = r; s < C; ++s) du += sP[s * C + r] * sO[s * VS + j];
+            for (int s = 0; s <= r; ++s) u += sT[r * PC + s] * sB[s] * sR[s * VS + j];
+            for (int s = r; s < C; ++s) du += sP[s * PC + r] * sO[s * VS + j];
             sU[e] = u;
             sDU[e] = du;
         }
@@ -488,17 +612,17 @@ __global__ __launch_bounds__(GNT) void bwd_grads_kernel(
             const int r = e / VS, j = e % VS;
             float acc = sDU[e];
             #pragma unroll 4
-            for (int c = 0; c < K; ++c) acc += sKm[r * K + c] * sX[c * VS + j];
+            for (int c = 0; c < K; ++c) acc += sKm[r * PK + c] * sX[c * PS + j];
             sDU[e] = acc;
         }
         // h[c] += sum_j S_end[c][j] dS_end[c][j], with S_end = F (S' + Km^T U), X = F dS_end
         for (int c = t; c < K; c += GNT) {
             float acc = 0.f;
             for (int j = 0; j < VS; ++j) {
-                float se = sS[c * VS + j];
+                float se = sS[c * PS + j];
                 #pragma unroll 4
-                for (int r = 0; r < C; ++r) se += sKm[r * K + c] * sU[r * VS + j];
-                acc += se * sX[c * VS + j];
+                for (int r = 0; r < C; ++r) se += sKm[r * PK + c] * sU[r * VS + j];
+                acc += se * sX[c * PS + j];
             }
             sH[c] += acc;
         }
@@ -507,7 +631,7 @@ __global__ __launch_bounds__(GNT) void bwd_grads_kernel(
             const int r = e / VS, j = e % VS;
             float acc = 0.f;
             #pragma unroll 4
-            for (int s = r; s < C; ++s) acc += sT[s * C + r] * sDU[s * VS + j];
+            for (int s = r; s < C; ++s) acc += sT[s * PC + r] * sDU[s * VS + j];
             sDY[e] = acc;
         }
         __syncthreads();
@@ -526,7 +650,7 @@ __global__ __launch_bounds__(GNT) void bwd_grads_kernel(
             const int c = t % K, r0 = t / K;
 #pragma unroll 1
             for (int j = 0; j < VS; ++j) {
-                const float sv = sS[c * VS + j], xv = sX[c * VS + j];
+                const float sv = sS[c * PS + j], xv = sX[c * PS + j];
 #pragma unroll
                 for (int i = 0; i < MCK; ++i) {
                     const int r = r0 + RK * i;
@@ -556,14 +680,14 @@ __global__ __launch_bounds__(GNT) void bwd_grads_kernel(
 #pragma unroll
     for (int i = 0; i < MCC; ++i) {
         const int e = t + GNT * i, r = e / C, s = e % C;
-        sP[e] = s < r ? aA[i] : 0.f;
-        sDp[e] = s <= r ? aP[i] : 0.f;
+        sP[r * PC + s] = s < r ? aA[i] : 0.f;
+        sDp[r * PC + s] = s <= r ? aP[i] : 0.f;
     }
-    for (int e = t; e < C * C; e += GNT) sT[e] = rec[Rc::GK + e];
+    rows_to_lds<C, C, PC, GNT>(sT, rec + Rc::GK);
     __syncthreads();
     for (int r = t; r < C; r += GNT) {  // dbeta += rowsum(Gk * dA)
         float acc = sDb[r];
-        for (int s = 0; s < r; ++s) acc += sT[r * C + s] * sP[r * C + s];
+        for (int s = 0; s < r; ++s) acc += sT[r * PC + s] * sP[r * PC + s];
         if (r < L) dbeta[(size_t)(c0 + r) * H + h] = acc;
     }
     // dKp += beta dA Km,  dQp += dP Km,  dKm += (beta dA)^T Kp + dP^T Qp
@@ -571,13 +695,13 @@ __global__ __launch_bounds__(GNT) void bwd_grads_kernel(
         const int c = t % K, r0 = t / K;
 #pragma unroll 1
         for (int s = 0; s < C; ++s) {
-            const float kms = sKm[s * K + c], bkp = sB[s] * sKp[s * K + c], qps = sQp[s * K + c];
+            const float kms = sKm[s * PK + c], bkp = sB[s] * sKp[s * PK + c], qps = sQp[s * PK + c];
 #pragma unroll
             for (int i = 0; i < MCK; ++i) {
                 const int r = r0 + RK * i;
-                aKp[i] += sB[r] * sP[r * C + s] * kms;
-                aQ[i] += sDp[r * C + s] * kms;
-                aKm[i] += sP[s * C + r] * bkp + sDp[s * C + r] * qps;
+                aKp[i] += sB[r] * sP[r * PC + s] * kms;
+                aQ[i] += sDp[r * PC + s] * kms;
+                aKm[i] += sP[s * PC + r] * bkp + sDp[s * PC + r] * qps;
             }
         }
     }
@@ -586,7 +710,8 @@ __global__ __launch_bounds__(GNT) void bwd_grads_kernel(
 #pragma unroll
     for (int i = 0; i < MCK; ++i) {
         const int e = t + GNT * i, r = e / K, c = e % K;
-        D[i] = aKp[i] * sKp[e] - aKm[i] * sKm[e] + aQ[i] * sQp[e] + (r == L - 1 ? sH[c] : 0.f);
+        D[i] = aKp[i] * sKp[r * PK + c] - aKm[i] * sKm[r * PK + c] + aQ[i] * sQp[r * PK + c] +
+               (r == L - 1 ? sH[c] : 0.f);
         if (r < L) {
             const float ep = rec[Rc::EE + e];
             const size_t off = ((size_t)(c0 + r) * H + h) * K + c;
@@ -596,19 +721,22 @@ __global__ __launch_bounds__(GNT) void bwd_grads_kernel(
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < MCK; ++i) sKp[t + GNT * i] = D[i];
+    for (int i = 0; i < MCK; ++i) {
+        const int e = t + GNT * i;
+        sKp[(e / K) * PK + e % K] = D[i];
+    }
     __syncthreads();
     for (int c = t; c < K; c += GNT) {  // dg = reverse running sum of D down each channel
         float acc = 0.f;
         for (int r = L - 1; r >= 0; --r) {
-            acc += sKp[r * K + c];
+            acc += sKp[r * PK + c];
             dg[((size_t)(c0 + r) * H + h) * K + c] = acc;
         }
     }
 }
 
 template <int K, int V, int C>
-size_t rec_bytes() { return sizeof(float) * BwdRec<K, C>::floats; }
+size_t rec_bytes() { return sizeof(float) * BwdRec<K, V, C>::floats; }
 
 // Upper bound on the packed chunk count of N sequences over total_T tokens.
 size_t chunk_cap(int N, int totalT, int fixedT, bool packed, int C) {
@@ -629,20 +757,24 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
                         hipStream_t stream) {
     const size_t cap = chunk_cap(N, totalT, fixedT, cu != nullptr, C);
     float *recs = static_cast<float *>(workspace);
-    float *Sst = recs + cap * H * BwdRec<K, C>::floats;
+    float *Sst = recs + cap * H * BwdRec<K, V, C>::floats;
     float *dSe = Sst + cap * H * (size_t)K * V;
     const size_t red = sizeof(int) * BNT, red3 = sizeof(int) * GNT;
-    const size_t lds0 = sizeof(float) * (4 * C * K + C + K) + red;
-    const size_t lds1 = sizeof(float) * (2 * C * K + C * C + K * VT + 2 * C * VT + C + 2 * K) + red;
-    const size_t lds2 = sizeof(float) * (3 * C * K + 2 * C * C + K * VT + 3 * C * VT + C + 2 * K) + red;
-    const size_t lds3 = sizeof(float) * (3 * C * K + 2 * C * C + 2 * K * VS + 5 * C * VS + 2 * C + 3 * K) + red3;
-    static std::atomic<uint64_t> set0{0}, set1{0}, set2{0}, set3{0};
+    const size_t lds0 = sizeof(float) * (3 * C * (K + 1) + C * K + C + K) + red;
+    const size_t ldsT = sizeof(float) * (3 * C * (K + 1) + 2 * C * (C + 1) + C + 2 * K) + red;
+    const size_t lds1 = sizeof(float) * (K * (K + 1) + K * VT) + red;
+    const size_t lds2 = lds1;
+    const size_t lds3 = sizeof(float) * (3 * C * (K + 1) + 2 * C * (C + 1) + 2 * K * (VS + 1) +
+                                         5 * C * VS + 2 * C + 3 * K) + red3;
+    static std::atomic<uint64_t> set0{0}, setT{0}, set1{0}, set2{0}, set3{0};
     auto k0 = bwd_prep_kernel<K, V, C, TIn>;
-    auto k1 = bwd_states_kernel<K, V, C, VT, TIn>;
+    auto kT = bwd_trans_kernel<K, V, C, TIn>;
+    auto k1 = bwd_states_kernel<K, V, C, VT>;
     auto k2 = bwd_dstate_kernel<K, V, C, VT>;
     auto k3 = bwd_grads_kernel<K, V, C, VS, GNT, TIn>;
     hipError_t e;
     if ((e = ensure_dynamic_lds(reinterpret_cast<const void *>(k0), (int)lds0, set0)) != hipSuccess) return e;
+    if ((e = ensure_dynamic_lds(reinterpret_cast<const void *>(kT), (int)ldsT, setT)) != hipSuccess) return e;
     if ((e = ensure_dynamic_lds(reinterpret_cast<const void *>(k1), (int)lds1, set1)) != hipSuccess) return e;
     if ((e = ensure_dynamic_lds(reinterpret_cast<const void *>(k2), (int)lds2, set2)) != hipSuccess) return e;
     if ((e = ensure_dynamic_lds(reinterpret_cast<const void *>(k3), (int)lds3, set3)) != hipSuccess) return e;
@@ -653,11 +785,14 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
         hipLaunchKernelGGL(k0, dim3((unsigned)cap, H), dim3(BNT), lds0, stream, tq, tk, tg, tb, cu, N,
                            fixedT, totalT, H, recs);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(k1, dim3(V / VT, H, N), dim3(BNT), lds1, stream, tv, s0, cu, fixedT,
+        hipLaunchKernelGGL(kT, dim3((unsigned)cap, H), dim3(BNT), ldsT, stream, tv, dout, cu, N,
+                           fixedT, totalT, H, recs);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(k1, dim3(V / VT, H, N), dim3(BNT), lds1, stream, s0, cu, fixedT,
                            totalT, H, recs, Sst);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k2, dim3(V / VT, H, N), dim3(BNT), lds2, stream, dout, dsT, ds0, cu, fixedT,
+    hipLaunchKernelGGL(k2, dim3(V / VT, H, N), dim3(BNT), lds2, stream, dsT, ds0, cu, fixedT,
                        totalT, H, recs, dSe);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (cap > 0) {

@@ -244,10 +244,11 @@ def test_binding_prologue_flags():
 
 def test_backward_argument_errors(lib):
     need = lib.kda_bwd_workspace_bytes(1, 64, 1, 128, 128, 64)
-    assert need == 1 * 1 * (4 * (4 * 64 * 128 + 3 * 64 * 64 + 64 + 2 * 128) + 2 * 4 * 128 * 128)
+    rec = lambda C, K: 4 * (4 * C * K + 3 * C * C + C + 2 * K + 3 * K * K)   # bytes per (chunk, head)
+    assert need == 1 * 1 * (rec(64, 128) + 2 * 4 * 128 * 128)
     assert lib.kda_bwd_workspace_bytes(1, 64, 1, 64, 64, 64) == 0        # unsupported
     assert lib.kda_bwd_workspace_bytes(3, 100, 2, 32, 32, 16) == \
-        ((100 + 15 * 3) // 16) * 2 * (4 * (4 * 16 * 32 + 3 * 16 * 16 + 16 + 2 * 32) + 2 * 4 * 32 * 32)
+        ((100 + 15 * 3) // 16) * 2 * (rec(16, 32) + 2 * 4 * 32 * 32)
     f = lib.kda_chunk_bwd
 
     def call(B=1, T=64, H=1, K=128, C=64, ind=1, null=None, ws=FAKE, nws=None):
