@@ -43,7 +43,9 @@
 namespace kda {
 namespace {
 
-constexpr int BNT = 256;  // threads per workgroup of the prep and state-chain kernels
+constexpr int BNT = 256;  // threads per workgroup of the state-chain kernels
+constexpr int PNT = 512;  // threads per workgroup of the record and transition kernels (one
+                          // workgroup per CU by LDS; eight waves hide LDS latency)
 
 // Record of one (chunk, head), in floats.  MM, NN, NB: the chunk's state
 // transition S_end = MM S_start + NN and its adjoint dS_start = MM^T dS_end + NB.
@@ -190,7 +192,7 @@ __device__ __forceinline__ void rows_to_lds(float *dst, const float *src) {
 
 // ------------------------------------------------------------------ pass 0
 template <int K, int V, int C, typename TIn>
-__global__ __launch_bounds__(BNT) void bwd_prep_kernel(
+__global__ __launch_bounds__(PNT) void bwd_prep_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ g,
     const TIn *__restrict__ beta, const int32_t *__restrict__ cu, int N, int fixedT, int totalT,
     int H, float *__restrict__ ws) {
@@ -203,12 +205,12 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(
     float *sX = sQp + C * PK;      // [C][K]: G, later Gk [C][C] and T [C][C]
     float *sB = sX + C * K;        // [C]
     float *sGm = sB + C;           // [K]
-    int *red = reinterpret_cast<int *>(sGm + K);  // [BNT]
+    int *red = reinterpret_cast<int *>(sGm + K);  // [PNT]
     static_assert(2 * C * C <= C * K, "Gk and T must fit the G buffer");
 
     const int gc = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
     int n, ci;
-    locate_chunk<BNT>(cu, N, fixedT, totalT, C, gc, n, ci, red);
+    locate_chunk<PNT>(cu, N, fixedT, totalT, C, gc, n, ci, red);
     if (n < 0) return;
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
@@ -216,13 +218,13 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(
     const int m = min(C / 2 - 1, L - 1);  // reference row
     float *rec = ws + ((size_t)gc * H + h) * Rc::floats;
 
-    for (int e = t; e < C * K; e += BNT) {
+    for (int e = t; e < C * K; e += PNT) {
         const int r = e / K, c = e % K;
         sX[e] = r < L ? to_f32(g[((size_t)(c0 + r) * H + h) * K + c]) : 0.f;
     }
-    for (int r = t; r < C; r += BNT) sB[r] = r < L ? to_f32(beta[(size_t)(c0 + r) * H + h]) : 0.f;
+    for (int r = t; r < C; r += PNT) sB[r] = r < L ? to_f32(beta[(size_t)(c0 + r) * H + h]) : 0.f;
     __syncthreads();
-    for (int c = t; c < K; c += BNT) {  // running sum down each channel
+    for (int c = t; c < K; c += PNT) {  // running sum down each channel
         float acc = 0.f;
         for (int r = 0; r < C; ++r) {
             acc += sX[r * K + c];
@@ -230,15 +232,15 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(
         }
     }
     __syncthreads();
-    for (int c = t; c < K; c += BNT) {
+    for (int c = t; c < K; c += PNT) {
         const float gm = sX[m * K + c];
         sGm[c] = gm;
         rec[Rc::FF + c] = fast_exp(sX[(L - 1) * K + c] - gm);
         rec[Rc::EGM + c] = fast_exp(gm);
     }
-    for (int r = t; r < C; r += BNT) rec[Rc::BETA + r] = sB[r];
+    for (int r = t; r < C; r += PNT) rec[Rc::BETA + r] = sB[r];
     __syncthreads();
-    for (int e = t; e < C * K; e += BNT) {
+    for (int e = t; e < C * K; e += PNT) {
         const int r = e / K, c = e % K;
         const float d = sX[e] - sGm[c];
         const float ep = fast_exp(d), em = fast_exp(-d);
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(
     __syncthreads();
     // Gram blocks: Gk strictly lower, P lower with the diagonal
     float *sGk = sX, *sT = sX + C * C;
-    for (int e = t; e < C * C; e += BNT) {
+    for (int e = t; e < C * C; e += PNT) {
         const int r = e / C, s = e % C;
         float a = 0.f, p = 0.f;
         if (s <= r) {
@@ -272,17 +274,17 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(
     }
     __syncthreads();
     // T = (I + Diag(beta) Gk)^-1, row by row: T_r = e_r - beta_r sum_{s<r} Gk_rs T_s
-    for (int e = t; e < C * C; e += BNT) sT[e] = (e / C == e % C) ? 1.f : 0.f;
+    for (int e = t; e < C * C; e += PNT) sT[e] = (e / C == e % C) ? 1.f : 0.f;
     __syncthreads();
     for (int r = 1; r < C; ++r) {
-        for (int col = t; col < r; col += BNT) {
+        for (int col = t; col < r; col += PNT) {
             float acc = 0.f;
             for (int s = col; s < r; ++s) acc += sGk[r * C + s] * sT[s * C + col];
             sT[r * C + col] = -sB[r] * acc;
         }
         __syncthreads();
     }
-    for (int e = t; e < C * C; e += BNT) rec[Rc::TT + e] = sT[e];
+    for (int e = t; e < C * C; e += PNT) rec[Rc::TT + e] = sT[e];
 }
 
 // -------------------------------------------------------------- pass 0b
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(BNT) void bwd_prep_kernel(
 // Three [C][D+1] buffers are reused in turn (pitch D+1: rows fall on
 // different banks when a wave reads one column).
 template <int K, int V, int C, typename TIn>
-__global__ __launch_bounds__(BNT) void bwd_trans_kernel(
+__global__ __launch_bounds__(PNT) void bwd_trans_kernel(
     const TIn *__restrict__ v, const float *__restrict__ dout, const int32_t *__restrict__ cu,
     int N, int fixedT, int totalT, int H, float *__restrict__ recs) {
     using Rc = BwdRec<K, V, C>;
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(BNT) void bwd_trans_kernel(
 
     const int gc = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
     int n, ci;
-    locate_chunk<BNT>(cu, N, fixedT, totalT, C, gc, n, ci, red);
+    locate_chunk<PNT>(cu, N, fixedT, totalT, C, gc, n, ci, red);
     if (n < 0) return;
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
@@ -315,11 +317,11 @@ __global__ __launch_bounds__(BNT) void bwd_trans_kernel(
     float *rec = recs + ((size_t)gc * H + h) * Rc::floats;
 
     auto load_rows = [&](float *dst, size_t src_off) {
-        rows_to_lds<C, K, PD, BNT>(dst, rec + src_off);
+        rows_to_lds<C, K, PD, PNT>(dst, rec + src_off);
     };
     // out[r][j] = sum_{s<=r} T[r][s] beta_s in[s][j]   (r < C, j < K)
     auto tri_apply = [&](float *out, const float *in) {
-        for (int e = t; e < C * K; e += BNT) {
+        for (int e = t; e < C * K; e += PNT) {
             const int r = e / K, j = e % K;
             float acc = 0.f;
             for (int s2 = 0; s2 <= r; ++s2) acc += sT[r * PC + s2] * sB[s2] * in[s2 * PD + j];
@@ -328,7 +330,7 @@ __global__ __launch_bounds__(BNT) void bwd_trans_kernel(
     };
     // out[c][j] = sum_r a[r][c] b[r][j] for RB consecutive c per thread
     auto at_b = [&](const float *a, const float *b, auto &&store) {
-        for (int e = t; e < (K / RB) * K; e += BNT) {
+        for (int e = t; e < (K / RB) * K; e += PNT) {
             const int cb = (e / K) * RB, j = e % K;
             float acc[RB] = {};
             for (int r = 0; r < C; ++r) {
@@ -341,12 +343,12 @@ __global__ __launch_bounds__(BNT) void bwd_trans_kernel(
         }
     };
 
-    for (int e = t; e < C * C; e += BNT) {
+    for (int e = t; e < C * C; e += PNT) {
         sT[(e / C) * PC + e % C] = rec[Rc::TT + e];
         sP[(e / C) * PC + e % C] = rec[Rc::PP + e];
     }
-    for (int r = t; r < C; r += BNT) sB[r] = rec[Rc::BETA + r];
-    for (int c = t; c < K; c += BNT) {
+    for (int r = t; r < C; r += PNT) sB[r] = rec[Rc::BETA + r];
+    for (int c = t; c < K; c += PNT) {
         sF[c] = rec[Rc::FF + c];
         sE[c] = rec[Rc::EGM + c];
     }
@@ -356,14 +358,14 @@ __global__ __launch_bounds__(BNT) void bwd_trans_kernel(
     __syncthreads();
     load_rows(b0, Rc::QP);
     __syncthreads();
-    for (int e = t; e < C * K; e += BNT) {  // Q^ = Qp - P W
+    for (int e = t; e < C * K; e += PNT) {  // Q^ = Qp - P W
         const int r = e / K, j = e % K;
         float acc = b0[r * PD + j];
         for (int s2 = 0; s2 <= r; ++s2) acc -= sP[r * PC + s2] * b1[s2 * PD + j];
         b2[r * PD + j] = acc;
     }
     __syncthreads();
-    for (int e = t; e < C * V; e += BNT) {
+    for (int e = t; e < C * V; e += PNT) {
         const int r = e / V, j = e % V;
         b0[r * PD + j] = r < L ? dout[((size_t)(c0 + r) * H + h) * V + j] : 0.f;
     }
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(BNT) void bwd_trans_kernel(
         rec[Rc::MM + (size_t)c * K + j] = sF[c] * ((c == j ? 1.f : 0.f) - x) * sE[j];
     });
     __syncthreads();
-    for (int e = t; e < C * V; e += BNT) {
+    for (int e = t; e < C * V; e += PNT) {
         const int r = e / V, j = e % V;
         b1[r * PD + j] = r < L ? to_f32(v[((size_t)(c0 + r) * H + h) * V + j]) : 0.f;
     }
@@ -759,9 +761,9 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
     float *recs = static_cast<float *>(workspace);
     float *Sst = recs + cap * H * BwdRec<K, V, C>::floats;
     float *dSe = Sst + cap * H * (size_t)K * V;
-    const size_t red = sizeof(int) * BNT, red3 = sizeof(int) * GNT;
-    const size_t lds0 = sizeof(float) * (3 * C * (K + 1) + C * K + C + K) + red;
-    const size_t ldsT = sizeof(float) * (3 * C * (K + 1) + 2 * C * (C + 1) + C + 2 * K) + red;
+    const size_t red = sizeof(int) * BNT, redP = sizeof(int) * PNT, red3 = sizeof(int) * GNT;
+    const size_t lds0 = sizeof(float) * (3 * C * (K + 1) + C * K + C + K) + redP;
+    const size_t ldsT = sizeof(float) * (3 * C * (K + 1) + 2 * C * (C + 1) + C + 2 * K) + redP;
     const size_t lds1 = sizeof(float) * (K * (K + 1) + K * VT) + red;
     const size_t lds2 = lds1;
     const size_t lds3 = sizeof(float) * (3 * C * (K + 1) + 2 * C * (C + 1) + 2 * K * (VS + 1) +
@@ -782,10 +784,10 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
     const TIn *tv = static_cast<const TIn *>(v), *tg = static_cast<const TIn *>(g);
     const TIn *tb = static_cast<const TIn *>(beta);
     if (cap > 0) {
-        hipLaunchKernelGGL(k0, dim3((unsigned)cap, H), dim3(BNT), lds0, stream, tq, tk, tg, tb, cu, N,
+        hipLaunchKernelGGL(k0, dim3((unsigned)cap, H), dim3(PNT), lds0, stream, tq, tk, tg, tb, cu, N,
                            fixedT, totalT, H, recs);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(kT, dim3((unsigned)cap, H), dim3(BNT), ldsT, stream, tv, dout, cu, N,
+        hipLaunchKernelGGL(kT, dim3((unsigned)cap, H), dim3(PNT), ldsT, stream, tv, dout, cu, N,
                            fixedT, totalT, H, recs);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(k1, dim3(V / VT, H, N), dim3(BNT), lds1, stream, s0, cu, fixedT,
@@ -825,8 +827,8 @@ hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const v
                             void *workspace, hipStream_t stream) {
     if (N == 0 || H == 0) return hipSuccess;
     if (K == 128 && V == 128 && C == 64)
-        return in_bf16 ? launch_bwd_t<128, 128, 64, 16, 8, 512, bf16_t>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream)
-                       : launch_bwd_t<128, 128, 64, 16, 8, 512, float>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream);
+        return in_bf16 ? launch_bwd_t<128, 128, 64, 4, 8, 512, bf16_t>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream)
+                       : launch_bwd_t<128, 128, 64, 4, 8, 512, float>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream);
     if (K == 32 && V == 32 && C == 16)
         return in_bf16 ? launch_bwd_t<32, 32, 16, 16, 8, 256, bf16_t>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream)
                        : launch_bwd_t<32, 32, 16, 16, 8, 256, float>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream);
