@@ -23,7 +23,7 @@
 // G_m cancels from the forward result, so its own gradient is zero and it is
 // treated as a constant.
 //
-// Five launches:
+// Six launches:
 //   bwd_prep_kernel    (chunk, head), all chunks at once: Kp, Km, Qp, E, Gk,
 //                      P, T, beta, F, exp(G_m) into the chunk's record;
 //   bwd_trans_kernel   (chunk, head): the chunk's state transition
@@ -34,18 +34,21 @@
 //   bwd_dstate_kernel  (sequence, head, value tile): the reverse chain
 //                      dS_start = MM^T dS_end + NB, chunk after chunk from
 //                      the last, and ds0;
-//   bwd_grads_kernel   (chunk, head): every input gradient of the chunk.
-// The state chains are column-separable (value tiles need no communication);
-// the gradients of q, k, g and beta sum over all value columns, so the last
-// pass loops over the columns in sub-tiles and accumulates in registers.
+//   bwd_udy_kernel     (chunk, head), value tile after value tile: R, U,
+//                      dU, dY and dv, and each tile's shares of dbeta and
+//                      rowsum(S_end * dS_end);
+//   bwd_kgrad_kernel   (chunk, head): the gradients that sum over all value
+//                      columns (of q, k, g and beta), as register-tiled
+//                      products over value slices.
+// The state chains are column-separable (value tiles need no communication).
 #include "kda_common.hpp"
 
 namespace kda {
 namespace {
 
 constexpr int BNT = 256;  // threads per workgroup of the state-chain kernels
-constexpr int PNT = 512;  // threads per workgroup of the record and transition kernels (one
-                          // workgroup per CU by LDS; eight waves hide LDS latency)
+constexpr int PNT = 512;  // threads per workgroup of the record, transition and column
+                          // passes (one workgroup per CU by LDS; eight waves hide LDS latency)
 
 // Record of one (chunk, head), in floats.  MM, NN, NB: the chunk's state
 // transition S_end = MM S_start + NN and its adjoint dS_start = MM^T dS_end + NB.
@@ -261,11 +264,17 @@ __global__ __launch_bounds__(PNT) void bwd_prep_kernel(
         const int r = e / C, s = e % C;
         float a = 0.f, p = 0.f;
         if (s <= r) {
-            for (int c = 0; c < K; ++c) {
-                const float km = sKm[s * PK + c];
-                a += sKp[r * PK + c] * km;
-                p += sQp[r * PK + c] * km;
+            float a4[4] = {}, p4[4] = {};  // four partial sums: shorter dependency chains
+            for (int c = 0; c < K; c += 4) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float km = sKm[s * PK + c + u];
+                    a4[u] += sKp[r * PK + c + u] * km;
+                    p4[u] += sQp[r * PK + c + u] * km;
+                }
             }
+            a = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+            p = (p4[0] + p4[1]) + (p4[2] + p4[3]);
         }
         const float gk = s < r ? a : 0.f;
         sGk[e] = gk;
@@ -323,9 +332,14 @@ __global__ __launch_bounds__(PNT) void bwd_trans_kernel(
     auto tri_apply = [&](float *out, const float *in) {
         for (int e = t; e < C * K; e += PNT) {
             const int r = e / K, j = e % K;
-            float acc = 0.f;
-            for (int s2 = 0; s2 <= r; ++s2) acc += sT[r * PC + s2] * sB[s2] * in[s2 * PD + j];
-            out[r * PD + j] = acc;
+            float a0 = 0.f, a1 = 0.f;
+            int s2 = 0;
+            for (; s2 + 1 <= r; s2 += 2) {
+                a0 += sT[r * PC + s2] * sB[s2] * in[s2 * PD + j];
+                a1 += sT[r * PC + s2 + 1] * sB[s2 + 1] * in[(s2 + 1) * PD + j];
+            }
+            if (s2 == r) a0 += sT[r * PC + r] * sB[r] * in[r * PD + j];
+            out[r * PD + j] = a0 + a1;
         }
     };
     // out[c][j] = sum_r a[r][c] b[r][j] for RB consecutive c per thread
@@ -360,9 +374,14 @@ __global__ __launch_bounds__(PNT) void bwd_trans_kernel(
     __syncthreads();
     for (int e = t; e < C * K; e += PNT) {  // Q^ = Qp - P W
         const int r = e / K, j = e % K;
-        float acc = b0[r * PD + j];
-        for (int s2 = 0; s2 <= r; ++s2) acc -= sP[r * PC + s2] * b1[s2 * PD + j];
-        b2[r * PD + j] = acc;
+        float a0 = 0.f, a1 = 0.f;
+        int s2 = 0;
+        for (; s2 + 1 <= r; s2 += 2) {
+            a0 += sP[r * PC + s2] * b1[s2 * PD + j];
+            a1 += sP[r * PC + s2 + 1] * b1[(s2 + 1) * PD + j];
+        }
+        if (s2 == r) a0 += sP[r * PC + r] * b1[r * PD + j];
+        b2[r * PD + j] = b0[r * PD + j] - (a0 + a1);
     }
     __syncthreads();
     for (int e = t; e < C * V; e += PNT) {
@@ -438,11 +457,17 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(
         }
         __syncthreads();
         if (ci + 1 < nch) fetch(ci + 1);
-        for (int c2 = 0; c2 < K; ++c2) {
-            const float sv = sS[c2 * VT + j];
+        float S2[RB] = {};  // odd columns: a second dependency chain per row
+        for (int c2 = 0; c2 < K; c2 += 2) {
+            const float sv = sS[c2 * VT + j], sw = sS[(c2 + 1) * VT + j];
 #pragma unroll
-            for (int i = 0; i < RB; ++i) S[i] += sM[(cb + i) * PK + c2] * sv;
+            for (int i = 0; i < RB; ++i) {
+                S[i] += sM[(cb + i) * PK + c2] * sv;
+                S2[i] += sM[(cb + i) * PK + c2 + 1] * sw;
+            }
         }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) S[i] += S2[i];
     }
 }
 
@@ -494,11 +519,17 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(
         }
         __syncthreads();
         if (ci > 0) fetch(ci - 1);
-        for (int c2 = 0; c2 < K; ++c2) {
-            const float dv = sS[c2 * VT + j];
+        float D2[RB] = {};  // odd rows of MM: a second dependency chain per column
+        for (int c2 = 0; c2 < K; c2 += 2) {
+            const float dv = sS[c2 * VT + j], dw = sS[(c2 + 1) * VT + j];
 #pragma unroll
-            for (int i = 0; i < RB; ++i) D[i] += sM[c2 * PK + cb + i] * dv;
+            for (int i = 0; i < RB; ++i) {
+                D[i] += sM[c2 * PK + cb + i] * dv;
+                D2[i] += sM[(c2 + 1) * PK + cb + i] * dw;
+            }
         }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) D[i] += D2[i];
     }
     if (ds0)
 #pragma unroll
@@ -506,229 +537,350 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(
 }
 
 // ------------------------------------------------------------------ pass 3
-// GNT threads: 512 at d = 128 (the per-thread accumulators stay in registers),
-// 256 at d = 32.
-template <int K, int V, int C, int VS, int GNT, typename TIn>
-__global__ __launch_bounds__(GNT) void bwd_grads_kernel(
+// Per (chunk, head): the column-separable part of the chunk's gradient, one
+// VT-column value tile after another with the chunk's operands staged once and
+// the next tile's inputs loaded into registers while the current one is
+// processed.  With S' = Diag(exp(G_m)) S_start and X = F dS_end on the tile:
+//   R = V - Kp S',  U = T Diag(beta) R,  dU = Km X + P^T dO,  dY = T^T dU,
+//   dv = Diag(beta) dY,
+// the tile's share of dbeta (rowsum(R * dY)) and of rowsum(S_end * dS_end)
+// (S_end = F (S' + Km^T U)), and U, dY stored transposed ([V][C] per
+// (chunk, head)) for pass 4.
+template <int K, int V, int C, int VT, typename TIn>
+__global__ __launch_bounds__(PNT) void bwd_udy_kernel(
     const TIn *__restrict__ v, const float *__restrict__ dout, const int32_t *__restrict__ cu,
     int N, int fixedT, int totalT, int H, const float *__restrict__ recs,
-    const float *__restrict__ Sst, const float *__restrict__ dSe, float *__restrict__ dq,
-    float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dg,
-    float *__restrict__ dbeta) {
+    const float *__restrict__ Sst, const float *__restrict__ dSe, float *__restrict__ UT,
+    float *__restrict__ dYT, float *__restrict__ dbp, float *__restrict__ hp,
+    float *__restrict__ dv) {
     using Rc = BwdRec<K, V, C>;
-    // thread t owns elements t + GNT i of the [C][K] and [C][C] accumulators:
-    // channel (or column) t % K (t % C) of rows t / K + RK i (t / C + RC i)
-    constexpr int MCK = C * K / GNT, MCC = C * C / GNT, RK = GNT / K, RC = GNT / C;
-    static_assert(C * K % GNT == 0 && C * C % GNT == 0 && GNT % K == 0 && GNT % C == 0,
-                  "ownership must tile the workgroup");
+    constexpr int PK = K + 1, PC = C + 1, PV = VT + 1, NVT = V / VT;
+    constexpr int QS = (K * VT + PNT - 1) / PNT, QV = (C * VT + PNT - 1) / PNT;  // per-thread loads
     extern __shared__ float smem[];
-    // row pitches PK = K + 1, PC = C + 1, PS = VS + 1: a wave reading one
-    // column of a tile touches distinct banks
-    constexpr int PK = K + 1, PC = C + 1, PS = VS + 1;
-    float *sKp = smem;           // [C][PK]  (finally D)
-    float *sKm = sKp + C * PK;   // [C][PK]
-    float *sQp = sKm + C * PK;   // [C][PK]
-    float *sT = sQp + C * PK;    // [C][PC]  (finally Gk)
-    float *sP = sT + C * PC;     // [C][PC]  (finally dA)
-    float *sS = sP + C * PC;     // [K][PS] S'
-    float *sX = sS + K * PS;     // [K][PS] X = F dS_end
-    float *sR = sX + K * PS;     // [C][VS] R = V - Kp S'
-    float *sO = sR + C * VS;     // [C][VS] dO
-    float *sU = sO + C * VS;     // [C][VS] U
-    float *sDU = sU + C * VS;    // [C][VS] dU
-    float *sDY = sDU + C * VS;   // [C][VS] dY
-    float *sB = sDY + C * VS;    // [C]
-    float *sF = sB + C;          // [K]
-    float *sE = sF + K;          // [K]
-    float *sH = sE + K;          // [K]   rowsum(S_end * dS_end)
-    float *sDb = sH + K;         // [C]   dbeta
-    int *red = reinterpret_cast<int *>(sDb + C);
-    float *sDp = sS;             // [C][PC] dP, over the column buffers after the loop
-    static_assert(C * PC <= 2 * K * PS + 5 * C * VS, "dP must fit the column buffers");
+    float *sKp = smem, *sKm = sKp + C * PK;              // [C][PK]
+    float *sT = sKm + C * PK, *sP = sT + C * PC;         // [C][PC]
+    float *sS = sP + C * PC, *sX = sS + K * PV;          // [K][PV]  S' (then S' + Km^T U), X
+    float *sR = sX + K * PV, *sO = sR + C * PV;          // [C][PV]  R, dO
+    float *sU = sO + C * PV, *sDU = sU + C * PV, *sDY = sDU + C * PV;  // [C][PV]
+    float *sB = sDY + C * PV, *sF = sB + C, *sE = sF + K;
+    int *red = reinterpret_cast<int *>(sE + K);
 
     const int gc = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
     int n, ci;
-    locate_chunk<GNT>(cu, N, fixedT, totalT, C, gc, n, ci, red);
+    locate_chunk<PNT>(cu, N, fixedT, totalT, C, gc, n, ci, red);
     if (n < 0) return;
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
     const int c0 = bos + ci * C, L = min(C, eos - c0);
-    const float *rec = recs + ((size_t)gc * H + h) * Rc::floats;
-    const float *S0c = Sst + ((size_t)gc * H + h) * K * V;
-    const float *dSc = dSe + ((size_t)gc * H + h) * K * V;
+    const size_t unit = (size_t)gc * H + h;
+    const float *rec = recs + unit * Rc::floats;
+    const float *S0c = Sst + unit * K * V, *dSc = dSe + unit * K * V;
 
-    rows_to_lds<C, K, PK, GNT>(sKp, rec + Rc::KP);
-    rows_to_lds<C, K, PK, GNT>(sKm, rec + Rc::KM);
-    rows_to_lds<C, K, PK, GNT>(sQp, rec + Rc::QP);
-    rows_to_lds<C, C, PC, GNT>(sT, rec + Rc::TT);
-    rows_to_lds<C, C, PC, GNT>(sP, rec + Rc::PP);
-    for (int r = t; r < C; r += GNT) {
-        sB[r] = rec[Rc::BETA + r];
-        sDb[r] = 0.f;
-    }
-    for (int c = t; c < K; c += GNT) {
+    float pS[QS], pX[QS], pV[QV], pO[QV];
+    auto fetch = [&](int j0) {  // tile inputs in registers
+#pragma unroll
+        for (int i = 0; i < QS; ++i) {
+            const int e = t + PNT * i;
+            if (e < K * VT) {
+                const int c = e / VT, j = e % VT;
+                pS[i] = S0c[(size_t)c * V + j0 + j];
+                pX[i] = dSc[(size_t)c * V + j0 + j];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < QV; ++i) {
+            const int e = t + PNT * i;
+            if (e < C * VT) {
+                const int r = e / VT, j = e % VT;
+                const size_t off = ((size_t)(c0 + r) * H + h) * V + j0 + j;
+                pV[i] = r < L ? to_f32(v[off]) : 0.f;
+                pO[i] = r < L ? dout[off] : 0.f;
+            }
+        }
+    };
+    fetch(0);
+    rows_to_lds<C, K, PK, PNT>(sKp, rec + Rc::KP);
+    rows_to_lds<C, K, PK, PNT>(sKm, rec + Rc::KM);
+    rows_to_lds<C, C, PC, PNT>(sT, rec + Rc::TT);
+    rows_to_lds<C, C, PC, PNT>(sP, rec + Rc::PP);
+    for (int r = t; r < C; r += PNT) sB[r] = rec[Rc::BETA + r];
+    for (int c = t; c < K; c += PNT) {
         sF[c] = rec[Rc::FF + c];
         sE[c] = rec[Rc::EGM + c];
-        sH[c] = 0.f;
+    }
+    __syncthreads();
+    for (int vt = 0; vt < NVT; ++vt) {
+        const int j0 = vt * VT;
+        if (vt > 0) __syncthreads();  // the previous tile's buffers are free
+#pragma unroll
+        for (int i = 0; i < QS; ++i) {
+            const int e = t + PNT * i;
+            if (e < K * VT) {
+                const int c = e / VT, j = e % VT;
+                sS[c * PV + j] = sE[c] * pS[i];
+                sX[c * PV + j] = sF[c] * pX[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < QV; ++i) {
+            const int e = t + PNT * i;
+            if (e < C * VT) {
+                const int r = e / VT, j = e % VT;
+                sR[r * PV + j] = pV[i];
+                sO[r * PV + j] = pO[i];
+            }
+        }
+        __syncthreads();
+        if (vt + 1 < NVT) fetch(j0 + VT);
+        for (int e = t; e < C * VT; e += PNT) {  // R = V - Kp S';  dU = P^T dO + Km X
+            const int r = e / VT, j = e % VT;
+            float a[4] = {}, d[4] = {};  // four partial sums: shorter dependency chains
+            for (int c = 0; c < K; c += 4) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    a[u] += sKp[r * PK + c + u] * sS[(c + u) * PV + j];
+                    d[u] += sKm[r * PK + c + u] * sX[(c + u) * PV + j];
+                }
+            }
+            float du = (d[0] + d[1]) + (d[2] + d[3]);
+            for (int s2 = r; s2 < C; ++s2) du += sP[s2 * PC + r] * sO[s2 * PV + j];
+            sR[r * PV + j] = sR[r * PV + j] - ((a[0] + a[1]) + (a[2] + a[3]));
+            sDU[r * PV + j] = du;
+        }
+        __syncthreads();
+        for (int e = t; e < C * VT; e += PNT) {  // U = T Diag(beta) R;  dY = T^T dU
+            const int r = e / VT, j = e % VT;
+            float u0 = 0.f, u1 = 0.f, y0 = 0.f, y1 = 0.f;
+            int s2 = 0;
+            for (; s2 + 1 <= r; s2 += 2) {
+                u0 += sT[r * PC + s2] * sB[s2] * sR[s2 * PV + j];
+                u1 += sT[r * PC + s2 + 1] * sB[s2 + 1] * sR[(s2 + 1) * PV + j];
+            }
+            if (s2 == r) u0 += sT[r * PC + r] * sB[r] * sR[r * PV + j];
+            for (s2 = r; s2 + 1 < C; s2 += 2) {
+                y0 += sT[s2 * PC + r] * sDU[s2 * PV + j];
+                y1 += sT[(s2 + 1) * PC + r] * sDU[(s2 + 1) * PV + j];
+            }
+            if (s2 < C) y0 += sT[s2 * PC + r] * sDU[s2 * PV + j];
+            const float dy = y0 + y1;
+            sU[r * PV + j] = u0 + u1;
+            sDY[r * PV + j] = dy;
+            if (r < L) dv[((size_t)(c0 + r) * H + h) * V + j0 + j] = sB[r] * dy;
+        }
+        __syncthreads();
+        for (int e = t; e < K * VT; e += PNT) {  // S' + Km^T U, in place
+            const int c = e / VT, j = e % VT;
+            float a[4] = {};
+            for (int r = 0; r < C; r += 4) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) a[u] += sKm[(r + u) * PK + c] * sU[(r + u) * PV + j];
+            }
+            sS[c * PV + j] += (a[0] + a[1]) + (a[2] + a[3]);
+        }
+        for (int r = t; r < C; r += PNT) {  // this tile's share of dbeta
+            float acc = 0.f;
+            for (int j = 0; j < VT; ++j) acc += sR[r * PV + j] * sDY[r * PV + j];
+            dbp[(unit * NVT + vt) * C + r] = acc;
+        }
+        for (int e = t; e < C * VT; e += PNT) {  // U and dY transposed: [V][C]
+            const int j = e / C, r = e % C;
+            UT[unit * V * C + (size_t)(j0 + j) * C + r] = sU[r * PV + j];
+            dYT[unit * V * C + (size_t)(j0 + j) * C + r] = sDY[r * PV + j];
+        }
+        __syncthreads();
+        for (int c = t; c < K; c += PNT) {  // and of rowsum(S_end * dS_end) = rowsum((S' + Km^T U) * X)
+            float acc = 0.f;
+            for (int j = 0; j < VT; ++j) acc += sS[c * PV + j] * sX[c * PV + j];
+            hp[(unit * NVT + vt) * K + c] = acc;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ pass 4
+// Per (chunk, head): the gradients that sum over all value columns,
+//   dQp = dO S'^T + dP Km,  dKp = -Diag(beta) dY S'^T + Diag(beta) dA Km,
+//   dKm = U X^T + (Diag(beta) dA)^T Kp + dP^T Qp,
+//   dA = -strict_lower(dY U^T),  dP = lower(dO U^T),
+// then dq, dk, dg and dbeta.  The products over the value columns run on
+// VB-column slices staged transposed in LDS, each thread holding an MR x MC
+// tile of the [C][K] sums and an AR x AC tile of the [C][C] sums.
+template <int K, int V, int C, int VT, int VB, int NT, int MR, int MC, int AR, int AC,
+          typename TIn>
+__global__ __launch_bounds__(NT) void bwd_kgrad_kernel(
+    const float *__restrict__ dout, const int32_t *__restrict__ cu, int N, int fixedT,
+    int totalT, int H, const float *__restrict__ recs, const float *__restrict__ Sst,
+    const float *__restrict__ dSe, const float *__restrict__ UT, const float *__restrict__ dYT,
+    const float *__restrict__ dbp, const float *__restrict__ hp, float *__restrict__ dq,
+    float *__restrict__ dk, float *__restrict__ dg, float *__restrict__ dbeta) {
+    using Rc = BwdRec<K, V, C>;
+    constexpr int NVT = V / VT, PK = K + 1, PC = C + 1, PTC = C + 4, PTK = K + 4;
+    constexpr int CG = K / MC, ACG = C / AC;  // column groups
+    static_assert((C / MR) * CG == NT && (C / AR) * ACG == NT, "tiles must cover the workgroup");
+    static_assert(V % VB == 0, "value slices");
+    extern __shared__ float smem[];
+    // value-column phase
+    float *sOT = smem, *sYT = sOT + VB * PTC, *sUT = sYT + VB * PTC;  // [VB][PTC]
+    float *sST = sUT + VB * PTC, *sXT = sST + VB * PTK;               // [VB][PTK]
+    // final phase (over the same space)
+    float *sKp = smem, *sKm = sKp + C * PK, *sQp = sKm + C * PK;      // [C][PK]
+    float *sA = sQp + C * PK, *sDp = sA + C * PC, *sG = sDp + C * PC; // [C][PC]
+    float *sB = sG + C * PC, *sH = sB + C, *sF = sH + K, *sE = sF + K;
+    int *red = reinterpret_cast<int *>(sE + K);
+    static_assert(3 * VB * PTC + 2 * VB * PTK <= 3 * C * PK + 3 * C * PC, "slices fit");
+
+    const int gc = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    int n, ci;
+    locate_chunk<NT>(cu, N, fixedT, totalT, C, gc, n, ci, red);
+    if (n < 0) return;
+    int bos, eos;
+    seq_bounds(cu, n, fixedT, totalT, bos, eos);
+    const int c0 = bos + ci * C, L = min(C, eos - c0);
+    const size_t unit = (size_t)gc * H + h;
+    const float *rec = recs + unit * Rc::floats;
+    const float *S0c = Sst + unit * K * V, *dSc = dSe + unit * K * V;
+    const float *Uc = UT + unit * V * C, *dYc = dYT + unit * V * C;
+    for (int r = t; r < C; r += NT) sB[r] = rec[Rc::BETA + r];
+    for (int c = t; c < K; c += NT) {
+        sF[c] = rec[Rc::FF + c];
+        sE[c] = rec[Rc::EGM + c];
     }
 
-    // owned accumulators: element e = t + GNT * i of a [C][K] (or [C][C]) array
-    float aQ[MCK], aKp[MCK], aKm[MCK], aA[MCC], aP[MCC];
+    const int r0 = (t / CG) * MR, cc0 = (t % CG) * MC;    // [C][K] tile
+    const int ar0 = (t / ACG) * AR, as0 = (t % ACG) * AC; // [C][C] tile
+    float aQ[MR][MC] = {}, aKp[MR][MC] = {}, aKm[MR][MC] = {}, aA[AR][AC] = {}, aP[AR][AC] = {};
+    for (int jb = 0; jb < V; jb += VB) {
+        __syncthreads();
+        for (int e = t; e < VB * C; e += NT) {
+            const int j = e / C, r = e % C;
+            sYT[j * PTC + r] = dYc[(size_t)(jb + j) * C + r];
+            sUT[j * PTC + r] = Uc[(size_t)(jb + j) * C + r];
+        }
+        for (int e = t; e < C * VB; e += NT) {
+            const int r = e / VB, j = e % VB;
+            sOT[j * PTC + r] = r < L ? dout[((size_t)(c0 + r) * H + h) * V + jb + j] : 0.f;
+        }
+        for (int e = t; e < K * VB; e += NT) {
+            const int c = e / VB, j = e % VB;
+            sST[j * PTK + c] = sE[c] * S0c[(size_t)c * V + jb + j];
+            sXT[j * PTK + c] = sF[c] * dSc[(size_t)c * V + jb + j];
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int j = 0; j < VB; ++j) {
+            float o[MR], y[MR], u[MR], sv[MC], xv[MC];
 #pragma unroll
-    for (int i = 0; i < MCK; ++i) aQ[i] = aKp[i] = aKm[i] = 0.f;
-#pragma unroll
-    for (int i = 0; i < MCC; ++i) aA[i] = aP[i] = 0.f;
-
-    for (int j0 = 0; j0 < V; j0 += VS) {
-        __syncthreads();
-        for (int e = t; e < K * VS; e += GNT) {
-            const int c = e / VS, j = e % VS;
-            sS[c * PS + j] = sE[c] * S0c[(size_t)c * V + j0 + j];
-            sX[c * PS + j] = sF[c] * dSc[(size_t)c * V + j0 + j];
-        }
-        for (int e = t; e < C * VS; e += GNT) {
-            const int r = e / VS, j = e % VS;
-            const size_t off = ((size_t)(c0 + r) * H + h) * V + j0 + j;
-            sR[e] = r < L ? to_f32(v[off]) : 0.f;
-            sO[e] = r < L ? dout[off] : 0.f;
-        }
-        __syncthreads();
-        for (int e = t; e < C * VS; e += GNT) {  // R = V - Kp S'
-            const int r = e / VS, j = e % VS;
-            float acc = sR[e];
-            #pragma unroll 4
-            for (int c = 0; c < K; ++c) acc -= sKp[r * PK + c] * sS[c * PS + j];
-            sR[e] = acc;
-        }
-        __syncthreads();
-        for (int e = t; e < C * VS; e += GNT) {  // U = T Diag(beta) R;  dU = P^T dO
-            const int r = e / VS, j = e % VS;
-            float u = 0.f, du = 0.f;
-            for (int s = 0; s <= r; ++s) u += sT[r * PC + s] * sB[s] * sR[s * VS + j];
-            for (int s = r; s < C; ++s) du += sP[s * PC + r] * sO[s * VS + j];
-            sU[e] = u;
-            sDU[e] = du;
-        }
-        __syncthreads();
-        for (int e = t; e < C * VS; e += GNT) {  // dU += Km X
-            const int r = e / VS, j = e % VS;
-            float acc = sDU[e];
-            #pragma unroll 4
-            for (int c = 0; c < K; ++c) acc += sKm[r * PK + c] * sX[c * PS + j];
-            sDU[e] = acc;
-        }
-        // h[c] += sum_j S_end[c][j] dS_end[c][j], with S_end = F (S' + Km^T U), X = F dS_end
-        for (int c = t; c < K; c += GNT) {
-            float acc = 0.f;
-            for (int j = 0; j < VS; ++j) {
-                float se = sS[c * PS + j];
-                #pragma unroll 4
-                for (int r = 0; r < C; ++r) se += sKm[r * PK + c] * sU[r * VS + j];
-                acc += se * sX[c * PS + j];
+            for (int i = 0; i < MR; ++i) {
+                o[i] = sOT[j * PTC + r0 + i];
+                y[i] = sYT[j * PTC + r0 + i];
+                u[i] = sUT[j * PTC + r0 + i];
             }
-            sH[c] += acc;
-        }
-        __syncthreads();
-        for (int e = t; e < C * VS; e += GNT) {  // dY = T^T dU
-            const int r = e / VS, j = e % VS;
-            float acc = 0.f;
-            #pragma unroll 4
-            for (int s = r; s < C; ++s) acc += sT[s * PC + r] * sDU[s * VS + j];
-            sDY[e] = acc;
-        }
-        __syncthreads();
-        for (int e = t; e < C * VS; e += GNT) {  // dv = beta dY
-            const int r = e / VS, j = e % VS;
-            if (r < L) dv[((size_t)(c0 + r) * H + h) * V + j0 + j] = sB[r] * sDY[e];
-        }
-        for (int r = t; r < C; r += GNT) {  // dbeta += rowsum(R * dY)
-            float acc = 0.f;
-            for (int j = 0; j < VS; ++j) acc += sR[r * VS + j] * sDY[r * VS + j];
-            sDb[r] += acc;
-        }
-        // owned [C][K] elements: dQp += dO S'^T, dKp -= beta dY S'^T, dKm += U X^T
-        // (column by column: the thread's channel operands are loaded once)
-        {
-            const int c = t % K, r0 = t / K;
-#pragma unroll 1
-            for (int j = 0; j < VS; ++j) {
-                const float sv = sS[c * PS + j], xv = sX[c * PS + j];
 #pragma unroll
-                for (int i = 0; i < MCK; ++i) {
-                    const int r = r0 + RK * i;
-                    aQ[i] += sO[r * VS + j] * sv;
-                    aKp[i] -= sB[r] * sDY[r * VS + j] * sv;
-                    aKm[i] += sU[r * VS + j] * xv;
+            for (int m = 0; m < MC; ++m) {
+                sv[m] = sST[j * PTK + cc0 + m];
+                xv[m] = sXT[j * PTK + cc0 + m];
+            }
+#pragma unroll
+            for (int i = 0; i < MR; ++i)
+#pragma unroll
+                for (int m = 0; m < MC; ++m) {
+                    aQ[i][m] += o[i] * sv[m];
+                    aKp[i][m] += y[i] * sv[m];
+                    aKm[i][m] += u[i] * xv[m];
                 }
-            }
-        }
-        // owned [C][C] elements: dA -= dY U^T, dP += dO U^T
-        {
-            const int sc = t % C, r0 = t / C;
-#pragma unroll 1
-            for (int j = 0; j < VS; ++j) {
-                const float u = sU[sc * VS + j];
+            float yy[AR], oo[AR], uu[AC];
 #pragma unroll
-                for (int i = 0; i < MCC; ++i) {
-                    const int r = r0 + RC * i;
-                    aA[i] -= sDY[r * VS + j] * u;
-                    aP[i] += sO[r * VS + j] * u;
-                }
+            for (int i = 0; i < AR; ++i) {
+                yy[i] = sYT[j * PTC + ar0 + i];
+                oo[i] = sOT[j * PTC + ar0 + i];
             }
+#pragma unroll
+            for (int m = 0; m < AC; ++m) uu[m] = sUT[j * PTC + as0 + m];
+#pragma unroll
+            for (int i = 0; i < AR; ++i)
+#pragma unroll
+                for (int m = 0; m < AC; ++m) {
+                    aA[i][m] -= yy[i] * uu[m];
+                    aP[i][m] += oo[i] * uu[m];
+                }
         }
     }
     __syncthreads();
-    // masked dA (strictly lower) and dP (lower) to LDS; Gk over T
+    // final phase: record operands, masked dA and dP, Gk, the tiles' partial sums
+    rows_to_lds<C, K, PK, NT>(sKp, rec + Rc::KP);
+    rows_to_lds<C, K, PK, NT>(sKm, rec + Rc::KM);
+    rows_to_lds<C, K, PK, NT>(sQp, rec + Rc::QP);
+    rows_to_lds<C, C, PC, NT>(sG, rec + Rc::GK);
 #pragma unroll
-    for (int i = 0; i < MCC; ++i) {
-        const int e = t + GNT * i, r = e / C, s = e % C;
-        sP[r * PC + s] = s < r ? aA[i] : 0.f;
-        sDp[r * PC + s] = s <= r ? aP[i] : 0.f;
+    for (int i = 0; i < AR; ++i)
+#pragma unroll
+        for (int m = 0; m < AC; ++m) {
+            const int r = ar0 + i, s2 = as0 + m;
+            sA[r * PC + s2] = s2 < r ? aA[i][m] : 0.f;
+            sDp[r * PC + s2] = s2 <= r ? aP[i][m] : 0.f;
+        }
+    for (int c = t; c < K; c += NT) {
+        float acc = 0.f;
+        for (int w = 0; w < NVT; ++w) acc += hp[(unit * NVT + w) * K + c];
+        sH[c] = acc;
     }
-    rows_to_lds<C, C, PC, GNT>(sT, rec + Rc::GK);
     __syncthreads();
-    for (int r = t; r < C; r += GNT) {  // dbeta += rowsum(Gk * dA)
-        float acc = sDb[r];
-        for (int s = 0; s < r; ++s) acc += sT[r * PC + s] * sP[r * PC + s];
+    for (int r = t; r < C; r += NT) {  // dbeta = tiles' rowsum(R * dY) + rowsum(Gk * dA)
+        float acc = 0.f;
+        for (int w = 0; w < NVT; ++w) acc += dbp[(unit * NVT + w) * C + r];
+        for (int s2 = 0; s2 < r; ++s2) acc += sG[r * PC + s2] * sA[r * PC + s2];
         if (r < L) dbeta[(size_t)(c0 + r) * H + h] = acc;
     }
-    // dKp += beta dA Km,  dQp += dP Km,  dKm += (beta dA)^T Kp + dP^T Qp
-    {
-        const int c = t % K, r0 = t / K;
-#pragma unroll 1
-        for (int s = 0; s < C; ++s) {
-            const float kms = sKm[s * PK + c], bkp = sB[s] * sKp[s * PK + c], qps = sQp[s * PK + c];
+    // dKp = beta (dA Km - dY S'^T),  dQp += dP Km,  dKm += (beta dA)^T Kp + dP^T Qp
 #pragma unroll
-            for (int i = 0; i < MCK; ++i) {
-                const int r = r0 + RK * i;
-                aKp[i] += sB[r] * sP[r * PC + s] * kms;
-                aQ[i] += sDp[r * PC + s] * kms;
-                aKm[i] += sP[s * PC + r] * bkp + sDp[s * PC + r] * qps;
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int m = 0; m < MC; ++m) aKp[i][m] = -aKp[i][m];
+    for (int s2 = 0; s2 < C; ++s2) {
+        float km[MC], kp[MC], qp[MC];
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+            km[m] = sKm[s2 * PK + cc0 + m];
+            kp[m] = sB[s2] * sKp[s2 * PK + cc0 + m];
+            qp[m] = sQp[s2 * PK + cc0 + m];
+        }
+#pragma unroll
+        for (int i = 0; i < MR; ++i) {
+            const int r = r0 + i;
+            const float a = sA[r * PC + s2], p = sDp[r * PC + s2];
+            const float at = sA[s2 * PC + r], pt = sDp[s2 * PC + r];
+#pragma unroll
+            for (int m = 0; m < MC; ++m) {
+                aKp[i][m] += a * km[m];
+                aQ[i][m] += p * km[m];
+                aKm[i][m] += at * kp[m] + pt * qp[m];
             }
         }
     }
-    // dq, dk, and D = dKp Kp - dKm Km + dQp Qp (+ h on the last row)
-    float D[MCK];
+    float D[MR][MC];
 #pragma unroll
-    for (int i = 0; i < MCK; ++i) {
-        const int e = t + GNT * i, r = e / K, c = e % K;
-        D[i] = aKp[i] * sKp[r * PK + c] - aKm[i] * sKm[r * PK + c] + aQ[i] * sQp[r * PK + c] +
-               (r == L - 1 ? sH[c] : 0.f);
-        if (r < L) {
-            const float ep = rec[Rc::EE + e];
-            const size_t off = ((size_t)(c0 + r) * H + h) * K + c;
-            dq[off] = aQ[i] * ep;
-            dk[off] = aKp[i] * ep + aKm[i] / ep;
+    for (int i = 0; i < MR; ++i) {
+        const int r = r0 + i;
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+            const int c = cc0 + m;
+            const float dKp = sB[r] * aKp[i][m];
+            D[i][m] = dKp * sKp[r * PK + c] - aKm[i][m] * sKm[r * PK + c] +
+                      aQ[i][m] * sQp[r * PK + c] + (r == L - 1 ? sH[c] : 0.f);
+            if (r < L) {
+                const float ep = rec[Rc::EE + (size_t)r * K + c];
+                const size_t off = ((size_t)(c0 + r) * H + h) * K + c;
+                dq[off] = aQ[i][m] * ep;
+                dk[off] = dKp * ep + aKm[i][m] / ep;
+            }
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < MCK; ++i) {
-        const int e = t + GNT * i;
-        sKp[(e / K) * PK + e % K] = D[i];
-    }
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int m = 0; m < MC; ++m) sKp[(r0 + i) * PK + cc0 + m] = D[i][m];
     __syncthreads();
-    for (int c = t; c < K; c += GNT) {  // dg = reverse running sum of D down each channel
+    for (int c = t; c < K; c += NT) {  // dg = reverse running sum of D down each channel
         float acc = 0.f;
         for (int r = L - 1; r >= 0; --r) {
             acc += sKp[r * PK + c];
@@ -746,12 +898,20 @@ size_t chunk_cap(int N, int totalT, int fixedT, bool packed, int C) {
     return ((size_t)totalT + (size_t)(C - 1) * N) / C;
 }
 
+constexpr int VT3 = 16;  // value columns per workgroup of pass 3
+
+// Per (chunk, head): the record, the start state and end-state gradient, U and
+// dY transposed, and pass 3's per-tile partial sums of dbeta and h.
 template <int K, int V, int C>
 size_t bwd_ws_bytes(size_t cap, int H) {
-    return cap * H * (rec_bytes<K, V, C>() + 2 * sizeof(float) * K * V);
+    return cap * H * (rec_bytes<K, V, C>() +
+                      sizeof(float) * (2 * K * V + 2 * C * V + (V / VT3) * (C + K)));
 }
 
-template <int K, int V, int C, int VT, int VS, int GNT, typename TIn>
+// VT: value columns per chain workgroup; VB, NT4, MR, MC, AR, AC: pass 4's
+// value slice, threads and per-thread tiles.
+template <int K, int V, int C, int VT, int VB, int NT4, int MR, int MC, int AR, int AC,
+          typename TIn>
 hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void *g,
                         const void *beta, const float *s0, const float *dout, const float *dsT,
                         float *dq, float *dk, float *dv, float *dg, float *dbeta, float *ds0,
@@ -761,25 +921,32 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
     float *recs = static_cast<float *>(workspace);
     float *Sst = recs + cap * H * BwdRec<K, V, C>::floats;
     float *dSe = Sst + cap * H * (size_t)K * V;
-    const size_t red = sizeof(int) * BNT, redP = sizeof(int) * PNT, red3 = sizeof(int) * GNT;
+    float *UTb = dSe + cap * H * (size_t)K * V;
+    float *dYTb = UTb + cap * H * (size_t)C * V;
+    float *dbp = dYTb + cap * H * (size_t)C * V;
+    float *hpb = dbp + cap * H * (size_t)(V / VT3) * C;
+    const size_t red = sizeof(int) * BNT, redP = sizeof(int) * PNT, red4 = sizeof(int) * NT4;
     const size_t lds0 = sizeof(float) * (3 * C * (K + 1) + C * K + C + K) + redP;
     const size_t ldsT = sizeof(float) * (3 * C * (K + 1) + 2 * C * (C + 1) + C + 2 * K) + redP;
     const size_t lds1 = sizeof(float) * (K * (K + 1) + K * VT) + red;
     const size_t lds2 = lds1;
-    const size_t lds3 = sizeof(float) * (3 * C * (K + 1) + 2 * C * (C + 1) + 2 * K * (VS + 1) +
-                                         5 * C * VS + 2 * C + 3 * K) + red3;
-    static std::atomic<uint64_t> set0{0}, setT{0}, set1{0}, set2{0}, set3{0};
+    const size_t lds3 = sizeof(float) * (2 * C * (K + 1) + 2 * C * (C + 1) + 2 * K * (VT3 + 1) +
+                                         5 * C * (VT3 + 1) + C + 2 * K) + redP;
+    const size_t lds4 = sizeof(float) * (3 * C * (K + 1) + 3 * C * (C + 1) + C + 3 * K) + red4;
+    static std::atomic<uint64_t> set0{0}, setT{0}, set1{0}, set2{0}, set3{0}, set4{0};
     auto k0 = bwd_prep_kernel<K, V, C, TIn>;
     auto kT = bwd_trans_kernel<K, V, C, TIn>;
     auto k1 = bwd_states_kernel<K, V, C, VT>;
     auto k2 = bwd_dstate_kernel<K, V, C, VT>;
-    auto k3 = bwd_grads_kernel<K, V, C, VS, GNT, TIn>;
+    auto k3 = bwd_udy_kernel<K, V, C, VT3, TIn>;
+    auto k4 = bwd_kgrad_kernel<K, V, C, VT3, VB, NT4, MR, MC, AR, AC, TIn>;
     hipError_t e;
     if ((e = ensure_dynamic_lds(reinterpret_cast<const void *>(k0), (int)lds0, set0)) != hipSuccess) return e;
     if ((e = ensure_dynamic_lds(reinterpret_cast<const void *>(kT), (int)ldsT, setT)) != hipSuccess) return e;
     if ((e = ensure_dynamic_lds(reinterpret_cast<const void *>(k1), (int)lds1, set1)) != hipSuccess) return e;
     if ((e = ensure_dynamic_lds(reinterpret_cast<const void *>(k2), (int)lds2, set2)) != hipSuccess) return e;
     if ((e = ensure_dynamic_lds(reinterpret_cast<const void *>(k3), (int)lds3, set3)) != hipSuccess) return e;
+    if ((e = ensure_dynamic_lds(reinterpret_cast<const void *>(k4), (int)lds4, set4)) != hipSuccess) return e;
     const TIn *tq = static_cast<const TIn *>(q), *tk = static_cast<const TIn *>(k);
     const TIn *tv = static_cast<const TIn *>(v), *tg = static_cast<const TIn *>(g);
     const TIn *tb = static_cast<const TIn *>(beta);
@@ -798,8 +965,11 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
                        totalT, H, recs, dSe);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (cap > 0) {
-        hipLaunchKernelGGL(k3, dim3((unsigned)cap, H), dim3(GNT), lds3, stream, tv, dout, cu, N,
-                           fixedT, totalT, H, recs, Sst, dSe, dq, dk, dv, dg, dbeta);
+        hipLaunchKernelGGL(k3, dim3((unsigned)cap, H), dim3(PNT), lds3, stream, tv, dout,
+                           cu, N, fixedT, totalT, H, recs, Sst, dSe, UTb, dYTb, dbp, hpb, dv);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(k4, dim3((unsigned)cap, H), dim3(NT4), lds4, stream, dout, cu, N, fixedT,
+                           totalT, H, recs, Sst, dSe, UTb, dYTb, dbp, hpb, dq, dk, dg, dbeta);
         e = hipGetLastError();
     }
     return e;
@@ -827,11 +997,11 @@ hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const v
                             void *workspace, hipStream_t stream) {
     if (N == 0 || H == 0) return hipSuccess;
     if (K == 128 && V == 128 && C == 64)
-        return in_bf16 ? launch_bwd_t<128, 128, 64, 4, 8, 512, bf16_t>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream)
-                       : launch_bwd_t<128, 128, 64, 4, 8, 512, float>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream);
+        return in_bf16 ? launch_bwd_t<128, 128, 64, 4, 32, 512, 4, 4, 2, 4, bf16_t>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream)
+                       : launch_bwd_t<128, 128, 64, 4, 32, 512, 4, 4, 2, 4, float>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream);
     if (K == 32 && V == 32 && C == 16)
-        return in_bf16 ? launch_bwd_t<32, 32, 16, 16, 8, 256, bf16_t>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream)
-                       : launch_bwd_t<32, 32, 16, 16, 8, 256, float>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream);
+        return in_bf16 ? launch_bwd_t<32, 32, 16, 16, 16, 256, 1, 2, 1, 1, bf16_t>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream)
+                       : launch_bwd_t<32, 32, 16, 16, 16, 256, 1, 2, 1, 1, float>(q, k, v, g, beta, s0, dout, dsT, dq, dk, dv, dg, dbeta, ds0, cu, N, fixedT, totalT, H, workspace, stream);
     return hipErrorInvalidValue;
 }
 

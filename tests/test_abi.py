@@ -244,11 +244,14 @@ def test_binding_prologue_flags():
 
 def test_backward_argument_errors(lib):
     need = lib.kda_bwd_workspace_bytes(1, 64, 1, 128, 128, 64)
-    rec = lambda C, K: 4 * (4 * C * K + 3 * C * C + C + 2 * K + 3 * K * K)   # bytes per (chunk, head)
-    assert need == 1 * 1 * (rec(64, 128) + 2 * 4 * 128 * 128)
+    # bytes per (chunk, head): the record (Kp, Km, Qp, E, Gk, P, T, beta, F, exp(G_m), MM, NN,
+    # NB), start state and end-state gradient, U and dY, per-16-column partial sums
+    rec = lambda C, K: 4 * (4 * C * K + 3 * C * C + C + 2 * K + 3 * K * K)
+    extra = lambda C, K: 4 * (2 * K * K + 2 * C * K + (K // 16) * (C + K))
+    assert need == 1 * 1 * (rec(64, 128) + extra(64, 128))
     assert lib.kda_bwd_workspace_bytes(1, 64, 1, 64, 64, 64) == 0        # unsupported
     assert lib.kda_bwd_workspace_bytes(3, 100, 2, 32, 32, 16) == \
-        ((100 + 15 * 3) // 16) * 2 * (rec(16, 32) + 2 * 4 * 32 * 32)
+        ((100 + 15 * 3) // 16) * 2 * (rec(16, 32) + extra(16, 32))
     f = lib.kda_chunk_bwd
 
     def call(B=1, T=64, H=1, K=128, C=64, ind=1, null=None, ws=FAKE, nws=None):
