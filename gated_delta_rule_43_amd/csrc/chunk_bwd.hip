@@ -193,6 +193,50 @@ __device__ __forceinline__ void rows_to_lds(float *dst, const float *src) {
     }
 }
 
+// 16-byte piece of a row of TIn values, widened to fp32 (8 values for bf16, 4 for fp32).
+__device__ __forceinline__ void widen(const uint4 &x, const bf16_t *, float *o) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(w[i] << 16);
+        o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void widen(const uint4 &x, const float *, float *o) {
+    o[0] = __uint_as_float(x.x);
+    o[1] = __uint_as_float(x.y);
+    o[2] = __uint_as_float(x.z);
+    o[3] = __uint_as_float(x.w);
+}
+
+// A chunk's [C][D] tile of a token-major [tokens, H, D] tensor (rows c0 ..,
+// head h; rows at or past L read as 0) to LDS as fp32 with row pitch P.
+// 16-byte loads, every one issued before the first store.
+template <int C, int D, int P, int NT, typename TIn>
+__device__ __forceinline__ void token_tile_to_lds(float *dst, const TIn *src, int c0, int L, int H,
+                                                  int h) {
+    constexpr int EP = 16 / sizeof(TIn), Q = C * D / EP, PER = (Q + NT - 1) / NT;
+    static_assert(D % EP == 0, "rows must split into 16-byte pieces");
+    uint4 x[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int qi = threadIdx.x + NT * i, r = qi * EP / D, c = qi * EP % D;
+        x[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (qi < Q && r < L)
+            x[i] = *reinterpret_cast<const uint4 *>(src + ((size_t)(c0 + r) * H + h) * D + c);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int qi = threadIdx.x + NT * i, r = qi * EP / D, c = qi * EP % D;
+        if (qi < Q) {
+            float f[EP];
+            widen(x[i], src, f);
+#pragma unroll
+            for (int u = 0; u < EP; ++u) dst[r * P + c + u] = f[u];
+        }
+    }
+}
+
 // ------------------------------------------------------------------ pass 0
 template <int K, int V, int C, typename TIn>
 __global__ __launch_bounds__(PNT) void bwd_prep_kernel(
@@ -221,10 +265,9 @@ __global__ __launch_bounds__(PNT) void bwd_prep_kernel(
     const int m = min(C / 2 - 1, L - 1);  // reference row
     float *rec = ws + ((size_t)gc * H + h) * Rc::floats;
 
-    for (int e = t; e < C * K; e += PNT) {
-        const int r = e / K, c = e % K;
-        sX[e] = r < L ? to_f32(g[((size_t)(c0 + r) * H + h) * K + c]) : 0.f;
-    }
+    token_tile_to_lds<C, K, K, PNT>(sX, g, c0, L, H, h);
+    token_tile_to_lds<C, K, PK, PNT>(sKp, k, c0, L, H, h);  // raw k and q until scaled below
+    token_tile_to_lds<C, K, PK, PNT>(sQp, q, c0, L, H, h);
     for (int r = t; r < C; r += PNT) sB[r] = r < L ? to_f32(beta[(size_t)(c0 + r) * H + h]) : 0.f;
     __syncthreads();
     for (int c = t; c < K; c += PNT) {  // running sum down each channel
@@ -247,8 +290,7 @@ __global__ __launch_bounds__(PNT) void bwd_prep_kernel(
         const int r = e / K, c = e % K;
         const float d = sX[e] - sGm[c];
         const float ep = fast_exp(d), em = fast_exp(-d);
-        const size_t off = ((size_t)(c0 + r) * H + h) * K + c;
-        const float kv = r < L ? to_f32(k[off]) : 0.f, qv = r < L ? to_f32(q[off]) : 0.f;
+        const float kv = sKp[r * PK + c], qv = sQp[r * PK + c];
         sKp[r * PK + c] = kv * ep;
         sKm[r * PK + c] = kv * em;
         sQp[r * PK + c] = qv * ep;
@@ -384,10 +426,7 @@ __global__ __launch_bounds__(PNT) void bwd_trans_kernel(
         b2[r * PD + j] = b0[r * PD + j] - (a0 + a1);
     }
     __syncthreads();
-    for (int e = t; e < C * V; e += PNT) {
-        const int r = e / V, j = e % V;
-        b0[r * PD + j] = r < L ? dout[((size_t)(c0 + r) * H + h) * V + j] : 0.f;
-    }
+    token_tile_to_lds<C, V, PD, PNT>(b0, dout, c0, L, H, h);
     __syncthreads();
     at_b(b2, b0, [&](int c, int j, float x) { rec[Rc::NB + (size_t)c * V + j] = sE[c] * x; });
     __syncthreads();
@@ -397,10 +436,7 @@ __global__ __launch_bounds__(PNT) void bwd_trans_kernel(
         rec[Rc::MM + (size_t)c * K + j] = sF[c] * ((c == j ? 1.f : 0.f) - x) * sE[j];
     });
     __syncthreads();
-    for (int e = t; e < C * V; e += PNT) {
-        const int r = e / V, j = e % V;
-        b1[r * PD + j] = r < L ? to_f32(v[((size_t)(c0 + r) * H + h) * V + j]) : 0.f;
-    }
+    token_tile_to_lds<C, V, PD, PNT>(b1, v, c0, L, H, h);
     __syncthreads();
     tri_apply(b2, b1);  // U~
     __syncthreads();
@@ -748,21 +784,53 @@ __global__ __launch_bounds__(NT) void bwd_kgrad_kernel(
     const int r0 = (t / CG) * MR, cc0 = (t % CG) * MC;    // [C][K] tile
     const int ar0 = (t / ACG) * AR, as0 = (t % ACG) * AC; // [C][C] tile
     float aQ[MR][MC] = {}, aKp[MR][MC] = {}, aKm[MR][MC] = {}, aA[AR][AC] = {}, aP[AR][AC] = {};
+    // transposed staging of a VB-column slice: 16-byte loads along the value
+    // columns, all issued before the stores
+    constexpr int QO = (C * VB / 4 + NT - 1) / NT, QS = (K * VB / 4 + NT - 1) / NT;
     for (int jb = 0; jb < V; jb += VB) {
         __syncthreads();
-        for (int e = t; e < VB * C; e += NT) {
-            const int j = e / C, r = e % C;
-            sYT[j * PTC + r] = dYc[(size_t)(jb + j) * C + r];
-            sUT[j * PTC + r] = Uc[(size_t)(jb + j) * C + r];
+        float4 xo[QO], xs[QS], xx[QS];
+#pragma unroll
+        for (int i = 0; i < QO; ++i) {
+            const int qi = t + NT * i, r = qi * 4 / VB, j = qi * 4 % VB;
+            xo[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (qi < C * VB / 4 && r < L)
+                xo[i] = *reinterpret_cast<const float4 *>(dout + ((size_t)(c0 + r) * H + h) * V + jb + j);
         }
-        for (int e = t; e < C * VB; e += NT) {
-            const int r = e / VB, j = e % VB;
-            sOT[j * PTC + r] = r < L ? dout[((size_t)(c0 + r) * H + h) * V + jb + j] : 0.f;
+#pragma unroll
+        for (int i = 0; i < QS; ++i) {
+            const int qi = t + NT * i, c = qi * 4 / VB, j = qi * 4 % VB;
+            if (qi < K * VB / 4) {
+                xs[i] = *reinterpret_cast<const float4 *>(S0c + (size_t)c * V + jb + j);
+                xx[i] = *reinterpret_cast<const float4 *>(dSc + (size_t)c * V + jb + j);
+            }
         }
-        for (int e = t; e < K * VB; e += NT) {
-            const int c = e / VB, j = e % VB;
-            sST[j * PTK + c] = sE[c] * S0c[(size_t)c * V + jb + j];
-            sXT[j * PTK + c] = sF[c] * dSc[(size_t)c * V + jb + j];
+        rows_to_lds<VB, C, PTC, NT>(sYT, dYc + (size_t)jb * C);
+        rows_to_lds<VB, C, PTC, NT>(sUT, Uc + (size_t)jb * C);
+#pragma unroll
+        for (int i = 0; i < QO; ++i) {
+            const int qi = t + NT * i, r = qi * 4 / VB, j = qi * 4 % VB;
+            if (qi < C * VB / 4) {
+                sOT[j * PTC + r] = xo[i].x;
+                sOT[(j + 1) * PTC + r] = xo[i].y;
+                sOT[(j + 2) * PTC + r] = xo[i].z;
+                sOT[(j + 3) * PTC + r] = xo[i].w;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < QS; ++i) {
+            const int qi = t + NT * i, c = qi * 4 / VB, j = qi * 4 % VB;
+            if (qi < K * VB / 4) {
+                const float e = sE[c], f = sF[c];
+                sST[j * PTK + c] = e * xs[i].x;
+                sST[(j + 1) * PTK + c] = e * xs[i].y;
+                sST[(j + 2) * PTK + c] = e * xs[i].z;
+                sST[(j + 3) * PTK + c] = e * xs[i].w;
+                sXT[j * PTK + c] = f * xx[i].x;
+                sXT[(j + 1) * PTK + c] = f * xx[i].y;
+                sXT[(j + 2) * PTK + c] = f * xx[i].z;
+                sXT[(j + 3) * PTK + c] = f * xx[i].w;
+            }
         }
         __syncthreads();
 #pragma unroll 2
