@@ -668,20 +668,40 @@ __global__ __launch_bounds__(PNT) void bwd_udy_kernel(
         }
         __syncthreads();
         if (vt + 1 < NVT) fetch(j0 + VT);
-        for (int e = t; e < C * VT; e += PNT) {  // R = V - Kp S';  dU = P^T dO + Km X
-            const int r = e / VT, j = e % VT;
-            float a[4] = {}, d[4] = {};  // four partial sums: shorter dependency chains
+        {  // R = V - Kp S';  dU = P^T dO + Km X.  Column jj, rows rr + RS m per thread
+           // (one read of S' and X serves every row), four partial sums per dot
+            constexpr int RS = PNT / VT, MR3 = (C + RS - 1) / RS;
+            const int jj = t % VT, rr = t / VT;
+            float a[MR3][4] = {}, d[MR3][4] = {};
             for (int c = 0; c < K; c += 4) {
+                float sv[4], xv[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    a[u] += sKp[r * PK + c + u] * sS[(c + u) * PV + j];
-                    d[u] += sKm[r * PK + c + u] * sX[(c + u) * PV + j];
+                    sv[u] = sS[(c + u) * PV + jj];
+                    xv[u] = sX[(c + u) * PV + jj];
+                }
+#pragma unroll
+                for (int m = 0; m < MR3; ++m) {
+                    const int r = rr + RS * m;
+                    if (r < C) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            a[m][u] += sKp[r * PK + c + u] * sv[u];
+                            d[m][u] += sKm[r * PK + c + u] * xv[u];
+                        }
+                    }
                 }
             }
-            float du = (d[0] + d[1]) + (d[2] + d[3]);
-            for (int s2 = r; s2 < C; ++s2) du += sP[s2 * PC + r] * sO[s2 * PV + j];
-            sR[r * PV + j] = sR[r * PV + j] - ((a[0] + a[1]) + (a[2] + a[3]));
-            sDU[r * PV + j] = du;
+#pragma unroll
+            for (int m = 0; m < MR3; ++m) {
+                const int r = rr + RS * m;
+                if (r < C) {
+                    float du = (d[m][0] + d[m][1]) + (d[m][2] + d[m][3]);
+                    for (int s2 = r; s2 < C; ++s2) du += sP[s2 * PC + r] * sO[s2 * PV + jj];
+                    sR[r * PV + jj] = sR[r * PV + jj] - ((a[m][0] + a[m][1]) + (a[m][2] + a[m][3]));
+                    sDU[r * PV + jj] = du;
+                }
+            }
         }
         __syncthreads();
         for (int e = t; e < C * VT; e += PNT) {  // U = T Diag(beta) R;  dY = T^T dU
