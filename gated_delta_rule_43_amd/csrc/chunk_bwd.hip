@@ -33,7 +33,8 @@
 //                      start state in the workspace;
 //   bwd_dstate_kernel  (sequence, head, value tile): the reverse chain
 //                      dS_start = MM^T dS_end + NB, chunk after chunk from
-//                      the last, and ds0;
+//                      the last, and ds0 (at d = 128 both chains run as
+//                      bwd_chain_mfma_kernel, on the matrix cores);
 //   bwd_udy_kernel     (chunk, head), value tile after value tile: R, U,
 //                      dU, dY and dv, and each tile's shares of dbeta and
 //                      rowsum(S_end * dS_end);
@@ -41,7 +42,7 @@
 //                      columns (of q, k, g and beta), as register-tiled
 //                      products over value slices.
 // The state chains are column-separable (value tiles need no communication).
-#include "kda_common.hpp"
+#include "kda_mfma.hpp"
 
 namespace kda {
 namespace {
@@ -58,7 +59,14 @@ struct BwdRec {
     static constexpr size_t GK = EE + C * K, PP = GK + C * C, TT = PP + C * C;
     static constexpr size_t BETA = TT + C * C, FF = BETA + C, EGM = FF + K;
     static constexpr size_t MM = EGM + K, NN = MM + K * K, NB = NN + K * V;
-    static constexpr size_t floats = NB + K * V;
+    // MM and MM^T as fp32 MFMA A fragments (16x16x4): [K/16 row blocks][K/4
+    // k-steps][64 lanes], lane l holding row 16 rb + (l % 16), column
+    // 4 ks + l / 16, so that a wave reads a fragment as one contiguous 256 B
+    static constexpr size_t MMA = NB + K * V, MMTA = MMA + K * K;
+    static constexpr size_t floats = MMTA + K * K;
+    __host__ __device__ static constexpr size_t frag(int row, int col) {
+        return ((size_t)(row / 16) * (K / 4) + col / 4) * 64 + (row % 16) + 16 * (col % 4);
+    }
 };
 
 __device__ __forceinline__ int chunks_of(const int32_t *cu, int n, int fixedT, int totalT, int C) {
@@ -433,7 +441,10 @@ __global__ __launch_bounds__(PNT) void bwd_trans_kernel(
     load_rows(b0, Rc::KM);
     __syncthreads();
     at_b(b0, b1, [&](int c, int j, float x) {
-        rec[Rc::MM + (size_t)c * K + j] = sF[c] * ((c == j ? 1.f : 0.f) - x) * sE[j];
+        const float m = sF[c] * ((c == j ? 1.f : 0.f) - x) * sE[j];
+        rec[Rc::MM + (size_t)c * K + j] = m;
+        rec[Rc::MMA + Rc::frag(c, j)] = m;
+        rec[Rc::MMTA + Rc::frag(j, c)] = m;
     });
     __syncthreads();
     token_tile_to_lds<C, V, PD, PNT>(b1, v, c0, L, H, h);
@@ -570,6 +581,102 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(
     if (ds0)
 #pragma unroll
         for (int i = 0; i < RB; ++i) ds0[sbase + (size_t)(cb + i) * V] = D[i];
+}
+
+// ------------------------------------------------- passes 1 and 2, d = 128
+// Both state chains on the matrix cores (v_mfma_f32_16x16x4_f32: exact fp32
+// products, fp32 accumulation), one workgroup of four waves per (sequence,
+// head, 16-column value tile).  Wave w owns row blocks 2w and 2w + 1 of the
+// tile as two accumulators; the tile goes through LDS each chunk to serve as
+// the B operand of every wave, and the chunk's A fragments (MM, or MM^T for
+// the adjoint, stored fragment-ordered in the record) stream from memory into
+// registers one chunk ahead.
+//   ADJ = false: S <- MM S + NN from s0, writing each chunk's start state;
+//   ADJ = true:  dS <- MM^T dS + NB from dsT, chunk after chunk from the last,
+//                writing each chunk's end-state gradient and finally ds0.
+template <int K, int V, int C, bool ADJ>
+__global__ __launch_bounds__(256) void bwd_chain_mfma_kernel(
+    const float *__restrict__ init, float *__restrict__ fin, const int32_t *__restrict__ cu,
+    int fixedT, int totalT, int H, const float *__restrict__ recs, float *__restrict__ out) {
+    using Rc = BwdRec<K, V, C>;
+    constexpr int KS = K / 4, RBW = K / 64;  // k-steps; row blocks per wave
+    static_assert(K == 128 && V % 16 == 0, "four waves of two 16-row blocks");
+    __shared__ float sS[K * 16];
+    __shared__ int red[256];
+    const int vt = blockIdx.x, h = blockIdx.y, n = blockIdx.z, t = threadIdx.x;
+    const int lane = t & 63, w = t >> 6;
+    int bos, eos;
+    seq_bounds(cu, n, fixedT, totalT, bos, eos);
+    const int nch = (eos - bos + C - 1) / C;
+    const int first = first_chunk<256>(cu, n, fixedT, totalT, C, red);
+    const int col = vt * 16 + (lane & 15);
+    const size_t sbase = ((size_t)n * H + h) * K * V + col;
+    const size_t fofs = ADJ ? Rc::MMTA : Rc::MMA, aofs = ADJ ? Rc::NB : Rc::NN;
+
+    floatx4 acc[RBW];
+#pragma unroll
+    for (int b = 0; b < RBW; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * (RBW * w + b) + 4 * (lane >> 4) + i;
+            acc[b][i] = init ? init[sbase + (size_t)row * V] : 0.f;
+        }
+    float cur[RBW][KS], nxt[RBW][KS], add[RBW][4];
+    auto fetch = [&](int ci) {  // chunk ci's A fragments and addend, into nxt / add
+        const float *rec = recs + ((size_t)(first + ci) * H + h) * Rc::floats;
+#pragma unroll
+        for (int b = 0; b < RBW; ++b) {
+            const int rb = RBW * w + b;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) nxt[b][ks] = rec[fofs + ((size_t)rb * KS + ks) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                add[b][i] = rec[aofs + (size_t)(16 * rb + 4 * (lane >> 4) + i) * V + col];
+        }
+    };
+    if (nch > 0) fetch(ADJ ? nch - 1 : 0);
+    for (int step = 0; step < nch; ++step) {
+        const int ci = ADJ ? nch - 1 - step : step;
+        float *dst = out + ((size_t)(first + ci) * H + h) * K * V + col;
+#pragma unroll
+        for (int b = 0; b < RBW; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * (RBW * w + b) + 4 * (lane >> 4) + i;
+                dst[(size_t)row * V] = acc[b][i];
+                sS[row * 16 + (lane & 15)] = acc[b][i];
+            }
+        float ad[RBW][4];
+#pragma unroll
+        for (int b = 0; b < RBW; ++b) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) cur[b][ks] = nxt[b][ks];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ad[b][i] = add[b][i];
+        }
+        __syncthreads();
+        if (step + 1 < nch) fetch(ADJ ? ci - 1 : ci + 1);
+#pragma unroll
+        for (int b = 0; b < RBW; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[b][i] = ad[b][i];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const float bv = sS[64 * ks + lane];  // B[k = 4 ks + lane / 16][lane % 16]
+#pragma unroll
+            for (int b = 0; b < RBW; ++b)
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[b][ks], bv, acc[b], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+    if (ADJ && fin)
+#pragma unroll
+        for (int b = 0; b < RBW; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * (RBW * w + b) + 4 * (lane >> 4) + i;
+                fin[sbase + (size_t)row * V] = acc[b][i];
+            }
 }
 
 // ------------------------------------------------------------------ pass 3
@@ -1045,12 +1152,20 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
         hipLaunchKernelGGL(kT, dim3((unsigned)cap, H), dim3(PNT), ldsT, stream, tv, dout, cu, N,
                            fixedT, totalT, H, recs);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(k1, dim3(V / VT, H, N), dim3(BNT), lds1, stream, s0, cu, fixedT,
-                           totalT, H, recs, Sst);
+        if constexpr (K == 128)
+            hipLaunchKernelGGL((bwd_chain_mfma_kernel<K, V, C, false>), dim3(V / 16, H, N), dim3(256),
+                               0, stream, s0, nullptr, cu, fixedT, totalT, H, recs, Sst);
+        else
+            hipLaunchKernelGGL(k1, dim3(V / VT, H, N), dim3(BNT), lds1, stream, s0, cu, fixedT,
+                               totalT, H, recs, Sst);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k2, dim3(V / VT, H, N), dim3(BNT), lds2, stream, dsT, ds0, cu, fixedT,
-                       totalT, H, recs, dSe);
+    if constexpr (K == 128)
+        hipLaunchKernelGGL((bwd_chain_mfma_kernel<K, V, C, true>), dim3(V / 16, H, N), dim3(256), 0,
+                           stream, dsT, ds0, cu, fixedT, totalT, H, recs, dSe);
+    else
+        hipLaunchKernelGGL(k2, dim3(V / VT, H, N), dim3(BNT), lds2, stream, dsT, ds0, cu, fixedT,
+                           totalT, H, recs, dSe);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (cap > 0) {
         hipLaunchKernelGGL(k3, dim3((unsigned)cap, H), dim3(PNT), lds3, stream, tv, dout,

@@ -245,8 +245,9 @@ def test_binding_prologue_flags():
 def test_backward_argument_errors(lib):
     need = lib.kda_bwd_workspace_bytes(1, 64, 1, 128, 128, 64)
     # bytes per (chunk, head): the record (Kp, Km, Qp, E, Gk, P, T, beta, F, exp(G_m), MM, NN,
-    # NB), start state and end-state gradient, U and dY, per-16-column partial sums
-    rec = lambda C, K: 4 * (4 * C * K + 3 * C * C + C + 2 * K + 3 * K * K)
+    # NB, MM and MM^T as MFMA fragments), start state and end-state gradient, U and dY,
+    # per-16-column partial sums
+    rec = lambda C, K: 4 * (4 * C * K + 3 * C * C + C + 2 * K + 5 * K * K)
     extra = lambda C, K: 4 * (2 * K * K + 2 * C * K + (K // 16) * (C + K))
     assert need == 1 * 1 * (rec(64, 128) + extra(64, 128))
     assert lib.kda_bwd_workspace_bytes(1, 64, 1, 64, 64, 64) == 0        # unsupported

@@ -106,3 +106,17 @@ def test_bwd_deterministic_and_fully_written():
     for u, w in zip(a, b):
         assert torch.isfinite(u).all()
         assert torch.equal(u, w)
+
+
+def test_bwd_many_sequences():
+    """300 packed sequences of 0..70 tokens (d = 32, chunk 16): the chunk map of
+    the per-chunk passes scans several sequences per thread."""
+    rng = np.random.default_rng(89)
+    lengths = [int(x) for x in rng.integers(0, 71, size=300)]
+    H, K = 1, 32
+    print(f"[case] bwd many sequences N={len(lengths)} total={sum(lengths)}", flush=True)
+    d = inputs.draw_varlen(90, H=H, K=K, V=K, dtype="f32", lengths=lengths, s0_std=0.1)
+    tot = int(sum(lengths))
+    do = torch.from_numpy(rng.standard_normal((tot, H, K)).astype(np.float32))
+    dsT = torch.from_numpy(rng.standard_normal((len(lengths), H, K, K)).astype(np.float32))
+    _grads_case("bwd_many_sequences", d, d["cu_seqlens"].numpy(), "f32", do, dsT)
