@@ -42,6 +42,8 @@
 //                      columns (of q, k, g and beta), as register-tiled
 //                      products over value slices.
 // The state chains are column-separable (value tiles need no communication).
+#include <type_traits>
+
 #include "kda_mfma.hpp"
 
 namespace kda {
@@ -859,6 +861,153 @@ __global__ __launch_bounds__(PNT) void bwd_udy_kernel(
     }
 }
 
+// ------------------------------------------------- pass 3, d = 128 (matrix cores)
+// The column pass with every product on v_mfma_f32_16x16x4_f32 (exact fp32
+// products).  Eight waves per (chunk, head): waves 0-3 form R = V - Kp S' and
+// then U = (T Diag(beta)) R for row block w; waves 4-7 form dU = Km X + P^T dO
+// and then dY = T^T dU for row block w - 4; then every wave forms one 16-row
+// block of S' + Km^T U (for rowsum(S_end * dS_end)).  The chunk's A fragments
+// (Kp, Km, T Diag(beta), P^T, T^T, Km^T) are loaded into registers once and
+// serve all the value tiles; the tiles' B operands come from LDS.
+template <int K, int V, int C, int VT>
+__global__ __launch_bounds__(512) void bwd_udy_mfma_kernel(
+    const bf16_t *__restrict__ vb, const float *__restrict__ vf, bool in_bf16,
+    const float *__restrict__ dout, const int32_t *__restrict__ cu, int N, int fixedT,
+    int totalT, int H, const float *__restrict__ recs, const float *__restrict__ Sst,
+    const float *__restrict__ dSe, float *__restrict__ UT, float *__restrict__ dYT,
+    float *__restrict__ dbp, float *__restrict__ hp, float *__restrict__ dv) {
+    using Rc = BwdRec<K, V, C>;
+    constexpr int PV = VT + 1, NVT = V / VT, KSK = K / 4, KSC = C / 4;
+    static_assert(K == 128 && C == 64 && VT == 16, "eight waves: four row blocks of C, eight of K");
+    __shared__ float sS[K * PV], sX[K * PV];                  // S', X (F dS_end)
+    __shared__ float sO[C * PV], sR[C * PV], sDU[C * PV];     // dO, R, dU
+    __shared__ float sU[C * PV], sDY[C * PV];                 // U, dY
+    __shared__ float sF[K], sE[K], sB[C];
+    __shared__ int red[512];
+
+    const int gc = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    const int lane = t & 63, w = t >> 6, rb = w & 3, lr = lane & 15, lq = lane >> 4;
+    int n, ci;
+    locate_chunk<512>(cu, N, fixedT, totalT, C, gc, n, ci, red);
+    if (n < 0) return;
+    int bos, eos;
+    seq_bounds(cu, n, fixedT, totalT, bos, eos);
+    const int c0 = bos + ci * C, L = min(C, eos - c0);
+    const size_t unit = (size_t)gc * H + h;
+    const float *rec = recs + unit * Rc::floats;
+    const float *S0c = Sst + unit * K * V, *dSc = dSe + unit * K * V;
+    for (int r = t; r < C; r += 512) sB[r] = rec[Rc::BETA + r];
+    for (int c = t; c < K; c += 512) {
+        sF[c] = rec[Rc::FF + c];
+        sE[c] = rec[Rc::EGM + c];
+    }
+    // A fragments: lane holds row 16 blk + lr, column 4 ks + lq
+    float a1[KSK], a2[KSC], a3[KSC];
+    const int arow = 16 * rb + lr;
+    if (w < 4) {  // Kp (for R), T Diag(beta) (for U)
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks) a1[ks] = rec[Rc::KP + (size_t)arow * K + 4 * ks + lq];
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+            const int s2 = 4 * ks + lq;
+            a2[ks] = rec[Rc::TT + (size_t)arow * C + s2] * rec[Rc::BETA + s2];
+            a3[ks] = 0.f;
+        }
+    } else {      // Km (for dU), P^T (for dU), T^T (for dY)
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks) a1[ks] = rec[Rc::KM + (size_t)arow * K + 4 * ks + lq];
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+            const int s2 = 4 * ks + lq;
+            a2[ks] = rec[Rc::PP + (size_t)s2 * C + arow];
+            a3[ks] = rec[Rc::TT + (size_t)s2 * C + arow];
+        }
+    }
+    float a4[KSC];  // Km^T, rows 16 w .. of K
+#pragma unroll
+    for (int ks = 0; ks < KSC; ++ks) a4[ks] = rec[Rc::KM + (size_t)(4 * ks + lq) * K + 16 * w + lr];
+    __syncthreads();
+
+    for (int vt = 0; vt < NVT; ++vt) {
+        const int j0 = vt * VT;
+        if (vt > 0) __syncthreads();
+        for (int e = t; e < K * VT; e += 512) {
+            const int c = e / VT, j = e % VT;
+            sS[c * PV + j] = sE[c] * S0c[(size_t)c * V + j0 + j];
+            sX[c * PV + j] = sF[c] * dSc[(size_t)c * V + j0 + j];
+        }
+        for (int e = t; e < C * VT; e += 512) {
+            const int r = e / VT, j = e % VT;
+            const size_t off = ((size_t)(c0 + r) * H + h) * V + j0 + j;
+            sR[r * PV + j] = r < L ? (in_bf16 ? to_f32(vb[off]) : vf[off]) : 0.f;
+            sO[r * PV + j] = r < L ? dout[off] : 0.f;
+        }
+        __syncthreads();
+        // phase A: R (waves 0-3) or dU (waves 4-7) for row block rb
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        const float *bk = w < 4 ? sS : sX;
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[ks], bk[(4 * ks + lq) * PV + lr], acc, 0, 0, 0);
+        if (w >= 4) {
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[ks], sO[(4 * ks + lq) * PV + lr], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rb + 4 * lq + i;
+            if (w < 4) sR[r * PV + lr] = sR[r * PV + lr] - acc[i];
+            else sDU[r * PV + lr] = acc[i];
+        }
+        __syncthreads();
+        // phase B: U = (T Diag(beta)) R (waves 0-3), dY = T^T dU (waves 4-7)
+        acc = floatx4{0.f, 0.f, 0.f, 0.f};
+        const float *bb = w < 4 ? sR : sDU;
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(w < 4 ? a2[ks] : a3[ks],
+                                                       bb[(4 * ks + lq) * PV + lr], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rb + 4 * lq + i;
+            if (w < 4) {
+                sU[r * PV + lr] = acc[i];
+            } else {
+                sDY[r * PV + lr] = acc[i];
+                if (r < L) dv[((size_t)(c0 + r) * H + h) * V + j0 + lr] = sB[r] * acc[i];
+            }
+        }
+        __syncthreads();
+        // phase C: S' + Km^T U for rows 16 w .. of K, then this tile's share of
+        // rowsum(S_end * dS_end) (a 16-lane sum per row)
+        acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[ks], sU[(4 * ks + lq) * PV + lr], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 16 * w + 4 * lq + i;
+            float x = (sS[c * PV + lr] + acc[i]) * sX[c * PV + lr];
+            x += __shfl_xor(x, 1);
+            x += __shfl_xor(x, 2);
+            x += __shfl_xor(x, 4);
+            x += __shfl_xor(x, 8);
+            if (lr == 0) hp[(unit * NVT + vt) * K + c] = x;
+        }
+        for (int r = t; r < C; r += 512) {  // this tile's share of dbeta
+            float s = 0.f;
+            for (int j = 0; j < VT; ++j) s += sR[r * PV + j] * sDY[r * PV + j];
+            dbp[(unit * NVT + vt) * C + r] = s;
+        }
+        for (int e = t; e < C * VT; e += 512) {  // U and dY transposed: [V][C]
+            const int j = e / C, r = e % C;
+            UT[unit * V * C + (size_t)(j0 + j) * C + r] = sU[r * PV + j];
+            dYT[unit * V * C + (size_t)(j0 + j) * C + r] = sDY[r * PV + j];
+        }
+    }
+}
+
 // ------------------------------------------------------------------ pass 4
 // Per (chunk, head): the gradients that sum over all value columns,
 //   dQp = dO S'^T + dP Km,  dKp = -Diag(beta) dY S'^T + Diag(beta) dA Km,
@@ -1168,8 +1317,15 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
                            totalT, H, recs, dSe);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (cap > 0) {
-        hipLaunchKernelGGL(k3, dim3((unsigned)cap, H), dim3(PNT), lds3, stream, tv, dout,
-                           cu, N, fixedT, totalT, H, recs, Sst, dSe, UTb, dYTb, dbp, hpb, dv);
+        if constexpr (K == 128)
+            hipLaunchKernelGGL((bwd_udy_mfma_kernel<K, V, C, VT3>), dim3((unsigned)cap, H), dim3(512),
+                               0, stream, reinterpret_cast<const bf16_t *>(v),
+                               reinterpret_cast<const float *>(v), std::is_same<TIn, bf16_t>::value,
+                               dout, cu, N, fixedT, totalT, H, recs, Sst, dSe, UTb, dYTb, dbp, hpb,
+                               dv);
+        else
+            hipLaunchKernelGGL(k3, dim3((unsigned)cap, H), dim3(PNT), lds3, stream, tv, dout,
+                               cu, N, fixedT, totalT, H, recs, Sst, dSe, UTb, dYTb, dbp, hpb, dv);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(k4, dim3((unsigned)cap, H), dim3(NT4), lds4, stream, dout, cu, N, fixedT,
                            totalT, H, recs, Sst, dSe, UTb, dYTb, dbp, hpb, dq, dk, dg, dbeta);
