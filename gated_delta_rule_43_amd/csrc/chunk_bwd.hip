@@ -1233,6 +1233,204 @@ __global__ __launch_bounds__(NT) void bwd_kgrad_kernel(
     }
 }
 
+// ------------------------------------------------- pass 4, d = 128 (matrix cores)
+// The cross-column gradients with every product on v_mfma_f32_16x16x4_f32.
+// Eight waves; wave w owns column block w of the three [C][K] sums (all four
+// row blocks) and two 16 x 16 tiles of each [C][C] sum.  The value-column
+// contractions read their fragments from 32-column slices staged transposed
+// in LDS; the C-contractions of the final phase read them from the staged
+// record tiles.
+template <int K, int V, int C, int VT, int VB>
+__global__ __launch_bounds__(512) void bwd_kgrad_mfma_kernel(
+    const float *__restrict__ dout, const int32_t *__restrict__ cu, int N, int fixedT,
+    int totalT, int H, const float *__restrict__ recs, const float *__restrict__ Sst,
+    const float *__restrict__ dSe, const float *__restrict__ UT, const float *__restrict__ dYT,
+    const float *__restrict__ dbp, const float *__restrict__ hp, float *__restrict__ dq,
+    float *__restrict__ dk, float *__restrict__ dg, float *__restrict__ dbeta) {
+    using Rc = BwdRec<K, V, C>;
+    constexpr int NT = 512, NVT = V / VT, PK = K + 1, PC = C + 1, PTC = C + 4, PTK = K + 4;
+    constexpr int RB = C / 16;  // row blocks
+    static_assert(K == 128 && C == 64 && V % VB == 0 && VB % 4 == 0, "eight waves, one column block each");
+    extern __shared__ float smem[];
+    float *sOT = smem, *sYT = sOT + VB * PTC, *sUT = sYT + VB * PTC;  // [VB][PTC]
+    float *sST = sUT + VB * PTC, *sXT = sST + VB * PTK;               // [VB][PTK]
+    float *sKp = smem, *sKm = sKp + C * PK, *sQp = sKm + C * PK;      // [C][PK]
+    float *sA = sQp + C * PK, *sDp = sA + C * PC, *sG = sDp + C * PC; // [C][PC]
+    float *sB = sG + C * PC, *sH = sB + C, *sF = sH + K, *sE = sF + K;
+    int *red = reinterpret_cast<int *>(sE + K);
+
+    const int gc = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    const int lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
+    int n, ci;
+    locate_chunk<NT>(cu, N, fixedT, totalT, C, gc, n, ci, red);
+    if (n < 0) return;
+    int bos, eos;
+    seq_bounds(cu, n, fixedT, totalT, bos, eos);
+    const int c0 = bos + ci * C, L = min(C, eos - c0);
+    const size_t unit = (size_t)gc * H + h;
+    const float *rec = recs + unit * Rc::floats;
+    const float *S0c = Sst + unit * K * V, *dSc = dSe + unit * K * V;
+    const float *Uc = UT + unit * V * C, *dYc = dYT + unit * V * C;
+    for (int r = t; r < C; r += NT) sB[r] = rec[Rc::BETA + r];
+    for (int c = t; c < K; c += NT) {
+        sF[c] = rec[Rc::FF + c];
+        sE[c] = rec[Rc::EGM + c];
+    }
+    const int cb = w;                       // this wave's column block of the [C][K] sums
+    const int t0 = 2 * w, t1 = 2 * w + 1;   // its two [C][C] tiles (row block t / 4, column block t % 4)
+    floatx4 aQ[RB], aKp[RB], aKm[RB], aA[2], aP[2];
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < RB; ++b) aQ[b] = aKp[b] = aKm[b] = z;
+    aA[0] = aA[1] = aP[0] = aP[1] = z;
+
+    constexpr int QO = (C * VB / 4 + NT - 1) / NT, QS = (K * VB / 4 + NT - 1) / NT;
+    for (int jb = 0; jb < V; jb += VB) {
+        __syncthreads();
+        float4 xo[QO], xs[QS], xx[QS];
+#pragma unroll
+        for (int i = 0; i < QO; ++i) {
+            const int qi = t + NT * i, r = qi * 4 / VB, j = qi * 4 % VB;
+            xo[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (qi < C * VB / 4 && r < L)
+                xo[i] = *reinterpret_cast<const float4 *>(dout + ((size_t)(c0 + r) * H + h) * V + jb + j);
+        }
+#pragma unroll
+        for (int i = 0; i < QS; ++i) {
+            const int qi = t + NT * i, c = qi * 4 / VB, j = qi * 4 % VB;
+            if (qi < K * VB / 4) {
+                xs[i] = *reinterpret_cast<const float4 *>(S0c + (size_t)c * V + jb + j);
+                xx[i] = *reinterpret_cast<const float4 *>(dSc + (size_t)c * V + jb + j);
+            }
+        }
+        rows_to_lds<VB, C, PTC, NT>(sYT, dYc + (size_t)jb * C);
+        rows_to_lds<VB, C, PTC, NT>(sUT, Uc + (size_t)jb * C);
+#pragma unroll
+        for (int i = 0; i < QO; ++i) {
+            const int qi = t + NT * i, r = qi * 4 / VB, j = qi * 4 % VB;
+            if (qi < C * VB / 4) {
+                sOT[j * PTC + r] = xo[i].x;
+                sOT[(j + 1) * PTC + r] = xo[i].y;
+                sOT[(j + 2) * PTC + r] = xo[i].z;
+                sOT[(j + 3) * PTC + r] = xo[i].w;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < QS; ++i) {
+            const int qi = t + NT * i, c = qi * 4 / VB, j = qi * 4 % VB;
+            if (qi < K * VB / 4) {
+                const float e = sE[c], f = sF[c];
+                sST[j * PTK + c] = e * xs[i].x;
+                sST[(j + 1) * PTK + c] = e * xs[i].y;
+                sST[(j + 2) * PTK + c] = e * xs[i].z;
+                sST[(j + 3) * PTK + c] = e * xs[i].w;
+                sXT[j * PTK + c] = f * xx[i].x;
+                sXT[(j + 1) * PTK + c] = f * xx[i].y;
+                sXT[(j + 2) * PTK + c] = f * xx[i].z;
+                sXT[(j + 3) * PTK + c] = f * xx[i].w;
+            }
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int ks = 0; ks < VB / 4; ++ks) {
+            const int jr = 4 * ks + lq;  // the k (value column) this lane supplies
+            const float bS = sST[jr * PTK + 16 * cb + lr], bX = sXT[jr * PTK + 16 * cb + lr];
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                const float o = sOT[jr * PTC + 16 * b + lr], y = sYT[jr * PTC + 16 * b + lr];
+                const float u = sUT[jr * PTC + 16 * b + lr];
+                aQ[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(o, bS, aQ[b], 0, 0, 0);
+                aKp[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(y, bS, aKp[b], 0, 0, 0);
+                aKm[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(u, bX, aKm[b], 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int tt = q ? t1 : t0, ar = tt / 4, as = tt % 4;
+                const float bU = sUT[jr * PTC + 16 * as + lr];
+                aA[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(sYT[jr * PTC + 16 * ar + lr], bU, aA[q], 0, 0, 0);
+                aP[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(sOT[jr * PTC + 16 * ar + lr], bU, aP[q], 0, 0, 0);
+            }
+        }
+    }
+    __syncthreads();
+    // final phase: record tiles, masked dA = -dY U^T and dP = dO U^T, Gk, partial sums
+    rows_to_lds<C, K, PK, NT>(sKp, rec + Rc::KP);
+    rows_to_lds<C, K, PK, NT>(sKm, rec + Rc::KM);
+    rows_to_lds<C, K, PK, NT>(sQp, rec + Rc::QP);
+    rows_to_lds<C, C, PC, NT>(sG, rec + Rc::GK);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int tt = q ? t1 : t0, ar = tt / 4, as = tt % 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * ar + 4 * lq + i, s2 = 16 * as + lr;
+            sA[r * PC + s2] = s2 < r ? -aA[q][i] : 0.f;
+            sDp[r * PC + s2] = s2 <= r ? aP[q][i] : 0.f;
+        }
+    }
+    for (int c = t; c < K; c += NT) {
+        float acc = 0.f;
+        for (int w2 = 0; w2 < NVT; ++w2) acc += hp[(unit * NVT + w2) * K + c];
+        sH[c] = acc;
+    }
+    __syncthreads();
+    for (int r = t; r < C; r += NT) {  // dbeta = tiles' rowsum(R * dY) + rowsum(Gk * dA)
+        float acc = 0.f;
+        for (int w2 = 0; w2 < NVT; ++w2) acc += dbp[(unit * NVT + w2) * C + r];
+        for (int s2 = 0; s2 < r; ++s2) acc += sG[r * PC + s2] * sA[r * PC + s2];
+        if (r < L) dbeta[(size_t)(c0 + r) * H + h] = acc;
+    }
+    // aKp <- dA Km - dY S'^T (times beta per row below); aQ += dP Km;
+    // aKm += (Diag(beta) dA)^T Kp + dP^T Qp; contractions over the C tokens
+#pragma unroll
+    for (int b = 0; b < RB; ++b) aKp[b] = -aKp[b];
+#pragma unroll 2
+    for (int ks = 0; ks < C / 4; ++ks) {
+        const int sr = 4 * ks + lq;  // the token this lane supplies
+        const float bKm = sKm[sr * PK + 16 * cb + lr], bKp = sKp[sr * PK + 16 * cb + lr];
+        const float bQp = sQp[sr * PK + 16 * cb + lr], bs = sB[sr];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const int ar = 16 * b + lr;
+            aKp[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[ar * PC + sr], bKm, aKp[b], 0, 0, 0);
+            aQ[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(sDp[ar * PC + sr], bKm, aQ[b], 0, 0, 0);
+            aKm[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(bs * sA[sr * PC + ar], bKp, aKm[b], 0, 0, 0);
+            aKm[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(sDp[sr * PC + ar], bQp, aKm[b], 0, 0, 0);
+        }
+    }
+    // dq, dk and D = dKp Kp - dKm Km + dQp Qp (+ h on the last row)
+    float D[RB][4];
+    const int c = 16 * cb + lr;
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * b + 4 * lq + i;
+            const float dKp = sB[r] * aKp[b][i];
+            D[b][i] = dKp * sKp[r * PK + c] - aKm[b][i] * sKm[r * PK + c] +
+                      aQ[b][i] * sQp[r * PK + c] + (r == L - 1 ? sH[c] : 0.f);
+            if (r < L) {
+                const float ep = rec[Rc::EE + (size_t)r * K + c];
+                const size_t off = ((size_t)(c0 + r) * H + h) * K + c;
+                dq[off] = aQ[b][i] * ep;
+                dk[off] = dKp * ep + aKm[b][i] / ep;
+            }
+        }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sKp[(16 * b + 4 * lq + i) * PK + c] = D[b][i];
+    __syncthreads();
+    for (int c2 = t; c2 < K; c2 += NT) {  // dg = reverse running sum of D down each channel
+        float acc = 0.f;
+        for (int r = L - 1; r >= 0; --r) {
+            acc += sKp[r * PK + c2];
+            dg[((size_t)(c0 + r) * H + h) * K + c2] = acc;
+        }
+    }
+}
+
 template <int K, int V, int C>
 size_t rec_bytes() { return sizeof(float) * BwdRec<K, V, C>::floats; }
 
@@ -1327,8 +1525,21 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
             hipLaunchKernelGGL(k3, dim3((unsigned)cap, H), dim3(PNT), lds3, stream, tv, dout,
                                cu, N, fixedT, totalT, H, recs, Sst, dSe, UTb, dYTb, dbp, hpb, dv);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(k4, dim3((unsigned)cap, H), dim3(NT4), lds4, stream, dout, cu, N, fixedT,
-                           totalT, H, recs, Sst, dSe, UTb, dYTb, dbp, hpb, dq, dk, dg, dbeta);
+        if constexpr (K == 128) {
+            auto k4m = bwd_kgrad_mfma_kernel<K, V, C, VT3, VB>;
+            static std::atomic<uint64_t> set4m{0};
+            const size_t lds4m = sizeof(float) * (3 * C * (K + 1) + 3 * C * (C + 1) + C + 3 * K) +
+                                 sizeof(int) * 512;
+            if ((e = ensure_dynamic_lds(reinterpret_cast<const void *>(k4m), (int)lds4m, set4m)) != hipSuccess)
+                return e;
+            hipLaunchKernelGGL(k4m, dim3((unsigned)cap, H), dim3(512), lds4m, stream, dout, cu, N,
+                               fixedT, totalT, H, recs, Sst, dSe, UTb, dYTb, dbp, hpb, dq, dk, dg,
+                               dbeta);
+        } else {
+            hipLaunchKernelGGL(k4, dim3((unsigned)cap, H), dim3(NT4), lds4, stream, dout, cu, N,
+                               fixedT, totalT, H, recs, Sst, dSe, UTb, dYTb, dbp, hpb, dq, dk, dg,
+                               dbeta);
+        }
         e = hipGetLastError();
     }
     return e;
