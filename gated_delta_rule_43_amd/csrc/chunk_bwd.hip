@@ -456,6 +456,133 @@ __global__ __launch_bounds__(PNT) void bwd_trans_kernel(
     at_b(b0, b2, [&](int c, int j, float x) { rec[Rc::NN + (size_t)c * V + j] = sF[c] * x; });
 }
 
+// Matrix-core variant of the transition pass at d = 128: the same six
+// products on v_mfma_f32_16x16x4_f32 with eight waves.  In the [C][K]
+// products (W, Q^, U~) wave w owns column block w for the four row blocks and
+// skips the k-steps above the diagonal of the triangular factor; in the
+// [K][K] products (NB, MM, NN) it owns row block w for all eight column
+// blocks, one A fragment serving the eight.  Tiles carry row pitch K + 16 and
+// the [C][C] factors C + 4, so that the lanes of a fragment read fall on
+// distinct banks.
+template <int K, int V, int C, typename TIn>
+__global__ __launch_bounds__(PNT) void bwd_trans_mfma_kernel(
+    const TIn *__restrict__ v, const float *__restrict__ dout, const int32_t *__restrict__ cu,
+    int N, int fixedT, int totalT, int H, float *__restrict__ recs) {
+    using Rc = BwdRec<K, V, C>;
+    static_assert(K == 128 && V == K && C == 64 && PNT == 512, "eight waves over 128 x 128 tiles");
+    constexpr int PD = K + 16, PC = C + 4, RB = C / 16, CB = K / 16, KS = C / 4;
+    extern __shared__ float smem[];
+    float *b0 = smem, *b1 = b0 + C * PD, *b2 = b1 + C * PD;
+    float *sT = b2 + C * PD, *sP = sT + C * PC;
+    float *sB = sP + C * PC, *sF = sB + C, *sE = sF + K;
+    int *red = reinterpret_cast<int *>(sE + K);
+
+    const int gc = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    const int lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
+    int n, ci;
+    locate_chunk<PNT>(cu, N, fixedT, totalT, C, gc, n, ci, red);
+    if (n < 0) return;
+    int bos, eos;
+    seq_bounds(cu, n, fixedT, totalT, bos, eos);
+    const int c0 = bos + ci * C, L = min(C, eos - c0);
+    float *rec = recs + ((size_t)gc * H + h) * Rc::floats;
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+
+    rows_to_lds<C, C, PC, PNT>(sT, rec + Rc::TT);
+    rows_to_lds<C, C, PC, PNT>(sP, rec + Rc::PP);
+    rows_to_lds<C, K, PD, PNT>(b0, rec + Rc::KP);
+    rows_to_lds<C, K, PD, PNT>(b2, rec + Rc::QP);
+    for (int r = t; r < C; r += PNT) sB[r] = rec[Rc::BETA + r];
+    for (int c = t; c < K; c += PNT) {
+        sF[c] = rec[Rc::FF + c];
+        sE[c] = rec[Rc::EGM + c];
+    }
+    __syncthreads();
+    // acc[b] = rows 16 b .. 16 b + 15, columns 16 w .. 16 w + 15 of L in, with
+    // L lower triangular (T Diag(beta), or P): block b needs only s <= 16 b + 15
+    auto tri = [&](const float *lo, bool scale, const float *in, floatx4(&acc)[RB]) {
+#pragma unroll
+        for (int b = 0; b < RB; ++b) acc[b] = z;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int s = 4 * ks + lq;
+            const float bv = in[s * PD + 16 * w + lr], bs = scale ? sB[s] : 1.f;
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+                if (b >= ks / 4)
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(lo[(16 * b + lr) * PC + s] * bs, bv,
+                                                                  acc[b], 0, 0, 0);
+        }
+    };
+    // acc[jb] = rows 16 w .. 16 w + 15, columns 16 jb .. 16 jb + 15 of a^T bm
+    auto at_b = [&](const float *a, const float *bm, floatx4(&acc)[CB]) {
+#pragma unroll
+        for (int jb = 0; jb < CB; ++jb) acc[jb] = z;
+#pragma unroll 4
+        for (int ks = 0; ks < KS; ++ks) {
+            const int s = 4 * ks + lq;
+            const float av = a[s * PD + 16 * w + lr];
+#pragma unroll
+            for (int jb = 0; jb < CB; ++jb)
+                acc[jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bm[s * PD + 16 * jb + lr], acc[jb],
+                                                               0, 0, 0);
+        }
+    };
+    floatx4 acc[RB], accU[RB], accM[CB];
+    tri(sT, true, b0, acc);  // W = T Diag(beta) Kp
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b1[(16 * b + 4 * lq + i) * PD + 16 * w + lr] = acc[b][i];
+    __syncthreads();
+    tri(sP, false, b1, acc);  // Q^ = Qp - P W, in place (each lane owns its elements)
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b2[(16 * b + 4 * lq + i) * PD + 16 * w + lr] -= acc[b][i];
+    __syncthreads();
+    token_tile_to_lds<C, V, PD, PNT>(b0, dout, c0, L, H, h);
+    __syncthreads();
+    at_b(b2, b0, accM);  // NB = Diag(exp(G_m)) Q^T dO
+#pragma unroll
+    for (int jb = 0; jb < CB; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 16 * w + 4 * lq + i, j = 16 * jb + lr;
+            rec[Rc::NB + (size_t)c * V + j] = sE[c] * accM[jb][i];
+        }
+    __syncthreads();
+    rows_to_lds<C, K, PD, PNT>(b0, rec + Rc::KM);
+    token_tile_to_lds<C, V, PD, PNT>(b2, v, c0, L, H, h);
+    __syncthreads();
+    tri(sT, true, b2, accU);  // U~ = T Diag(beta) V
+    at_b(b0, b1, accM);       // MM = F (I - Km^T W) Diag(exp(G_m))
+#pragma unroll
+    for (int jb = 0; jb < CB; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 16 * w + 4 * lq + i, j = 16 * jb + lr;
+            const float m = sF[c] * ((c == j ? 1.f : 0.f) - accM[jb][i]) * sE[j];
+            rec[Rc::MM + (size_t)c * K + j] = m;
+            rec[Rc::MMA + Rc::frag(c, j)] = m;
+            rec[Rc::MMTA + Rc::frag(j, c)] = m;
+        }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b1[(16 * b + 4 * lq + i) * PD + 16 * w + lr] = accU[b][i];
+    __syncthreads();
+    at_b(b0, b1, accM);  // NN = F Km^T U~
+#pragma unroll
+    for (int jb = 0; jb < CB; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 16 * w + 4 * lq + i, j = 16 * jb + lr;
+            rec[Rc::NN + (size_t)c * V + j] = sF[c] * accM[jb][i];
+        }
+}
+
 // ------------------------------------------------------------------ pass 1
 // Forward state chain of one value tile, S <- MM S + NN chunk after chunk:
 // writes the start state of every chunk of the sequence to Sst[chunk][h].
@@ -1496,8 +1623,18 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
         hipLaunchKernelGGL(k0, dim3((unsigned)cap, H), dim3(PNT), lds0, stream, tq, tk, tg, tb, cu, N,
                            fixedT, totalT, H, recs);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(kT, dim3((unsigned)cap, H), dim3(PNT), ldsT, stream, tv, dout, cu, N,
-                           fixedT, totalT, H, recs);
+        if constexpr (K == 128) {
+            auto kTm = bwd_trans_mfma_kernel<K, V, C, TIn>;
+            static std::atomic<uint64_t> setTm{0};
+            const size_t ldsTm = sizeof(float) * (3 * C * (K + 16) + 2 * C * (C + 4) + C + 2 * K) + redP;
+            if ((e = ensure_dynamic_lds(reinterpret_cast<const void *>(kTm), (int)ldsTm, setTm)) != hipSuccess)
+                return e;
+            hipLaunchKernelGGL(kTm, dim3((unsigned)cap, H), dim3(PNT), ldsTm, stream, tv, dout, cu, N,
+                               fixedT, totalT, H, recs);
+        } else {
+            hipLaunchKernelGGL(kT, dim3((unsigned)cap, H), dim3(PNT), ldsT, stream, tv, dout, cu, N,
+                               fixedT, totalT, H, recs);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if constexpr (K == 128)
             hipLaunchKernelGGL((bwd_chain_mfma_kernel<K, V, C, false>), dim3(V / 16, H, N), dim3(256),
