@@ -255,15 +255,15 @@ __global__ __launch_bounds__(PNT) void bwd_prep_kernel(
     int H, float *__restrict__ ws) {
     using Rc = BwdRec<K, V, C>;
     extern __shared__ float smem[];
-    constexpr int PK = K + 1;     // row pitch: a wave reading one column hits distinct banks
+    constexpr int PK = K + 4;     // row pitch: the 16 rows x 4 columns of a fragment read hit distinct banks
     float *sKp = smem;             // [C][PK]
     float *sKm = sKp + C * PK;     // [C][PK]
     float *sQp = sKm + C * PK;     // [C][PK]
-    float *sX = sQp + C * PK;      // [C][K]: G, later Gk [C][C] and T [C][C]
+    float *sX = sQp + C * PK;      // [C][K]: G, later Gk [C][C]
     float *sB = sX + C * K;        // [C]
     float *sGm = sB + C;           // [K]
     int *red = reinterpret_cast<int *>(sGm + K);  // [PNT]
-    static_assert(2 * C * C <= C * K, "Gk and T must fit the G buffer");
+    static_assert(C <= K, "Gk must fit the G buffer");
 
     const int gc = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
     int n, ci;
@@ -311,7 +311,36 @@ __global__ __launch_bounds__(PNT) void bwd_prep_kernel(
     }
     __syncthreads();
     // Gram blocks: Gk strictly lower, P lower with the diagonal
-    float *sGk = sX, *sT = sX + C * C;
+    float *sGk = sX;
+    if constexpr (K == 128 && C == 64 && PNT == 512) {
+        // on the matrix cores: wave w forms tiles 2 w and 2 w + 1 (row block
+        // tile / 4, column block tile % 4) of both blocks; tiles above the
+        // diagonal are zero
+        const int lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
+        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tt = 2 * w + u, ar = tt / 4, as = tt % 4;
+            floatx4 a = z, p = z;
+            if (as <= ar) {
+#pragma unroll 8
+                for (int ks = 0; ks < K / 4; ++ks) {
+                    const int c = 4 * ks + lq;
+                    const float km = sKm[(16 * as + lr) * PK + c];
+                    a = __builtin_amdgcn_mfma_f32_16x16x4f32(sKp[(16 * ar + lr) * PK + c], km, a, 0, 0, 0);
+                    p = __builtin_amdgcn_mfma_f32_16x16x4f32(sQp[(16 * ar + lr) * PK + c], km, p, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * ar + 4 * lq + i, s2 = 16 * as + lr;
+                const float gk = s2 < r ? a[i] : 0.f;
+                sGk[r * C + s2] = gk;
+                rec[Rc::GK + r * C + s2] = gk;
+                rec[Rc::PP + r * C + s2] = s2 <= r ? p[i] : 0.f;
+            }
+        }
+    } else {
     for (int e = t; e < C * C; e += PNT) {
         const int r = e / C, s = e % C;
         float a = 0.f, p = 0.f;
@@ -333,19 +362,32 @@ __global__ __launch_bounds__(PNT) void bwd_prep_kernel(
         rec[Rc::GK + e] = gk;
         rec[Rc::PP + e] = p;
     }
-    __syncthreads();
-    // T = (I + Diag(beta) Gk)^-1, row by row: T_r = e_r - beta_r sum_{s<r} Gk_rs T_s
-    for (int e = t; e < C * C; e += PNT) sT[e] = (e / C == e % C) ? 1.f : 0.f;
-    __syncthreads();
-    for (int r = 1; r < C; ++r) {
-        for (int col = t; col < r; col += PNT) {
-            float acc = 0.f;
-            for (int s = col; s < r; ++s) acc += sGk[r * C + s] * sT[s * C + col];
-            sT[r * C + col] = -sB[r] * acc;
-        }
-        __syncthreads();
     }
-    for (int e = t; e < C * C; e += PNT) rec[Rc::TT + e] = sT[e];
+    __syncthreads();
+    // T = (I + Diag(beta) Gk)^-1 by forward substitution, one column per lane
+    // of wave 0 held in registers: column j solves (I + Diag(beta) Gk) x = e_j,
+    // x_r = [r == j] - beta_r sum_{s<r} Gk_rs x_s.  Entries not yet formed are
+    // 0 and Gk is 0 on and above the diagonal, so each row's sum may run over
+    // whole groups of four.
+    static_assert(C <= 64 && C % 4 == 0, "one column per lane of a wave");
+    if (t < C) {
+        float x[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) x[r] = 0.f;
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int s4 = 0; s4 < (r + 3) / 4; ++s4) {
+                const float4 gv = *reinterpret_cast<const float4 *>(sGk + r * C + 4 * s4);
+                a0 += gv.x * x[4 * s4] + gv.z * x[4 * s4 + 2];
+                a1 += gv.y * x[4 * s4 + 1] + gv.w * x[4 * s4 + 3];
+            }
+            x[r] = (r == t ? 1.f : 0.f) - sB[r] * (a0 + a1);
+        }
+#pragma unroll
+        for (int r = 0; r < C; ++r) rec[Rc::TT + r * C + t] = x[r];
+    }
 }
 
 // -------------------------------------------------------------- pass 0b
@@ -1595,7 +1637,7 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
     float *dbp = dYTb + cap * H * (size_t)C * V;
     float *hpb = dbp + cap * H * (size_t)(V / VT3) * C;
     const size_t red = sizeof(int) * BNT, redP = sizeof(int) * PNT, red4 = sizeof(int) * NT4;
-    const size_t lds0 = sizeof(float) * (3 * C * (K + 1) + C * K + C + K) + redP;
+    const size_t lds0 = sizeof(float) * (3 * C * (K + 4) + C * K + C + K) + redP;
     const size_t ldsT = sizeof(float) * (3 * C * (K + 1) + 2 * C * (C + 1) + C + 2 * K) + redP;
     const size_t lds1 = sizeof(float) * (K * (K + 1) + K * VT) + red;
     const size_t lds2 = lds1;
