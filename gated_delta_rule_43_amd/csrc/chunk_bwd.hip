@@ -756,9 +756,10 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(
 
 // ------------------------------------------------- passes 1 and 2, d = 128
 // Both state chains on the matrix cores (v_mfma_f32_16x16x4_f32: exact fp32
-// products, fp32 accumulation), one workgroup of four waves per (sequence,
-// head, 16-column value tile).  Wave w owns row blocks 2w and 2w + 1 of the
-// tile as two accumulators; the tile goes through LDS each chunk to serve as
+// products, fp32 accumulation), one workgroup of eight waves per (sequence,
+// head, 16-column value tile).  Wave w owns row block w of the tile (two per
+// SIMD, so that one wave's fragment loads overlap the other's matrix
+// instructions); the tile goes through LDS each chunk to serve as
 // the B operand of every wave, and the chunk's A fragments (MM, or MM^T for
 // the adjoint, stored fragment-ordered in the record) stream from memory into
 // registers one chunk ahead.
@@ -766,20 +767,30 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(
 //   ADJ = true:  dS <- MM^T dS + NB from dsT, chunk after chunk from the last,
 //                writing each chunk's end-state gradient and finally ds0.
 template <int K, int V, int C, bool ADJ>
-__global__ __launch_bounds__(256) void bwd_chain_mfma_kernel(
+__global__ __launch_bounds__(512) void bwd_chain_mfma_kernel(
     const float *__restrict__ init, float *__restrict__ fin, const int32_t *__restrict__ cu,
     int fixedT, int totalT, int H, const float *__restrict__ recs, float *__restrict__ out) {
     using Rc = BwdRec<K, V, C>;
-    constexpr int KS = K / 4, RBW = K / 64;  // k-steps; row blocks per wave
-    static_assert(K == 128 && V % 16 == 0, "four waves of two 16-row blocks");
+    constexpr int NW = 8, KS = K / 4, RBW = K / (16 * NW);  // waves; k-steps; row blocks per wave
+    static_assert(K == 128 && V % 16 == 0 && RBW == 1, "eight waves of one 16-row block");
     __shared__ float sS[K * 16];
-    __shared__ int red[256];
-    const int vt = blockIdx.x, h = blockIdx.y, n = blockIdx.z, t = threadIdx.x;
+    __shared__ int red[64 * NW];
+    // Workgroups are dealt to the eight XCDs round-robin in dispatch order;
+    // when there are eight value tiles and the (head, sequence) pairs come in
+    // eights, the tiles of one pair are mapped to one XCD, so that their reads
+    // of the chunk's MM (or MM^T) fragments share that XCD's L2.
+    int vt = blockIdx.x, hn = blockIdx.y + gridDim.y * blockIdx.z;
+    if (gridDim.x == 8 && (gridDim.y * gridDim.z) % 8 == 0) {
+        const int id = blockIdx.x + 8 * hn;  // dispatch order
+        vt = (id / 8) % 8;
+        hn = id % 8 + 8 * (id / 64);
+    }
+    const int h = hn % gridDim.y, n = hn / gridDim.y, t = threadIdx.x;
     const int lane = t & 63, w = t >> 6;
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
     const int nch = (eos - bos + C - 1) / C;
-    const int first = first_chunk<256>(cu, n, fixedT, totalT, C, red);
+    const int first = first_chunk<64 * NW>(cu, n, fixedT, totalT, C, red);
     const int col = vt * 16 + (lane & 15);
     const size_t sbase = ((size_t)n * H + h) * K * V + col;
     const size_t fofs = ADJ ? Rc::MMTA : Rc::MMA, aofs = ADJ ? Rc::NB : Rc::NN;
@@ -827,17 +838,27 @@ __global__ __launch_bounds__(256) void bwd_chain_mfma_kernel(
         }
         __syncthreads();
         if (step + 1 < nch) fetch(ADJ ? ci - 1 : ci + 1);
+        // even and odd k-steps in two accumulators: two dependency chains
+        floatx4 acc2[RBW];
 #pragma unroll
         for (int b = 0; b < RBW; ++b)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[b][i] = ad[b][i];
+            for (int i = 0; i < 4; ++i) {
+                acc[b][i] = ad[b][i];
+                acc2[b][i] = 0.f;
+            }
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ks += 2) {
             const float bv = sS[64 * ks + lane];  // B[k = 4 ks + lane / 16][lane % 16]
+            const float bw = sS[64 * (ks + 1) + lane];
 #pragma unroll
-            for (int b = 0; b < RBW; ++b)
+            for (int b = 0; b < RBW; ++b) {
                 acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[b][ks], bv, acc[b], 0, 0, 0);
+                acc2[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[b][ks + 1], bw, acc2[b], 0, 0, 0);
+            }
         }
+#pragma unroll
+        for (int b = 0; b < RBW; ++b) acc[b] += acc2[b];
         __syncthreads();
     }
     if (ADJ && fin)
@@ -1679,7 +1700,7 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if constexpr (K == 128)
-            hipLaunchKernelGGL((bwd_chain_mfma_kernel<K, V, C, false>), dim3(V / 16, H, N), dim3(256),
+            hipLaunchKernelGGL((bwd_chain_mfma_kernel<K, V, C, false>), dim3(V / 16, H, N), dim3(512),
                                0, stream, s0, nullptr, cu, fixedT, totalT, H, recs, Sst);
         else
             hipLaunchKernelGGL(k1, dim3(V / VT, H, N), dim3(BNT), lds1, stream, s0, cu, fixedT,
@@ -1687,7 +1708,7 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if constexpr (K == 128)
-        hipLaunchKernelGGL((bwd_chain_mfma_kernel<K, V, C, true>), dim3(V / 16, H, N), dim3(256), 0,
+        hipLaunchKernelGGL((bwd_chain_mfma_kernel<K, V, C, true>), dim3(V / 16, H, N), dim3(512), 0,
                            stream, dsT, ds0, cu, fixedT, totalT, H, recs, dSe);
     else
         hipLaunchKernelGGL(k2, dim3(V / VT, H, N), dim3(BNT), lds2, stream, dsT, ds0, cu, fixedT,
