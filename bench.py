@@ -415,7 +415,7 @@ def main():
         "prefix_cache": {"ms_per_step_with_snapshots": ms_snap, "snap_tokens": snap,
                          "page_tokens": page, "snapshots_per_call": w.B * w.H * (w.T // snap)},
         "backward": {"ms_per_step": ms_bwd, "tokens_per_s": tokens / (ms_bwd * 1e-3),
-                     "kernels": "bwd_prep_kernel + bwd_trans_mfma_kernel + 2 x bwd_chain_mfma_kernel + "
+                     "kernels": "bwd_prep_kernel + bwd_trans_mfma_kernel + bwd_chain_mfma_kernel (both chains) + "
                                 "bwd_udy_mfma_kernel + bwd_kgrad_mfma_kernel (fp32, MFMA at d = 128)",
                      "alg_bytes_per_call": bwd_b,
                      "achieved_GBps": bwd_b / (ms_bwd * 1e-3) / 1e9,

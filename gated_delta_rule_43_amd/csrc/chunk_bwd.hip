@@ -767,26 +767,16 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(
 //   ADJ = true:  dS <- MM^T dS + NB from dsT, chunk after chunk from the last,
 //                writing each chunk's end-state gradient and finally ds0.
 template <int K, int V, int C, bool ADJ>
-__global__ __launch_bounds__(512) void bwd_chain_mfma_kernel(
-    const float *__restrict__ init, float *__restrict__ fin, const int32_t *__restrict__ cu,
-    int fixedT, int totalT, int H, const float *__restrict__ recs, float *__restrict__ out) {
+__device__ __forceinline__ void chain_mfma(int vt, int h, int n, const float *__restrict__ init,
+                                           float *__restrict__ fin, const int32_t *__restrict__ cu,
+                                           int fixedT, int totalT, int H,
+                                           const float *__restrict__ recs, float *__restrict__ out) {
     using Rc = BwdRec<K, V, C>;
     constexpr int NW = 8, KS = K / 4, RBW = K / (16 * NW);  // waves; k-steps; row blocks per wave
     static_assert(K == 128 && V % 16 == 0 && RBW == 1, "eight waves of one 16-row block");
     __shared__ float sS[K * 16];
     __shared__ int red[64 * NW];
-    // Workgroups are dealt to the eight XCDs round-robin in dispatch order;
-    // when there are eight value tiles and the (head, sequence) pairs come in
-    // eights, the tiles of one pair are mapped to one XCD, so that their reads
-    // of the chunk's MM (or MM^T) fragments share that XCD's L2.
-    int vt = blockIdx.x, hn = blockIdx.y + gridDim.y * blockIdx.z;
-    if (gridDim.x == 8 && (gridDim.y * gridDim.z) % 8 == 0) {
-        const int id = blockIdx.x + 8 * hn;  // dispatch order
-        vt = (id / 8) % 8;
-        hn = id % 8 + 8 * (id / 64);
-    }
-    const int h = hn % gridDim.y, n = hn / gridDim.y, t = threadIdx.x;
-    const int lane = t & 63, w = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
     const int nch = (eos - bos + C - 1) / C;
@@ -869,6 +859,33 @@ __global__ __launch_bounds__(512) void bwd_chain_mfma_kernel(
                 const int row = 16 * (RBW * w + b) + 4 * (lane >> 4) + i;
                 fin[sbase + (size_t)row * V] = acc[b][i];
             }
+}
+
+// Both chains in one launch (they read different parts of the record and
+// write different buffers, and each alone fills a quarter of the CUs at most
+// on one sequence): grid (V / 16, H, 2 N) (launched in z slices from z0), z < N
+// the state chain of sequence z, z >= N the state-gradient chain of sequence
+// z - N.  Workgroups are dealt
+// to the eight XCDs round-robin in dispatch order; when there are eight value
+// tiles and the (head, z) pairs come in eights, the tiles of one pair are
+// mapped to one XCD, so that their reads of the chunk's fragments share that
+// XCD's L2.
+template <int K, int V, int C>
+__global__ __launch_bounds__(512) void bwd_chain_mfma_kernel(
+    const float *__restrict__ s0, const float *__restrict__ dsT, float *__restrict__ ds0,
+    const int32_t *__restrict__ cu, int N, int z0, int fixedT, int totalT, int H,
+    const float *__restrict__ recs, float *__restrict__ Sst, float *__restrict__ dSe) {
+    int vt = blockIdx.x, hz = blockIdx.y + gridDim.y * blockIdx.z;
+    if (gridDim.x == 8 && (gridDim.y * gridDim.z) % 8 == 0) {
+        const int id = blockIdx.x + 8 * hz;  // dispatch order
+        vt = (id / 8) % 8;
+        hz = id % 8 + 8 * (id / 64);
+    }
+    const int h = hz % gridDim.y, z = z0 + hz / gridDim.y;
+    if (z < N)
+        chain_mfma<K, V, C, false>(vt, h, z, s0, nullptr, cu, fixedT, totalT, H, recs, Sst);
+    else
+        chain_mfma<K, V, C, true>(vt, h, z - N, dsT, ds0, cu, fixedT, totalT, H, recs, dSe);
 }
 
 // ------------------------------------------------------------------ pass 3
@@ -1699,21 +1716,25 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
                                fixedT, totalT, H, recs);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if constexpr (K == 128)
-            hipLaunchKernelGGL((bwd_chain_mfma_kernel<K, V, C, false>), dim3(V / 16, H, N), dim3(512),
-                               0, stream, s0, nullptr, cu, fixedT, totalT, H, recs, Sst);
-        else
+        if constexpr (K != 128) {
             hipLaunchKernelGGL(k1, dim3(V / VT, H, N), dim3(BNT), lds1, stream, s0, cu, fixedT,
                                totalT, H, recs, Sst);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     }
-    if constexpr (K == 128)
-        hipLaunchKernelGGL((bwd_chain_mfma_kernel<K, V, C, true>), dim3(V / 16, H, N), dim3(512), 0,
-                           stream, dsT, ds0, cu, fixedT, totalT, H, recs, dSe);
-    else
+    if constexpr (K == 128) {
+        // both chains in one grid; z slices of at most 65535 workgroups
+        for (int z0 = 0; z0 < 2 * N; z0 += 65535) {
+            const int nz = std::min(65535, 2 * N - z0);
+            hipLaunchKernelGGL((bwd_chain_mfma_kernel<K, V, C>), dim3(V / 16, H, nz), dim3(512), 0,
+                               stream, s0, dsT, ds0, cu, N, z0, fixedT, totalT, H, recs, Sst, dSe);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    } else {
         hipLaunchKernelGGL(k2, dim3(V / VT, H, N), dim3(BNT), lds2, stream, dsT, ds0, cu, fixedT,
                            totalT, H, recs, dSe);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (cap > 0) {
         if constexpr (K == 128)
             hipLaunchKernelGGL((bwd_udy_mfma_kernel<K, V, C, VT3>), dim3((unsigned)cap, H), dim3(512),
