@@ -605,7 +605,8 @@ __global__ __launch_bounds__(PNT) void bwd_trans_mfma_kernel(
         for (int i = 0; i < 4; ++i) {
             const int c = 16 * w + 4 * lq + i, j = 16 * jb + lr;
             const float m = sF[c] * ((c == j ? 1.f : 0.f) - accM[jb][i]) * sE[j];
-            rec[Rc::MM + (size_t)c * K + j] = m;
+            // only the fragment-ordered copies: the matrix-core chains read
+            // those, and nothing reads the row-major MM at this size
             rec[Rc::MMA + Rc::frag(c, j)] = m;
             rec[Rc::MMTA + Rc::frag(j, c)] = m;
         }
