@@ -95,6 +95,16 @@ __device__ int first_chunk(const int32_t *cu, int n, int fixedT, int totalT, int
     return r;
 }
 
+// Chunks of sequence [bos, eos) that a state chain walks, clamped so that
+// its records [first, first + nch) stay inside the workspace's cap chunks:
+// with malformed (non-monotone) cu_seqlens the per-sequence counts can sum
+// past cap, and those chunks are then skipped rather than addressed.
+__device__ __forceinline__ int chain_chunks(int bos, int eos, int C, int first, int cap) {
+    const int nch = (eos - bos + C - 1) / C;
+    const int room = cap - first;
+    return nch < room ? nch : (room > 0 ? room : 0);
+}
+
 // Sequence and local chunk of packed chunk gc; n = -1 past the last chunk
 // (all NT threads; red holds NT ints).
 template <int NT>
@@ -635,7 +645,7 @@ __global__ __launch_bounds__(PNT) void bwd_trans_mfma_kernel(
 template <int K, int V, int C, int VT>
 __global__ __launch_bounds__(BNT) void bwd_states_kernel(
     const float *__restrict__ s0, const int32_t *__restrict__ cu, int fixedT, int totalT, int H,
-    const float *__restrict__ recs, float *__restrict__ Sst) {
+    int cap, const float *__restrict__ recs, float *__restrict__ Sst) {
     using Rc = BwdRec<K, V, C>;
     constexpr int PK = K + 1, RB = K * VT / BNT;
     static_assert(K * VT % BNT == 0 && BNT % VT == 0, "tile must cover the workgroup");
@@ -647,8 +657,8 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(
     const int vt = blockIdx.x, h = blockIdx.y, n = blockIdx.z, t = threadIdx.x;
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
-    const int nch = (eos - bos + C - 1) / C;
     const int first = first_chunk<BNT>(cu, n, fixedT, totalT, C, red);
+    const int nch = chain_chunks(bos, eos, C, first, cap);
     const int j = t % VT, cb = (t / VT) * RB;  // this thread's column and first row
     float S[RB], nn[RB];
 #pragma unroll
@@ -697,7 +707,8 @@ __global__ __launch_bounds__(BNT) void bwd_states_kernel(
 template <int K, int V, int C, int VT>
 __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(
     const float *__restrict__ dsT, float *__restrict__ ds0, const int32_t *__restrict__ cu,
-    int fixedT, int totalT, int H, const float *__restrict__ recs, float *__restrict__ dSe) {
+    int fixedT, int totalT, int H, int cap, const float *__restrict__ recs,
+    float *__restrict__ dSe) {
     using Rc = BwdRec<K, V, C>;
     constexpr int PK = K + 1, RB = K * VT / BNT;
     static_assert(K * VT % BNT == 0 && BNT % VT == 0, "tile must cover the workgroup");
@@ -709,8 +720,8 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(
     const int vt = blockIdx.x, h = blockIdx.y, n = blockIdx.z, t = threadIdx.x;
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
-    const int nch = (eos - bos + C - 1) / C;
     const int first = first_chunk<BNT>(cu, n, fixedT, totalT, C, red);
+    const int nch = chain_chunks(bos, eos, C, first, cap);
     const int j = t % VT, cb = (t / VT) * RB;
     const size_t sbase = ((size_t)n * H + h) * K * V + vt * VT + j;
     float D[RB], nb[RB];
@@ -770,7 +781,7 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(
 template <int K, int V, int C, bool ADJ>
 __device__ __forceinline__ void chain_mfma(int vt, int h, int n, const float *__restrict__ init,
                                            float *__restrict__ fin, const int32_t *__restrict__ cu,
-                                           int fixedT, int totalT, int H,
+                                           int fixedT, int totalT, int H, int cap,
                                            const float *__restrict__ recs, float *__restrict__ out) {
     using Rc = BwdRec<K, V, C>;
     constexpr int NW = 8, KS = K / 4, RBW = K / (16 * NW);  // waves; k-steps; row blocks per wave
@@ -780,8 +791,8 @@ __device__ __forceinline__ void chain_mfma(int vt, int h, int n, const float *__
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     int bos, eos;
     seq_bounds(cu, n, fixedT, totalT, bos, eos);
-    const int nch = (eos - bos + C - 1) / C;
     const int first = first_chunk<64 * NW>(cu, n, fixedT, totalT, C, red);
+    const int nch = chain_chunks(bos, eos, C, first, cap);
     const int col = vt * 16 + (lane & 15);
     const size_t sbase = ((size_t)n * H + h) * K * V + col;
     const size_t fofs = ADJ ? Rc::MMTA : Rc::MMA, aofs = ADJ ? Rc::NB : Rc::NN;
@@ -874,7 +885,7 @@ __device__ __forceinline__ void chain_mfma(int vt, int h, int n, const float *__
 template <int K, int V, int C>
 __global__ __launch_bounds__(512) void bwd_chain_mfma_kernel(
     const float *__restrict__ s0, const float *__restrict__ dsT, float *__restrict__ ds0,
-    const int32_t *__restrict__ cu, int N, int z0, int fixedT, int totalT, int H,
+    const int32_t *__restrict__ cu, int N, int z0, int fixedT, int totalT, int H, int cap,
     const float *__restrict__ recs, float *__restrict__ Sst, float *__restrict__ dSe) {
     int vt = blockIdx.x, hz = blockIdx.y + gridDim.y * blockIdx.z;
     if (gridDim.x == 8 && (gridDim.y * gridDim.z) % 8 == 0) {
@@ -884,9 +895,9 @@ __global__ __launch_bounds__(512) void bwd_chain_mfma_kernel(
     }
     const int h = hz % gridDim.y, z = z0 + hz / gridDim.y;
     if (z < N)
-        chain_mfma<K, V, C, false>(vt, h, z, s0, nullptr, cu, fixedT, totalT, H, recs, Sst);
+        chain_mfma<K, V, C, false>(vt, h, z, s0, nullptr, cu, fixedT, totalT, H, cap, recs, Sst);
     else
-        chain_mfma<K, V, C, true>(vt, h, z - N, dsT, ds0, cu, fixedT, totalT, H, recs, dSe);
+        chain_mfma<K, V, C, true>(vt, h, z - N, dsT, ds0, cu, fixedT, totalT, H, cap, recs, dSe);
 }
 
 // ------------------------------------------------------------------ pass 3
@@ -1719,7 +1730,7 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if constexpr (K != 128) {
             hipLaunchKernelGGL(k1, dim3(V / VT, H, N), dim3(BNT), lds1, stream, s0, cu, fixedT,
-                               totalT, H, recs, Sst);
+                               totalT, H, (int)cap, recs, Sst);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
@@ -1728,12 +1739,13 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
         for (int z0 = 0; z0 < 2 * N; z0 += 65535) {
             const int nz = std::min(65535, 2 * N - z0);
             hipLaunchKernelGGL((bwd_chain_mfma_kernel<K, V, C>), dim3(V / 16, H, nz), dim3(512), 0,
-                               stream, s0, dsT, ds0, cu, N, z0, fixedT, totalT, H, recs, Sst, dSe);
+                               stream, s0, dsT, ds0, cu, N, z0, fixedT, totalT, H, (int)cap, recs,
+                               Sst, dSe);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     } else {
         hipLaunchKernelGGL(k2, dim3(V / VT, H, N), dim3(BNT), lds2, stream, dsT, ds0, cu, fixedT,
-                           totalT, H, recs, dSe);
+                           totalT, H, (int)cap, recs, dSe);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (cap > 0) {
