@@ -28,3 +28,28 @@ def to_gpu(d: dict) -> dict:
 
 def report(name: str, **errs):
     print(f"[parity] {name}: " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+
+
+class StreamErr:
+    """max|x - x_ref| / RMS(x_ref) over a tensor compared piece by piece: the
+    maximum and the sum of squares are accumulated over the pieces, so the
+    ratio is the one over the whole tensor."""
+
+    def __init__(self):
+        self.max_abs = 0.0
+        self.sumsq = 0.0
+        self.count = 0
+
+    def update(self, x, ref):
+        x = x.detach().cpu().double().numpy() if hasattr(x, "detach") else np.asarray(x, np.float64)
+        ref = np.asarray(ref, np.float64)
+        assert x.shape == ref.shape, (x.shape, ref.shape)
+        assert np.all(np.isfinite(x)), "non-finite values in GPU output"
+        if x.size:
+            self.max_abs = max(self.max_abs, float(np.max(np.abs(x - ref))))
+            self.sumsq += float(np.sum(ref * ref))
+            self.count += ref.size
+
+    def value(self) -> float:
+        rms = float(np.sqrt(self.sumsq / self.count)) if self.count else 0.0
+        return self.max_abs / rms if rms > 0.0 else self.max_abs

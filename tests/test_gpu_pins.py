@@ -1,0 +1,209 @@
+"""Exactness and closed-form pins on the device, input-scale and decay-bound
+cases.
+
+* Retrieval with standard-basis keys ("Kimi K3: Open Frontier Intelligence
+  and Implementation Framework", section "Hybrid Attention Mechanism": KDA is
+  the delta rule with a channel-wise forget gate).  With alpha = 1, beta = 1,
+  S_0 = 0 and distinct keys k_t = e_pi(t) (T <= K), the delta rule stores
+  row pi(s) of S as exactly v_s, so a query q_t = k_s (s <= t) returns v_s and
+  S_T[pi(s), :] = v_s.  Every quantity the chunked kernels form from such
+  inputs is a sum with at most one nonzero term of values that fp16 and fp32
+  hold exactly, so the GPU must reproduce them bit for bit, on every path.
+* Pure decay (beta = 0): S_T = Diag(exp(sum_t g_t)) S_0 and
+  o_t = S_0^T (exp(G_t) * q_t) with G_t the inclusive running sum of g.
+* Scaled inputs: v and S_0 multiplied by 1e3 and by 1e-4 (the bf16 kernels
+  hold state and value tiles as fp16 matrix operands; these scales sit inside
+  the documented range).
+* Decay at the bf16 kernels' lower bound, and beyond it through fp32 inputs
+  (the documented route for steeper decay).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_43_amd import inputs, kda
+from oracle import oracle
+from tests.parity import TOL, rel_err, report, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+PATHS = {"two_pass": True, "fused": False}
+
+
+def _basis_inputs(seed, B, T, H, K, dtype):
+    """Standard-basis keys (a fresh permutation per (sequence, head)), queries
+    equal to an earlier or the current key, beta = 1, g = 0, and values that
+    bf16, fp16 and fp32 all hold exactly (|v| in [2^-8, 2^8], 8 significant bits)."""
+    assert T <= K
+    rng = np.random.default_rng(seed)
+    k = np.zeros((B, T, H, K), np.float32)
+    q = np.zeros((B, T, H, K), np.float32)
+    src = np.zeros((B, T, H), np.int64)
+    perm = np.zeros((B, H, K), np.int64)
+    for b in range(B):
+        for h in range(H):
+            pi = rng.permutation(K)
+            perm[b, h] = pi
+            for t in range(T):
+                s = int(rng.integers(0, t + 1))
+                src[b, t, h] = s
+                k[b, t, h, pi[t]] = 1.0
+                q[b, t, h, pi[s]] = 1.0
+    mant = rng.integers(128, 256, size=(B, T, H, K)).astype(np.float32) / 128.0
+    expo = rng.integers(-8, 8, size=(B, T, H, K)).astype(np.float32)
+    sign = np.where(rng.random((B, T, H, K)) < 0.5, -1.0, 1.0).astype(np.float32)
+    v = sign * mant * np.exp2(expo)
+    to = lambda a: inputs.to_dtype(a, dtype)
+    d = dict(q=to(q), k=to(k), v=to(v), g=to(np.zeros_like(q)),
+             beta=to(np.ones((B, T, H), np.float32)))
+    # expected: o_t = v_{src(t)}, S_T[pi(s), :] = v_s for s < T, other rows 0
+    o_exp = np.zeros((B, T, H, K), np.float32)
+    s_exp = np.zeros((B, H, K, K), np.float32)
+    for b in range(B):
+        for h in range(H):
+            for t in range(T):
+                o_exp[b, t, h] = v[b, src[b, t, h], h]
+                s_exp[b, h, perm[b, h, t]] = v[b, t, h]
+    return d, torch.from_numpy(o_exp), torch.from_numpy(s_exp)
+
+
+@pytest.mark.parametrize("K,dtype,path", [(128, "bf16", "two_pass"), (128, "bf16", "fused"),
+                                          (128, "f32", "fused"), (32, "f32", "fused"),
+                                          (32, "bf16", "fused")])
+def test_basis_key_retrieval_bit_exact(K, dtype, path):
+    T = K  # two chunks at K = 128 (chunk 64), two at K = 32 (chunk 16)
+    print(f"[case] basis-key retrieval K={K} {dtype} path={path}", flush=True)
+    d, o_exp, s_exp = _basis_inputs(50 + K, 3, T, 2, K, dtype)
+    # the oracle reaches the same exact values
+    o_ref, s_ref = oracle.fixed(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    assert np.array_equal(o_ref, o_exp.double().numpy()) and np.array_equal(s_ref, s_exp.double().numpy())
+    x = to_gpu(d)
+    tp = PATHS[path] if (K == 128 and dtype == "bf16") else None
+    o, sT = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], two_pass=tp)
+    torch.cuda.synchronize()
+    assert torch.equal(o.cpu(), o_exp), "retrieved values differ from the stored ones"
+    assert torch.equal(sT.cpu(), s_exp), "final state differs from the written rows"
+
+
+@pytest.mark.parametrize("K", [128, 32])
+def test_basis_key_retrieval_decode_bit_exact(K):
+    print(f"[case] basis-key retrieval, decode K={K}", flush=True)
+    T, N, H = K, 3, 2
+    d, o_exp, s_exp = _basis_inputs(60 + K, N, T, H, K, "bf16")
+    x = to_gpu(d)
+    st = torch.zeros(N, H, K, K, device="cuda")
+    outs = []
+    for t in range(T):
+        outs.append(kda.decode_step(x["q"][:, t].contiguous(), x["k"][:, t].contiguous(),
+                                    x["v"][:, t].contiguous(), x["g"][:, t].contiguous(),
+                                    x["beta"][:, t].contiguous(), st))
+    torch.cuda.synchronize()
+    assert torch.equal(torch.stack(outs, 1).cpu(), o_exp)
+    assert torch.equal(st.cpu(), s_exp)
+
+
+def _decay_only_expected(d):
+    """beta = 0 closed form, fp64: S_T = Diag(exp(sum g)) S_0, o_t = S_0^T (exp(G_t) q_t)."""
+    g = d["g"].double().numpy()                   # [B, T, H, K]
+    G = np.cumsum(g, axis=1)                      # inclusive running sum
+    q = d["q"].double().numpy()
+    s0 = d["s0"].double().numpy()                 # [B, H, K, V]
+    o = np.einsum("bthk,bhkv->bthv", np.exp(G) * q, s0)
+    sT = np.exp(G[:, -1])[..., None] * s0
+    return o, sT
+
+
+@pytest.mark.parametrize("K,dtype,path", [(128, "bf16", "two_pass"), (128, "bf16", "fused"),
+                                          (128, "f32", "fused"), (32, "f32", "fused"),
+                                          (32, "bf16", "fused")])
+def test_pure_decay_closed_form(K, dtype, path):
+    print(f"[case] beta = 0 closed form K={K} {dtype} path={path}", flush=True)
+    d = inputs.draw_fixed(70 + K, 2, 200, 2, K, K, dtype, s0_std=0.1)
+    d["beta"] = torch.zeros_like(d["beta"])
+    o_exp, s_exp = _decay_only_expected(d)
+    x = to_gpu(d)
+    tp = PATHS[path] if (K == 128 and dtype == "bf16") else None
+    o, sT = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], two_pass=tp)
+    torch.cuda.synchronize()
+    eo, es = rel_err(o, o_exp), rel_err(sT, s_exp)
+    report(f"pure_decay_K{K}_{dtype}_{path}", o=eo, sT=es)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+# (scale, paths): the single-pass kernel holds Diag(exp(G_m)) S as an fp16
+# operand, so its range ends where that product leaves fp16's normal range;
+# the two-pass path stores the chunk-start state itself in fp16.
+@pytest.mark.parametrize("scale,path", [(1e3, "two_pass"), (1e3, "fused"), (1e-2, "two_pass"),
+                                        (1e-2, "fused"), (1e-4, "two_pass")])
+def test_bf16_value_and_state_scale(scale, path):
+    print(f"[case] v, s0 scaled by {scale} path={path}", flush=True)
+    d = inputs.draw_fixed(90, 2, 300, 2, 128, 128, "bf16", s0_std=0.1)
+    d["v"] = (d["v"].float() * scale).to(torch.bfloat16)
+    d["s0"] = d["s0"] * scale
+    o_ref, s_ref = oracle.fixed(d["q"], d["k"], d["v"], d["g"], d["beta"], oracle.as_f64(d["s0"]))
+    x = to_gpu(d)
+    o, sT = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], two_pass=PATHS[path])
+    torch.cuda.synchronize()
+    eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+    report(f"scale_{scale}_{path}", o=eo, sT=es)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("K", [128, 32])
+def test_steep_decay_through_fp32_inputs(K):
+    # decay down to -2 per step (8x the workloads' bound): beyond what the bf16
+    # kernels take, the documented route is fp32 inputs, whose kernel forms
+    # every decay factor exactly
+    print(f"[case] fp32 inputs, g in [-2, 0], K={K}", flush=True)
+    d = inputs.draw_fixed(95, 1, 300, 2, K, K, "f32", s0_std=0.1, g_lb=2.0, g_mode="uniform")
+    o_ref, s_ref = oracle.fixed(d["q"], d["k"], d["v"], d["g"], d["beta"], oracle.as_f64(d["s0"]))
+    x = to_gpu(d)
+    o, sT = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"])
+    torch.cuda.synchronize()
+    eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+    report(f"steep_decay_f32_K{K}", o=eo, sT=es)
+    assert eo <= TOL["f32"] and es <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_decay_at_the_bound(dtype):
+    # every step at g = -0.25 (the bound the backward's fp32 factoring takes at chunk 64)
+    print(f"[case] backward, g = -0.25 everywhere, {dtype}", flush=True)
+    B, T, H, K = 1, 150, 2, 128
+    d = inputs.draw_fixed(96, B, T, H, K, K, dtype, s0_std=0.1, g_mode="bound")
+    rng = np.random.default_rng(97)
+    do = torch.from_numpy(rng.standard_normal((B, T, H, K)).astype(np.float32))
+    dsT = torch.from_numpy(rng.standard_normal((B, H, K, K)).astype(np.float32))
+    flat = lambda t: t.reshape(B * T, *t.shape[2:])
+    ref = oracle.backward(flat(d["q"]), flat(d["k"]), flat(d["v"]), flat(d["g"]), flat(d["beta"]),
+                          np.array([0, T]), oracle.as_f64(d["s0"]), flat(do).double().numpy(),
+                          dsT.double().numpy())
+    x = to_gpu(d)
+    got = kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do.cuda(),
+                        initial_state=x["s0"], dsT=dsT.cuda())
+    torch.cuda.synchronize()
+    errs = {n: rel_err(a.reshape(r.shape), r)
+            for n, a, r in zip(("dq", "dk", "dv", "dg", "dbeta", "ds0"), got, ref)}
+    report(f"bwd_bound_{dtype}", **errs)
+    assert all(e <= TOL[dtype] for e in errs.values()), errs
+
+
+def test_backward_malformed_cu_seqlens_stays_in_workspace():
+    """Non-monotone cu_seqlens (a precondition violation: values unspecified)
+    must not make the backward write outside its workspace: the bytes after
+    kda_bwd_workspace_bytes in a sentinel-filled buffer stay untouched."""
+    print("[case] backward, malformed cu_seqlens, sentinel-padded workspace", flush=True)
+    H, K, total = 2, 128, 6400
+    cu = torch.tensor([0, 6400, 0, 6400, 0, 6400], dtype=torch.int32, device="cuda")
+    N = cu.numel() - 1
+    d = to_gpu(inputs.draw_fixed(98, 1, total, H, K, K, "bf16"))
+    flat = {key: d[key].reshape(total, *d[key].shape[2:]) for key in ("q", "k", "v", "g", "beta")}
+    need = kda.bwd_workspace_bytes(N, total, H, K, K, 64)
+    pad = 4 << 20
+    ws = torch.full((need + pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    do = torch.randn(total, H, K, device="cuda")
+    kda.varlen_bwd(flat["q"], flat["k"], flat["v"], flat["g"], flat["beta"], do, cu,
+                   workspace=ws[:need])
+    torch.cuda.synchronize()
+    assert bool((ws[need:] == 0xA5).all()), "the backward wrote past its workspace"
