@@ -18,22 +18,27 @@
 // -g_lb <= g <= 0 and g_lb * C / 2 <= 8 every factor stays within e^8, inside
 // fp16 range: this is where the lower bound on the decay is used.
 //
-// Mapping onto CDNA4.  One workgroup = 8 wavefronts owns one (sequence, head,
-// 64-column V tile) and runs two wave groups concurrently:
-//  * state waves 0-3: wave jb owns value columns 16 jb..16 jb+15 and keeps the
+// Mapping onto CDNA4.  One workgroup of 12 wavefronts owns one (sequence,
+// head, 64-column V tile); the two tiles of a head run side by side on two
+// CUs of one XCD.  Two wave groups run concurrently, separated by two
+// workgroup barriers per chunk:
+//  * state waves 0-3: wave w owns value columns 16 w .. 16 w + 15 and keeps the
 //    128 x 16 fp32 state slice in MFMA accumulators for the whole sequence.
-//    Per chunk it forms S', the inter-chunk products Kp S' and Qp S'
-//    (v_mfma_f32_16x16x32_f16), solves (I + A) U = rhs by 16-row block
-//    substitution entirely in registers (the 16x16 accumulator layout is the
-//    B-operand layout of v_mfma_f32_16x16x16_f16), adds P U, stores O and
-//    advances the state.  Its LDS traffic is wave-private or read-only.
-//  * prep waves 4-7: wave p owns key channels 32p..32p+31.  While the state
-//    waves finish chunk c they build chunk c+1's operands (16-byte loads
-//    issued one chunk ahead, running decay sums by wave-local shuffles,
-//    exponentials, fp16 tiles in LDS); then, while the state waves start
-//    chunk c+1, they form its Gram and query-key blocks and the 16 x 16
-//    diagonal inverses (I + A_ii)^-1 in fp32.
-// Two workgroup barriers per chunk separate these phases.
+//    Per chunk (phase A) it forms S', takes its fp16 B fragments straight from
+//    the accumulators (the operand tiles store their contraction index in the
+//    matching permuted order), and forms Kp S' and, transposed, (Qp S')^T with
+//    v_mfma_f32_16x16x32_f16; then (phase B) it solves (I + A) U = Y by 16-row
+//    block substitution in registers (the 16x16 accumulator layout is the B
+//    layout of v_mfma_f32_16x16x16_f16), advances the state with Km^T U,
+//    adds (P U)^T to the transposed output and stores four consecutive
+//    columns of an output row per lane.
+//  * prep waves 4-11: prep wave p owns tokens 8p .. 8p + 7 of a chunk.  In
+//    phase A they form the current chunk's Gram and query-key blocks and the
+//    16 x 16 diagonal inverses (I + A_ii)^-1 in fp32; in phase B they build
+//    the next chunk's fp16 operand tiles (running decay sums, exponentials),
+//    take the running decay sums of the chunk after it, and issue the global
+//    loads for the iteration after this one.
+// Packed sequences are dealt to workgroups longest first.
 #include "kda_mfma.hpp"
 #include "prologue.hpp"
 #include "state_io.hpp"
@@ -51,92 +56,133 @@ constexpr int PK = 144;  // LDS pitch (halves) of [64][128] fp16 tiles
 constexpr int PC = 72;   // LDS pitch (halves) of [*][64] fp16 tiles read as 16-byte fragments
 constexpr int P4 = 68;   // LDS pitch (halves) of [64][64] fp16 tiles read as 8-byte fragments
 constexpr int PI = 20;   // LDS pitch (halves) of 16 x 16 fp16 blocks
-constexpr int PF = 17;   // LDS pitch (floats) of 16 x 16 fp32 blocks
+constexpr int PF = 20;   // LDS pitch (floats) of 16 x 16 fp32 blocks
+constexpr int PV = 72;   // LDS pitch (halves) of the transposed V tile
+
+// Position of index x (0..31) inside its 32-block in the permuted operand
+// order: x = 4 g + t -> 8 g + t and x = 16 + 4 g + t -> 8 g + 4 + t (t < 4).
+// A lane of a 16 x 16 accumulator holds rows 4 (lane >> 4) + t of two
+// consecutive 16-row blocks; in this order those eight rows are exactly the
+// contraction indices 8 (lane >> 4) .. + 7 of a 16x16x32 B fragment.  Tiles
+// whose contraction index is a state row (the channel index of Kp, Qp, Km)
+// or a chunk row (the token index of Km^T) are stored in this order, so that
+// the state and U serve as B operands straight from the accumulators.
+__device__ __forceinline__ int perm32(int x) {
+    return x < 16 ? 8 * (x >> 2) + (x & 3) : 8 * ((x - 16) >> 2) + 4 + (x & 3);
+}
 
 struct Smem {
-    _Float16 kp[C * PK];        // Kp [s][c]
-    _Float16 qp[C * PK];        // Qp [s][c]
-    _Float16 km[C * PK];        // Km [s][c]   (Gram / query-key B operand)
-    _Float16 kmt[2][KD * PC];   // Km^T [c][s] (state-advance A operand), by chunk parity;
-                                // 8-token column blocks XOR-swizzled by (c >> 3) & 7
+    _Float16 kp[C * PK];        // Kp [s][c'] (c' = channel position, permuted order)
+    _Float16 qp[C * PK];        // Qp [s][c']
+    _Float16 km[C * PK];        // Km [s][c']  (Gram / query-key B operand)
+    _Float16 kmt[2][KD * PC];   // Km^T [c][s'] (state-advance A operand; s' permuted order),
+                                // by chunk parity; 8-token blocks XOR-swizzled by (c >> 3) & 7
     _Float16 a16[C * P4];       // A [r][s], lower blocks
     _Float16 p[C * P4];         // P [r][s], lower blocks
     _Float16 tii[4][16 * PI];   // (I + A_ii)^-1, diagonal blocks
-    uint16_t v[C * PC];         // bf16 V tile [r][j]
+    uint16_t vt[VT * PV];       // bf16 V tile, transposed [j][r]
     float beta[C];
     float fm[2][KD];            // exp(G_m), by chunk parity
     float fc[2][KD];            // exp(G_C - G_m), by chunk parity
-    _Float16 st[4][16 * PK];    // state waves: S'^T [j][c] (private)
-    _Float16 ut[4][16 * PC];    // state waves: U^T [j][s] (private)
     float ad[4][16 * PF];       // prep waves: diagonal A blocks (private)
-    float gsum[NP][KD];         // prep waves: per-wave channel sums of g (next chunk)
+    float gsum[2][NP][KD];      // prep waves: per-wave channel sums of g, by chunk parity
 };
 
-// frag8 from the swizzled Km^T tile: row c, logical 8-token block kb = 4 ks + (lane >> 4)
+// frag8 from the swizzled Km^T tile: row c, 8-position block kb = 4 ks + (lane >> 4)
 // stored at block kb ^ ((c >> 3) & 7).
 __device__ __forceinline__ half8 frag8_kmt(const _Float16 *base, int row0, int ks, int lane) {
     const int c = row0 + (lane & 15);
     const int kb = (4 * ks + (lane >> 4)) ^ ((c >> 3) & 7);
     return *reinterpret_cast<const half8 *>(base + c * PC + 8 * kb);
 }
-// One chunk's inputs, held in a prep wave's registers ahead of use.
-// Lane (cg = lane & 15, tb = lane >> 4) of prep wave p holds channels
-// 8 cg .. 8 cg + 7 of tokens 8p + 2 tb and 8p + 2 tb + 1, so each wave reads
-// whole 256-byte rows.  g is fetched one phase earlier than the rest because
-// its running sum is needed first.
-struct Raw {
-    uint4 q[2], k[2];
-    uint4 v;         // V tile piece: row idx >> 3, columns 8 (idx & 7) .., idx = 64p + lane
-    uint32_t beta;   // prep wave 0: beta of token lane
-};
 
-// Rows past the chunk's end read as `pad` (zeros, or gate logits mapping to 0).
-__device__ __forceinline__ void load_g(uint4 *rg, const uint16_t *g, int c0, int L, int H, int h,
-                                       int p, int lane, uint32_t pad) {
-    const int cg = lane & 15, tb = lane >> 4;
+__device__ __forceinline__ half8 cat8(half4 a, half4 b) {
+    half8 r;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int r = 8 * p + 2 * tb + u;
-        rg[u] = make_uint4(pad, pad, pad, pad);
-        if (r < L) rg[u] = *reinterpret_cast<const uint4 *>(g + ((size_t)(c0 + r) * H + h) * KD + 8 * cg);
+    for (int i = 0; i < 4; ++i) {
+        r[i] = a[i];
+        r[i + 4] = b[i];
     }
+    return r;
 }
 
-// Beta of tokens past the chunk's end reads as `bpad` (zero, or a logit mapping to 0).
-__device__ __forceinline__ void load_raw(Raw &R, const uint16_t *q, const uint16_t *k,
-                                         const uint16_t *v, const uint16_t *beta, int c0, int L,
-                                         int H, int h, int vt, int p, int lane, uint32_t bpad) {
+// One chunk's inputs, held in a prep wave's registers ahead of use.
+// Lane (cg = lane & 15, tb = lane >> 4) of prep wave p holds channels
+// 8 cg .. 8 cg + 7 of tokens 8p + 2 tb and 8p + 2 tb + 1 (16-byte loads, each
+// instruction reading four whole 256-byte rows).  Every lane loads the same
+// rows whatever the chunk's length L >= 1: rows past the end re-read row
+// L - 1, and the consumers replace them by padding (at use, so that no wait is
+// forced at the load).
+struct Raw {
+    uint4 q[2], k[2];
+    uint4 v;         // V tile piece: row lane, columns 8p .. 8p + 7
+    uint32_t beta;   // beta of token lane (used by prep wave 0)
+    int L;           // the chunk's length
+};
+
+// Offsets (in 16-byte units, from the chunk's first row of head h) of this
+// lane's two token rows, clamped to the chunk.
+__device__ __forceinline__ void row_vecs(int *off, int L, int H, int p, int lane) {
     const int cg = lane & 15, tb = lane >> 4;
 #pragma unroll
+    for (int u = 0; u < 2; ++u) off[u] = min(8 * p + 2 * tb + u, L - 1) * (H * KD / 8) + cg;
+}
+
+__device__ __forceinline__ void load_g(uint4 *rg, const uint16_t *g, int c0, int L, int H, int h,
+                                       int p, int lane) {
+    const uint4 *base = reinterpret_cast<const uint4 *>(g + ((size_t)c0 * H + h) * KD);
+    int off[2];
+    row_vecs(off, L, H, p, lane);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) rg[u] = base[off[u]];
+}
+
+__device__ __forceinline__ void load_raw(Raw &R, const uint16_t *q, const uint16_t *k,
+                                         const uint16_t *v, const uint16_t *beta, int c0, int L,
+                                         int H, int h, int vt, int p, int lane) {
+    const size_t cb = ((size_t)c0 * H + h) * KD;
+    const uint4 *bq = reinterpret_cast<const uint4 *>(q + cb);
+    const uint4 *bk = reinterpret_cast<const uint4 *>(k + cb);
+    int off[2];
+    row_vecs(off, L, H, p, lane);
+#pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int r = 8 * p + 2 * tb + u;
-        R.q[u] = make_uint4(0u, 0u, 0u, 0u);
-        R.k[u] = R.q[u];
-        if (r < L) {
-            const size_t off = ((size_t)(c0 + r) * H + h) * KD + 8 * cg;
-            R.q[u] = *reinterpret_cast<const uint4 *>(q + off);
-            R.k[u] = *reinterpret_cast<const uint4 *>(k + off);
-        }
+        R.q[u] = bq[off[u]];
+        R.k[u] = bk[off[u]];
     }
-    const int idx = 64 * p + lane;
-    R.v = make_uint4(0u, 0u, 0u, 0u);
-    if ((idx >> 3) < L)
-        R.v = *reinterpret_cast<const uint4 *>(v + ((size_t)(c0 + (idx >> 3)) * H + h) * VD +
-                                               vt * VT + 8 * (idx & 7));
-    R.beta = (p == 0 && lane < L) ? beta[(size_t)(c0 + lane) * H + h] : bpad;
+    const uint4 *bv = reinterpret_cast<const uint4 *>(v + ((size_t)c0 * H + h) * VD + vt * VT + 8 * p);
+    R.v = bv[min(lane, L - 1) * (H * VD / 8)];
+    R.beta = beta[((size_t)c0 + min(lane, L - 1)) * H + h];
+    R.L = L;
+}
+
+// The lane values of the even and of the odd 16-lane row of this lane's row
+// pair (rows 0-1, 2-3), and of the lower and upper row pairs, through the
+// row-swapping permutes (v_permlane16_swap / v_permlane32_swap).
+__device__ __forceinline__ void pair_rows(float x, float &even, float &odd) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    even = __uint_as_float(r[0]);
+    odd = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void half_rows(float x, float &lower, float &upper) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    lower = __uint_as_float(r[0]);
+    upper = __uint_as_float(r[1]);
 }
 
 // Prep wave p, first half of the running log-decay sum: lc = running sum over
-// this lane's two tokens, then an inclusive scan over the wave's four token
-// pairs (lanes 16 apart share channels).  The wave's channel totals go to LDS;
-// ex keeps the in-wave exclusive prefix.  PM (a ProMode): rg holds gate
-// logits when the prologue's gate map applies.
+// this lane's two tokens, then the exclusive prefix ex over the wave's four
+// 16-lane rows (token pairs; lanes 16 apart share channels) by row permutes.
+// The wave's channel totals go to LDS.  Rows at or past L read as `pad`.
+// PM (a ProMode): rg holds gate logits when the prologue's gate map applies.
 template <int PM>
-__device__ __forceinline__ void scan_partials(Smem &sm, const uint4 *rg, int p, int lane,
-                                              float (*lc)[8], float *ex, const Prologue &pro) {
+__device__ __forceinline__ void scan_partials(Smem &sm, const uint4 *rg, int L, uint32_t pad,
+                                              int par, int p, int lane, float (*lc)[8], float *ex,
+                                              const Prologue &pro) {
     const int cg = lane & 15, tb = lane >> 4;
-    unpack8(rg[0], lc[0]);
-    unpack8(rg[1], lc[1]);
+    const uint4 pad4 = make_uint4(pad, pad, pad, pad);
+    unpack8(8 * p + 2 * tb < L ? rg[0] : pad4, lc[0]);
+    unpack8(8 * p + 2 * tb + 1 < L ? rg[1] : pad4, lc[1]);
     if (pro_on<PM>(pro, PRO_GATE_LOGIT)) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -144,17 +190,20 @@ __device__ __forceinline__ void scan_partials(Smem &sm, const uint4 *rg, int p, 
             lc[1][e] = gate_from_logit(lc[1][e], pro.glb);
         }
     }
+    float tot[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         lc[1][e] += lc[0][e];
         const float loc = lc[1][e];
-        float s = loc;
-        float x = __shfl_up(s, 16);
-        if (tb >= 1) s += x;
-        x = __shfl_up(s, 32);
-        if (tb >= 2) s += x;
-        ex[e] = s - loc;
-        if (tb == 3) sm.gsum[p][8 * cg + e] = s;
+        float ev, od, lower, upper;
+        pair_rows(loc, ev, od);
+        half_rows(ev + od, lower, upper);
+        ex[e] = ((tb & 1) ? ev : 0.f) + (tb >= 2 ? lower : 0.f);
+        tot[e] = lower + upper;
+    }
+    if (tb == 0) {
+        *reinterpret_cast<floatx4 *>(&sm.gsum[par][p][8 * cg]) = floatx4{tot[0], tot[1], tot[2], tot[3]};
+        *reinterpret_cast<floatx4 *>(&sm.gsum[par][p][8 * cg + 4]) = floatx4{tot[4], tot[5], tot[6], tot[7]};
     }
 }
 
@@ -163,9 +212,9 @@ __device__ __forceinline__ void scan_partials(Smem &sm, const uint4 *rg, int p, 
 // prologue's normalisation of q and k, whose 128 channels of a token lie in
 // one 16-lane DPP row).
 template <int PM>
-__device__ __forceinline__ void build_operands(Smem &sm, const Raw &R, int par, int p, int lane,
-                                               const float (*lc)[8], const float *ex,
-                                               const Prologue &pro) {
+__device__ __forceinline__ void build_operands(Smem &sm, const Raw &R, uint32_t bpad, int par,
+                                               int p, int lane, const float (*lc)[8],
+                                               const float *ex, const Prologue &pro) {
     const int cg = lane & 15, tb = lane >> 4;
     const int ch0 = 8 * cg;
     const int r0 = 8 * p + 2 * tb;
@@ -176,39 +225,46 @@ __device__ __forceinline__ void build_operands(Smem &sm, const Raw &R, int par, 
     for (int e = 0; e < 8; ++e) d[e] = 0.f;
     const int lo = p < 4 ? p : 4, hi = p < 4 ? 4 : p;
     for (int ww = lo; ww < hi; ++ww) {
-        const floatx4 a = *reinterpret_cast<const floatx4 *>(&sm.gsum[ww][ch0]);
-        const floatx4 b = *reinterpret_cast<const floatx4 *>(&sm.gsum[ww][ch0 + 4]);
+        const floatx4 a = *reinterpret_cast<const floatx4 *>(&sm.gsum[par][ww][ch0]);
+        const floatx4 b = *reinterpret_cast<const floatx4 *>(&sm.gsum[par][ww][ch0 + 4]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             d[e] += a[e];
             d[e + 4] += b[e];
         }
     }
-    if (p == 0 && tb == 0) {  // per-channel factors exp(G_m) and exp(G_C - G_m)
+    if (p == 4) {  // per-channel factors exp(G_m) and exp(G_C - G_m), two channels per lane
+        float gm0 = 0.f, gm1 = 0.f, gc0 = 0.f, gc1 = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float gm = 0.f, gc = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NP; ++ww) {
-                const float x = sm.gsum[ww][ch0 + e];
-                if (ww < 4) gm += x;
-                gc += x;
+        for (int ww = 0; ww < NP; ++ww) {
+            const float2 x = *reinterpret_cast<const float2 *>(&sm.gsum[par][ww][2 * lane]);
+            if (ww < 4) {
+                gm0 += x.x;
+                gm1 += x.y;
             }
-            sm.fm[par][ch0 + e] = fast_exp(gm);
-            sm.fc[par][ch0 + e] = fast_exp(gc - gm);
+            gc0 += x.x;
+            gc1 += x.y;
         }
+        *reinterpret_cast<float2 *>(&sm.fm[par][2 * lane]) = make_float2(fast_exp(gm0), fast_exp(gm1));
+        *reinterpret_cast<float2 *>(&sm.fc[par][2 * lane]) =
+            make_float2(fast_exp(gc0 - gm0), fast_exp(gc1 - gm1));
     }
     float pre[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) pre[e] = ex[e] + (p < 4 ? -d[e] : d[e]);
+    // channels ch0 .. ch0 + 3 and ch0 + 4 .. ch0 + 7 sit 8 positions apart in
+    // the permuted order
+    const int cpos = (ch0 & ~31) + perm32(ch0 & 31);
     // one token row at a time (fewer live registers); Km of both rows is kept
     // for the transposed tile
     half8 hkm0, hkm1;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         float kv[8], qv[8];
-        unpack8(R.k[u], kv);
-        unpack8(R.q[u], qv);
+        const bool valid = r0 + u < R.L;
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        unpack8(valid ? R.k[u] : z, kv);
+        unpack8(valid ? R.q[u] : z, qv);
         if (pro_on<PM>(pro, PRO_NORM_QK)) {
             const float ik = inv_norm(row16_sum(sumsq8(kv)), pro.eps);
             const float iq = inv_norm(row16_sum(sumsq8(qv)), pro.eps);
@@ -227,34 +283,50 @@ __device__ __forceinline__ void build_operands(Smem &sm, const Raw &R, int par, 
             hkm[e] = (_Float16)(kv[e] * i);
             hqp[e] = (_Float16)(qv[e] * f);
         }
-        *reinterpret_cast<half8 *>(&sm.kp[(r0 + u) * PK + ch0]) = hkp;
-        *reinterpret_cast<half8 *>(&sm.km[(r0 + u) * PK + ch0]) = hkm;
-        *reinterpret_cast<half8 *>(&sm.qp[(r0 + u) * PK + ch0]) = hqp;
+        const int rb = (r0 + u) * PK + cpos;
+        *reinterpret_cast<half4 *>(&sm.kp[rb]) = hkp.lo;
+        *reinterpret_cast<half4 *>(&sm.kp[rb + 8]) = hkp.hi;
+        *reinterpret_cast<half4 *>(&sm.km[rb]) = hkm.lo;
+        *reinterpret_cast<half4 *>(&sm.km[rb + 8]) = hkm.hi;
+        *reinterpret_cast<half4 *>(&sm.qp[rb]) = hqp.lo;
+        *reinterpret_cast<half4 *>(&sm.qp[rb + 8]) = hqp.hi;
         if (u == 0) hkm0 = hkm;
         else hkm1 = hkm;
     }
+    // Km^T: tokens r0, r0 + 1 sit next to each other in the permuted order
+    const int tp = 32 * (p >> 2) + 16 * (p & 1) + 4 * ((p >> 1) & 1) + 8 * (tb >> 1) + 2 * (tb & 1);
+    const int kb = tp >> 3, ko = tp & 7;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         half2v pr;
         pr[0] = hkm0[e];
         pr[1] = hkm1[e];
-        // column block p of row ch0 + e, swizzled by the row's channel group cg
-        *reinterpret_cast<half2v *>(&sm.kmt[par][(ch0 + e) * PC + 8 * (p ^ (cg & 7)) + 2 * tb]) = pr;
+        *reinterpret_cast<half2v *>(&sm.kmt[par][(ch0 + e) * PC + 8 * (kb ^ (cg & 7)) + ko]) = pr;
     }
-    const int idx = 64 * p + lane;
-    *reinterpret_cast<uint4 *>(&sm.v[(idx >> 3) * PC + 8 * (idx & 7)]) = R.v;
+    // V transposed: columns 8p .. 8p + 7, row lane (consecutive lanes write
+    // consecutive halves)
+    const uint4 vv = lane < R.L ? R.v : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        sm.vt[(8 * p + 2 * e) * PV + lane] = (uint16_t)(vw[e] & 0xFFFFu);
+        sm.vt[(8 * p + 2 * e + 1) * PV + lane] = (uint16_t)(vw[e] >> 16);
+    }
     if (p == 0) {
-        const float b = __uint_as_float(R.beta << 16);
+        const float b = __uint_as_float((lane < R.L ? R.beta : bpad) << 16);
         sm.beta[lane] = pro_on<PM>(pro, PRO_BETA_LOGIT) ? sigmoid_f(b) : b;
     }
 }
 
-__device__ __forceinline__ floatx4 block_product(const _Float16 *lhs, const _Float16 *rhs, int bi,
-                                                 int bj, int lane) {
+// Transposed block product: lane (l16, lg) receives element i =
+// (lhs rhs^T)[16 bi + l16][16 bj + 4 lg + i], i.e. one row of the block and
+// four consecutive columns (which an 8-byte store keeps together).
+__device__ __forceinline__ floatx4 block_product_t(const _Float16 *lhs, const _Float16 *rhs,
+                                                   int bi, int bj, int lane) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-        acc = mma32(frag8(lhs, PK, 16 * bi, 32 * ks, lane), frag8(rhs, PK, 16 * bj, 32 * ks, lane), acc);
+        acc = mma32(frag8(rhs, PK, 16 * bj, 32 * ks, lane), frag8(lhs, PK, 16 * bi, 32 * ks, lane), acc);
     return acc;
 }
 
@@ -264,19 +336,18 @@ __device__ __forceinline__ floatx4 block_product(const _Float16 *lhs, const _Flo
 __device__ __forceinline__ void prep_blocks(Smem &sm, int p, int lane) {
     const int l16 = lane & 15, lg = lane >> 4;
     if (p < 4) {
-        const floatx4 a = block_product(sm.kp, sm.km, p, p, lane);
+        const floatx4 a = block_product_t(sm.kp, sm.km, p, p, lane);
+        const float br = sm.beta[16 * p + l16];
+        floatx4 am;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) am[i] = 4 * lg + i < l16 ? br * a[i] : 0.f;
         float *ad = sm.ad[p];
+        *reinterpret_cast<floatx4 *>(&ad[l16 * PF + 4 * lg]) = am;
+        const floatx4 pq = block_product_t(sm.qp, sm.km, p, p, lane);
+        half4 ph;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * lg + i;
-            ad[r * PF + l16] = l16 < r ? sm.beta[16 * p + r] * a[i] : 0.f;
-        }
-        const floatx4 pq = block_product(sm.qp, sm.km, p, p, lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * lg + i;
-            sm.p[(16 * p + r) * P4 + 16 * p + l16] = (_Float16)(l16 <= r ? pq[i] : 0.f);
-        }
+        for (int i = 0; i < 4; ++i) ph[i] = (_Float16)(4 * lg + i <= l16 ? pq[i] : 0.f);
+        *reinterpret_cast<half4 *>(&sm.p[(16 * p + l16) * P4 + 16 * p + 4 * lg]) = ph;
         // (I + A_pp)^-1 by forward substitution: the quad of lanes 4j..4j+3
         // owns column j; lane q of the quad sums the terms s = q (mod 4), a
         // quad butterfly completes each row, and lane r & 3 keeps t_r.
@@ -308,22 +379,60 @@ __device__ __forceinline__ void prep_blocks(Smem &sm, int p, int lane) {
     } else {
 #pragma unroll
         for (int tsk = 0; tsk < 3; ++tsk) {
-            const int o = 3 * (p - 4) + tsk;  // 0..11
+            const int o = 3 * (p - 4) + tsk;  // 0..11: six Gram blocks, then six query-key blocks
             const int oo = o % 6;
             const bool gram = o < 6;
             const int bi = oo < 1 ? 1 : (oo < 3 ? 2 : 3);
             const int bj = oo < 1 ? 0 : (oo < 3 ? oo - 1 : oo - 3);
-            const floatx4 acc = block_product(gram ? sm.kp : sm.qp, sm.km, bi, bj, lane);
+            const floatx4 acc = block_product_t(gram ? sm.kp : sm.qp, sm.km, bi, bj, lane);
+            const float sc = gram ? sm.beta[16 * bi + l16] : 1.f;
+            half4 hv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * bi + 4 * lg + i, s = 16 * bj + l16;
-                if (gram)
-                    sm.a16[r * P4 + s] = (_Float16)(sm.beta[r] * acc[i]);
-                else
-                    sm.p[r * P4 + s] = (_Float16)acc[i];
-            }
+            for (int i = 0; i < 4; ++i) hv[i] = (_Float16)(sc * acc[i]);
+            _Float16 *dst = gram ? sm.a16 : sm.p;
+            *reinterpret_cast<half4 *>(&dst[(16 * bi + l16) * P4 + 16 * bj + 4 * lg]) = hv;
         }
     }
+}
+
+// The packed sequence of rank rho when sequences are ordered by length,
+// longest first (ties in index order): every thread of the workgroup takes
+// part (two workgroup barriers); scratch holds SORT_MAX + 1 ints of LDS.
+constexpr int SORT_MAX = 256;
+__device__ __forceinline__ int sequence_of_rank(const int32_t *cu, int N, int totalT, int rho,
+                                             int *scratch) {
+    const int t = threadIdx.x;
+    for (int m = t; m < N; m += NT) {
+        int a, e;
+        seq_bounds(cu, m, 0, totalT, a, e);
+        scratch[m] = e - a;
+    }
+    __syncthreads();
+    if (t < N) {
+        const int len = scratch[t];
+        int rank = 0;
+        for (int m = 0; m < N; ++m) {
+            const int lm = scratch[m];
+            rank += (lm > len || (lm == len && m < t)) ? 1 : 0;
+        }
+        if (rank == rho) scratch[SORT_MAX] = t;
+    }
+    __syncthreads();
+    return scratch[SORT_MAX];
+}
+
+template <typename TOut>
+__device__ __forceinline__ void store4(TOut *dst, floatx4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float *dst, floatx4 v) {
+    *reinterpret_cast<floatx4 *>(dst) = v;
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t *dst, floatx4 v) {
+    uint2 w;
+    w.x = (uint32_t)from_f32_bf16(v[0]).bits | ((uint32_t)from_f32_bf16(v[1]).bits << 16);
+    w.y = (uint32_t)from_f32_bf16(v[2]).bits | ((uint32_t)from_f32_bf16(v[3]).bits << 16);
+    *reinterpret_cast<uint2 *>(dst) = w;
 }
 
 template <typename TOut, int PM>
@@ -340,9 +449,14 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
     const int b = blockIdx.x;
     const int xcd = b & 7, slot = b >> 3;
     const int vt = slot & 1;
-    const int unit = (slot >> 1) * 8 + xcd;
+    const int unit = (slot >> 1) * 8 + xcd;  // position in the work order
     if (unit >= N * H) return;
-    const int n = unit / H, h = unit % H;
+    const int h = unit % H;
+    // Packed sequences run longest first: workgroups are dispatched in
+    // order, so the longest chains start earliest and the short ones fill in
+    int n = unit / H;
+    if (cu && N > 1 && N <= SORT_MAX)
+        n = sequence_of_rank(cu, N, totalT, n, reinterpret_cast<int *>(sm.kp));
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -367,81 +481,123 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 S[cb][i] = s0p ? s0p[(16 * cb + 4 * lg + i) * VD + col] : 0.f;
-        _Float16 *st = sm.st[w];
-        _Float16 *ut = sm.ut[w];
+        // the initial state has landed before the loop, so the loop's waits
+        // never cover the previous chunk's output stores
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
         __syncthreads();
         for (int ci = 0; ci < nchunks; ++ci) {
             const int c0 = bos + ci * C;
             const int L = min(C, eos - c0);
             const int par = ci & 1;
-            floatx4 Y[4], O[4];
-            // ---- phase A: S' = Diag(exp(G_m)) S (kept in S, written transposed),
-            // the inter-chunk products Kp S' and Qp S', and beta (V - Kp S')
+
+            // straight from the accumulators, the inter-chunk products Kp S'
+            // and Qp S', and Y = Diag(beta) (V - Kp S')
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) {
                 const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.fm[par][16 * cb + 4 * lg]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[cb][i] *= f[i];
-                *reinterpret_cast<half4 *>(&st[l16 * PK + 16 * cb + 4 * lg]) = to_half4(S[cb]);
             }
             half8 bs[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) bs[ks] = frag8(st, PK, 0, 32 * ks, lane);
+            for (int ks = 0; ks < 4; ++ks) bs[ks] = cat8(to_half4(S[2 * ks]), to_half4(S[2 * ks + 1]));
+            // the four row blocks advance together (eight independent
+            // accumulation chains); each fragment register is refilled with the
+            // next k-step's fragment as soon as its product has issued.  The
+            // output is accumulated transposed, O^T = S'^T Qp^T (the same
+            // fragments with the operand roles swapped), so that a lane ends
+            // with four consecutive columns of one output row
+            floatx4 X[4], O[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) X[rb] = O[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            half8 fk[4], fq[4];
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-                floatx4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+                fk[rb] = frag8(sm.kp, PK, 16 * rb, 0, lane);
+                fq[rb] = frag8(sm.qp, PK, 16 * rb, 0, lane);
+            }
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    x = mma32(frag8(sm.kp, PK, 16 * rb, 32 * ks, lane), bs[ks], x);
-                    y = mma32(frag8(sm.qp, PK, 16 * rb, 32 * ks, lane), bs[ks], y);
-                }
-                O[rb] = y;
+            for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * rb + 4 * lg + i;
-                    const float vv = __uint_as_float((uint32_t)sm.v[r * PC + 16 * w + l16] << 16);
-                    Y[rb][i] = sm.beta[r] * (vv - x[i]);
+                for (int rb = 0; rb < 4; ++rb) {
+                    X[rb] = mma32(fk[rb], bs[ks], X[rb]);
+                    if (ks < 3) fk[rb] = frag8(sm.kp, PK, 16 * rb, 32 * (ks + 1), lane);
+                    O[rb] = mma32(bs[ks], fq[rb], O[rb]);
+                    if (ks < 3) fq[rb] = frag8(sm.qp, PK, 16 * rb, 32 * (ks + 1), lane);
                 }
+            }
+            floatx4 Y[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const uint2 vv = *reinterpret_cast<const uint2 *>(&sm.vt[(16 * w + l16) * PV + 16 * rb + 4 * lg]);
+                const floatx4 bb = *reinterpret_cast<const floatx4 *>(&sm.beta[16 * rb + 4 * lg]);
+                Y[rb][0] = bb[0] * (bf16lo(vv.x) - X[rb][0]);
+                Y[rb][1] = bb[1] * (bf16hi(vv.x) - X[rb][1]);
+                Y[rb][2] = bb[2] * (bf16lo(vv.y) - X[rb][2]);
+                Y[rb][3] = bb[3] * (bf16hi(vv.y) - X[rb][3]);
             }
             __syncthreads();
             // ---- phase B: (I + A) U = Y by 16-row blocks,
-            // U_i = T_ii (Y_i - sum_{j<i} A_ij U_j), all in registers
+            // U_i = T_ii (Y_i - sum_{j<i} A_ij U_j), all in registers; the
+            // fragments of A, of the inverses and of the first half of Km^T are
+            // loaded before the substitution starts
+            half4 Aij[6], Tii[4];
+#pragma unroll
+            for (int i = 1, x = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < i; ++j, ++x) Aij[x] = frag4(sm.a16, P4, 16 * i, 16 * j, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Tii[i] = frag4(sm.tii[i], PI, 0, 0, lane);
+            half8 km[8];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                km[2 * cb] = frag8_kmt(sm.kmt[par], 16 * cb, 0, lane);
+                km[2 * cb + 1] = frag8_kmt(sm.kmt[par], 16 * cb, 1, lane);
+            }
             half4 U[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0, x = 0; i < 4; ++i) {
                 floatx4 z = Y[i];
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (i > 0) {
+                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < i; ++j) acc = mma16(frag4(sm.a16, P4, 16 * i, 16 * j, lane), U[j], acc);
+                    for (int j = 0; j < i; ++j, ++x) acc = mma16(Aij[x], U[j], acc);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) z[e] -= acc[e];
-                const floatx4 u = mma16(frag4(sm.tii[i], PI, 0, 0, lane), to_half4(z),
-                                        floatx4{0.f, 0.f, 0.f, 0.f});
-                U[i] = to_half4(u);
-                *reinterpret_cast<half4 *>(&ut[l16 * PC + 16 * i + 4 * lg]) = U[i];
+                    for (int e = 0; e < 4; ++e) z[e] -= acc[e];
+                }
+                U[i] = to_half4(mma16(Tii[i], to_half4(z), floatx4{0.f, 0.f, 0.f, 0.f}));
             }
-            // O = Qp S' + P U, stored for the valid rows
+            // S = Diag(exp(G_C - G_m)) (S' + Km^T U), U as B fragments straight
+            // from the accumulators (the Km^T fragment registers refilled with
+            // the second half's as they issue); O^T += U^T P^T
+            const half8 bu0 = cat8(U[0], U[1]), bu1 = cat8(U[2], U[3]);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                S[cb] = mma32(km[2 * cb], bu0, S[cb]);
+                km[2 * cb] = frag8_kmt(sm.kmt[par], 16 * (cb + 4), 0, lane);
+                S[cb] = mma32(km[2 * cb + 1], bu1, S[cb]);
+                km[2 * cb + 1] = frag8_kmt(sm.kmt[par], 16 * (cb + 4), 1, lane);
+            }
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int i = 0; i <= rb; ++i) O[rb] = mma16(U[i], frag4(sm.p, P4, 16 * rb, 16 * i, lane), O[rb]);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                S[cb + 4] = mma32(km[2 * cb], bu0, S[cb + 4]);
+                S[cb + 4] = mma32(km[2 * cb + 1], bu1, S[cb + 4]);
+            }
+            // O^T blocks: a lane holds chunk row 16 rb + l16, value columns
+            // 4 lg .. 4 lg + 3 (one 16-byte store)
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-                for (int i = 0; i <= rb; ++i) O[rb] = mma16(frag4(sm.p, P4, 16 * rb, 16 * i, lane), U[i], O[rb]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * rb + 4 * lg + e;
-                    if (r < L)
-                        o[((size_t)(c0 + r) * H + h) * VD + vt * VT + 16 * w + l16] = from_f32<TOut>(O[rb][e]);
-                }
+                const int r = 16 * rb + l16;
+                if (r < L)
+                    store4<TOut>(o + ((size_t)(c0 + r) * H + h) * VD + vt * VT + 16 * w + 4 * lg, O[rb]);
             }
-            // S = Diag(exp(G_C - G_m)) (S' + Km^T U)
-            half8 bu[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) bu[ks] = frag8(ut, PC, 0, 32 * ks, lane);
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    S[cb] = mma32(frag8_kmt(sm.kmt[par], 16 * cb, ks, lane), bu[ks], S[cb]);
                 const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.fc[par][16 * cb + 4 * lg]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[cb][i] *= f[i];
@@ -477,37 +633,40 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
         Raw R;
         uint4 rg[2];
         float lc[2][8], ex[8];
+        // chunk i of the sequence, clamped to the last one (a chunk past the
+        // end is loaded as the last one again and never used)
+        const int last = nchunks > 0 ? nchunks - 1 : 0;
+        auto cstart = [&](int i) { return bos + min(i, last) * C; };
+        auto clen = [&](int i) { return min(C, eos - cstart(i)); };
+        // Pipeline: in the iteration that handles chunk ci, the prep waves form
+        // chunk ci's Gram / query-key blocks (phase A), then chunk ci + 1's
+        // operands and chunk ci + 2's decay sums (phase B), and issue the loads
+        // of chunk ci + 2's inputs and chunk ci + 3's gates, which are used one
+        // iteration later.
         if (nchunks > 0) {
-            load_g(rg, g, bos, min(C, eos - bos), H, h, p, lane, gpad);
-            load_raw(R, q, k, v, beta, bos, min(C, eos - bos), H, h, vt, p, lane, bpad);
-            scan_partials<PM>(sm, rg, p, lane, lc, ex, pro);
-            if (nchunks > 1) load_g(rg, g, bos + C, min(C, eos - bos - C), H, h, p, lane, gpad);
+            load_g(rg, g, cstart(0), clen(0), H, h, p, lane);
+            load_raw(R, q, k, v, beta, cstart(0), clen(0), H, h, vt, p, lane);
+            scan_partials<PM>(sm, rg, clen(0), gpad, 0, p, lane, lc, ex, pro);
+            load_g(rg, g, cstart(1), clen(1), H, h, p, lane);
         }
         __syncthreads();
         if (nchunks > 0) {
-            build_operands<PM>(sm, R, 0, p, lane, lc, ex, pro);
-            if (nchunks > 1)
-                load_raw(R, q, k, v, beta, bos + C, min(C, eos - bos - C), H, h, vt, p, lane, bpad);
+            build_operands<PM>(sm, R, bpad, 0, p, lane, lc, ex, pro);
+            if (nchunks > 1) scan_partials<PM>(sm, rg, clen(1), gpad, 1, p, lane, lc, ex, pro);
+            load_raw(R, q, k, v, beta, cstart(1), clen(1), H, h, vt, p, lane);
+            load_g(rg, g, cstart(2), clen(2), H, h, p, lane);
         }
         __syncthreads();
         for (int ci = 0; ci < nchunks; ++ci) {
-            const bool next = ci + 1 < nchunks, next2 = ci + 2 < nchunks;
-            const int c2 = bos + (ci + 2) * C;
-            // ---- phase A: the next chunk's per-wave decay sums (then fetch g
-            // two chunks ahead), and this chunk's Gram / query-key blocks and
-            // diagonal inverses
-            if (next) {
-                scan_partials<PM>(sm, rg, p, lane, lc, ex, pro);
-                if (next2) load_g(rg, g, c2, min(C, eos - c2), H, h, p, lane, gpad);
-            }
+            // ---- phase A: this chunk's Gram / query-key blocks and diagonal inverses
             prep_blocks(sm, p, lane);
             __syncthreads();
-            // ---- phase B: operands of the next chunk; then fetch the rest of
-            // the chunk after it
-            if (next) {
-                build_operands<PM>(sm, R, (ci & 1) ^ 1, p, lane, lc, ex, pro);
-                if (next2) load_raw(R, q, k, v, beta, c2, min(C, eos - c2), H, h, vt, p, lane, bpad);
-            }
+            // ---- phase B: the next chunk's operands, the decay sums of the
+            // chunk after it, and the loads for the iteration after this one
+            if (ci + 1 < nchunks) build_operands<PM>(sm, R, bpad, (ci & 1) ^ 1, p, lane, lc, ex, pro);
+            if (ci + 2 < nchunks) scan_partials<PM>(sm, rg, clen(ci + 2), gpad, ci & 1, p, lane, lc, ex, pro);
+            load_raw(R, q, k, v, beta, cstart(ci + 2), clen(ci + 2), H, h, vt, p, lane);
+            load_g(rg, g, cstart(ci + 3), clen(ci + 3), H, h, p, lane);
             __syncthreads();
         }
     }

@@ -226,3 +226,29 @@ def test_varlen_many_sequences_two_pass():
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
     for n in (0, 63, 64, 65, 99):
         assert torch.equal(sT[n], x["s0"][n])
+
+
+@pytest.mark.parametrize("N", [200, 300])
+def test_varlen_many_sequences_fused(N):
+    """Packed sequences on the single-pass kernel: up to 256 sequences run
+    longest first (ranked inside the kernel, ties in index order), more than
+    that in sequence order; lengths include repeats, zeros and one long
+    sequence."""
+    rng = np.random.default_rng(33 + N)
+    lengths = rng.integers(1, 150, size=N)
+    lengths[[0, 5, N - 1]] = 0
+    lengths[[1, 2, 3]] = 77          # ties
+    lengths[N // 2] = 1000           # one long sequence
+    print(f"[case] varlen fused N={N} total={int(lengths.sum())}", flush=True)
+    d = inputs.draw_varlen(33 + N, H=2, K=128, V=128, dtype="bf16", lengths=lengths, s0_std=0.1)
+    o_ref, s_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                     d["cu_seqlens"].numpy(), oracle.as_f64(d["s0"]))
+    x = to_gpu(d)
+    o, sT = kda.varlen_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"], x["s0"],
+                           two_pass=False)
+    torch.cuda.synchronize()
+    eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+    report(f"varlen_many_fused_N{N}", o=eo, sT=es)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    for n in (0, 5, N - 1):
+        assert torch.equal(sT[n], x["s0"][n])
