@@ -110,6 +110,8 @@ def measured_traffic(stem):
 
 
 def time_launches(fn, steps, warmup, stream):
+    """Mean ms per call of `steps` back-to-back calls after `warmup` calls (one
+    event pair around the loop: the warm, pipelined rate)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -126,25 +128,81 @@ def time_launches(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps, wall
 
 
-def cpu_baseline(d, w, wall_budget_s=2.5):
-    """fp64 oracle over the whole prefill workload (all heads), repeated until
-    about wall_budget_s of wall time (at most 20 passes); input conversion is
-    outside the timing."""
+class CacheFlush:
+    """Writes a 512 MiB buffer (twice the 256 MB Infinity Cache) between timed
+    calls, so that each call starts with its inputs in HBM only."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(self.i & 0xFF)
+
+
+def time_calls(fn, steps, warmup, stream, flush=None):
+    """Each of `steps` calls timed by its own HIP event pair on `stream` (the
+    stream the kernels run on), after `warmup` untimed calls; with `flush`, the
+    cache is flushed before every call, outside its events.  Returns per-call
+    statistics in ms and the wall time of the timed region."""
+    import torch
+    for _ in range(warmup):
+        if flush:
+            flush()
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        if flush:
+            flush()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"median_ms": ms[len(ms) // 2] if len(ms) % 2 else 0.5 * (ms[len(ms) // 2 - 1] + ms[len(ms) // 2]),
+            "min_ms": ms[0], "mean_ms": sum(ms) / len(ms), "max_ms": ms[-1],
+            "cold": flush is not None, "wall_s": wall}
+
+
+def settle_clock(stream, fills=1000):
+    """Keep the GPU busy for ~50 ms (1000 writes of 256 MiB) so that it reaches
+    its steady clock before anything is timed (the first ~50 short calls
+    otherwise run slower)."""
+    import torch
+    buf = torch.empty(256 << 20, dtype=torch.uint8, device=stream.device)
+    for i in range(fills):
+        buf.fill_(i & 0xFF)
+    torch.cuda.synchronize()
+
+
+def cpu_baseline(d, cu, H, what, max_passes=3, wall_budget_s=8.0):
+    """fp64 oracle over the whole packed workload d (all (sequence, head)
+    units), repeated while the wall budget lasts (at most max_passes); input
+    conversion is outside the timing."""
     from oracle import oracle
     q, k, v, g, beta = (oracle.as_f64(d[x]) for x in ("q", "k", "v", "g", "beta"))
+    s0 = oracle.as_f64(d["s0"]) if d.get("s0") is not None else None
     threads = oracle.host_threads()
-    used = min(threads, w.B * w.H)
+    units = (len(cu) - 1) * H
+    used = min(threads, units)
     times = []
-    while len(times) < 20 and sum(times) < wall_budget_s:
+    while len(times) < max_passes and sum(times) < wall_budget_s:
         t0 = time.perf_counter()
-        oracle.fixed(q, k, v, g, beta, nthreads=used)
+        oracle.recurrence(q, k, v, g, beta, cu, s0, nthreads=used)
         times.append(time.perf_counter() - t0)
     dt = sum(times) / len(times)
-    return {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"whole prefill workload B={w.B} H={w.H} T={w.T} ({len(times)} passes, "
-                      f"mean {dt:.3f} s wall each, ~{sum(times) * used:.0f} core-s in total), "
-                      f"parallel over the {w.B * w.H} (sequence, head) units; "
-                      f"{threads} host threads available"}
+    tokens = int(cu[-1])
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{what}: the whole workload, {tokens} tokens x {H} heads ({len(times)} "
+                      f"pass(es), mean {dt:.2f} s wall each, ~{sum(times) * used:.0f} core-s in "
+                      f"total), parallel over its {units} (sequence, head) units; {threads} "
+                      f"host threads available"}
 
 
 def decode_leg(args, dev, stream):
@@ -235,19 +293,205 @@ def decode_leg(args, dev, stream):
     }
 
 
+def _tag(name):
+    """Profile-file tag of a workload name."""
+    return (name.replace("prefill_bf16_", "prefill_").replace("batched_bf16_", "batched_")
+            .replace("varlen_bf16_", "varlen_"))
+
+
+def load_prefill(w, dev):
+    """The workload's inputs on the GPU, as a packed call: flat [tokens, H, *]
+    tensors and cu_seqlens (fixed-length batches are run through their own
+    entry point, kda_chunk_fwd, with [B, T, H, *] views)."""
+    import torch
+    from gated_delta_rule_43_amd import inputs
+    if w.kind == "varlen":
+        d = inputs.draw_varlen(w.seed, w.H, w.K, w.V, w.dtype, N=w.N, len_min=w.len_min,
+                               len_max=w.len_max, s0_std=w.s0_std)
+        cu = d["cu_seqlens"].numpy().astype("int64")
+    else:
+        d = inputs.draw_fixed(w.seed, w.B, w.T, w.H, w.K, w.V, w.dtype, s0_std=w.s0_std)
+        for key in ("q", "k", "v", "g", "beta"):
+            d[key] = d[key].reshape(w.B * w.T, *d[key].shape[2:])
+        import numpy as np
+        cu = np.arange(w.B + 1, dtype="int64") * w.T
+    x = {key: (val.to(dev) if isinstance(val, torch.Tensor) else val) for key, val in d.items()}
+    x["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=dev)
+    return d, x, cu
+
+
+def prefill_call(w, x, cu, dev):
+    """The benchmarked call: the library's recommended implementation for the
+    workload (kda_workspace_bytes), outputs preallocated."""
+    import torch
+    from gated_delta_rule_43_amd import kda
+    N, tokens = len(cu) - 1, int(cu[-1])
+    o = torch.empty(tokens, w.H, w.V, device=dev)
+    sT = torch.empty(N, w.H, w.K, w.V, device=dev)
+    nws = kda.workspace_bytes(N, tokens, w.H, w.K, w.V, w.chunk)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    if w.kind == "varlen":
+        def fn():
+            kda.varlen_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"], x["s0"],
+                           chunk=w.chunk, final_state=sT, out=o, workspace=ws)
+    else:
+        v4 = {key: x[key].view(w.B, w.T, *x[key].shape[1:]) for key in ("q", "k", "v", "g", "beta")}
+        o4 = o.view(w.B, w.T, w.H, w.V)
+
+        def fn():
+            kda.chunk_fwd(v4["q"], v4["k"], v4["v"], v4["g"], v4["beta"], x["s0"], chunk=w.chunk,
+                          final_state=sT, out=o4, workspace=ws)
+    kernels = ("chunk_prep_kernel + chunk_state_kernel + chunk_output_kernel" if nws
+               else "chunk_mfma_kernel")
+    return fn, ("two-pass" if nws else "fused single-pass"), kernels, (o, sT, ws)
+
+
+def prefill_leg(w, args, dev, stream, flush, steps, warmup):
+    """Cold per-call timing (median, min) with the cache flushed between calls,
+    and the warm back-to-back rate, of one prefill workload; roofline of the
+    call against HBM (algorithmic bytes) and the MFMA peak (algorithmic flops)."""
+    d, x, cu = load_prefill(w, dev)
+    fn, path, kernels, _bufs = prefill_call(w, x, cu, dev)
+    cold = time_calls(fn, steps, warmup, stream, flush=flush)
+    warm_ms, _ = time_launches(fn, steps, 2, stream)
+    N, tokens = len(cu) - 1, int(cu[-1])
+    ms = cold["median_ms"]
+    alg_b = prefill_alg_bytes(1, tokens, w.H, w.K, w.V, s0=w.s0_std is not None, sT=True)
+    alg_b += (N - 1) * w.H * w.K * w.V * 4 * (int(w.s0_std is not None) + 1)
+    alg_f = prefill_alg_flops(1, tokens, w.H, w.K, w.V, w.chunk)
+    achieved = alg_b / (ms * 1e-3) / 1e9
+    stem = ("kda_chunk_fwd_two_pass_" if path == "two-pass" else "chunk_mfma_kernel_") + _tag(w.name)
+    leg = {
+        "workload": w.name, "tokens": tokens, "sequences": N, "heads": w.H,
+        "value": tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+        "timing": {**cold, "warm_mean_ms": warm_ms,
+                   "flush": "512 MiB written between timed calls (cold); warm = back-to-back loop"},
+        "path": path,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(stem),
+                     "kernel": f"kda_{'varlen' if w.kind == 'varlen' else 'chunk'}_fwd {path}: {kernels}",
+                     "alg_bytes_per_launch": alg_b},
+        "roofline_mfma": {"achieved": alg_f / (ms * 1e-3) / 1e12, "peak": MFMA_F16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s",
+                          "frac": alg_f / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                          "flops": "algorithmic", "alg_flops_per_launch": alg_f},
+    }
+    return leg, d, cu
+
+
+def next_legs(args, dev, stream):
+    """Prefix-cache snapshots, the fused input prologue and the backward pass,
+    on the 8-head prefill workload (B=1, H=8, T=4096)."""
+    import torch
+    from gated_delta_rule_43_amd import inputs, kda
+    w = inputs.WORKLOADS[PREFILL]
+    d = inputs.draw_fixed(w.seed, w.B, w.T, w.H, w.K, w.V, w.dtype, s0_std=w.s0_std)
+    x = {key: (val.to(dev) if val is not None else None) for key, val in d.items()}
+    o = torch.empty(w.B, w.T, w.H, w.V, device=dev)
+    sT = torch.empty(w.B, w.H, w.K, w.V, device=dev)
+    nws = kda.workspace_bytes(w.B, w.B * w.T, w.H, w.K, w.V, w.chunk)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    steps = max(10, args.steps)
+
+    # the same call through the paged entry point, leaving a state snapshot
+    # every 512 tokens (prefix caching: one 6144-token page per sequence)
+    snap, page = 512, 6144
+    per_page = page // snap
+    pages = -(-w.T // page)
+    pool = torch.zeros(w.B * pages * per_page + w.B, w.H, w.K, w.V, device=dev)
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)
+    table = i32([[b * pages + j for j in range(pages)] for b in range(w.B)])
+    sT_slot = i32([w.B * pages * per_page + b for b in range(w.B)])
+    cu = i32([b * w.T for b in range(w.B + 1)])
+    flat = {key: x[key].reshape(w.B * w.T, *x[key].shape[2:]) for key in ("q", "k", "v", "g", "beta")}
+    o_flat = o.view(w.B * w.T, w.H, w.V)
+
+    def step_plain():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], chunk=w.chunk,
+                      final_state=sT, out=o, workspace=ws)
+
+    def step_snap():
+        kda.varlen_fwd_paged(flat["q"], flat["k"], flat["v"], flat["g"], flat["beta"], cu, pool,
+                             sT_slot=sT_slot, block_table=table, snap_tokens=snap,
+                             page_tokens=page, chunk=w.chunk, out=o_flat,
+                             workspace=ws if nws else None, two_pass=bool(nws))
+
+    ms_plain, _ = time_launches(step_plain, steps, 20, stream)
+    ms_snap, _ = time_launches(step_snap, steps, 20, stream)
+
+    # raw projections (unnormalised q and k, gate logits, beta logits): the maps
+    # run inside the kernels' loads (kda_chunk_fwd_prologue), against running
+    # them first as separate elementwise passes in torch and then the plain call
+    r = inputs.draw_raw_fixed(w.seed + 100, w.B, w.T, w.H, w.K, w.V, w.dtype, s0_std=w.s0_std)
+    xr = {key: (val.to(dev) if val is not None else None) for key, val in r.items()}
+    pro = kda.Prologue(normalize_qk=True, gate_lower_bound=0.25, beta_logits=True, norm_eps=1e-6)
+
+    def step_pro():
+        kda.chunk_fwd(xr["q"], xr["k"], xr["v"], xr["g"], xr["beta"], xr["s0"], chunk=w.chunk,
+                      final_state=sT, out=o, workspace=ws, prologue=pro)
+
+    def step_torch_prologue():
+        def unit(t):
+            t32 = t.float()
+            return (t32 * torch.rsqrt((t32 * t32).sum(-1, keepdim=True) + 1e-6)).to(t.dtype)
+        gq, gk = unit(xr["q"]), unit(xr["k"])
+        gg = (-0.25 * torch.sigmoid(xr["g"].float())).to(xr["g"].dtype)
+        gb = torch.sigmoid(xr["beta"].float()).to(xr["beta"].dtype)
+        kda.chunk_fwd(gq, gk, xr["v"], gg, gb, xr["s0"], chunk=w.chunk, final_state=sT, out=o,
+                      workspace=ws)
+
+    ms_pro, _ = time_launches(step_pro, steps, 20, stream)
+    ms_torch_pro, _ = time_launches(step_torch_prologue, steps, 20, stream)
+
+    # backward of the same call (kda_chunk_bwd): gradients of every input for
+    # a given do and dsT, workspace preallocated
+    do = torch.randn(w.B, w.T, w.H, w.V, device=dev, generator=torch.Generator(dev).manual_seed(7))
+    dsT = torch.randn(w.B, w.H, w.K, w.V, device=dev, generator=torch.Generator(dev).manual_seed(8))
+    bws = torch.empty(kda.bwd_workspace_bytes(w.B, w.B * w.T, w.H, w.K, w.V, w.chunk),
+                      dtype=torch.uint8, device=dev)
+
+    def step_bwd():
+        kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, initial_state=x["s0"],
+                      dsT=dsT, chunk=w.chunk, workspace=bws)
+
+    ms_bwd, _ = time_launches(step_bwd, max(5, steps // 5), 3, stream)
+    bwd_b = bwd_alg_bytes(w.B, w.T, w.H, w.K, w.V)
+    tokens = w.B * w.T
+    return {
+        "prefix_cache": {"workload": w.name, "ms_per_step_plain": ms_plain,
+                         "ms_per_step_with_snapshots": ms_snap, "snap_tokens": snap,
+                         "page_tokens": page, "snapshots_per_call": w.B * w.H * (w.T // snap)},
+        "prologue": {"workload": w.name, "ms_per_step_fused_maps": ms_pro,
+                     "ms_per_step_torch_maps_then_plain_call": ms_torch_pro,
+                     "maps": "q, k L2-normalised (eps 1e-6); g = -0.25 sigmoid(gate logits); "
+                             "beta = sigmoid(beta logits)"},
+        "backward": {"workload": w.name, "ms_per_step": ms_bwd,
+                     "tokens_per_s": tokens / (ms_bwd * 1e-3),
+                     "kernels": "bwd_prep_kernel + bwd_trans_mfma_kernel + bwd_chain_mfma_kernel "
+                                "(both chains) + bwd_udy_mfma_kernel + bwd_kgrad_mfma_kernel "
+                                "(fp32, MFMA at d = 128)",
+                     "alg_bytes_per_call": bwd_b,
+                     "achieved_GBps": bwd_b / (ms_bwd * 1e-3) / 1e9,
+                     "hbm_frac": bwd_b / (ms_bwd * 1e-3) / 1e9 / HBM_PEAK_GBS},
+    }
+
+
+PREFILL_WORKLOADS = ["varlen_bf16_N64_H16", "batched_bf16_B4_H32_T8192", "prefill_bf16_B1_H8_T4096"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # the GPU reaches its steady clock after ~100 prefill calls (~7 ms)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--prefill-workload", default=PREFILL,
-                    choices=["prefill_bf16_B1_H8_T4096", "batched_bf16_B4_H32_T8192"])
+    ap.add_argument("--no-legs", action="store_true",
+                    help="time the headline workload (and decode) only")
+    ap.add_argument("--prefill-workload", default=PREFILL_WORKLOADS[0], choices=PREFILL_WORKLOADS)
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward"], default=None,
-                    help="profiling mode: launch only this kernel --steps times and print "
+                    help="profiling mode: launch only this call --steps times and print "
                          "nothing else (copy = a 512 MiB device copy for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -275,162 +519,72 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"only": "copy", "bytes_per_copy": src.numel()}), flush=True)
         return
-
     if args.only == "decode":
         print(json.dumps(decode_leg(args, dev, stream)), flush=True)
         return
-
-    # ---- prefill: the step
-    w = inputs.WORKLOADS[args.prefill_workload]
-    d = inputs.draw_fixed(w.seed, w.B, w.T, w.H, w.K, w.V, w.dtype, s0_std=w.s0_std)
-    x = {key: (val.to(dev) if val is not None else None) for key, val in d.items()}
-    o = torch.empty(w.B, w.T, w.H, w.V, device=dev)
-    sT = torch.empty(w.B, w.H, w.K, w.V, device=dev)
-    nws = kda.workspace_bytes(w.B, w.B * w.T, w.H, w.K, w.V, w.chunk)
-    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
-    path = "two-pass" if nws else "fused single-pass"
-    kernels = ("chunk_prep_kernel + chunk_state_kernel + chunk_output_kernel" if nws
-               else "chunk_mfma_kernel")
-
-    def step():
-        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], chunk=w.chunk,
-                      final_state=sT, out=o, workspace=ws)
-
-    def step_fused():
-        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], chunk=w.chunk,
-                      final_state=sT, out=o, two_pass=False)
-
+    if args.only == "prefill":
+        w = inputs.WORKLOADS[args.prefill_workload]
+        d, x, cu = load_prefill(w, dev)
+        fn, path, kernels, _bufs = prefill_call(w, x, cu, dev)
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "prefill", "workload": w.name, "path": path,
+                          "kernels": kernels, "launches": args.steps}), flush=True)
+        return
     if args.only == "backward":
+        w = inputs.WORKLOADS[PREFILL]
+        d = inputs.draw_fixed(w.seed, w.B, w.T, w.H, w.K, w.V, w.dtype)
+        x = {key: (val.to(dev) if val is not None else None) for key, val in d.items()}
         do = torch.randn(w.B, w.T, w.H, w.V, device=dev)
         for _ in range(args.steps):
-            kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, initial_state=x["s0"],
-                          chunk=w.chunk)
+            kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, chunk=w.chunk)
         torch.cuda.synchronize()
         print(json.dumps({"only": "backward", "workload": w.name, "launches": args.steps}),
               flush=True)
         return
-    if args.only == "prefill":
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        print(json.dumps({"only": "prefill", "workload": w.name, "launches": args.steps}),
-              flush=True)
-        return
 
-    ms, wall = time_launches(step, args.steps, args.warmup, stream)
-    ms_fused, _ = time_launches(step_fused, max(5, args.steps // 5), 2, stream) if nws else (ms, 0)
-
-    # the same step through the paged entry point, leaving a state snapshot
-    # every 512 tokens (prefix caching: one 6144-token page per sequence)
-    snap, page = 512, 6144
-    per_page = page // snap
-    pages = -(-w.T // page)
-    pool = torch.zeros(w.B * pages * per_page + w.B, w.H, w.K, w.V, device=dev)
-    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)
-    table = i32([[b * pages + j for j in range(pages)] for b in range(w.B)])
-    sT_slot = i32([w.B * pages * per_page + b for b in range(w.B)])
-    cu = i32([b * w.T for b in range(w.B + 1)])
-    flat = {key: x[key].reshape(w.B * w.T, *x[key].shape[2:]) for key in ("q", "k", "v", "g", "beta")}
-    o_flat = o.view(w.B * w.T, w.H, w.V)
-    nws_p = kda.workspace_bytes(w.B, w.B * w.T, w.H, w.K, w.V, w.chunk)
-
-    def step_snap():
-        kda.varlen_fwd_paged(flat["q"], flat["k"], flat["v"], flat["g"], flat["beta"], cu, pool,
-                             sT_slot=sT_slot, block_table=table, snap_tokens=snap,
-                             page_tokens=page, chunk=w.chunk, out=o_flat,
-                             workspace=ws if nws_p else None, two_pass=bool(nws_p))
-
-    ms_snap, _ = time_launches(step_snap, args.steps, 20, stream)
-
-    # the same step from raw projections (unnormalised q and k, gate logits,
-    # beta logits): the maps run inside the kernels' loads
-    # (kda_chunk_fwd_prologue), against a model-side version that first runs
-    # them as separate elementwise passes in torch and then makes the plain call
-    r = inputs.draw_raw_fixed(w.seed + 100, w.B, w.T, w.H, w.K, w.V, w.dtype, s0_std=w.s0_std)
-    xr = {key: (val.to(dev) if val is not None else None) for key, val in r.items()}
-    pro = kda.Prologue(normalize_qk=True, gate_lower_bound=0.25, beta_logits=True, norm_eps=1e-6)
-
-    def step_pro():
-        kda.chunk_fwd(xr["q"], xr["k"], xr["v"], xr["g"], xr["beta"], xr["s0"], chunk=w.chunk,
-                      final_state=sT, out=o, workspace=ws, prologue=pro)
-
-    def step_torch_prologue():
-        def unit(t):
-            t32 = t.float()
-            return (t32 * torch.rsqrt((t32 * t32).sum(-1, keepdim=True) + 1e-6)).to(t.dtype)
-        gq, gk = unit(xr["q"]), unit(xr["k"])
-        gg = (-0.25 * torch.sigmoid(xr["g"].float())).to(xr["g"].dtype)
-        gb = torch.sigmoid(xr["beta"].float()).to(xr["beta"].dtype)
-        kda.chunk_fwd(gq, gk, xr["v"], gg, gb, xr["s0"], chunk=w.chunk, final_state=sT, out=o,
-                      workspace=ws)
-
-    ms_pro, _ = time_launches(step_pro, args.steps, 20, stream)
-    ms_torch_pro, _ = time_launches(step_torch_prologue, args.steps, 20, stream)
-
-    # backward of the same step (kda_chunk_bwd): gradients of every input for
-    # a given do and dsT, workspace preallocated
-    do = torch.randn(w.B, w.T, w.H, w.V, device=dev, generator=torch.Generator(dev).manual_seed(7))
-    dsT = torch.randn(w.B, w.H, w.K, w.V, device=dev, generator=torch.Generator(dev).manual_seed(8))
-    bws = torch.empty(kda.bwd_workspace_bytes(w.B, w.B * w.T, w.H, w.K, w.V, w.chunk),
-                      dtype=torch.uint8, device=dev)
-
-    def step_bwd():
-        kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, initial_state=x["s0"],
-                      dsT=dsT, chunk=w.chunk, workspace=bws)
-
-    ms_bwd, _ = time_launches(step_bwd, max(5, args.steps // 5), 3, stream)
-    bwd_b = bwd_alg_bytes(w.B, w.T, w.H, w.K, w.V)
-    tokens = w.B * w.T
-    alg_b = prefill_alg_bytes(w.B, w.T, w.H, w.K, w.V, s0=w.s0_std is not None, sT=True)
-    alg_f = prefill_alg_flops(w.B, w.T, w.H, w.K, w.V, w.chunk)
-    achieved = alg_b / (ms * 1e-3) / 1e9
-    tag = w.name.replace("prefill_bf16_", "prefill_").replace("batched_bf16_", "batched_")
-    traffic = measured_traffic(("kda_chunk_fwd_two_pass_" if nws else "chunk_mfma_kernel_") + tag)
+    settle_clock(stream)
+    flush = CacheFlush(dev)
+    w = inputs.WORKLOADS[args.prefill_workload]
+    head, d_head, cu_head = prefill_leg(w, args, dev, stream, flush, args.steps, args.warmup)
+    cfg = {"workload": w.name, "sequences": head["sequences"], "tokens": head["tokens"],
+           "H": w.H, "d_k": w.K, "d_v": w.V, "chunk": w.chunk, "global_batch": head["sequences"],
+           "seq_len": (w.T if w.kind == "fixed" else f"log-uniform [{w.len_min}, {w.len_max}]"),
+           "parallelism": "none (1 GPU)"}
     result = {
         "metric": "KDA fwd tokens/s (prefill, decode) + % of MFMA/HBM roofline, 1 MI355X",
-        "value": tokens / (ms * 1e-3),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 in, f16 MFMA operands, f32 accumulate/state/out",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d_k": w.K, "d_v": w.V,
-                   "chunk": w.chunk, "global_batch": w.B, "seq_len": w.T,
-                   "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": f"kda_chunk_fwd {path}: {kernels}",
-                     "alg_bytes_per_launch": alg_b},
-        "roofline_mfma": {"achieved": alg_f / (ms * 1e-3) / 1e12, "peak": MFMA_F16_PEAK_TFLOPS,
-                          "unit": "TFLOP/s", "frac": alg_f / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                          "flops": "algorithmic", "alg_flops_per_launch": alg_f},
-        "wall_s_timed_region": wall,
-        "path": path,
-        "fused_single_pass_ms_per_step": ms_fused,
-        "prefix_cache": {"ms_per_step_with_snapshots": ms_snap, "snap_tokens": snap,
-                         "page_tokens": page, "snapshots_per_call": w.B * w.H * (w.T // snap)},
-        "backward": {"ms_per_step": ms_bwd, "tokens_per_s": tokens / (ms_bwd * 1e-3),
-                     "kernels": "bwd_prep_kernel + bwd_trans_mfma_kernel + bwd_chain_mfma_kernel (both chains) + "
-                                "bwd_udy_mfma_kernel + bwd_kgrad_mfma_kernel (fp32, MFMA at d = 128)",
-                     "alg_bytes_per_call": bwd_b,
-                     "achieved_GBps": bwd_b / (ms_bwd * 1e-3) / 1e9,
-                     "hbm_frac": bwd_b / (ms_bwd * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "prologue": {"ms_per_step_fused_maps": ms_pro,
-                     "ms_per_step_torch_maps_then_plain_call": ms_torch_pro,
-                     "maps": "q, k L2-normalised (eps 1e-6); g = -0.25 sigmoid(gate logits); "
-                             "beta = sigmoid(beta logits)"},
+        "config": cfg,
+        "roofline": head["roofline"],
+        "roofline_mfma": head["roofline_mfma"],
+        "timing": head["timing"],
+        "path": head["path"],
     }
-
-    # ---- decode leg
+    if not args.no_legs:
+        legs = {}
+        for name in PREFILL_WORKLOADS:
+            if name != w.name:
+                leg, _, _ = prefill_leg(inputs.WORKLOADS[name], args, dev, stream, flush,
+                                        args.steps, args.warmup)
+                legs[name] = leg
+        result["prefill_legs"] = legs
+        result.update(next_legs(args, dev, stream))
     if not args.no_decode:
         result["decode"] = decode_leg(args, dev, stream)
+    del flush
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(d, w)
+        result["cpu_baseline"] = cpu_baseline(d_head, cu_head, w.H, w.name)
     print(json.dumps(result), flush=True)
 
 
