@@ -8,6 +8,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/kda.h"
 #include "prologue.hpp"
@@ -141,11 +142,45 @@ bool pool_ok(int pool_slots, int H, int K, int V) {
     return pool_slots >= 1 && (long long)pool_slots * H <= LLONG_MAX / 4 / ((long long)K * V);
 }
 
+// Scratch of kda_varlen_fwd_noalloc: a file-scope device array of
+// KDA_NOALLOC_SCRATCH_BYTES, one copy per GPU the library is loaded on, held
+// until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it only stands for the symbol): the device address is
+// looked up once per device with hipGetSymbolAddress and kept below.
+constexpr size_t kScratchBytes = (size_t)80 << 20;
+static_assert(kScratchBytes == KDA_NOALLOC_SCRATCH_BYTES, "scratch size and its documented value");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+hipError_t scratch_of_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = __atomic_load_n(&g_scratch_ptr[dev], __ATOMIC_ACQUIRE);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev];
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            __atomic_store_n(&g_scratch_ptr[dev], p, __ATOMIC_RELEASE);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
 
-int kda_version(void) { return 104; }
+int kda_version(void) { return 105; }
 
 const char *kda_status_str(kda_status_t s) {
     switch (s) {
@@ -154,7 +189,7 @@ const char *kda_status_str(kda_status_t s) {
         case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: invalid or oversized dimensions";
         case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: unknown dtype";
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: (K, V, chunk) or dtype not supported";
-        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace too small";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace too small (or, without a workspace argument, the call needs more than the library's scratch)";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error";
         case KDA_ERR_VALUE: return "KDA_ERR_VALUE: scalar argument out of range";
     }
@@ -237,6 +272,28 @@ kda_status_t kda_varlen_fwd(const void *q, const void *k, const void *v, const v
     return kda_varlen_fwd_prologue(q, k, v, g, beta, s0, o, sT, cu_seqlens, N, total_T, H, K, V,
                                    chunk, in_dtype, out_dtype, workspace, workspace_bytes, 0u,
                                    0.f, 0.f, stream);
+}
+
+kda_status_t kda_varlen_fwd_noalloc(const void *q, const void *k, const void *v, const void *g,
+                                    const void *beta, const float *s0, void *o, float *sT,
+                                    const int32_t *cu_seqlens, int N, int total_T, int H, int K,
+                                    int V, int chunk, kda_dtype_t in_dtype,
+                                    kda_dtype_t out_dtype, void *stream) {
+    kda_status_t s = validate_fwd(q, k, v, g, beta, o, N, total_T, H, K, V, chunk, in_dtype,
+                                  out_dtype);
+    if (s != KDA_OK) return s;
+    if (N > 0 && !cu_seqlens) return KDA_ERR_NULL;
+    if (N == 0) return KDA_OK;
+    if (in_dtype != KDA_BF16 || !kda::chunk_split_supported(N, H, K, V, chunk))
+        return KDA_ERR_UNSUPPORTED;
+    const size_t need = kda::chunk_split_workspace_bytes(N, total_T, H);
+    if (need > kScratchBytes) return KDA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    hipError_t e = scratch_of_current_device(&ws);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    kda::Prologue pro;
+    return run_fwd(q, k, v, g, beta, dense_states(s0, sT), pro, o, cu_seqlens, N, 0, total_T, H,
+                   K, V, chunk, in_dtype, out_dtype, ws, true, stream);
 }
 
 kda_status_t kda_varlen_fwd_paged_prologue(

@@ -15,7 +15,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["chunk_fwd", "varlen_fwd", "decode_step", "varlen_fwd_paged", "decode_step_paged",
+__all__ = ["chunk_fwd", "varlen_fwd", "varlen_fwd_noalloc", "decode_step", "varlen_fwd_paged", "decode_step_paged",
            "decode_multi_paged", "Prologue", "chunk_bwd", "varlen_bwd", "bwd_workspace_bytes",
            "workspace_bytes",
            "two_pass_workspace_bytes", "library",
@@ -73,6 +73,9 @@ def library():
     lib.kda_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     lib.kda_varlen_fwd.restype = i32
+    lib.kda_varlen_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           i32, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.kda_varlen_fwd_noalloc.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_step.restype = i32
     lib.kda_varlen_fwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
@@ -275,6 +278,38 @@ def varlen_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, output_final_st
           _ptr(initial_state), _ptr(o), _ptr(sT), _ptr(cu_seqlens), N, total, H, K, V, chunk,
           _dtype_code(dt), _dtype_code(o.dtype), _ptr(ws), nws, _stream(dev))
     return o, sT
+
+
+def varlen_fwd_noalloc(q, k, v, g, beta, cu_seqlens, initial_state=None, final_state=None,
+                       out=None, chunk=None):
+    """kda_varlen_fwd_noalloc: the two-pass packed forward with the library's
+    static scratch instead of a workspace (no device allocation in the library;
+    the outputs are the caller's when `out` / `final_state` are given, else
+    allocated here by torch).  bf16 inputs, K = V = 128, at most 126 sequences
+    and a two-pass workspace within the 80 MiB scratch.  Returns
+    (o [total_T, H, V] float32, final states [N, H, K, V] or None)."""
+    _need_gpu(q, k, v, g, beta, cu_seqlens, initial_state, final_state, out)
+    total, H, K = q.shape
+    V = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    dt = q.dtype
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if any(x.dtype != dt for x in (k, v, g, beta)):
+        raise ValueError("q, k, v, g and beta must share one dtype")
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (total, H, V) or beta.shape != (total, H):
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    for s in (initial_state, final_state):
+        if s is not None and (s.dtype != torch.float32 or s.shape != (N, H, K, V)):
+            raise ValueError("states must be float32 [N, H, K, V]")
+    chunk = chunk or _default_chunk(K)
+    o = out if out is not None else torch.empty((total, H, V), dtype=torch.float32, device=q.device)
+    if o.shape != (total, H, V):
+        raise ValueError("out must be [total_T, H, V]")
+    _call("kda_varlen_fwd_noalloc", None, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+          _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(cu_seqlens), N, total, H, K, V,
+          chunk, _dtype_code(dt), _dtype_code(o.dtype), _stream(q.device))
+    return o, final_state
 
 
 def decode_step(q, k, v, g, beta, state, out_dtype=torch.float32, out=None, prologue=None):

@@ -37,7 +37,8 @@
  *
  * Ownership and ordering.  The caller allocates every buffer; the library
  * allocates no device memory, keeps no state between calls and is
- * thread-safe.  All pointers except the cu_seqlens host-side description
+ * thread-safe (one exception: kda_varlen_fwd_noalloc below uses a static
+ * scratch array that the library's code object holds on each GPU).  All pointers except the cu_seqlens host-side description
  * below are device pointers.  Every call validates its arguments on the host,
  * then enqueues its kernels on `stream` (a hipStream_t; NULL = the default
  * stream) and returns without synchronising.  Results are ready when the
@@ -118,6 +119,32 @@ kda_status_t kda_varlen_fwd(const void *q, const void *k, const void *v, const v
                             const int32_t *cu_seqlens, int N, int total_T, int H, int K,
                             int V, int chunk, kda_dtype_t in_dtype, kda_dtype_t out_dtype,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_varlen_fwd without allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the two-pass bf16 path of kda_varlen_fwd, with the
+ * library's own static scratch in place of the caller's workspace.  The
+ * scratch is a device array of KDA_NOALLOC_SCRATCH_BYTES (80 MiB), one copy
+ * on every GPU the library is loaded on, held until the process ends; the
+ * call itself allocates nothing.  Arguments, layouts and results are those of
+ * kda_varlen_fwd with a two-pass-sized workspace (bit-identical output).
+ * Limits, checked before any launch: bf16 inputs, (K, V, chunk) =
+ * (128, 128, 64) and 1 <= N <= 126, else KDA_ERR_UNSUPPORTED; a call whose
+ * two-pass workspace (kda_two_pass_workspace_bytes) exceeds the scratch,
+ * KDA_ERR_WORKSPACE.  The scratch found on the CURRENT device is used, so
+ * the stream must belong to the current device.  Every call on a GPU shares
+ * that GPU's one scratch: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and give undefined results; calls
+ * ordered on one stream are safe.  Nothing in the scratch needs clearing
+ * between calls (every byte read is written earlier in the same call).
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
+kda_status_t kda_varlen_fwd_noalloc(const void *q, const void *k, const void *v, const void *g,
+                                    const void *beta, const float *s0, void *o, float *sT,
+                                    const int32_t *cu_seqlens, int N, int total_T, int H, int K,
+                                    int V, int chunk, kda_dtype_t in_dtype,
+                                    kda_dtype_t out_dtype, void *stream);
 
 /*
  * One recurrent decode step: one new token for each of N sequences.

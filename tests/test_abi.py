@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
               "kda_chunk_fwd_prologue", "kda_varlen_fwd_prologue",
               "kda_varlen_fwd_paged_prologue", "kda_decode_step_prologue",
               "kda_decode_step_paged_prologue", "kda_decode_multi_paged_prologue",
-              "kda_chunk_bwd", "kda_varlen_bwd", "kda_bwd_workspace_bytes"):
+              "kda_chunk_bwd", "kda_varlen_bwd", "kda_bwd_workspace_bytes",
+              "kda_varlen_fwd_noalloc"):
         assert n in names
 
 
@@ -50,7 +51,7 @@ def test_status_strings_and_version(lib):
         assert s.startswith("KDA_")
     assert lib.kda_status_str(7).decode().startswith("KDA_ERR_VALUE")
     assert lib.kda_status_str(99).decode() == "KDA_ERR_UNKNOWN"
-    assert lib.kda_version() == 104
+    assert lib.kda_version() == 105
 
 
 def two_pass_size(N, total, H):
@@ -111,6 +112,26 @@ def test_varlen_argument_errors(lib):
     assert f(*[FAKE] * 9, 2, -10, 1, 128, 128, 64, 1, 0, None, 0, None) == 2
     assert f(*[FAKE] * 9, 2, 10, 1, 96, 128, 64, 1, 0, None, 0, None) == 4
     assert f(*[FAKE] * 9, 2, 10, 1, 128, 128, 64, 5, 0, None, 0, None) == 3
+
+
+def test_noalloc_argument_errors(lib):
+    """kda_varlen_fwd_noalloc rejects, before any HIP call, what its static
+    scratch cannot serve: other than bf16 / (128, 128, 64) / N < 127, or a
+    two-pass workspace above KDA_NOALLOC_SCRATCH_BYTES (80 MiB)."""
+    f = lib.kda_varlen_fwd_noalloc
+    assert f(*[FAKE] * 8, None, 2, 10, 1, 128, 128, 64, 1, 0, None) == 1       # no cu_seqlens
+    assert f(*[FAKE] * 9, 0, 0, 1, 128, 128, 64, 1, 0, None) == 0              # nothing to do
+    assert f(*[FAKE] * 9, 2, 10, 1, 128, 128, 64, 0, 0, None) == 4             # fp32 inputs
+    assert f(*[FAKE] * 9, 2, 10, 1, 32, 32, 16, 1, 0, None) == 4               # d = 32
+    assert f(*[FAKE] * 9, 127, 1000, 1, 128, 128, 64, 1, 0, None) == 4         # N > 126
+    limit = 80 << 20
+    assert two_pass_size(1, 4096, 8) <= limit < two_pass_size(1, 4096 * 2, 8)
+    assert f(*[FAKE] * 9, 1, 8192, 8, 128, 128, 64, 1, 0, None) == 5          # above the scratch
+    assert f(*[FAKE] * 9, 2, 10, 1, 128, 128, 64, 1, 9, None) == 3             # bad out dtype
+    for i in (0, 1, 2, 3, 4, 6):
+        ptrs = [FAKE] * 9
+        ptrs[i] = None
+        assert f(*ptrs, 1, 10, 1, 128, 128, 64, 1, 0, None) == 1
 
 
 def test_decode_argument_errors(lib):
