@@ -84,7 +84,6 @@ struct Smem {
     float beta[C];
     float fm[2][KD];            // exp(G_m), by chunk parity
     float fc[2][KD];            // exp(G_C - G_m), by chunk parity
-    float ad[4][16 * PF];       // prep waves: diagonal A blocks (private)
     float gsum[2][NP][KD];      // prep waves: per-wave channel sums of g, by chunk parity
 };
 
@@ -109,10 +108,10 @@ __device__ __forceinline__ half8 cat8(half4 a, half4 b) {
 // One chunk's inputs, held in a prep wave's registers ahead of use.
 // Lane (cg = lane & 15, tb = lane >> 4) of prep wave p holds channels
 // 8 cg .. 8 cg + 7 of tokens 8p + 2 tb and 8p + 2 tb + 1 (16-byte loads, each
-// instruction reading four whole 256-byte rows).  Every lane loads the same
-// rows whatever the chunk's length L >= 1: rows past the end re-read row
-// L - 1, and the consumers replace them by padding (at use, so that no wait is
-// forced at the load).
+// instruction reading four whole 256-byte rows).  The loads go through buffer
+// resources whose extent ends at the chunk's last token, so rows past a short
+// chunk's end read as zero without touching memory, and all address
+// arithmetic but one scalar base per chunk is fixed for the whole kernel.
 struct Raw {
     uint4 q[2], k[2];
     uint4 v;         // V tile piece: row lane, columns 8p .. 8p + 7
@@ -120,40 +119,87 @@ struct Raw {
     int L;           // the chunk's length
 };
 
-// Offsets (in 16-byte units, from the chunk's first row of head h) of this
-// lane's two token rows, clamped to the chunk.
-__device__ __forceinline__ void row_vecs(int *off, int L, int H, int p, int lane) {
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes from base (raw addressing; accesses past
+// the extent return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t extent(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+
+// Byte offsets, inside a chunk, of one lane's loads (the same for every chunk).
+struct LaneOffs {
+    uint32_t row[2];  // q / k / g: tokens 8p + 2 tb + u, channels 8 cg ..
+    uint32_t v;       // V: token lane
+    uint32_t beta;    // beta: token lane
+};
+
+__device__ __forceinline__ LaneOffs lane_offsets(int H, int p, int lane) {
     const int cg = lane & 15, tb = lane >> 4;
+    LaneOffs o;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) off[u] = min(8 * p + 2 * tb + u, L - 1) * (H * KD / 8) + cg;
+    for (int u = 0; u < 2; ++u) o.row[u] = (uint32_t)((8 * p + 2 * tb + u) * H * KD * 2 + 16 * cg);
+    o.v = (uint32_t)(lane * H * VD * 2);
+    o.beta = (uint32_t)(lane * H * 2);
+    return o;
 }
 
 __device__ __forceinline__ void load_g(uint4 *rg, const uint16_t *g, int c0, int L, int H, int h,
-                                       int p, int lane) {
-    const uint4 *base = reinterpret_cast<const uint4 *>(g + ((size_t)c0 * H + h) * KD);
-    int off[2];
-    row_vecs(off, L, H, p, lane);
+                                       const LaneOffs &lof) {
+    const auto r = extent(g + ((size_t)c0 * H + h) * KD, (uint32_t)(L * H * KD * 2));
 #pragma unroll
-    for (int u = 0; u < 2; ++u) rg[u] = base[off[u]];
+    for (int u = 0; u < 2; ++u) rg[u] = load16(r, lof.row[u]);
 }
 
 __device__ __forceinline__ void load_raw(Raw &R, const uint16_t *q, const uint16_t *k,
                                          const uint16_t *v, const uint16_t *beta, int c0, int L,
-                                         int H, int h, int vt, int p, int lane) {
+                                         int H, int h, int vt, int p, const LaneOffs &lof) {
     const size_t cb = ((size_t)c0 * H + h) * KD;
-    const uint4 *bq = reinterpret_cast<const uint4 *>(q + cb);
-    const uint4 *bk = reinterpret_cast<const uint4 *>(k + cb);
-    int off[2];
-    row_vecs(off, L, H, p, lane);
+    const uint32_t rows = (uint32_t)(L * H * KD * 2);
+    const auto rq = extent(q + cb, rows), rk = extent(k + cb, rows);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        R.q[u] = bq[off[u]];
-        R.k[u] = bk[off[u]];
+        R.q[u] = load16(rq, lof.row[u]);
+        R.k[u] = load16(rk, lof.row[u]);
     }
-    const uint4 *bv = reinterpret_cast<const uint4 *>(v + ((size_t)c0 * H + h) * VD + vt * VT + 8 * p);
-    R.v = bv[min(lane, L - 1) * (H * VD / 8)];
-    R.beta = beta[((size_t)c0 + min(lane, L - 1)) * H + h];
+    const auto rv = extent(v + ((size_t)c0 * H + h) * VD + vt * VT + 8 * p,
+                           (uint32_t)((L - 1) * H * VD * 2 + 16));
+    R.v = load16(rv, lof.v);
+    const auto rb = extent(beta + (size_t)c0 * H + h, (uint32_t)((L - 1) * H * 2 + 2));
+    R.beta = p == 0 ? __builtin_amdgcn_raw_buffer_load_b16(rb, lof.beta, 0, 0) : 0u;
     R.L = L;
+}
+
+// Extents of one chunk's inputs, from which a prep wave refills its input
+// registers as soon as their previous contents are used (spreading the loads
+// over the work rather than issuing them in one burst).
+struct Src {
+    __amdgpu_buffer_rsrc_t q, k, v, beta;
+    int L;
+};
+
+__device__ __forceinline__ Src chunk_src(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                         const uint16_t *beta, int c0, int L, int H, int h, int vt,
+                                         int p) {
+    const size_t cb = ((size_t)c0 * H + h) * KD;
+    const uint32_t rows = (uint32_t)(L * H * KD * 2);
+    Src s;
+    s.q = extent(q + cb, rows);
+    s.k = extent(k + cb, rows);
+    s.v = extent(v + ((size_t)c0 * H + h) * VD + vt * VT + 8 * p, (uint32_t)((L - 1) * H * VD * 2 + 16));
+    s.beta = extent(beta + (size_t)c0 * H + h, (uint32_t)((L - 1) * H * 2 + 2));
+    s.L = L;
+    return s;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gate_src(const uint16_t *g, int c0, int L, int H,
+                                                           int h) {
+    return extent(g + ((size_t)c0 * H + h) * KD, (uint32_t)(L * H * KD * 2));
 }
 
 // The lane values of the even and of the odd 16-lane row of this lane's row
@@ -176,14 +222,21 @@ __device__ __forceinline__ void half_rows(float x, float &lower, float &upper) {
 // The wave's channel totals go to LDS.  Rows at or past L read as `pad`.
 // PM (a ProMode): rg holds gate logits when the prologue's gate map applies.
 template <int PM>
-__device__ __forceinline__ void scan_partials(Smem &sm, const uint4 *rg, int L, uint32_t pad,
+__device__ __forceinline__ void scan_partials(Smem &sm, uint4 *rg, int L, uint32_t pad,
                                               int par, int p, int lane, float (*lc)[8], float *ex,
-                                              const Prologue &pro) {
+                                              const Prologue &pro, __amdgpu_buffer_rsrc_t gnext,
+                                              const LaneOffs &lof) {
     const int cg = lane & 15, tb = lane >> 4;
     const uint4 pad4 = make_uint4(pad, pad, pad, pad);
-    unpack8(8 * p + 2 * tb < L ? rg[0] : pad4, lc[0]);
-    unpack8(8 * p + 2 * tb + 1 < L ? rg[1] : pad4, lc[1]);
-    if (pro_on<PM>(pro, PRO_GATE_LOGIT)) {
+    // rows past the end loaded as zero: no decay, except through the gate map
+    const bool gl = pro_on<PM>(pro, PRO_GATE_LOGIT);
+    unpack8(gl && 8 * p + 2 * tb >= L ? pad4 : rg[0], lc[0]);
+    unpack8(gl && 8 * p + 2 * tb + 1 >= L ? pad4 : rg[1], lc[1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) rg[u] = load16(gnext, lof.row[u]);  // the next chunk's gates
+    __builtin_amdgcn_sched_barrier(0);
+    if (gl) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             lc[0][e] = gate_from_logit(lc[0][e], pro.glb);
@@ -212,46 +265,58 @@ __device__ __forceinline__ void scan_partials(Smem &sm, const uint4 *rg, int L, 
 // prologue's normalisation of q and k, whose 128 channels of a token lie in
 // one 16-lane DPP row).
 template <int PM>
-__device__ __forceinline__ void build_operands(Smem &sm, const Raw &R, uint32_t bpad, int par,
+__device__ __forceinline__ void build_operands(Smem &sm, Raw &R, uint32_t bpad, int par,
                                                int p, int lane, const float (*lc)[8],
-                                               const float *ex, const Prologue &pro) {
+                                               const float *ex, const Prologue &pro, const Src &nx,
+                                               const LaneOffs &lof) {
+    const int L = R.L;
     const int cg = lane & 15, tb = lane >> 4;
     const int ch0 = 8 * cg;
     const int r0 = 8 * p + 2 * tb;
     // offset of this wave's first token from the reference row m = 31 (the end
     // of wave 3's tokens): + sum of waves 4..p-1, or - sum of waves p..3
+    // (the four candidate wave totals are read at once and masked)
+    const int lo = p < 4 ? p : 4, hi = p < 4 ? 4 : p;
+    floatx4 ga[4], gb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        ga[j] = *reinterpret_cast<const floatx4 *>(&sm.gsum[par][lo + j][ch0]);
+        gb[j] = *reinterpret_cast<const floatx4 *>(&sm.gsum[par][lo + j][ch0 + 4]);
+    }
     float d[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = 0.f;
-    const int lo = p < 4 ? p : 4, hi = p < 4 ? 4 : p;
-    for (int ww = lo; ww < hi; ++ww) {
-        const floatx4 a = *reinterpret_cast<const floatx4 *>(&sm.gsum[par][ww][ch0]);
-        const floatx4 b = *reinterpret_cast<const floatx4 *>(&sm.gsum[par][ww][ch0 + 4]);
+    for (int e = 0; e < 4; ++e) {
+        d[e] = 0.f;
+        d[e + 4] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            d[e] += a[e];
-            d[e + 4] += b[e];
+        for (int j = 0; j < 4; ++j) {
+            d[e] += lo + j < hi ? ga[j][e] : 0.f;
+            d[e + 4] += lo + j < hi ? gb[j][e] : 0.f;
         }
     }
     if (p == 4) {  // per-channel factors exp(G_m) and exp(G_C - G_m), two channels per lane
+        float2 x[NP];
+#pragma unroll
+        for (int ww = 0; ww < NP; ++ww) x[ww] = *reinterpret_cast<const float2 *>(&sm.gsum[par][ww][2 * lane]);
         float gm0 = 0.f, gm1 = 0.f, gc0 = 0.f, gc1 = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NP; ++ww) {
-            const float2 x = *reinterpret_cast<const float2 *>(&sm.gsum[par][ww][2 * lane]);
             if (ww < 4) {
-                gm0 += x.x;
-                gm1 += x.y;
+                gm0 += x[ww].x;
+                gm1 += x[ww].y;
             }
-            gc0 += x.x;
-            gc1 += x.y;
+            gc0 += x[ww].x;
+            gc1 += x[ww].y;
         }
         *reinterpret_cast<float2 *>(&sm.fm[par][2 * lane]) = make_float2(fast_exp(gm0), fast_exp(gm1));
         *reinterpret_cast<float2 *>(&sm.fc[par][2 * lane]) =
             make_float2(fast_exp(gc0 - gm0), fast_exp(gc1 - gm1));
     }
+    // exp(G - G_m) = 2^(log2(e) (pre + lc)), the scale folded into one fma
+    constexpr float LOG2E = 1.4426950408889634f;
     float pre[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pre[e] = ex[e] + (p < 4 ? -d[e] : d[e]);
+    for (int e = 0; e < 8; ++e) pre[e] = LOG2E * (ex[e] + (p < 4 ? -d[e] : d[e]));
     // channels ch0 .. ch0 + 3 and ch0 + 4 .. ch0 + 7 sit 8 positions apart in
     // the permuted order
     const int cpos = (ch0 & ~31) + perm32(ch0 & 31);
@@ -261,10 +326,14 @@ __device__ __forceinline__ void build_operands(Smem &sm, const Raw &R, uint32_t 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         float kv[8], qv[8];
-        const bool valid = r0 + u < R.L;
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        unpack8(valid ? R.k[u] : z, kv);
-        unpack8(valid ? R.q[u] : z, qv);
+        unpack8(R.k[u], kv);  // zero past the chunk's end
+        unpack8(R.q[u], qv);
+        // refill with the next chunk's rows, pinned here (after the last use
+        // of the old contents) so the loop-carried registers stay in place
+        __builtin_amdgcn_sched_barrier(0);
+        R.k[u] = load16(nx.k, lof.row[u]);
+        R.q[u] = load16(nx.q, lof.row[u]);
+        __builtin_amdgcn_sched_barrier(0);
         if (pro_on<PM>(pro, PRO_NORM_QK)) {
             const float ik = inv_norm(row16_sum(sumsq8(kv)), pro.eps);
             const float iq = inv_norm(row16_sum(sumsq8(qv)), pro.eps);
@@ -277,7 +346,7 @@ __device__ __forceinline__ void build_operands(Smem &sm, const Raw &R, uint32_t 
         half8 hkp, hkm, hqp;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float f = fast_exp(pre[e] + lc[u][e]);  // exp(G - G_m)
+            const float f = __builtin_amdgcn_exp2f(__builtin_fmaf(lc[u][e], LOG2E, pre[e]));
             const float i = __builtin_amdgcn_rcpf(f);
             hkp[e] = (_Float16)(kv[e] * f);
             hkm[e] = (_Float16)(kv[e] * i);
@@ -305,17 +374,33 @@ __device__ __forceinline__ void build_operands(Smem &sm, const Raw &R, uint32_t 
     }
     // V transposed: columns 8p .. 8p + 7, row lane (consecutive lanes write
     // consecutive halves)
-    const uint4 vv = lane < R.L ? R.v : make_uint4(0u, 0u, 0u, 0u);
-    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+    const uint32_t vw[4] = {R.v.x, R.v.y, R.v.z, R.v.w};  // zero past the end
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         sm.vt[(8 * p + 2 * e) * PV + lane] = (uint16_t)(vw[e] & 0xFFFFu);
         sm.vt[(8 * p + 2 * e + 1) * PV + lane] = (uint16_t)(vw[e] >> 16);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    R.v = load16(nx.v, lof.v);
+    __builtin_amdgcn_sched_barrier(0);
     if (p == 0) {
-        const float b = __uint_as_float((lane < R.L ? R.beta : bpad) << 16);
+        const bool bl = pro_on<PM>(pro, PRO_BETA_LOGIT);
+        const float b = __uint_as_float((bl && lane >= L ? bpad : R.beta) << 16);
+        R.beta = __builtin_amdgcn_raw_buffer_load_b16(nx.beta, lof.beta, 0, 0);
         sm.beta[lane] = pro_on<PM>(pro, PRO_BETA_LOGIT) ? sigmoid_f(b) : b;
     }
+    R.L = nx.L;
+}
+
+// Block product: lane (l16, lg) receives element i =
+// (lhs rhs^T)[16 bi + 4 lg + i][16 bj + l16].
+__device__ __forceinline__ floatx4 block_product(const _Float16 *lhs, const _Float16 *rhs, int bi,
+                                                 int bj, int lane) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        acc = mma32(frag8(lhs, PK, 16 * bi, 32 * ks, lane), frag8(rhs, PK, 16 * bj, 32 * ks, lane), acc);
+    return acc;
 }
 
 // Transposed block product: lane (l16, lg) receives element i =
@@ -336,46 +421,40 @@ __device__ __forceinline__ floatx4 block_product_t(const _Float16 *lhs, const _F
 __device__ __forceinline__ void prep_blocks(Smem &sm, int p, int lane) {
     const int l16 = lane & 15, lg = lane >> 4;
     if (p < 4) {
-        const floatx4 a = block_product_t(sm.kp, sm.km, p, p, lane);
+        // A_pp = Diag(beta) strict_lower(Kp Km^T) on this block, held twice:
+        // in the A layout (lane: row l16, columns 4 lg .. +3; the transposed
+        // product) and in the B layout (lane: column l16, rows 4 lg .. +3)
+        const floatx4 at = block_product_t(sm.kp, sm.km, p, p, lane);
+        const floatx4 ab = block_product(sm.kp, sm.km, p, p, lane);
         const float br = sm.beta[16 * p + l16];
-        floatx4 am;
+        const floatx4 bc = *reinterpret_cast<const floatx4 *>(&sm.beta[16 * p + 4 * lg]);
+        half4 LA, LB;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) am[i] = 4 * lg + i < l16 ? br * a[i] : 0.f;
-        float *ad = sm.ad[p];
-        *reinterpret_cast<floatx4 *>(&ad[l16 * PF + 4 * lg]) = am;
+        for (int i = 0; i < 4; ++i) {
+            LA[i] = (_Float16)(4 * lg + i < l16 ? br * at[i] : 0.f);
+            LB[i] = (_Float16)(l16 < 4 * lg + i ? bc[i] * ab[i] : 0.f);
+        }
         const floatx4 pq = block_product_t(sm.qp, sm.km, p, p, lane);
         half4 ph;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ph[i] = (_Float16)(4 * lg + i <= l16 ? pq[i] : 0.f);
         *reinterpret_cast<half4 *>(&sm.p[(16 * p + l16) * P4 + 16 * p + 4 * lg]) = ph;
-        // (I + A_pp)^-1 by forward substitution: the quad of lanes 4j..4j+3
-        // owns column j; lane q of the quad sums the terms s = q (mod 4), a
-        // quad butterfly completes each row, and lane r & 3 keeps t_r.
-        const int j = lane >> 2, q = lane & 3;
-        float coef[4][16];               // A[r][s] for this lane's s = 4m + q (0 when s >= r)
+        // (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8) for the strictly lower
+        // 16 x 16 block L (L^16 = 0), as 16x16x16 products.  A product Z = X Y
+        // from X in the A layout and Y in the B layout gives Z in the B layout
+        // (accumulator = B fragment); Z^T = Y^T X^T from the same registers,
+        // operands swapped, gives Z in the A layout.
+        const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+        half4 eye;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                coef[m][r] = (4 * m < r) ? ad[r * PF + 4 * m + q] : 0.f;  // s = 4m + q
-        float t_own[4];                  // t_s for s = 4m + q
-#pragma unroll
-        for (int m = 0; m < 4; ++m) t_own[m] = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float part = 0.f;
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-                if (4 * m < r) part += coef[m][r] * t_own[m];
-            part += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                                                  __builtin_bit_cast(int, part), 0xB1, 0xF, 0xF, true));
-            part += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                                                  __builtin_bit_cast(int, part), 0x4E, 0xF, 0xF, true));
-            const float tr = (r == j ? 1.f : 0.f) - part;
-            if ((r & 3) == q) t_own[r >> 2] = tr;
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) sm.tii[p][(4 * m + q) * PI + j] = (_Float16)t_own[m];
+        for (int i = 0; i < 4; ++i) eye[i] = (_Float16)(4 * lg + i == l16 ? 1.f : 0.f);
+        const half4 L2B = to_half4(mma16(LA, LB, z4)), L2A = to_half4(mma16(LB, LA, z4));
+        const half4 L4B = to_half4(mma16(L2A, L2B, z4)), L4A = to_half4(mma16(L2B, L2A, z4));
+        const half4 L8B = to_half4(mma16(L4A, L4B, z4));
+        const half4 R1A = to_half4(mma16(eye + L2B, eye - LA, z4));   // ((I - L)(I + L^2))^T
+        const half4 R2A = to_half4(mma16(eye + L4B, R1A, z4));        // (R1 (I + L^4))^T
+        const half4 TA = to_half4(mma16(eye + L8B, R2A, z4));         // (R2 (I + L^8))^T
+        *reinterpret_cast<half4 *>(&sm.tii[p][l16 * PI + 4 * lg]) = TA;
     } else {
 #pragma unroll
         for (int tsk = 0; tsk < 3; ++tsk) {
@@ -429,9 +508,12 @@ __device__ __forceinline__ void store4<float>(float *dst, floatx4 v) {
 }
 template <>
 __device__ __forceinline__ void store4<bf16_t>(bf16_t *dst, floatx4 v) {
+    // round to nearest even by the packed hardware conversion
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
     uint2 w;
-    w.x = (uint32_t)from_f32_bf16(v[0]).bits | ((uint32_t)from_f32_bf16(v[1]).bits << 16);
-    w.y = (uint32_t)from_f32_bf16(v[2]).bits | ((uint32_t)from_f32_bf16(v[3]).bits << 16);
+    w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){v[0], v[1]}, b2));
+    w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){v[2], v[3]}, b2));
     *reinterpret_cast<uint2 *>(dst) = w;
 }
 
@@ -630,6 +712,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
         const int p = w - 4;
         const uint32_t gpad = pro_on<PM>(pro, PRO_GATE_LOGIT) ? BF16_NEG_INF_PAIR : 0u;
         const uint32_t bpad = pro_on<PM>(pro, PRO_BETA_LOGIT) ? (BF16_NEG_INF_PAIR & 0xFFFFu) : 0u;
+        const LaneOffs lof = lane_offsets(H, p, lane);
         Raw R;
         uint4 rg[2];
         float lc[2][8], ex[8];
@@ -643,30 +726,31 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
         // operands and chunk ci + 2's decay sums (phase B), and issue the loads
         // of chunk ci + 2's inputs and chunk ci + 3's gates, which are used one
         // iteration later.
+        auto src = [&](int i) { return chunk_src(q, k, v, beta, cstart(i), clen(i), H, h, vt, p); };
+        auto gsrc = [&](int i) { return gate_src(g, cstart(i), clen(i), H, h); };
         if (nchunks > 0) {
-            load_g(rg, g, cstart(0), clen(0), H, h, p, lane);
-            load_raw(R, q, k, v, beta, cstart(0), clen(0), H, h, vt, p, lane);
-            scan_partials<PM>(sm, rg, clen(0), gpad, 0, p, lane, lc, ex, pro);
-            load_g(rg, g, cstart(1), clen(1), H, h, p, lane);
+            load_g(rg, g, cstart(0), clen(0), H, h, lof);
+            load_raw(R, q, k, v, beta, cstart(0), clen(0), H, h, vt, p, lof);
+            scan_partials<PM>(sm, rg, clen(0), gpad, 0, p, lane, lc, ex, pro, gsrc(1), lof);
         }
         __syncthreads();
         if (nchunks > 0) {
-            build_operands<PM>(sm, R, bpad, 0, p, lane, lc, ex, pro);
-            if (nchunks > 1) scan_partials<PM>(sm, rg, clen(1), gpad, 1, p, lane, lc, ex, pro);
-            load_raw(R, q, k, v, beta, cstart(1), clen(1), H, h, vt, p, lane);
-            load_g(rg, g, cstart(2), clen(2), H, h, p, lane);
+            build_operands<PM>(sm, R, bpad, 0, p, lane, lc, ex, pro, src(1), lof);
+            scan_partials<PM>(sm, rg, clen(1), gpad, 1, p, lane, lc, ex, pro, gsrc(2), lof);
         }
         __syncthreads();
         for (int ci = 0; ci < nchunks; ++ci) {
             // ---- phase A: this chunk's Gram / query-key blocks and diagonal inverses
             prep_blocks(sm, p, lane);
             __syncthreads();
-            // ---- phase B: the next chunk's operands, the decay sums of the
-            // chunk after it, and the loads for the iteration after this one
-            if (ci + 1 < nchunks) build_operands<PM>(sm, R, bpad, (ci & 1) ^ 1, p, lane, lc, ex, pro);
-            if (ci + 2 < nchunks) scan_partials<PM>(sm, rg, clen(ci + 2), gpad, ci & 1, p, lane, lc, ex, pro);
-            load_raw(R, q, k, v, beta, cstart(ci + 2), clen(ci + 2), H, h, vt, p, lane);
-            load_g(rg, g, cstart(ci + 3), clen(ci + 3), H, h, p, lane);
+            // ---- phase B: the next chunk's operands and the decay sums of the
+            // chunk after it; their input registers are refilled (for chunks
+            // ci + 2 and ci + 3) as they are consumed.  Both run in every
+            // iteration (unconditional register refills keep the loop-carried
+            // inputs in place): past the last chunk they rework the last
+            // chunk's inputs into buffers that are not read again.
+            build_operands<PM>(sm, R, bpad, (ci & 1) ^ 1, p, lane, lc, ex, pro, src(ci + 2), lof);
+            scan_partials<PM>(sm, rg, clen(ci + 2), gpad, ci & 1, p, lane, lc, ex, pro, gsrc(ci + 3), lof);
             __syncthreads();
         }
     }
