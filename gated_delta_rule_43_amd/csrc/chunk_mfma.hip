@@ -260,6 +260,26 @@ __device__ __forceinline__ void scan_partials(Smem &sm, uint4 *rg, int L, uint32
     }
 }
 
+// The chunk's per-channel factors exp(G_m) and exp(G_C - G_m) from the
+// prep waves' channel totals of parity par: state wave w, lanes 0..31, takes
+// channels 32 w .. 32 w + 31.
+__device__ __forceinline__ void chunk_factors(Smem &sm, int par, int w, int lane) {
+    if (lane < 32) {
+        const int c = 32 * w + lane;
+        float x[NP];
+#pragma unroll
+        for (int ww = 0; ww < NP; ++ww) x[ww] = sm.gsum[par][ww][c];
+        float gm = 0.f, gc = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NP; ++ww) {
+            if (ww < 4) gm += x[ww];
+            gc += x[ww];
+        }
+        sm.fm[par][c] = fast_exp(gm);
+        sm.fc[par][c] = fast_exp(gc - gm);
+    }
+}
+
 // Prep wave p, second half: combine the wave totals into G - G_m for this
 // lane's tokens and write the fp16 operand tiles of the chunk (after the
 // prologue's normalisation of q and k, whose 128 channels of a token lie in
@@ -293,24 +313,6 @@ __device__ __forceinline__ void build_operands(Smem &sm, Raw &R, uint32_t bpad, 
             d[e] += lo + j < hi ? ga[j][e] : 0.f;
             d[e + 4] += lo + j < hi ? gb[j][e] : 0.f;
         }
-    }
-    if (p == 4) {  // per-channel factors exp(G_m) and exp(G_C - G_m), two channels per lane
-        float2 x[NP];
-#pragma unroll
-        for (int ww = 0; ww < NP; ++ww) x[ww] = *reinterpret_cast<const float2 *>(&sm.gsum[par][ww][2 * lane]);
-        float gm0 = 0.f, gm1 = 0.f, gc0 = 0.f, gc1 = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NP; ++ww) {
-            if (ww < 4) {
-                gm0 += x[ww].x;
-                gm1 += x[ww].y;
-            }
-            gc0 += x[ww].x;
-            gc1 += x[ww].y;
-        }
-        *reinterpret_cast<float2 *>(&sm.fm[par][2 * lane]) = make_float2(fast_exp(gm0), fast_exp(gm1));
-        *reinterpret_cast<float2 *>(&sm.fc[par][2 * lane]) =
-            make_float2(fast_exp(gc0 - gm0), fast_exp(gc1 - gm1));
     }
     // exp(G - G_m) = 2^(log2(e) (pre + lc)), the scale folded into one fma
     constexpr float LOG2E = 1.4426950408889634f;
@@ -567,6 +569,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
         // never cover the previous chunk's output stores
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
+        chunk_factors(sm, 0, w, lane);  // chunk 0's (its channel totals are in)
         __syncthreads();
         for (int ci = 0; ci < nchunks; ++ci) {
             const int c0 = bos + ci * C;
@@ -684,6 +687,9 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[cb][i] *= f[i];
             }
+            // the next chunk's factors (its channel totals landed one
+            // iteration ago), while the prep waves finish its operands
+            chunk_factors(sm, par ^ 1, w, lane);
             // prefix snapshot when the state now covers a boundary
             if (snap.due(c0 - bos + L)) {
                 float *sp = snap.dest(io, h, H, KD * VD);
