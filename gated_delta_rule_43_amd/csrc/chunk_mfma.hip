@@ -23,21 +23,24 @@
 // CUs of one XCD.  Two wave groups run concurrently, separated by two
 // workgroup barriers per chunk:
 //  * state waves 0-3: wave w owns value columns 16 w .. 16 w + 15 and keeps the
-//    128 x 16 fp32 state slice in MFMA accumulators for the whole sequence.
-//    Per chunk (phase A) it forms S', takes its fp16 B fragments straight from
-//    the accumulators (the operand tiles store their contraction index in the
-//    matching permuted order), and forms Kp S' and, transposed, (Qp S')^T with
-//    v_mfma_f32_16x16x32_f16; then (phase B) it solves (I + A) U = Y by 16-row
+//    128 x 16 fp32 state slice in MFMA accumulators for the whole sequence
+//    (rows in the order that makes two accumulator blocks one fp16 B
+//    fragment).  Per chunk (phase A) it forms S', takes its B fragments
+//    straight from the accumulators and forms Kp S' and, transposed,
+//    (Qp S')^T with v_mfma_f32_16x16x32_f16, plus the next chunk's
+//    per-channel factors; then (phase B) it solves (I + A) U = Y by 16-row
 //    block substitution in registers (the 16x16 accumulator layout is the B
-//    layout of v_mfma_f32_16x16x16_f16), advances the state with Km^T U,
-//    adds (P U)^T to the transposed output and stores four consecutive
-//    columns of an output row per lane.
+//    layout of v_mfma_f32_16x16x16_f16), advances the state with Km^T U (Km^T
+//    read from the Km tile by the transposing LDS read ds_read_b64_tr_b16),
+//    adds (P U)^T to the transposed output and stores four consecutive columns
+//    of an output row per lane.
 //  * prep waves 4-11: prep wave p owns tokens 8p .. 8p + 7 of a chunk.  In
 //    phase A they form the current chunk's Gram and query-key blocks and the
-//    16 x 16 diagonal inverses (I + A_ii)^-1 in fp32; in phase B they build
-//    the next chunk's fp16 operand tiles (running decay sums, exponentials),
-//    take the running decay sums of the chunk after it, and issue the global
-//    loads for the iteration after this one.
+//    16 x 16 diagonal inverses (I + A_ii)^-1 (a product form on the matrix
+//    cores); in phase B they build the next chunk's fp16 operand tiles
+//    (exponentials of the running decay sums), take the running decay sums of
+//    the chunk after it, and refill their input registers from buffer loads as
+//    the old contents are consumed.
 // Packed sequences are dealt to workgroups longest first.
 #include "kda_mfma.hpp"
 #include "prologue.hpp"
@@ -53,46 +56,65 @@ constexpr int VT = 64;   // value columns per workgroup
 constexpr int NT = 768;  // threads per workgroup: 4 state waves + 8 prep waves
 constexpr int NP = 8;    // prep waves
 constexpr int PK = 144;  // LDS pitch (halves) of [64][128] fp16 tiles
-constexpr int PC = 72;   // LDS pitch (halves) of [*][64] fp16 tiles read as 16-byte fragments
 constexpr int P4 = 68;   // LDS pitch (halves) of [64][64] fp16 tiles read as 8-byte fragments
 constexpr int PI = 20;   // LDS pitch (halves) of 16 x 16 fp16 blocks
-constexpr int PF = 20;   // LDS pitch (floats) of 16 x 16 fp32 blocks
-constexpr int PV = 72;   // LDS pitch (halves) of the transposed V tile
+constexpr int PV = 72;   // LDS pitch (halves) of the V tile
 
-// Position of index x (0..31) inside its 32-block in the permuted operand
-// order: x = 4 g + t -> 8 g + t and x = 16 + 4 g + t -> 8 g + 4 + t (t < 4).
-// A lane of a 16 x 16 accumulator holds rows 4 (lane >> 4) + t of two
-// consecutive 16-row blocks; in this order those eight rows are exactly the
-// contraction indices 8 (lane >> 4) .. + 7 of a 16x16x32 B fragment.  Tiles
-// whose contraction index is a state row (the channel index of Kp, Qp, Km)
-// or a chunk row (the token index of Km^T) are stored in this order, so that
-// the state and U serve as B operands straight from the accumulators.
-__device__ __forceinline__ int perm32(int x) {
-    return x < 16 ? 8 * (x >> 2) + (x & 3) : 8 * ((x - 16) >> 2) + 4 + (x & 3);
+// State rows.  Accumulator block cb of a state wave holds, in lane group
+// g = lane >> 4, element i, the state row (key channel)
+//   sigma(cb, g, i) = 32 (cb >> 1) + 8 g + 4 (cb & 1) + i,
+// so that blocks 2 k and 2 k + 1 of lane group g together hold channels
+// 32 k + 8 g .. 32 k + 8 g + 7: exactly the contraction indices of a 16x16x32
+// B fragment.  The state thus serves as the B operand of Kp S' and Qp S'
+// straight from the accumulators while Kp, Qp and Km keep their channels in
+// natural order (a token row of eight channels is one 16-byte store).
+__device__ __forceinline__ int sigma(int cb, int g, int i) {
+    return 32 * (cb >> 1) + 8 * g + 4 * (cb & 1) + i;
 }
 
 struct Smem {
-    _Float16 kp[C * PK];        // Kp [s][c'] (c' = channel position, permuted order)
-    _Float16 qp[C * PK];        // Qp [s][c']
-    _Float16 km[C * PK];        // Km [s][c']  (Gram / query-key B operand)
-    _Float16 kmt[2][KD * PC];   // Km^T [c][s'] (state-advance A operand; s' permuted order),
-                                // by chunk parity; 8-token blocks XOR-swizzled by (c >> 3) & 7
+    _Float16 kp[C * PK];        // Kp [s][c]
+    _Float16 qp[C * PK];        // Qp [s][c]
+    _Float16 km[2][C * PK];     // Km [s][c] by chunk parity: Gram / query-key B operand, and
+                                // (read transposed) the state-advance A operand
     _Float16 a16[C * P4];       // A [r][s], lower blocks
     _Float16 p[C * P4];         // P [r][s], lower blocks
     _Float16 tii[4][16 * PI];   // (I + A_ii)^-1, diagonal blocks
-    uint16_t vt[VT * PV];       // bf16 V tile, transposed [j][r]
+    uint16_t vr[C * PV];        // bf16 V tile [r][j]
     float beta[C];
     float fm[2][KD];            // exp(G_m), by chunk parity
     float fc[2][KD];            // exp(G_C - G_m), by chunk parity
     float gsum[2][NP][KD];      // prep waves: per-wave channel sums of g, by chunk parity
+    float woff[2][NP][KD];      // log2(e) (G at prep wave p's first token - G_m), by parity
 };
 
-// frag8 from the swizzled Km^T tile: row c, 8-position block kb = 4 ks + (lane >> 4)
-// stored at block kb ^ ((c >> 3) & 7).
-__device__ __forceinline__ half8 frag8_kmt(const _Float16 *base, int row0, int ks, int lane) {
-    const int c = row0 + (lane & 15);
-    const int kb = (4 * ks + (lane >> 4)) ^ ((c >> 3) & 7);
-    return *reinterpret_cast<const half8 *>(base + c * PC + 8 * kb);
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane j
+// receives as element i the (j & 3)-th 16-bit value of the 8 bytes addressed
+// by lane 4 i + (j >> 2) of its group.
+__device__ __forceinline__ short4v read_tr(const void *addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4v *)(const_cast<void *>(addr)));
+}
+
+// Km^T A fragment of state block cb, contraction half ks: lane (l16, g) gets
+// row sigma(cb, l16 >> 2, l16 & 3) (a key channel) and, as contraction
+// positions 8 g .. 8 g + 7, the tokens 32 ks + 4 g + t and 32 ks + 16 + 4 g + t
+// (t < 4): the order in which two 16-row U blocks serve as a B fragment.
+__device__ __forceinline__ half8 frag_kmT(const _Float16 *km, int cb, int ks, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int c = 32 * (cb >> 1) + 8 * (j & 3) + 4 * (cb & 1);
+    const int t = 32 * ks + 4 * g + (j >> 2);
+    const half4 lo = __builtin_bit_cast(half4, read_tr(km + t * PK + c));
+    const half4 hi = __builtin_bit_cast(half4, read_tr(km + (t + 16) * PK + c));
+    half8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = lo[i];
+        r[i + 4] = hi[i];
+    }
+    return r;
 }
 
 __device__ __forceinline__ half8 cat8(half4 a, half4 b) {
@@ -260,23 +282,33 @@ __device__ __forceinline__ void scan_partials(Smem &sm, uint4 *rg, int L, uint32
     }
 }
 
-// The chunk's per-channel factors exp(G_m) and exp(G_C - G_m) from the
-// prep waves' channel totals of parity par: state wave w, lanes 0..31, takes
-// channels 32 w .. 32 w + 31.
+// From the prep waves' channel totals of parity par, the chunk's per-channel
+// factors exp(G_m) and exp(G_C - G_m) and each prep wave's offset to the
+// reference row, log2(e) (G_{8p - 1} - G_m) (minus the totals of waves p..3,
+// or plus those of waves 4..p-1): state wave w, lanes 0..31, takes channels
+// 32 w .. 32 w + 31.
 __device__ __forceinline__ void chunk_factors(Smem &sm, int par, int w, int lane) {
+    constexpr float LOG2E = 1.4426950408889634f;
     if (lane < 32) {
         const int c = 32 * w + lane;
         float x[NP];
 #pragma unroll
         for (int ww = 0; ww < NP; ++ww) x[ww] = sm.gsum[par][ww][c];
-        float gm = 0.f, gc = 0.f;
+        float below = 0.f;  // - sum of waves p..3, built downward from p = 3
 #pragma unroll
-        for (int ww = 0; ww < NP; ++ww) {
-            if (ww < 4) gm += x[ww];
-            gc += x[ww];
+        for (int ww = 3; ww >= 0; --ww) {
+            below -= x[ww];
+            sm.woff[par][ww][c] = LOG2E * below;
+        }
+        const float gm = -below;
+        float above = 0.f;  // sum of waves 4..p-1
+#pragma unroll
+        for (int ww = 4; ww < NP; ++ww) {
+            sm.woff[par][ww][c] = LOG2E * above;
+            above += x[ww];
         }
         sm.fm[par][c] = fast_exp(gm);
-        sm.fc[par][c] = fast_exp(gc - gm);
+        sm.fc[par][c] = fast_exp(above);
     }
 }
 
@@ -293,38 +325,19 @@ __device__ __forceinline__ void build_operands(Smem &sm, Raw &R, uint32_t bpad, 
     const int cg = lane & 15, tb = lane >> 4;
     const int ch0 = 8 * cg;
     const int r0 = 8 * p + 2 * tb;
-    // offset of this wave's first token from the reference row m = 31 (the end
-    // of wave 3's tokens): + sum of waves 4..p-1, or - sum of waves p..3
-    // (the four candidate wave totals are read at once and masked)
-    const int lo = p < 4 ? p : 4, hi = p < 4 ? 4 : p;
-    floatx4 ga[4], gb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        ga[j] = *reinterpret_cast<const floatx4 *>(&sm.gsum[par][lo + j][ch0]);
-        gb[j] = *reinterpret_cast<const floatx4 *>(&sm.gsum[par][lo + j][ch0 + 4]);
-    }
-    float d[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        d[e] = 0.f;
-        d[e + 4] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            d[e] += lo + j < hi ? ga[j][e] : 0.f;
-            d[e + 4] += lo + j < hi ? gb[j][e] : 0.f;
-        }
-    }
-    // exp(G - G_m) = 2^(log2(e) (pre + lc)), the scale folded into one fma
+    // this wave's offset to the reference row m = 31 (the end of wave 3's
+    // tokens), in log2 units
+    const floatx4 wa = *reinterpret_cast<const floatx4 *>(&sm.woff[par][p][ch0]);
+    const floatx4 wb = *reinterpret_cast<const floatx4 *>(&sm.woff[par][p][ch0 + 4]);
+    // exp(G - G_m) = 2^(log2(e) (ex + lc) + offset), the scale folded into fmas
     constexpr float LOG2E = 1.4426950408889634f;
     float pre[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pre[e] = LOG2E * (ex[e] + (p < 4 ? -d[e] : d[e]));
-    // channels ch0 .. ch0 + 3 and ch0 + 4 .. ch0 + 7 sit 8 positions apart in
-    // the permuted order
-    const int cpos = (ch0 & ~31) + perm32(ch0 & 31);
-    // one token row at a time (fewer live registers); Km of both rows is kept
-    // for the transposed tile
-    half8 hkm0, hkm1;
+    for (int e = 0; e < 4; ++e) {
+        pre[e] = __builtin_fmaf(ex[e], LOG2E, wa[e]);
+        pre[e + 4] = __builtin_fmaf(ex[e + 4], LOG2E, wb[e]);
+    }
+    // one token row at a time (fewer live registers)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         float kv[8], qv[8];
@@ -354,34 +367,13 @@ __device__ __forceinline__ void build_operands(Smem &sm, Raw &R, uint32_t bpad, 
             hkm[e] = (_Float16)(kv[e] * i);
             hqp[e] = (_Float16)(qv[e] * f);
         }
-        const int rb = (r0 + u) * PK + cpos;
-        *reinterpret_cast<half4 *>(&sm.kp[rb]) = hkp.lo;
-        *reinterpret_cast<half4 *>(&sm.kp[rb + 8]) = hkp.hi;
-        *reinterpret_cast<half4 *>(&sm.km[rb]) = hkm.lo;
-        *reinterpret_cast<half4 *>(&sm.km[rb + 8]) = hkm.hi;
-        *reinterpret_cast<half4 *>(&sm.qp[rb]) = hqp.lo;
-        *reinterpret_cast<half4 *>(&sm.qp[rb + 8]) = hqp.hi;
-        if (u == 0) hkm0 = hkm;
-        else hkm1 = hkm;
+        const int rb = (r0 + u) * PK + ch0;
+        *reinterpret_cast<half8 *>(&sm.kp[rb]) = hkp;
+        *reinterpret_cast<half8 *>(&sm.km[par][rb]) = hkm;
+        *reinterpret_cast<half8 *>(&sm.qp[rb]) = hqp;
     }
-    // Km^T: tokens r0, r0 + 1 sit next to each other in the permuted order
-    const int tp = 32 * (p >> 2) + 16 * (p & 1) + 4 * ((p >> 1) & 1) + 8 * (tb >> 1) + 2 * (tb & 1);
-    const int kb = tp >> 3, ko = tp & 7;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        half2v pr;
-        pr[0] = hkm0[e];
-        pr[1] = hkm1[e];
-        *reinterpret_cast<half2v *>(&sm.kmt[par][(ch0 + e) * PC + 8 * (kb ^ (cg & 7)) + ko]) = pr;
-    }
-    // V transposed: columns 8p .. 8p + 7, row lane (consecutive lanes write
-    // consecutive halves)
-    const uint32_t vw[4] = {R.v.x, R.v.y, R.v.z, R.v.w};  // zero past the end
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        sm.vt[(8 * p + 2 * e) * PV + lane] = (uint16_t)(vw[e] & 0xFFFFu);
-        sm.vt[(8 * p + 2 * e + 1) * PV + lane] = (uint16_t)(vw[e] >> 16);
-    }
+    // V: token lane, columns 8p .. 8p + 7 (zero past the end)
+    *reinterpret_cast<uint4 *>(&sm.vr[lane * PV + 8 * p]) = R.v;
     __builtin_amdgcn_sched_barrier(0);
     R.v = load16(nx.v, lof.v);
     __builtin_amdgcn_sched_barrier(0);
@@ -420,14 +412,15 @@ __device__ __forceinline__ floatx4 block_product_t(const _Float16 *lhs, const _F
 // Prep wave p: the chunk's Gram / query-key blocks.  Waves 0-3 take the
 // diagonal blocks (p, p) and the inverse (I + A_pp)^-1; waves 4-7 take the
 // twelve off-diagonal blocks (six Gram, six query-key), three each.
-__device__ __forceinline__ void prep_blocks(Smem &sm, int p, int lane) {
+__device__ __forceinline__ void prep_blocks(Smem &sm, int par, int p, int lane) {
+    const _Float16 *km = sm.km[par];
     const int l16 = lane & 15, lg = lane >> 4;
     if (p < 4) {
         // A_pp = Diag(beta) strict_lower(Kp Km^T) on this block, held twice:
         // in the A layout (lane: row l16, columns 4 lg .. +3; the transposed
         // product) and in the B layout (lane: column l16, rows 4 lg .. +3)
-        const floatx4 at = block_product_t(sm.kp, sm.km, p, p, lane);
-        const floatx4 ab = block_product(sm.kp, sm.km, p, p, lane);
+        const floatx4 at = block_product_t(sm.kp, km, p, p, lane);
+        const floatx4 ab = block_product(sm.kp, km, p, p, lane);
         const float br = sm.beta[16 * p + l16];
         const floatx4 bc = *reinterpret_cast<const floatx4 *>(&sm.beta[16 * p + 4 * lg]);
         half4 LA, LB;
@@ -436,7 +429,7 @@ __device__ __forceinline__ void prep_blocks(Smem &sm, int p, int lane) {
             LA[i] = (_Float16)(4 * lg + i < l16 ? br * at[i] : 0.f);
             LB[i] = (_Float16)(l16 < 4 * lg + i ? bc[i] * ab[i] : 0.f);
         }
-        const floatx4 pq = block_product_t(sm.qp, sm.km, p, p, lane);
+        const floatx4 pq = block_product_t(sm.qp, km, p, p, lane);
         half4 ph;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ph[i] = (_Float16)(4 * lg + i <= l16 ? pq[i] : 0.f);
@@ -465,7 +458,7 @@ __device__ __forceinline__ void prep_blocks(Smem &sm, int p, int lane) {
             const bool gram = o < 6;
             const int bi = oo < 1 ? 1 : (oo < 3 ? 2 : 3);
             const int bj = oo < 1 ? 0 : (oo < 3 ? oo - 1 : oo - 3);
-            const floatx4 acc = block_product_t(gram ? sm.kp : sm.qp, sm.km, bi, bj, lane);
+            const floatx4 acc = block_product_t(gram ? sm.kp : sm.qp, km, bi, bj, lane);
             const float sc = gram ? sm.beta[16 * bi + l16] : 1.f;
             half4 hv;
 #pragma unroll
@@ -551,7 +544,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
     const int nchunks = (eos - bos + C - 1) / C;
 
     // The two wave groups run separate loops with the same barrier sequence
-    // (two before the loop, two per chunk), so their registers never overlap.
+    // (three before the loop, two per chunk), so their registers never overlap.
     if (state_wave) {
         // S[cb] holds rows c = 16 cb + 4 lg + i, column 16 w + l16 of the tile;
         // element (c, column) of a state is at [c * VD + column]
@@ -564,12 +557,13 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
         for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                S[cb][i] = s0p ? s0p[(16 * cb + 4 * lg + i) * VD + col] : 0.f;
+                S[cb][i] = s0p ? s0p[sigma(cb, lg, i) * VD + col] : 0.f;
         // the initial state has landed before the loop, so the loop's waits
         // never cover the previous chunk's output stores
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
         chunk_factors(sm, 0, w, lane);  // chunk 0's (its channel totals are in)
+        __syncthreads();
         __syncthreads();
         for (int ci = 0; ci < nchunks; ++ci) {
             const int c0 = bos + ci * C;
@@ -580,7 +574,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             // and Qp S', and Y = Diag(beta) (V - Kp S')
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) {
-                const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.fm[par][16 * cb + 4 * lg]);
+                const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.fm[par][sigma(cb, lg, 0)]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[cb][i] *= f[i];
             }
@@ -615,13 +609,16 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             floatx4 Y[4];
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-                const uint2 vv = *reinterpret_cast<const uint2 *>(&sm.vt[(16 * w + l16) * PV + 16 * rb + 4 * lg]);
+                // V rows 16 rb + 4 lg + i of column 16 w + l16, transposed on read
+                const short4v vv = read_tr(&sm.vr[(16 * rb + 4 * lg + (l16 >> 2)) * PV + 16 * w + 4 * (l16 & 3)]);
                 const floatx4 bb = *reinterpret_cast<const floatx4 *>(&sm.beta[16 * rb + 4 * lg]);
-                Y[rb][0] = bb[0] * (bf16lo(vv.x) - X[rb][0]);
-                Y[rb][1] = bb[1] * (bf16hi(vv.x) - X[rb][1]);
-                Y[rb][2] = bb[2] * (bf16lo(vv.y) - X[rb][2]);
-                Y[rb][3] = bb[3] * (bf16hi(vv.y) - X[rb][3]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Y[rb][i] = bb[i] * (__uint_as_float((uint32_t)(uint16_t)vv[i] << 16) - X[rb][i]);
             }
+            // the next chunk's factors and offsets (its channel totals landed
+            // one iteration ago), for the prep waves' phase B
+            chunk_factors(sm, par ^ 1, w, lane);
             __syncthreads();
             // ---- phase B: (I + A) U = Y by 16-row blocks,
             // U_i = T_ii (Y_i - sum_{j<i} A_ij U_j), all in registers; the
@@ -637,8 +634,8 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             half8 km[8];
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
-                km[2 * cb] = frag8_kmt(sm.kmt[par], 16 * cb, 0, lane);
-                km[2 * cb + 1] = frag8_kmt(sm.kmt[par], 16 * cb, 1, lane);
+                km[2 * cb] = frag_kmT(sm.km[par], cb, 0, lane);
+                km[2 * cb + 1] = frag_kmT(sm.km[par], cb, 1, lane);
             }
             half4 U[4];
 #pragma unroll
@@ -660,9 +657,9 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
                 S[cb] = mma32(km[2 * cb], bu0, S[cb]);
-                km[2 * cb] = frag8_kmt(sm.kmt[par], 16 * (cb + 4), 0, lane);
+                km[2 * cb] = frag_kmT(sm.km[par], cb + 4, 0, lane);
                 S[cb] = mma32(km[2 * cb + 1], bu1, S[cb]);
-                km[2 * cb + 1] = frag8_kmt(sm.kmt[par], 16 * (cb + 4), 1, lane);
+                km[2 * cb + 1] = frag_kmT(sm.km[par], cb + 4, 1, lane);
             }
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb)
@@ -683,13 +680,10 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             }
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) {
-                const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.fc[par][16 * cb + 4 * lg]);
+                const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.fc[par][sigma(cb, lg, 0)]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[cb][i] *= f[i];
             }
-            // the next chunk's factors (its channel totals landed one
-            // iteration ago), while the prep waves finish its operands
-            chunk_factors(sm, par ^ 1, w, lane);
             // prefix snapshot when the state now covers a boundary
             if (snap.due(c0 - bos + L)) {
                 float *sp = snap.dest(io, h, H, KD * VD);
@@ -701,7 +695,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
 #pragma unroll
                     for (int cb = 0; cb < 8; ++cb) {
                         const floatx4 t = quad_transpose(S[cb], lane);
-                        *reinterpret_cast<floatx4 *>(&sp[(16 * cb + 4 * lg + (lane & 3)) * VD + col - (lane & 3)]) = t;
+                        *reinterpret_cast<floatx4 *>(&sp[sigma(cb, lg, lane & 3) * VD + col - (lane & 3)]) = t;
                     }
                 }
             }
@@ -712,10 +706,14 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sTp[(16 * cb + 4 * lg + i) * VD + col] = S[cb][i];
+                for (int i = 0; i < 4; ++i) sTp[sigma(cb, lg, i) * VD + col] = S[cb][i];
         }
     } else {
         const int p = w - 4;
+        // Waves are issued oldest first: prep waves 0-3 would always win the
+        // vector ALU against waves 4-7 on the same SIMD, and the chunk waits
+        // for the slowest prep wave; raising 4-7 evens the two out.
+        if (p >= 4) __builtin_amdgcn_s_setprio(1);
         const uint32_t gpad = pro_on<PM>(pro, PRO_GATE_LOGIT) ? BF16_NEG_INF_PAIR : 0u;
         const uint32_t bpad = pro_on<PM>(pro, PRO_BETA_LOGIT) ? (BF16_NEG_INF_PAIR & 0xFFFFu) : 0u;
         const LaneOffs lof = lane_offsets(H, p, lane);
@@ -740,6 +738,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             scan_partials<PM>(sm, rg, clen(0), gpad, 0, p, lane, lc, ex, pro, gsrc(1), lof);
         }
         __syncthreads();
+        __syncthreads();  // (chunk 0's offsets)
         if (nchunks > 0) {
             build_operands<PM>(sm, R, bpad, 0, p, lane, lc, ex, pro, src(1), lof);
             scan_partials<PM>(sm, rg, clen(1), gpad, 1, p, lane, lc, ex, pro, gsrc(2), lof);
@@ -747,7 +746,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
         __syncthreads();
         for (int ci = 0; ci < nchunks; ++ci) {
             // ---- phase A: this chunk's Gram / query-key blocks and diagonal inverses
-            prep_blocks(sm, p, lane);
+            prep_blocks(sm, ci & 1, p, lane);
             __syncthreads();
             // ---- phase B: the next chunk's operands and the decay sums of the
             // chunk after it; their input registers are refilled (for chunks
