@@ -22,6 +22,22 @@ def rel_err(x, ref) -> float:
     return float(np.max(np.abs(x - ref))) / rms if x.size else 0.0
 
 
+def rel_err_rounded(x, ref, ulp_rel: float) -> float:
+    """rel_err for an output stored in a narrower format: each element may
+    also carry that format's own rounding, up to ulp_rel |ref| (half an ulp of
+    bf16 is 2^-9 of the value; 2^-8 covers the kernel's own error moving an
+    element across a rounding boundary)."""
+    x = x.detach().cpu().double().numpy() if hasattr(x, "detach") else np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    assert np.all(np.isfinite(x)), "non-finite values in GPU output"
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    if not x.size:
+        return 0.0
+    excess = np.maximum(np.abs(x - ref) - ulp_rel * np.abs(ref), 0.0)
+    return float(np.max(excess)) / (rms if rms > 0.0 else 1.0)
+
+
 def to_gpu(d: dict) -> dict:
     return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
 

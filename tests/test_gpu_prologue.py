@@ -71,6 +71,27 @@ def test_prologue_chunk_fwd(dtype, K, two_pass, flags):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+@pytest.mark.parametrize("flags", [ALL, 2])
+def test_prologue_fused_many_heads(flags):
+    """The prologue on the single-pass kernel with 256 heads: all maps fixed at
+    compile time, and one map chosen at run time."""
+    B, H, T = 1, 256, 100
+    print(f"[case] prologue fused many heads flags={flags} B={B} T={T} H={H}", flush=True)
+    raw = inputs.draw_raw_fixed(62, B, T, H, 128, 128, "bf16", s0_std=0.1)
+    plain = inputs.draw_fixed(63, B, T, H, 128, 128, "bf16", g_lb=G_LB)
+    d = _mix(raw, plain, flags)
+    p = _prologue(flags, eps=1e-6 if flags & 1 else 0.0)
+    r = _oracle_inputs(d, p)
+    o_ref, s_ref = oracle.fixed(r["q"], r["k"], r["v"], r["g"], r["beta"], oracle.as_f64(d["s0"]))
+    x = to_gpu(d)
+    o, sT = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], initial_state=x["s0"],
+                          two_pass=False, prologue=p)
+    torch.cuda.synchronize()
+    eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+    report(f"prologue_fused_many_heads_f{flags}", o=eo, sT=es)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("two_pass", [True, False])
 def test_prologue_varlen_edge_lengths(two_pass):
     """Empty, single-token, chunk-edge and ragged sequences: the padding rows of
