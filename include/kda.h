@@ -33,7 +33,23 @@
  * bf16 chunked kernels factor the intra-chunk decay around the middle of the
  * chunk and hold the factors in fp16; outside this bound results are
  * unspecified (but every access stays in bounds).  The fp32-input kernels
- * evaluate every decay factor exactly and accept any g <= 0.
+ * evaluate every decay factor exactly and accept any g <= 0: a model whose
+ * decay goes below -0.25 per token (at chunk 64) must pass fp32 inputs.
+ *
+ * Magnitudes on the bf16 d = 128 kernels.  Their matrix-core operands are
+ * fp16 (11-bit significand, normal range 6.1e-5 .. 6.5e4); accumulation, the
+ * state between calls and the outputs are fp32.  The single-pass kernel
+ * (workspace_bytes == 0) also rounds the running state, scaled by
+ * exp(G_m) <= 1, to fp16 once per chunk, so values and states far below
+ * unit scale fall into fp16's subnormal range and lose relative precision:
+ * with unit-norm q and k its largest error stays within 2e-2 of the
+ * output's RMS (the accuracy the bf16 kernels are held to against an fp64
+ * evaluation of the recurrence) for value and state scales from 1e-2 to 1e3
+ * (at 1e-3 it is about 3e-2).  The two-pass path advances the state in fp32
+ * (decay and value terms), rounding it to fp16 only for the key-correction
+ * product, and stays within 2e-2 from 1e-4 to 1e3.  For smaller scales use
+ * the two-pass path or fp32 inputs, or rescale v and s0 (the recurrence is
+ * linear in them).
  *
  * Ownership and ordering.  The caller allocates every buffer; the library
  * allocates no device memory, keeps no state between calls and is
