@@ -85,8 +85,10 @@ def test_bf16_d128_decay_stress(g_mode, g_lb, path):
 
 @pytest.mark.parametrize("path", list(PATHS))
 def test_bf16_output_dtype(path):
+    # held to the 2e-2 bound on the arithmetic; the output's own bf16 rounding
+    # (at most half an ulp of each value) is allowed on top
     _fixed_case("bf16_out", 11, 1, 256, 2, 128, 128, "bf16", s0_std=0.1,
-                out_dtype=torch.bfloat16, tol=3e-2, path=path)
+                out_dtype=torch.bfloat16, path=path)
 
 
 @pytest.mark.parametrize("H,expect_two_pass", [(48, True), (49, False)])
