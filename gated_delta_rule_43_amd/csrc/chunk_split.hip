@@ -979,15 +979,18 @@ int max_chunks(int N, int totalT, int fixedT, bool varlen) {
 // The two-pass path serves bf16 inputs with (K, V, C) = (128, 128, 64) and
 // fewer than 127 sequences.  It beats the single-pass kernel while its pass-2
 // workgroups (8 per unit) leave the GPU underfilled and sequences are long
-// enough to amortise the extra launches: up to 32 units, at least 8 chunks
-// per sequence on average.
+// enough to amortise the extra launches (MI355X, warm): up to 24 units, or 32
+// when sequences average at most 16 chunks (at 32 units: 42 vs 51 us at
+// T = 1024, 194 vs 178 us at T = 4096), and at least 4 chunks per sequence on
+// average.
 bool chunk_split_supported(int N, int H, int K, int V, int Cc) {
     return K == KD && V == VD && Cc == C && N > 0 && N < 127 && H > 0;
 }
 
 bool chunk_split_recommended(int N, int totalT, int H, int K, int V, int Cc) {
-    return chunk_split_supported(N, H, K, V, Cc) && (long long)N * H <= 48 &&
-           (long long)totalT >= 4LL * C * N;
+    if (!chunk_split_supported(N, H, K, V, Cc) || (long long)totalT < 4LL * C * N) return false;
+    const long long units = (long long)N * H;
+    return units <= 24 || (units <= 32 && (long long)totalT <= 16LL * C * N);
 }
 
 size_t chunk_split_workspace_bytes(int N, int totalT, int H) {

@@ -375,8 +375,9 @@ size_t kda_bwd_workspace_bytes(int N, int total_T, int H, int K, int V, int chun
 
 /* Workspace bytes for the recommended implementation of a forward call over
  * N sequences, total_T tokens: nonzero (the two-pass size) when the two-pass
- * path is supported and expected to be faster (bf16 inputs assumed; at most
- * 48 units, sequences of at least 4 chunks on average), else 0. */
+ * path is supported and expected to be faster (bf16 inputs assumed; at least
+ * 4 chunks per sequence on average, and at most 24 (sequence, head) units, or
+ * 32 when sequences average at most 16 chunks), else 0. */
 size_t kda_workspace_bytes(int N, int total_T, int H, int K, int V, int chunk);
 
 /* Workspace bytes that select the two-pass path whenever it is supported:

@@ -91,11 +91,13 @@ def test_bf16_output_dtype(path):
                 out_dtype=torch.bfloat16, path=path)
 
 
-@pytest.mark.parametrize("H,expect_two_pass", [(48, True), (49, False)])
-def test_bf16_d128_default_choice_at_the_unit_switch(H, expect_two_pass):
+@pytest.mark.parametrize("T,H,expect_two_pass", [(600, 32, True), (600, 33, False),
+                                                 (1100, 24, True), (1100, 25, False)])
+def test_bf16_d128_default_choice_at_the_unit_switch(T, H, expect_two_pass):
     # with the default arguments the library recommends the two-pass path up to
-    # 48 (sequence, head) units of long enough sequences, the fused kernel above
-    B, T = 1, 600
+    # 32 (sequence, head) units of sequences of at most 16 chunks, up to 24
+    # units of longer ones, and the fused kernel above
+    B = 1
     assert (kda.workspace_bytes(B, B * T, H, 128, 128, 64) > 0) == expect_two_pass
     print(f"[case] default choice B={B} T={T} H={H} two_pass={expect_two_pass}", flush=True)
     d = inputs.draw_fixed(16, B, T, H, 128, 128, "bf16", s0_std=0.1)
