@@ -68,16 +68,12 @@ bool fits(long long rows, long long H, long long D) {
 
 kda_status_t from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
-// Range checks of the prologue's scalars.  chunk > 0 with bf16 inputs: the
-// gate's lower bound must keep the chunked kernels' fp16 decay factors in
-// range (g_lb * chunk / 2 <= 8).
-kda_status_t make_prologue(unsigned flags, float glb, float eps, kda_dtype_t in_dtype, int chunk,
-                           kda::Prologue &pro) {
+// Range checks of the prologue's scalars.
+kda_status_t make_prologue(unsigned flags, float glb, float eps, kda::Prologue &pro) {
     if (flags & ~kda::PRO_ALL) return KDA_ERR_VALUE;
     if (!std::isfinite(eps) || eps < 0.f) return KDA_ERR_VALUE;
     if (flags & kda::PRO_GATE_LOGIT) {
         if (!std::isfinite(glb) || glb < 0.f) return KDA_ERR_VALUE;
-        if (chunk > 0 && in_dtype == KDA_BF16 && (double)glb * chunk > 16.0) return KDA_ERR_VALUE;
     }
     pro.flags = flags;
     pro.glb = glb;
@@ -117,8 +113,15 @@ kda_status_t run_fwd(const void *q, const void *k, const void *v, const void *g,
                      bool two_pass, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool in_bf16 = in_dtype == KDA_BF16, out_bf16 = out_dtype == KDA_BF16;
+    // A declared gate bound beyond what the fp16 decay factors of the bf16
+    // chunked kernels hold (g_lb * chunk / 2 > 8) sends the call to the
+    // exact-decay kernel, which reads the same bf16 inputs.
+    const bool steep = (pro.flags & kda::PRO_GATE_LOGIT) && (double)pro.glb * chunk > 16.0;
     hipError_t e;
-    if (in_bf16 && two_pass && kda::chunk_split_supported(N, H, K, V, chunk))
+    if (steep)
+        e = kda::launch_chunk_valu(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H, K, V,
+                                   chunk, in_bf16, out_bf16, st);
+    else if (in_bf16 && two_pass && kda::chunk_split_supported(N, H, K, V, chunk))
         e = kda::launch_chunk_split(q, k, v, g, beta, io, pro, o, cu, N, fixedT, totalT, H,
                                     out_bf16, workspace, st);
     else if (in_bf16 && kda::chunk_mfma_supported(K, V, chunk))
@@ -220,7 +223,7 @@ kda_status_t kda_chunk_fwd_prologue(const void *q, const void *k, const void *v,
                                   out_dtype);
     if (s != KDA_OK) return s;
     kda::Prologue pro;
-    s = make_prologue(prologue, gate_lower_bound, norm_eps, in_dtype, chunk, pro);
+    s = make_prologue(prologue, gate_lower_bound, norm_eps, pro);
     if (s != KDA_OK) return s;
     bool two_pass;
     s = check_workspace(workspace, workspace_bytes,
@@ -252,7 +255,7 @@ kda_status_t kda_varlen_fwd_prologue(const void *q, const void *k, const void *v
                                   out_dtype);
     if (s != KDA_OK) return s;
     kda::Prologue pro;
-    s = make_prologue(prologue, gate_lower_bound, norm_eps, in_dtype, chunk, pro);
+    s = make_prologue(prologue, gate_lower_bound, norm_eps, pro);
     if (s != KDA_OK) return s;
     if (N > 0 && !cu_seqlens) return KDA_ERR_NULL;
     bool two_pass;
@@ -307,7 +310,7 @@ kda_status_t kda_varlen_fwd_paged_prologue(
                                   out_dtype);
     if (s != KDA_OK) return s;
     kda::Prologue pro;
-    s = make_prologue(prologue, gate_lower_bound, norm_eps, in_dtype, chunk, pro);
+    s = make_prologue(prologue, gate_lower_bound, norm_eps, pro);
     if (s != KDA_OK) return s;
     if (!pool) return KDA_ERR_NULL;
     if (!pool_ok(pool_slots, H, K, V)) return KDA_ERR_SHAPE;
@@ -365,7 +368,7 @@ kda_status_t kda_decode_step_prologue(const void *q, const void *k, const void *
     if (!fits(N, H, (long long)K * V)) return KDA_ERR_SHAPE;
     if (!((K == 128 && V == 128) || (K == 32 && V == 32))) return KDA_ERR_UNSUPPORTED;
     kda::Prologue pro;
-    kda_status_t s = make_prologue(prologue, gate_lower_bound, norm_eps, in_dtype, 0, pro);
+    kda_status_t s = make_prologue(prologue, gate_lower_bound, norm_eps, pro);
     if (s != KDA_OK) return s;
     if (N == 0) return KDA_OK;
     if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
@@ -395,7 +398,7 @@ kda_status_t kda_decode_step_paged_prologue(const void *q, const void *k, const 
     if (!((K == 128 && V == 128) || (K == 32 && V == 32))) return KDA_ERR_UNSUPPORTED;
     if (!pool_ok(pool_slots, H, K, V)) return KDA_ERR_SHAPE;
     kda::Prologue pro;
-    kda_status_t s = make_prologue(prologue, gate_lower_bound, norm_eps, in_dtype, 0, pro);
+    kda_status_t s = make_prologue(prologue, gate_lower_bound, norm_eps, pro);
     if (s != KDA_OK) return s;
     if (N == 0) return KDA_OK;
     if (!q || !k || !v || !g || !beta || !pool || !slot_in || !slot_out || !o) return KDA_ERR_NULL;
@@ -428,7 +431,7 @@ kda_status_t kda_decode_multi_paged_prologue(const void *q, const void *k, const
     if (!((K == 128 && V == 128) || (K == 32 && V == 32))) return KDA_ERR_UNSUPPORTED;
     if (!pool_ok(pool_slots, H, K, V)) return KDA_ERR_SHAPE;
     kda::Prologue pro;
-    kda_status_t s = make_prologue(prologue, gate_lower_bound, norm_eps, in_dtype, 0, pro);
+    kda_status_t s = make_prologue(prologue, gate_lower_bound, norm_eps, pro);
     if (s != KDA_OK) return s;
     if (N == 0 || T == 0) return KDA_OK;
     if (!q || !k || !v || !g || !beta || !pool || !slot_in || !slot_out || !o) return KDA_ERR_NULL;

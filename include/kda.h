@@ -34,7 +34,8 @@
  * chunk and hold the factors in fp16; outside this bound results are
  * unspecified (but every access stays in bounds).  The fp32-input kernels
  * evaluate every decay factor exactly and accept any g <= 0: a model whose
- * decay goes below -0.25 per token (at chunk 64) must pass fp32 inputs.
+ * decay goes below -0.25 per token (at chunk 64) must pass fp32 inputs, or
+ * bf16 gate logits with its bound through a _prologue entry point (below).
  *
  * Magnitudes on the bf16 d = 128 kernels.  Their matrix-core operands are
  * fp16 (11-bit significand, normal range 6.1e-5 .. 6.5e4); accumulation, the
@@ -276,8 +277,12 @@ kda_status_t kda_decode_multi_paged(const void *q, const void *k, const void *v,
  *   KDA_PROLOGUE_BETA_LOGIT beta holds logits b; the value used is sigmoid(b).
  * prologue = 0 is the plain entry point.  Range checks (KDA_ERR_VALUE):
  * unknown bits; norm_eps negative or not finite; with GATE_LOGIT,
- * gate_lower_bound negative or not finite, or, for bf16 inputs of a chunked
- * call, gate_lower_bound * chunk > 16 (the numerical precondition above).
+ * gate_lower_bound negative or not finite.  With GATE_LOGIT and
+ * gate_lower_bound * chunk > 16 (a decay steeper than the bf16 chunked
+ * kernels' fp16 factors hold, see the numerical precondition above), a
+ * chunked call runs the exact-decay kernel whatever in_dtype is (fp32
+ * arithmetic, every decay factor evaluated exactly: correct for any bound,
+ * slower), so bf16 inputs with, for example, g_lb = 2 at chunk 64 are served.
  * Everything else (shapes, layouts, states, workspace, errors) is as for the
  * entry point of the same name without the suffix.
  */

@@ -14,7 +14,7 @@ from tests.test_gpu_paged import _expected_paged_fwd, _pool
 
 pytestmark = pytest.mark.gpu
 
-G_LB = 0.25  # the largest gate bound the bf16 chunked kernels accept at chunk 64
+G_LB = 0.25  # the largest gate bound the bf16 chunked kernels hold in fp16 at chunk 64
 ALL = 7
 
 
@@ -89,6 +89,50 @@ def test_prologue_fused_many_heads(flags):
     torch.cuda.synchronize()
     eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
     report(f"prologue_fused_many_heads_f{flags}", o=eo, sT=es)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("glb,flags", [(2.0, 2), (2.0, ALL), (0.5, 2)])
+def test_prologue_steep_gate_bf16(glb, flags):
+    """bf16 inputs with a gate bound past the fp16 factors' range (g in
+    (-2, 0) at chunk 64): the call runs the exact-decay kernel and meets the
+    bf16 bound, with and without a workspace (which would otherwise select
+    the two-pass path)."""
+    B, H, T = 2, 3, 300
+    print(f"[case] prologue steep gate bf16 glb={glb} flags={flags} B={B} T={T} H={H}", flush=True)
+    raw = inputs.draw_raw_fixed(64, B, T, H, 128, 128, "bf16", s0_std=0.1)
+    plain = inputs.draw_fixed(65, B, T, H, 128, 128, "bf16", g_lb=G_LB)
+    d = _mix(raw, plain, flags)
+    p = _prologue(flags, eps=1e-6 if flags & 1 else 0.0, glb=glb)
+    r = _oracle_inputs(d, p)
+    assert float(r["g"].min()) < -0.25              # past the fp16-factor bound
+    o_ref, s_ref = oracle.fixed(r["q"], r["k"], r["v"], r["g"], r["beta"], oracle.as_f64(d["s0"]))
+    x = to_gpu(d)
+    for two_pass in (False, True):
+        o, sT = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], initial_state=x["s0"],
+                              two_pass=two_pass, prologue=p)
+        torch.cuda.synchronize()
+        eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+        report(f"prologue_steep_bf16_glb{glb}_f{flags}_tp{two_pass}", o=eo, sT=es)
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_prologue_steep_gate_bf16_varlen():
+    """The same through the packed entry point, with edge lengths."""
+    lengths = [0, 1, 63, 64, 65, 200]
+    print(f"[case] prologue steep gate bf16 varlen lengths={lengths}", flush=True)
+    d = inputs.draw_raw_varlen(66, 2, 128, 128, "bf16", lengths, s0_std=0.1)
+    p = _prologue(ALL, eps=1e-6, glb=2.0)
+    r = _oracle_inputs(d, p)
+    cu = d["cu_seqlens"].numpy().astype(np.int64)
+    o_ref, s_ref = oracle.recurrence(r["q"], r["k"], r["v"], r["g"], r["beta"], cu,
+                                     oracle.as_f64(d["s0"]))
+    x = to_gpu(d)
+    o, sT = kda.varlen_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"],
+                           initial_state=x["s0"], prologue=p)
+    torch.cuda.synchronize()
+    eo, es = rel_err(o, o_ref), rel_err(sT, s_ref)
+    report("prologue_steep_bf16_varlen", o=eo, sT=es)
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
