@@ -285,7 +285,7 @@ __device__ __forceinline__ void scan_partials(Smem &sm, uint4 *rg, int L, uint32
 // From the prep waves' channel totals of parity par, the chunk's per-channel
 // factors exp(G_m) and exp(G_C - G_m) and each prep wave's offset to the
 // reference row, log2(e) (G_{8p - 1} - G_m) (minus the totals of waves p..3,
-// or plus those of waves 4..p-1): state wave w, lanes 0..31, takes channels
+// or plus those of waves 4..p-1): channel group w (0..3), lanes 0..31, takes channels
 // 32 w .. 32 w + 31.
 __device__ __forceinline__ void chunk_factors(Smem &sm, int par, int w, int lane) {
     constexpr float LOG2E = 1.4426950408889634f;
@@ -562,7 +562,6 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
         // never cover the previous chunk's output stores
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
-        chunk_factors(sm, 0, w, lane);  // chunk 0's (its channel totals are in)
         __syncthreads();
         __syncthreads();
         for (int ci = 0; ci < nchunks; ++ci) {
@@ -616,9 +615,6 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
                 for (int i = 0; i < 4; ++i)
                     Y[rb][i] = bb[i] * (__uint_as_float((uint32_t)(uint16_t)vv[i] << 16) - X[rb][i]);
             }
-            // the next chunk's factors and offsets (its channel totals landed
-            // one iteration ago), for the prep waves' phase B
-            chunk_factors(sm, par ^ 1, w, lane);
             __syncthreads();
             // ---- phase B: (I + A) U = Y by 16-row blocks,
             // U_i = T_ii (Y_i - sum_{j<i} A_ij U_j), all in registers; the
@@ -738,7 +734,8 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             scan_partials<PM>(sm, rg, clen(0), gpad, 0, p, lane, lc, ex, pro, gsrc(1), lof);
         }
         __syncthreads();
-        __syncthreads();  // (chunk 0's offsets)
+        if (p >= 4) chunk_factors(sm, 0, p - 4, lane);  // chunk 0's (its channel totals are in)
+        __syncthreads();
         if (nchunks > 0) {
             build_operands<PM>(sm, R, bpad, 0, p, lane, lc, ex, pro, src(1), lof);
             scan_partials<PM>(sm, rg, clen(1), gpad, 1, p, lane, lc, ex, pro, gsrc(2), lof);
@@ -747,6 +744,9 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
         for (int ci = 0; ci < nchunks; ++ci) {
             // ---- phase A: this chunk's Gram / query-key blocks and diagonal inverses
             prep_blocks(sm, ci & 1, p, lane);
+            // the next chunk's factors and offsets (its channel totals landed
+            // one iteration ago), for phase B: waves 4-7, whose blocks finish first
+            if (p >= 4) chunk_factors(sm, (ci & 1) ^ 1, p - 4, lane);
             __syncthreads();
             // ---- phase B: the next chunk's operands and the decay sums of the
             // chunk after it; their input registers are refilled (for chunks
