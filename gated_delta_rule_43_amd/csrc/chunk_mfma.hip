@@ -27,20 +27,23 @@
 //    (rows in the order that makes two accumulator blocks one fp16 B
 //    fragment).  Per chunk (phase A) it forms S', takes its B fragments
 //    straight from the accumulators and forms Kp S' and, transposed,
-//    (Qp S')^T with v_mfma_f32_16x16x32_f16, plus the next chunk's
-//    per-channel factors; then (phase B) it solves (I + A) U = Y by 16-row
-//    block substitution in registers (the 16x16 accumulator layout is the B
-//    layout of v_mfma_f32_16x16x16_f16), advances the state with Km^T U (Km^T
-//    read from the Km tile by the transposing LDS read ds_read_b64_tr_b16),
-//    adds (P U)^T to the transposed output and stores four consecutive columns
-//    of an output row per lane.
-//  * prep waves 4-11: prep wave p owns tokens 8p .. 8p + 7 of a chunk.  In
-//    phase A they form the current chunk's Gram and query-key blocks and the
-//    16 x 16 diagonal inverses (I + A_ii)^-1 (a product form on the matrix
-//    cores); in phase B they build the next chunk's fp16 operand tiles
-//    (exponentials of the running decay sums), take the running decay sums of
-//    the chunk after it, and refill their input registers from buffer loads as
-//    the old contents are consumed.
+//    (Qp S')^T with v_mfma_f32_16x16x32_f16; then (phase B) it solves
+//    (I + A) U = Y by 16-row block substitution in registers (the 16x16
+//    accumulator layout is the B layout of v_mfma_f32_16x16x16_f16), advances
+//    the state with Km^T U (Km^T read from the Km tile by the transposing LDS
+//    read ds_read_b64_tr_b16), adds (P U)^T to the transposed output and
+//    stages it in LDS.
+//  * prep waves 4-11: prep wave p owns tokens 8p .. 8p + 7 of a chunk (a
+//    lane holds two channels of all eight).  In phase A they form the current
+//    chunk's Gram and query-key blocks and the 16 x 16 diagonal inverses
+//    (I + A_ii)^-1 (a product form on the matrix cores), and waves 4-7 the
+//    next chunk's per-channel factors; in phase B they build the next chunk's
+//    fp16 operand tiles (exponentials of the running decay sums), take the
+//    running decay sums of the chunk after it, refill their input registers
+//    from buffer loads as the old contents are consumed, and waves 4-7 store
+//    the previous chunk's staged output as whole rows (each store instruction
+//    then covers whole cache lines, where the accumulator layout gives a
+//    quarter row per lane group).
 // Packed sequences are dealt to workgroups longest first.
 #include "kda_mfma.hpp"
 #include "prologue.hpp"
@@ -59,6 +62,7 @@ constexpr int PK = 144;  // LDS pitch (halves) of [64][128] fp16 tiles
 constexpr int P4 = 68;   // LDS pitch (halves) of [64][64] fp16 tiles read as 8-byte fragments
 constexpr int PI = 20;   // LDS pitch (halves) of 16 x 16 fp16 blocks
 constexpr int PV = 72;   // LDS pitch (halves) of the V tile
+constexpr int PO = 68;   // LDS pitch (floats) of the output staging tile
 
 // State rows.  Accumulator block cb of a state wave holds, in lane group
 // g = lane >> 4, element i, the state row (key channel)
@@ -67,7 +71,7 @@ constexpr int PV = 72;   // LDS pitch (halves) of the V tile
 // 32 k + 8 g .. 32 k + 8 g + 7: exactly the contraction indices of a 16x16x32
 // B fragment.  The state thus serves as the B operand of Kp S' and Qp S'
 // straight from the accumulators while Kp, Qp and Km keep their channels in
-// natural order (a token row of eight channels is one 16-byte store).
+// natural order (the layout every reader of the tiles expects).
 __device__ __forceinline__ int sigma(int cb, int g, int i) {
     return 32 * (cb >> 1) + 8 * g + 4 * (cb & 1) + i;
 }
@@ -86,6 +90,8 @@ struct Smem {
     float fc[2][KD];            // exp(G_C - G_m), by chunk parity
     float gsum[2][NP][KD];      // prep waves: per-wave channel sums of g, by chunk parity
     float woff[2][NP][KD];      // log2(e) (G at prep wave p's first token - G_m), by parity
+    float ost[2][C * PO];       // the chunk's output tile [r][j], staged for whole-row stores,
+                                // by chunk parity
 };
 
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -128,17 +134,18 @@ __device__ __forceinline__ half8 cat8(half4 a, half4 b) {
 }
 
 // One chunk's inputs, held in a prep wave's registers ahead of use.
-// Lane (cg = lane & 15, tb = lane >> 4) of prep wave p holds channels
-// 8 cg .. 8 cg + 7 of tokens 8p + 2 tb and 8p + 2 tb + 1 (16-byte loads, each
-// instruction reading four whole 256-byte rows).  The loads go through buffer
-// resources whose extent ends at the chunk's last token, so rows past a short
-// chunk's end read as zero without touching memory, and all address
-// arithmetic but one scalar base per chunk is fixed for the whole kernel.
+// Lane l of prep wave p holds channels 2 l and 2 l + 1 of tokens 8 p .. 8 p + 7
+// (one 4-byte load per token row, each instruction reading one whole 256-byte
+// row), so the running decay sum over a wave's tokens stays inside the lane.
+// The loads go through buffer resources whose extent ends at the chunk's last
+// token, so rows past a short chunk's end read as zero without touching
+// memory, and all address arithmetic but one scalar base per chunk is fixed
+// for the whole kernel.
 struct Raw {
-    uint4 q[2], k[2];
-    uint4 v;         // V tile piece: row lane, columns 8p .. 8p + 7
-    uint32_t beta;   // beta of token lane (used by prep wave 0)
-    int L;           // the chunk's length
+    uint32_t q[8], k[8];  // token 8 p + t: bf16 channels 2 l (low half) and 2 l + 1
+    uint4 v;              // V tile piece: row 8 p + (l >> 3), columns 8 (l & 7) .. + 7
+    uint32_t beta;        // beta of token lane (used by prep wave 0)
+    int L;                // the chunk's length
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -154,28 +161,32 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
     return make_uint4(x.x, x.y, x.z, x.w);
 }
 
-// Byte offsets, inside a chunk, of one lane's loads (the same for every chunk).
+__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// Byte offsets, inside a chunk, of one lane's loads (the same for every chunk;
+// the whole offset is in the lane's register, where the extent check sees it).
 struct LaneOffs {
-    uint32_t row[2];  // q / k / g: tokens 8p + 2 tb + u, channels 8 cg ..
-    uint32_t v;       // V: token lane
+    uint32_t row[8];  // q / k / g: token 8p + t, channels 2 l, 2 l + 1
+    uint32_t v;       // V: token 8 p + (l >> 3), columns 8 (l & 7) .. + 7
     uint32_t beta;    // beta: token lane
 };
 
 __device__ __forceinline__ LaneOffs lane_offsets(int H, int p, int lane) {
-    const int cg = lane & 15, tb = lane >> 4;
     LaneOffs o;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) o.row[u] = (uint32_t)((8 * p + 2 * tb + u) * H * KD * 2 + 16 * cg);
-    o.v = (uint32_t)(lane * H * VD * 2);
+    for (int t = 0; t < 8; ++t) o.row[t] = (uint32_t)((8 * p + t) * H * KD * 2 + 4 * lane);
+    o.v = (uint32_t)((8 * p + (lane >> 3)) * H * VD * 2 + 16 * (lane & 7));
     o.beta = (uint32_t)(lane * H * 2);
     return o;
 }
 
-__device__ __forceinline__ void load_g(uint4 *rg, const uint16_t *g, int c0, int L, int H, int h,
+__device__ __forceinline__ void load_g(uint32_t *rg, const uint16_t *g, int c0, int L, int H, int h,
                                        const LaneOffs &lof) {
     const auto r = extent(g + ((size_t)c0 * H + h) * KD, (uint32_t)(L * H * KD * 2));
 #pragma unroll
-    for (int u = 0; u < 2; ++u) rg[u] = load16(r, lof.row[u]);
+    for (int t = 0; t < 8; ++t) rg[t] = load4(r, lof.row[t]);
 }
 
 __device__ __forceinline__ void load_raw(Raw &R, const uint16_t *q, const uint16_t *k,
@@ -185,12 +196,12 @@ __device__ __forceinline__ void load_raw(Raw &R, const uint16_t *q, const uint16
     const uint32_t rows = (uint32_t)(L * H * KD * 2);
     const auto rq = extent(q + cb, rows), rk = extent(k + cb, rows);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        R.q[u] = load16(rq, lof.row[u]);
-        R.k[u] = load16(rk, lof.row[u]);
+    for (int t = 0; t < 8; ++t) {
+        R.q[t] = load4(rq, lof.row[t]);
+        R.k[t] = load4(rk, lof.row[t]);
     }
-    const auto rv = extent(v + ((size_t)c0 * H + h) * VD + vt * VT + 8 * p,
-                           (uint32_t)((L - 1) * H * VD * 2 + 16));
+    const auto rv = extent(v + ((size_t)c0 * H + h) * VD + vt * VT,
+                           (uint32_t)((L - 1) * H * VD * 2 + 2 * VT));
     R.v = load16(rv, lof.v);
     const auto rb = extent(beta + (size_t)c0 * H + h, (uint32_t)((L - 1) * H * 2 + 2));
     R.beta = p == 0 ? __builtin_amdgcn_raw_buffer_load_b16(rb, lof.beta, 0, 0) : 0u;
@@ -213,7 +224,7 @@ __device__ __forceinline__ Src chunk_src(const uint16_t *q, const uint16_t *k, c
     Src s;
     s.q = extent(q + cb, rows);
     s.k = extent(k + cb, rows);
-    s.v = extent(v + ((size_t)c0 * H + h) * VD + vt * VT + 8 * p, (uint32_t)((L - 1) * H * VD * 2 + 16));
+    s.v = extent(v + ((size_t)c0 * H + h) * VD + vt * VT, (uint32_t)((L - 1) * H * VD * 2 + 2 * VT));
     s.beta = extent(beta + (size_t)c0 * H + h, (uint32_t)((L - 1) * H * 2 + 2));
     s.L = L;
     return s;
@@ -224,62 +235,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gate_src(const uint16_t *g, in
     return extent(g + ((size_t)c0 * H + h) * KD, (uint32_t)(L * H * KD * 2));
 }
 
-// The lane values of the even and of the odd 16-lane row of this lane's row
-// pair (rows 0-1, 2-3), and of the lower and upper row pairs, through the
-// row-swapping permutes (v_permlane16_swap / v_permlane32_swap).
-__device__ __forceinline__ void pair_rows(float x, float &even, float &odd) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    even = __uint_as_float(r[0]);
-    odd = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void half_rows(float x, float &lower, float &upper) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    lower = __uint_as_float(r[0]);
-    upper = __uint_as_float(r[1]);
-}
-
-// Prep wave p, first half of the running log-decay sum: lc = running sum over
-// this lane's two tokens, then the exclusive prefix ex over the wave's four
-// 16-lane rows (token pairs; lanes 16 apart share channels) by row permutes.
-// The wave's channel totals go to LDS.  Rows at or past L read as `pad`.
+// Prep wave p, first half of the running log-decay sum: lc[t] = sum of g over
+// tokens 8p .. 8p + t for this lane's two channels (inside the lane), and the
+// wave's channel totals to LDS.  Rows at or past L read as `pad`.
 // PM (a ProMode): rg holds gate logits when the prologue's gate map applies.
 template <int PM>
-__device__ __forceinline__ void scan_partials(Smem &sm, uint4 *rg, int L, uint32_t pad,
-                                              int par, int p, int lane, float (*lc)[8], float *ex,
+__device__ __forceinline__ void scan_partials(Smem &sm, uint32_t *rg, int L, uint32_t pad,
+                                              int par, int p, int lane, float (*lc)[2],
                                               const Prologue &pro, __amdgpu_buffer_rsrc_t gnext,
                                               const LaneOffs &lof) {
-    const int cg = lane & 15, tb = lane >> 4;
-    const uint4 pad4 = make_uint4(pad, pad, pad, pad);
     // rows past the end loaded as zero: no decay, except through the gate map
     const bool gl = pro_on<PM>(pro, PRO_GATE_LOGIT);
-    unpack8(gl && 8 * p + 2 * tb >= L ? pad4 : rg[0], lc[0]);
-    unpack8(gl && 8 * p + 2 * tb + 1 >= L ? pad4 : rg[1], lc[1]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t w = gl && 8 * p + t >= L ? pad : rg[t];
+        lc[t][0] = bf16lo(w);
+        lc[t][1] = bf16hi(w);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) rg[u] = load16(gnext, lof.row[u]);  // the next chunk's gates
+    for (int t = 0; t < 8; ++t) rg[t] = load4(gnext, lof.row[t]);  // the next chunk's gates
     __builtin_amdgcn_sched_barrier(0);
     if (gl) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            lc[0][e] = gate_from_logit(lc[0][e], pro.glb);
-            lc[1][e] = gate_from_logit(lc[1][e], pro.glb);
+        for (int t = 0; t < 8; ++t) {
+            lc[t][0] = gate_from_logit(lc[t][0], pro.glb);
+            lc[t][1] = gate_from_logit(lc[t][1], pro.glb);
         }
     }
-    float tot[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        lc[1][e] += lc[0][e];
-        const float loc = lc[1][e];
-        float ev, od, lower, upper;
-        pair_rows(loc, ev, od);
-        half_rows(ev + od, lower, upper);
-        ex[e] = ((tb & 1) ? ev : 0.f) + (tb >= 2 ? lower : 0.f);
-        tot[e] = lower + upper;
+    for (int t = 1; t < 8; ++t) {
+        lc[t][0] += lc[t - 1][0];
+        lc[t][1] += lc[t - 1][1];
     }
-    if (tb == 0) {
-        *reinterpret_cast<floatx4 *>(&sm.gsum[par][p][8 * cg]) = floatx4{tot[0], tot[1], tot[2], tot[3]};
-        *reinterpret_cast<floatx4 *>(&sm.gsum[par][p][8 * cg + 4]) = floatx4{tot[4], tot[5], tot[6], tot[7]};
-    }
+    *reinterpret_cast<float2 *>(&sm.gsum[par][p][2 * lane]) = make_float2(lc[7][0], lc[7][1]);
 }
 
 // From the prep waves' channel totals of parity par, the chunk's per-channel
@@ -312,68 +301,119 @@ __device__ __forceinline__ void chunk_factors(Smem &sm, int par, int w, int lane
     }
 }
 
-// Prep wave p, second half: combine the wave totals into G - G_m for this
-// lane's tokens and write the fp16 operand tiles of the chunk (after the
-// prologue's normalisation of q and k, whose 128 channels of a token lie in
-// one 16-lane DPP row).
+
+// Sums over the 64 lanes of a wave of eight values per lane, by halving
+// exchanges: lanes 32 apart (v_permlane32_swap) leave four sums per lane,
+// 16-lane rows (v_permlane16_swap) two, lanes 8 apart (DPP row rotate) one,
+// then quad and half-row DPP steps finish the 8-lane groups.  Lane
+// 8 j + i ends with the total of value j.  The totals are returned as
+// wave-uniform values read from lanes 0, 8, .., 56.
+__device__ __forceinline__ void wave_sums8(const float *x, float *tot, int lane) {
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[j + 4]), false, false);
+        y[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // lanes < 32: value j, else j + 4
+    }
+    float z[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[j]), __float_as_uint(y[j + 2]), false, false);
+        z[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // even rows: j (+4), odd rows: j + 2 (+4)
+    }
+    const bool up = (lane & 8) != 0;
+    const float keep = up ? z[1] : z[0], give = up ? z[0] : z[1];
+    // row_ror:8 -- lane l of a row reads lane (l + 8) mod 16 of it
+    float u = keep + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, give), 0x128, 0xF, 0xF, false));
+    u += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, u), 0xB1, 0xF, 0xF, false));
+    u += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, u), 0x4E, 0xF, 0xF, false));
+    u += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, u), 0x141, 0xF, 0xF, false));
+    // lane 8 j holds value (4 (j >= 4) + 2 (j & 2 ? 1 : 0) + (j & 1)) = j
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tot[j] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(u), 8 * j));
+}
+
+// Prep wave p, second half: exp(G - G_m) for this lane's tokens from the
+// running sums and the wave's offset to the reference row, and the fp16
+// operand tiles of the chunk (after the prologue's normalisation of q and k,
+// whose 128 channels of a token are spread over the wave's 64 lanes).
 template <int PM>
 __device__ __forceinline__ void build_operands(Smem &sm, Raw &R, uint32_t bpad, int par,
-                                               int p, int lane, const float (*lc)[8],
-                                               const float *ex, const Prologue &pro, const Src &nx,
+                                               int p, int lane, const float (*lc)[2],
+                                               const Prologue &pro, const Src &nx,
                                                const LaneOffs &lof) {
     const int L = R.L;
-    const int cg = lane & 15, tb = lane >> 4;
-    const int ch0 = 8 * cg;
-    const int r0 = 8 * p + 2 * tb;
+    const int c = 2 * lane;
     // this wave's offset to the reference row m = 31 (the end of wave 3's
     // tokens), in log2 units
-    const floatx4 wa = *reinterpret_cast<const floatx4 *>(&sm.woff[par][p][ch0]);
-    const floatx4 wb = *reinterpret_cast<const floatx4 *>(&sm.woff[par][p][ch0 + 4]);
-    // exp(G - G_m) = 2^(log2(e) (ex + lc) + offset), the scale folded into fmas
+    const float2 wo = *reinterpret_cast<const float2 *>(&sm.woff[par][p][c]);
     constexpr float LOG2E = 1.4426950408889634f;
-    float pre[8];
+    float ik[8], iq[8];
+    if (pro_on<PM>(pro, PRO_NORM_QK)) {
+        float sk[8], sq[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        pre[e] = __builtin_fmaf(ex[e], LOG2E, wa[e]);
-        pre[e + 4] = __builtin_fmaf(ex[e + 4], LOG2E, wb[e]);
+        for (int t = 0; t < 8; ++t) {
+            const float k0 = bf16lo(R.k[t]), k1 = bf16hi(R.k[t]);
+            const float q0 = bf16lo(R.q[t]), q1 = bf16hi(R.q[t]);
+            sk[t] = __builtin_fmaf(k1, k1, k0 * k0);
+            sq[t] = __builtin_fmaf(q1, q1, q0 * q0);
+        }
+        float tk[8], tq[8];
+        wave_sums8(sk, tk, lane);
+        wave_sums8(sq, tq, lane);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            ik[t] = inv_norm(tk[t], pro.eps);
+            iq[t] = inv_norm(tq[t], pro.eps);
+        }
     }
-    // one token row at a time (fewer live registers)
+    // four token rows at a time (fewer live registers)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        float kv[8], qv[8];
-        unpack8(R.k[u], kv);  // zero past the chunk's end
-        unpack8(R.q[u], qv);
+    for (int hh = 0; hh < 2; ++hh) {
+        float kv[4][2], qv[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            kv[t][0] = bf16lo(R.k[4 * hh + t]);  // zero past the chunk's end
+            kv[t][1] = bf16hi(R.k[4 * hh + t]);
+            qv[t][0] = bf16lo(R.q[4 * hh + t]);
+            qv[t][1] = bf16hi(R.q[4 * hh + t]);
+        }
         // refill with the next chunk's rows, pinned here (after the last use
         // of the old contents) so the loop-carried registers stay in place
         __builtin_amdgcn_sched_barrier(0);
-        R.k[u] = load16(nx.k, lof.row[u]);
-        R.q[u] = load16(nx.q, lof.row[u]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            R.k[4 * hh + t] = load4(nx.k, lof.row[4 * hh + t]);
+            R.q[4 * hh + t] = load4(nx.q, lof.row[4 * hh + t]);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        if (pro_on<PM>(pro, PRO_NORM_QK)) {
-            const float ik = inv_norm(row16_sum(sumsq8(kv)), pro.eps);
-            const float iq = inv_norm(row16_sum(sumsq8(qv)), pro.eps);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kv[e] *= ik;
-                qv[e] *= iq;
+        for (int t = 0; t < 4; ++t) {
+            const int tt = 4 * hh + t;
+            if (pro_on<PM>(pro, PRO_NORM_QK)) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    kv[t][j] *= ik[tt];
+                    qv[t][j] *= iq[tt];
+                }
             }
-        }
-        half8 hkp, hkm, hqp;
+            half2v hkp, hkm, hqp;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float f = __builtin_amdgcn_exp2f(__builtin_fmaf(lc[u][e], LOG2E, pre[e]));
-            const float i = __builtin_amdgcn_rcpf(f);
-            hkp[e] = (_Float16)(kv[e] * f);
-            hkm[e] = (_Float16)(kv[e] * i);
-            hqp[e] = (_Float16)(qv[e] * f);
+            for (int j = 0; j < 2; ++j) {
+                const float f = __builtin_amdgcn_exp2f(__builtin_fmaf(lc[tt][j], LOG2E, j ? wo.y : wo.x));
+                const float i = __builtin_amdgcn_rcpf(f);
+                hkp[j] = (_Float16)(kv[t][j] * f);
+                hkm[j] = (_Float16)(kv[t][j] * i);
+                hqp[j] = (_Float16)(qv[t][j] * f);
+            }
+            const int rb = (8 * p + tt) * PK + c;
+            *reinterpret_cast<half2v *>(&sm.kp[rb]) = hkp;
+            *reinterpret_cast<half2v *>(&sm.km[par][rb]) = hkm;
+            *reinterpret_cast<half2v *>(&sm.qp[rb]) = hqp;
         }
-        const int rb = (r0 + u) * PK + ch0;
-        *reinterpret_cast<half8 *>(&sm.kp[rb]) = hkp;
-        *reinterpret_cast<half8 *>(&sm.km[par][rb]) = hkm;
-        *reinterpret_cast<half8 *>(&sm.qp[rb]) = hqp;
     }
-    // V: token lane, columns 8p .. 8p + 7 (zero past the end)
-    *reinterpret_cast<uint4 *>(&sm.vr[lane * PV + 8 * p]) = R.v;
+    // V: rows 8p .. 8p + 7, eight lanes per row (zero past the end)
+    *reinterpret_cast<uint4 *>(&sm.vr[(8 * p + (lane >> 3)) * PV + 8 * (lane & 7)]) = R.v;
     __builtin_amdgcn_sched_barrier(0);
     R.v = load16(nx.v, lof.v);
     __builtin_amdgcn_sched_barrier(0);
@@ -385,7 +425,6 @@ __device__ __forceinline__ void build_operands(Smem &sm, Raw &R, uint32_t bpad, 
     }
     R.L = nx.L;
 }
-
 // Block product: lane (l16, lg) receives element i =
 // (lhs rhs^T)[16 bi + 4 lg + i][16 bj + l16].
 __device__ __forceinline__ floatx4 block_product(const _Float16 *lhs, const _Float16 *rhs, int bi,
@@ -510,6 +549,20 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t *dst, floatx4 v) {
     w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){v[0], v[1]}, b2));
     w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){v[2], v[3]}, b2));
     *reinterpret_cast<uint2 *>(dst) = w;
+}
+
+// Prep wave 4 + j: rows 16 j .. 16 j + 15 of a chunk's staged output tile to
+// o, four whole rows (the workgroup's 64 columns) per store instruction:
+// lane holds row 16 j + 4 s + (lane >> 4), columns 4 (lane & 15) .. + 3.
+template <typename TOut>
+__device__ __forceinline__ void store_output(const Smem &sm, int par, TOut *o, int c0, int L, int H,
+                                             int h, int vt, int j, int lane) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int r = 16 * j + 4 * s + (lane >> 4);
+        const floatx4 x = *reinterpret_cast<const floatx4 *>(&sm.ost[par][r * PO + 4 * (lane & 15)]);
+        if (r < L) store4<TOut>(o + ((size_t)(c0 + r) * H + h) * VD + vt * VT + 4 * (lane & 15), x);
+    }
 }
 
 template <typename TOut, int PM>
@@ -666,13 +719,14 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
                 S[cb + 4] = mma32(km[2 * cb], bu0, S[cb + 4]);
                 S[cb + 4] = mma32(km[2 * cb + 1], bu1, S[cb + 4]);
             }
-            // O^T blocks: a lane holds chunk row 16 rb + l16, value columns
-            // 4 lg .. 4 lg + 3 (one 16-byte store)
+            // O^T blocks to the staging tile (a lane holds chunk row
+            // 16 rb + l16, columns 16 w + 4 lg .. + 3); prep waves 4-7 store
+            // it at the end of the next phase B as whole rows
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
                 const int r = 16 * rb + l16;
                 if (r < L)
-                    store4<TOut>(o + ((size_t)(c0 + r) * H + h) * VD + vt * VT + 16 * w + 4 * lg, O[rb]);
+                    *reinterpret_cast<floatx4 *>(&sm.ost[par][(16 * rb + l16) * PO + 16 * w + 4 * lg]) = O[rb];
             }
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) {
@@ -714,8 +768,8 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
         const uint32_t bpad = pro_on<PM>(pro, PRO_BETA_LOGIT) ? (BF16_NEG_INF_PAIR & 0xFFFFu) : 0u;
         const LaneOffs lof = lane_offsets(H, p, lane);
         Raw R;
-        uint4 rg[2];
-        float lc[2][8], ex[8];
+        uint32_t rg[8];
+        float lc[8][2];
         // chunk i of the sequence, clamped to the last one (a chunk past the
         // end is loaded as the last one again and never used)
         const int last = nchunks > 0 ? nchunks - 1 : 0;
@@ -731,14 +785,14 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
         if (nchunks > 0) {
             load_g(rg, g, cstart(0), clen(0), H, h, lof);
             load_raw(R, q, k, v, beta, cstart(0), clen(0), H, h, vt, p, lof);
-            scan_partials<PM>(sm, rg, clen(0), gpad, 0, p, lane, lc, ex, pro, gsrc(1), lof);
+            scan_partials<PM>(sm, rg, clen(0), gpad, 0, p, lane, lc, pro, gsrc(1), lof);
         }
         __syncthreads();
         if (p >= 4) chunk_factors(sm, 0, p - 4, lane);  // chunk 0's (its channel totals are in)
         __syncthreads();
         if (nchunks > 0) {
-            build_operands<PM>(sm, R, bpad, 0, p, lane, lc, ex, pro, src(1), lof);
-            scan_partials<PM>(sm, rg, clen(1), gpad, 1, p, lane, lc, ex, pro, gsrc(2), lof);
+            build_operands<PM>(sm, R, bpad, 0, p, lane, lc, pro, src(1), lof);
+            scan_partials<PM>(sm, rg, clen(1), gpad, 1, p, lane, lc, pro, gsrc(2), lof);
         }
         __syncthreads();
         for (int ci = 0; ci < nchunks; ++ci) {
@@ -754,10 +808,18 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             // iteration (unconditional register refills keep the loop-carried
             // inputs in place): past the last chunk they rework the last
             // chunk's inputs into buffers that are not read again.
-            build_operands<PM>(sm, R, bpad, (ci & 1) ^ 1, p, lane, lc, ex, pro, src(ci + 2), lof);
-            scan_partials<PM>(sm, rg, clen(ci + 2), gpad, ci & 1, p, lane, lc, ex, pro, gsrc(ci + 3), lof);
+            build_operands<PM>(sm, R, bpad, (ci & 1) ^ 1, p, lane, lc, pro, src(ci + 2), lof);
+            scan_partials<PM>(sm, rg, clen(ci + 2), gpad, ci & 1, p, lane, lc, pro, gsrc(ci + 3), lof);
+            // the previous chunk's output (staged by the state waves in its
+            // phase B): waves 4-7 finish this phase early
+            if (p >= 4 && ci > 0)
+                store_output<TOut>(sm, (ci & 1) ^ 1, o, cstart(ci - 1), clen(ci - 1), H, h, vt, p - 4, lane);
             __syncthreads();
         }
+        // the last chunk's output (its staging tile is complete after the
+        // loop's last barrier)
+        if (p >= 4 && nchunks > 0)
+            store_output<TOut>(sm, (nchunks - 1) & 1, o, cstart(nchunks - 1), clen(nchunks - 1), H, h, vt, p - 4, lane);
     }
 }
 
