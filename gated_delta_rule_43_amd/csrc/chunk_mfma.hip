@@ -144,7 +144,7 @@ __device__ __forceinline__ half8 cat8(half4 a, half4 b) {
 struct Raw {
     uint32_t q[8], k[8];  // token 8 p + t: bf16 channels 2 l (low half) and 2 l + 1
     uint4 v;              // V tile piece: row 8 p + (l >> 3), columns 8 (l & 7) .. + 7
-    uint32_t beta;        // beta of token lane (used by prep wave 0)
+    uint32_t beta;        // beta of token lane (used by prep wave 4, which finishes its phases early)
     int L;                // the chunk's length
 };
 
@@ -204,7 +204,7 @@ __device__ __forceinline__ void load_raw(Raw &R, const uint16_t *q, const uint16
                            (uint32_t)((L - 1) * H * VD * 2 + 2 * VT));
     R.v = load16(rv, lof.v);
     const auto rb = extent(beta + (size_t)c0 * H + h, (uint32_t)((L - 1) * H * 2 + 2));
-    R.beta = p == 0 ? __builtin_amdgcn_raw_buffer_load_b16(rb, lof.beta, 0, 0) : 0u;
+    R.beta = p == 4 ? __builtin_amdgcn_raw_buffer_load_b16(rb, lof.beta, 0, 0) : 0u;
     R.L = L;
 }
 
@@ -417,7 +417,7 @@ __device__ __forceinline__ void build_operands(Smem &sm, Raw &R, uint32_t bpad, 
     __builtin_amdgcn_sched_barrier(0);
     R.v = load16(nx.v, lof.v);
     __builtin_amdgcn_sched_barrier(0);
-    if (p == 0) {
+    if (p == 4) {
         const bool bl = pro_on<PM>(pro, PRO_BETA_LOGIT);
         const float b = __uint_as_float((bl && lane >= L ? bpad : R.beta) << 16);
         R.beta = __builtin_amdgcn_raw_buffer_load_b16(nx.beta, lof.beta, 0, 0);
