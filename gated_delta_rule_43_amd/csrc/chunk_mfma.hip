@@ -762,8 +762,8 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
         const int p = w - 4;
         // Waves are issued oldest first: prep waves 0-3 would always win the
         // vector ALU against waves 4-7 on the same SIMD, and the chunk waits
-        // for the slowest prep wave; raising 4-7 evens the two out.
-        if (p >= 4) __builtin_amdgcn_s_setprio(1);
+        // for the slowest prep wave; raising 4-7 (from the start of each
+        // phase A to the end of their operand build) evens the two out.
         const uint32_t gpad = pro_on<PM>(pro, PRO_GATE_LOGIT) ? BF16_NEG_INF_PAIR : 0u;
         const uint32_t bpad = pro_on<PM>(pro, PRO_BETA_LOGIT) ? (BF16_NEG_INF_PAIR & 0xFFFFu) : 0u;
         const LaneOffs lof = lane_offsets(H, p, lane);
@@ -797,6 +797,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
         __syncthreads();
         for (int ci = 0; ci < nchunks; ++ci) {
             // ---- phase A: this chunk's Gram / query-key blocks and diagonal inverses
+            if (p >= 4) __builtin_amdgcn_s_setprio(1);
             prep_blocks(sm, ci & 1, p, lane);
             // the next chunk's factors and offsets (its channel totals landed
             // one iteration ago), for phase B: waves 4-7, whose blocks finish first
@@ -809,6 +810,9 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             // inputs in place): past the last chunk they rework the last
             // chunk's inputs into buffers that are not read again.
             build_operands<PM>(sm, R, bpad, (ci & 1) ^ 1, p, lane, lc, pro, src(ci + 2), lof);
+            // waves 4-7 give way to 0-3 (their phase-B work is the longer
+            // path) until the next phase A
+            if (p >= 4) __builtin_amdgcn_s_setprio(0);
             scan_partials<PM>(sm, rg, clen(ci + 2), gpad, ci & 1, p, lane, lc, pro, gsrc(ci + 3), lof);
             // the previous chunk's output (staged by the state waves in its
             // phase B): waves 4-7 finish this phase early
