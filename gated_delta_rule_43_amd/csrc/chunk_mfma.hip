@@ -86,7 +86,8 @@ struct Smem {
     _Float16 tii[4][16 * PI];   // (I + A_ii)^-1, diagonal blocks
     uint16_t vr[C * PV];        // bf16 V tile [r][j]
     float beta[C];
-    float fm[2][KD];            // exp(G_m), by chunk parity
+    float fm[2][KD];            // exp(G_m) times the previous chunk's exp(G_C - G_m): the
+                                // state's scaling at a chunk's start, by chunk parity
     float fc[2][KD];            // exp(G_C - G_m), by chunk parity
     float gsum[2][NP][KD];      // prep waves: per-wave channel sums of g, by chunk parity
     float woff[2][NP][KD];      // log2(e) (G at prep wave p's first token - G_m), by parity
@@ -276,7 +277,7 @@ __device__ __forceinline__ void scan_partials(Smem &sm, uint32_t *rg, int L, uin
 // reference row, log2(e) (G_{8p - 1} - G_m) (minus the totals of waves p..3,
 // or plus those of waves 4..p-1): channel group w (0..3), lanes 0..31, takes channels
 // 32 w .. 32 w + 31.
-__device__ __forceinline__ void chunk_factors(Smem &sm, int par, int w, int lane) {
+__device__ __forceinline__ void chunk_factors(Smem &sm, int par, int w, int lane, bool first) {
     constexpr float LOG2E = 1.4426950408889634f;
     if (lane < 32) {
         const int c = 32 * w + lane;
@@ -296,7 +297,9 @@ __device__ __forceinline__ void chunk_factors(Smem &sm, int par, int w, int lane
             sm.woff[par][ww][c] = LOG2E * above;
             above += x[ww];
         }
-        sm.fm[par][c] = fast_exp(gm);
+        // the end-of-chunk scaling of the previous chunk is folded into this
+        // chunk's start scaling (the state is kept without it in between)
+        sm.fm[par][c] = fast_exp(gm) * (first ? 1.f : sm.fc[par ^ 1][c]);
         sm.fc[par][c] = fast_exp(above);
     }
 }
@@ -728,12 +731,9 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
                 if (r < L)
                     *reinterpret_cast<floatx4 *>(&sm.ost[par][(16 * rb + l16) * PO + 16 * w + 4 * lg]) = O[rb];
             }
-#pragma unroll
-            for (int cb = 0; cb < 8; ++cb) {
-                const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.fc[par][sigma(cb, lg, 0)]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[cb][i] *= f[i];
-            }
+            // S now holds S' + Km^T U; its end-of-chunk scaling
+            // Diag(exp(G_C - G_m)) is applied with the next chunk's start
+            // scaling (and here only to the copies that leave the kernel)
             // prefix snapshot when the state now covers a boundary
             if (snap.due(c0 - bos + L)) {
                 float *sp = snap.dest(io, h, H, KD * VD);
@@ -744,7 +744,8 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
                     // col - (lane & 3) .. +3
 #pragma unroll
                     for (int cb = 0; cb < 8; ++cb) {
-                        const floatx4 t = quad_transpose(S[cb], lane);
+                        const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.fc[par][sigma(cb, lg, 0)]);
+                        const floatx4 t = quad_transpose(S[cb] * f, lane);
                         *reinterpret_cast<floatx4 *>(&sp[sigma(cb, lg, lane & 3) * VD + col - (lane & 3)]) = t;
                     }
                 }
@@ -752,6 +753,13 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             __syncthreads();
         }
         float *sTp = state_out(io, n, h, H, KD * VD);
+        if (sTp && nchunks > 0) {
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) {
+                const floatx4 f = *reinterpret_cast<const floatx4 *>(&sm.fc[(nchunks - 1) & 1][sigma(cb, lg, 0)]);
+                S[cb] *= f;
+            }
+        }
         if (sTp) {
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb)
@@ -788,7 +796,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             scan_partials<PM>(sm, rg, clen(0), gpad, 0, p, lane, lc, pro, gsrc(1), lof);
         }
         __syncthreads();
-        if (p >= 4) chunk_factors(sm, 0, p - 4, lane);  // chunk 0's (its channel totals are in)
+        if (p >= 4) chunk_factors(sm, 0, p - 4, lane, true);  // chunk 0's (its channel totals are in)
         __syncthreads();
         if (nchunks > 0) {
             build_operands<PM>(sm, R, bpad, 0, p, lane, lc, pro, src(1), lof);
@@ -801,7 +809,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             prep_blocks(sm, ci & 1, p, lane);
             // the next chunk's factors and offsets (its channel totals landed
             // one iteration ago), for phase B: waves 4-7, whose blocks finish first
-            if (p >= 4) chunk_factors(sm, (ci & 1) ^ 1, p - 4, lane);
+            if (p >= 4) chunk_factors(sm, (ci & 1) ^ 1, p - 4, lane, false);
             __syncthreads();
             // ---- phase B: the next chunk's operands and the decay sums of the
             // chunk after it; their input registers are refilled (for chunks
