@@ -96,6 +96,7 @@ struct Smem {
 };
 
 typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 // Transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane j
 // receives as element i the (j & 3)-th 16-bit value of the 8 bytes addressed
@@ -275,12 +276,10 @@ __device__ __forceinline__ void scan_partials(Smem &sm, uint32_t *rg, int L, uin
 // From the prep waves' channel totals of parity par, the chunk's per-channel
 // factors exp(G_m) and exp(G_C - G_m) and each prep wave's offset to the
 // reference row, log2(e) (G_{8p - 1} - G_m) (minus the totals of waves p..3,
-// or plus those of waves 4..p-1): channel group w (0..3), lanes 0..31, takes channels
-// 32 w .. 32 w + 31.
-__device__ __forceinline__ void chunk_factors(Smem &sm, int par, int w, int lane, bool first) {
+// or plus those of waves 4..p-1), for channel c.
+__device__ __forceinline__ void chunk_factors(Smem &sm, int par, int c, bool first) {
     constexpr float LOG2E = 1.4426950408889634f;
-    if (lane < 32) {
-        const int c = 32 * w + lane;
+    {
         float x[NP];
 #pragma unroll
         for (int ww = 0; ww < NP; ++ww) x[ww] = sm.gsum[par][ww][c];
@@ -452,8 +451,8 @@ __device__ __forceinline__ floatx4 block_product_t(const _Float16 *lhs, const _F
 }
 
 // Prep wave p: the chunk's Gram / query-key blocks.  Waves 0-3 take the
-// diagonal blocks (p, p) and the inverse (I + A_pp)^-1; waves 4-7 take the
-// twelve off-diagonal blocks (six Gram, six query-key), three each.
+// diagonal blocks (p, p) and the inverse (I + A_pp)^-1; waves 4-7 the
+// off-diagonal blocks of the Gram and query-key products.
 __device__ __forceinline__ void prep_blocks(Smem &sm, int par, int p, int lane) {
     const _Float16 *km = sm.km[par];
     const int l16 = lane & 15, lg = lane >> 4;
@@ -492,14 +491,38 @@ __device__ __forceinline__ void prep_blocks(Smem &sm, int par, int p, int lane) 
         const half4 R2A = to_half4(mma16(eye + L4B, R1A, z4));        // (R1 (I + L^4))^T
         const half4 TA = to_half4(mma16(eye + L8B, R2A, z4));         // (R2 (I + L^8))^T
         *reinterpret_cast<half4 *>(&sm.tii[p][l16 * PI + 4 * lg]) = TA;
-    } else {
+    } else if (p < 6) {
+        // waves 4 and 5: rows 32-63 x columns 0-31 of the Gram (wave 4) or
+        // query-key (wave 5) product -- blocks (2,0), (2,1), (3,0), (3,1) --
+        // as one 32x32 tile (half the LDS reads of four 16x16 blocks),
+        // transposed: lane l gets row 32 + (l & 31), columns
+        // 8 q + 4 (l >> 5) .. + 3 in registers 4 q .. 4 q + 3
+        const bool gram = p == 4;
+        const _Float16 *lhs = gram ? sm.kp : sm.qp;
+        const int r32 = lane & 31, kh = 8 * (lane >> 5);
+        floatx16 acc = {};
 #pragma unroll
-        for (int tsk = 0; tsk < 3; ++tsk) {
-            const int o = 3 * (p - 4) + tsk;  // 0..11: six Gram blocks, then six query-key blocks
-            const int oo = o % 6;
-            const bool gram = o < 6;
-            const int bi = oo < 1 ? 1 : (oo < 3 ? 2 : 3);
-            const int bj = oo < 1 ? 0 : (oo < 3 ? oo - 1 : oo - 3);
+        for (int ks = 0; ks < 8; ++ks) {
+            const half8 a = *reinterpret_cast<const half8 *>(&km[r32 * PK + 16 * ks + kh]);
+            const half8 b = *reinterpret_cast<const half8 *>(&lhs[(32 + r32) * PK + 16 * ks + kh]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+        }
+        const float sc = gram ? sm.beta[32 + r32] : 1.f;
+        _Float16 *dst = gram ? sm.a16 : sm.p;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            half4 hv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hv[i] = (_Float16)(sc * acc[4 * qq + i]);
+            *reinterpret_cast<half4 *>(&dst[(32 + r32) * P4 + 8 * qq + 4 * (lane >> 5)]) = hv;
+        }
+    } else {
+        // waves 6 and 7: blocks (1,0) and (3,2) of the Gram (wave 6) or
+        // query-key (wave 7) product
+        const bool gram = p == 6;
+#pragma unroll
+        for (int tsk = 0; tsk < 2; ++tsk) {
+            const int bi = tsk ? 3 : 1, bj = tsk ? 2 : 0;
             const floatx4 acc = block_product_t(gram ? sm.kp : sm.qp, km, bi, bj, lane);
             const float sc = gram ? sm.beta[16 * bi + l16] : 1.f;
             half4 hv;
@@ -796,7 +819,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             scan_partials<PM>(sm, rg, clen(0), gpad, 0, p, lane, lc, pro, gsrc(1), lof);
         }
         __syncthreads();
-        if (p >= 4) chunk_factors(sm, 0, p - 4, lane, true);  // chunk 0's (its channel totals are in)
+        if (p >= 6) chunk_factors(sm, 0, 64 * (p - 6) + lane, true);  // chunk 0's (its channel totals are in)
         __syncthreads();
         if (nchunks > 0) {
             build_operands<PM>(sm, R, bpad, 0, p, lane, lc, pro, src(1), lof);
@@ -808,8 +831,9 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(
             if (p >= 4) __builtin_amdgcn_s_setprio(1);
             prep_blocks(sm, ci & 1, p, lane);
             // the next chunk's factors and offsets (its channel totals landed
-            // one iteration ago), for phase B: waves 4-7, whose blocks finish first
-            if (p >= 4) chunk_factors(sm, (ci & 1) ^ 1, p - 4, lane, false);
+            // one iteration ago), for phase B: waves 6 and 7, whose blocks
+            // finish first
+            if (p >= 6) chunk_factors(sm, (ci & 1) ^ 1, 64 * (p - 6) + lane, false);
             __syncthreads();
             // ---- phase B: the next chunk's operands and the decay sums of the
             // chunk after it; their input registers are refilled (for chunks
