@@ -84,6 +84,15 @@ def test_bf16_d128_decay_stress(g_mode, g_lb, path):
 
 
 @pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("B,H", [(3, 1), (1, 5)])
+def test_bf16_d128_head_counts(B, H, path):
+    # one head (token rows 256 bytes apart, the narrowest stride the loads and
+    # the whole-row output stores see) and an odd head count
+    _fixed_case(f"bf16_d128_B{B}_H{H}", 400 + 10 * B + H, B, 300, H, 128, 128, "bf16",
+                s0_std=0.1, path=path)
+
+
+@pytest.mark.parametrize("path", list(PATHS))
 def test_bf16_output_dtype(path):
     # held to the 2e-2 bound on the arithmetic; the output's own bf16 rounding
     # (at most half an ulp of each value) is allowed on top
