@@ -1147,20 +1147,44 @@ __global__ __launch_bounds__(512) void bwd_udy_mfma_kernel(
     for (int ks = 0; ks < KSC; ++ks) a4[ks] = rec[Rc::KM + (size_t)(4 * ks + lq) * K + 16 * w + lr];
     __syncthreads();
 
+    // Each value tile's inputs (its columns of S_start, dS_end, V and dO) are
+    // loaded into registers one tile ahead, so their latency overlaps the
+    // previous tile's products instead of stalling every tile.
+    constexpr int NS = K * VT / 512, NR = C * VT / 512;
+    static_assert(NS * 512 == K * VT && NR * 512 == C * VT, "tile elements per thread");
+    float pS[NS], pX[NS], pR[NR], pO[NR];
+    auto fetch = [&](int j0) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int e = t + 512 * i, c = e / VT, j = e % VT;
+            pS[i] = S0c[(size_t)c * V + j0 + j];
+            pX[i] = dSc[(size_t)c * V + j0 + j];
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int e = t + 512 * i, r = e / VT, j = e % VT;
+            const size_t off = ((size_t)(c0 + r) * H + h) * V + j0 + j;
+            pR[i] = r < L ? (in_bf16 ? to_f32(vb[off]) : vf[off]) : 0.f;
+            pO[i] = r < L ? dout[off] : 0.f;
+        }
+    };
+    fetch(0);
     for (int vt = 0; vt < NVT; ++vt) {
         const int j0 = vt * VT;
         if (vt > 0) __syncthreads();
-        for (int e = t; e < K * VT; e += 512) {
-            const int c = e / VT, j = e % VT;
-            sS[c * PV + j] = sE[c] * S0c[(size_t)c * V + j0 + j];
-            sX[c * PV + j] = sF[c] * dSc[(size_t)c * V + j0 + j];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int e = t + 512 * i, c = e / VT, j = e % VT;
+            sS[c * PV + j] = sE[c] * pS[i];
+            sX[c * PV + j] = sF[c] * pX[i];
         }
-        for (int e = t; e < C * VT; e += 512) {
-            const int r = e / VT, j = e % VT;
-            const size_t off = ((size_t)(c0 + r) * H + h) * V + j0 + j;
-            sR[r * PV + j] = r < L ? (in_bf16 ? to_f32(vb[off]) : vf[off]) : 0.f;
-            sO[r * PV + j] = r < L ? dout[off] : 0.f;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int e = t + 512 * i, r = e / VT, j = e % VT;
+            sR[r * PV + j] = pR[i];
+            sO[r * PV + j] = pO[i];
         }
+        if (vt + 1 < NVT) fetch(j0 + VT);
         __syncthreads();
         // phase A: R (waves 0-3) or dU (waves 4-7) for row block rb
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
