@@ -805,63 +805,76 @@ __device__ __forceinline__ void chain_mfma(int vt, int h, int n, const float *__
             const int row = 16 * (RBW * w + b) + 4 * (lane >> 4) + i;
             acc[b][i] = init ? init[sbase + (size_t)row * V] : 0.f;
         }
-    float cur[RBW][KS], nxt[RBW][KS], add[RBW][4];
-    auto fetch = [&](int ci) {  // chunk ci's A fragments and addend, into nxt / add
+    // The chunks' A fragments and addends are fetched DEPTH steps ahead into a
+    // ring of register stages: one step's products take far less time than a
+    // load's latency, so a one-step lookahead left every step waiting on its
+    // loads.
+    constexpr int DEPTH = 4;
+    float cur[RBW][KS], nxt[DEPTH][RBW][KS], add[DEPTH][RBW][4];
+    auto fetch = [&](int ci, float (&fr)[RBW][KS], float (&fa)[RBW][4]) {
         const float *rec = recs + ((size_t)(first + ci) * H + h) * Rc::floats;
 #pragma unroll
         for (int b = 0; b < RBW; ++b) {
             const int rb = RBW * w + b;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) nxt[b][ks] = rec[fofs + ((size_t)rb * KS + ks) * 64 + lane];
+            for (int ks = 0; ks < KS; ++ks) fr[b][ks] = rec[fofs + ((size_t)rb * KS + ks) * 64 + lane];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                add[b][i] = rec[aofs + (size_t)(16 * rb + 4 * (lane >> 4) + i) * V + col];
+                fa[b][i] = rec[aofs + (size_t)(16 * rb + 4 * (lane >> 4) + i) * V + col];
         }
     };
-    if (nch > 0) fetch(ADJ ? nch - 1 : 0);
-    for (int step = 0; step < nch; ++step) {
-        const int ci = ADJ ? nch - 1 - step : step;
-        float *dst = out + ((size_t)(first + ci) * H + h) * K * V + col;
+    auto chunk_of = [&](int step) { return ADJ ? nch - 1 - step : step; };
 #pragma unroll
-        for (int b = 0; b < RBW; ++b)
+    for (int d = 0; d < DEPTH; ++d)
+        if (d < nch) fetch(chunk_of(d), nxt[d], add[d]);
+    for (int step0 = 0; step0 < nch; step0 += DEPTH) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * (RBW * w + b) + 4 * (lane >> 4) + i;
-                dst[(size_t)row * V] = acc[b][i];
-                sS[row * 16 + (lane & 15)] = acc[b][i];
-            }
-        float ad[RBW][4];
+        for (int d = 0; d < DEPTH; ++d) {
+            const int step = step0 + d;
+            if (step >= nch) break;
+            const int ci = chunk_of(step);
+            float *dst = out + ((size_t)(first + ci) * H + h) * K * V + col;
 #pragma unroll
-        for (int b = 0; b < RBW; ++b) {
+            for (int b = 0; b < RBW; ++b)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) cur[b][ks] = nxt[b][ks];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ad[b][i] = add[b][i];
-        }
-        __syncthreads();
-        if (step + 1 < nch) fetch(ADJ ? ci - 1 : ci + 1);
-        // even and odd k-steps in two accumulators: two dependency chains
-        floatx4 acc2[RBW];
-#pragma unroll
-        for (int b = 0; b < RBW; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[b][i] = ad[b][i];
-                acc2[b][i] = 0.f;
-            }
-#pragma unroll
-        for (int ks = 0; ks < KS; ks += 2) {
-            const float bv = sS[64 * ks + lane];  // B[k = 4 ks + lane / 16][lane % 16]
-            const float bw = sS[64 * (ks + 1) + lane];
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * (RBW * w + b) + 4 * (lane >> 4) + i;
+                    dst[(size_t)row * V] = acc[b][i];
+                    sS[row * 16 + (lane & 15)] = acc[b][i];
+                }
+            float ad[RBW][4];
 #pragma unroll
             for (int b = 0; b < RBW; ++b) {
-                acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[b][ks], bv, acc[b], 0, 0, 0);
-                acc2[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[b][ks + 1], bw, acc2[b], 0, 0, 0);
-            }
-        }
 #pragma unroll
-        for (int b = 0; b < RBW; ++b) acc[b] += acc2[b];
-        __syncthreads();
+                for (int ks = 0; ks < KS; ++ks) cur[b][ks] = nxt[d][b][ks];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ad[b][i] = add[d][b][i];
+            }
+            __syncthreads();
+            if (step + DEPTH < nch) fetch(chunk_of(step + DEPTH), nxt[d], add[d]);
+            // even and odd k-steps in two accumulators: two dependency chains
+            floatx4 acc2[RBW];
+#pragma unroll
+            for (int b = 0; b < RBW; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[b][i] = ad[b][i];
+                    acc2[b][i] = 0.f;
+                }
+#pragma unroll
+            for (int ks = 0; ks < KS; ks += 2) {
+                const float bv = sS[64 * ks + lane];  // B[k = 4 ks + lane / 16][lane % 16]
+                const float bw = sS[64 * (ks + 1) + lane];
+#pragma unroll
+                for (int b = 0; b < RBW; ++b) {
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[b][ks], bv, acc[b], 0, 0, 0);
+                    acc2[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[b][ks + 1], bw, acc2[b], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < RBW; ++b) acc[b] += acc2[b];
+            __syncthreads();
+        }
     }
     if (ADJ && fin)
 #pragma unroll
