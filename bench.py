@@ -1,15 +1,20 @@
 #!/usr/bin/env python3
 """KDA forward throughput on one MI355X: chunked prefill and recurrent decode.
 
-One JSON line on stdout.  A step is one chunked forward pass (kda_chunk_fwd)
-over the prefill workload B=1, H=8, T=4096, d_k=d_v=128, chunk 64, bf16
-inputs with fp32 state, accumulation and output, on the implementation the
-library recommends for it (kda_workspace_bytes > 0: the two-pass path, three
-launches: the intra-chunk pass over all chunks, the sequential state pass, the
-output pass over all chunks); `value` is its tokens/s.  The single-pass fused kernel's time on
-the same workload is reported alongside.  The decode leg (one token for each
-of 256 sequences x 32 heads, persistent fp32 state, kda_decode_step) is
-reported in the same line under "decode".
+One JSON line on stdout.  A step is one chunked forward pass over a prefill
+workload (bf16 inputs, d_k = d_v = 128, chunk 64, fp32 state, accumulation and
+output) on the implementation the library recommends for it
+(kda_workspace_bytes: 0 bytes runs the single-pass fused kernel, a workspace
+the two-pass path).  The headline workload is the largest one that fits one
+GPU: 64 packed sequences with log-uniform lengths in [16, 32768] (seed 3:
+219,348 tokens), 16 heads, run through kda_varlen_fwd from zero initial
+states; `value` is its tokens/s, from the median of per-call HIP-event
+timings with a 512 MiB cache flush before every call.  The batched workload
+(B=4, H=32, T=8192) and the small prefill workload (B=1, H=8, T=4096) are
+reported alongside under "prefill_legs", together with the prefix-cache,
+prologue and backward legs on the small workload, and the decode leg (one
+token for each of 256 sequences x 32 heads, persistent fp32 state,
+kda_decode_step) under "decode".
 
 Inputs are synthetic and already resident in HBM when the timed region starts.
 The roofline objects price the ALGORITHMIC bytes (and flops) of one forward
