@@ -59,7 +59,10 @@
  * below are device pointers.  Every call validates its arguments on the host,
  * then enqueues its kernels on `stream` (a hipStream_t; NULL = the default
  * stream) and returns without synchronising.  Results are ready when the
- * stream is.
+ * stream is.  A call issues no memset, copy or host-device
+ * synchronisation, so calls may be captured into a HIP graph; the first call
+ * of each kernel on a device sets its LDS attribute, so make one call of each
+ * entry point in use before capturing.
  *
  * Aliasing.  q, k, v, g, beta and o must not overlap each other or the
  * states.  sT == s0 is allowed (in place); otherwise sT and s0 must not overlap.
