@@ -55,8 +55,9 @@
  * Ownership and ordering.  The caller allocates every buffer; the library
  * allocates no device memory, keeps no state between calls and is
  * thread-safe (one exception: kda_varlen_fwd_noalloc below uses a static
- * scratch array that the library's code object holds on each GPU).  All pointers except the cu_seqlens host-side description
- * below are device pointers.  Every call validates its arguments on the host,
+ * scratch array that the library's code object holds on each GPU).  Every
+ * pointer argument is a device pointer (cu_seqlens, slot lists and block
+ * tables included).  Every call validates its arguments on the host,
  * then enqueues its kernels on `stream` (a hipStream_t; NULL = the default
  * stream) and returns without synchronising.  Results are ready when the
  * stream is.  A call issues no memset, copy or host-device
