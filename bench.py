@@ -114,6 +114,22 @@ def measured_traffic(stem):
     return float(b.group(1))
 
 
+def measured_mfma_flops(stem):
+    """Executed matrix-core flops per call from the committed rocprofv3 counter
+    summary (profiles/<stem>_mfma.md: the MFMA operation counters, in units of
+    512 flops, summed over the call's kernels), or None when that summary was
+    taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{stem}_mfma.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source hash:\s*`?([0-9a-f]+)`?", text)
+    f = re.search(r"executed MFMA flops per launch:\s*([0-9.eE+]+)", text)
+    if not m or not f or m.group(1) != kernel_source_hash(stem):
+        return None
+    return float(f.group(1))
+
+
 def time_launches(fn, steps, warmup, stream):
     """Mean ms per call of `steps` back-to-back calls after `warmup` calls (one
     event pair around the loop: the warm, pipelined rate)."""
@@ -186,10 +202,20 @@ def settle_clock(stream, fills=1000):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(d, cu, H, what, max_passes=3, wall_budget_s=8.0):
+def rel_err(x, ref):
+    """max|x - ref| / RMS(ref) over a whole tensor (the parity measure)."""
+    import numpy as np
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = float(np.max(np.abs(x - ref))) if x.size else 0.0
+    return err / rms if rms > 0.0 else err
+
+
+def cpu_baseline(d, cu, H, what, gpu_out=None, max_passes=3, wall_budget_s=8.0):
     """fp64 oracle over the whole packed workload d (all (sequence, head)
     units), repeated while the wall budget lasts (at most max_passes); input
-    conversion is outside the timing."""
+    conversion is outside the timing.  With gpu_out = (o, sT) of the timed
+    GPU call on the same inputs, the oracle's result also gives that call's
+    max|err| / RMS on o and on S_T (after the timing)."""
     from oracle import oracle
     q, k, v, g, beta = (oracle.as_f64(d[x]) for x in ("q", "k", "v", "g", "beta"))
     s0 = oracle.as_f64(d["s0"]) if d.get("s0") is not None else None
@@ -199,15 +225,25 @@ def cpu_baseline(d, cu, H, what, max_passes=3, wall_budget_s=8.0):
     times = []
     while len(times) < max_passes and sum(times) < wall_budget_s:
         t0 = time.perf_counter()
-        oracle.recurrence(q, k, v, g, beta, cu, s0, nthreads=used)
+        ref = oracle.recurrence(q, k, v, g, beta, cu, s0, nthreads=used)
         times.append(time.perf_counter() - t0)
     dt = sum(times) / len(times)
     tokens = int(cu[-1])
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"{what}: the whole workload, {tokens} tokens x {H} heads ({len(times)} "
-                      f"pass(es), mean {dt:.2f} s wall each, ~{sum(times) * used:.0f} core-s in "
-                      f"total), parallel over its {units} (sequence, head) units; {threads} "
-                      f"host threads available"}
+    res = {"value": tokens / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+           "sample": f"{what}: the whole workload, {tokens} tokens x {H} heads ({len(times)} "
+                     f"pass(es), mean {dt:.2f} s wall each, ~{sum(times) * used:.0f} core-s in "
+                     f"total), parallel over its {units} (sequence, head) units; {threads} "
+                     f"host threads available"}
+    if gpu_out is not None:
+        o_ref, s_ref = ref
+        del ref
+        o = gpu_out[0].detach().cpu().double().numpy().reshape(o_ref.shape)
+        e_o = rel_err(o, o_ref)
+        del o, o_ref
+        e_s = rel_err(gpu_out[1].detach().cpu().double().numpy().reshape(s_ref.shape), s_ref)
+        res["parity_of_timed_call"] = {"o": e_o, "sT": e_s, "measure": "max|err|/RMS(ref), whole tensors",
+                                       "bound": 2e-2}
+    return res
 
 
 def decode_leg(args, dev, stream):
@@ -379,9 +415,20 @@ def prefill_leg(w, args, dev, stream, flush, steps, warmup):
         "roofline_mfma": {"achieved": alg_f / (ms * 1e-3) / 1e12, "peak": MFMA_F16_PEAK_TFLOPS,
                           "unit": "TFLOP/s",
                           "frac": alg_f / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                          "flops": "algorithmic", "alg_flops_per_launch": alg_f},
+                          "flops": "algorithmic", "alg_flops_per_launch": alg_f,
+                          # the most the algorithmic flops can reach: the call
+                          # running at the HBM floor of its algorithmic bytes
+                          "ceiling_frac_at_hbm_floor":
+                              alg_f / (alg_b / (HBM_PEAK_GBS * 1e9)) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                          "target_frac": 0.40},
     }
-    return leg, d, cu
+    ex = measured_mfma_flops(stem)
+    if ex is not None:
+        leg["roofline_mfma"]["executed"] = {
+            "flops_per_launch": ex, "achieved": ex / (ms * 1e-3) / 1e12,
+            "frac": ex / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "source": f"profiles/{stem}_mfma.md (rocprofv3 MFMA operation counters)"}
+    return leg, d, cu, _bufs[:2]
 
 
 def next_legs(args, dev, stream):
@@ -552,7 +599,8 @@ def main():
     settle_clock(stream)
     flush = CacheFlush(dev)
     w = inputs.WORKLOADS[args.prefill_workload]
-    head, d_head, cu_head = prefill_leg(w, args, dev, stream, flush, args.steps, args.warmup)
+    head, d_head, cu_head, out_head = prefill_leg(w, args, dev, stream, flush, args.steps,
+                                                  args.warmup)
     cfg = {"workload": w.name, "sequences": head["sequences"], "tokens": head["tokens"],
            "H": w.H, "d_k": w.K, "d_v": w.V, "chunk": w.chunk, "global_batch": head["sequences"],
            "seq_len": (w.T if w.kind == "fixed" else f"log-uniform [{w.len_min}, {w.len_max}]"),
@@ -580,7 +628,7 @@ def main():
         legs = {}
         for name in PREFILL_WORKLOADS:
             if name != w.name:
-                leg, _, _ = prefill_leg(inputs.WORKLOADS[name], args, dev, stream, flush,
+                leg, _, _, _ = prefill_leg(inputs.WORKLOADS[name], args, dev, stream, flush,
                                         args.steps, args.warmup)
                 legs[name] = leg
         result["prefill_legs"] = legs
@@ -589,7 +637,7 @@ def main():
         result["decode"] = decode_leg(args, dev, stream)
     del flush
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(d_head, cu_head, w.H, w.name)
+        result["cpu_baseline"] = cpu_baseline(d_head, cu_head, w.H, w.name, gpu_out=out_head)
     print(json.dumps(result), flush=True)
 
 
