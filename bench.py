@@ -20,7 +20,12 @@ Inputs are synthetic and already resident in HBM when the timed region starts.
 The roofline objects price the ALGORITHMIC bytes (and flops) of one forward
 call against MI355X peaks (HBM 8 TB/s; dense fp16/bf16 MFMA 2.5 PFLOP/s);
 call time comes from HIP events on the stream the kernels run on.
-The cpu_baseline leg times the fp64 oracle on the host cores.
+roofline_mfma also gives the ceiling the algorithmic flops have at the HBM
+floor and, from the committed rocprofv3 counter summary of the same kernel
+source, the executed matrix-core rate.
+The cpu_baseline leg times the fp64 oracle on the host cores over the whole
+headline workload, and compares its result with the timed GPU call's outputs
+(max|err|/RMS on o and S_T).
 """
 
 import argparse
