@@ -772,9 +772,12 @@ __global__ __launch_bounds__(BNT) void bwd_dstate_kernel(
 // head, 16-column value tile).  Wave w owns row block w of the tile (two per
 // SIMD, so that one wave's fragment loads overlap the other's matrix
 // instructions); the tile goes through LDS each chunk to serve as
-// the B operand of every wave, and the chunk's A fragments (MM, or MM^T for
-// the adjoint, stored fragment-ordered in the record) stream from memory into
-// registers one chunk ahead.
+// the B operand of every wave (two LDS copies by step parity, so one barrier
+// per step suffices: a wave writes a copy in step s + 1 only after every wave
+// has passed step s's barrier, and with it finished reading that copy in step
+// s - 1), and the chunk's A fragments (MM, or MM^T for the adjoint, stored
+// fragment-ordered in the record) stream from memory into registers ahead of
+// use.
 //   ADJ = false: S <- MM S + NN from s0, writing each chunk's start state;
 //   ADJ = true:  dS <- MM^T dS + NB from dsT, chunk after chunk from the last,
 //                writing each chunk's end-state gradient and finally ds0.
@@ -786,7 +789,7 @@ __device__ __forceinline__ void chain_mfma(int vt, int h, int n, const float *__
     using Rc = BwdRec<K, V, C>;
     constexpr int NW = 8, KS = K / 4, RBW = K / (16 * NW);  // waves; k-steps; row blocks per wave
     static_assert(K == 128 && V % 16 == 0 && RBW == 1, "eight waves of one 16-row block");
-    __shared__ float sS[K * 16];
+    __shared__ float sS[2][K * 16];
     __shared__ int red[64 * NW];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     int bos, eos;
@@ -840,7 +843,7 @@ __device__ __forceinline__ void chain_mfma(int vt, int h, int n, const float *__
                 for (int i = 0; i < 4; ++i) {
                     const int row = 16 * (RBW * w + b) + 4 * (lane >> 4) + i;
                     dst[(size_t)row * V] = acc[b][i];
-                    sS[row * 16 + (lane & 15)] = acc[b][i];
+                    sS[step & 1][row * 16 + (lane & 15)] = acc[b][i];
                 }
             float ad[RBW][4];
 #pragma unroll
@@ -863,8 +866,8 @@ __device__ __forceinline__ void chain_mfma(int vt, int h, int n, const float *__
                 }
 #pragma unroll
             for (int ks = 0; ks < KS; ks += 2) {
-                const float bv = sS[64 * ks + lane];  // B[k = 4 ks + lane / 16][lane % 16]
-                const float bw = sS[64 * (ks + 1) + lane];
+                const float bv = sS[step & 1][64 * ks + lane];  // B[k = 4 ks + lane / 16][lane % 16]
+                const float bw = sS[step & 1][64 * (ks + 1) + lane];
 #pragma unroll
                 for (int b = 0; b < RBW; ++b) {
                     acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[b][ks], bv, acc[b], 0, 0, 0);
@@ -873,7 +876,6 @@ __device__ __forceinline__ void chain_mfma(int vt, int h, int n, const float *__
             }
 #pragma unroll
             for (int b = 0; b < RBW; ++b) acc[b] += acc2[b];
-            __syncthreads();
         }
     }
     if (ADJ && fin)
