@@ -15,7 +15,9 @@ cases.
   hold state and value tiles as fp16 matrix operands; these scales sit inside
   the documented range).
 * Decay at the bf16 kernels' lower bound, and beyond it through fp32 inputs
-  (the documented route for steeper decay).
+  (the documented route for steeper decay); plain bf16 calls past the bound
+  (values unspecified) are held to what is documented for them: every write
+  lands in the outputs or the workspace (guard zones around each).
 """
 
 import numpy as np
@@ -207,3 +209,35 @@ def test_backward_malformed_cu_seqlens_stays_in_workspace():
                    workspace=ws[:need])
     torch.cuda.synchronize()
     assert bool((ws[need:] == 0xA5).all()), "the backward wrote past its workspace"
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_bf16_past_the_decay_bound_stays_in_bounds(path):
+    """Plain bf16 calls with g below the bound (every step at -2, 8x past it:
+    a precondition violation, values unspecified, since the fp16 decay
+    factors overflow) still write only their outputs: guard zones around o
+    and S_T, and around the two-pass workspace, stay bit-identical, and the
+    call returns normally."""
+    print(f"[case] bf16 past the decay bound (g = -2), {path}, guard zones", flush=True)
+    B, T, H, K = 2, 300, 3, 128
+    d = to_gpu(inputs.draw_fixed(99, B, T, H, K, K, "bf16", s0_std=0.1, g_lb=2.0, g_mode="bound"))
+    pad = 1 << 16
+    no, ns = B * T * H * K, B * H * K * K
+    ob = torch.full((no + 2 * pad,), float("nan"), device="cuda")
+    sb = torch.full((ns + 2 * pad,), float("nan"), device="cuda")
+    o = ob[pad:pad + no].view(B, T, H, K)
+    sT = sb[pad:pad + ns].view(B, H, K, K)
+    ws = None
+    if PATHS[path]:
+        need = kda.two_pass_workspace_bytes(B, B * T, H, K, K, 64)
+        wsb = torch.full((need + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda")
+        ws = wsb[pad:pad + need]
+    kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], out=o, final_state=sT,
+                  two_pass=PATHS[path], workspace=ws)
+    torch.cuda.synchronize()
+    for buf, n in ((ob, no), (sb, ns)):
+        assert bool(torch.isnan(buf[:pad]).all() and torch.isnan(buf[pad + n:]).all()), \
+            "a write landed outside the output"
+    if ws is not None:
+        assert bool((wsb[:pad] == 0xA5).all() and (wsb[pad + need:] == 0xA5).all()), \
+            "a write landed outside the workspace"
