@@ -323,6 +323,38 @@ def decode_leg(args, dev, stream):
 
     vms_all, _ = time_launches(verify(keep_all), args.decode_steps, 10, stream)
     vms_last, _ = time_launches(verify(keep_last), args.decode_steps, 10, stream)
+
+    # the workload's whole 1000-step loop, one launch per step, and the same
+    # steps as a HIP graph of the 8 pre-drawn steps replayed 125 times (the
+    # library allocates nothing and launches only on the caller's stream, so
+    # its calls can be captured)
+    n_loop = 1000
+
+    def timed(run):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    def eager_loop():
+        for _ in range(n_loop):
+            dstep()
+
+    loop_ms = timed(eager_loop)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for xi in steps_in:
+            kda.decode_step(xi["q"], xi["k"], xi["v"], xi["g"], xi["beta"], state, out=od)
+    graph.replay()
+
+    def graph_loop():
+        for _ in range(n_loop // nin):
+            graph.replay()
+
+    graph_ms = timed(graph_loop)
     return {
         "workload": DECODE, "value": wd.N / (dms * 1e-3), "unit": "tokens/s",
         "ms_per_step": dms, "steps": args.decode_steps,
@@ -332,6 +364,9 @@ def decode_leg(args, dev, stream):
                      "kernel": "decode_step_kernel", "alg_bytes_per_launch": db},
         "paged_ms_per_step": pms,
         "prologue_ms_per_step": proms,
+        "loop_1000": {"steps": n_loop, "eager_ms_total": loop_ms, "eager_ms_per_step": loop_ms / n_loop,
+                      "graph_ms_total": graph_ms, "graph_ms_per_step": graph_ms / n_loop,
+                      "graph": f"{nin} steps per graph, replayed {n_loop // nin} times"},
         "draft_verify": {"draft_tokens": td, "ms_keep_every_state": vms_all,
                          "ms_keep_last_state": vms_last,
                          "tokens_per_s_keep_last": wd.N * td / (vms_last * 1e-3),
