@@ -1542,10 +1542,13 @@ __global__ __launch_bounds__(512) void bwd_kgrad_mfma_kernel(
     for (int b = 0; b < RB; ++b) aQ[b] = aKp[b] = aKm[b] = z;
     aA[0] = aA[1] = aP[0] = aP[1] = z;
 
+    // Each value slice's inputs are loaded into registers one slice ahead
+    // (issued once the slice before is staged, in flight during its
+    // products), then staged transposed in LDS.
     constexpr int QO = (C * VB / 4 + NT - 1) / NT, QS = (K * VB / 4 + NT - 1) / NT;
-    for (int jb = 0; jb < V; jb += VB) {
-        __syncthreads();
-        float4 xo[QO], xs[QS], xx[QS];
+    constexpr int QR = (VB * C / 4 + NT - 1) / NT;
+    float4 xo[QO], xs[QS], xx[QS], xy[QR], xu[QR];
+    auto load_slice = [&](int jb) {
 #pragma unroll
         for (int i = 0; i < QO; ++i) {
             const int qi = t + NT * i, r = qi * 4 / VB, j = qi * 4 % VB;
@@ -1561,8 +1564,34 @@ __global__ __launch_bounds__(512) void bwd_kgrad_mfma_kernel(
                 xx[i] = *reinterpret_cast<const float4 *>(dSc + (size_t)c * V + jb + j);
             }
         }
-        rows_to_lds<VB, C, PTC, NT>(sYT, dYc + (size_t)jb * C);
-        rows_to_lds<VB, C, PTC, NT>(sUT, Uc + (size_t)jb * C);
+#pragma unroll
+        for (int i = 0; i < QR; ++i) {
+            const int qi = t + NT * i;
+            if (qi < VB * C / 4) {
+                xy[i] = reinterpret_cast<const float4 *>(dYc + (size_t)jb * C)[qi];
+                xu[i] = reinterpret_cast<const float4 *>(Uc + (size_t)jb * C)[qi];
+            }
+        }
+    };
+    load_slice(0);
+    for (int jb = 0; jb < V; jb += VB) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < QR; ++i) {  // the slice's dY^T and U^T rows, [VB][C] at pitch PTC
+            const int qi = t + NT * i;
+            if (qi < VB * C / 4) {
+                const int e = 4 * qi, r = e / C, c = e % C;
+                float *dy = sYT + r * PTC + c, *du = sUT + r * PTC + c;
+                dy[0] = xy[i].x;
+                dy[1] = xy[i].y;
+                dy[2] = xy[i].z;
+                dy[3] = xy[i].w;
+                du[0] = xu[i].x;
+                du[1] = xu[i].y;
+                du[2] = xu[i].z;
+                du[3] = xu[i].w;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < QO; ++i) {
             const int qi = t + NT * i, r = qi * 4 / VB, j = qi * 4 % VB;
@@ -1589,6 +1618,7 @@ __global__ __launch_bounds__(512) void bwd_kgrad_mfma_kernel(
             }
         }
         __syncthreads();
+        if (jb + VB < V) load_slice(jb + VB);
 #pragma unroll 2
         for (int ks = 0; ks < VB / 4; ++ks) {
             const int jr = 4 * ks + lq;  // the k (value column) this lane supplies
