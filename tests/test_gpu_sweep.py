@@ -91,3 +91,111 @@ def test_forward_sweep(seed):
     es = rel_err(sT, s_ref)
     report(f"sweep_{seed}", o=eo, sT=es)
     assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+# The paged prefill (prefix-cache snapshots): each seeded case draws the
+# implementation, packed lengths, start positions on the chunk grid, a block
+# table with unmapped pages, initial states from slots or none, final states in
+# place or in fresh slots, and a random subset of the prologue maps; expected
+# values: the oracle's outputs and final states, and for a snapshot at
+# boundary p the oracle's state after the sequence's first p - start tokens;
+# slots the call must not write stay bit-identical.
+PAGED_IMPLS = [("bf16", 128, True), ("bf16", 128, False), ("bf16", 128, None), ("f32", 128, None),
+               ("f32", 32, None), ("bf16", 32, None)]
+PAGED_CASES = 16
+
+
+def _paged_case(seed):
+    rng = np.random.default_rng(9500 + seed)
+    dtype, K, two_pass = PAGED_IMPLS[int(rng.integers(0, len(PAGED_IMPLS)))]
+    C = 16 if K == 32 else 64
+    f = C // 16 if K == 32 else 4
+    snap, page = 64 * f, 256 * f                     # 4 snapshot slots per page
+    N = int(rng.integers(1, 6))
+    cap = 300 if (dtype == "f32" and K == 128) else 3 * page
+    lengths = [int(rng.choice([0, 1, C - 1, C, snap, snap + 1, page])) if rng.random() < 0.4
+               else int(rng.integers(0, cap)) for _ in range(N)]
+    start = [int(rng.integers(0, 3 * page // C)) * C for _ in range(N)]
+    per = page // snap
+    pages_used, table = 0, []
+    nblk = max((s + L) // page + 1 for s, L in zip(start, lengths))
+    for n in range(N):
+        row = []
+        for b in range(nblk):
+            if rng.random() < 0.75:
+                row.append(pages_used)
+                pages_used += 1
+            else:
+                row.append(-1)
+        table.append(row)
+    nxt = pages_used * per                            # state slots after the pages
+    s0_slot, sT_slot = [], []
+    for n in range(N):
+        if rng.random() < 0.6:
+            s0_slot.append(nxt)
+            nxt += 1
+        else:
+            s0_slot.append(-1)
+        if s0_slot[-1] >= 0 and rng.random() < 0.5:
+            sT_slot.append(s0_slot[-1])               # in place
+        else:
+            sT_slot.append(nxt)
+            nxt += 1
+    flags = int(rng.integers(1, 8)) if rng.random() < 0.4 else 0
+    return dict(dtype=dtype, K=K, two_pass=two_pass, snap=snap, page=page, lengths=lengths,
+                start=start, table=table, s0_slot=s0_slot, sT_slot=sT_slot, slots=nxt + 1,
+                H=int(rng.choice([1, 2, 3])), flags=flags)
+
+
+@pytest.mark.parametrize("seed", range(PAGED_CASES))
+def test_paged_prefill_sweep(seed):
+    from tests.test_gpu_paged import _expected_paged_fwd, _pool
+    c = _paged_case(seed)
+    print(f"[case] paged sweep seed={seed} {c}", flush=True)
+    dtype, K, H = c["dtype"], c["K"], c["H"]
+    p = None
+    if c["flags"]:
+        fl = c["flags"]
+        raw = inputs.draw_raw_varlen(600 + seed, H, K, K, dtype, c["lengths"])
+        plain = inputs.draw_varlen(800 + seed, H, K, K, dtype, lengths=c["lengths"], g_lb=G_LB)
+        d = dict(raw)
+        if not fl & 1:
+            d["q"], d["k"] = plain["q"], plain["k"]
+        if not fl & 2:
+            d["g"] = plain["g"]
+        if not fl & 4:
+            d["beta"] = plain["beta"]
+        p = kda.Prologue(normalize_qk=bool(fl & 1), gate_lower_bound=G_LB if fl & 2 else None,
+                         beta_logits=bool(fl & 4), norm_eps=1e-6 if fl & 1 else 0.0)
+        q, k, g, b = oracle.prologue(d["q"], d["k"], d["g"], d["beta"],
+                                     normalize_qk=p.normalize_qk,
+                                     gate_lower_bound=p.gate_lower_bound,
+                                     beta_logits=p.beta_logits, norm_eps=p.norm_eps)
+        ref_in = dict(q=q, k=k, v=oracle.as_f64(d["v"]), g=g, beta=b)
+    else:
+        d = inputs.draw_varlen(600 + seed, H, K, K, dtype, lengths=c["lengths"], g_lb=G_LB)
+        ref_in = {x: oracle.as_f64(d[x]) for x in ("q", "k", "v", "g", "beta")}
+    cu = d["cu_seqlens"].numpy().astype(np.int64)
+    pool0 = _pool(700 + seed, c["slots"], H, K, K)
+    o_ref, s_ref, snaps = _expected_paged_fwd(ref_in, cu, pool0, c["s0_slot"], c["start"],
+                                              c["table"], c["snap"], c["page"])
+    x = to_gpu(d)
+    pool = pool0.cuda()
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    o = kda.varlen_fwd_paged(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"], pool,
+                             s0_slot=i32(c["s0_slot"]), sT_slot=i32(c["sT_slot"]),
+                             start_pos=i32(c["start"]), block_table=i32(c["table"]),
+                             snap_tokens=c["snap"], page_tokens=c["page"],
+                             two_pass=c["two_pass"], prologue=p)
+    torch.cuda.synchronize()
+    errs = {"o": rel_err(o, o_ref)}
+    for n, sl in enumerate(c["sT_slot"]):
+        errs[f"sT{n}"] = rel_err(pool[sl], s_ref[n])
+    for slot, ref in snaps.items():
+        errs[f"snap{slot}"] = rel_err(pool[slot], ref)
+    report(f"paged_sweep_{seed}", **{k2: v2 for k2, v2 in list(errs.items())[:6]})
+    assert all(e <= TOL[dtype] for e in errs.values()), errs
+    written = set(snaps) | set(c["sT_slot"])
+    for s in range(c["slots"]):
+        if s not in written:
+            assert torch.equal(pool[s].cpu(), pool0[s]), f"slot {s} was modified"
