@@ -199,3 +199,39 @@ def test_paged_prefill_sweep(seed):
     for s in range(c["slots"]):
         if s not in written:
             assert torch.equal(pool[s].cpu(), pool0[s]), f"slot {s} was modified"
+
+
+# The backward pass: each seeded case draws the input dtype and head size,
+# packed lengths (zeros and chunk edges among them), head count, and whether
+# an initial state and a final-state gradient are given; every gradient is
+# compared with the oracle's (autograd of the plain fp64 recurrence).
+BWD_CASES = 12
+
+
+def _bwd_case(seed):
+    rng = np.random.default_rng(9700 + seed)
+    dtype, K = [("bf16", 128), ("bf16", 128), ("f32", 128), ("f32", 32), ("bf16", 32)][
+        int(rng.integers(0, 5))]
+    C = 64 if K == 128 else 16
+    N = int(rng.integers(1, 5))
+    hi = 260 if K == 128 else 120
+    lengths = [int(rng.choice([0, 1, C - 1, C, C + 1])) if rng.random() < 0.4
+               else int(rng.integers(0, hi)) for _ in range(N)]
+    return dict(dtype=dtype, K=K, lengths=lengths, H=int(rng.choice([1, 2, 3])),
+                s0=bool(rng.random() < 0.6), dsT=bool(rng.random() < 0.6))
+
+
+@pytest.mark.parametrize("seed", range(BWD_CASES))
+def test_backward_sweep(seed):
+    from tests.test_gpu_bwd import _grads_case
+    c = _bwd_case(seed)
+    print(f"[case] backward sweep seed={seed} {c}", flush=True)
+    dtype, K, H, lengths = c["dtype"], c["K"], c["H"], c["lengths"]
+    d = inputs.draw_varlen(900 + seed, H, K, K, dtype, lengths=lengths,
+                           s0_std=0.1 if c["s0"] else None, g_lb=G_LB)
+    rng = np.random.default_rng(950 + seed)
+    tot = int(sum(lengths))
+    do = torch.from_numpy(rng.standard_normal((tot, H, K)).astype(np.float32))
+    dsT = (torch.from_numpy(rng.standard_normal((len(lengths), H, K, K)).astype(np.float32))
+           if c["dsT"] else None)
+    _grads_case(f"bwd_sweep_{seed}", d, d["cu_seqlens"].numpy(), dtype, do, dsT)
