@@ -1,4 +1,5 @@
-"""Seeded combinational sweep of the forward entry points against the oracle.
+"""Seeded combinational sweeps of the entry points against the oracle: the
+packed forward, the paged forward, the backward pass and multi-token decode.
 
 The other GPU tests vary one property at a time (length, head count, path,
 output type, prologue map); here each case draws all of them together from
@@ -235,3 +236,108 @@ def test_backward_sweep(seed):
     dsT = (torch.from_numpy(rng.standard_normal((len(lengths), H, K, K)).astype(np.float32))
            if c["dsT"] else None)
     _grads_case(f"bwd_sweep_{seed}", d, d["cu_seqlens"].numpy(), dtype, do, dsT)
+
+
+# Multi-token decode through state slots (T = 1 is the single paged step):
+# each seeded case draws dtype and head size, T, the input slots (none, own,
+# or one shared by two sequences that branch from it), which token states are
+# kept and where (fresh slots, or the sequence's own input slot for its last
+# token), and prologue maps; outputs and every kept state are compared with
+# the oracle, and every other slot must stay bit-identical.
+DEC_CASES = 12
+
+
+def _decode_case(seed):
+    rng = np.random.default_rng(9900 + seed)
+    dtype, K = [("bf16", 128), ("f32", 128), ("bf16", 32), ("f32", 32)][int(rng.integers(0, 4))]
+    N, T, H = int(rng.integers(1, 7)), int(rng.integers(1, 6)), int(rng.choice([1, 2, 3]))
+    nxt = 0
+    slot_in = []
+    for n in range(N):
+        r = rng.random()
+        if r < 0.2:
+            slot_in.append(-1)
+        elif r < 0.35 and n > 0 and slot_in[-1] >= 0:
+            slot_in.append(slot_in[-1])               # branch from the previous sequence's state
+        else:
+            slot_in.append(nxt)
+            nxt += 1
+    shared = {s for s in slot_in if s >= 0 and slot_in.count(s) > 1}
+    slot_out = []
+    for n in range(N):
+        row = []
+        for j in range(T):
+            if j == T - 1 and slot_in[n] >= 0 and slot_in[n] not in shared and rng.random() < 0.5:
+                row.append(slot_in[n])                # the accepted state back in place
+            elif rng.random() < 0.5:
+                row.append(nxt + 100)                 # fresh slots, numbered after the inputs
+                nxt += 1
+            else:
+                row.append(-1)
+        slot_out.append(row)
+    n_in = max([s for s in slot_in if s >= 0] + [-1]) + 1
+    slot_out = [[s - 100 + n_in if s >= 100 else s for s in row] for row in slot_out]
+    flags = int(rng.integers(1, 8)) if rng.random() < 0.4 else 0
+    return dict(dtype=dtype, K=K, N=N, T=T, H=H, slot_in=slot_in, slot_out=slot_out,
+                slots=nxt + n_in + 1, flags=flags)
+
+
+@pytest.mark.parametrize("seed", range(DEC_CASES))
+def test_decode_sweep(seed):
+    from tests.test_gpu_paged import _pool
+    c = _decode_case(seed)
+    print(f"[case] decode sweep seed={seed} {c}", flush=True)
+    dtype, K, N, T, H = c["dtype"], c["K"], c["N"], c["T"], c["H"]
+    lengths = [T] * N
+    p = None
+    if c["flags"]:
+        fl = c["flags"]
+        raw = inputs.draw_raw_varlen(1000 + seed, H, K, K, dtype, lengths)
+        plain = inputs.draw_varlen(1100 + seed, H, K, K, dtype, lengths=lengths, g_lb=G_LB)
+        d = dict(raw)
+        if not fl & 1:
+            d["q"], d["k"] = plain["q"], plain["k"]
+        if not fl & 2:
+            d["g"] = plain["g"]
+        if not fl & 4:
+            d["beta"] = plain["beta"]
+        p = kda.Prologue(normalize_qk=bool(fl & 1), gate_lower_bound=G_LB if fl & 2 else None,
+                         beta_logits=bool(fl & 4), norm_eps=1e-6 if fl & 1 else 0.0)
+        q, k, g, b = oracle.prologue(d["q"], d["k"], d["g"], d["beta"],
+                                     normalize_qk=p.normalize_qk,
+                                     gate_lower_bound=p.gate_lower_bound,
+                                     beta_logits=p.beta_logits, norm_eps=p.norm_eps)
+        r = dict(q=q, k=k, v=oracle.as_f64(d["v"]), g=g, beta=b)
+    else:
+        d = inputs.draw_varlen(1000 + seed, H, K, K, dtype, lengths=lengths, g_lb=G_LB)
+        r = {x: oracle.as_f64(d[x]) for x in ("q", "k", "v", "g", "beta")}
+    pool0 = _pool(1200 + seed, c["slots"], H, K, K)
+    s0 = np.zeros((N, H, K, K))
+    for n in range(N):
+        if c["slot_in"][n] >= 0:
+            s0[n] = pool0[c["slot_in"][n]].double().numpy()
+    cu = np.arange(N + 1) * T
+    o_ref, _ = oracle.recurrence(r["q"], r["k"], r["v"], r["g"], r["beta"], cu, s0)
+    kept = {}
+    for n in range(N):
+        for j in range(T):
+            if c["slot_out"][n][j] >= 0:
+                sl = {x: r[x][n * T:n * T + j + 1] for x in r}
+                _, st = oracle.recurrence(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"],
+                                          np.array([0, j + 1]), s0[n:n + 1])
+                kept[c["slot_out"][n][j]] = st[0]
+    x = to_gpu(d)
+    shp = lambda t, D: t.reshape(N, T, H, D) if D else t.reshape(N, T, H)
+    pool = pool0.cuda()
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    o = kda.decode_multi_paged(shp(x["q"], K), shp(x["k"], K), shp(x["v"], K), shp(x["g"], K),
+                               shp(x["beta"], 0), pool, i32(c["slot_in"]), i32(c["slot_out"]),
+                               prologue=p)
+    torch.cuda.synchronize()
+    errs = {"o": rel_err(o.reshape(N * T, H, K), o_ref)}
+    for slot, ref in kept.items():
+        errs[f"s{slot}"] = rel_err(pool[slot], ref)
+    report(f"decode_sweep_{seed}", **{k2: v2 for k2, v2 in list(errs.items())[:6]})
+    assert all(e <= TOL[dtype] for e in errs.values()), errs
+    for s in set(range(c["slots"])) - set(kept):
+        assert torch.equal(pool[s].cpu(), pool0[s]), f"slot {s} was modified"
