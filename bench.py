@@ -546,7 +546,7 @@ def next_legs(args, dev, stream):
         kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, initial_state=x["s0"],
                       dsT=dsT, chunk=w.chunk, workspace=bws)
 
-    ms_bwd, _ = time_launches(step_bwd, max(5, steps // 5), 3, stream)
+    ms_bwd, _ = time_launches(step_bwd, max(20, steps), 5, stream)
     bwd_b = bwd_alg_bytes(w.B, w.T, w.H, w.K, w.V)
     tokens = w.B * w.T
     return {
