@@ -18,7 +18,7 @@ import torch
 __all__ = ["chunk_fwd", "varlen_fwd", "varlen_fwd_noalloc", "decode_step", "varlen_fwd_paged", "decode_step_paged",
            "decode_multi_paged", "Prologue", "chunk_bwd", "varlen_bwd", "bwd_workspace_bytes",
            "workspace_bytes",
-           "two_pass_workspace_bytes", "library",
+           "two_pass_workspace_bytes", "library", "kda_varlen", "kda_chunk",
            "KdaError", "LIB_PATH", "F32", "BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -501,3 +501,46 @@ def varlen_bwd(q, k, v, g, beta, do, cu_seqlens, initial_state=None, dsT=None, c
           _ptr(cu_seqlens), N, total, H, K, V, chunk, _dtype_code(dt), _ptr(ws), ws.numel(),
           _stream(q.device))
     return (*grads, ds0)
+
+
+class _KdaVarlen(torch.autograd.Function):
+    """varlen_fwd with its gradients from varlen_bwd (both the library's
+    kernels); outputs that the loss does not use contribute no gradient."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, cu_seqlens, initial_state, two_pass):
+        o, sT = varlen_fwd(q, k, v, g, beta, cu_seqlens, initial_state, two_pass=two_pass)
+        ctx.save_for_backward(q, k, v, g, beta, cu_seqlens, initial_state)
+        ctx.set_materialize_grads(False)
+        return o, sT
+
+    @staticmethod
+    def backward(ctx, do, dsT):
+        q, k, v, g, beta, cu, s0 = ctx.saved_tensors
+        if do is None:
+            do = torch.zeros(v.shape, dtype=torch.float32, device=v.device)
+        do = do.float().contiguous()
+        dsT = dsT.float().contiguous() if dsT is not None else None
+        dq, dk, dv, dg, db, ds0 = varlen_bwd(q, k, v, g, beta, do, cu, initial_state=s0,
+                                             dsT=dsT, need_ds0=ctx.needs_input_grad[6])
+        return (dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dg.to(g.dtype),
+                db.to(beta.dtype), None, ds0, None)
+
+
+def kda_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, two_pass=None):
+    """Differentiable packed KDA: (o [total_T, H, V] float32, S_T [N, H, K, V]
+    float32), with gradients for q, k, v, g, beta (in their own dtype) and
+    initial_state through torch autograd.  Arguments as for varlen_fwd; the
+    gradients are those of varlen_bwd (fp32 arithmetic), so the decay
+    precondition of the backward applies."""
+    return _KdaVarlen.apply(q, k, v, g, beta, cu_seqlens, initial_state, two_pass)
+
+
+def kda_chunk(q, k, v, g, beta, initial_state=None, two_pass=None):
+    """kda_varlen over a fixed-length batch: q, k, g [B, T, H, K], v [B, T, H, V],
+    beta [B, T, H]; returns (o [B, T, H, V], S_T [B, H, K, V])."""
+    B, T, H = q.shape[0], q.shape[1], q.shape[2]
+    cu = torch.arange(B + 1, dtype=torch.int32, device=q.device) * T
+    flat = [x.reshape(B * T, *x.shape[2:]) for x in (q, k, v, g, beta)]
+    o, sT = kda_varlen(*flat, cu, initial_state, two_pass)
+    return o.view(B, T, H, v.shape[-1]), sT
